@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X Gated DeltaNet path; prints ONE JSON line.
+
+Headline workload: batched decode, B=64, Hk=16, Hv=32, D=128, bf16 operands,
+float32 state, 100 chained decode steps updating the state in place (fresh
+operands per step, already resident in HBM).  One benchmark "step" is one
+such 100-token chain; ``value`` is the state traffic of the chain
+(2 * 4 * B * Hv * D * D bytes per decode step: one read and one write of every
+state row) divided by its time, in GB/s.
+
+Also measured (object "scan"): the prefill scan B=1 T=4096 (bf16, token-major)
+and the head-major scan B=16 T=1024 (f16), in tokens/s and algorithmic
+TFLOP/s (7 * D * D flops per head-token) against the FP32 vector peak.
+
+``roofline`` is for the decode kernel: algorithmic bytes per launch over its
+average launch time (HIP events on the launch stream over the timed region),
+against MI355X's 8 TB/s; ``traffic`` comes from the committed rocprofv3
+FETCH_SIZE/WRITE_SIZE summary when it was taken on the current kernel source.
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN decode state GB/s + scan tokens/s, % of MI355X HBM/FP32 roofline"
+HBM_PEAK_GBS = 8000.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_b64_counters.txt")
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrence_recurrent_amd", "csrc",
+                          "gdn_kernels.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_counters():
+    """HBM bytes per decode launch from the committed rocprofv3 summary, or None
+    when the summary is missing or was taken on another kernel source."""
+    if not os.path.exists(DECODE_COUNTERS):
+        return None
+    kv = {}
+    for line in open(DECODE_COUNTERS):
+        m = re.match(r"^\s*([a-z_0-9]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Launcher:
+    """Pre-marshalled C-ABI call (no per-call Python validation in the timed loop)."""
+
+    def __init__(self, fn_name, desc, tensors, stream):
+        from linear_attention_recurrence_recurrent_amd import _native
+        self.fn = getattr(_native.lib(), fn_name)
+        self.desc = desc
+        self.args = [ctypes.byref(desc)] + [
+            None if t is None else ctypes.c_void_p(t.data_ptr()) for t in tensors
+        ] + [ctypes.c_void_p(stream)]
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc:
+            from linear_attention_recurrence_recurrent_amd import _native
+            raise RuntimeError("launch rejected: %s" % _native.last_error())
+
+
+def bench_decode(args, torch):
+    import linear_attention_recurrence_recurrent_amd as gdn
+    from linear_attention_recurrence_recurrent_amd import synth
+    wl = synth.WORKLOADS[2]
+    log("decode: drawing operands (B=%d, %d steps)" % (wl.B, wl.steps))
+    ops = synth.make(wl)
+    steps = synth.step_slices(ops, head_major=False)
+    dev = torch.device("cuda:0")
+    d_steps = [{n: t.to(dev) for n, t in st.items()} for st in steps]
+    w = ops["w"].to(dev)
+    state = ops["s0"].to(dev).clone()
+    ys = [torch.empty(st["v"].shape, dtype=torch.float32, device=dev) for st in d_steps]
+    stream = torch.cuda.current_stream(dev)
+    desc = gdn._desc(wl.B, 1, wl.Hk, wl.Hv, wl.Dk, wl.Dv, False, 2, 2, True, True, 1e-6, 1e-6)
+    calls = [Launcher("gdn_recurrent_step", desc,
+                      [st["q"], st["k"], st["v"], st["log_decay"], st["beta"], state, st["z"], w,
+                       y, state], stream.cuda_stream) for st, y in zip(d_steps, ys)]
+
+    def chain():
+        for c in calls:
+            c()
+
+    for _ in range(args.warmup):
+        chain()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        chain()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    launches = args.steps * wl.steps
+    state_bytes = 2 * 4 * wl.B * wl.Hv * wl.Dv * wl.Dk
+    es = 2  # bf16
+    io_bytes = (2 * wl.B * wl.Hk * wl.Dk * es + 2 * wl.B * wl.Hv * wl.Dv * es
+                + 2 * wl.B * wl.Hv * es + wl.Dv * es + wl.B * wl.Hv * wl.Dv * 4)
+    launch_s = ms * 1e-3 / launches
+    ms_per_chain = ms / args.steps
+    value = state_bytes * wl.steps / (ms_per_chain * 1e-3) / 1e9
+    achieved = (state_bytes + io_bytes) / launch_s / 1e9
+    traffic = read_counters()
+    res = dict(ms_per_step=ms_per_chain, value=value, launch_us=launch_s * 1e6,
+               roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic, "kernel": "decode_kernel<128,8,2,8>",
+                         "algorithmic_bytes_per_launch": state_bytes + io_bytes,
+                         "avg_launch_us": round(launch_s * 1e6, 3)})
+    log("decode: %.3f ms per 100-step chain, %.1f us per launch, state %.1f GB/s" %
+        (ms_per_chain, launch_s * 1e6, value))
+    return res, ops
+
+
+def bench_scan(idx, args, torch):
+    import linear_attention_recurrence_recurrent_amd as gdn
+    from linear_attention_recurrence_recurrent_amd import synth
+    wl = synth.WORKLOADS[idx]
+    log("scan %d: drawing operands (%s)" % (idx, wl.name))
+    ops = synth.make(wl)
+    dev = torch.device("cuda:0")
+    d = {n: t.to(dev) for n, t in ops.items()}
+    del ops
+    y = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
+    s_out = torch.empty_like(d["s0"])
+    stream = torch.cuda.current_stream(dev)
+    dt = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+    desc = gdn._desc(wl.B, wl.T, wl.Hk, wl.Hv, wl.Dk, wl.Dv, wl.head_major, dt, dt, True, True,
+                     1e-6, 1e-6)
+    call = Launcher("gdn_scan", desc, [d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
+                                       d["z"], d["w"], y, s_out], stream.cuda_stream)
+    reps = max(3, args.steps)
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 7.0 * wl.B * wl.T * wl.Hv * wl.Dv * wl.Dk
+    tflops = flops / (ms * 1e-3) / 1e12
+    tok = wl.B * wl.T / (ms * 1e-3)
+    log("scan %d: %.1f us per call, %.2f M tok/s, %.1f TFLOP/s" % (idx, ms * 1e3, tok / 1e6, tflops))
+    return {"workload": wl.name, "us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(tok, 1),
+            "tflops": round(tflops, 2), "peak_tflops": FP32_VALU_PEAK_TFLOPS,
+            "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4), "bound": "alu",
+            "algorithmic_flops_per_call": flops}
+
+
+def cpu_baseline(ops, args):
+    """The float64 oracle on the first ``n`` tokens of the decode chain, all 64
+    sequences (n chained steps == the scan over n tokens)."""
+    import numpy as np
+    from oracle import gdn_oracle as orc
+    n = args.cpu_tokens
+    sl = {k: (v[:, :n] if k not in ("s0", "w") else v) for k, v in ops.items()}
+    f64 = {k: np.ascontiguousarray(v.double().numpy()) for k, v in sl.items()}
+    threads = orc.default_threads()
+    orc.scan(**{k: (v[:1, :1] if k not in ("w",) else v) for k, v in f64.items()})  # load/build
+    t0 = time.perf_counter()
+    orc.scan(**f64, threads=threads)
+    dt = time.perf_counter() - t0
+    B, Hv, D = ops["s0"].shape[0], ops["s0"].shape[1], ops["s0"].shape[2]
+    gbs = 2 * 4 * B * Hv * D * D * n / dt / 1e9
+    log("cpu oracle: %d tokens x B=%d in %.2f s on %d threads: %.3f GB/s" % (n, B, dt, threads, gbs))
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "float64 three-pass oracle, decode B=64 Hk16 Hv32 D128, first %d of the "
+                      "100 chained steps (%.1f s)" % (n, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-scan", action="store_true", help="skip the scan sub-measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode (each (batch, "
+              "value head) pair is independent; see the sharding note in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import linear_attention_recurrence_recurrent_amd  # noqa: F401  (fails loudly if unbuilt)
+    dec, ops = bench_decode(args, torch)
+    scan = {}
+    if not args.no_scan:
+        scan["prefill_b1_t4096_bf16"] = bench_scan(3, args, torch)
+        scan["head_major_b16_t1024_f16"] = bench_scan(4, args, torch)
+    out = {
+        "metric": METRIC,
+        "value": round(dec["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode B64 Hk16 Hv32 D128, bf16 operands, f32 state, 100 chained "
+                               "in-place steps per benchmark step",
+                   "B": 64, "Hk": 16, "Hv": 32, "D": 128, "tokens_per_step": 100,
+                   "parallelism": "single GPU"},
+        "roofline": dec["roofline"],
+    }
+    if scan:
+        out["scan"] = scan
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(ops, args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet recurrence library
+ * (libgdn_hip.so).
+ *
+ * What the library computes.  Each value head (b, hv) keeps a D x D float32
+ * memory S whose row a is a value lane and whose column c is a key lane
+ * (S is stored [B, Hv, Dv, Dk]).  Per token, with q, k read from key head
+ * hk = hv / (Hv / Hk):
+ *     k^ = k / sqrt(sum k^2 + qk_eps)              (GDN_FOLD_QK_L2NORM)
+ *     q^ = q / sqrt(sum q^2 + qk_eps) / sqrt(Dk)   (GDN_FOLD_QK_L2NORM, GDN_FOLD_Q_SCALE)
+ *     alpha = exp(log_decay),  beta as given
+ *     u = S.k^ ;  S = alpha*S + beta*(v - alpha*u) k^T ;  o = S.q^  (updated S)
+ *     y = rmsnorm(o * silu(z)) * w   when z and w are given, else y = o.
+ * Sources: the "Module gdn" page (logicaffeine codegen_cuda/gdn), module
+ * description, for the recurrence and the gate-first RMSNorm, and its section
+ * "The fusion" for the single pass per state row that the kernels use
+ * (o = alpha*(S_old.q) + coef*(k.q), coef = beta*(v - alpha*u)); the
+ * "gated_delta" page (torch-to-nnef op reference): emit_native_gdn_recurrent
+ * for the operand tuple (q, k, v, log_decay, beta, s0), the [B, S, H, W] and
+ * head-major [B, H, S, W] layouts and the caller-created (output,
+ * final_state); gated_delta_fake for the float32 output whatever the input
+ * dtype; native_gdn_reject_reason for the folded q/k L2 norm and
+ * 1/sqrt(head_dim) scale and the short reject reason; native_gdn_min_version
+ * for the version query.
+ *
+ * Conventions common to every call.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, dense and
+ *     row-major in the layout given below.  The library allocates nothing,
+ *     keeps no state between calls and never synchronises: all work is
+ *     enqueued on `stream` (a hipStream_t; NULL is the null stream) on the
+ *     current HIP device, and the call returns as soon as it is enqueued.
+ *   - Layouts (head_major == 0 / 1):
+ *         q, k        [B, T, Hk, Dk]   /  [B, Hk, T, Dk]      dtype
+ *         v, z        [B, T, Hv, Dv]   /  [B, Hv, T, Dv]      dtype
+ *         log_decay,
+ *         beta        [B, T, Hv]       /  [B, Hv, T]          gate_dtype
+ *         y           [B, T, Hv, Dv]   /  [B, Hv, T, Dv]      float32
+ *         s0, s_out   [B, Hv, Dv, Dk]                          float32
+ *         w           [Dv]                                     dtype
+ *   - z and w are optional and go together: both NULL gives the raw output
+ *     y = o; both given gives the gated output.
+ *   - s_out may be exactly s0 (in-place state update); any other overlap
+ *     between an output and any operand is rejected.
+ *   - q, k, v, z, y, s0, s_out must be 16-byte aligned; log_decay, beta and w
+ *     aligned to their element size.
+ *   - Supported by the kernels: Dk == Dv in {16, 32, 64, 128}; dtype and
+ *     gate_dtype in {GDN_F32, GDN_F16, GDN_BF16}; Hv a multiple of Hk.
+ *   - Error behaviour: every call returns GDN_OK or a gdn_status; the short
+ *     reason of the last failure on the calling thread is gdn_last_error().
+ *     A rejected call enqueues nothing.  A HIP launch failure returns
+ *     GDN_EDEVICE.  NaN/Inf in the operands propagate; they are not checked.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_EINVAL = 1,       /* null descriptor or pointer, bad flag, eps or layout value */
+  GDN_ESHAPE = 2,       /* negative or zero extent, or sizes that overflow */
+  GDN_EDTYPE = 3,       /* dtype or gate_dtype not one of gdn_dtype */
+  GDN_EGROUP = 4,       /* Hv is not a multiple of Hk */
+  GDN_EUNSUPPORTED = 5, /* valid, but not covered by the kernels (head dims, T != 1 for a step) */
+  GDN_EALIGN = 6,       /* pointer alignment */
+  GDN_EALIAS = 7,       /* an output overlaps an operand (other than s_out == s0) */
+  GDN_EDEVICE = 8       /* the HIP runtime reported an error */
+} gdn_status;
+
+/* flags */
+#define GDN_FOLD_QK_L2NORM 1u /* L2-normalise q and k inside the op */
+#define GDN_FOLD_Q_SCALE 2u   /* multiply q^ by 1/sqrt(Dk) inside the op */
+
+typedef struct gdn_desc {
+  int64_t B, T, Hk, Hv, Dk, Dv; /* batch, tokens, key heads, value heads, head dims */
+  int32_t head_major;           /* 0: [B, T, H, ...] operands; 1: [B, H, T, ...] */
+  int32_t dtype;                /* gdn_dtype of q, k, v, z, w */
+  int32_t gate_dtype;           /* gdn_dtype of log_decay and beta */
+  uint32_t flags;               /* GDN_FOLD_* bits */
+  float qk_eps;                 /* eps inside the q/k L2 norm's square root (1e-6) */
+  float norm_eps;               /* eps of the gated RMSNorm (1e-6) */
+} gdn_desc;
+
+/* One decode step (d->T must be 1): reads s0, writes y [B, 1, Hv, Dv] and the
+ * updated state to s_out (s_out == s0 updates the state in place).  The
+ * fused decode operator of the "gated_delta" page (native_gdn_reject_reason)
+ * with the recurrence and gated norm of the "Module gdn" page.  Each state
+ * row is read from memory once and written once. */
+int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const void* v,
+                       const void* log_decay, const void* beta, const float* s0,
+                       const void* z, const void* w, float* y, float* s_out, void* stream);
+
+/* The recurrence over the whole time axis ("gated_delta" page,
+ * gated_delta_reference: the recurrence over the time axis returning
+ * (output, final_state)).  Any T >= 0; T == 0 copies s0 to s_out (unless
+ * they are the same buffer) and writes no y.  The state stays in registers
+ * for the whole time axis; s_out receives the state after the last token. */
+int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
+             const void* log_decay, const void* beta, const float* s0, const void* z,
+             const void* w, float* y, float* s_out, void* stream);
+
+/* Validation only, no device work: GDN_OK when gdn_scan would accept these
+ * arguments, else the status with its short reason in gdn_last_error()
+ * ("gated_delta" page, native_gdn_reject_reason: why operands cannot become
+ * the fused operator, as a short reason for logging).  Host-only; safe to
+ * call on a machine with no GPU. */
+int gdn_check(const gdn_desc* d, const void* q, const void* k, const void* v,
+              const void* log_decay, const void* beta, const float* s0, const void* z,
+              const void* w, const float* y, const float* s_out);
+
+/* Short reason for the last non-OK status returned on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* Static name of a gdn_status value. */
+const char* gdn_status_str(int status);
+
+/* GDN_ABI_VERSION of the loaded library ("gated_delta" page,
+ * native_gdn_min_version: the first release carrying the fused operator). */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,167 @@
+"""MI355X (gfx950) Gated DeltaNet recurrence: thin Python binding of libgdn_hip.so.
+
+``recurrent_step`` (single-token decode) and ``scan`` (the whole time axis)
+follow the operator contract of the "gated_delta" page (torch-to-nnef op
+reference): operands (q, k, v, log_decay, beta, s0), token-major
+[B, S, H, W] or head-major [B, H, S, W] layout, outputs (y, final_state) with
+y in float32 whatever the input dtype.  The recurrence and the optional
+gate-first RMSNorm are those of the "Module gdn" page (logicaffeine
+codegen_cuda/gdn).  torch supplies device memory and the current stream; all
+arithmetic runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _native
+from ._native import GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GdnDesc
+
+__all__ = ["recurrent_step", "scan", "check", "abi_version", "GdnError"]
+
+_DT = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
+       torch.bfloat16: _native.GDN_BF16}
+
+
+class GdnError(ValueError):
+    """A call the library rejected; ``status`` is the gdn_status name."""
+
+    def __init__(self, status: int, reason: str):
+        self.status = _native.STATUS.get(status, str(status))
+        super().__init__("%s: %s" % (self.status, reason))
+
+
+def abi_version() -> int:
+    return _native.lib().gdn_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _desc(B, T, Hk, Hv, Dk, Dv, head_major, dtype, gate_dtype, fold_qk_l2norm, fold_q_scale,
+          qk_eps, norm_eps) -> GdnDesc:
+    flags = (GDN_FOLD_QK_L2NORM if fold_qk_l2norm else 0) | (GDN_FOLD_Q_SCALE if fold_q_scale else 0)
+    return GdnDesc(B, T, Hk, Hv, Dk, Dv, int(bool(head_major)), dtype, gate_dtype, flags,
+                   float(qk_eps), float(norm_eps))
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise GdnError(3, "%s has unsupported dtype %s" % (name, t.dtype))
+    return _DT[t.dtype]
+
+
+def _prepare(q, k, v, log_decay, beta, s0, z, w, head_major, T_expected=None):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
+        raise GdnError(2, "q, k must be 4-d with equal shapes and v 4-d")
+    if head_major:
+        B, Hk, T, Dk = q.shape
+        Bv, Hv, Tv, Dv = v.shape
+        gshape = (B, Hv, T)
+    else:
+        B, T, Hk, Dk = q.shape
+        Bv, Tv, Hv, Dv = v.shape
+        gshape = (B, T, Hv)
+    if (Bv, Tv) != (B, T):
+        raise GdnError(2, "v batch/time %s do not match q %s" % ((Bv, Tv), (B, T)))
+    if tuple(log_decay.shape) != gshape or tuple(beta.shape) != gshape:
+        raise GdnError(2, "log_decay and beta must have shape %s" % (gshape,))
+    if z is not None and z.shape != v.shape:
+        raise GdnError(2, "z must have v's shape")
+    if (z is None) != (w is None):
+        raise GdnError(1, "z and w must be given together")
+    if w is not None and tuple(w.shape) != (Dv,):
+        raise GdnError(2, "w must have shape (%d,)" % Dv)
+    dev = q.device
+    if dev.type != "cuda":
+        raise GdnError(8, "operands must be on a GPU device")
+    tensors = dict(q=q, k=k, v=v, log_decay=log_decay, beta=beta, z=z, w=w, s0=s0)
+    for n, t in tensors.items():
+        if t is None:
+            continue
+        if t.device != dev:
+            raise GdnError(1, "%s is on %s, q on %s" % (n, t.device, dev))
+        if not t.is_contiguous():
+            raise GdnError(1, "%s must be contiguous" % n)
+    dt = _dtype_code(q, "q")
+    for n in ("k", "v", "z", "w"):
+        t = tensors[n]
+        if t is not None and _DT.get(t.dtype) != dt:
+            raise GdnError(3, "%s dtype %s differs from q's %s" % (n, t.dtype, q.dtype))
+    gdt = _dtype_code(log_decay, "log_decay")
+    if _DT.get(beta.dtype) != gdt:
+        raise GdnError(3, "beta dtype must equal log_decay dtype")
+    if s0 is not None:
+        if s0.dtype != torch.float32 or tuple(s0.shape) != (B, Hv, Dv, Dk):
+            raise GdnError(2, "s0 must be float32 [%d, %d, %d, %d]" % (B, Hv, Dv, Dk))
+    return B, T, Hk, Hv, Dk, Dv, dt, gdt
+
+
+def _call(fn_name, desc, q, k, v, log_decay, beta, s0, z, w, y, s_out):
+    L = _native.lib()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = getattr(L, fn_name)(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay),
+                                 _ptr(beta), _ptr(s0), _ptr(z), _ptr(w), _ptr(y), _ptr(s_out),
+                                 ctypes.c_void_p(stream))
+    if rc != 0:
+        reason = _native.last_error()
+        if rc == 8:
+            raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
+        raise GdnError(rc, reason)
+
+
+def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+         beta: torch.Tensor, s0: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+         w: Optional[torch.Tensor] = None, *, head_major: bool = False,
+         fold_qk_l2norm: bool = True, fold_q_scale: bool = True, qk_eps: float = 1e-6,
+         norm_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+         state_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gated DeltaNet recurrence over the time axis; returns (y, final_state).
+
+    q, k: [B, T, Hk, D] (head-major: [B, Hk, T, D]); v, z: [B, T, Hv, D]
+    ([B, Hv, T, D]); log_decay, beta: [B, T, Hv] ([B, Hv, T]); s0:
+    float32 [B, Hv, D, D] (None: zeros); w: [D].  y is float32 in v's layout;
+    final_state is float32 [B, Hv, D, D] (``state_out`` may be ``s0`` for an
+    in-place update)."""
+    B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
+    if s0 is None:
+        s0 = torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=q.device)
+    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    s_out = state_out if state_out is not None else torch.empty_like(s0)
+    desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
+                 qk_eps, norm_eps)
+    _call("gdn_scan", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
+    return y, s_out
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+                   beta: torch.Tensor, s0: torch.Tensor, z: Optional[torch.Tensor] = None,
+                   w: Optional[torch.Tensor] = None, *, head_major: bool = False,
+                   inplace: bool = False, fold_qk_l2norm: bool = True, fold_q_scale: bool = True,
+                   qk_eps: float = 1e-6, norm_eps: float = 1e-6,
+                   out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One decode step.  Operands carry T == 1 ([B, 1, H, D] etc., or the
+    head-major equivalent); ``inplace`` writes the new state into ``s0``."""
+    B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
+    if s0 is None:
+        raise GdnError(1, "recurrent_step needs s0")
+    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    s_out = s0 if inplace else torch.empty_like(s0)
+    desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
+                 qk_eps, norm_eps)
+    _call("gdn_recurrent_step", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
+    return y, s_out
+
+
+def check(desc: GdnDesc, q=None, k=None, v=None, log_decay=None, beta=None, s0=None, z=None,
+          w=None, y=None, s_out=None) -> Tuple[int, str]:
+    """Host-only validation (gdn_check) on raw integer addresses; returns (status, reason)."""
+    L = _native.lib()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    rc = L.gdn_check(ctypes.byref(desc), vp(q), vp(k), vp(v), vp(log_decay), vp(beta), vp(s0),
+                     vp(z), vp(w), vp(y), vp(s_out))
+    return rc, (_native.last_error() if rc else "")

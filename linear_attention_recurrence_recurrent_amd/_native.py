@@ -1,0 +1,67 @@
+"""ctypes view of libgdn_hip.so (the C ABI declared in include/gdn.h).
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels behind these symbols.  There is no fallback: if the library is not
+built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn_hip.so")
+
+GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
+GDN_FOLD_QK_L2NORM = 1
+GDN_FOLD_Q_SCALE = 2
+STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_ESHAPE", 3: "GDN_EDTYPE", 4: "GDN_EGROUP",
+          5: "GDN_EUNSUPPORTED", 6: "GDN_EALIGN", 7: "GDN_EALIAS", 8: "GDN_EDEVICE"}
+
+# Every symbol include/gdn.h declares.
+EXPORTS = ("gdn_recurrent_step", "gdn_scan", "gdn_check", "gdn_last_error", "gdn_status_str",
+           "gdn_abi_version")
+
+
+class GdnDesc(ctypes.Structure):
+    """Mirror of ``gdn_desc`` (same field order and C alignment)."""
+
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("Hk", ctypes.c_int64),
+                ("Hv", ctypes.c_int64), ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
+                ("head_major", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("gate_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("qk_eps", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libgdn_hip.so is not built (run `python -m "
+                "linear_attention_recurrence_recurrent_amd.build` or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        dp = ctypes.POINTER(GdnDesc)
+        for name in ("gdn_recurrent_step", "gdn_scan"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [dp] + [vp] * 11
+        L.gdn_check.restype = ctypes.c_int
+        L.gdn_check.argtypes = [dp] + [vp] * 10
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        L.gdn_status_str.restype = ctypes.c_char_p
+        L.gdn_status_str.argtypes = [ctypes.c_int]
+        L.gdn_abi_version.restype = ctypes.c_int
+        L.gdn_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().gdn_last_error().decode()

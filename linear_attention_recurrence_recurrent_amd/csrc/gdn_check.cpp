@@ -1,0 +1,160 @@
+// Host-side argument validation of the C ABI (pure C++, no HIP calls).
+//
+// The fused operator of the "gated_delta" page (native_gdn_reject_reason) has
+// hard constraints checked before anything runs, and a rejected call returns
+// a short reason for logging.  gdn_check is that check; gdn_scan and
+// gdn_recurrent_step run it before every launch.
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int64_t elem_size(int32_t dt) { return dt == GDN_F32 ? 4 : 2; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a == 0 || b == 0) {
+    *out = 0;
+    return true;
+  }
+  if (a > INT64_MAX / b) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+}  // namespace
+
+namespace gdn {
+
+void set_error(const char* msg) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+}
+
+int check(const gdn_desc* d, const void* q, const void* k, const void* v, const void* log_decay,
+          const void* beta, const float* s0, const void* z, const void* w, const float* y,
+          const float* s_out) {
+  g_last_error[0] = '\0';
+  if (!d) return fail(GDN_EINVAL, "null descriptor");
+  if (d->B < 0 || d->T < 0) return fail(GDN_ESHAPE, "negative B (%lld) or T (%lld)",
+                                        (long long)d->B, (long long)d->T);
+  if (d->Hk <= 0 || d->Hv <= 0 || d->Dk <= 0 || d->Dv <= 0)
+    return fail(GDN_ESHAPE, "Hk, Hv, Dk, Dv must be positive (got %lld, %lld, %lld, %lld)",
+                (long long)d->Hk, (long long)d->Hv, (long long)d->Dk, (long long)d->Dv);
+  if (d->Hv % d->Hk)
+    return fail(GDN_EGROUP, "Hv (%lld) is not a multiple of Hk (%lld)", (long long)d->Hv,
+                (long long)d->Hk);
+  if (d->dtype < GDN_F32 || d->dtype > GDN_BF16) return fail(GDN_EDTYPE, "bad dtype %d", d->dtype);
+  if (d->gate_dtype < GDN_F32 || d->gate_dtype > GDN_BF16)
+    return fail(GDN_EDTYPE, "bad gate_dtype %d", d->gate_dtype);
+  if (d->head_major != 0 && d->head_major != 1)
+    return fail(GDN_EINVAL, "head_major must be 0 or 1 (got %d)", d->head_major);
+  if (d->flags & ~(GDN_FOLD_QK_L2NORM | GDN_FOLD_Q_SCALE))
+    return fail(GDN_EINVAL, "unknown flag bits 0x%x", d->flags);
+  if (!(d->qk_eps >= 0.0f && d->qk_eps < 1e30f) || !(d->norm_eps >= 0.0f && d->norm_eps < 1e30f))
+    return fail(GDN_EINVAL, "eps must be finite and >= 0");
+  if (d->Dk != d->Dv)
+    return fail(GDN_EUNSUPPORTED, "kernels need Dk == Dv (got %lld, %lld)", (long long)d->Dk,
+                (long long)d->Dv);
+  if (d->Dk != 16 && d->Dk != 32 && d->Dk != 64 && d->Dk != 128)
+    return fail(GDN_EUNSUPPORTED, "head dim %lld not in {16, 32, 64, 128}", (long long)d->Dk);
+
+  // sizes in bytes (with overflow checks)
+  int64_t bt, nqk, nv, ng, ns, tmp;
+  if (!mul_ok(d->B, d->T, &bt) || !mul_ok(bt, d->Hk, &tmp) || !mul_ok(tmp, d->Dk, &nqk) ||
+      !mul_ok(bt, d->Hv, &ng) || !mul_ok(ng, d->Dv, &nv) || !mul_ok(d->B, d->Hv, &tmp) ||
+      !mul_ok(tmp, d->Dv * d->Dk, &ns) || nv > (INT64_MAX / 8) || ns > (INT64_MAX / 8) ||
+      nqk > (INT64_MAX / 8))
+    return fail(GDN_ESHAPE, "operand sizes overflow");
+  if (ng >= (int64_t)1 << 31 || nv >= (int64_t)1 << 40)
+    return fail(GDN_ESHAPE, "B*T*Hv (%lld) too large for the launch grid", (long long)ng);
+
+  const int64_t es = elem_size(d->dtype), ges = elem_size(d->gate_dtype);
+  const bool has_tokens = bt > 0;
+  const bool has_state = d->B > 0;
+  if ((z == nullptr) != (w == nullptr)) return fail(GDN_EINVAL, "z and w must be given together");
+  if (has_tokens && (!q || !k || !v || !log_decay || !beta || !y))
+    return fail(GDN_EINVAL, "null operand pointer");
+  if (has_state && (!s0 || !s_out)) return fail(GDN_EINVAL, "null state pointer");
+
+  auto al = [](const void* p, uintptr_t a) { return p == nullptr || (uintptr_t)p % a == 0; };
+  if (!al(q, 16) || !al(k, 16) || !al(v, 16) || !al(z, 16) || !al(y, 16) || !al(s0, 16) ||
+      !al(s_out, 16))
+    return fail(GDN_EALIGN, "q, k, v, z, y, s0, s_out must be 16-byte aligned");
+  if (!al(log_decay, (uintptr_t)ges) || !al(beta, (uintptr_t)ges) || !al(w, (uintptr_t)es))
+    return fail(GDN_EALIGN, "log_decay, beta, w must be aligned to their element size");
+
+  auto rng = [](const char* n, const void* p, int64_t bytes) {
+    return Range{n, (uintptr_t)p, p ? (uintptr_t)p + (uintptr_t)bytes : (uintptr_t)p};
+  };
+  const Range ins[] = {rng("q", q, nqk * es),          rng("k", k, nqk * es),
+                       rng("v", v, nv * es),           rng("z", z, z ? nv * es : 0),
+                       rng("w", w, w ? d->Dv * es : 0), rng("log_decay", log_decay, ng * ges),
+                       rng("beta", beta, ng * ges)};
+  const Range ry = rng("y", y, nv * 4);
+  const Range rs0 = rng("s0", s0, ns * 4);
+  const Range rso = rng("s_out", s_out, ns * 4);
+  for (const Range& r : ins) {
+    if (overlap(ry, r)) return fail(GDN_EALIAS, "y overlaps %s", r.name);
+    if (overlap(rso, r)) return fail(GDN_EALIAS, "s_out overlaps %s", r.name);
+  }
+  if (overlap(ry, rs0)) return fail(GDN_EALIAS, "y overlaps s0");
+  if (overlap(ry, rso)) return fail(GDN_EALIAS, "y overlaps s_out");
+  if (overlap(rso, rs0) && rso.lo != rs0.lo)
+    return fail(GDN_EALIAS, "s_out partially overlaps s0 (only s_out == s0 is allowed)");
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+int gdn_check(const gdn_desc* d, const void* q, const void* k, const void* v,
+              const void* log_decay, const void* beta, const float* s0, const void* z,
+              const void* w, const float* y, const float* s_out) {
+  return gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+}
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+const char* gdn_status_str(int status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_EINVAL: return "GDN_EINVAL";
+    case GDN_ESHAPE: return "GDN_ESHAPE";
+    case GDN_EDTYPE: return "GDN_EDTYPE";
+    case GDN_EGROUP: return "GDN_EGROUP";
+    case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED";
+    case GDN_EALIGN: return "GDN_EALIGN";
+    case GDN_EALIAS: return "GDN_EALIAS";
+    case GDN_EDEVICE: return "GDN_EDEVICE";
+    default: return "GDN_UNKNOWN";
+  }
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

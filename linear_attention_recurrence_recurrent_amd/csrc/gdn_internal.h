@@ -1,0 +1,16 @@
+// Internal declarations shared by the host-side validator and the HIP launchers.
+#pragma once
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Validation behind gdn_check (sets the thread's last error on failure).
+int check(const gdn_desc* d, const void* q, const void* k, const void* v, const void* log_decay,
+          const void* beta, const float* s0, const void* z, const void* w, const float* y,
+          const float* s_out);
+
+// Replace the thread's last-error text.
+void set_error(const char* msg);
+
+}  // namespace gdn

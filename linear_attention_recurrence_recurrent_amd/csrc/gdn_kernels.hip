@@ -1,0 +1,587 @@
+// Gated DeltaNet recurrence on MI355X (gfx950): decode step, time-axis scan
+// and gated RMSNorm kernels, plus the C-ABI entry points that launch them.
+//
+// Recurrence ("Module gdn" page, module description), per value head with a
+// D x D float32 memory S (row a = value lane, column c = key lane):
+//     u = S.k ;  S = alpha*S + beta*(v - alpha*u) k^T ;  o = S.q (updated S)
+//     y = rmsnorm(o * silu(z)) * w        (gate first, then normalise)
+// Fused row pass ("Module gdn" page, "The fusion"): because the update is
+// affine in S, o[a] = alpha*(S_old.q)[a] + coef[a]*(k.q) with
+// coef[a] = beta*(v[a] - alpha*u[a]).  One pass over a state row held in
+// registers yields both dots; the row is then rewritten from the same
+// registers, so each row is read once and written once per token.
+//
+// Work layout on CDNA4 (wave64):
+//   - a row of D columns is split over CL consecutive lanes ("row group");
+//     lane j of the group owns the float4 column chunks j, j+CL, j+2CL, ...,
+//     so a wave-wide float4 access of one chunk index touches CL contiguous
+//     16-byte pieces per row;
+//   - the two dots are reduced inside the row group with DPP butterflies
+//     (quad_perm, row_half_mirror, row_mirror), which leave the same sum in
+//     every lane of the group, so every lane updates its own columns with an
+//     identical coef;
+//   - a lane owns RPL rows, a wave 64/CL*RPL rows, a workgroup of NW waves
+//     ROWS = NW*(64/CL)*RPL rows of one value head.
+// Decode: a workgroup owns a whole head, streams its rows from HBM with
+// nontemporal loads/stores (all loads of a lane issued before any math), and
+// applies the gated RMSNorm in the same launch.
+// Scan: the state stays in VGPRs for the whole time axis; q/k/v/gates are
+// staged through LDS in chunks of TC tokens, q/k are normalised once per
+// token per workgroup, and the outputs of a chunk are buffered in LDS and
+// written back coalesced (gated in the same launch when the workgroup owns
+// the whole head, else by the separate gated-norm kernel).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ loads
+__device__ __forceinline__ float load1(const void* p, int64_t i, int dt) {
+  if (dt == GDN_F32) return static_cast<const float*>(p)[i];
+  const uint16_t h = static_cast<const uint16_t*>(p)[i];
+  if (dt == GDN_F16) return (float)__builtin_bit_cast(_Float16, h);
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Four consecutive elements starting at i (i is a multiple of 4 and the base
+// pointer is 16-byte aligned, so the access is 16 or 8 bytes aligned).
+__device__ __forceinline__ float4 load4(const void* p, int64_t i, int dt) {
+  if (dt == GDN_F32) return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  if (dt == GDN_F16) {
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    const half4_t h = __builtin_bit_cast(half4_t, r);
+    return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
+  }
+  return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+}
+
+__device__ __forceinline__ float dot4(const float4 a, const float4 b, float acc) {
+  acc = fmaf(a.x, b.x, acc);
+  acc = fmaf(a.y, b.y, acc);
+  acc = fmaf(a.z, b.z, acc);
+  return fmaf(a.w, b.w, acc);
+}
+
+__device__ __forceinline__ float4 scale4(const float4 a, float s) {
+  return make_float4(a.x * s, a.y * s, a.z * s, a.w * s);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Streaming (nontemporal) 16-byte state accesses: the state is touched once per
+// decode step, so it should not displace other lines from the caches.
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 nt_load4(const float* p) {
+  const v4f r = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ void nt_store4(const float4 s, float* p) {
+  const v4f r = {s.x, s.y, s.z, s.w};
+  __builtin_nontemporal_store(r, reinterpret_cast<v4f*>(p));
+}
+
+// ------------------------------------------------------------------ lane reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of CL consecutive lanes (CL = 1, 2, 4, 8, 16).
+// Butterfly order: every lane of a group ends with bit-identical sums.
+template <int CL>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(CL == 1 || CL == 2 || CL == 4 || CL == 8 || CL == 16, "row group size");
+  if constexpr (CL >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (CL >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (CL >= 8) x += dpp<0x141>(x);  // row_half_mirror: the other quad of 8
+  if constexpr (CL >= 16) x += dpp<0x140>(x); // row_mirror: the other half of 16
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
+// XCD receives a contiguous range of tiles (the row blocks of one head, and
+// the value heads of one key group, then share an L2).
+__device__ __forceinline__ int64_t xcd_tile(int64_t i, int64_t n) {
+  if (n % 8) return i;
+  return (i % 8) * (n / 8) + i / 8;
+}
+
+// ------------------------------------------------------------------ decode step
+struct StepArgs {
+  const void *q, *k, *v, *ld, *beta, *z, *w;
+  const float* s0;
+  float* y;
+  float* s_out;
+  int Hk, Hv, G, dt, gdt;
+  uint32_t flags;
+  float qk_eps, norm_eps, qscale;
+};
+
+template <int D, int CL, int RPL, int NW>
+__global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
+  constexpr int NCOL = D / CL, NV4 = NCOL / 4, RG = kWave / CL;
+  static_assert(NCOL % 4 == 0, "a lane owns whole float4 chunks");
+  static_assert(NW * RG * RPL == D, "a workgroup owns the whole head");
+  __shared__ float red[NW];
+
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int64_t b = tile / a.Hv;
+  const int hv = (int)(tile % a.Hv), hk = hv / a.G;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int g = lane / CL, j = lane % CL;
+  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(D * D);
+
+  // 1. issue every state load of this lane before any arithmetic
+  float4 S[RPL][NV4];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int row = (wave * RPL + r) * RG + g;
+#pragma unroll
+    for (int m = 0; m < NV4; ++m)
+      S[r][m] = nt_load4(a.s0 + sbase + row * D + 4 * (m * CL + j));
+  }
+
+  // 2. this lane's columns of q and k; the row group covers all D columns,
+  //    so the group sums are the full norms and k.q
+  const int64_t qk = (b * a.Hk + hk) * D;  // T == 1: both layouts coincide
+  float4 kc[NV4], qc[NV4];
+  float skk = 0.f, sqq = 0.f, skq = 0.f;
+#pragma unroll
+  for (int m = 0; m < NV4; ++m) {
+    kc[m] = load4(a.k, qk + 4 * (m * CL + j), a.dt);
+    qc[m] = load4(a.q, qk + 4 * (m * CL + j), a.dt);
+    skk = dot4(kc[m], kc[m], skk);
+    sqq = dot4(qc[m], qc[m], sqq);
+    skq = dot4(kc[m], qc[m], skq);
+  }
+  skk = group_sum<CL>(skk);
+  sqq = group_sum<CL>(sqq);
+  skq = group_sum<CL>(skq);
+  float rk = 1.f, rq = a.qscale;
+  if (a.flags & GDN_FOLD_QK_L2NORM) {
+    rk = rsqrtf(skk + a.qk_eps);
+    rq *= rsqrtf(sqq + a.qk_eps);
+  }
+  const float kq = skq * rk * rq;
+#pragma unroll
+  for (int m = 0; m < NV4; ++m) {
+    kc[m] = scale4(kc[m], rk);
+    qc[m] = scale4(qc[m], rq);
+  }
+  const int64_t gi = b * a.Hv + hv;
+  const float al = expf(load1(a.ld, gi, a.gdt));
+  const float be = load1(a.beta, gi, a.gdt);
+  const int64_t vbase = gi * D;
+
+  // 3. fused row pass: both dots from the registers, update, write back
+  float o[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int row = (wave * RPL + r) * RG + g;
+    float u0 = 0.f, u1 = 0.f, w0 = 0.f, w1 = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV4; ++m) {
+      if (m & 1) {
+        u1 = dot4(S[r][m], kc[m], u1);
+        w1 = dot4(S[r][m], qc[m], w1);
+      } else {
+        u0 = dot4(S[r][m], kc[m], u0);
+        w0 = dot4(S[r][m], qc[m], w0);
+      }
+    }
+    const float u = group_sum<CL>(u0 + u1);
+    const float wq = group_sum<CL>(w0 + w1);
+    const float coef = be * (load1(a.v, vbase + row, a.dt) - al * u);
+    o[r] = al * wq + coef * kq;
+#pragma unroll
+    for (int m = 0; m < NV4; ++m) {
+      float4 s = S[r][m];
+      s.x = fmaf(coef, kc[m].x, al * s.x);
+      s.y = fmaf(coef, kc[m].y, al * s.y);
+      s.z = fmaf(coef, kc[m].z, al * s.z);
+      s.w = fmaf(coef, kc[m].w, al * s.w);
+      nt_store4(s, a.s_out + sbase + row * D + 4 * (m * CL + j));
+    }
+  }
+
+  // 4. output: raw o, or the gated RMSNorm over the whole head
+  if (a.z == nullptr) {
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) a.y[vbase + (wave * RPL + r) * RG + g] = o[r];
+    }
+    return;
+  }
+  float x[RPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int row = (wave * RPL + r) * RG + g;
+    x[r] = o[r] * silu(load1(a.z, vbase + row, a.dt));
+    ss = fmaf(x[r], x[r], ss);
+  }
+  ss = wave_sum(j == 0 ? ss : 0.f);  // every lane of a group holds the same rows
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) tot += red[i];
+  const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
+  if (j == 0) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int row = (wave * RPL + r) * RG + g;
+      a.y[vbase + row] = x[r] * inv * load1(a.w, row, a.dt);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ scan
+struct ScanArgs {
+  const void *q, *k, *v, *ld, *beta, *z, *w;
+  const float* s0;
+  float* y;
+  float* s_out;
+  int64_t T;
+  int Hk, Hv, G, nrb, dt, gdt, head_major;
+  uint32_t flags;
+  float qk_eps, norm_eps, qscale;
+};
+
+template <int D, int CL, int RPL, int NW, int TC, bool FUSE_NORM>
+__global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
+  constexpr int NCOL = D / CL, NV4 = NCOL / 4, RG = kWave / CL, ROWS = NW * RG * RPL;
+  constexpr int NT = NW * kWave, D4 = D / 4;
+  static_assert(NCOL % 4 == 0, "a lane owns whole float4 chunks");
+  static_assert(D % ROWS == 0, "row blocks tile the head");
+  static_assert(!FUSE_NORM || ROWS == D, "the fused norm needs the whole head");
+  static_assert(D4 <= kWave, "one wave normalises one token");
+  __shared__ float4 sk[TC][D4];
+  __shared__ float4 sq[TC][D4];
+  __shared__ float sv[TC][ROWS];
+  __shared__ float so[TC][ROWS];
+  __shared__ float sal[TC], sbe[TC], skq[TC];
+
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int rb = (int)(tile % a.nrb);
+  const int64_t bh = tile / a.nrb;
+  const int hv = (int)(bh % a.Hv), hk = hv / a.G;
+  const int64_t b = bh / a.Hv;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int g = lane / CL, j = lane % CL;
+  const int64_t T = a.T;
+
+  // operand bases and per-token strides for the two layouts
+  int64_t qk_base, qk_ts, v_base, v_ts, g_base, g_ts;
+  if (a.head_major) {
+    qk_base = (b * a.Hk + hk) * T * D;
+    qk_ts = D;
+    v_base = (b * a.Hv + hv) * T * D;
+    v_ts = D;
+    g_base = (b * a.Hv + hv) * T;
+    g_ts = 1;
+  } else {
+    qk_base = (b * T * a.Hk + hk) * D;
+    qk_ts = (int64_t)a.Hk * D;
+    v_base = (b * T * a.Hv + hv) * D;
+    v_ts = (int64_t)a.Hv * D;
+    g_base = b * T * a.Hv + hv;
+    g_ts = a.Hv;
+  }
+  const int row0 = rb * ROWS;
+  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(D * D);
+
+  float4 S[RPL][NV4];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int row = row0 + (wave * RPL + r) * RG + g;
+#pragma unroll
+    for (int m = 0; m < NV4; ++m)
+      S[r][m] = *reinterpret_cast<const float4*>(a.s0 + sbase + row * D + 4 * (m * CL + j));
+  }
+
+  for (int64_t t0 = 0; t0 < T; t0 += TC) {
+    const int tc = (int)((T - t0) < TC ? (T - t0) : TC);
+
+    // A. stage this chunk's raw q, k, v and gates
+    for (int e = tid; e < tc * D4; e += NT) {
+      const int tt = e / D4, c4 = e % D4;
+      const int64_t off = qk_base + (t0 + tt) * qk_ts + 4 * c4;
+      sk[tt][c4] = load4(a.k, off, a.dt);
+      sq[tt][c4] = load4(a.q, off, a.dt);
+    }
+    for (int e = tid; e < tc * ROWS; e += NT) {
+      const int tt = e / ROWS, rr = e % ROWS;
+      sv[tt][rr] = load1(a.v, v_base + (t0 + tt) * v_ts + row0 + rr, a.dt);
+    }
+    for (int e = tid; e < tc; e += NT) {
+      const int64_t gi = g_base + (t0 + e) * g_ts;
+      sal[e] = expf(load1(a.ld, gi, a.gdt));
+      sbe[e] = load1(a.beta, gi, a.gdt);
+    }
+    __syncthreads();
+
+    // B. fold the L2 norms and the q scale, once per token
+    for (int tt = wave; tt < tc; tt += NW) {
+      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 kk = lane < D4 ? sk[tt][lane] : zero;
+      const float4 qq = lane < D4 ? sq[tt][lane] : zero;
+      const float skk = wave_sum(dot4(kk, kk, 0.f));
+      const float sqq = wave_sum(dot4(qq, qq, 0.f));
+      const float sqk = wave_sum(dot4(kk, qq, 0.f));
+      float rk = 1.f, rq = a.qscale;
+      if (a.flags & GDN_FOLD_QK_L2NORM) {
+        rk = rsqrtf(skk + a.qk_eps);
+        rq *= rsqrtf(sqq + a.qk_eps);
+      }
+      if (lane < D4) {
+        sk[tt][lane] = scale4(kk, rk);
+        sq[tt][lane] = scale4(qq, rq);
+      }
+      if (lane == 0) skq[tt] = sqk * rk * rq;
+    }
+    __syncthreads();
+
+    // C. the recurrence, token after token, state in registers
+    for (int tt = 0; tt < tc; ++tt) {
+      const float al = sal[tt], be = sbe[tt], kq = skq[tt];
+      float4 kc[NV4];
+      float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV4; ++m) {
+        kc[m] = sk[tt][m * CL + j];
+        const float4 qc = sq[tt][m * CL + j];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+          if (m & 1) {
+            u1[r] = dot4(S[r][m], kc[m], u1[r]);
+            w1[r] = dot4(S[r][m], qc, w1[r]);
+          } else {
+            u0[r] = dot4(S[r][m], kc[m], u0[r]);
+            w0[r] = dot4(S[r][m], qc, w0[r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const int lr = (wave * RPL + r) * RG + g;
+        const float u = group_sum<CL>(u0[r] + u1[r]);
+        const float wq = group_sum<CL>(w0[r] + w1[r]);
+        const float coef = be * (sv[tt][lr] - al * u);
+        const float o = al * wq + coef * kq;
+#pragma unroll
+        for (int m = 0; m < NV4; ++m) {
+          S[r][m].x = fmaf(coef, kc[m].x, al * S[r][m].x);
+          S[r][m].y = fmaf(coef, kc[m].y, al * S[r][m].y);
+          S[r][m].z = fmaf(coef, kc[m].z, al * S[r][m].z);
+          S[r][m].w = fmaf(coef, kc[m].w, al * S[r][m].w);
+        }
+        if (j == 0) so[tt][lr] = o;
+      }
+    }
+    __syncthreads();
+
+    // D. write this chunk's outputs (gated here when the workgroup owns the head)
+    bool written = false;
+    if constexpr (FUSE_NORM) {
+      if (a.z != nullptr) {
+        constexpr int EPL = (D + kWave - 1) / kWave;
+        for (int tt = wave; tt < tc; tt += NW) {
+          const int64_t vo = v_base + (t0 + tt) * v_ts;
+          float x[EPL];
+          float ss = 0.f;
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            const int rr = lane + kWave * i;
+            x[i] = 0.f;
+            if (rr < D) x[i] = so[tt][rr] * silu(load1(a.z, vo + rr, a.dt));
+            ss = fmaf(x[i], x[i], ss);
+          }
+          const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + a.norm_eps);
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            const int rr = lane + kWave * i;
+            if (rr < D) a.y[vo + rr] = x[i] * inv * load1(a.w, rr, a.dt);
+          }
+        }
+        written = true;
+      }
+    }
+    if (!written) {
+      for (int e = tid; e < tc * ROWS; e += NT) {
+        const int tt = e / ROWS, rr = e % ROWS;
+        a.y[v_base + (t0 + tt) * v_ts + row0 + rr] = so[tt][rr];
+      }
+    }
+    // The next chunk's staging writes sk/sq/sv/gates only; so[] is rewritten
+    // after two more barriers, so no barrier is needed here.
+  }
+
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int row = row0 + (wave * RPL + r) * RG + g;
+#pragma unroll
+    for (int m = 0; m < NV4; ++m)
+      *reinterpret_cast<float4*>(a.s_out + sbase + row * D + 4 * (m * CL + j)) = S[r][m];
+  }
+}
+
+// ------------------------------------------------------------------ gated RMSNorm
+// In place over y viewed as [nvec, D] (both layouts keep the head dim last and
+// dense, and z shares y's layout); one wave per head vector.
+template <int D>
+__global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z, const void* w,
+                                                         int dt, int64_t nvec, float eps) {
+  constexpr int EPL = (D + kWave - 1) / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t vec = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (vec >= nvec) return;  // uniform per wave
+  const int64_t base = vec * D;
+  float x[EPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int rr = lane + kWave * i;
+    x[i] = 0.f;
+    if (rr < D) x[i] = y[base + rr] * silu(load1(z, base + rr, dt));
+    ss = fmaf(x[i], x[i], ss);
+  }
+  const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + eps);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int rr = lane + kWave * i;
+    if (rr < D) y[base + rr] = x[i] * inv * load1(w, rr, dt);
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+int device_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return GDN_OK;
+  char msg[200];
+  std::snprintf(msg, sizeof(msg), "%s: %s", what, hipGetErrorString(e));
+  set_error(msg);
+  return GDN_EDEVICE;
+}
+
+float q_scale(const gdn_desc& d) {
+  return (d.flags & GDN_FOLD_Q_SCALE) ? 1.0f / std::sqrt((float)d.Dk) : 1.0f;
+}
+
+int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v,
+                const void* ld, const void* beta, const float* s0, const void* z, const void* w,
+                float* y, float* s_out, hipStream_t st) {
+  StepArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, (int)d.Hk, (int)d.Hv, (int)(d.Hv / d.Hk),
+             d.dtype, d.gate_dtype, d.flags, d.qk_eps, d.norm_eps, q_scale(d)};
+  const dim3 grid((unsigned)(d.B * d.Hv));
+  switch (d.Dk) {
+    case 128: decode_kernel<128, 8, 2, 8><<<grid, 8 * kWave, 0, st>>>(a); break;
+    case 64: decode_kernel<64, 4, 2, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
+    case 32: decode_kernel<32, 4, 1, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
+    case 16: decode_kernel<16, 4, 1, 1><<<grid, 1 * kWave, 0, st>>>(a); break;
+    default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
+  }
+  return device_status("decode_kernel launch");
+}
+
+template <int D, int CL, int RPL, int NW, int TC>
+int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
+  constexpr int ROWS = NW * (kWave / CL) * RPL;
+  a.nrb = D / ROWS;
+  const dim3 grid((unsigned)(heads * a.nrb));
+  if constexpr (ROWS == D) {
+    scan_kernel<D, CL, RPL, NW, TC, true><<<grid, NW * kWave, 0, st>>>(a);
+    return device_status("scan_kernel launch");
+  } else {
+    scan_kernel<D, CL, RPL, NW, TC, false><<<grid, NW * kWave, 0, st>>>(a);
+    int rc = device_status("scan_kernel launch");
+    if (rc != GDN_OK || a.z == nullptr) return rc;
+    const int64_t nvec = heads * a.T;
+    gated_norm_kernel<D><<<dim3((unsigned)((nvec + 3) / 4)), 256, 0, st>>>(
+        a.y, a.z, a.w, a.dt, nvec, a.norm_eps);
+    return device_status("gated_norm_kernel launch");
+  }
+}
+
+int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
+                const void* beta, const float* s0, const void* z, const void* w, float* y,
+                float* s_out, hipStream_t st) {
+  ScanArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, d.T, (int)d.Hk, (int)d.Hv,
+             (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags, d.qk_eps,
+             d.norm_eps, q_scale(d)};
+  const int64_t heads = d.B * d.Hv;
+  switch (d.Dk) {
+    case 128:
+      // enough heads to fill the chip with whole-head workgroups: keep the
+      // norm fused; otherwise split each head's rows over more workgroups
+      if (heads >= 512) return launch_scan_cfg<128, 4, 2, 4, 16>(a, heads, st);
+      if (heads >= 128) return launch_scan_cfg<128, 8, 1, 4, 16>(a, heads, st);
+      return launch_scan_cfg<128, 16, 1, 4, 16>(a, heads, st);
+    case 64:
+      if (heads >= 256) return launch_scan_cfg<64, 4, 1, 4, 32>(a, heads, st);
+      return launch_scan_cfg<64, 8, 1, 2, 32>(a, heads, st);
+    case 32: return launch_scan_cfg<32, 4, 1, 2, 32>(a, heads, st);
+    case 16: return launch_scan_cfg<16, 4, 1, 1, 32>(a, heads, st);
+    default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
+  }
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" {
+
+int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const void* v,
+                       const void* log_decay, const void* beta, const float* s0, const void* z,
+                       const void* w, float* y, float* s_out, void* stream) {
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+  if (rc != GDN_OK) return rc;
+  if (d->T != 1) {
+    gdn::set_error("gdn_recurrent_step needs T == 1 (use gdn_scan for a time axis)");
+    return GDN_EUNSUPPORTED;
+  }
+  if (d->B == 0) return GDN_OK;
+  return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out,
+                          static_cast<hipStream_t>(stream));
+}
+
+int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
+             const void* log_decay, const void* beta, const float* s0, const void* z,
+             const void* w, float* y, float* s_out, void* stream) {
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+  if (rc != GDN_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d->B == 0) return GDN_OK;
+  if (d->T == 0) {
+    if (s_out == s0) return GDN_OK;
+    const size_t bytes = (size_t)(d->B * d->Hv * d->Dv * d->Dk) * sizeof(float);
+    if (hipMemcpyAsync(s_out, s0, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return gdn::device_status("state copy for T == 0");
+    return GDN_OK;
+  }
+  if (d->T == 1)  // one token: the decode kernel is the same computation, streamed once
+    return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, st);
+  return gdn::launch_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, st);
+}
+
+}  // extern "C"

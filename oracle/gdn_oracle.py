@@ -173,7 +173,7 @@ def select_heads(ops: dict, heads, *, head_major: bool) -> dict:
             if head_major:
                 parts.append(a[b:b + 1, h:h + 1])
             else:
-                parts.append(a[b:b + 1, :, h:h + 1] if a.ndim >= 3 else a[b:b + 1, :, h:h + 1])
+                parts.append(a[b:b + 1, :, h:h + 1])
         out[name] = np.concatenate(parts, axis=0)
     s0 = _f64(ops["s0"])
     out["s0"] = np.concatenate([s0[b:b + 1, hv:hv + 1] for (b, hv) in heads], axis=0)

@@ -1,0 +1,205 @@
+"""Host-side tests of the C ABI: the library loads, exports what include/gdn.h
+declares, agrees with the header on the descriptor layout, and rejects bad
+arguments with a status and a short reason (no device work, no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_recurrence_recurrent_amd import _native as nat
+from linear_attention_recurrence_recurrent_amd import GdnDesc, abi_version, check
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = nat.lib()
+    names = _declared_functions()
+    assert set(names) == set(nat.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", nat.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert re.search(r"\bT %s$" % n, out, flags=re.M), n
+
+
+def test_abi_version_and_status_names():
+    assert abi_version() == 1
+    L = nat.lib()
+    for code, name in nat.STATUS.items():
+        assert L.gdn_status_str(code).decode() == name
+
+
+def test_descriptor_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stddef.h>
+#include <stdio.h>
+#include "gdn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(gdn_desc), offsetof(gdn_desc, head_major),
+         offsetof(gdn_desc, dtype), offsetof(gdn_desc, flags), offsetof(gdn_desc, qk_eps),
+         offsetof(gdn_desc, norm_eps));
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                           str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(GdnDesc), GdnDesc.head_major.offset, GdnDesc.dtype.offset,
+            GdnDesc.flags.offset, GdnDesc.qk_eps.offset, GdnDesc.norm_eps.offset]
+    assert got == want
+
+
+# Fake, well-separated, 256-byte aligned addresses: gdn_check never dereferences them.
+BASE = 1 << 32
+
+
+def _addrs(n=10, gap=1 << 28):
+    return [BASE + i * gap for i in range(n)]
+
+
+def _good(**kw):
+    d = dict(B=2, T=8, Hk=2, Hv=4, Dk=64, Dv=64, head_major=0, dtype=2, gate_dtype=2, flags=3,
+             qk_eps=1e-6, norm_eps=1e-6)
+    d.update(kw)
+    return GdnDesc(**d)
+
+
+def _ops(z=True):
+    q, k, v, g, b, s0, zz, w, y, so = _addrs()
+    return dict(q=q, k=k, v=v, log_decay=g, beta=b, s0=s0, z=zz if z else None,
+                w=w if z else None, y=y, s_out=so)
+
+
+def test_accepts_valid_arguments():
+    assert check(_good(), **_ops())[0] == 0
+    assert check(_good(), **_ops(z=False))[0] == 0
+    ops = _ops()
+    ops["s_out"] = ops["s0"]  # exact in-place alias is allowed
+    assert check(_good(), **ops)[0] == 0
+    assert check(_good(head_major=1, dtype=0, gate_dtype=0, flags=0), **ops)[0] == 0
+    for D in (16, 32, 64, 128):
+        assert check(_good(Dk=D, Dv=D), **_ops())[0] == 0
+    # empty batch or empty time axis
+    assert check(_good(T=0), **_ops())[0] == 0
+    ops = _ops()
+    for n in ("q", "k", "v", "log_decay", "beta", "y", "z", "w"):
+        ops[n] = None
+    assert check(_good(T=0), **ops)[0] == 0
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("Hv", 3, 4, "multiple"),
+    ("Hk", 0, 2, "positive"),
+    ("B", -1, 2, "negative"),
+    ("T", -2, 2, "negative"),
+    ("Dk", 48, 5, "Dk == Dv"),
+    ("Dv", 48, 5, "Dk == Dv"),
+    ("dtype", 7, 3, "dtype"),
+    ("gate_dtype", -1, 3, "gate_dtype"),
+    ("flags", 8, 1, "flag"),
+    ("head_major", 2, 1, "head_major"),
+    ("qk_eps", -1.0, 1, "eps"),
+    ("norm_eps", float("inf"), 1, "eps"),
+])
+def test_rejects_bad_descriptor(field, value, status, needle):
+    kw = {field: value}
+    rc, why = check(_good(**kw), **_ops())
+    assert rc == status and needle in why, (rc, why)
+
+
+def test_rejects_unsupported_head_dim():
+    rc, why = check(_good(Dk=256, Dv=256), **_ops())
+    assert rc == 5 and "head dim" in why
+    rc, why = check(_good(Dk=8, Dv=8), **_ops())
+    assert rc == 5
+
+
+def test_rejects_null_and_half_gate_pair():
+    L = nat.lib()
+    assert L.gdn_check(None, *([None] * 10)) == 1
+    assert "null descriptor" in nat.last_error()
+    ops = _ops()
+    ops["q"] = None
+    rc, why = check(_good(), **ops)
+    assert rc == 1 and "null" in why
+    ops = _ops()
+    ops["w"] = None
+    rc, why = check(_good(), **ops)
+    assert rc == 1 and "together" in why
+    ops = _ops()
+    ops["s0"] = None
+    assert check(_good(T=0), **ops)[0] == 1
+
+
+def test_rejects_misalignment():
+    ops = _ops()
+    ops["v"] += 8
+    rc, why = check(_good(), **ops)
+    assert rc == 6 and "aligned" in why
+    ops = _ops()
+    ops["beta"] += 1
+    assert check(_good(), **ops)[0] == 6
+
+
+def test_rejects_overlaps():
+    ops = _ops()
+    ops["y"] = ops["v"] + 256  # y inside v
+    rc, why = check(_good(), **ops)
+    assert rc == 7 and "y overlaps v" in why
+    ops = _ops()
+    ops["s_out"] = ops["s0"] + 256  # partial overlap of the state buffers
+    rc, why = check(_good(), **ops)
+    assert rc == 7 and "partially" in why
+    ops = _ops()
+    ops["s_out"] = ops["q"]
+    assert check(_good(), **ops)[0] == 7
+    ops = _ops()
+    ops["y"] = ops["s0"]
+    assert check(_good(), **ops)[0] == 7
+
+
+def test_rejects_size_overflow():
+    rc, why = check(_good(B=1 << 40, T=1 << 30), **_ops())
+    assert rc == 2
+
+
+def test_step_needs_one_token_and_no_device_work_on_reject():
+    L = nat.lib()
+    ops = _ops()
+    d = _good(T=2)
+    args = [ctypes.c_void_p(ops[n]) if ops[n] else None for n in
+            ("q", "k", "v", "log_decay", "beta", "s0", "z", "w", "y", "s_out")]
+    rc = L.gdn_recurrent_step(ctypes.byref(d), *args, None)
+    assert rc == 5 and "T == 1" in nat.last_error()
+    # a descriptor rejected by validation returns before any HIP call
+    d = _good(Hv=3)
+    assert L.gdn_scan(ctypes.byref(d), *args, None) == 4
+
+
+def test_last_error_is_per_thread():
+    import threading
+    L = nat.lib()
+    check(_good(Hv=3), **_ops())
+    seen = []
+
+    def other():
+        seen.append(L.gdn_last_error().decode())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert "multiple" in nat.last_error()

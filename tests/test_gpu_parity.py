@@ -1,0 +1,290 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Bar: |gpu - ref| <= tol * (1 + |ref|) element by element, with tol = 1e-4 for
+float32 operands and 3e-3 for float16/bfloat16 operands (float32 state in both
+cases), applied to y AND the final state.  Small cases are compared in full;
+the full-size workloads compare every output of a sample of heads, which the
+oracle computes one by one (heads are independent through the recurrence).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_recurrence_recurrent_amd import GdnError, recurrent_step, scan, synth
+from oracle import gdn_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "f16": 3e-3, "bf16": 3e-3}
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(ops):
+    return {n: t.to(DEV) for n, t in ops.items()}
+
+
+def assert_close(got, ref, tol, what):
+    got = got.detach().double().cpu().numpy() if hasattr(got, "detach") else np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = np.abs(got - ref) / (1.0 + np.abs(ref))
+    worst = float(err.max()) if err.size else 0.0
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    assert worst <= tol, "%s: max |gpu-ref|/(1+|ref|) = %.3e > %.1e at %s" % (
+        what, worst, tol, np.unravel_index(int(err.argmax()), err.shape))
+
+
+def run_both(ops, *, head_major, gated, dtype, **kw):
+    d = dev(ops)
+    z, w = (d.get("z"), d.get("w")) if gated else (None, None)
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], z, w,
+                head_major=head_major, **kw)
+    torch.cuda.synchronize()
+    yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                      ops.get("z") if gated else None, ops.get("w") if gated else None,
+                      head_major=head_major, **kw)
+    tol = TOL[dtype]
+    assert y.dtype == torch.float32 and s.dtype == torch.float32
+    assert_close(y, yr, tol, "y")
+    assert_close(s, sr, tol, "final_state")
+    return y, s
+
+
+# ------------------------------------------------------------------ configs 0 and 1 in full
+@pytest.mark.parametrize("gated", [True, False])
+def test_config0_tiny_scan_f32(gated):
+    w = synth.WORKLOADS[0]
+    say("config0 gated=%s" % gated)
+    run_both(synth.make(w), head_major=False, gated=gated, dtype="f32")
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_config1_decode_step_bf16(gated):
+    wl = synth.WORKLOADS[1]
+    say("config1 gated=%s" % gated)
+    ops = synth.make(wl)
+    d = dev(ops)
+    z, w = (d["z"], d["w"]) if gated else (None, None)
+    y, s = recurrent_step(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], z, w)
+    torch.cuda.synchronize()
+    yr, sr = orc.step(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                      ops["z"] if gated else None, ops["w"] if gated else None)
+    assert_close(y, yr, TOL["bf16"], "y")
+    assert_close(s, sr, TOL["bf16"], "state")
+
+
+# ------------------------------------------------------------------ small cases spanning tiles
+SMALL = [
+    # (B, T, Hk, Hv, D, dtype, head_major)
+    (1, 37, 2, 4, 128, "bf16", False),   # narrow row split, ragged chunk tail
+    (4, 19, 16, 32, 128, "f16", True),   # 128 heads: mid row split
+    (16, 5, 8, 32, 128, "f32", False),   # 512 heads: whole-head workgroups, fused norm
+    (2, 50, 3, 6, 64, "bf16", True),     # D=64 row split, G=2
+    (8, 33, 16, 32, 64, "f32", False),   # D=64 whole-head
+    (3, 65, 2, 6, 32, "f16", False),     # D=32, G=3
+    (2, 70, 1, 3, 16, "f32", True),      # D=16, G=3
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dT%dHk%dHv%dD%d-%s-%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "hm" if c[6] else "tm"))
+@pytest.mark.parametrize("gated", [True, False])
+def test_small_cases(case, gated):
+    B, T, Hk, Hv, D, dtype, hm = case
+    say("small %s gated=%s" % (case, gated))
+    ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm, seed=B * 131 + T)
+    run_both(ops, head_major=hm, gated=gated, dtype=dtype)
+
+
+def test_gate_dtype_differs_from_operand_dtype():
+    ops = synth.random_operands(2, 21, 2, 4, 64, 64, dtype="bf16", gate_dtype="f32", seed=5)
+    run_both(ops, head_major=False, gated=True, dtype="bf16")
+
+
+@pytest.mark.parametrize("flags", [(False, False), (True, False), (False, True)])
+def test_fold_flags(flags):
+    fq, fs = flags
+    ops = synth.random_operands(1, 9, 2, 4, 64, 64, dtype="f32", seed=7)
+    if not fq:  # unnormalised keys make the recurrence unstable: feed unit-scale rows
+        for n in ("q", "k"):
+            ops[n] = ops[n] / ops[n].norm(dim=-1, keepdim=True)
+    run_both(ops, head_major=False, gated=False, dtype="f32", fold_qk_l2norm=fq, fold_q_scale=fs)
+
+
+def test_step_on_small_shapes_and_dims():
+    for D in (16, 32, 64, 128):
+        for hm in (False, True):
+            ops = synth.random_operands(3, 1, 2, 4, D, D, dtype="f16", head_major=hm, seed=D)
+            d = dev(ops)
+            y, s = recurrent_step(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
+                                  d["z"], d["w"], head_major=hm)
+            torch.cuda.synchronize()
+            yr, sr = orc.step(**ops, head_major=hm)
+            assert_close(y, yr, TOL["f16"], "y D=%d" % D)
+            assert_close(s, sr, TOL["f16"], "state D=%d" % D)
+
+
+# ------------------------------------------------------------------ edge cases
+def test_empty_time_axis_and_empty_batch():
+    ops = dev(synth.random_operands(2, 0, 2, 4, 64, 64, dtype="bf16", seed=1))
+    y, s = scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                ops["z"], ops["w"])
+    torch.cuda.synchronize()
+    assert y.shape[1] == 0
+    assert torch.equal(s, ops["s0"])
+    ops = dev(synth.random_operands(0, 4, 2, 4, 64, 64, dtype="bf16", seed=1))
+    y, s = scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"])
+    assert y.numel() == 0 and s.numel() == 0
+
+
+def test_degenerate_gates_and_zero_vectors():
+    ops = synth.random_operands(2, 12, 2, 4, 128, 128, dtype="f32", seed=3)
+    ops["log_decay"][:, 3] = -math.inf   # alpha = 0: the memory restarts at beta v k^T
+    ops["beta"][:, 5] = 0.0              # beta = 0: decay only
+    ops["log_decay"][:, 6] = 0.0         # alpha = 1
+    ops["q"][0, 7] = 0.0                 # zero q and k normalise to zero
+    ops["k"][1, 8] = 0.0
+    ops["z"][0, 9] = 0.0                 # z = 0 gives y = 0 exactly
+    y, s = run_both(ops, head_major=False, gated=True, dtype="f32")
+    assert torch.all(y[0, 9] == 0)
+
+
+def test_in_place_state_and_time_chaining():
+    ops = synth.random_operands(2, 40, 2, 4, 128, 128, dtype="bf16", seed=9)
+    d = dev(ops)
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"])
+    st = d["s0"].clone()
+    parts = []
+    for a, b in ((0, 13), (13, 14), (14, 40)):  # includes a single-token piece
+        sl = {n: d[n][:, a:b].contiguous() for n in ("q", "k", "v", "z", "log_decay", "beta")}
+        yp, st2 = scan(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["beta"], st, sl["z"],
+                       d["w"], state_out=st)
+        assert st2.data_ptr() == st.data_ptr()
+        parts.append(yp)
+    torch.cuda.synchronize()
+    ych = torch.cat(parts, dim=1)
+    assert_close(ych, y.double().cpu().numpy(), 1e-5, "chained y")
+    assert_close(st, s.double().cpu().numpy(), 1e-5, "chained state")
+
+
+def test_steps_equal_scan():
+    ops = synth.random_operands(3, 10, 2, 6, 64, 64, dtype="f16", seed=11)
+    d = dev(ops)
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"])
+    st = d["s0"].clone()
+    ys = []
+    for t in range(10):
+        sl = {n: d[n][:, t:t + 1].contiguous() for n in ("q", "k", "v", "z", "log_decay", "beta")}
+        yt, st = recurrent_step(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["beta"], st,
+                                sl["z"], d["w"], inplace=True)
+        ys.append(yt)
+    torch.cuda.synchronize()
+    assert_close(torch.cat(ys, dim=1), y.double().cpu().numpy(), 1e-5, "steps y")
+    assert_close(st, s.double().cpu().numpy(), 1e-5, "steps state")
+
+
+def test_head_major_equals_token_major_bitwise():
+    ops = synth.random_operands(2, 33, 2, 4, 128, 128, dtype="bf16", seed=12)
+    d = dev(ops)
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"])
+    t4 = lambda x: x.transpose(1, 2).contiguous()  # noqa: E731
+    yh, sh = scan(t4(d["q"]), t4(d["k"]), t4(d["v"]), t4(d["log_decay"]), t4(d["beta"]),
+                  d["s0"], t4(d["z"]), d["w"], head_major=True)
+    torch.cuda.synchronize()
+    assert torch.equal(yh.transpose(1, 2), y)
+    assert torch.equal(sh, s)
+
+
+def test_bitwise_deterministic():
+    for (B, T, Hk, Hv) in ((1, 30, 16, 32), (16, 7, 16, 32)):
+        ops = dev(synth.random_operands(B, T, Hk, Hv, 128, 128, dtype="bf16", seed=13))
+        a = scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                 ops["z"], ops["w"])
+        b = scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                 ops["z"], ops["w"])
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_rejections_raise():
+    ops = dev(synth.random_operands(1, 4, 2, 4, 64, 64, dtype="bf16", seed=1))
+    with pytest.raises(GdnError, match="together"):
+        scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"], ops["z"],
+             None)
+    big = torch.empty(ops["s0"].numel() + 64, dtype=torch.float32, device=DEV)
+    s0 = big[:ops["s0"].numel()].view_as(ops["s0"]).copy_(ops["s0"])
+    s_out = big[64:].view_as(ops["s0"])
+    with pytest.raises(GdnError, match="EALIAS"):
+        scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], s0, state_out=s_out)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled heads
+def _sample_heads(B, Hv, n, seed):
+    r = np.random.default_rng(seed)
+    pairs = [(0, 0), (B - 1, Hv - 1)]
+    while len(pairs) < n:
+        p = (int(r.integers(B)), int(r.integers(Hv)))
+        if p not in pairs:
+            pairs.append(p)
+    return pairs
+
+
+def _check_heads(y, s, ops, heads, head_major, tol, what):
+    sel = orc.select_heads(ops, heads, head_major=head_major)
+    yr, sr = orc.scan(sel["q"], sel["k"], sel["v"], sel["log_decay"], sel["beta"], sel["s0"],
+                      sel.get("z"), sel.get("w"), head_major=head_major)
+    for i, (b, hv) in enumerate(heads):
+        yg = y[b, hv] if head_major else y[b, :, hv]
+        yo = yr[i, 0] if head_major else yr[i, :, 0]
+        assert_close(yg, yo, tol, "%s y head (%d,%d)" % (what, b, hv))
+        assert_close(s[b, hv], sr[i, 0], tol, "%s state head (%d,%d)" % (what, b, hv))
+
+
+def test_config2_chained_decode_sampled():
+    wl = synth.WORKLOADS[2]
+    say("config2: 100 chained in-place decode steps, B=64")
+    ops = synth.make(wl)
+    steps = synth.step_slices(ops, head_major=False)
+    d_steps = [dev(st) for st in steps]
+    wd = ops["w"].to(DEV)
+    state = ops["s0"].to(DEV).clone()
+    ys = []
+    for st in d_steps:
+        y, _ = recurrent_step(st["q"], st["k"], st["v"], st["log_decay"], st["beta"], state,
+                              st["z"], wd, inplace=True)
+        ys.append(y)
+    torch.cuda.synchronize()
+    yall = torch.cat(ys, dim=1).cpu()  # [B, 100, Hv, D]
+    heads = _sample_heads(wl.B, wl.Hv, 12, 2)
+    _check_heads(yall, state.cpu(), ops, heads, False, TOL["bf16"], "config2")
+
+
+def test_config3_prefill_scan_sampled():
+    wl = synth.WORKLOADS[3]
+    say("config3: B=1 T=4096 token-major scan")
+    ops = synth.make(wl)
+    d = dev(ops)
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"])
+    torch.cuda.synchronize()
+    heads = _sample_heads(wl.B, wl.Hv, 6, 3)
+    _check_heads(y.cpu(), s.cpu(), ops, heads, False, TOL["bf16"], "config3")
+
+
+def test_config4_head_major_scan_sampled():
+    wl = synth.WORKLOADS[4]
+    say("config4: B=16 T=1024 head-major f16 scan")
+    ops = synth.make(wl)
+    d = dev(ops)
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"],
+                head_major=True)
+    torch.cuda.synchronize()
+    heads = _sample_heads(wl.B, wl.Hv, 10, 4)
+    _check_heads(y.cpu(), s.cpu(), ops, heads, True, TOL["f16"], "config4")
