@@ -185,7 +185,7 @@ def cpu_baseline(ops, args):
     sl = {k: (v[:, :n] if k not in ("s0", "w") else v) for k, v in ops.items()}
     f64 = {k: np.ascontiguousarray(v.double().numpy()) for k, v in sl.items()}
     threads = orc.default_threads()
-    orc.scan(**{k: (v[:1, :1] if k not in ("w",) else v) for k, v in f64.items()})  # load/build
+    orc._load()  # build/load outside the timed region
     t0 = time.perf_counter()
     orc.scan(**f64, threads=threads)
     dt = time.perf_counter() - t0
@@ -197,6 +197,18 @@ def cpu_baseline(ops, args):
                       "100 chained steps (%.1f s)" % (n, dt)}
 
 
+def copy_reference(args, torch):
+    """A plain copy kernel of known size: its FETCH_SIZE/WRITE_SIZE readings give the
+    factor that turns those counters into bytes."""
+    n = args.copy_ref_mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(max(1, args.steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes_each_way": n * 4, "launches": max(1, args.steps)}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +217,8 @@ def main():
     ap.add_argument("--no-scan", action="store_true", help="skip the scan sub-measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=10)
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this size (counter reference)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (each (batch, "
@@ -215,6 +229,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_ref_mib:
+        copy_reference(args, torch)
+        return
     import linear_attention_recurrence_recurrent_amd  # noqa: F401  (fails loudly if unbuilt)
     dec, ops = bench_decode(args, torch)
     scan = {}

@@ -95,7 +95,8 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
   const int64_t es = elem_size(d->dtype), ges = elem_size(d->gate_dtype);
   const bool has_tokens = bt > 0;
   const bool has_state = d->B > 0;
-  if ((z == nullptr) != (w == nullptr)) return fail(GDN_EINVAL, "z and w must be given together");
+  if (has_tokens && (z == nullptr) != (w == nullptr))
+    return fail(GDN_EINVAL, "z and w must be given together");
   if (has_tokens && (!q || !k || !v || !log_decay || !beta || !y))
     return fail(GDN_EINVAL, "null operand pointer");
   if (has_state && (!s0 || !s_out)) return fail(GDN_EINVAL, "null state pointer");
