@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 #include <cstdint>
 #include <cstdio>
 
@@ -52,18 +53,32 @@ __device__ __forceinline__ float load1(const void* p, int64_t i, int dt) {
   return __uint_as_float((uint32_t)h << 16);
 }
 
-// Four consecutive elements starting at i (i is a multiple of 4 and the base
+// Compile-time dtype versions for the operand loads of the kernels.  ld4 reads
+// four consecutive elements starting at i (i is a multiple of 4 and the base
 // pointer is 16-byte aligned, so the access is 16 or 8 bytes aligned).
-__device__ __forceinline__ float4 load4(const void* p, int64_t i, int dt) {
-  if (dt == GDN_F32) return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-  const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
-  if (dt == GDN_F16) {
-    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-    const half4_t h = __builtin_bit_cast(half4_t, r);
-    return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
+template <int DT>
+__device__ __forceinline__ float ld1(const void* p, int64_t i) {
+  if constexpr (DT == GDN_F32) return static_cast<const float*>(p)[i];
+  const uint16_t h = static_cast<const uint16_t*>(p)[i];
+  if constexpr (DT == GDN_F16) return (float)__builtin_bit_cast(_Float16, h);
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
+  if constexpr (DT == GDN_F32) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  } else {
+    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    if constexpr (DT == GDN_F16) {
+      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+      const half4_t h = __builtin_bit_cast(half4_t, r);
+      return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
+    } else {
+      return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                         __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
   }
-  return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
 }
 
 __device__ __forceinline__ float dot4(const float4 a, const float4 b, float acc) {
@@ -135,42 +150,124 @@ struct StepArgs {
   float qk_eps, norm_eps, qscale;
 };
 
-template <int D, int CL, int RPL, int NW>
-__global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
-  constexpr int NCOL = D / CL, NV4 = NCOL / 4, RG = kWave / CL;
-  static_assert(NCOL % 4 == 0, "a lane owns whole float4 chunks");
-  static_assert(NW * RG * RPL == D, "a workgroup owns the whole head");
-  __shared__ float red[NW];
+// N consecutive operand elements kept as their raw bits (16-bit dtypes stay
+// packed two per VGPR) and widened to f32 on use.  N = 1, 2 or 4; the access
+// is N elements wide, so the element index must be a multiple of N.
+template <int DT, int N>
+struct Raw {
+  static_assert(N == 1 || N == 2 || N == 4, "Raw holds 1, 2 or 4 elements");
+  static constexpr bool kF32 = DT == GDN_F32;
+  typedef typename std::conditional<kF32, float, uint32_t>::type Word;
+  static constexpr int kWords = kF32 ? N : (N + 1) / 2;
+  Word w[kWords];
+  __device__ __forceinline__ void load(const void* p, int64_t i) {
+    if constexpr (kF32) {
+      const float* f = static_cast<const float*>(p) + i;
+      if constexpr (N == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(f);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+      } else if constexpr (N == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(f);
+        w[0] = t.x; w[1] = t.y;
+      } else {
+        w[0] = f[0];
+      }
+    } else {
+      const uint16_t* h = static_cast<const uint16_t*>(p) + i;
+      if constexpr (N == 4) {
+        const uint2 t = *reinterpret_cast<const uint2*>(h);
+        w[0] = t.x; w[1] = t.y;
+      } else if constexpr (N == 2) {
+        w[0] = *reinterpret_cast<const uint32_t*>(h);
+      } else {
+        w[0] = h[0];
+      }
+    }
+  }
+  __device__ __forceinline__ float get(int k) const {
+    if constexpr (kF32) {
+      return w[k];
+    } else if constexpr (DT == GDN_BF16) {
+      return __uint_as_float((k & 1) ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
+    } else {
+      const uint16_t bits = (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
+      return (float)__builtin_bit_cast(_Float16, bits);
+    }
+  }
+  __device__ __forceinline__ float4 get4(int c) const {  // elements 4c .. 4c+3
+    return make_float4(get(4 * c), get(4 * c + 1), get(4 * c + 2), get(4 * c + 3));
+  }
+};
 
-  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t b = tile / a.Hv;
-  const int hv = (int)(tile % a.Hv), hk = hv / a.G;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int g = lane / CL, j = lane % CL;
-  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(D * D);
-
-  // 1. issue every state load of this lane before any arithmetic
+// Registers of one head in flight: this lane's columns of q and k (raw), its
+// RPL state rows (adjacent rows, float4 chunks), and its rows' v and z (raw).
+template <int DT, int D, int CL, int RPL>
+struct HeadRegs {
+  static constexpr int NV4 = D / CL / 4;
+  Raw<DT, 4> k[NV4], q[NV4];
   float4 S[RPL][NV4];
+  Raw<DT, RPL> v, z;
+  float ld, be;
+};
+
+// Lane layout of the decode: row group g of a wave owns rows
+// (wave*RG + g)*RPL ... +RPL-1; lane j of the group owns float4 chunks j, j+CL, ...
+template <int CL, int RPL>
+__device__ __forceinline__ int decode_row0() {
+  constexpr int RG = kWave / CL;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  return (wave * RG + lane / CL) * RPL;
+}
+
+// Issue every load of one head.  The small operands go first: loads complete
+// in issue order, so the q/k norms can start while the state is in flight.
+template <int DT, int GT, int D, int CL, int RPL, int NW>
+__device__ __forceinline__ void decode_fetch(const StepArgs& a, int64_t head,
+                                             HeadRegs<DT, D, CL, RPL>& R) {
+  constexpr int NV4 = D / CL / 4;
+  const int j = threadIdx.x % CL;
+  const int row0 = decode_row0<CL, RPL>();
+  const int64_t b = head / a.Hv;
+  const int hv = (int)(head % a.Hv), hk = hv / a.G;
+  R.ld = ld1<GT>(a.ld, head);  // T == 1: gates are [B, Hv] in both layouts
+  R.be = ld1<GT>(a.beta, head);
+  const int64_t qk = (b * a.Hk + hk) * D;  // T == 1: both layouts coincide
+#pragma unroll
+  for (int m = 0; m < NV4; ++m) {
+    R.k[m].load(a.k, qk + 4 * (m * CL + j));
+    R.q[m].load(a.q, qk + 4 * (m * CL + j));
+  }
+  const float* s0 = a.s0 + head * (int64_t)(D * D);
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int row = (wave * RPL + r) * RG + g;
 #pragma unroll
-    for (int m = 0; m < NV4; ++m)
-      S[r][m] = nt_load4(a.s0 + sbase + row * D + 4 * (m * CL + j));
+    for (int m = 0; m < NV4; ++m) R.S[r][m] = nt_load4(s0 + (row0 + r) * D + 4 * (m * CL + j));
   }
+  R.v.load(a.v, head * D + row0);
+  if (a.z) R.z.load(a.z, head * D + row0);
+}
 
-  // 2. this lane's columns of q and k; the row group covers all D columns,
-  //    so the group sums are the full norms and k.q
-  const int64_t qk = (b * a.Hk + hk) * D;  // T == 1: both layouts coincide
-  float4 kc[NV4], qc[NV4];
+// Fold the norms, run the fused row pass, write the state back and the
+// (gated) output.  The L2 norms and the q scale are applied to the reduced
+// dots as scalars (u = rk*(S.k), w = rq*(S.q), S += (coef*rk) k), so the
+// normalised vectors are never materialised.  red[NW] is this head's slot for
+// the cross-wave sum of the gated norm.
+template <int DT, int GT, int D, int CL, int RPL, int NW>
+__device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
+                                              HeadRegs<DT, D, CL, RPL>& R, float* red) {
+  constexpr int NV4 = D / CL / 4;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int j = lane % CL;
+  const int row0 = decode_row0<CL, RPL>();
+
+  // the row group covers all D columns: its sums are the full norms and k.q
   float skk = 0.f, sqq = 0.f, skq = 0.f;
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
-    kc[m] = load4(a.k, qk + 4 * (m * CL + j), a.dt);
-    qc[m] = load4(a.q, qk + 4 * (m * CL + j), a.dt);
-    skk = dot4(kc[m], kc[m], skk);
-    sqq = dot4(qc[m], qc[m], sqq);
-    skq = dot4(kc[m], qc[m], skq);
+    const float4 kf = R.k[m].get4(0), qf = R.q[m].get4(0);
+    skk = dot4(kf, kf, skk);
+    sqq = dot4(qf, qf, sqq);
+    skq = dot4(kf, qf, skq);
   }
   skk = group_sum<CL>(skk);
   sqq = group_sum<CL>(sqq);
@@ -181,76 +278,116 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
     rq *= rsqrtf(sqq + a.qk_eps);
   }
   const float kq = skq * rk * rq;
+  const float al = expf(R.ld), be = R.be;
+
+  // both dots of every row from the registers
+  float u[RPL], w[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) u[r] = w[r] = 0.f;
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
-    kc[m] = scale4(kc[m], rk);
-    qc[m] = scale4(qc[m], rq);
-  }
-  const int64_t gi = b * a.Hv + hv;
-  const float al = expf(load1(a.ld, gi, a.gdt));
-  const float be = load1(a.beta, gi, a.gdt);
-  const int64_t vbase = gi * D;
-
-  // 3. fused row pass: both dots from the registers, update, write back
-  float o[RPL];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int row = (wave * RPL + r) * RG + g;
-    float u0 = 0.f, u1 = 0.f, w0 = 0.f, w1 = 0.f;
-#pragma unroll
-    for (int m = 0; m < NV4; ++m) {
-      if (m & 1) {
-        u1 = dot4(S[r][m], kc[m], u1);
-        w1 = dot4(S[r][m], qc[m], w1);
-      } else {
-        u0 = dot4(S[r][m], kc[m], u0);
-        w0 = dot4(S[r][m], qc[m], w0);
-      }
-    }
-    const float u = group_sum<CL>(u0 + u1);
-    const float wq = group_sum<CL>(w0 + w1);
-    const float coef = be * (load1(a.v, vbase + row, a.dt) - al * u);
-    o[r] = al * wq + coef * kq;
-#pragma unroll
-    for (int m = 0; m < NV4; ++m) {
-      float4 s = S[r][m];
-      s.x = fmaf(coef, kc[m].x, al * s.x);
-      s.y = fmaf(coef, kc[m].y, al * s.y);
-      s.z = fmaf(coef, kc[m].z, al * s.z);
-      s.w = fmaf(coef, kc[m].w, al * s.w);
-      nt_store4(s, a.s_out + sbase + row * D + 4 * (m * CL + j));
-    }
-  }
-
-  // 4. output: raw o, or the gated RMSNorm over the whole head
-  if (a.z == nullptr) {
-    if (j == 0) {
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) a.y[vbase + (wave * RPL + r) * RG + g] = o[r];
-    }
-    return;
-  }
-  float x[RPL];
-  float ss = 0.f;
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int row = (wave * RPL + r) * RG + g;
-    x[r] = o[r] * silu(load1(a.z, vbase + row, a.dt));
-    ss = fmaf(x[r], x[r], ss);
-  }
-  ss = wave_sum(j == 0 ? ss : 0.f);  // every lane of a group holds the same rows
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) tot += red[i];
-  const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
-  if (j == 0) {
+    const float4 kf = R.k[m].get4(0), qf = R.q[m].get4(0);
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const int row = (wave * RPL + r) * RG + g;
-      a.y[vbase + row] = x[r] * inv * load1(a.w, row, a.dt);
+      u[r] = dot4(R.S[r][m], kf, u[r]);
+      w[r] = dot4(R.S[r][m], qf, w[r]);
     }
+  }
+  float o[RPL], ck[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float ur = group_sum<CL>(u[r]) * rk;
+    const float wr = group_sum<CL>(w[r]) * rq;
+    const float coef = be * (R.v.get(r) - al * ur);
+    o[r] = al * wr + coef * kq;
+    ck[r] = coef * rk;  // coefficient of the raw k in the update
+  }
+  // S = alpha*S + coef*k^, written back from the registers
+  float* so = a.s_out + head * (int64_t)(D * D);
+#pragma unroll
+  for (int m = 0; m < NV4; ++m) {
+    const float4 kf = R.k[m].get4(0);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      float4 s = R.S[r][m];
+      s.x = fmaf(ck[r], kf.x, al * s.x);
+      s.y = fmaf(ck[r], kf.y, al * s.y);
+      s.z = fmaf(ck[r], kf.z, al * s.z);
+      s.w = fmaf(ck[r], kf.w, al * s.w);
+      nt_store4(s, so + (row0 + r) * D + 4 * (m * CL + j));
+    }
+  }
+
+  // output: raw o, or the gated RMSNorm over the whole head
+  float* y = a.y + head * D + row0;
+  if (a.z != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      o[r] *= silu(R.z.get(r));
+      ss = fmaf(o[r], o[r], ss);
+    }
+    ss = wave_sum(j == 0 ? ss : 0.f);  // every lane of a group holds the same rows
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) tot += red[i];
+    const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
+    Raw<DT, RPL> wr;
+    wr.load(a.w, row0);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) o[r] *= inv * wr.get(r);
+  }
+  if (j == 0) {
+    if constexpr (RPL == 4) {
+      *reinterpret_cast<float4*>(y) = make_float4(o[0], o[1], o[2], o[3]);
+    } else if constexpr (RPL == 2) {
+      *reinterpret_cast<float2*>(y) = make_float2(o[0], o[1]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) y[r] = o[r];
+    }
+  }
+}
+
+// One workgroup per head (b, hv): every state row of the head is read once
+// and written once.  Heads are taken in launch order: for this pure stream
+// the plain order spreads the concurrent workgroups' addresses over the HBM
+// channels better than grouping contiguous head ranges per XCD (measured).
+template <int DT, int GT, int D, int CL, int RPL, int NW>
+__global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
+  static_assert((D / CL) % 4 == 0, "a lane owns whole float4 chunks");
+  static_assert(NW * (kWave / CL) * RPL == D, "a workgroup owns the whole head");
+  __shared__ float red[NW];
+  const int64_t head = blockIdx.x;
+  HeadRegs<DT, D, CL, RPL> R;
+  decode_fetch<DT, GT, D, CL, RPL, NW>(a, head, R);
+  decode_finish<DT, GT, D, CL, RPL, NW>(a, head, R, red);
+}
+
+// Persistent variant: a workgroup walks heads blockIdx.x, +gridDim.x, ... and
+// issues the loads of its next head before finishing the current one, so the
+// memory system stays busy through the arithmetic and the norm's barrier.
+template <int DT, int GT, int D, int CL, int RPL, int NW>
+__global__ __launch_bounds__(NW* kWave) void decode_persistent_kernel(StepArgs a, int64_t nheads) {
+  static_assert((D / CL) % 4 == 0, "a lane owns whole float4 chunks");
+  static_assert(NW * (kWave / CL) * RPL == D, "a workgroup owns the whole head");
+  // two slots: a head's slot is rewritten only after the next head's barrier
+  __shared__ float red[2][NW];
+  HeadRegs<DT, D, CL, RPL> A, B;
+  const int64_t stride = gridDim.x;
+  int64_t h = blockIdx.x;
+  if (h < nheads) decode_fetch<DT, GT, D, CL, RPL, NW>(a, h, A);
+  while (h < nheads) {
+    const int64_t h1 = h + stride;
+    if (h1 < nheads) decode_fetch<DT, GT, D, CL, RPL, NW>(a, h1, B);
+    decode_finish<DT, GT, D, CL, RPL, NW>(a, h, A, red[0]);
+    if (h1 >= nheads) break;
+    const int64_t h2 = h1 + stride;
+    if (h2 < nheads) decode_fetch<DT, GT, D, CL, RPL, NW>(a, h2, A);
+    decode_finish<DT, GT, D, CL, RPL, NW>(a, h1, B, red[1]);
+    h = h2;
   }
 }
 
@@ -266,7 +403,7 @@ struct ScanArgs {
   float qk_eps, norm_eps, qscale;
 };
 
-template <int D, int CL, int RPL, int NW, int TC, bool FUSE_NORM>
+template <int DT, int D, int CL, int RPL, int NW, int TC, bool FUSE_NORM>
 __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
   constexpr int NCOL = D / CL, NV4 = NCOL / 4, RG = kWave / CL, ROWS = NW * RG * RPL;
   constexpr int NT = NW * kWave, D4 = D / 4;
@@ -325,12 +462,12 @@ __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
     for (int e = tid; e < tc * D4; e += NT) {
       const int tt = e / D4, c4 = e % D4;
       const int64_t off = qk_base + (t0 + tt) * qk_ts + 4 * c4;
-      sk[tt][c4] = load4(a.k, off, a.dt);
-      sq[tt][c4] = load4(a.q, off, a.dt);
+      sk[tt][c4] = ld4<DT>(a.k, off);
+      sq[tt][c4] = ld4<DT>(a.q, off);
     }
     for (int e = tid; e < tc * ROWS; e += NT) {
       const int tt = e / ROWS, rr = e % ROWS;
-      sv[tt][rr] = load1(a.v, v_base + (t0 + tt) * v_ts + row0 + rr, a.dt);
+      sv[tt][rr] = ld1<DT>(a.v, v_base + (t0 + tt) * v_ts + row0 + rr);
     }
     for (int e = tid; e < tc; e += NT) {
       const int64_t gi = g_base + (t0 + e) * g_ts;
@@ -414,14 +551,14 @@ __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
           for (int i = 0; i < EPL; ++i) {
             const int rr = lane + kWave * i;
             x[i] = 0.f;
-            if (rr < D) x[i] = so[tt][rr] * silu(load1(a.z, vo + rr, a.dt));
+            if (rr < D) x[i] = so[tt][rr] * silu(ld1<DT>(a.z, vo + rr));
             ss = fmaf(x[i], x[i], ss);
           }
           const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + a.norm_eps);
 #pragma unroll
           for (int i = 0; i < EPL; ++i) {
             const int rr = lane + kWave * i;
-            if (rr < D) a.y[vo + rr] = x[i] * inv * load1(a.w, rr, a.dt);
+            if (rr < D) a.y[vo + rr] = x[i] * inv * ld1<DT>(a.w, rr);
           }
         }
         written = true;
@@ -449,9 +586,9 @@ __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
 // ------------------------------------------------------------------ gated RMSNorm
 // In place over y viewed as [nvec, D] (both layouts keep the head dim last and
 // dense, and z shares y's layout); one wave per head vector.
-template <int D>
+template <int DT, int D>
 __global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z, const void* w,
-                                                         int dt, int64_t nvec, float eps) {
+                                                         int64_t nvec, float eps) {
   constexpr int EPL = (D + kWave - 1) / kWave;
   const int lane = threadIdx.x % kWave;
   const int64_t vec = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
@@ -463,14 +600,14 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z
   for (int i = 0; i < EPL; ++i) {
     const int rr = lane + kWave * i;
     x[i] = 0.f;
-    if (rr < D) x[i] = y[base + rr] * silu(load1(z, base + rr, dt));
+    if (rr < D) x[i] = y[base + rr] * silu(ld1<DT>(z, base + rr));
     ss = fmaf(x[i], x[i], ss);
   }
   const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + eps);
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int rr = lane + kWave * i;
-    if (rr < D) y[base + rr] = x[i] * inv * load1(w, rr, dt);
+    if (rr < D) y[base + rr] = x[i] * inv * ld1<DT>(w, rr);
   }
 }
 
@@ -488,61 +625,89 @@ float q_scale(const gdn_desc& d) {
   return (d.flags & GDN_FOLD_Q_SCALE) ? 1.0f / std::sqrt((float)d.Dk) : 1.0f;
 }
 
-int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v,
-                const void* ld, const void* beta, const float* s0, const void* z, const void* w,
-                float* y, float* s_out, hipStream_t st) {
-  StepArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, (int)d.Hk, (int)d.Hv, (int)(d.Hv / d.Hk),
-             d.dtype, d.gate_dtype, d.flags, d.qk_eps, d.norm_eps, q_scale(d)};
+template <int DT, int GT>
+int launch_step_dt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(d.B * d.Hv));
   switch (d.Dk) {
-    case 128: decode_kernel<128, 8, 2, 8><<<grid, 8 * kWave, 0, st>>>(a); break;
-    case 64: decode_kernel<64, 4, 2, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
-    case 32: decode_kernel<32, 4, 1, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
-    case 16: decode_kernel<16, 4, 1, 1><<<grid, 1 * kWave, 0, st>>>(a); break;
+    case 128: decode_kernel<DT, GT, 128, 8, 2, 8><<<grid, 8 * kWave, 0, st>>>(a); break;
+    case 64: decode_kernel<DT, GT, 64, 4, 2, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
+    case 32: decode_kernel<DT, GT, 32, 4, 1, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
+    case 16: decode_kernel<DT, GT, 16, 4, 1, 1><<<grid, 1 * kWave, 0, st>>>(a); break;
     default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
   }
   return device_status("decode_kernel launch");
 }
 
-template <int D, int CL, int RPL, int NW, int TC>
+template <int DT>
+int launch_step_gt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
+  switch (d.gate_dtype) {
+    case GDN_F32: return launch_step_dt<DT, GDN_F32>(d, a, st);
+    case GDN_F16: return launch_step_dt<DT, GDN_F16>(d, a, st);
+    default: return launch_step_dt<DT, GDN_BF16>(d, a, st);
+  }
+}
+
+int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v,
+                const void* ld, const void* beta, const float* s0, const void* z, const void* w,
+                float* y, float* s_out, hipStream_t st) {
+  const StepArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, (int)d.Hk, (int)d.Hv,
+                   (int)(d.Hv / d.Hk), d.dtype, d.gate_dtype, d.flags, d.qk_eps, d.norm_eps,
+                   q_scale(d)};
+  switch (d.dtype) {
+    case GDN_F32: return launch_step_gt<GDN_F32>(d, a, st);
+    case GDN_F16: return launch_step_gt<GDN_F16>(d, a, st);
+    default: return launch_step_gt<GDN_BF16>(d, a, st);
+  }
+}
+
+template <int DT, int D, int CL, int RPL, int NW, int TC>
 int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
   constexpr int ROWS = NW * (kWave / CL) * RPL;
   a.nrb = D / ROWS;
   const dim3 grid((unsigned)(heads * a.nrb));
   if constexpr (ROWS == D) {
-    scan_kernel<D, CL, RPL, NW, TC, true><<<grid, NW * kWave, 0, st>>>(a);
+    scan_kernel<DT, D, CL, RPL, NW, TC, true><<<grid, NW * kWave, 0, st>>>(a);
     return device_status("scan_kernel launch");
   } else {
-    scan_kernel<D, CL, RPL, NW, TC, false><<<grid, NW * kWave, 0, st>>>(a);
+    scan_kernel<DT, D, CL, RPL, NW, TC, false><<<grid, NW * kWave, 0, st>>>(a);
     int rc = device_status("scan_kernel launch");
     if (rc != GDN_OK || a.z == nullptr) return rc;
     const int64_t nvec = heads * a.T;
-    gated_norm_kernel<D><<<dim3((unsigned)((nvec + 3) / 4)), 256, 0, st>>>(
-        a.y, a.z, a.w, a.dt, nvec, a.norm_eps);
+    gated_norm_kernel<DT, D><<<dim3((unsigned)((nvec + 3) / 4)), 256, 0, st>>>(
+        a.y, a.z, a.w, nvec, a.norm_eps);
     return device_status("gated_norm_kernel launch");
+  }
+}
+
+template <int DT>
+int launch_scan_dt(const ScanArgs& a, int D, int64_t heads, hipStream_t st) {
+  switch (D) {
+    case 128:
+      // enough heads to fill the chip with whole-head workgroups: keep the
+      // norm fused; otherwise split each head's rows over more workgroups
+      if (heads >= 512) return launch_scan_cfg<DT, 128, 4, 2, 4, 16>(a, heads, st);
+      if (heads >= 128) return launch_scan_cfg<DT, 128, 8, 1, 4, 16>(a, heads, st);
+      return launch_scan_cfg<DT, 128, 16, 1, 4, 16>(a, heads, st);
+    case 64:
+      if (heads >= 256) return launch_scan_cfg<DT, 64, 4, 1, 4, 32>(a, heads, st);
+      return launch_scan_cfg<DT, 64, 8, 1, 2, 32>(a, heads, st);
+    case 32: return launch_scan_cfg<DT, 32, 4, 1, 2, 32>(a, heads, st);
+    case 16: return launch_scan_cfg<DT, 16, 4, 1, 1, 32>(a, heads, st);
+    default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
   }
 }
 
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
                 float* s_out, hipStream_t st) {
-  ScanArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, d.T, (int)d.Hk, (int)d.Hv,
-             (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags, d.qk_eps,
-             d.norm_eps, q_scale(d)};
+  const ScanArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, d.T, (int)d.Hk, (int)d.Hv,
+                   (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags,
+                   d.qk_eps, d.norm_eps, q_scale(d)};
   const int64_t heads = d.B * d.Hv;
-  switch (d.Dk) {
-    case 128:
-      // enough heads to fill the chip with whole-head workgroups: keep the
-      // norm fused; otherwise split each head's rows over more workgroups
-      if (heads >= 512) return launch_scan_cfg<128, 4, 2, 4, 16>(a, heads, st);
-      if (heads >= 128) return launch_scan_cfg<128, 8, 1, 4, 16>(a, heads, st);
-      return launch_scan_cfg<128, 16, 1, 4, 16>(a, heads, st);
-    case 64:
-      if (heads >= 256) return launch_scan_cfg<64, 4, 1, 4, 32>(a, heads, st);
-      return launch_scan_cfg<64, 8, 1, 2, 32>(a, heads, st);
-    case 32: return launch_scan_cfg<32, 4, 1, 2, 32>(a, heads, st);
-    case 16: return launch_scan_cfg<16, 4, 1, 1, 32>(a, heads, st);
-    default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
+  switch (d.dtype) {
+    case GDN_F32: return launch_scan_dt<GDN_F32>(a, (int)d.Dk, heads, st);
+    case GDN_F16: return launch_scan_dt<GDN_F16>(a, (int)d.Dk, heads, st);
+    default: return launch_scan_dt<GDN_BF16>(a, (int)d.Dk, heads, st);
   }
 }
 
