@@ -46,12 +46,6 @@ namespace {
 constexpr int kWave = 64;
 
 // ------------------------------------------------------------------ loads
-__device__ __forceinline__ float load1(const void* p, int64_t i, int dt) {
-  if (dt == GDN_F32) return static_cast<const float*>(p)[i];
-  const uint16_t h = static_cast<const uint16_t*>(p)[i];
-  if (dt == GDN_F16) return (float)__builtin_bit_cast(_Float16, h);
-  return __uint_as_float((uint32_t)h << 16);
-}
 
 // Compile-time dtype versions for the operand loads of the kernels.  ld4 reads
 // four consecutive elements starting at i (i is a multiple of 4 and the base
@@ -403,19 +397,62 @@ struct ScanArgs {
   float qk_eps, norm_eps, qscale;
 };
 
-template <int DT, int D, int CL, int RPL, int NW, int TC, bool FUSE_NORM>
-__global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
+// Raw operands of one chunk of TC tokens, held in registers while the previous
+// chunk computes.  Thread tid covers chunk items tid, tid + NT, ...
+template <int DT, int GT, int D, int ROWS, int TC, int NT, bool WITH_Z>
+struct ChunkRegs {
+  static constexpr int D4 = D / 4, R2 = ROWS / 2;
+  static constexpr int NQK = (TC * D4 + NT - 1) / NT;  // float4 groups of q and of k
+  static constexpr int NV = (TC * R2 + NT - 1) / NT;   // pairs of v (and z) elements
+  Raw<DT, 4> k[NQK], q[NQK];
+  Raw<DT, 2> v[NV];
+  Raw<DT, 2> z[WITH_Z ? NV : 1];
+  Raw<GT, 1> ld, be;
+};
+
+// Operand bases and per-token strides of one (b, head) in either layout.
+struct ScanBases {
+  int64_t qk_base, qk_ts, v_base, v_ts, g_base, g_ts;
+};
+
+// Smallest and largest decay scale kept folded: outside [2^-30, 2^30] the
+// state is brought back to scale 1 (and alpha == 0 always lands here).
+constexpr float kFoldMin = 9.3132257e-10f, kFoldMax = 1.0737418e9f;
+
+// The scan processes the time axis in chunks of TC tokens staged through LDS,
+// and each chunk in blocks of L tokens.  Within a block the recurrence is
+// unrolled with the affine argument of the "Module gdn" page ("The fusion"),
+// carried across tokens: with S the state at the block start,
+//   S_i = A_{i+1} S + sum_{j<=i} (prod_{m=j+1..i} alpha_m) c_j k_j^T,
+//   A_i = prod_{m<i} alpha_m,   c_i = beta_i (v_i - alpha_i u_i),
+//   u_i = S_{i-1}.k_i = A_i (S.k_i) + sum_{j<i} P_ij c_j,
+//   o_i = S_i.q_i     = A_{i+1} (S.q_i) + sum_{j<=i} Q_ij c_j,
+// with P_ij = (prod_{m=j+1..i-1} alpha_m)(k_j.k_i) and
+// Q_ij = (prod_{m=j+1..i} alpha_m)(k_j.q_i) the same for every row of a head.
+// So the 2L dots of a row against the block-start state are independent, a
+// short L x L substitution per row gives every c_i and o_i, and the state
+// takes one rank-L update.  L = 1 is the plain per-token recurrence.
+template <int DT, int GT, int D, int CL, int RPL, int NW, int TC, int L, bool FUSE_NORM>
+__global__ __launch_bounds__(NW* kWave)
+__attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArgs a) {
   constexpr int NCOL = D / CL, NV4 = NCOL / 4, RG = kWave / CL, ROWS = NW * RG * RPL;
-  constexpr int NT = NW * kWave, D4 = D / 4;
+  constexpr int NT = NW * kWave, D4 = D / 4, R2 = ROWS / 2;
+  constexpr int LPT = D / 8;  // lanes per token in the norm pass (8 elements of q and k each)
+  constexpr int NB = TC / L;  // blocks per chunk
+  constexpr int NPB = L * (L - 1);  // off-diagonal Gram entries per block (k.k and k.q)
+  constexpr bool KEEP_K = L * NV4 <= 8;  // keep the block's k columns for the update
   static_assert(NCOL % 4 == 0, "a lane owns whole float4 chunks");
-  static_assert(D % ROWS == 0, "row blocks tile the head");
+  static_assert(D % ROWS == 0 && ROWS % 2 == 0, "row blocks tile the head");
   static_assert(!FUSE_NORM || ROWS == D, "the fused norm needs the whole head");
-  static_assert(D4 <= kWave, "one wave normalises one token");
+  static_assert(TC <= NT && NT % LPT == 0 && TC % L == 0, "chunk shape");
+  typedef ChunkRegs<DT, GT, D, ROWS, TC, NT, FUSE_NORM> Chunk;
   __shared__ float4 sk[TC][D4];
   __shared__ float4 sq[TC][D4];
   __shared__ float sv[TC][ROWS];
+  __shared__ float sz[FUSE_NORM ? 2 : 1][FUSE_NORM ? TC : 1][FUSE_NORM ? D : 1];
   __shared__ float so[TC][ROWS];
   __shared__ float sal[TC], sbe[TC], skq[TC];
+  __shared__ float sP[NB][L][L], sQ[NB][L][L], sA[NB][L + 1], sR[NB][L], sAmin[NB], sAmax[NB];
 
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int rb = (int)(tile % a.nrb);
@@ -425,115 +462,320 @@ __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int g = lane / CL, j = lane % CL;
   const int64_t T = a.T;
+  const bool has_z = FUSE_NORM && a.z != nullptr;
 
-  // operand bases and per-token strides for the two layouts
-  int64_t qk_base, qk_ts, v_base, v_ts, g_base, g_ts;
+  ScanBases sb;
   if (a.head_major) {
-    qk_base = (b * a.Hk + hk) * T * D;
-    qk_ts = D;
-    v_base = (b * a.Hv + hv) * T * D;
-    v_ts = D;
-    g_base = (b * a.Hv + hv) * T;
-    g_ts = 1;
+    sb = {(b * a.Hk + hk) * T * D, D, (b * a.Hv + hv) * T * D, D, (b * a.Hv + hv) * T, 1};
   } else {
-    qk_base = (b * T * a.Hk + hk) * D;
-    qk_ts = (int64_t)a.Hk * D;
-    v_base = (b * T * a.Hv + hv) * D;
-    v_ts = (int64_t)a.Hv * D;
-    g_base = b * T * a.Hv + hv;
-    g_ts = a.Hv;
+    sb = {(b * T * a.Hk + hk) * D, (int64_t)a.Hk * D, (b * T * a.Hv + hv) * D,
+          (int64_t)a.Hv * D, b * T * a.Hv + hv, a.Hv};
   }
   const int row0 = rb * ROWS;
   const int64_t sbase = (b * a.Hv + hv) * (int64_t)(D * D);
 
-  float4 S[RPL][NV4];
+  // chunk staging: global -> registers (issued early) -> LDS
+  auto chunk_load = [&](Chunk& P, int64_t t0, int tc) {
+#pragma unroll
+    for (int i = 0; i < Chunk::NQK; ++i) {
+      const int e = tid + i * NT, tt = e / D4, c4 = e % D4;
+      if (e < TC * D4 && tt < tc) {
+        const int64_t off = sb.qk_base + (t0 + tt) * sb.qk_ts + 4 * c4;
+        P.k[i].load(a.k, off);
+        P.q[i].load(a.q, off);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Chunk::NV; ++i) {
+      const int e = tid + i * NT, tt = e / R2, r2 = e % R2;
+      if (e < TC * R2 && tt < tc) {
+        const int64_t off = sb.v_base + (t0 + tt) * sb.v_ts + row0 + 2 * r2;
+        P.v[i].load(a.v, off);
+        if constexpr (FUSE_NORM) {
+          if (has_z) P.z[i].load(a.z, off);
+        }
+      }
+    }
+    if (tid < tc) {
+      const int64_t gi = sb.g_base + (t0 + tid) * sb.g_ts;
+      P.ld.load(a.ld, gi);
+      P.be.load(a.beta, gi);
+    }
+  };
+  // Tokens tc..TC-1 of a short last chunk become identity steps (alpha = 1,
+  // beta = 0, k = q = v = 0), so whole blocks can always be processed.
+  auto chunk_store = [&](const Chunk& P, int tc, int zbuf) {
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < Chunk::NQK; ++i) {
+      const int e = tid + i * NT, tt = e / D4, c4 = e % D4;
+      if (e < TC * D4) {
+        sk[tt][c4] = tt < tc ? P.k[i].get4(0) : zero4;
+        sq[tt][c4] = tt < tc ? P.q[i].get4(0) : zero4;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Chunk::NV; ++i) {
+      const int e = tid + i * NT, tt = e / R2, r2 = e % R2;
+      if (e < TC * R2) {
+        sv[tt][2 * r2] = tt < tc ? P.v[i].get(0) : 0.f;
+        sv[tt][2 * r2 + 1] = tt < tc ? P.v[i].get(1) : 0.f;
+        if constexpr (FUSE_NORM) {
+          if (has_z && tt < tc) {
+            sz[zbuf][tt][2 * r2] = P.z[i].get(0);
+            sz[zbuf][tt][2 * r2 + 1] = P.z[i].get(1);
+          }
+        }
+      }
+    }
+    if (tid < TC) {
+      sal[tid] = tid < tc ? expf(P.ld.get(0)) : 1.f;
+      sbe[tid] = tid < tc ? P.be.get(0) : 0.f;
+    }
+  };
+
+  // State S = gsc * St: St lives in VGPRs for the whole time axis.
+  float4 St[RPL][NV4];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int row = row0 + (wave * RPL + r) * RG + g;
 #pragma unroll
     for (int m = 0; m < NV4; ++m)
-      S[r][m] = *reinterpret_cast<const float4*>(a.s0 + sbase + row * D + 4 * (m * CL + j));
+      St[r][m] = *reinterpret_cast<const float4*>(a.s0 + sbase + row * D + 4 * (m * CL + j));
+  }
+  float gsc = 1.f;
+  float wgt[(D + kWave - 1) / kWave];  // norm weight for the fused output
+  if constexpr (FUSE_NORM) {
+#pragma unroll
+    for (int i = 0; i < (D + kWave - 1) / kWave; ++i)
+      wgt[i] = (has_z && lane + kWave * i < D) ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
   }
 
-  for (int64_t t0 = 0; t0 < T; t0 += TC) {
+  Chunk P;
+  chunk_load(P, 0, (int)(T < TC ? T : TC));
+  chunk_store(P, (int)(T < TC ? T : TC), 0);
+  // Every load issued so far (state, weights, first chunk) is complete here;
+  // saying so explicitly keeps the compiler from re-waiting for them inside
+  // the token loop, where the next chunk's loads are in flight.
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  for (int64_t c = 0;; ++c) {
+    const int64_t t0 = c * TC;
     const int tc = (int)((T - t0) < TC ? (T - t0) : TC);
-
-    // A. stage this chunk's raw q, k, v and gates
-    for (int e = tid; e < tc * D4; e += NT) {
-      const int tt = e / D4, c4 = e % D4;
-      const int64_t off = qk_base + (t0 + tt) * qk_ts + 4 * c4;
-      sk[tt][c4] = ld4<DT>(a.k, off);
-      sq[tt][c4] = ld4<DT>(a.q, off);
-    }
-    for (int e = tid; e < tc * ROWS; e += NT) {
-      const int tt = e / ROWS, rr = e % ROWS;
-      sv[tt][rr] = ld1<DT>(a.v, v_base + (t0 + tt) * v_ts + row0 + rr);
-    }
-    for (int e = tid; e < tc; e += NT) {
-      const int64_t gi = g_base + (t0 + e) * g_ts;
-      sal[e] = expf(load1(a.ld, gi, a.gdt));
-      sbe[e] = load1(a.beta, gi, a.gdt);
-    }
+    const int nblk = (tc + L - 1) / L;
     __syncthreads();
 
-    // B. fold the L2 norms and the q scale, once per token
-    for (int tt = wave; tt < tc; tt += NW) {
-      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 kk = lane < D4 ? sk[tt][lane] : zero;
-      const float4 qq = lane < D4 ? sq[tt][lane] : zero;
-      const float skk = wave_sum(dot4(kk, kk, 0.f));
-      const float sqq = wave_sum(dot4(qq, qq, 0.f));
-      const float sqk = wave_sum(dot4(kk, qq, 0.f));
+    // B1. fold the L2 norms and the q scale into the staged q and k, all
+    //     tokens of the chunk at once (LPT lanes per token); padding tokens
+    //     stay exactly zero
+    for (int tt = tid / LPT; tt < tc; tt += NT / LPT) {
+      const int p = tid % LPT;
+      float4 k0 = sk[tt][2 * p], k1 = sk[tt][2 * p + 1];
+      float4 q0 = sq[tt][2 * p], q1 = sq[tt][2 * p + 1];
+      float skk = dot4(k1, k1, dot4(k0, k0, 0.f));
+      float sqq = dot4(q1, q1, dot4(q0, q0, 0.f));
+      float sqk = dot4(k1, q1, dot4(k0, q0, 0.f));
+      skk = group_sum<LPT>(skk);
+      sqq = group_sum<LPT>(sqq);
+      sqk = group_sum<LPT>(sqk);
       float rk = 1.f, rq = a.qscale;
       if (a.flags & GDN_FOLD_QK_L2NORM) {
         rk = rsqrtf(skk + a.qk_eps);
         rq *= rsqrtf(sqq + a.qk_eps);
       }
-      if (lane < D4) {
-        sk[tt][lane] = scale4(kk, rk);
-        sq[tt][lane] = scale4(qq, rq);
+      sk[tt][2 * p] = scale4(k0, rk);
+      sk[tt][2 * p + 1] = scale4(k1, rk);
+      sq[tt][2 * p] = scale4(q0, rq);
+      sq[tt][2 * p + 1] = scale4(q1, rq);
+      if (p == 0) skq[tt] = sqk * rk * rq;
+    }
+    const bool more = t0 + TC < T;
+    if (more) chunk_load(P, t0 + TC, (int)((T - t0 - TC) < TC ? (T - t0 - TC) : TC));
+    if constexpr (L > 1) {
+      __syncthreads();
+      // B2. per-block coefficients shared by every row: the off-diagonal Gram
+      //     entries times their decay products, and the decay prefixes.
+      for (int x = tid / LPT; x < NB * NPB; x += NT / LPT) {
+        const int p = tid % LPT;
+        const int bk = x / NPB, y = x % NPB, kind = y / (NPB / 2);
+        int pr = y % (NPB / 2), i = 1;
+        while (pr >= i) { pr -= i; ++i; }
+        const int jj = pr;  // j < i
+        const int ti = bk * L + i, tj = bk * L + jj;
+        const float4* other = kind ? sq[ti] : sk[ti];
+        float dv = dot4(sk[tj][2 * p], other[2 * p], 0.f);
+        dv = dot4(sk[tj][2 * p + 1], other[2 * p + 1], dv);
+        dv = group_sum<LPT>(dv);
+        if (p == 0) {
+          float prod = 1.f;
+          for (int m = jj + 1; m < i; ++m) prod *= sal[bk * L + m];
+          if (kind) sQ[bk][i][jj] = dv * prod * sal[ti];
+          else sP[bk][i][jj] = dv * prod;
+        }
       }
-      if (lane == 0) skq[tt] = sqk * rk * rq;
+      if (tid < NB) {
+        const int bk = tid;
+        float acc = 1.f, amin = 3.0e38f, amax = 0.f;
+        sA[bk][0] = 1.f;
+        for (int i = 0; i < L; ++i) {
+          acc *= sal[bk * L + i];
+          sA[bk][i + 1] = acc;
+          amin = fminf(amin, acc);
+          amax = fmaxf(amax, acc);
+          sQ[bk][i][i] = skq[bk * L + i];
+        }
+        sAmin[bk] = amin;
+        sAmax[bk] = amax;
+        float rr = 1.f;
+        for (int i = L - 1; i >= 0; --i) {
+          sR[bk][i] = rr;
+          rr *= sal[bk * L + i];
+        }
+      }
     }
     __syncthreads();
 
-    // C. the recurrence, token after token, state in registers
-    for (int tt = 0; tt < tc; ++tt) {
-      const float al = sal[tt], be = sbe[tt], kq = skq[tt];
-      float4 kc[NV4];
-      float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
+    // C. the recurrence: token by token (L == 1) or one block of L tokens after the other.  With
+    //    S = gsc*St the update becomes St += sum_j c_j/(gsc*A_{j+1}) k_j and
+    //    gsc *= A_L: one FMA per state element per token.  When the scale
+    //    would leave [2^-30, 2^30] (and whenever an alpha is 0) St is brought
+    //    to the block's end scale in place and the scale restarts at 1.
+    if constexpr (L == 1) {
+      // one token at a time: St += (coef/gsc') k with gsc' = alpha*gsc
+      for (int tt = 0; tt < tc; ++tt) {
+        const float al = sal[tt], be = sbe[tt], kq = skq[tt];
+        const float gn = gsc * al;
+        const bool rescale = !(gn >= kFoldMin && gn <= kFoldMax);  // uniform, rare
+        const float gnext = rescale ? 1.f : gn;
+        const float ig = rescale ? 1.f : __builtin_amdgcn_rcpf(gn);
+        float4 kc[NV4];
+        float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
-#pragma unroll
-      for (int m = 0; m < NV4; ++m) {
-        kc[m] = sk[tt][m * CL + j];
-        const float4 qc = sq[tt][m * CL + j];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          if (m & 1) {
-            u1[r] = dot4(S[r][m], kc[m], u1[r]);
-            w1[r] = dot4(S[r][m], qc, w1[r]);
-          } else {
-            u0[r] = dot4(S[r][m], kc[m], u0[r]);
-            w0[r] = dot4(S[r][m], qc, w0[r]);
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        const int lr = (wave * RPL + r) * RG + g;
-        const float u = group_sum<CL>(u0[r] + u1[r]);
-        const float wq = group_sum<CL>(w0[r] + w1[r]);
-        const float coef = be * (sv[tt][lr] - al * u);
-        const float o = al * wq + coef * kq;
+        for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
 #pragma unroll
         for (int m = 0; m < NV4; ++m) {
-          S[r][m].x = fmaf(coef, kc[m].x, al * S[r][m].x);
-          S[r][m].y = fmaf(coef, kc[m].y, al * S[r][m].y);
-          S[r][m].z = fmaf(coef, kc[m].z, al * S[r][m].z);
-          S[r][m].w = fmaf(coef, kc[m].w, al * S[r][m].w);
+          kc[m] = sk[tt][m * CL + j];
+          const float4 qc = sq[tt][m * CL + j];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) {
+            if (m & 1) {
+              u1[r] = dot4(St[r][m], kc[m], u1[r]);
+              w1[r] = dot4(St[r][m], qc, w1[r]);
+            } else {
+              u0[r] = dot4(St[r][m], kc[m], u0[r]);
+              w0[r] = dot4(St[r][m], qc, w0[r]);
+            }
+          }
         }
-        if (j == 0) so[tt][lr] = o;
+        float c2[RPL];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+          const int lr = (wave * RPL + r) * RG + g;
+          const float u = group_sum<CL>(u0[r] + u1[r]) * gsc;
+          const float wq = group_sum<CL>(w0[r] + w1[r]) * gsc;
+          const float coef = be * (sv[tt][lr] - al * u);
+          if (j == 0) so[tt][lr] = al * wq + coef * kq;
+          c2[r] = coef * ig;
+        }
+        if (rescale) {
+#pragma unroll
+          for (int r = 0; r < RPL; ++r)
+#pragma unroll
+            for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gn);
+        }
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+          for (int m = 0; m < NV4; ++m) {
+            St[r][m].x = fmaf(c2[r], kc[m].x, St[r][m].x);
+            St[r][m].y = fmaf(c2[r], kc[m].y, St[r][m].y);
+            St[r][m].z = fmaf(c2[r], kc[m].z, St[r][m].z);
+            St[r][m].w = fmaf(c2[r], kc[m].w, St[r][m].w);
+          }
+        }
+        gsc = gnext;
+      }
+    } else {
+      for (int bk = 0; bk < nblk; ++bk) {
+        const int tb = bk * L;
+        float4 kreg[KEEP_K ? L : 1][KEEP_K ? NV4 : 1];
+        float d[RPL][L], e[RPL][L];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)
+#pragma unroll
+          for (int i = 0; i < L; ++i) d[r][i] = e[r][i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < NV4; ++m) {
+#pragma unroll
+          for (int i = 0; i < L; ++i) {
+            const float4 kc = sk[tb + i][m * CL + j];
+            const float4 qc = sq[tb + i][m * CL + j];
+            if constexpr (KEEP_K) kreg[i][m] = kc;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+              d[r][i] = dot4(St[r][m], kc, d[r][i]);
+              e[r][i] = dot4(St[r][m], qc, e[r][i]);
+            }
+          }
+        }
+        float cc[RPL][L];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+          const int lr = (wave * RPL + r) * RG + g;
+#pragma unroll
+          for (int i = 0; i < L; ++i) {
+            d[r][i] = group_sum<CL>(d[r][i]) * gsc;
+            e[r][i] = group_sum<CL>(e[r][i]) * gsc;
+          }
+#pragma unroll
+          for (int i = 0; i < L; ++i) {
+            float u = sA[bk][i] * d[r][i];
+#pragma unroll
+            for (int jj = 0; jj < i; ++jj) u = fmaf(sP[bk][i][jj], cc[r][jj], u);
+            cc[r][i] = sbe[tb + i] * (sv[tb + i][lr] - sal[tb + i] * u);
+          }
+#pragma unroll
+          for (int i = 0; i < L; ++i) {
+            float o = sA[bk][i + 1] * e[r][i];
+#pragma unroll
+            for (int jj = 0; jj <= i; ++jj) o = fmaf(sQ[bk][i][jj], cc[r][jj], o);
+            if (j == 0) so[tb + i][lr] = o;
+          }
+        }
+        const bool fold = gsc * sAmin[bk] >= kFoldMin && gsc * sAmax[bk] <= kFoldMax;  // uniform
+        float f[L];
+        if (fold) {
+#pragma unroll
+          for (int i = 0; i < L; ++i) f[i] = __builtin_amdgcn_rcpf(gsc * sA[bk][i + 1]);
+        } else {
+          const float gl = gsc * sA[bk][L];
+#pragma unroll
+          for (int i = 0; i < L; ++i) f[i] = sR[bk][i];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r)
+#pragma unroll
+            for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gl);
+        }
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)
+#pragma unroll
+          for (int i = 0; i < L; ++i) cc[r][i] *= f[i];
+#pragma unroll
+        for (int m = 0; m < NV4; ++m) {
+#pragma unroll
+          for (int i = 0; i < L; ++i) {
+            float4 kc;
+            if constexpr (KEEP_K) kc = kreg[i][m];
+            else kc = sk[tb + i][m * CL + j];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+              St[r][m].x = fmaf(cc[r][i], kc.x, St[r][m].x);
+              St[r][m].y = fmaf(cc[r][i], kc.y, St[r][m].y);
+              St[r][m].z = fmaf(cc[r][i], kc.z, St[r][m].z);
+              St[r][m].w = fmaf(cc[r][i], kc.w, St[r][m].w);
+            }
+          }
+        }
+        gsc = fold ? gsc * sA[bk][L] : 1.f;
       }
     }
     __syncthreads();
@@ -541,24 +783,25 @@ __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
     // D. write this chunk's outputs (gated here when the workgroup owns the head)
     bool written = false;
     if constexpr (FUSE_NORM) {
-      if (a.z != nullptr) {
+      if (has_z) {
         constexpr int EPL = (D + kWave - 1) / kWave;
+        const int zb = (int)(c & 1);
         for (int tt = wave; tt < tc; tt += NW) {
-          const int64_t vo = v_base + (t0 + tt) * v_ts;
+          const int64_t vo = sb.v_base + (t0 + tt) * sb.v_ts;
           float x[EPL];
           float ss = 0.f;
 #pragma unroll
           for (int i = 0; i < EPL; ++i) {
             const int rr = lane + kWave * i;
             x[i] = 0.f;
-            if (rr < D) x[i] = so[tt][rr] * silu(ld1<DT>(a.z, vo + rr));
+            if (rr < D) x[i] = so[tt][rr] * silu(sz[zb][tt][rr]);
             ss = fmaf(x[i], x[i], ss);
           }
           const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + a.norm_eps);
 #pragma unroll
           for (int i = 0; i < EPL; ++i) {
             const int rr = lane + kWave * i;
-            if (rr < D) a.y[vo + rr] = x[i] * inv * ld1<DT>(a.w, rr);
+            if (rr < D) a.y[vo + rr] = x[i] * inv * wgt[i];
           }
         }
         written = true;
@@ -567,11 +810,14 @@ __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
     if (!written) {
       for (int e = tid; e < tc * ROWS; e += NT) {
         const int tt = e / ROWS, rr = e % ROWS;
-        a.y[v_base + (t0 + tt) * v_ts + row0 + rr] = so[tt][rr];
+        a.y[sb.v_base + (t0 + tt) * sb.v_ts + row0 + rr] = so[tt][rr];
       }
     }
-    // The next chunk's staging writes sk/sq/sv/gates only; so[] is rewritten
-    // after two more barriers, so no barrier is needed here.
+    if (!more) break;
+    // next chunk into LDS: sk/sq/sv/gates/block coefficients were last read in
+    // phase C, before the barrier above; z is double-buffered because phase D
+    // may still be reading this chunk's slot in other waves.
+    chunk_store(P, (int)((T - t0 - TC) < TC ? (T - t0 - TC) : TC), (int)((c + 1) & 1));
   }
 
 #pragma unroll
@@ -579,7 +825,8 @@ __global__ __launch_bounds__(NW* kWave) void scan_kernel(ScanArgs a) {
     const int row = row0 + (wave * RPL + r) * RG + g;
 #pragma unroll
     for (int m = 0; m < NV4; ++m)
-      *reinterpret_cast<float4*>(a.s_out + sbase + row * D + 4 * (m * CL + j)) = S[r][m];
+      *reinterpret_cast<float4*>(a.s_out + sbase + row * D + 4 * (m * CL + j)) =
+          scale4(St[r][m], gsc);
   }
 }
 
@@ -660,16 +907,16 @@ int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v,
   }
 }
 
-template <int DT, int D, int CL, int RPL, int NW, int TC>
+template <int DT, int GT, int D, int CL, int RPL, int NW, int TC, int L>
 int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
   constexpr int ROWS = NW * (kWave / CL) * RPL;
   a.nrb = D / ROWS;
   const dim3 grid((unsigned)(heads * a.nrb));
   if constexpr (ROWS == D) {
-    scan_kernel<DT, D, CL, RPL, NW, TC, true><<<grid, NW * kWave, 0, st>>>(a);
+    scan_kernel<DT, GT, D, CL, RPL, NW, TC, L, true><<<grid, NW * kWave, 0, st>>>(a);
     return device_status("scan_kernel launch");
   } else {
-    scan_kernel<DT, D, CL, RPL, NW, TC, false><<<grid, NW * kWave, 0, st>>>(a);
+    scan_kernel<DT, GT, D, CL, RPL, NW, TC, L, false><<<grid, NW * kWave, 0, st>>>(a);
     int rc = device_status("scan_kernel launch");
     if (rc != GDN_OK || a.z == nullptr) return rc;
     const int64_t nvec = heads * a.T;
@@ -679,21 +926,30 @@ int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
   }
 }
 
-template <int DT>
+template <int DT, int GT>
 int launch_scan_dt(const ScanArgs& a, int D, int64_t heads, hipStream_t st) {
   switch (D) {
     case 128:
       // enough heads to fill the chip with whole-head workgroups: keep the
       // norm fused; otherwise split each head's rows over more workgroups
-      if (heads >= 512) return launch_scan_cfg<DT, 128, 4, 2, 4, 16>(a, heads, st);
-      if (heads >= 128) return launch_scan_cfg<DT, 128, 8, 1, 4, 16>(a, heads, st);
-      return launch_scan_cfg<DT, 128, 16, 1, 4, 16>(a, heads, st);
+      if (heads >= 512) return launch_scan_cfg<DT, GT, 128, 4, 2, 4, 16, 1>(a, heads, st);
+      if (heads >= 128) return launch_scan_cfg<DT, GT, 128, 8, 1, 4, 16, 1>(a, heads, st);
+      return launch_scan_cfg<DT, GT, 128, 16, 1, 4, 32, 1>(a, heads, st);
     case 64:
-      if (heads >= 256) return launch_scan_cfg<DT, 64, 4, 1, 4, 32>(a, heads, st);
-      return launch_scan_cfg<DT, 64, 8, 1, 2, 32>(a, heads, st);
-    case 32: return launch_scan_cfg<DT, 32, 4, 1, 2, 32>(a, heads, st);
-    case 16: return launch_scan_cfg<DT, 16, 4, 1, 1, 32>(a, heads, st);
+      if (heads >= 256) return launch_scan_cfg<DT, GT, 64, 4, 1, 4, 32, 1>(a, heads, st);
+      return launch_scan_cfg<DT, GT, 64, 8, 1, 2, 32, 1>(a, heads, st);
+    case 32: return launch_scan_cfg<DT, GT, 32, 4, 1, 2, 32, 1>(a, heads, st);
+    case 16: return launch_scan_cfg<DT, GT, 16, 4, 1, 1, 32, 1>(a, heads, st);
     default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
+  }
+}
+
+template <int DT>
+int launch_scan_gt(const ScanArgs& a, int gdt, int D, int64_t heads, hipStream_t st) {
+  switch (gdt) {
+    case GDN_F32: return launch_scan_dt<DT, GDN_F32>(a, D, heads, st);
+    case GDN_F16: return launch_scan_dt<DT, GDN_F16>(a, D, heads, st);
+    default: return launch_scan_dt<DT, GDN_BF16>(a, D, heads, st);
   }
 }
 
@@ -705,9 +961,9 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
                    d.qk_eps, d.norm_eps, q_scale(d)};
   const int64_t heads = d.B * d.Hv;
   switch (d.dtype) {
-    case GDN_F32: return launch_scan_dt<GDN_F32>(a, (int)d.Dk, heads, st);
-    case GDN_F16: return launch_scan_dt<GDN_F16>(a, (int)d.Dk, heads, st);
-    default: return launch_scan_dt<GDN_BF16>(a, (int)d.Dk, heads, st);
+    case GDN_F32: return launch_scan_gt<GDN_F32>(a, d.gate_dtype, (int)d.Dk, heads, st);
+    case GDN_F16: return launch_scan_gt<GDN_F16>(a, d.gate_dtype, (int)d.Dk, heads, st);
+    default: return launch_scan_gt<GDN_BF16>(a, d.gate_dtype, (int)d.Dk, heads, st);
   }
 }
 
