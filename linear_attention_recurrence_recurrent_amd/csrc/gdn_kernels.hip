@@ -418,6 +418,11 @@ struct ScanBases {
 // Smallest and largest decay scale kept folded: outside [2^-30, 2^30] the
 // state is brought back to scale 1 (and alpha == 0 always lands here).
 constexpr float kFoldMin = 9.3132257e-10f, kFoldMax = 1.0737418e9f;
+// Range of a chunk's running decay product for the unchecked chunk loop: the
+// state is brought to scale 1 at every chunk start, so the scale inside the
+// chunk is exactly this product; [2^-60, 2^60] keeps every folded quantity far
+// from f32 overflow and underflow.
+constexpr float kFastMin = 8.6736174e-19f, kFastMax = 1.1529215e18f;
 
 // The scan processes the time axis in chunks of TC tokens staged through LDS,
 // and each chunk in blocks of L tokens.  Within a block the recurrence is
@@ -441,6 +446,9 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
   constexpr int NB = TC / L;  // blocks per chunk
   constexpr int NPB = L * (L - 1);  // off-diagonal Gram entries per block (k.k and k.q)
   constexpr bool KEEP_K = L * NV4 <= 8;  // keep the block's k columns for the update
+  // Row-split shapes (one wave per SIMD, latency-bound) get a fully unrolled,
+  // unchecked token loop for chunks whose decay products stay in range.
+  constexpr bool UNROLL = !FUSE_NORM && L == 1 && NV4 * RPL <= 2;
   static_assert(NCOL % 4 == 0, "a lane owns whole float4 chunks");
   static_assert(D % ROWS == 0 && ROWS % 2 == 0, "row blocks tile the head");
   static_assert(!FUSE_NORM || ROWS == D, "the fused norm needs the whole head");
@@ -453,6 +461,7 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
   __shared__ float so[TC][ROWS];
   __shared__ float sal[TC], sbe[TC], skq[TC];
   __shared__ float sP[NB][L][L], sQ[NB][L][L], sA[NB][L + 1], sR[NB][L], sAmin[NB], sAmax[NB];
+  __shared__ int sfast;  // the chunk's decay products stay inside the folding range
 
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int rb = (int)(tile % a.nrb);
@@ -590,6 +599,15 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
     }
     const bool more = t0 + TC < T;
     if (more) chunk_load(P, t0 + TC, (int)((T - t0 - TC) < TC ? (T - t0 - TC) : TC));
+    if (tid == 0) {  // range of the chunk's running decay product (padding has alpha = 1)
+      float acc = 1.f;
+      bool ok = true;
+      for (int tt = 0; tt < TC; ++tt) {
+        acc *= sal[tt];
+        ok = ok && acc >= kFastMin && acc <= kFastMax;
+      }
+      sfast = ok ? 1 : 0;
+    }
     if constexpr (L > 1) {
       __syncthreads();
       // B2. per-block coefficients shared by every row: the off-diagonal Gram
@@ -639,61 +657,140 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
     //    gsc *= A_L: one FMA per state element per token.  When the scale
     //    would leave [2^-30, 2^30] (and whenever an alpha is 0) St is brought
     //    to the block's end scale in place and the scale restarts at 1.
-    if constexpr (L == 1) {
-      // one token at a time: St += (coef/gsc') k with gsc' = alpha*gsc
-      for (int tt = 0; tt < tc; ++tt) {
-        const float al = sal[tt], be = sbe[tt], kq = skq[tt];
-        const float gn = gsc * al;
-        const bool rescale = !(gn >= kFoldMin && gn <= kFoldMax);  // uniform, rare
-        const float gnext = rescale ? 1.f : gn;
-        const float ig = rescale ? 1.f : __builtin_amdgcn_rcpf(gn);
-        float4 kc[NV4];
-        float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
+    // Bring the state to scale 1 at the chunk start (one multiply per element
+    // per chunk); when the chunk's decay products stay in range the whole chunk
+    // then runs without per-token range checks.
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
+    for (int r = 0; r < RPL; ++r)
 #pragma unroll
-        for (int m = 0; m < NV4; ++m) {
-          kc[m] = sk[tt][m * CL + j];
-          const float4 qc = sq[tt][m * CL + j];
+      for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gsc);
+    gsc = 1.f;
+    auto checked_tokens = [&]() {
+        // one token at a time with range checks: St += (coef/gsc') k with
+        // gsc' = alpha*gsc, or a rescale of St when gsc' leaves the range
+        for (int tt = 0; tt < tc; ++tt) {
+          const float al = sal[tt], be = sbe[tt], kq = skq[tt];
+          const float gn = gsc * al;
+          const bool rescale = !(gn >= kFoldMin && gn <= kFoldMax);  // uniform, rare
+          const float gnext = rescale ? 1.f : gn;
+          const float ig = rescale ? 1.f : __builtin_amdgcn_rcpf(gn);
+          float4 kc[NV4];
+          float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
 #pragma unroll
-          for (int r = 0; r < RPL; ++r) {
-            if (m & 1) {
-              u1[r] = dot4(St[r][m], kc[m], u1[r]);
-              w1[r] = dot4(St[r][m], qc, w1[r]);
-            } else {
-              u0[r] = dot4(St[r][m], kc[m], u0[r]);
-              w0[r] = dot4(St[r][m], qc, w0[r]);
-            }
-          }
-        }
-        float c2[RPL];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          const int lr = (wave * RPL + r) * RG + g;
-          const float u = group_sum<CL>(u0[r] + u1[r]) * gsc;
-          const float wq = group_sum<CL>(w0[r] + w1[r]) * gsc;
-          const float coef = be * (sv[tt][lr] - al * u);
-          if (j == 0) so[tt][lr] = al * wq + coef * kq;
-          c2[r] = coef * ig;
-        }
-        if (rescale) {
-#pragma unroll
-          for (int r = 0; r < RPL; ++r)
-#pragma unroll
-            for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gn);
-        }
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
+          for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
 #pragma unroll
           for (int m = 0; m < NV4; ++m) {
-            St[r][m].x = fmaf(c2[r], kc[m].x, St[r][m].x);
-            St[r][m].y = fmaf(c2[r], kc[m].y, St[r][m].y);
-            St[r][m].z = fmaf(c2[r], kc[m].z, St[r][m].z);
-            St[r][m].w = fmaf(c2[r], kc[m].w, St[r][m].w);
+            kc[m] = sk[tt][m * CL + j];
+            const float4 qc = sq[tt][m * CL + j];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+              if (m & 1) {
+                u1[r] = dot4(St[r][m], kc[m], u1[r]);
+                w1[r] = dot4(St[r][m], qc, w1[r]);
+              } else {
+                u0[r] = dot4(St[r][m], kc[m], u0[r]);
+                w0[r] = dot4(St[r][m], qc, w0[r]);
+              }
+            }
+          }
+          float c2[RPL];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) {
+            const int lr = (wave * RPL + r) * RG + g;
+            const float u = group_sum<CL>(u0[r] + u1[r]) * gsc;
+            const float wq = group_sum<CL>(w0[r] + w1[r]) * gsc;
+            const float coef = be * (sv[tt][lr] - al * u);
+            if (j == 0) so[tt][lr] = al * wq + coef * kq;
+            c2[r] = coef * ig;
+          }
+          if (rescale) {
+#pragma unroll
+            for (int r = 0; r < RPL; ++r)
+#pragma unroll
+              for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gn);
+          }
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+            for (int m = 0; m < NV4; ++m) {
+              St[r][m].x = fmaf(c2[r], kc[m].x, St[r][m].x);
+              St[r][m].y = fmaf(c2[r], kc[m].y, St[r][m].y);
+              St[r][m].z = fmaf(c2[r], kc[m].z, St[r][m].z);
+              St[r][m].w = fmaf(c2[r], kc[m].w, St[r][m].w);
+            }
+          }
+          gsc = gnext;
+        }
+    };
+    if constexpr (UNROLL) {
+      if (sfast != 0) {
+      // one token at a time, unchecked: St += (coef/g_t) k with g_t the running
+        // decay product; short chunks are padded with identity tokens
+        float obuf[UNROLL ? TC : 1][RPL];
+#pragma unroll(UNROLL ? TC : 1)
+        for (int tt = 0; tt < (UNROLL ? TC : tc); ++tt) {
+          const float al = sal[tt], be = sbe[tt], kq = skq[tt];
+          const float gn = gsc * al;
+          const float ig = __builtin_amdgcn_rcpf(gn);
+          float4 kc[NV4];
+          float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
+#pragma unroll
+          for (int m = 0; m < NV4; ++m) {
+            kc[m] = sk[tt][m * CL + j];
+            const float4 qc = sq[tt][m * CL + j];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+              if (m & 1) {
+                u1[r] = dot4(St[r][m], kc[m], u1[r]);
+                w1[r] = dot4(St[r][m], qc, w1[r]);
+              } else {
+                u0[r] = dot4(St[r][m], kc[m], u0[r]);
+                w0[r] = dot4(St[r][m], qc, w0[r]);
+              }
+            }
+          }
+          float c2[RPL];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) {
+            const int lr = (wave * RPL + r) * RG + g;
+            const float u = group_sum<CL>(u0[r] + u1[r]) * gsc;
+            const float wq = group_sum<CL>(w0[r] + w1[r]) * gsc;
+            const float coef = be * (sv[tt][lr] - al * u);
+            const float o = al * wq + coef * kq;
+            if constexpr (UNROLL) {
+              obuf[tt][r] = o;
+            } else {
+              if (j == 0) so[tt][lr] = o;
+            }
+            c2[r] = coef * ig;
+          }
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+            for (int m = 0; m < NV4; ++m) {
+              St[r][m].x = fmaf(c2[r], kc[m].x, St[r][m].x);
+              St[r][m].y = fmaf(c2[r], kc[m].y, St[r][m].y);
+              St[r][m].z = fmaf(c2[r], kc[m].z, St[r][m].z);
+              St[r][m].w = fmaf(c2[r], kc[m].w, St[r][m].w);
+            }
+          }
+          gsc = gn;
+        }
+        if constexpr (UNROLL) {
+          if (j == 0) {
+#pragma unroll
+            for (int tt = 0; tt < TC; ++tt)
+#pragma unroll
+              for (int r = 0; r < RPL; ++r) so[tt][(wave * RPL + r) * RG + g] = obuf[tt][r];
           }
         }
-        gsc = gnext;
+      } else {
+        checked_tokens();
       }
+    } else if constexpr (L == 1) {
+      checked_tokens();
     } else {
       for (int bk = 0; bk < nblk; ++bk) {
         const int tb = bk * L;
@@ -934,7 +1031,7 @@ int launch_scan_dt(const ScanArgs& a, int D, int64_t heads, hipStream_t st) {
       // norm fused; otherwise split each head's rows over more workgroups
       if (heads >= 512) return launch_scan_cfg<DT, GT, 128, 4, 2, 4, 16, 1>(a, heads, st);
       if (heads >= 128) return launch_scan_cfg<DT, GT, 128, 8, 1, 4, 16, 1>(a, heads, st);
-      return launch_scan_cfg<DT, GT, 128, 16, 1, 4, 32, 1>(a, heads, st);
+      return launch_scan_cfg<DT, GT, 128, 16, 1, 4, 16, 1>(a, heads, st);
     case 64:
       if (heads >= 256) return launch_scan_cfg<DT, GT, 64, 4, 1, 4, 32, 1>(a, heads, st);
       return launch_scan_cfg<DT, GT, 64, 8, 1, 2, 32, 1>(a, heads, st);
