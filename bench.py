@@ -37,8 +37,9 @@ METRIC = "GDN decode state GB/s + scan tokens/s, % of MI355X HBM/FP32 roofline"
 HBM_PEAK_GBS = 8000.0
 FP32_VALU_PEAK_TFLOPS = 157.3
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_b64_counters.txt")
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrence_recurrent_amd", "csrc",
-                          "gdn_kernels.hip")
+# sources the decode kernel is built from: its counters are stale once these change
+DECODE_SRC = [os.path.join(ROOT, "linear_attention_recurrence_recurrent_amd", "csrc", f)
+              for f in ("gdn_decode.hip", "gdn_device.h")]
 
 
 def log(msg):
@@ -46,7 +47,10 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in DECODE_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_counters():

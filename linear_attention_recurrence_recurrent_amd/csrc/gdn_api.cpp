@@ -1,0 +1,42 @@
+// C-ABI entry points (include/gdn.h): validate, then enqueue the kernels.
+#include <hip/hip_runtime.h>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+#include "gdn_launch.h"
+
+extern "C" {
+
+int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const void* v,
+                       const void* log_decay, const void* beta, const float* s0, const void* z,
+                       const void* w, float* y, float* s_out, void* stream) {
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+  if (rc != GDN_OK) return rc;
+  if (d->T != 1) {
+    gdn::set_error("gdn_recurrent_step needs T == 1 (use gdn_scan for a time axis)");
+    return GDN_EUNSUPPORTED;
+  }
+  if (d->B == 0) return GDN_OK;
+  return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
+}
+
+int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
+             const void* log_decay, const void* beta, const float* s0, const void* z,
+             const void* w, float* y, float* s_out, void* stream) {
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+  if (rc != GDN_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d->B == 0) return GDN_OK;
+  if (d->T == 0) {
+    if (s_out == s0) return GDN_OK;
+    const size_t bytes = (size_t)(d->B * d->Hv * d->Dv * d->Dk) * sizeof(float);
+    if (hipMemcpyAsync(s_out, s0, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return gdn::device_status("state copy for T == 0");
+    return GDN_OK;
+  }
+  if (d->T == 1)  // one token: the decode kernel is the same computation, streamed once
+    return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
+  return gdn::launch_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
+}
+
+}  // extern "C"

@@ -13,4 +13,13 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
 // Replace the thread's last-error text.
 void set_error(const char* msg);
 
+// Launchers (validated arguments; stream is a hipStream_t).  They return GDN_OK,
+// GDN_EUNSUPPORTED or GDN_EDEVICE.
+int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
+                const void* beta, const float* s0, const void* z, const void* w, float* y,
+                float* s_out, void* stream);
+int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
+                const void* beta, const float* s0, const void* z, const void* w, float* y,
+                float* s_out, void* stream);
+
 }  // namespace gdn

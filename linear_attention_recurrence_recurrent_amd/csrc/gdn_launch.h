@@ -1,0 +1,29 @@
+// Host-side helpers shared by the launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// GDN_OK, or GDN_EDEVICE with the HIP error text as the thread's last error.
+inline int device_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return GDN_OK;
+  char msg[200];
+  std::snprintf(msg, sizeof(msg), "%s: %s", what, hipGetErrorString(e));
+  set_error(msg);
+  return GDN_EDEVICE;
+}
+
+// Scale folded into q-hat: 1/sqrt(Dk) when GDN_FOLD_Q_SCALE is set.
+inline float q_scale(const gdn_desc& d) {
+  return (d.flags & GDN_FOLD_Q_SCALE) ? 1.0f / std::sqrt((float)d.Dk) : 1.0f;
+}
+
+}  // namespace gdn

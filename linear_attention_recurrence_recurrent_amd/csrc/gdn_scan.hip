@@ -1,391 +1,21 @@
-// Gated DeltaNet recurrence on MI355X (gfx950): decode step, time-axis scan
-// and gated RMSNorm kernels, plus the C-ABI entry points that launch them.
+// Time-axis scan of the Gated DeltaNet recurrence on MI355X (gfx950), and the
+// standalone gated RMSNorm used when a head's rows are split over workgroups.
 //
-// Recurrence ("Module gdn" page, module description), per value head with a
-// D x D float32 memory S (row a = value lane, column c = key lane):
-//     u = S.k ;  S = alpha*S + beta*(v - alpha*u) k^T ;  o = S.q (updated S)
-//     y = rmsnorm(o * silu(z)) * w        (gate first, then normalise)
-// Fused row pass ("Module gdn" page, "The fusion"): because the update is
-// affine in S, o[a] = alpha*(S_old.q)[a] + coef[a]*(k.q) with
-// coef[a] = beta*(v[a] - alpha*u[a]).  One pass over a state row held in
-// registers yields both dots; the row is then rewritten from the same
-// registers, so each row is read once and written once per token.
-//
-// Work layout on CDNA4 (wave64):
-//   - a row of D columns is split over CL consecutive lanes ("row group");
-//     lane j of the group owns the float4 column chunks j, j+CL, j+2CL, ...,
-//     so a wave-wide float4 access of one chunk index touches CL contiguous
-//     16-byte pieces per row;
-//   - the two dots are reduced inside the row group with DPP butterflies
-//     (quad_perm, row_half_mirror, row_mirror), which leave the same sum in
-//     every lane of the group, so every lane updates its own columns with an
-//     identical coef;
-//   - a lane owns RPL rows, a wave 64/CL*RPL rows, a workgroup of NW waves
-//     ROWS = NW*(64/CL)*RPL rows of one value head.
-// Decode: a workgroup owns a whole head, streams its rows from HBM with
-// nontemporal loads/stores (all loads of a lane issued before any math), and
-// applies the gated RMSNorm in the same launch.
-// Scan: the state stays in VGPRs for the whole time axis; q/k/v/gates are
-// staged through LDS in chunks of TC tokens, q/k are normalised once per
-// token per workgroup, and the outputs of a chunk are buffered in LDS and
-// written back coalesced (gated in the same launch when the workgroup owns
-// the whole head, else by the separate gated-norm kernel).
-#include <hip/hip_runtime.h>
-
-#include <cmath>
-#include <type_traits>
-#include <cstdint>
-#include <cstdio>
-
-#include "gdn.h"
-#include "gdn_internal.h"
+// The recurrence is the one of the "Module gdn" page (module description),
+// fused per row as in its section "The fusion"; the scan covers the time axis
+// as the "gated_delta" page's gated_delta_reference does, returning
+// (output, final_state).  The state stays in VGPRs for the whole time axis;
+// q/k/v/gates are staged through LDS in chunks of TC tokens (the next chunk
+// loads into registers while the current one computes); q/k are normalised
+// once per token per workgroup; outputs are buffered in LDS and written back
+// coalesced, gated in the same launch when the workgroup owns the whole head.
+// Rows are split over lanes exactly as in the decode kernel.
+#include "gdn_device.h"
+#include "gdn_launch.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kWave = 64;
-
-// ------------------------------------------------------------------ loads
-
-// Compile-time dtype versions for the operand loads of the kernels.  ld4 reads
-// four consecutive elements starting at i (i is a multiple of 4 and the base
-// pointer is 16-byte aligned, so the access is 16 or 8 bytes aligned).
-template <int DT>
-__device__ __forceinline__ float ld1(const void* p, int64_t i) {
-  if constexpr (DT == GDN_F32) return static_cast<const float*>(p)[i];
-  const uint16_t h = static_cast<const uint16_t*>(p)[i];
-  if constexpr (DT == GDN_F16) return (float)__builtin_bit_cast(_Float16, h);
-  return __uint_as_float((uint32_t)h << 16);
-}
-
-template <int DT>
-__device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
-  if constexpr (DT == GDN_F32) {
-    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-  } else {
-    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
-    if constexpr (DT == GDN_F16) {
-      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-      const half4_t h = __builtin_bit_cast(half4_t, r);
-      return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
-    } else {
-      return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                         __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
-    }
-  }
-}
-
-__device__ __forceinline__ float dot4(const float4 a, const float4 b, float acc) {
-  acc = fmaf(a.x, b.x, acc);
-  acc = fmaf(a.y, b.y, acc);
-  acc = fmaf(a.z, b.z, acc);
-  return fmaf(a.w, b.w, acc);
-}
-
-__device__ __forceinline__ float4 scale4(const float4 a, float s) {
-  return make_float4(a.x * s, a.y * s, a.z * s, a.w * s);
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// Streaming (nontemporal) 16-byte state accesses: the state is touched once per
-// decode step, so it should not displace other lines from the caches.
-typedef float v4f __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 nt_load4(const float* p) {
-  const v4f r = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
-  return make_float4(r.x, r.y, r.z, r.w);
-}
-__device__ __forceinline__ void nt_store4(const float4 s, float* p) {
-  const v4f r = {s.x, s.y, s.z, s.w};
-  __builtin_nontemporal_store(r, reinterpret_cast<v4f*>(p));
-}
-
-// ------------------------------------------------------------------ lane reductions
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over each aligned group of CL consecutive lanes (CL = 1, 2, 4, 8, 16).
-// Butterfly order: every lane of a group ends with bit-identical sums.
-template <int CL>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(CL == 1 || CL == 2 || CL == 4 || CL == 8 || CL == 16, "row group size");
-  if constexpr (CL >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-  if constexpr (CL >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (CL >= 8) x += dpp<0x141>(x);  // row_half_mirror: the other quad of 8
-  if constexpr (CL >= 16) x += dpp<0x140>(x); // row_mirror: the other half of 16
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-  x = group_sum<16>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
-// XCD receives a contiguous range of tiles (the row blocks of one head, and
-// the value heads of one key group, then share an L2).
-__device__ __forceinline__ int64_t xcd_tile(int64_t i, int64_t n) {
-  if (n % 8) return i;
-  return (i % 8) * (n / 8) + i / 8;
-}
-
-// ------------------------------------------------------------------ decode step
-struct StepArgs {
-  const void *q, *k, *v, *ld, *beta, *z, *w;
-  const float* s0;
-  float* y;
-  float* s_out;
-  int Hk, Hv, G, dt, gdt;
-  uint32_t flags;
-  float qk_eps, norm_eps, qscale;
-};
-
-// N consecutive operand elements kept as their raw bits (16-bit dtypes stay
-// packed two per VGPR) and widened to f32 on use.  N = 1, 2 or 4; the access
-// is N elements wide, so the element index must be a multiple of N.
-template <int DT, int N>
-struct Raw {
-  static_assert(N == 1 || N == 2 || N == 4, "Raw holds 1, 2 or 4 elements");
-  static constexpr bool kF32 = DT == GDN_F32;
-  typedef typename std::conditional<kF32, float, uint32_t>::type Word;
-  static constexpr int kWords = kF32 ? N : (N + 1) / 2;
-  Word w[kWords];
-  __device__ __forceinline__ void load(const void* p, int64_t i) {
-    if constexpr (kF32) {
-      const float* f = static_cast<const float*>(p) + i;
-      if constexpr (N == 4) {
-        const float4 t = *reinterpret_cast<const float4*>(f);
-        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
-      } else if constexpr (N == 2) {
-        const float2 t = *reinterpret_cast<const float2*>(f);
-        w[0] = t.x; w[1] = t.y;
-      } else {
-        w[0] = f[0];
-      }
-    } else {
-      const uint16_t* h = static_cast<const uint16_t*>(p) + i;
-      if constexpr (N == 4) {
-        const uint2 t = *reinterpret_cast<const uint2*>(h);
-        w[0] = t.x; w[1] = t.y;
-      } else if constexpr (N == 2) {
-        w[0] = *reinterpret_cast<const uint32_t*>(h);
-      } else {
-        w[0] = h[0];
-      }
-    }
-  }
-  __device__ __forceinline__ float get(int k) const {
-    if constexpr (kF32) {
-      return w[k];
-    } else if constexpr (DT == GDN_BF16) {
-      return __uint_as_float((k & 1) ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
-    } else {
-      const uint16_t bits = (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xffffu));
-      return (float)__builtin_bit_cast(_Float16, bits);
-    }
-  }
-  __device__ __forceinline__ float4 get4(int c) const {  // elements 4c .. 4c+3
-    return make_float4(get(4 * c), get(4 * c + 1), get(4 * c + 2), get(4 * c + 3));
-  }
-};
-
-// Registers of one head in flight: this lane's columns of q and k (raw), its
-// RPL state rows (adjacent rows, float4 chunks), and its rows' v and z (raw).
-template <int DT, int D, int CL, int RPL>
-struct HeadRegs {
-  static constexpr int NV4 = D / CL / 4;
-  Raw<DT, 4> k[NV4], q[NV4];
-  float4 S[RPL][NV4];
-  Raw<DT, RPL> v, z;
-  float ld, be;
-};
-
-// Lane layout of the decode: row group g of a wave owns rows
-// (wave*RG + g)*RPL ... +RPL-1; lane j of the group owns float4 chunks j, j+CL, ...
-template <int CL, int RPL>
-__device__ __forceinline__ int decode_row0() {
-  constexpr int RG = kWave / CL;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  return (wave * RG + lane / CL) * RPL;
-}
-
-// Issue every load of one head.  The small operands go first: loads complete
-// in issue order, so the q/k norms can start while the state is in flight.
-template <int DT, int GT, int D, int CL, int RPL, int NW>
-__device__ __forceinline__ void decode_fetch(const StepArgs& a, int64_t head,
-                                             HeadRegs<DT, D, CL, RPL>& R) {
-  constexpr int NV4 = D / CL / 4;
-  const int j = threadIdx.x % CL;
-  const int row0 = decode_row0<CL, RPL>();
-  const int64_t b = head / a.Hv;
-  const int hv = (int)(head % a.Hv), hk = hv / a.G;
-  R.ld = ld1<GT>(a.ld, head);  // T == 1: gates are [B, Hv] in both layouts
-  R.be = ld1<GT>(a.beta, head);
-  const int64_t qk = (b * a.Hk + hk) * D;  // T == 1: both layouts coincide
-#pragma unroll
-  for (int m = 0; m < NV4; ++m) {
-    R.k[m].load(a.k, qk + 4 * (m * CL + j));
-    R.q[m].load(a.q, qk + 4 * (m * CL + j));
-  }
-  const float* s0 = a.s0 + head * (int64_t)(D * D);
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-#pragma unroll
-    for (int m = 0; m < NV4; ++m) R.S[r][m] = nt_load4(s0 + (row0 + r) * D + 4 * (m * CL + j));
-  }
-  R.v.load(a.v, head * D + row0);
-  if (a.z) R.z.load(a.z, head * D + row0);
-}
-
-// Fold the norms, run the fused row pass, write the state back and the
-// (gated) output.  The L2 norms and the q scale are applied to the reduced
-// dots as scalars (u = rk*(S.k), w = rq*(S.q), S += (coef*rk) k), so the
-// normalised vectors are never materialised.  red[NW] is this head's slot for
-// the cross-wave sum of the gated norm.
-template <int DT, int GT, int D, int CL, int RPL, int NW>
-__device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
-                                              HeadRegs<DT, D, CL, RPL>& R, float* red) {
-  constexpr int NV4 = D / CL / 4;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int j = lane % CL;
-  const int row0 = decode_row0<CL, RPL>();
-
-  // the row group covers all D columns: its sums are the full norms and k.q
-  float skk = 0.f, sqq = 0.f, skq = 0.f;
-#pragma unroll
-  for (int m = 0; m < NV4; ++m) {
-    const float4 kf = R.k[m].get4(0), qf = R.q[m].get4(0);
-    skk = dot4(kf, kf, skk);
-    sqq = dot4(qf, qf, sqq);
-    skq = dot4(kf, qf, skq);
-  }
-  skk = group_sum<CL>(skk);
-  sqq = group_sum<CL>(sqq);
-  skq = group_sum<CL>(skq);
-  float rk = 1.f, rq = a.qscale;
-  if (a.flags & GDN_FOLD_QK_L2NORM) {
-    rk = rsqrtf(skk + a.qk_eps);
-    rq *= rsqrtf(sqq + a.qk_eps);
-  }
-  const float kq = skq * rk * rq;
-  const float al = expf(R.ld), be = R.be;
-
-  // both dots of every row from the registers
-  float u[RPL], w[RPL];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) u[r] = w[r] = 0.f;
-#pragma unroll
-  for (int m = 0; m < NV4; ++m) {
-    const float4 kf = R.k[m].get4(0), qf = R.q[m].get4(0);
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      u[r] = dot4(R.S[r][m], kf, u[r]);
-      w[r] = dot4(R.S[r][m], qf, w[r]);
-    }
-  }
-  float o[RPL], ck[RPL];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const float ur = group_sum<CL>(u[r]) * rk;
-    const float wr = group_sum<CL>(w[r]) * rq;
-    const float coef = be * (R.v.get(r) - al * ur);
-    o[r] = al * wr + coef * kq;
-    ck[r] = coef * rk;  // coefficient of the raw k in the update
-  }
-  // S = alpha*S + coef*k^, written back from the registers
-  float* so = a.s_out + head * (int64_t)(D * D);
-#pragma unroll
-  for (int m = 0; m < NV4; ++m) {
-    const float4 kf = R.k[m].get4(0);
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      float4 s = R.S[r][m];
-      s.x = fmaf(ck[r], kf.x, al * s.x);
-      s.y = fmaf(ck[r], kf.y, al * s.y);
-      s.z = fmaf(ck[r], kf.z, al * s.z);
-      s.w = fmaf(ck[r], kf.w, al * s.w);
-      nt_store4(s, so + (row0 + r) * D + 4 * (m * CL + j));
-    }
-  }
-
-  // output: raw o, or the gated RMSNorm over the whole head
-  float* y = a.y + head * D + row0;
-  if (a.z != nullptr) {
-    float ss = 0.f;
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      o[r] *= silu(R.z.get(r));
-      ss = fmaf(o[r], o[r], ss);
-    }
-    ss = wave_sum(j == 0 ? ss : 0.f);  // every lane of a group holds the same rows
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) tot += red[i];
-    const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
-    Raw<DT, RPL> wr;
-    wr.load(a.w, row0);
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) o[r] *= inv * wr.get(r);
-  }
-  if (j == 0) {
-    if constexpr (RPL == 4) {
-      *reinterpret_cast<float4*>(y) = make_float4(o[0], o[1], o[2], o[3]);
-    } else if constexpr (RPL == 2) {
-      *reinterpret_cast<float2*>(y) = make_float2(o[0], o[1]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) y[r] = o[r];
-    }
-  }
-}
-
-// One workgroup per head (b, hv): every state row of the head is read once
-// and written once.  Heads are taken in launch order: for this pure stream
-// the plain order spreads the concurrent workgroups' addresses over the HBM
-// channels better than grouping contiguous head ranges per XCD (measured).
-template <int DT, int GT, int D, int CL, int RPL, int NW>
-__global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
-  static_assert((D / CL) % 4 == 0, "a lane owns whole float4 chunks");
-  static_assert(NW * (kWave / CL) * RPL == D, "a workgroup owns the whole head");
-  __shared__ float red[NW];
-  const int64_t head = blockIdx.x;
-  HeadRegs<DT, D, CL, RPL> R;
-  decode_fetch<DT, GT, D, CL, RPL, NW>(a, head, R);
-  decode_finish<DT, GT, D, CL, RPL, NW>(a, head, R, red);
-}
-
-// Persistent variant: a workgroup walks heads blockIdx.x, +gridDim.x, ... and
-// issues the loads of its next head before finishing the current one, so the
-// memory system stays busy through the arithmetic and the norm's barrier.
-template <int DT, int GT, int D, int CL, int RPL, int NW>
-__global__ __launch_bounds__(NW* kWave) void decode_persistent_kernel(StepArgs a, int64_t nheads) {
-  static_assert((D / CL) % 4 == 0, "a lane owns whole float4 chunks");
-  static_assert(NW * (kWave / CL) * RPL == D, "a workgroup owns the whole head");
-  // two slots: a head's slot is rewritten only after the next head's barrier
-  __shared__ float red[2][NW];
-  HeadRegs<DT, D, CL, RPL> A, B;
-  const int64_t stride = gridDim.x;
-  int64_t h = blockIdx.x;
-  if (h < nheads) decode_fetch<DT, GT, D, CL, RPL, NW>(a, h, A);
-  while (h < nheads) {
-    const int64_t h1 = h + stride;
-    if (h1 < nheads) decode_fetch<DT, GT, D, CL, RPL, NW>(a, h1, B);
-    decode_finish<DT, GT, D, CL, RPL, NW>(a, h, A, red[0]);
-    if (h1 >= nheads) break;
-    const int64_t h2 = h1 + stride;
-    if (h2 < nheads) decode_fetch<DT, GT, D, CL, RPL, NW>(a, h2, A);
-    decode_finish<DT, GT, D, CL, RPL, NW>(a, h1, B, red[1]);
-    h = h2;
-  }
-}
-
-// ------------------------------------------------------------------ scan
 struct ScanArgs {
   const void *q, *k, *v, *ld, *beta, *z, *w;
   const float* s0;
@@ -955,54 +585,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z
   }
 }
 
-// ------------------------------------------------------------------ launchers
-int device_status(const char* what) {
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess) return GDN_OK;
-  char msg[200];
-  std::snprintf(msg, sizeof(msg), "%s: %s", what, hipGetErrorString(e));
-  set_error(msg);
-  return GDN_EDEVICE;
-}
-
-float q_scale(const gdn_desc& d) {
-  return (d.flags & GDN_FOLD_Q_SCALE) ? 1.0f / std::sqrt((float)d.Dk) : 1.0f;
-}
-
-template <int DT, int GT>
-int launch_step_dt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(d.B * d.Hv));
-  switch (d.Dk) {
-    case 128: decode_kernel<DT, GT, 128, 8, 2, 8><<<grid, 8 * kWave, 0, st>>>(a); break;
-    case 64: decode_kernel<DT, GT, 64, 4, 2, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
-    case 32: decode_kernel<DT, GT, 32, 4, 1, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
-    case 16: decode_kernel<DT, GT, 16, 4, 1, 1><<<grid, 1 * kWave, 0, st>>>(a); break;
-    default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
-  }
-  return device_status("decode_kernel launch");
-}
-
-template <int DT>
-int launch_step_gt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
-  switch (d.gate_dtype) {
-    case GDN_F32: return launch_step_dt<DT, GDN_F32>(d, a, st);
-    case GDN_F16: return launch_step_dt<DT, GDN_F16>(d, a, st);
-    default: return launch_step_dt<DT, GDN_BF16>(d, a, st);
-  }
-}
-
-int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v,
-                const void* ld, const void* beta, const float* s0, const void* z, const void* w,
-                float* y, float* s_out, hipStream_t st) {
-  const StepArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, (int)d.Hk, (int)d.Hv,
-                   (int)(d.Hv / d.Hk), d.dtype, d.gate_dtype, d.flags, d.qk_eps, d.norm_eps,
-                   q_scale(d)};
-  switch (d.dtype) {
-    case GDN_F32: return launch_step_gt<GDN_F32>(d, a, st);
-    case GDN_F16: return launch_step_gt<GDN_F16>(d, a, st);
-    default: return launch_step_gt<GDN_BF16>(d, a, st);
-  }
-}
+}  // namespace
 
 template <int DT, int GT, int D, int CL, int RPL, int NW, int TC, int L>
 int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
@@ -1031,7 +614,7 @@ int launch_scan_dt(const ScanArgs& a, int D, int64_t heads, hipStream_t st) {
       // norm fused; otherwise split each head's rows over more workgroups
       if (heads >= 512) return launch_scan_cfg<DT, GT, 128, 4, 2, 4, 16, 1>(a, heads, st);
       if (heads >= 128) return launch_scan_cfg<DT, GT, 128, 8, 1, 4, 16, 1>(a, heads, st);
-      return launch_scan_cfg<DT, GT, 128, 16, 1, 4, 16, 1>(a, heads, st);
+      return launch_scan_cfg<DT, GT, 128, 16, 1, 4, 32, 1>(a, heads, st);
     case 64:
       if (heads >= 256) return launch_scan_cfg<DT, GT, 64, 4, 1, 4, 32, 1>(a, heads, st);
       return launch_scan_cfg<DT, GT, 64, 8, 1, 2, 32, 1>(a, heads, st);
@@ -1052,7 +635,8 @@ int launch_scan_gt(const ScanArgs& a, int gdt, int D, int64_t heads, hipStream_t
 
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
-                float* s_out, hipStream_t st) {
+                float* s_out, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
   const ScanArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, d.T, (int)d.Hk, (int)d.Hv,
                    (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags,
                    d.qk_eps, d.norm_eps, q_scale(d)};
@@ -1064,42 +648,4 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
   }
 }
 
-}  // namespace
 }  // namespace gdn
-
-extern "C" {
-
-int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const void* v,
-                       const void* log_decay, const void* beta, const float* s0, const void* z,
-                       const void* w, float* y, float* s_out, void* stream) {
-  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
-  if (rc != GDN_OK) return rc;
-  if (d->T != 1) {
-    gdn::set_error("gdn_recurrent_step needs T == 1 (use gdn_scan for a time axis)");
-    return GDN_EUNSUPPORTED;
-  }
-  if (d->B == 0) return GDN_OK;
-  return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out,
-                          static_cast<hipStream_t>(stream));
-}
-
-int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
-             const void* log_decay, const void* beta, const float* s0, const void* z,
-             const void* w, float* y, float* s_out, void* stream) {
-  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
-  if (rc != GDN_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (d->B == 0) return GDN_OK;
-  if (d->T == 0) {
-    if (s_out == s0) return GDN_OK;
-    const size_t bytes = (size_t)(d->B * d->Hv * d->Dv * d->Dk) * sizeof(float);
-    if (hipMemcpyAsync(s_out, s0, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
-      return gdn::device_status("state copy for T == 0");
-    return GDN_OK;
-  }
-  if (d->T == 1)  // one token: the decode kernel is the same computation, streamed once
-    return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, st);
-  return gdn::launch_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, st);
-}
-
-}  // extern "C"
