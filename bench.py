@@ -139,6 +139,31 @@ def bench_decode(args, torch):
                          "avg_launch_us": round(launch_s * 1e6, 3)})
     log("decode: %.3f ms per 100-step chain, %.1f us per launch, state %.1f GB/s" %
         (ms_per_chain, launch_s * 1e6, value))
+
+    # ablation: the literal three-pass step on the same chain (3 reads + 1 write of S)
+    calls3 = [Launcher("gdn_recurrent_step_three_pass", desc,
+                       [st["q"], st["k"], st["v"], st["log_decay"], st["beta"], state, st["z"], w,
+                        y, state], stream.cuda_stream) for st, y in zip(d_steps, ys)]
+    for c in calls3:
+        c()
+    torch.cuda.synchronize()
+    reps3 = max(1, args.steps // 4)
+    e0.record(stream)
+    for _ in range(reps3):
+        for c in calls3:
+            c()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms3 = e0.elapsed_time(e1) / reps3
+    step3_us = ms3 * 1e3 / wl.steps
+    res["ablation"] = {
+        "three_pass_us_per_step": round(step3_us, 2),
+        "three_pass_state_bytes_per_step": 2 * state_bytes,
+        "three_pass_gbs": round(2 * state_bytes / (step3_us * 1e-6) / 1e9, 1),
+        "fused_us_per_step": round(launch_s * 1e6, 2),
+        "fusion_speedup": round(step3_us / (launch_s * 1e6), 3)}
+    log("decode three-pass: %.1f us per step (fusion speedup %.2fx)" %
+        (step3_us, step3_us / (launch_s * 1e6)))
     return res, ops
 
 
@@ -265,6 +290,7 @@ def main():
                    "B": 64, "Hk": 16, "Hv": 32, "D": 128, "tokens_per_step": 100,
                    "parallelism": "single GPU"},
         "roofline": dec["roofline"],
+        "ablation_three_pass_decode": dec["ablation"],
     }
     if scan:
         out["scan"] = scan

@@ -98,6 +98,21 @@ int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const vo
                        const void* log_decay, const void* beta, const float* s0,
                        const void* z, const void* w, float* y, float* s_out, void* stream);
 
+/* The same step in its literal three-pass form ("Module gdn" page, "The
+ * fusion": written literally the step is three passes over S -- one for S.k,
+ * one for the rank-1 update, one for S.q), as three launches: u = S.k into
+ * the y buffer (reads S), the update (reads S, writes s_out), o = S.q on the
+ * updated state plus the output (reads s_out).  Same arguments and results
+ * as gdn_recurrent_step; it exists to measure the fusion's saving (three
+ * reads and one write of the state instead of one read and one write).
+ * The passes are ordered on `stream`, so s_out == s0 (in place) is allowed
+ * as for gdn_recurrent_step.  Supported for Dk == Dv == 128 only (else
+ * GDN_EUNSUPPORTED). */
+int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* k,
+                                  const void* v, const void* log_decay, const void* beta,
+                                  const float* s0, const void* z, const void* w, float* y,
+                                  float* s_out, void* stream);
+
 /* The recurrence over the whole time axis ("gated_delta" page,
  * gated_delta_reference: the recurrence over the time axis returning
  * (output, final_state)).  Any T >= 0; T == 0 copies s0 to s_out (unless

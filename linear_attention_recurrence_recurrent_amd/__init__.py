@@ -19,7 +19,8 @@ import torch
 from . import _native
 from ._native import GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GdnDesc
 
-__all__ = ["recurrent_step", "scan", "check", "abi_version", "GdnError"]
+__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "check", "abi_version",
+           "GdnError"]
 
 _DT = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
        torch.bfloat16: _native.GDN_BF16}
@@ -154,6 +155,24 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay:
     desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
                  qk_eps, norm_eps)
     _call("gdn_recurrent_step", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
+    return y, s_out
+
+
+def recurrent_step_three_pass(q, k, v, log_decay, beta, s0, z=None, w=None, *,
+                              head_major: bool = False, inplace: bool = False,
+                              fold_qk_l2norm: bool = True, fold_q_scale: bool = True,
+                              qk_eps: float = 1e-6, norm_eps: float = 1e-6, out=None):
+    """The decode step in its literal three-pass form (u = S.k, the update,
+    o = S.q as three launches, "Module gdn" page, "The fusion"); same results
+    as ``recurrent_step``, kept to measure the fusion's saving.  D == 128 only."""
+    B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
+    if s0 is None:
+        raise GdnError(1, "recurrent_step_three_pass needs s0")
+    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    s_out = s0 if inplace else torch.empty_like(s0)
+    desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
+                 qk_eps, norm_eps)
+    _call("gdn_recurrent_step_three_pass", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
     return y, s_out
 
 

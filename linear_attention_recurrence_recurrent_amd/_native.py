@@ -19,8 +19,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_ESHAPE", 3: "GDN_EDTYPE", 4: "GD
           5: "GDN_EUNSUPPORTED", 6: "GDN_EALIGN", 7: "GDN_EALIAS", 8: "GDN_EDEVICE"}
 
 # Every symbol include/gdn.h declares.
-EXPORTS = ("gdn_recurrent_step", "gdn_scan", "gdn_check", "gdn_last_error", "gdn_status_str",
-           "gdn_abi_version")
+EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan", "gdn_check",
+           "gdn_last_error", "gdn_status_str", "gdn_abi_version")
 
 
 class GdnDesc(ctypes.Structure):
@@ -47,7 +47,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp = ctypes.c_void_p
         dp = ctypes.POINTER(GdnDesc)
-        for name in ("gdn_recurrent_step", "gdn_scan"):
+        for name in ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan"):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [dp] + [vp] * 11

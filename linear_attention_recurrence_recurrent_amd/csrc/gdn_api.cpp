@@ -20,6 +20,20 @@ int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const vo
   return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
 }
 
+int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* k,
+                                  const void* v, const void* log_decay, const void* beta,
+                                  const float* s0, const void* z, const void* w, float* y,
+                                  float* s_out, void* stream) {
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+  if (rc != GDN_OK) return rc;
+  if (d->T != 1) {
+    gdn::set_error("gdn_recurrent_step_three_pass needs T == 1");
+    return GDN_EUNSUPPORTED;
+  }
+  if (d->B == 0) return GDN_OK;
+  return gdn::launch_step_three_pass(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
+}
+
 int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
              const void* log_decay, const void* beta, const float* s0, const void* z,
              const void* w, float* y, float* s_out, void* stream) {

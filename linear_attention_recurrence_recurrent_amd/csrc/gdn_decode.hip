@@ -202,6 +202,104 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
   decode_finish<DT, GT, D, CL, RPL, NW>(a, head, R, red);
 }
 
+// ---------------------------------------------------------------- three-pass form
+// The literal form of the step ("Module gdn" page, "The fusion": written
+// literally it is three passes over S), kept to measure what the fusion saves:
+//   pass 1: u = S.k^            (reads S; u goes to the y buffer)
+//   pass 2: S = alpha*S + beta*(v - alpha*u) k^T   (reads S, writes S)
+//   pass 3: o = S.q^ on the updated S, then the gated norm (reads S)
+// Each pass is its own launch over the whole state, as separate operators
+// with materialised outputs would be.
+template <int DT, int GT, int D, int CL, int RPL, int NW, int PASS>
+__global__ __launch_bounds__(NW* kWave) void threepass_kernel(StepArgs a) {
+  constexpr int NV4 = D / CL / 4;
+  __shared__ float red[NW];
+  const int64_t head = blockIdx.x;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int j = lane % CL;
+  const int row0 = decode_row0<CL, RPL>();
+  HeadRegs<DT, D, CL, RPL> R;
+  decode_fetch<DT, GT, D, CL, RPL, NW>(a, head, R);
+  float skk = 0.f, sqq = 0.f;
+#pragma unroll
+  for (int m = 0; m < NV4; ++m) {
+    const float4 kf = R.k[m].get4(0), qf = R.q[m].get4(0);
+    skk = dot4(kf, kf, skk);
+    sqq = dot4(qf, qf, sqq);
+  }
+  skk = group_sum<CL>(skk);
+  sqq = group_sum<CL>(sqq);
+  float rk = 1.f, rq = a.qscale;
+  if (a.flags & GDN_FOLD_QK_L2NORM) {
+    rk = rsqrtf(skk + a.qk_eps);
+    rq *= rsqrtf(sqq + a.qk_eps);
+  }
+  float* y = a.y + head * D + row0;
+  float* so = a.s_out + head * (int64_t)(D * D);
+  if constexpr (PASS == 1) {  // u = S.k^
+    float u[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV4; ++m) acc = dot4(R.S[r][m], R.k[m].get4(0), acc);
+      u[r] = group_sum<CL>(acc) * rk;
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) y[r] = u[r];
+    }
+  } else if constexpr (PASS == 2) {  // S = alpha*S + beta*(v - alpha*u) k^
+    const float al = expf(R.ld), be = R.be;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const float ck = be * (R.v.get(r) - al * y[r]) * rk;
+#pragma unroll
+      for (int m = 0; m < NV4; ++m) {
+        const float4 kf = R.k[m].get4(0);
+        float4 s = R.S[r][m];
+        s.x = fmaf(ck, kf.x, al * s.x);
+        s.y = fmaf(ck, kf.y, al * s.y);
+        s.z = fmaf(ck, kf.z, al * s.z);
+        s.w = fmaf(ck, kf.w, al * s.w);
+        nt_store4(s, so + (row0 + r) * D + 4 * (m * CL + j));
+      }
+    }
+  } else {  // o = S.q^ on the updated S, then the output
+    float o[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV4; ++m) acc = dot4(R.S[r][m], R.q[m].get4(0), acc);
+      o[r] = group_sum<CL>(acc) * rq;
+    }
+    if (a.z != nullptr) {
+      float ss = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        o[r] *= silu(R.z.get(r));
+        ss = fmaf(o[r], o[r], ss);
+      }
+      ss = wave_sum(j == 0 ? ss : 0.f);
+      if (lane == 0) red[wave] = ss;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) tot += red[i];
+      const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
+      Raw<DT, RPL> wr;
+      wr.load(a.w, row0);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) o[r] *= inv * wr.get(r);
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) y[r] = o[r];
+    }
+  }
+}
+
 }  // namespace
 
 template <int DT, int GT>
@@ -237,6 +335,49 @@ int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v,
     case GDN_F32: return launch_step_gt<GDN_F32>(d, a, st);
     case GDN_F16: return launch_step_gt<GDN_F16>(d, a, st);
     default: return launch_step_gt<GDN_BF16>(d, a, st);
+  }
+}
+
+template <int DT, int GT>
+int launch_three_pass_dt(const gdn_desc& d, StepArgs a, hipStream_t st) {
+  const dim3 grid((unsigned)(d.B * d.Hv));
+  if (d.Dk != 128) {
+    set_error("the three-pass step is built for D == 128 only");
+    return GDN_EUNSUPPORTED;
+  }
+  // pass 1 reads s0 and pass 2 rewrites it into s_out (the launches are
+  // ordered on the stream, so s_out == s0 is fine); pass 3 reads s_out
+  threepass_kernel<DT, GT, 128, 8, 2, 8, 1><<<grid, 8 * kWave, 0, st>>>(a);
+  int rc = device_status("three-pass kernel 1 launch");
+  if (rc != GDN_OK) return rc;
+  threepass_kernel<DT, GT, 128, 8, 2, 8, 2><<<grid, 8 * kWave, 0, st>>>(a);
+  rc = device_status("three-pass kernel 2 launch");
+  if (rc != GDN_OK) return rc;
+  a.s0 = a.s_out;
+  threepass_kernel<DT, GT, 128, 8, 2, 8, 3><<<grid, 8 * kWave, 0, st>>>(a);
+  return device_status("three-pass kernel 3 launch");
+}
+
+template <int DT>
+int launch_three_pass_gt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
+  switch (d.gate_dtype) {
+    case GDN_F32: return launch_three_pass_dt<DT, GDN_F32>(d, a, st);
+    case GDN_F16: return launch_three_pass_dt<DT, GDN_F16>(d, a, st);
+    default: return launch_three_pass_dt<DT, GDN_BF16>(d, a, st);
+  }
+}
+
+int launch_step_three_pass(const gdn_desc& d, const void* q, const void* k, const void* v,
+                           const void* ld, const void* beta, const float* s0, const void* z,
+                           const void* w, float* y, float* s_out, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const StepArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, (int)d.Hk, (int)d.Hv,
+                   (int)(d.Hv / d.Hk), d.dtype, d.gate_dtype, d.flags, d.qk_eps, d.norm_eps,
+                   q_scale(d)};
+  switch (d.dtype) {
+    case GDN_F32: return launch_three_pass_gt<GDN_F32>(d, a, st);
+    case GDN_F16: return launch_three_pass_gt<GDN_F16>(d, a, st);
+    default: return launch_three_pass_gt<GDN_BF16>(d, a, st);
   }
 }
 

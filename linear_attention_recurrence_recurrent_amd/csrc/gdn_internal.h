@@ -18,6 +18,9 @@ void set_error(const char* msg);
 int launch_step(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
                 float* s_out, void* stream);
+int launch_step_three_pass(const gdn_desc& d, const void* q, const void* k, const void* v,
+                           const void* ld, const void* beta, const float* s0, const void* z,
+                           const void* w, float* y, float* s_out, void* stream);
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
                 float* s_out, void* stream);

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 import torch
 
-from linear_attention_recurrence_recurrent_amd import GdnError, recurrent_step, scan, synth
+from linear_attention_recurrence_recurrent_amd import (GdnError, recurrent_step,
+                                                       recurrent_step_three_pass, scan, synth)
 from oracle import gdn_oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -79,6 +80,36 @@ def test_config1_decode_step_bf16(gated):
                       ops["z"] if gated else None, ops["w"] if gated else None)
     assert_close(y, yr, TOL["bf16"], "y")
     assert_close(s, sr, TOL["bf16"], "state")
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_three_pass_step_matches_oracle_and_fused_step(gated):
+    """The literal three-pass form gives the oracle's result (and the fused step's, to
+    rounding), in place and out of place."""
+    ops = synth.random_operands(4, 1, 16, 32, 128, 128, dtype="bf16", seed=21)
+    d = dev(ops)
+    z, w = (d["z"], d["w"]) if gated else (None, None)
+    y3, s3 = recurrent_step_three_pass(d["q"], d["k"], d["v"], d["log_decay"], d["beta"],
+                                       d["s0"], z, w)
+    yf, sf = recurrent_step(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], z, w)
+    st = d["s0"].clone()
+    yi, si = recurrent_step_three_pass(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], st,
+                                       z, w, inplace=True)
+    torch.cuda.synchronize()
+    yr, sr = orc.step(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                      ops["z"] if gated else None, ops["w"] if gated else None)
+    assert_close(y3, yr, TOL["bf16"], "three-pass y")
+    assert_close(s3, sr, TOL["bf16"], "three-pass state")
+    assert_close(y3, yf.double().cpu().numpy(), 1e-5, "three-pass vs fused y")
+    assert_close(s3, sf.double().cpu().numpy(), 1e-6, "three-pass vs fused state")
+    assert torch.equal(yi, y3) and torch.equal(si, s3)
+
+
+def test_three_pass_rejects_other_head_dims():
+    ops = dev(synth.random_operands(1, 1, 2, 4, 64, 64, dtype="bf16", seed=1))
+    with pytest.raises(GdnError, match="EUNSUPPORTED"):
+        recurrent_step_three_pass(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"],
+                                  ops["s0"])
 
 
 # ------------------------------------------------------------------ small cases spanning tiles
