@@ -205,6 +205,37 @@ def bench_scan(idx, args, torch):
             "algorithmic_flops_per_call": flops}
 
 
+def bench_gates(args, torch):
+    """Gate producer on the head-major scan's gate count (B*T*Hv = 16*1024*32), f16."""
+    from linear_attention_recurrence_recurrent_amd import _native
+    n = 16 * 1024 * 32
+    g = torch.Generator(device="cpu").manual_seed(5)
+    a = torch.randn(n, generator=g).to(torch.float16).cuda()
+    b = torch.randn(n, generator=g).to(torch.float16).cuda()
+    ld = torch.empty_like(a)
+    be = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    L = _native.lib()
+    args_c = (n, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), 1, 0.01,
+              ctypes.c_void_p(ld.data_ptr()), ctypes.c_void_p(be.data_ptr()), 1,
+              ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(3):
+        assert L.gdn_gates(*args_c) == 0
+    torch.cuda.synchronize()
+    reps = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        L.gdn_gates(*args_c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = 4 * 2 * n
+    log("gates: %.2f us per launch for %d elements" % (us, n))
+    return {"elements": n, "us_per_launch": round(us, 2), "bytes_per_launch": nbytes,
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "dtype": "f16"}
+
+
 def cpu_baseline(ops, args):
     """The float64 oracle on the whole decode chain (100 chained steps of all 64
     sequences == the scan over 100 tokens), repeated until about ``cpu_seconds``
@@ -294,6 +325,8 @@ def main():
     }
     if scan:
         out["scan"] = scan
+    if not args.no_scan:
+        out["gate_producer"] = bench_gates(args, torch)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(ops, args)
     print(json.dumps(out), flush=True)

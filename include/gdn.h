@@ -122,6 +122,18 @@ int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
              const void* log_decay, const void* beta, const float* s0, const void* z,
              const void* w, float* y, float* s_out, void* stream);
 
+/* Gate producer: both gates from their pre-activations in one launch ("Module
+ * gdn" page, QWEN38_KERNELS: the gate kernel computes both gates from one
+ * launch; the pages do not give the formulas, these are the workloads' own):
+ *     log_decay[i] = -decay_scale * softplus(a[i]),   beta[i] = sigmoid(b[i]).
+ * a, b: n device elements of in_dtype; log_decay, beta: n device elements of
+ * out_dtype (16-bit outputs rounded to nearest even), ready to be passed to
+ * gdn_recurrent_step / gdn_scan as their gates.  Pointers aligned to their
+ * element size; outputs must not overlap inputs or each other (GDN_EALIAS).
+ * n == 0 does nothing.  Asynchronous on `stream`, allocates nothing. */
+int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,
+              void* log_decay, void* beta, int32_t out_dtype, void* stream);
+
 /* Validation only, no device work: GDN_OK when gdn_scan would accept these
  * arguments, else the status with its short reason in gdn_last_error()
  * ("gated_delta" page, native_gdn_reject_reason: why operands cannot become

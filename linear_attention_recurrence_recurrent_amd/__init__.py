@@ -19,8 +19,8 @@ import torch
 from . import _native
 from ._native import GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GdnDesc
 
-__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "check", "abi_version",
-           "GdnError"]
+__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "gates", "check",
+           "abi_version", "GdnError"]
 
 _DT = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
        torch.bfloat16: _native.GDN_BF16}
@@ -174,6 +174,32 @@ def recurrent_step_three_pass(q, k, v, log_decay, beta, s0, z=None, w=None, *,
                  qk_eps, norm_eps)
     _call("gdn_recurrent_step_three_pass", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
     return y, s_out
+
+
+def gates(a: torch.Tensor, b: torch.Tensor, *, decay_scale: float = 1.0,
+          out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gate producer (one launch): log_decay = -decay_scale*softplus(a),
+    beta = sigmoid(b), elementwise; outputs in ``out_dtype`` (default a's)."""
+    if a.shape != b.shape or a.dtype != b.dtype or a.device != b.device:
+        raise GdnError(2, "a and b must match in shape, dtype and device")
+    if a.device.type != "cuda":
+        raise GdnError(8, "operands must be on a GPU device")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise GdnError(1, "a and b must be contiguous")
+    odt = out_dtype or a.dtype
+    ld = torch.empty(a.shape, dtype=odt, device=a.device)
+    be = torch.empty(a.shape, dtype=odt, device=a.device)
+    L = _native.lib()
+    stream = torch.cuda.current_stream(a.device).cuda_stream
+    with torch.cuda.device(a.device):
+        rc = L.gdn_gates(a.numel(), _ptr(a), _ptr(b), _dtype_code(a, "a"), float(decay_scale),
+                         _ptr(ld), _ptr(be), _DT[odt], ctypes.c_void_p(stream))
+    if rc != 0:
+        reason = _native.last_error()
+        if rc == 8:
+            raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
+        raise GdnError(rc, reason)
+    return ld, be
 
 
 def check(desc: GdnDesc, q=None, k=None, v=None, log_decay=None, beta=None, s0=None, z=None,

@@ -19,7 +19,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_ESHAPE", 3: "GDN_EDTYPE", 4: "GD
           5: "GDN_EUNSUPPORTED", 6: "GDN_EALIGN", 7: "GDN_EALIAS", 8: "GDN_EDEVICE"}
 
 # Every symbol include/gdn.h declares.
-EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan", "gdn_check",
+EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan", "gdn_gates",
+           "gdn_check",
            "gdn_last_error", "gdn_status_str", "gdn_abi_version")
 
 
@@ -51,6 +52,9 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [dp] + [vp] * 11
+        L.gdn_gates.restype = ctypes.c_int
+        L.gdn_gates.argtypes = [ctypes.c_int64, vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
+                                ctypes.c_int32, vp]
         L.gdn_check.restype = ctypes.c_int
         L.gdn_check.argtypes = [dp] + [vp] * 10
         L.gdn_last_error.restype = ctypes.c_char_p

@@ -53,4 +53,11 @@ int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
   return gdn::launch_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
 }
 
+int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,
+              void* log_decay, void* beta, int32_t out_dtype, void* stream) {
+  int rc = gdn::check_gates(n, a, b, in_dtype, decay_scale, log_decay, beta, out_dtype);
+  if (rc != GDN_OK || n == 0) return rc;
+  return gdn::launch_gates(n, a, b, in_dtype, decay_scale, log_decay, beta, out_dtype, stream);
+}
+
 }  // extern "C"

@@ -129,6 +129,34 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
   return GDN_OK;
 }
 
+int check_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,
+                const void* log_decay, const void* beta, int32_t out_dtype) {
+  g_last_error[0] = '\0';
+  if (n < 0) return fail(GDN_ESHAPE, "negative element count %lld", (long long)n);
+  if (n >= (int64_t)1 << 40) return fail(GDN_ESHAPE, "element count too large");
+  if (in_dtype < GDN_F32 || in_dtype > GDN_BF16 || out_dtype < GDN_F32 || out_dtype > GDN_BF16)
+    return fail(GDN_EDTYPE, "bad dtype (in %d, out %d)", in_dtype, out_dtype);
+  if (!(decay_scale >= 0.0f && decay_scale < 1e30f))
+    return fail(GDN_EINVAL, "decay_scale must be finite and >= 0");
+  if (n == 0) return GDN_OK;
+  if (!a || !b || !log_decay || !beta) return fail(GDN_EINVAL, "null pointer");
+  const int64_t ies = elem_size(in_dtype), oes = elem_size(out_dtype);
+  auto al = [](const void* p, int64_t e) { return (uintptr_t)p % (uintptr_t)e == 0; };
+  if (!al(a, ies) || !al(b, ies) || !al(log_decay, oes) || !al(beta, oes))
+    return fail(GDN_EALIGN, "pointers must be aligned to their element size");
+  auto rng = [](const char* nm, const void* p, int64_t bytes) {
+    return Range{nm, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+  };
+  const Range ra = rng("a", a, n * ies), rb = rng("b", b, n * ies);
+  const Range rl = rng("log_decay", log_decay, n * oes), rB = rng("beta", beta, n * oes);
+  if (overlap(rl, rB)) return fail(GDN_EALIAS, "log_decay overlaps beta");
+  for (const Range* in : {&ra, &rb}) {
+    if (overlap(rl, *in)) return fail(GDN_EALIAS, "log_decay overlaps %s", in->name);
+    if (overlap(rB, *in)) return fail(GDN_EALIAS, "beta overlaps %s", in->name);
+  }
+  return GDN_OK;
+}
+
 }  // namespace gdn
 
 extern "C" {

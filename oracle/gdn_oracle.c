@@ -75,6 +75,22 @@ void gdn_oracle_gated_rmsnorm(const double* o, const double* z, const double* w,
   free(x);
 }
 
+/* Gate producer: log_decay = -decay_scale * softplus(a), beta = sigmoid(b), for
+ * n elements.  "Module gdn" page, QWEN38_KERNELS (both gates from one launch);
+ * the formulas are the workloads' own recipe, the pages do not give them.
+ * softplus(x) = log(1 + exp(x)) and sigmoid(x) = 1 / (1 + exp(-x)), written in
+ * forms that do not overflow for large |x|. */
+void gdn_oracle_gates(int64_t n, const double* a, const double* b, double decay_scale,
+                      double* log_decay, double* beta) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double x = a[i];
+    const double sp = (x > 0 ? x : 0.0) + log1p(exp(-fabs(x)));
+    log_decay[i] = -decay_scale * sp;
+    const double y = b[i];
+    beta[i] = y >= 0 ? 1.0 / (1.0 + exp(-y)) : exp(y) / (1.0 + exp(y));
+  }
+}
+
 typedef struct {
   int64_t B, T, Hk, Hv, Dk, Dv;
   uint32_t flags;

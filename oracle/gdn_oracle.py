@@ -56,6 +56,8 @@ def _load():
                                                     ctypes.c_double] + [dp] * 10 + [ctypes.c_int]
         lib.gdn_oracle_l2norm.restype = None
         lib.gdn_oracle_l2norm.argtypes = [dp, i64, ctypes.c_double]
+        lib.gdn_oracle_gates.restype = None
+        lib.gdn_oracle_gates.argtypes = [i64, dp, dp, ctypes.c_double, dp, dp]
         lib.gdn_oracle_gated_rmsnorm.restype = None
         lib.gdn_oracle_gated_rmsnorm.argtypes = [dp, dp, dp, i64, ctypes.c_double, dp]
         _lib = lib
@@ -149,6 +151,16 @@ def gated_rmsnorm(o, z, w=None, eps: float = 1e-6) -> np.ndarray:
         lib.gdn_oracle_gated_rmsnorm(_ptr(orow), _ptr(zrow), _ptr(w), n, eps, _ptr(yrow))
         y[r] = yrow
     return y.reshape(o.shape)
+
+
+def gates(a, b, decay_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Gate producer: (log_decay, beta) = (-decay_scale*softplus(a), sigmoid(b)), float64."""
+    a, b = _f64(a), _f64(b)
+    assert a.shape == b.shape
+    ld = np.empty_like(a)
+    be = np.empty_like(b)
+    _load().gdn_oracle_gates(a.size, _ptr(a), _ptr(b), decay_scale, _ptr(ld), _ptr(be))
+    return ld, be
 
 
 def select_heads(ops: dict, heads, *, head_major: bool) -> dict:

@@ -203,3 +203,18 @@ def test_last_error_is_per_thread():
     t.join()
     assert seen == [""]
     assert "multiple" in nat.last_error()
+
+
+def test_gates_validation():
+    L = nat.lib()
+    a, b, ld, be = _addrs(4)
+    chk = L.gdn_gates
+    # rejections return before any HIP call
+    assert chk(-1, a, b, 2, 1.0, ld, be, 0, None) == 2
+    assert chk(16, a, b, 5, 1.0, ld, be, 0, None) == 3
+    assert chk(16, a, b, 2, -1.0, ld, be, 0, None) == 1
+    assert chk(16, None, b, 2, 1.0, ld, be, 0, None) == 1
+    assert chk(16, a + 1, b, 2, 1.0, ld, be, 0, None) == 6
+    assert chk(16, a, b, 2, 1.0, a + 8, be, 0, None) == 7 and "overlaps" in nat.last_error()
+    assert chk(16, a, b, 2, 1.0, ld, ld + 32, 0, None) == 7
+    assert chk(0, None, None, 2, 1.0, None, None, 0, None) == 0

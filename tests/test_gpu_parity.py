@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from linear_attention_recurrence_recurrent_amd import (GdnError, recurrent_step,
+from linear_attention_recurrence_recurrent_amd import (GdnError, gates, recurrent_step,
                                                        recurrent_step_three_pass, scan, synth)
 from oracle import gdn_oracle as orc
 
@@ -110,6 +110,40 @@ def test_three_pass_rejects_other_head_dims():
     with pytest.raises(GdnError, match="EUNSUPPORTED"):
         recurrent_step_three_pass(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"],
                                   ops["s0"])
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("bf16", "f32"), ("f16", "f16"),
+                                          ("bf16", "bf16")])
+def test_gate_producer(in_dt, out_dt):
+    r = np.random.default_rng(40)
+    n = 4099  # ragged against the 4-elements-per-thread tiling
+    a = synth._cast(np.concatenate([r.standard_normal(n - 5) * 3,
+                                    [0.0, 40.0, -40.0, 1e-3, -9.0]]), in_dt)
+    b = synth._cast(np.concatenate([r.standard_normal(n - 5) * 3,
+                                    [0.0, 30.0, -30.0, 2.0, -2.0]]), in_dt)
+    ld, be = gates(a.to(DEV), b.to(DEV), decay_scale=0.5, out_dtype=synth.DTYPES[out_dt])
+    torch.cuda.synchronize()
+    lr, br = orc.gates(a, b, decay_scale=0.5)
+    tol = 2e-6 if out_dt == "f32" else 3e-3
+    assert_close(ld, lr, tol, "log_decay")
+    assert_close(be, br, tol, "beta")
+
+
+def test_gates_feed_the_scan():
+    """Raw pre-activations -> gate producer -> scan equals the oracle run on the
+    oracle's own gates."""
+    r = np.random.default_rng(41)
+    ops = synth.random_operands(2, 24, 2, 4, 64, 64, dtype="f32", seed=42)
+    a = synth._cast(r.standard_normal((2, 24, 4)), "f32")
+    b = synth._cast(r.standard_normal((2, 24, 4)), "f32")
+    d = dev(ops)
+    ld, be = gates(a.to(DEV), b.to(DEV))
+    y, s = scan(d["q"], d["k"], d["v"], ld, be, d["s0"], d["z"], d["w"])
+    torch.cuda.synchronize()
+    lr, br = orc.gates(a, b)
+    yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], lr, br, ops["s0"], ops["z"], ops["w"])
+    assert_close(y, yr, TOL["f32"], "y")
+    assert_close(s, sr, TOL["f32"], "state")
 
 
 # ------------------------------------------------------------------ small cases spanning tiles

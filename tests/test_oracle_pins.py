@@ -367,3 +367,28 @@ def test_matches_hf_recurrent_rule():
         use_qk_l2norm_in_kernel=True)
     np.testing.assert_allclose(out.double().numpy(), y, rtol=0, atol=2e-5)
     np.testing.assert_allclose(fin.double().transpose(-1, -2).numpy(), s, rtol=0, atol=2e-5)
+
+
+# ---------------------------------------------------------------- gate producer
+def test_gate_producer_closed_forms():
+    """softplus(0) = ln 2, sigmoid(0) = 1/2; softplus(x) -> x and -> e^x in the tails;
+    sigmoid(-x) = 1 - sigmoid(x); the scale multiplies log_decay only."""
+    a = np.array([0.0, 40.0, -40.0, 1.0])
+    b = np.array([0.0, 3.0, -3.0, 50.0])
+    ld, be = orc.gates(a, b, decay_scale=0.5)
+    np.testing.assert_allclose(ld[0], -0.5 * math.log(2.0), rtol=1e-15)
+    np.testing.assert_allclose(ld[1], -0.5 * 40.0, rtol=1e-15)
+    np.testing.assert_allclose(ld[2], -0.5 * math.exp(-40.0), rtol=1e-12)
+    np.testing.assert_allclose(ld[3], -0.5 * math.log1p(math.e), rtol=1e-15)
+    np.testing.assert_allclose(be[0], 0.5, rtol=0)
+    np.testing.assert_allclose(be[1] + be[2], 1.0, rtol=1e-15)
+    np.testing.assert_allclose(be[3], 1.0, rtol=1e-15)
+
+
+def test_gate_producer_matches_library_routines():
+    r = np.random.default_rng(30)
+    a, b = r.standard_normal(1000) * 5, r.standard_normal(1000) * 5
+    ld, be = orc.gates(a, b, decay_scale=0.01)
+    np.testing.assert_allclose(ld, -0.01 * np.logaddexp(0.0, a), rtol=1e-14)
+    from scipy.special import expit
+    np.testing.assert_allclose(be, expit(b), rtol=1e-14)
