@@ -55,7 +55,11 @@ __device__ __forceinline__ float4 scale4(const float4 a, float s) {
   return make_float4(a.x * s, a.y * s, a.z * s, a.w * s);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z * sigmoid(z), from the hardware exp2 and reciprocal (a few ulp;
+// z -> -inf gives -0, z -> +inf gives z).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504f));
+}
 
 // Streaming (nontemporal) 16-byte state accesses: the state is touched once per
 // decode step, so it should not displace other lines from the caches.
@@ -87,11 +91,16 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Sum over the whole wave, returned in every lane.  The four row sums are read
+// out lane by lane, so no cross-row exchange through LDS is needed; the exec
+// mask must be full.
 __device__ __forceinline__ float wave_sum(float x) {
   x = group_sum<16>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const int b = __float_as_int(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
@@ -105,7 +114,7 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t i, int64_t n) {
 // is N elements wide, so the element index must be a multiple of N.
 template <int DT, int N>
 struct Raw {
-  static_assert(N == 1 || N == 2 || N == 4, "Raw holds 1, 2 or 4 elements");
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "Raw holds 1, 2, 4 or 8 elements");
   static constexpr bool kF32 = DT == GDN_F32;
   typedef typename std::conditional<kF32, float, uint32_t>::type Word;
   static constexpr int kWords = kF32 ? N : (N + 1) / 2;
@@ -113,7 +122,12 @@ struct Raw {
   __device__ __forceinline__ void load(const void* p, int64_t i) {
     if constexpr (kF32) {
       const float* f = static_cast<const float*>(p) + i;
-      if constexpr (N == 4) {
+      if constexpr (N == 8) {
+        const float4 t = *reinterpret_cast<const float4*>(f);
+        const float4 u = *reinterpret_cast<const float4*>(f + 4);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+        w[4] = u.x; w[5] = u.y; w[6] = u.z; w[7] = u.w;
+      } else if constexpr (N == 4) {
         const float4 t = *reinterpret_cast<const float4*>(f);
         w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
       } else if constexpr (N == 2) {
@@ -124,7 +138,10 @@ struct Raw {
       }
     } else {
       const uint16_t* h = static_cast<const uint16_t*>(p) + i;
-      if constexpr (N == 4) {
+      if constexpr (N == 8) {
+        const uint4 t = *reinterpret_cast<const uint4*>(h);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+      } else if constexpr (N == 4) {
         const uint2 t = *reinterpret_cast<const uint2*>(h);
         w[0] = t.x; w[1] = t.y;
       } else if constexpr (N == 2) {
@@ -133,6 +150,10 @@ struct Raw {
         w[0] = h[0];
       }
     }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = 0;
   }
   __device__ __forceinline__ float get(int k) const {
     if constexpr (kF32) {
@@ -148,9 +169,6 @@ struct Raw {
     return make_float4(get(4 * c), get(4 * c + 1), get(4 * c + 2), get(4 * c + 3));
   }
 };
-
-// Registers of one head in flight: this lane's columns of q and k (raw), its
-// RPL state rows (adjacent rows, float4 chunks), and its rows' v and z (raw).
 
 }  // namespace
 }  // namespace gdn

@@ -6,8 +6,8 @@
 // as the "gated_delta" page's gated_delta_reference does, returning
 // (output, final_state).  The state stays in VGPRs for the whole time axis;
 // q/k/v/gates are staged through LDS in chunks of TC tokens (the next chunk
-// loads into registers while the current one computes); q/k are normalised
-// once per token per workgroup; outputs are buffered in LDS and written back
+// loads into registers while the current one computes, and is normalised in
+// registers on its way into LDS); outputs are buffered in LDS and written back
 // coalesced, gated in the same launch when the workgroup owns the whole head.
 // Rows are split over lanes exactly as in the decode kernel.
 #include "gdn_device.h"
@@ -28,13 +28,15 @@ struct ScanArgs {
 };
 
 // Raw operands of one chunk of TC tokens, held in registers while the previous
-// chunk computes.  Thread tid covers chunk items tid, tid + NT, ...
+// chunk computes.  Thread tid covers chunk items tid, tid + NT, ...; an item of
+// q and k is 8 consecutive elements, so one token's q (or k) spans D/8
+// adjacent lanes.
 template <int DT, int GT, int D, int ROWS, int TC, int NT, bool WITH_Z>
 struct ChunkRegs {
-  static constexpr int D4 = D / 4, R2 = ROWS / 2;
-  static constexpr int NQK = (TC * D4 + NT - 1) / NT;  // float4 groups of q and of k
+  static constexpr int D8 = D / 8, R2 = ROWS / 2;
+  static constexpr int NQK = (TC * D8 + NT - 1) / NT;  // 8-element groups of q and of k
   static constexpr int NV = (TC * R2 + NT - 1) / NT;   // pairs of v (and z) elements
-  Raw<DT, 4> k[NQK], q[NQK];
+  Raw<DT, 8> k[NQK], q[NQK];
   Raw<DT, 2> v[NV];
   Raw<DT, 2> z[WITH_Z ? NV : 1];
   Raw<GT, 1> ld, be;
@@ -48,11 +50,12 @@ struct ScanBases {
 // Smallest and largest decay scale kept folded: outside [2^-30, 2^30] the
 // state is brought back to scale 1 (and alpha == 0 always lands here).
 constexpr float kFoldMin = 9.3132257e-10f, kFoldMax = 1.0737418e9f;
-// Range of a chunk's running decay product for the unchecked chunk loop: the
-// state is brought to scale 1 at every chunk start, so the scale inside the
-// chunk is exactly this product; [2^-60, 2^60] keeps every folded quantity far
-// from f32 overflow and underflow.
-constexpr float kFastMin = 8.6736174e-19f, kFastMax = 1.1529215e18f;
+// Bound on a chunk's sum of |log_decay| for the unchecked chunk loop: the state
+// is brought to scale 1 at every chunk start, so the scale inside the chunk is
+// the running decay product, and every such product then lies within
+// [e^-41, e^41] (about 2^-59 .. 2^59), far from f32 overflow and underflow.
+// NaN or infinite gates fail the test and take the checked loop.
+constexpr float kFastLogSum = 41.0f;
 
 // The scan processes the time axis in chunks of TC tokens staged through LDS,
 // and each chunk in blocks of L tokens.  Within a block the recurrence is
@@ -71,7 +74,7 @@ template <int DT, int GT, int D, int CL, int RPL, int NW, int TC, int L, bool FU
 __global__ __launch_bounds__(NW* kWave)
 __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArgs a) {
   constexpr int NCOL = D / CL, NV4 = NCOL / 4, RG = kWave / CL, ROWS = NW * RG * RPL;
-  constexpr int NT = NW * kWave, D4 = D / 4, R2 = ROWS / 2;
+  constexpr int NT = NW * kWave, D4 = D / 4, D8 = D / 8, R2 = ROWS / 2;
   constexpr int LPT = D / 8;  // lanes per token in the norm pass (8 elements of q and k each)
   constexpr int NB = TC / L;  // blocks per chunk
   constexpr int NPB = L * (L - 1);  // off-diagonal Gram entries per block (k.k and k.q)
@@ -80,15 +83,17 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
   // unchecked token loop for chunks whose decay products stay in range.
   constexpr bool UNROLL = !FUSE_NORM && L == 1 && NV4 * RPL <= 2;
   static_assert(NCOL % 4 == 0, "a lane owns whole float4 chunks");
-  static_assert(D % ROWS == 0 && ROWS % 2 == 0, "row blocks tile the head");
+  static_assert(D % ROWS == 0 && ROWS % 4 == 0, "row blocks tile the head");
   static_assert(!FUSE_NORM || ROWS == D, "the fused norm needs the whole head");
-  static_assert(TC <= NT && NT % LPT == 0 && TC % L == 0, "chunk shape");
+  static_assert(TC <= kWave && NT % LPT == 0 && TC % L == 0, "chunk shape");
+  static_assert(D / 8 <= 16, "a token's q/k groups span at most one DPP row");
+  static_assert(!FUSE_NORM || TC % NW == 0, "whole tokens per wave in the fused output");
   typedef ChunkRegs<DT, GT, D, ROWS, TC, NT, FUSE_NORM> Chunk;
   __shared__ float4 sk[TC][D4];
   __shared__ float4 sq[TC][D4];
   __shared__ float sv[TC][ROWS];
   __shared__ float sz[FUSE_NORM ? 2 : 1][FUSE_NORM ? TC : 1][FUSE_NORM ? D : 1];
-  __shared__ float so[TC][ROWS];
+  __shared__ __align__(16) float so[TC][ROWS];
   __shared__ float sal[TC], sbe[TC], skq[TC];
   __shared__ float sP[NB][L][L], sQ[NB][L][L], sA[NB][L + 1], sR[NB][L], sAmin[NB], sAmax[NB];
   __shared__ int sfast;  // the chunk's decay products stay inside the folding range
@@ -117,11 +122,14 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
   auto chunk_load = [&](Chunk& P, int64_t t0, int tc) {
 #pragma unroll
     for (int i = 0; i < Chunk::NQK; ++i) {
-      const int e = tid + i * NT, tt = e / D4, c4 = e % D4;
-      if (e < TC * D4 && tt < tc) {
-        const int64_t off = sb.qk_base + (t0 + tt) * sb.qk_ts + 4 * c4;
+      const int e = tid + i * NT, tt = e / D8, c8 = e % D8;
+      if (e < TC * D8 && tt < tc) {
+        const int64_t off = sb.qk_base + (t0 + tt) * sb.qk_ts + 8 * c8;
         P.k[i].load(a.k, off);
         P.q[i].load(a.q, off);
+      } else {  // padding: exact zeros, so staging needs no select
+        P.k[i].zero();
+        P.q[i].zero();
       }
     }
 #pragma unroll
@@ -141,26 +149,65 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
       P.be.load(a.beta, gi);
     }
   };
-  // Tokens tc..TC-1 of a short last chunk become identity steps (alpha = 1,
-  // beta = 0, k = q = v = 0), so whole blocks can always be processed.
-  auto chunk_store = [&](const Chunk& P, int tc, int zbuf) {
-    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  // Registers -> LDS, folding in the L2 norms and the q scale on the way: the
+  // D8 lanes holding one token's q and k are adjacent and aligned inside one
+  // DPP row, so the three dot products reduce across them.  Tokens tc..TC-1 of
+  // a short last chunk become identity steps (alpha = 1, beta = 0,
+  // k = q = v = 0), so whole blocks can always be processed.  FULL (tc == TC,
+  // every chunk but a short last one) drops the per-token tests, leaving
+  // straight-line code whose chains the compiler can interleave.
+  auto chunk_store = [&](const Chunk& P, int tc, int zbuf, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    constexpr bool ALL_E = (TC * D8) % NT == 0;  // every item index is in range
+    const bool l2 = (a.flags & GDN_FOLD_QK_L2NORM) != 0;
+    // The chunk's loads (issued a whole recurrence phase ago) are complete.
+    // Waiting for all of them here, on every path, also tells the compiler
+    // that none is pending afterwards; otherwise the lanes that load nothing
+    // leave a possible pending load into these registers, and the next chunk's
+    // load issue would wait for the output stores issued in between.
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    constexpr int N = Chunk::NQK;
+    float skk[N], sqq[N], sqk[N];
 #pragma unroll
-    for (int i = 0; i < Chunk::NQK; ++i) {
-      const int e = tid + i * NT, tt = e / D4, c4 = e % D4;
-      if (e < TC * D4) {
-        sk[tt][c4] = tt < tc ? P.k[i].get4(0) : zero4;
-        sq[tt][c4] = tt < tc ? P.q[i].get4(0) : zero4;
+    for (int i = 0; i < N; ++i) {
+      const float4 k0 = P.k[i].get4(0), k1 = P.k[i].get4(1);
+      const float4 q0 = P.q[i].get4(0), q1 = P.q[i].get4(1);
+      skk[i] = dot4(k1, k1, dot4(k0, k0, 0.f));
+      sqq[i] = dot4(q1, q1, dot4(q0, q0, 0.f));
+      sqk[i] = dot4(k1, q1, dot4(k0, q0, 0.f));
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      skk[i] = group_sum<D8>(skk[i]);
+      sqq[i] = group_sum<D8>(sqq[i]);
+      sqk[i] = group_sum<D8>(sqk[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = tid + i * NT, tt = e / D8, c8 = e % D8;
+      // without the L2 fold the square roots see 1 and return 1
+      float rk = rsqrtf(l2 ? skk[i] + a.qk_eps : 1.f);
+      float rq = a.qscale * rsqrtf(l2 ? sqq[i] + a.qk_eps : 1.f);
+      if constexpr (!FULL) {
+        if (tt >= tc) rk = rq = 0.f;  // padding stays exactly zero even with eps == 0
+      }
+      if (ALL_E || e < TC * D8) {
+        sk[tt][2 * c8] = scale4(P.k[i].get4(0), rk);
+        sk[tt][2 * c8 + 1] = scale4(P.k[i].get4(1), rk);
+        sq[tt][2 * c8] = scale4(P.q[i].get4(0), rq);
+        sq[tt][2 * c8 + 1] = scale4(P.q[i].get4(1), rq);
+        if (c8 == 0) skq[tt] = sqk[i] * rk * rq;
       }
     }
 #pragma unroll
     for (int i = 0; i < Chunk::NV; ++i) {
       const int e = tid + i * NT, tt = e / R2, r2 = e % R2;
       if (e < TC * R2) {
-        sv[tt][2 * r2] = tt < tc ? P.v[i].get(0) : 0.f;
-        sv[tt][2 * r2 + 1] = tt < tc ? P.v[i].get(1) : 0.f;
+        const bool real = FULL || tt < tc;
+        sv[tt][2 * r2] = real ? P.v[i].get(0) : 0.f;
+        sv[tt][2 * r2 + 1] = real ? P.v[i].get(1) : 0.f;
         if constexpr (FUSE_NORM) {
-          if (has_z && tt < tc) {
+          if (has_z && real) {
             sz[zbuf][tt][2 * r2] = P.z[i].get(0);
             sz[zbuf][tt][2 * r2 + 1] = P.z[i].get(1);
           }
@@ -168,9 +215,20 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
       }
     }
     if (tid < TC) {
-      sal[tid] = tid < tc ? expf(P.ld.get(0)) : 1.f;
-      sbe[tid] = tid < tc ? P.be.get(0) : 0.f;
+      const bool real = FULL || tid < tc;
+      sal[tid] = real ? expf(P.ld.get(0)) : 1.f;
+      sbe[tid] = real ? P.be.get(0) : 0.f;
     }
+    if constexpr (UNROLL) {
+      if (wave == 0) {  // the chunk's decay products stay in the unchecked range
+        const float s = wave_sum(tid < tc ? fabsf(P.ld.get(0)) : 0.f);
+        if (tid == 0) sfast = s <= kFastLogSum ? 1 : 0;
+      }
+    }
+  };
+  auto stage = [&](const Chunk& P, int tc, int zbuf) {
+    if (tc == TC) chunk_store(P, tc, zbuf, std::true_type{});
+    else chunk_store(P, tc, zbuf, std::false_type{});
   };
 
   // State S = gsc * St: St lives in VGPRs for the whole time axis.
@@ -190,57 +248,65 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
       wgt[i] = (has_z && lane + kWave * i < D) ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
   }
 
+  // Gated output of a chunk when the workgroup owns the whole head: one wave
+  // per token, the wave's TC/NW tokens unrolled so that their reductions
+  // overlap.  Every value is computed for every token slot (padding slots read
+  // stale but in-range LDS); only the stores are guarded, and only in a short
+  // last chunk (FULL false).
+  auto write_gated = [&](int64_t t0, int tc, int zb, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    constexpr int EPL = (D + kWave - 1) / kWave, TPW = TC / NW;
+    float x[TPW][EPL], inv[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = wave + NW * u;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int rr = lane + kWave * i, rc = rr < D ? rr : D - 1;
+        x[u][i] = so[tt][rc] * silu(sz[zb][tt][rc]);
+        ss = fmaf(x[u][i], (D >= kWave || rr < D) ? x[u][i] : 0.f, ss);
+      }
+      inv[u] = ss;
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) inv[u] = rsqrtf(wave_sum(inv[u]) * (1.0f / D) + a.norm_eps);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = wave + NW * u;
+      if (FULL || tt < tc) {
+        const int64_t vo = sb.v_base + (t0 + tt) * sb.v_ts;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          const int rr = lane + kWave * i;
+          if (D >= kWave || rr < D) a.y[vo + rr] = x[u][i] * inv[u] * wgt[i];
+        }
+      }
+    }
+  };
+
   Chunk P;
   chunk_load(P, 0, (int)(T < TC ? T : TC));
-  chunk_store(P, (int)(T < TC ? T : TC), 0);
+  stage(P, (int)(T < TC ? T : TC), 0);
   // Every load issued so far (state, weights, first chunk) is complete here;
   // saying so explicitly keeps the compiler from re-waiting for them inside
   // the token loop, where the next chunk's loads are in flight.
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  // Per chunk: barrier; issue the next chunk's loads; the recurrence (C);
+  // barrier; the next chunk into LDS; this chunk's outputs (D).  The outputs
+  // are stored after the next chunk's registers are consumed, so waiting for
+  // those loads never waits for the output stores as well.
   for (int64_t c = 0;; ++c) {
     const int64_t t0 = c * TC;
     const int tc = (int)((T - t0) < TC ? (T - t0) : TC);
     const int nblk = (tc + L - 1) / L;
-    __syncthreads();
-
-    // B1. fold the L2 norms and the q scale into the staged q and k, all
-    //     tokens of the chunk at once (LPT lanes per token); padding tokens
-    //     stay exactly zero
-    for (int tt = tid / LPT; tt < tc; tt += NT / LPT) {
-      const int p = tid % LPT;
-      float4 k0 = sk[tt][2 * p], k1 = sk[tt][2 * p + 1];
-      float4 q0 = sq[tt][2 * p], q1 = sq[tt][2 * p + 1];
-      float skk = dot4(k1, k1, dot4(k0, k0, 0.f));
-      float sqq = dot4(q1, q1, dot4(q0, q0, 0.f));
-      float sqk = dot4(k1, q1, dot4(k0, q0, 0.f));
-      skk = group_sum<LPT>(skk);
-      sqq = group_sum<LPT>(sqq);
-      sqk = group_sum<LPT>(sqk);
-      float rk = 1.f, rq = a.qscale;
-      if (a.flags & GDN_FOLD_QK_L2NORM) {
-        rk = rsqrtf(skk + a.qk_eps);
-        rq *= rsqrtf(sqq + a.qk_eps);
-      }
-      sk[tt][2 * p] = scale4(k0, rk);
-      sk[tt][2 * p + 1] = scale4(k1, rk);
-      sq[tt][2 * p] = scale4(q0, rq);
-      sq[tt][2 * p + 1] = scale4(q1, rq);
-      if (p == 0) skq[tt] = sqk * rk * rq;
-    }
     const bool more = t0 + TC < T;
-    if (more) chunk_load(P, t0 + TC, (int)((T - t0 - TC) < TC ? (T - t0 - TC) : TC));
-    if (tid == 0) {  // range of the chunk's running decay product (padding has alpha = 1)
-      float acc = 1.f;
-      bool ok = true;
-      for (int tt = 0; tt < TC; ++tt) {
-        acc *= sal[tt];
-        ok = ok && acc >= kFastMin && acc <= kFastMax;
-      }
-      sfast = ok ? 1 : 0;
-    }
+    const int tcn = more ? (int)((T - t0 - TC) < TC ? (T - t0 - TC) : TC) : 0;
+    __syncthreads();
+    if (more) chunk_load(P, t0 + TC, tcn);
+
     if constexpr (L > 1) {
-      __syncthreads();
-      // B2. per-block coefficients shared by every row: the off-diagonal Gram
+      // B. per-block coefficients shared by every row: the off-diagonal Gram
       //     entries times their decay products, and the decay prefixes.
       for (int x = tid / LPT; x < NB * NPB; x += NT / LPT) {
         const int p = tid % LPT;
@@ -279,8 +345,8 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
           rr *= sal[bk * L + i];
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
 
     // C. the recurrence: token by token (L == 1) or one block of L tokens after the other.  With
     //    S = gsc*St the update becomes St += sum_j c_j/(gsc*A_{j+1}) k_j and
@@ -507,44 +573,33 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
     }
     __syncthreads();
 
+    // next chunk into LDS: sk/sq/sv/gates/block coefficients were last read in
+    // phase C, before the barrier above; z is double-buffered because phase D
+    // below still reads this chunk's slot.  After the last chunk this stages
+    // an empty chunk (tcn == 0): unconditional, so that its wait for the loads
+    // lies on every path through the loop.
+    stage(P, tcn, (int)((c + 1) & 1));
+
     // D. write this chunk's outputs (gated here when the workgroup owns the head)
     bool written = false;
     if constexpr (FUSE_NORM) {
       if (has_z) {
-        constexpr int EPL = (D + kWave - 1) / kWave;
-        const int zb = (int)(c & 1);
-        for (int tt = wave; tt < tc; tt += NW) {
-          const int64_t vo = sb.v_base + (t0 + tt) * sb.v_ts;
-          float x[EPL];
-          float ss = 0.f;
-#pragma unroll
-          for (int i = 0; i < EPL; ++i) {
-            const int rr = lane + kWave * i;
-            x[i] = 0.f;
-            if (rr < D) x[i] = so[tt][rr] * silu(sz[zb][tt][rr]);
-            ss = fmaf(x[i], x[i], ss);
-          }
-          const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + a.norm_eps);
-#pragma unroll
-          for (int i = 0; i < EPL; ++i) {
-            const int rr = lane + kWave * i;
-            if (rr < D) a.y[vo + rr] = x[i] * inv * wgt[i];
-          }
-        }
+        if (tc == TC) write_gated(t0, tc, (int)(c & 1), std::true_type{});
+        else write_gated(t0, tc, (int)(c & 1), std::false_type{});
         written = true;
       }
     }
-    if (!written) {
-      for (int e = tid; e < tc * ROWS; e += NT) {
-        const int tt = e / ROWS, rr = e % ROWS;
-        a.y[sb.v_base + (t0 + tt) * sb.v_ts + row0 + rr] = so[tt][rr];
+    if (!written) {  // 16-byte stores of 4 rows of one token
+      constexpr int R4 = ROWS / 4, NYS = (TC * R4 + NT - 1) / NT;
+#pragma unroll
+      for (int i = 0; i < NYS; ++i) {
+        const int e = tid + i * NT, tt = e / R4, r4 = e % R4;
+        if (e < TC * R4 && tt < tc)
+          *reinterpret_cast<float4*>(a.y + sb.v_base + (t0 + tt) * sb.v_ts + row0 + 4 * r4) =
+              *reinterpret_cast<const float4*>(&so[tt][4 * r4]);
       }
     }
     if (!more) break;
-    // next chunk into LDS: sk/sq/sv/gates/block coefficients were last read in
-    // phase C, before the barrier above; z is double-buffered because phase D
-    // may still be reading this chunk's slot in other waves.
-    chunk_store(P, (int)((T - t0 - TC) < TC ? (T - t0 - TC) : TC), (int)((c + 1) & 1));
   }
 
 #pragma unroll
