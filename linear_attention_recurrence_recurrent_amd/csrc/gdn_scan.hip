@@ -6,9 +6,10 @@
 // as the "gated_delta" page's gated_delta_reference does, returning
 // (output, final_state).  The state stays in VGPRs for the whole time axis;
 // q/k/v/gates are staged through LDS in chunks of TC tokens (the next chunk
-// loads into registers while the current one computes, and is normalised in
-// registers on its way into LDS); outputs are buffered in LDS and written back
-// coalesced, gated in the same launch when the workgroup owns the whole head.
+// loads into registers while the current one computes, and its q/k norms are
+// reduced in registers on the way into LDS); outputs are buffered in LDS and
+// written back coalesced, gated in the same launch when the workgroup owns the
+// whole head.
 // Rows are split over lanes exactly as in the decode kernel.
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -47,56 +48,83 @@ struct ScanBases {
   int64_t qk_base, qk_ts, v_base, v_ts, g_base, g_ts;
 };
 
-// Smallest and largest decay scale kept folded: outside [2^-30, 2^30] the
-// state is brought back to scale 1 (and alpha == 0 always lands here).
+// Smallest and largest decay scale kept folded in the per-token loop: outside
+// [2^-30, 2^30] the state is brought back to scale 1 (and alpha == 0 always
+// lands here).
 constexpr float kFoldMin = 9.3132257e-10f, kFoldMax = 1.0737418e9f;
-// Bound on a chunk's sum of |log_decay| for the unchecked chunk loop: the state
-// is brought to scale 1 at every chunk start, so the scale inside the chunk is
-// the running decay product, and every such product then lies within
+// Bound on a chunk's sum of |log_decay| for the chunk-scalar loop: the state is
+// brought to scale 1 at every chunk start, so the scale inside the chunk is the
+// running decay product, and every such product then lies within
 // [e^-41, e^41] (about 2^-59 .. 2^59), far from f32 overflow and underflow.
-// NaN or infinite gates fail the test and take the checked loop.
+// NaN or infinite gates fail the test and take the per-token loop.
 constexpr float kFastLogSum = 41.0f;
 
-// The scan processes the time axis in chunks of TC tokens staged through LDS,
-// and each chunk in blocks of L tokens.  Within a block the recurrence is
-// unrolled with the affine argument of the "Module gdn" page ("The fusion"),
-// carried across tokens: with S the state at the block start,
-//   S_i = A_{i+1} S + sum_{j<=i} (prod_{m=j+1..i} alpha_m) c_j k_j^T,
-//   A_i = prod_{m<i} alpha_m,   c_i = beta_i (v_i - alpha_i u_i),
-//   u_i = S_{i-1}.k_i = A_i (S.k_i) + sum_{j<i} P_ij c_j,
-//   o_i = S_i.q_i     = A_{i+1} (S.q_i) + sum_{j<=i} Q_ij c_j,
-// with P_ij = (prod_{m=j+1..i-1} alpha_m)(k_j.k_i) and
-// Q_ij = (prod_{m=j+1..i} alpha_m)(k_j.q_i) the same for every row of a head.
-// So the 2L dots of a row against the block-start state are independent, a
-// short L x L substitution per row gives every c_i and o_i, and the state
-// takes one rank-L update.  L = 1 is the plain per-token recurrence.
-template <int DT, int GT, int D, int CL, int RPL, int NW, int TC, int L, bool FUSE_NORM>
+// One multiplicative DPP step: x from the lane selected by CTRL, or 1 where
+// that lane lies outside the row or the row is masked off by ROW_MASK.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_one(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+
+// Inclusive prefix product over the 64 lanes of a wave (exec must be full):
+// Hillis-Steele inside each row of 16 (row_shr 1, 2, 4, 8), then the row
+// products carried forward (row_bcast 15 into rows 1 and 3, row_bcast 31 into
+// rows 2 and 3).
+__device__ __forceinline__ float wave_prefix_prod(float x) {
+  x *= dpp_or_one<0x111, 0xF>(x);
+  x *= dpp_or_one<0x112, 0xF>(x);
+  x *= dpp_or_one<0x114, 0xF>(x);
+  x *= dpp_or_one<0x118, 0xF>(x);
+  x *= dpp_or_one<0x142, 0xA>(x);
+  x *= dpp_or_one<0x143, 0xC>(x);
+  return x;
+}
+
+// The scan keeps each value head's state in VGPRs for the whole time axis
+// (rows split over lanes as in the decode kernel: CL lanes per row, RPL rows
+// per lane, NW waves, ROWS rows per workgroup) and processes the time axis in
+// chunks of TC tokens staged through LDS.  q and k are staged raw (f32); their
+// L2 norms and the q scale enter as per-token scalars rk, rq, and k^.q^.
+//
+// The state is kept as S = g * St with one FMA per element per token: with the
+// "Module gdn" page's step (module description) and its fused form ("The
+// fusion"), du = St.k, dw = St.q (raw vectors) and g_t the running decay
+// product inside the chunk (g_t = alpha_t g_{t-1}, 1 at the chunk start),
+//   coef' = v - g_t rk du              (= v - alpha u)
+//   o     = g_t rq dw + (beta k^.q^) coef'
+//   St   += (beta rk / g_t) coef' k    (S_t = alpha S_{t-1} + beta coef' k^)
+// When the chunk's |log_decay| sum is small (kFastLogSum) the four per-token
+// scalars g rk, g rq, beta rk / g and beta k^.q^ are formed for the whole chunk
+// at once (a prefix product of the decays across lanes) and the token loop
+// needs four scalar operations per row; otherwise the loop keeps g itself and
+// rescales St whenever g leaves [2^-30, 2^30].  St returns to scale 1 at every
+// chunk start.
+template <int DT, int GT, int D, int CL, int RPL, int NW, int TC, bool FUSE_NORM>
 __global__ __launch_bounds__(NW* kWave)
 __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArgs a) {
   constexpr int NCOL = D / CL, NV4 = NCOL / 4, RG = kWave / CL, ROWS = NW * RG * RPL;
   constexpr int NT = NW * kWave, D4 = D / 4, D8 = D / 8, R2 = ROWS / 2;
-  constexpr int LPT = D / 8;  // lanes per token in the norm pass (8 elements of q and k each)
-  constexpr int NB = TC / L;  // blocks per chunk
-  constexpr int NPB = L * (L - 1);  // off-diagonal Gram entries per block (k.k and k.q)
-  constexpr bool KEEP_K = L * NV4 <= 8;  // keep the block's k columns for the update
-  // Row-split shapes (one wave per SIMD, latency-bound) get a fully unrolled,
-  // unchecked token loop for chunks whose decay products stay in range.
-  constexpr bool UNROLL = !FUSE_NORM && L == 1 && NV4 * RPL <= 2;
+  // Row-split shapes (one wave per SIMD, latency-bound) get a fully unrolled
+  // chunk-scalar loop with the outputs buffered in registers.
+  constexpr bool UNROLL = !FUSE_NORM && NV4 * RPL <= 2;
+  // Two accumulators per dot product when the lane's row part is long (a
+  // shorter dependent chain); short parts keep one (fewer instructions).
+  constexpr bool SPLIT_U = NV4 >= 4, SPLIT_W = NV4 >= 4;
   static_assert(NCOL % 4 == 0, "a lane owns whole float4 chunks");
   static_assert(D % ROWS == 0 && ROWS % 4 == 0, "row blocks tile the head");
   static_assert(!FUSE_NORM || ROWS == D, "the fused norm needs the whole head");
-  static_assert(TC <= kWave && NT % LPT == 0 && TC % L == 0, "chunk shape");
-  static_assert(D / 8 <= 16, "a token's q/k groups span at most one DPP row");
-  static_assert(!FUSE_NORM || TC % NW == 0, "whole tokens per wave in the fused output");
+  static_assert(TC <= kWave && TC % NW == 0, "chunk shape");
+  static_assert(D8 <= 16, "a token's q/k groups span at most one DPP row");
   typedef ChunkRegs<DT, GT, D, ROWS, TC, NT, FUSE_NORM> Chunk;
-  __shared__ float4 sk[TC][D4];
+  __shared__ float4 sk[TC][D4];  // raw k and q of the chunk
   __shared__ float4 sq[TC][D4];
   __shared__ float sv[TC][ROWS];
   __shared__ float sz[FUSE_NORM ? 2 : 1][FUSE_NORM ? TC : 1][FUSE_NORM ? D : 1];
   __shared__ __align__(16) float so[TC][ROWS];
-  __shared__ float sal[TC], sbe[TC], skq[TC];
-  __shared__ float sP[NB][L][L], sQ[NB][L][L], sA[NB][L + 1], sR[NB][L], sAmin[NB], sAmax[NB];
-  __shared__ int sfast;  // the chunk's decay products stay inside the folding range
+  __shared__ float sal[TC], sbe[TC], srk[TC], srq[TC], skq[TC];
+  __shared__ float4 spv[NW][TC];  // chunk scalars per token, one copy per wave
+  __shared__ int sfast;           // the chunk takes the chunk-scalar loop
 
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int rb = (int)(tile % a.nrb);
@@ -149,13 +177,12 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
       P.be.load(a.beta, gi);
     }
   };
-  // Registers -> LDS, folding in the L2 norms and the q scale on the way: the
-  // D8 lanes holding one token's q and k are adjacent and aligned inside one
-  // DPP row, so the three dot products reduce across them.  Tokens tc..TC-1 of
-  // a short last chunk become identity steps (alpha = 1, beta = 0,
-  // k = q = v = 0), so whole blocks can always be processed.  FULL (tc == TC,
-  // every chunk but a short last one) drops the per-token tests, leaving
-  // straight-line code whose chains the compiler can interleave.
+  // Registers -> LDS, with the per-token norm scalars: the D8 lanes holding one
+  // token's q and k are adjacent and aligned inside one DPP row, so the three
+  // dot products reduce across them.  Tokens tc..TC-1 of a short last chunk
+  // become identity steps (alpha = 1, beta = 0, k = q = v = 0, rk = rq = 0).
+  // FULL (tc == TC, every chunk but a short last one) drops the per-token
+  // tests, leaving straight-line code whose chains the compiler interleaves.
   auto chunk_store = [&](const Chunk& P, int tc, int zbuf, auto full) {
     constexpr bool FULL = decltype(full)::value;
     constexpr bool ALL_E = (TC * D8) % NT == 0;  // every item index is in range
@@ -185,18 +212,20 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = tid + i * NT, tt = e / D8, c8 = e % D8;
-      // without the L2 fold the square roots see 1 and return 1
-      float rk = rsqrtf(l2 ? skk[i] + a.qk_eps : 1.f);
-      float rq = a.qscale * rsqrtf(l2 ? sqq[i] + a.qk_eps : 1.f);
-      if constexpr (!FULL) {
-        if (tt >= tc) rk = rq = 0.f;  // padding stays exactly zero even with eps == 0
-      }
       if (ALL_E || e < TC * D8) {
-        sk[tt][2 * c8] = scale4(P.k[i].get4(0), rk);
-        sk[tt][2 * c8 + 1] = scale4(P.k[i].get4(1), rk);
-        sq[tt][2 * c8] = scale4(P.q[i].get4(0), rq);
-        sq[tt][2 * c8 + 1] = scale4(P.q[i].get4(1), rq);
-        if (c8 == 0) skq[tt] = sqk[i] * rk * rq;
+        sk[tt][2 * c8] = P.k[i].get4(0);
+        sk[tt][2 * c8 + 1] = P.k[i].get4(1);
+        sq[tt][2 * c8] = P.q[i].get4(0);
+        sq[tt][2 * c8 + 1] = P.q[i].get4(1);
+        if (c8 == 0) {
+          // without the L2 fold the square roots see 1 and return 1
+          float rk = rsqrtf(l2 ? skk[i] + a.qk_eps : 1.f);
+          float rq = a.qscale * rsqrtf(l2 ? sqq[i] + a.qk_eps : 1.f);
+          if (!FULL && tt >= tc) rk = rq = 0.f;  // exact zeros even with eps == 0
+          srk[tt] = rk;
+          srq[tt] = rq;
+          skq[tt] = sqk[i] * rk * rq;
+        }
       }
     }
 #pragma unroll
@@ -219,11 +248,9 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
       sal[tid] = real ? expf(P.ld.get(0)) : 1.f;
       sbe[tid] = real ? P.be.get(0) : 0.f;
     }
-    if constexpr (UNROLL) {
-      if (wave == 0) {  // the chunk's decay products stay in the unchecked range
-        const float s = wave_sum(tid < tc ? fabsf(P.ld.get(0)) : 0.f);
-        if (tid == 0) sfast = s <= kFastLogSum ? 1 : 0;
-      }
+    if (wave == 0) {  // the chunk's decay products stay in the chunk-scalar range
+      const float sum = wave_sum(tid < tc ? fabsf(P.ld.get(0)) : 0.f);
+      if (tid == 0) sfast = sum <= kFastLogSum ? 1 : 0;
     }
   };
   auto stage = [&](const Chunk& P, int tc, int zbuf) {
@@ -285,6 +312,96 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
     }
   };
 
+  // du = St.k and dw = St.q for this lane's columns of its RPL rows (partial
+  // sums; the caller reduces them over the CL lanes of each row).
+  auto dots = [&](int tt, float4 (&kc)[NV4], float (&du)[RPL], float (&dw)[RPL]) {
+    float u1[RPL], w1[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) du[r] = dw[r] = u1[r] = w1[r] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV4; ++m) {
+      kc[m] = sk[tt][m * CL + j];
+      const float4 qc = sq[tt][m * CL + j];
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        if (SPLIT_U && (m & 1)) u1[r] = dot4(St[r][m], kc[m], u1[r]);
+        else du[r] = dot4(St[r][m], kc[m], du[r]);
+        if (SPLIT_W && (m & 1)) w1[r] = dot4(St[r][m], qc, w1[r]);
+        else dw[r] = dot4(St[r][m], qc, dw[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      du[r] = group_sum<CL>(SPLIT_U ? du[r] + u1[r] : du[r]);
+      dw[r] = group_sum<CL>(SPLIT_W ? dw[r] + w1[r] : dw[r]);
+    }
+  };
+  auto update = [&](const float4 (&kc)[NV4], const float (&c2)[RPL]) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+      for (int m = 0; m < NV4; ++m) {
+        St[r][m].x = fmaf(c2[r], kc[m].x, St[r][m].x);
+        St[r][m].y = fmaf(c2[r], kc[m].y, St[r][m].y);
+        St[r][m].z = fmaf(c2[r], kc[m].z, St[r][m].z);
+        St[r][m].w = fmaf(c2[r], kc[m].w, St[r][m].w);
+      }
+    }
+  };
+  // One token given its scalars pv = (g rk, g rq, beta rk / g, beta k^.q^)
+  // (g the state's scale after the token); resc first brings St from scale
+  // gn to scale 1 (then pv was formed with g = 1 in its third entry).
+  auto token = [&](int tt, const float4 pv, bool resc, float gn, float (&o)[RPL]) {
+    float4 kc[NV4];
+    float du[RPL], dw[RPL], c2[RPL];
+    dots(tt, kc, du, dw);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const float cf = fmaf(-pv.x, du[r], sv[tt][(wave * RPL + r) * RG + g]);
+      o[r] = fmaf(pv.y, dw[r], pv.w * cf);
+      c2[r] = cf * pv.z;
+    }
+    if (resc) {  // uniform, rare
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gn);
+    }
+    update(kc, c2);
+  };
+  // The scalars of one token when the loop keeps the scale itself: the new
+  // scale gn = alpha gsc is kept folded while it stays in [2^-30, 2^30];
+  // otherwise St is brought to scale 1 in the token (alpha == 0 lands here).
+  auto checked_scalars = [&](int tt, float4& pv, bool& resc, float& gn) {
+    const float al = sal[tt], be = sbe[tt], kq = skq[tt], rk = srk[tt], rq = srq[tt];
+    gn = gsc * al;
+    resc = !(gn >= kFoldMin && gn <= kFoldMax);
+    pv = make_float4(gn * rk, gn * rq, be * rk * (resc ? 1.f : __builtin_amdgcn_rcpf(gn)), be * kq);
+    gsc = resc ? 1.f : gn;
+  };
+  // The chunk scalars for every token at once, one token per lane (padding
+  // lanes: alpha = 1, rk = rq = beta = 0); each wave writes and reads its own
+  // copy.  Returns the chunk's decay product.
+  auto chunk_scalars = [&]() {
+    const int tl = lane < TC ? lane : 0;
+    const float gt = wave_prefix_prod(lane < TC ? sal[tl] : 1.f);
+    if (lane < TC) {
+      const float rk = srk[tl], be = sbe[tl];
+      spv[wave][lane] = make_float4(gt * rk, gt * srq[tl], be * rk * __builtin_amdgcn_rcpf(gt),
+                                    be * skq[tl]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt), TC - 1));
+  };
+  auto store_o = [&](int tt, const float (&o)[RPL]) {
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) so[tt][(wave * RPL + r) * RG + g] = o[r];
+    }
+  };
+
   Chunk P;
   chunk_load(P, 0, (int)(T < TC ? T : TC));
   stage(P, (int)(T < TC ? T : TC), 0);
@@ -299,285 +416,62 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
   for (int64_t c = 0;; ++c) {
     const int64_t t0 = c * TC;
     const int tc = (int)((T - t0) < TC ? (T - t0) : TC);
-    const int nblk = (tc + L - 1) / L;
     const bool more = t0 + TC < T;
     const int tcn = more ? (int)((T - t0 - TC) < TC ? (T - t0 - TC) : TC) : 0;
     __syncthreads();
     if (more) chunk_load(P, t0 + TC, tcn);
 
-    if constexpr (L > 1) {
-      // B. per-block coefficients shared by every row: the off-diagonal Gram
-      //     entries times their decay products, and the decay prefixes.
-      for (int x = tid / LPT; x < NB * NPB; x += NT / LPT) {
-        const int p = tid % LPT;
-        const int bk = x / NPB, y = x % NPB, kind = y / (NPB / 2);
-        int pr = y % (NPB / 2), i = 1;
-        while (pr >= i) { pr -= i; ++i; }
-        const int jj = pr;  // j < i
-        const int ti = bk * L + i, tj = bk * L + jj;
-        const float4* other = kind ? sq[ti] : sk[ti];
-        float dv = dot4(sk[tj][2 * p], other[2 * p], 0.f);
-        dv = dot4(sk[tj][2 * p + 1], other[2 * p + 1], dv);
-        dv = group_sum<LPT>(dv);
-        if (p == 0) {
-          float prod = 1.f;
-          for (int m = jj + 1; m < i; ++m) prod *= sal[bk * L + m];
-          if (kind) sQ[bk][i][jj] = dv * prod * sal[ti];
-          else sP[bk][i][jj] = dv * prod;
-        }
-      }
-      if (tid < NB) {
-        const int bk = tid;
-        float acc = 1.f, amin = 3.0e38f, amax = 0.f;
-        sA[bk][0] = 1.f;
-        for (int i = 0; i < L; ++i) {
-          acc *= sal[bk * L + i];
-          sA[bk][i + 1] = acc;
-          amin = fminf(amin, acc);
-          amax = fmaxf(amax, acc);
-          sQ[bk][i][i] = skq[bk * L + i];
-        }
-        sAmin[bk] = amin;
-        sAmax[bk] = amax;
-        float rr = 1.f;
-        for (int i = L - 1; i >= 0; --i) {
-          sR[bk][i] = rr;
-          rr *= sal[bk * L + i];
-        }
-      }
-      __syncthreads();
-    }
-
-    // C. the recurrence: token by token (L == 1) or one block of L tokens after the other.  With
-    //    S = gsc*St the update becomes St += sum_j c_j/(gsc*A_{j+1}) k_j and
-    //    gsc *= A_L: one FMA per state element per token.  When the scale
-    //    would leave [2^-30, 2^30] (and whenever an alpha is 0) St is brought
-    //    to the block's end scale in place and the scale restarts at 1.
-    // Bring the state to scale 1 at the chunk start (one multiply per element
-    // per chunk); when the chunk's decay products stay in range the whole chunk
-    // then runs without per-token range checks.
+    // C. the recurrence.  St to scale 1 at the chunk start (one multiply per
+    //    element per chunk).
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
 #pragma unroll
       for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gsc);
     gsc = 1.f;
-    auto checked_tokens = [&]() {
-        // one token at a time with range checks: St += (coef/gsc') k with
-        // gsc' = alpha*gsc, or a rescale of St when gsc' leaves the range
-        for (int tt = 0; tt < tc; ++tt) {
-          const float al = sal[tt], be = sbe[tt], kq = skq[tt];
-          const float gn = gsc * al;
-          const bool rescale = !(gn >= kFoldMin && gn <= kFoldMax);  // uniform, rare
-          const float gnext = rescale ? 1.f : gn;
-          const float ig = rescale ? 1.f : __builtin_amdgcn_rcpf(gn);
-          float4 kc[NV4];
-          float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
-#pragma unroll
-          for (int m = 0; m < NV4; ++m) {
-            kc[m] = sk[tt][m * CL + j];
-            const float4 qc = sq[tt][m * CL + j];
-#pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-              if (m & 1) {
-                u1[r] = dot4(St[r][m], kc[m], u1[r]);
-                w1[r] = dot4(St[r][m], qc, w1[r]);
-              } else {
-                u0[r] = dot4(St[r][m], kc[m], u0[r]);
-                w0[r] = dot4(St[r][m], qc, w0[r]);
-              }
-            }
-          }
-          float c2[RPL];
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) {
-            const int lr = (wave * RPL + r) * RG + g;
-            const float u = group_sum<CL>(u0[r] + u1[r]) * gsc;
-            const float wq = group_sum<CL>(w0[r] + w1[r]) * gsc;
-            const float coef = be * (sv[tt][lr] - al * u);
-            if (j == 0) so[tt][lr] = al * wq + coef * kq;
-            c2[r] = coef * ig;
-          }
-          if (rescale) {
-#pragma unroll
-            for (int r = 0; r < RPL; ++r)
-#pragma unroll
-              for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gn);
-          }
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) {
-#pragma unroll
-            for (int m = 0; m < NV4; ++m) {
-              St[r][m].x = fmaf(c2[r], kc[m].x, St[r][m].x);
-              St[r][m].y = fmaf(c2[r], kc[m].y, St[r][m].y);
-              St[r][m].z = fmaf(c2[r], kc[m].z, St[r][m].z);
-              St[r][m].w = fmaf(c2[r], kc[m].w, St[r][m].w);
-            }
-          }
-          gsc = gnext;
-        }
-    };
     if constexpr (UNROLL) {
       if (sfast != 0) {
-      // one token at a time, unchecked: St += (coef/g_t) k with g_t the running
-        // decay product; short chunks are padded with identity tokens
-        float obuf[UNROLL ? TC : 1][RPL];
-#pragma unroll(UNROLL ? TC : 1)
-        for (int tt = 0; tt < (UNROLL ? TC : tc); ++tt) {
-          const float al = sal[tt], be = sbe[tt], kq = skq[tt];
-          const float gn = gsc * al;
-          const float ig = __builtin_amdgcn_rcpf(gn);
-          float4 kc[NV4];
-          float u0[RPL], u1[RPL], w0[RPL], w1[RPL];
+        const float gl = chunk_scalars();
+        float obuf[TC][RPL];
 #pragma unroll
-          for (int r = 0; r < RPL; ++r) u0[r] = u1[r] = w0[r] = w1[r] = 0.f;
+        for (int tt = 0; tt < TC; ++tt) token(tt, spv[wave][tt], false, 1.f, obuf[tt]);
 #pragma unroll
-          for (int m = 0; m < NV4; ++m) {
-            kc[m] = sk[tt][m * CL + j];
-            const float4 qc = sq[tt][m * CL + j];
-#pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-              if (m & 1) {
-                u1[r] = dot4(St[r][m], kc[m], u1[r]);
-                w1[r] = dot4(St[r][m], qc, w1[r]);
-              } else {
-                u0[r] = dot4(St[r][m], kc[m], u0[r]);
-                w0[r] = dot4(St[r][m], qc, w0[r]);
-              }
-            }
-          }
-          float c2[RPL];
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) {
-            const int lr = (wave * RPL + r) * RG + g;
-            const float u = group_sum<CL>(u0[r] + u1[r]) * gsc;
-            const float wq = group_sum<CL>(w0[r] + w1[r]) * gsc;
-            const float coef = be * (sv[tt][lr] - al * u);
-            const float o = al * wq + coef * kq;
-            if constexpr (UNROLL) {
-              obuf[tt][r] = o;
-            } else {
-              if (j == 0) so[tt][lr] = o;
-            }
-            c2[r] = coef * ig;
-          }
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) {
-#pragma unroll
-            for (int m = 0; m < NV4; ++m) {
-              St[r][m].x = fmaf(c2[r], kc[m].x, St[r][m].x);
-              St[r][m].y = fmaf(c2[r], kc[m].y, St[r][m].y);
-              St[r][m].z = fmaf(c2[r], kc[m].z, St[r][m].z);
-              St[r][m].w = fmaf(c2[r], kc[m].w, St[r][m].w);
-            }
-          }
-          gsc = gn;
-        }
-        if constexpr (UNROLL) {
-          if (j == 0) {
-#pragma unroll
-            for (int tt = 0; tt < TC; ++tt)
-#pragma unroll
-              for (int r = 0; r < RPL; ++r) so[tt][(wave * RPL + r) * RG + g] = obuf[tt][r];
-          }
-        }
+        for (int tt = 0; tt < TC; ++tt) store_o(tt, obuf[tt]);
+        gsc = gl;
       } else {
-        checked_tokens();
+#pragma unroll 1
+        for (int tt = 0; tt < tc; ++tt) {
+          float4 pv;
+          bool resc;
+          float gn, o[RPL];
+          checked_scalars(tt, pv, resc, gn);
+          token(tt, pv, resc, gn, o);
+          store_o(tt, o);
+        }
       }
-    } else if constexpr (L == 1) {
-      checked_tokens();
     } else {
-      for (int bk = 0; bk < nblk; ++bk) {
-        const int tb = bk * L;
-        float4 kreg[KEEP_K ? L : 1][KEEP_K ? NV4 : 1];
-        float d[RPL][L], e[RPL][L];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r)
-#pragma unroll
-          for (int i = 0; i < L; ++i) d[r][i] = e[r][i] = 0.f;
-#pragma unroll
-        for (int m = 0; m < NV4; ++m) {
-#pragma unroll
-          for (int i = 0; i < L; ++i) {
-            const float4 kc = sk[tb + i][m * CL + j];
-            const float4 qc = sq[tb + i][m * CL + j];
-            if constexpr (KEEP_K) kreg[i][m] = kc;
-#pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-              d[r][i] = dot4(St[r][m], kc, d[r][i]);
-              e[r][i] = dot4(St[r][m], qc, e[r][i]);
-            }
-          }
-        }
-        float cc[RPL][L];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          const int lr = (wave * RPL + r) * RG + g;
-#pragma unroll
-          for (int i = 0; i < L; ++i) {
-            d[r][i] = group_sum<CL>(d[r][i]) * gsc;
-            e[r][i] = group_sum<CL>(e[r][i]) * gsc;
-          }
-#pragma unroll
-          for (int i = 0; i < L; ++i) {
-            float u = sA[bk][i] * d[r][i];
-#pragma unroll
-            for (int jj = 0; jj < i; ++jj) u = fmaf(sP[bk][i][jj], cc[r][jj], u);
-            cc[r][i] = sbe[tb + i] * (sv[tb + i][lr] - sal[tb + i] * u);
-          }
-#pragma unroll
-          for (int i = 0; i < L; ++i) {
-            float o = sA[bk][i + 1] * e[r][i];
-#pragma unroll
-            for (int jj = 0; jj <= i; ++jj) o = fmaf(sQ[bk][i][jj], cc[r][jj], o);
-            if (j == 0) so[tb + i][lr] = o;
-          }
-        }
-        const bool fold = gsc * sAmin[bk] >= kFoldMin && gsc * sAmax[bk] <= kFoldMax;  // uniform
-        float f[L];
-        if (fold) {
-#pragma unroll
-          for (int i = 0; i < L; ++i) f[i] = __builtin_amdgcn_rcpf(gsc * sA[bk][i + 1]);
-        } else {
-          const float gl = gsc * sA[bk][L];
-#pragma unroll
-          for (int i = 0; i < L; ++i) f[i] = sR[bk][i];
-#pragma unroll
-          for (int r = 0; r < RPL; ++r)
-#pragma unroll
-            for (int m = 0; m < NV4; ++m) St[r][m] = scale4(St[r][m], gl);
-        }
-#pragma unroll
-        for (int r = 0; r < RPL; ++r)
-#pragma unroll
-          for (int i = 0; i < L; ++i) cc[r][i] *= f[i];
-#pragma unroll
-        for (int m = 0; m < NV4; ++m) {
-#pragma unroll
-          for (int i = 0; i < L; ++i) {
-            float4 kc;
-            if constexpr (KEEP_K) kc = kreg[i][m];
-            else kc = sk[tb + i][m * CL + j];
-#pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-              St[r][m].x = fmaf(cc[r][i], kc.x, St[r][m].x);
-              St[r][m].y = fmaf(cc[r][i], kc.y, St[r][m].y);
-              St[r][m].z = fmaf(cc[r][i], kc.z, St[r][m].z);
-              St[r][m].w = fmaf(cc[r][i], kc.w, St[r][m].w);
-            }
-          }
-        }
-        gsc = fold ? gsc * sA[bk][L] : 1.f;
+      // one loop body for both kinds of chunk keeps the register pressure of one
+      const bool fast = sfast != 0;
+      float gl = 1.f;
+      if (fast) gl = chunk_scalars();
+#pragma unroll 1
+      for (int tt = 0; tt < tc; ++tt) {
+        float4 pv;
+        bool resc = false;
+        float gn = 1.f, o[RPL];
+        if (fast) pv = spv[wave][tt];
+        else checked_scalars(tt, pv, resc, gn);
+        token(tt, pv, resc, gn, o);
+        store_o(tt, o);
       }
+      if (fast) gsc = gl;
     }
     __syncthreads();
 
-    // next chunk into LDS: sk/sq/sv/gates/block coefficients were last read in
-    // phase C, before the barrier above; z is double-buffered because phase D
-    // below still reads this chunk's slot.  After the last chunk this stages
-    // an empty chunk (tcn == 0): unconditional, so that its wait for the loads
-    // lies on every path through the loop.
+    // next chunk into LDS: every chunk array was last read in phase C, before
+    // the barrier above; z is double-buffered because phase D below still
+    // reads this chunk's slot.  After the last chunk this stages an empty
+    // chunk (tcn == 0): unconditional, so that its wait for the loads lies on
+    // every path through the loop.
     stage(P, tcn, (int)((c + 1) & 1));
 
     // D. write this chunk's outputs (gated here when the workgroup owns the head)
@@ -642,16 +536,16 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z
 
 }  // namespace
 
-template <int DT, int GT, int D, int CL, int RPL, int NW, int TC, int L>
+template <int DT, int GT, int D, int CL, int RPL, int NW, int TC>
 int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
   constexpr int ROWS = NW * (kWave / CL) * RPL;
   a.nrb = D / ROWS;
   const dim3 grid((unsigned)(heads * a.nrb));
   if constexpr (ROWS == D) {
-    scan_kernel<DT, GT, D, CL, RPL, NW, TC, L, true><<<grid, NW * kWave, 0, st>>>(a);
+    scan_kernel<DT, GT, D, CL, RPL, NW, TC, true><<<grid, NW * kWave, 0, st>>>(a);
     return device_status("scan_kernel launch");
   } else {
-    scan_kernel<DT, GT, D, CL, RPL, NW, TC, L, false><<<grid, NW * kWave, 0, st>>>(a);
+    scan_kernel<DT, GT, D, CL, RPL, NW, TC, false><<<grid, NW * kWave, 0, st>>>(a);
     int rc = device_status("scan_kernel launch");
     if (rc != GDN_OK || a.z == nullptr) return rc;
     const int64_t nvec = heads * a.T;
@@ -667,14 +561,14 @@ int launch_scan_dt(const ScanArgs& a, int D, int64_t heads, hipStream_t st) {
     case 128:
       // enough heads to fill the chip with whole-head workgroups: keep the
       // norm fused; otherwise split each head's rows over more workgroups
-      if (heads >= 512) return launch_scan_cfg<DT, GT, 128, 4, 2, 4, 16, 1>(a, heads, st);
-      if (heads >= 128) return launch_scan_cfg<DT, GT, 128, 8, 1, 4, 16, 1>(a, heads, st);
-      return launch_scan_cfg<DT, GT, 128, 16, 1, 4, 32, 1>(a, heads, st);
+      if (heads >= 512) return launch_scan_cfg<DT, GT, 128, 4, 2, 4, 16>(a, heads, st);
+      if (heads >= 128) return launch_scan_cfg<DT, GT, 128, 8, 1, 4, 16>(a, heads, st);
+      return launch_scan_cfg<DT, GT, 128, 16, 1, 4, 32>(a, heads, st);
     case 64:
-      if (heads >= 256) return launch_scan_cfg<DT, GT, 64, 4, 1, 4, 32, 1>(a, heads, st);
-      return launch_scan_cfg<DT, GT, 64, 8, 1, 2, 32, 1>(a, heads, st);
-    case 32: return launch_scan_cfg<DT, GT, 32, 4, 1, 2, 32, 1>(a, heads, st);
-    case 16: return launch_scan_cfg<DT, GT, 16, 4, 1, 1, 32, 1>(a, heads, st);
+      if (heads >= 256) return launch_scan_cfg<DT, GT, 64, 4, 1, 4, 32>(a, heads, st);
+      return launch_scan_cfg<DT, GT, 64, 8, 1, 2, 32>(a, heads, st);
+    case 32: return launch_scan_cfg<DT, GT, 32, 4, 1, 2, 32>(a, heads, st);
+    case 16: return launch_scan_cfg<DT, GT, 16, 4, 1, 1, 32>(a, heads, st);
     default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
   }
 }

@@ -222,6 +222,39 @@ def test_degenerate_gates_and_zero_vectors():
     assert torch.all(y[0, 9] == 0)
 
 
+MIXED = [
+    # (B, T, Hk, Hv, D, dtype, head_major): one shape per kernel variant
+    (1, 100, 2, 4, 128, "f32", False),   # narrow row split (unrolled chunk loop)
+    (4, 70, 16, 32, 128, "bf16", True),  # mid row split
+    (16, 40, 8, 32, 128, "f32", False),  # whole-head workgroups, fused norm
+    (2, 90, 2, 4, 64, "f16", False),     # D=64 row split
+    (8, 70, 16, 32, 64, "f32", True),    # D=64 whole-head
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=lambda c: "B%dT%dHv%dD%d-%s" % (
+    c[0], c[1], c[3], c[4], c[5]))
+def test_mixed_fast_and_checked_chunks(case):
+    """Chunks whose decays stay mild take the chunk-scalar loop; chunks with a
+    large |log_decay| sum, an alpha of 0 or growth (alpha > 1) take the loop
+    that keeps the scale per token.  Both kinds alternate along one sequence."""
+    B, T, Hk, Hv, D, dtype, hm = case
+    say("mixed %s" % (case,))
+    ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm, seed=T + D)
+    ld = ops["log_decay"]
+
+    def at(t):  # index of token t in either gate layout
+        return (slice(None), slice(None), t) if hm else (slice(None), t)
+
+    ld[at(20)] = -45.0                   # one token past the chunk bound
+    ld[at(min(T - 1, 37))] = -math.inf   # alpha = 0
+    for t in range(50, min(T, 60)):
+        ld[at(t)] = 0.3                  # growth over ten tokens
+    for t in range(3, 9):
+        ld[at(t)] = -6.5                 # six strong decays: a sum near the bound
+    run_both(ops, head_major=hm, gated=True, dtype=dtype)
+
+
 def test_in_place_state_and_time_chaining():
     ops = synth.random_operands(2, 40, 2, 4, 128, 128, dtype="bf16", seed=9)
     d = dev(ops)
