@@ -91,6 +91,47 @@ void gdn_oracle_gates(int64_t n, const double* a, const double* b, double decay_
   }
 }
 
+/* Causal depthwise convolution over the time axis, optionally followed by
+ * silu: the producer of q, k and v ("Module gdn" page, QWEN38_KERNELS: the
+ * convolution carries the silu).  The pages give neither the width nor the
+ * weight layout; the reading used here is the usual causal form, one filter of
+ * W taps per channel with the last tap on the current token:
+ *   pre[b,t,c] = bias[c] + sum_{i<W} w[c][i] * xx(b, t - (W-1) + i, c)
+ *   xx(b,t',c) = x[b][t'][c] for t' >= 0, else the carried context
+ *                state_in[b][c][(W-1) + t'] (zero when there is none)
+ *   y = pre * sigmoid(pre)  (act != 0)  or  y = pre
+ *   state_out[b][c][j] = xx(b, T - (W-1) + j, c)  for j < W-1
+ * x, y: [B][T][C]; w: [C][W]; bias: [C] or NULL; state_in, state_out:
+ * [B][C][W-1] or NULL. */
+void gdn_oracle_conv(int64_t B, int64_t T, int64_t C, int64_t W, int act, const double* x,
+                     const double* w, const double* bias, const double* state_in, double* y,
+                     double* state_out) {
+  const int64_t K = W - 1; /* carried context per channel */
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t c = 0; c < C; ++c) {
+      for (int64_t t = -K; t < T; ++t) {
+        /* xx at time t, for the state output */
+        if (state_out && t >= T - K) {
+          double v = 0.0;
+          if (t >= 0) v = x[(b * T + t) * C + c];
+          else if (state_in) v = state_in[(b * C + c) * K + (K + t)];
+          state_out[(b * C + c) * K + (t - (T - K))] = v;
+        }
+        if (t < 0) continue;
+        double pre = bias ? bias[c] : 0.0;
+        for (int64_t i = 0; i < W; ++i) {
+          const int64_t tt = t - K + i;
+          double v = 0.0;
+          if (tt >= 0) v = x[(b * T + tt) * C + c];
+          else if (state_in) v = state_in[(b * C + c) * K + (K + tt)];
+          pre += w[c * W + i] * v;
+        }
+        y[(b * T + t) * C + c] = act ? pre / (1.0 + exp(-pre)) : pre;
+      }
+    }
+  }
+}
+
 typedef struct {
   int64_t B, T, Hk, Hv, Dk, Dv;
   uint32_t flags;

@@ -14,6 +14,10 @@ transposed to token-major before the call and the output is transposed back.
 
 Inputs may be numpy arrays or torch tensors of any float dtype; they are
 widened to float64 exactly.  Outputs are float64 numpy arrays.
+
+``gates`` and ``conv_silu`` are the two producers next to the recurrence
+("Module gdn" page, QWEN38_KERNELS): both gates from their pre-activations,
+and the causal convolution with silu that produces q, k and v.
 """
 from __future__ import annotations
 
@@ -58,6 +62,8 @@ def _load():
         lib.gdn_oracle_l2norm.argtypes = [dp, i64, ctypes.c_double]
         lib.gdn_oracle_gates.restype = None
         lib.gdn_oracle_gates.argtypes = [i64, dp, dp, ctypes.c_double, dp, dp]
+        lib.gdn_oracle_conv.restype = None
+        lib.gdn_oracle_conv.argtypes = [i64, i64, i64, i64, ctypes.c_int] + [dp] * 6
         lib.gdn_oracle_gated_rmsnorm.restype = None
         lib.gdn_oracle_gated_rmsnorm.argtypes = [dp, dp, dp, i64, ctypes.c_double, dp]
         _lib = lib
@@ -161,6 +167,27 @@ def gates(a, b, decay_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
     be = np.empty_like(b)
     _load().gdn_oracle_gates(a.size, _ptr(a), _ptr(b), decay_scale, _ptr(ld), _ptr(be))
     return ld, be
+
+
+def conv_silu(x, weight, bias=None, state=None, *, apply_silu: bool = True):
+    """Causal depthwise convolution over time, then silu ("Module gdn" page,
+    QWEN38_KERNELS: the convolution carries the silu).  x: [B, T, C]; weight:
+    [C, W] (tap W-1 on the current token); bias: [C]; state: [B, C, W-1], the
+    W-1 inputs before x (zeros when None).  Returns (y [B, T, C], state_out
+    [B, C, W-1] = the last W-1 inputs), float64."""
+    x, weight, bias, state = map(_f64, (x, weight, bias, state))
+    B, T, C = x.shape
+    W = weight.shape[1]
+    assert weight.shape == (C, W) and W >= 1
+    if bias is not None:
+        assert bias.shape == (C,)
+    if state is not None:
+        assert state.shape == (B, C, W - 1)
+    y = np.empty((B, T, C), dtype=np.float64)
+    st = np.empty((B, C, W - 1), dtype=np.float64)
+    _load().gdn_oracle_conv(B, T, C, W, int(bool(apply_silu)), _ptr(x), _ptr(weight), _ptr(bias),
+                            _ptr(state), _ptr(y), _ptr(st))
+    return y, st
 
 
 def select_heads(ops: dict, heads, *, head_major: bool) -> dict:

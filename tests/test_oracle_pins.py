@@ -392,3 +392,83 @@ def test_gate_producer_matches_library_routines():
     np.testing.assert_allclose(ld, -0.01 * np.logaddexp(0.0, a), rtol=1e-14)
     from scipy.special import expit
     np.testing.assert_allclose(be, expit(b), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- conv + silu producer
+def _conv_operands(seed, B=2, T=9, C=5, W=4, state=True, bias=True):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((B, T, C))
+    w = r.standard_normal((C, W))
+    b = r.standard_normal(C) if bias else None
+    s = r.standard_normal((B, C, W - 1)) if state else None
+    return x, w, b, s
+
+
+@pytest.mark.parametrize("W", [1, 2, 4, 6])
+def test_conv_linear_part_matches_numpy_correlate(W):
+    """Without the silu, each channel is a cross-correlation of its carried
+    context followed by its inputs with the channel's taps (numpy.correlate,
+    'valid' mode), plus the bias."""
+    x, w, b, s = _conv_operands(40 + W, W=W)
+    pre, _ = orc.conv_silu(x, w, b, s, apply_silu=False)
+    B, T, C = x.shape
+    for bb in range(B):
+        for c in range(C):
+            xx = np.concatenate([s[bb, c], x[bb, :, c]])
+            ref = np.correlate(xx, w[c], mode="valid") + b[c]
+            np.testing.assert_allclose(pre[bb, :, c], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv_silu_is_pre_times_sigmoid():
+    from scipy.special import expit
+    x, w, b, s = _conv_operands(50, T=12, C=7)
+    pre, _ = orc.conv_silu(x, w, b, s, apply_silu=False)
+    y, _ = orc.conv_silu(x, w, b, s)
+    np.testing.assert_allclose(y, pre * expit(pre), rtol=1e-13, atol=1e-15)
+
+
+def test_conv_impulse_response():
+    """A unit impulse at (t0, c0) with no bias and no context gives
+    silu(w[c0, W-1-i]) at t0 + i for i < W, and exactly zero elsewhere."""
+    B, T, C, W = 1, 11, 3, 4
+    w = np.random.default_rng(51).standard_normal((C, W))
+    x = np.zeros((B, T, C))
+    x[0, 4, 1] = 1.0
+    y, st = orc.conv_silu(x, w)
+    silu = lambda v: v / (1.0 + math.exp(-v))  # noqa: E731
+    expect = np.zeros((B, T, C))
+    for i in range(W):
+        expect[0, 4 + i, 1] = silu(w[1, W - 1 - i])
+    np.testing.assert_allclose(y, expect, rtol=1e-15, atol=0)
+    assert np.all(st == 0.0)
+
+
+def test_conv_width_one_is_elementwise():
+    x, w, b, _ = _conv_operands(52, W=1, state=False)
+    y, st = orc.conv_silu(x, w, b)
+    pre = x * w[:, 0] + b
+    np.testing.assert_allclose(y, pre / (1.0 + np.exp(-pre)), rtol=1e-14)
+    assert st.shape == (x.shape[0], x.shape[2], 0)
+
+
+def test_conv_time_chaining_through_the_state():
+    """Splitting the time axis and carrying the last W-1 inputs as the state
+    reproduces the whole sequence exactly; with fewer than W-1 new tokens the
+    state is a shift register over the old state and the new inputs."""
+    x, w, b, s = _conv_operands(53, T=10, C=6, W=4)
+    y, st = orc.conv_silu(x, w, b, s)
+    for T1 in (1, 2, 3, 7):
+        y1, s1 = orc.conv_silu(x[:, :T1], w, b, s)
+        y2, s2 = orc.conv_silu(x[:, T1:], w, b, s1)
+        assert np.array_equal(np.concatenate([y1, y2], axis=1), y)
+        assert np.array_equal(s2, st)
+    # state after two tokens: the last old entry, then the two inputs
+    _, s2 = orc.conv_silu(x[:, :2], w, b, s)
+    np.testing.assert_array_equal(s2[:, :, 0], s[:, :, 2])
+    np.testing.assert_array_equal(s2[:, :, 1:], x[:, :2].transpose(0, 2, 1))
+    # no context is the same as a zero context; T = 0 returns the context
+    y0, _ = orc.conv_silu(x, w, b, np.zeros_like(s))
+    yn, _ = orc.conv_silu(x, w, b, None)
+    assert np.array_equal(y0, yn)
+    ye, se = orc.conv_silu(x[:, :0], w, b, s)
+    assert ye.shape == (2, 0, 6) and np.array_equal(se, s)
