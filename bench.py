@@ -17,7 +17,8 @@ average launch time (HIP events on the launch stream over the timed region),
 against MI355X's 8 TB/s; ``traffic`` comes from the committed rocprofv3
 FETCH_SIZE/WRITE_SIZE summary when it was taken on the current kernel source.
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
-workload on this host.
+workload on this host.  ``gate_producer`` and ``conv_producer`` time the two
+producers next to the recurrence (HBM-bound, algorithmic GB/s).
 """
 from __future__ import annotations
 
@@ -236,6 +237,48 @@ def bench_gates(args, torch):
             "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "dtype": "f16"}
 
 
+def bench_conv(args, torch):
+    """Conv + silu producer (W=4, bf16) on the q/k/v channels of the scan's heads:
+    C = 2*Hk*D + Hv*D = 8192.  Prefill: B=1, T=4096, no context.  Decode: B=64,
+    T=1 with its [B, C, 3] context updated in place.  HBM-bound: algorithmic
+    bytes = x read + y written + carried context read and written + weights."""
+    from linear_attention_recurrence_recurrent_amd import _native
+    L = _native.lib()
+    C, W, es = 2 * 16 * 128 + 32 * 128, 4, 2
+    g = torch.Generator(device="cpu").manual_seed(7)
+    out = {}
+    for name, B, T, with_state in (("prefill_b1_t4096_c8192_w4_bf16", 1, 4096, False),
+                                   ("decode_b64_t1_c8192_w4_bf16", 64, 1, True)):
+        x = torch.randn((B, T, C), generator=g).to(torch.bfloat16).cuda()
+        w = (torch.randn((C, W), generator=g) * 0.5).to(torch.bfloat16).cuda()
+        y = torch.empty_like(x)
+        st = torch.randn((B, C, W - 1), generator=g).to(torch.bfloat16).cuda() if with_state \
+            else None
+        stream = torch.cuda.current_stream()
+        vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        args_c = (B, T, C, W, 2, 1, vp(x), vp(w), None, vp(st), vp(y), vp(st),
+                  ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(3):
+            assert L.gdn_conv_silu(*args_c) == 0
+        torch.cuda.synchronize()
+        reps = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            L.gdn_conv_silu(*args_c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = 2 * B * T * C * es + C * W * es + (2 * B * C * (W - 1) * es if with_state else 0)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log("conv %s: %.2f us per launch, %.1f GB/s" % (name, us, gbs))
+        out[name] = {"us_per_launch": round(us, 2), "algorithmic_bytes_per_launch": nbytes,
+                     "gbs": round(gbs, 1), "peak_gbs": HBM_PEAK_GBS,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+                     "tokens_per_s": round(B * T / (us * 1e-6), 1)}
+    return out
+
+
 def cpu_baseline(ops, args):
     """The float64 oracle on the whole decode chain (100 chained steps of all 64
     sequences == the scan over 100 tokens), repeated until about ``cpu_seconds``
@@ -327,6 +370,7 @@ def main():
         out["scan"] = scan
     if not args.no_scan:
         out["gate_producer"] = bench_gates(args, torch)
+        out["conv_producer"] = bench_conv(args, torch)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(ops, args)
     print(json.dumps(out), flush=True)

@@ -134,6 +134,30 @@ int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
 int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,
               void* log_decay, void* beta, int32_t out_dtype, void* stream);
 
+/* Producer of q, k and v: causal depthwise convolution over the time axis with
+ * the silu fused in ("Module gdn" page, QWEN38_KERNELS: the convolution
+ * carries the silu).  The pages give neither the width nor the weight layout;
+ * this is the usual causal form, one filter of W taps per channel with the
+ * last tap on the current token:
+ *     pre[b,t,c] = bias[c] + sum_{i<W} w[c*W + i] * xx(b, t - (W-1) + i, c)
+ *     xx(b,t',c) = x[(b*T + t')*C + c] for t' >= 0, else the carried context
+ *                  state_in[(b*C + c)*(W-1) + (W-1) + t'] (zero when NULL)
+ *     y[(b*T + t)*C + c] = apply_silu ? pre * sigmoid(pre) : pre
+ *     state_out[(b*C + c)*(W-1) + j] = xx(b, T - (W-1) + j, c),  j < W-1
+ * x, y: [B, T, C]; w: [C, W]; bias: [C] or NULL; state_in, state_out:
+ * [B, C, W-1] or NULL (state_out NULL: not written).  Every tensor is dtype
+ * (y rounded to nearest even for 16-bit types; the state holds exact copies of
+ * inputs).  1 <= W <= 8.  Device pointers aligned to the element size
+ * (16-byte alignment of x and y and C % 4 == 0 take the vector path).
+ * state_out may be exactly state_in (updated in place); any other overlap of
+ * an output with an operand is GDN_EALIAS.  T == 0 only writes state_out
+ * (= state_in, or zeros).  Decode is T == 1 with a state.  Asynchronous on
+ * `stream`, allocates nothing; returns GDN_OK or a gdn_status with its reason
+ * in gdn_last_error(). */
+int gdn_conv_silu(int64_t B, int64_t T, int64_t C, int32_t W, int32_t dtype, int32_t apply_silu,
+                  const void* x, const void* w, const void* bias, const void* state_in, void* y,
+                  void* state_out, void* stream);
+
 /* Validation only, no device work: GDN_OK when gdn_scan would accept these
  * arguments, else the status with its short reason in gdn_last_error()
  * ("gated_delta" page, native_gdn_reject_reason: why operands cannot become

@@ -19,7 +19,7 @@ import torch
 from . import _native
 from ._native import GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GdnDesc
 
-__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "gates", "check",
+__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "gates", "conv_silu", "check",
            "abi_version", "GdnError"]
 
 _DT = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
@@ -200,6 +200,49 @@ def gates(a: torch.Tensor, b: torch.Tensor, *, decay_scale: float = 1.0,
             raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
         raise GdnError(rc, reason)
     return ld, be
+
+
+def conv_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+              state: Optional[torch.Tensor] = None, *, apply_silu: bool = True,
+              inplace: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Causal depthwise convolution over time with silu, one launch: the
+    producer of q, k and v ("Module gdn" page, QWEN38_KERNELS).  x: [B, T, C];
+    weight: [C, W] (tap W-1 on the current token); bias: [C]; state: the
+    [B, C, W-1] inputs before x (None: zeros).  Returns (y [B, T, C] in x's
+    dtype, new state [B, C, W-1] = the last W-1 inputs); ``inplace`` writes the
+    new state into ``state``."""
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[2]:
+        raise GdnError(2, "x must be [B, T, C] and weight [C, W]")
+    B, T, C = x.shape
+    W = weight.shape[1]
+    if x.device.type != "cuda":
+        raise GdnError(8, "operands must be on a GPU device")
+    for n, t in (("weight", weight), ("bias", bias), ("state", state)):
+        if t is not None and (t.dtype != x.dtype or t.device != x.device):
+            raise GdnError(3, "%s must match x in dtype and device" % n)
+    if bias is not None and tuple(bias.shape) != (C,):
+        raise GdnError(2, "bias must have shape (%d,)" % C)
+    if state is not None and tuple(state.shape) != (B, C, W - 1):
+        raise GdnError(2, "state must have shape %s" % ((B, C, W - 1),))
+    for n, t in (("x", x), ("weight", weight), ("bias", bias), ("state", state)):
+        if t is not None and not t.is_contiguous():
+            raise GdnError(1, "%s must be contiguous" % n)
+    if inplace and state is None:
+        raise GdnError(1, "inplace needs a state")
+    y = torch.empty_like(x)
+    new_state = state if inplace else torch.empty((B, C, W - 1), dtype=x.dtype, device=x.device)
+    L = _native.lib()
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = L.gdn_conv_silu(B, T, C, W, _dtype_code(x, "x"), int(bool(apply_silu)), _ptr(x),
+                             _ptr(weight), _ptr(bias), _ptr(state), _ptr(y), _ptr(new_state),
+                             ctypes.c_void_p(stream))
+    if rc != 0:
+        reason = _native.last_error()
+        if rc == 8:
+            raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
+        raise GdnError(rc, reason)
+    return y, new_state
 
 
 def check(desc: GdnDesc, q=None, k=None, v=None, log_decay=None, beta=None, s0=None, z=None,

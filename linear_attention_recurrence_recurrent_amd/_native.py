@@ -20,7 +20,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_ESHAPE", 3: "GDN_EDTYPE", 4: "GD
 
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan", "gdn_gates",
-           "gdn_check",
+           "gdn_conv_silu", "gdn_check",
            "gdn_last_error", "gdn_status_str", "gdn_abi_version")
 
 
@@ -55,6 +55,8 @@ def lib():
         L.gdn_gates.restype = ctypes.c_int
         L.gdn_gates.argtypes = [ctypes.c_int64, vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
                                 ctypes.c_int32, vp]
+        L.gdn_conv_silu.restype = ctypes.c_int
+        L.gdn_conv_silu.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int32] * 3 + [vp] * 7
         L.gdn_check.restype = ctypes.c_int
         L.gdn_check.argtypes = [dp] + [vp] * 10
         L.gdn_last_error.restype = ctypes.c_char_p

@@ -60,4 +60,14 @@ int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float d
   return gdn::launch_gates(n, a, b, in_dtype, decay_scale, log_decay, beta, out_dtype, stream);
 }
 
+int gdn_conv_silu(int64_t B, int64_t T, int64_t C, int32_t W, int32_t dtype, int32_t apply_silu,
+                  const void* x, const void* w, const void* bias, const void* state_in, void* y,
+                  void* state_out, void* stream) {
+  int rc = gdn::check_conv(B, T, C, W, dtype, apply_silu, x, w, bias, state_in, y, state_out);
+  if (rc != GDN_OK || B == 0 || C == 0) return rc;
+  if (T == 0 && (state_out == nullptr || W == 1)) return GDN_OK;
+  return gdn::launch_conv(B, T, C, W, dtype, apply_silu, x, w, bias, state_in, y, state_out,
+                          stream);
+}
+
 }  // extern "C"

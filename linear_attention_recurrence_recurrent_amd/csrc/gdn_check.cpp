@@ -157,6 +157,46 @@ int check_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float
   return GDN_OK;
 }
 
+int check_conv(int64_t B, int64_t T, int64_t C, int32_t W, int32_t dtype, int32_t apply_silu,
+               const void* x, const void* w, const void* bias, const void* state_in,
+               const void* y, const void* state_out) {
+  g_last_error[0] = '\0';
+  if (B < 0 || T < 0 || C < 0) return fail(GDN_ESHAPE, "negative extent");
+  if (W < 1 || W > 8) return fail(GDN_EUNSUPPORTED, "conv width %d not in [1, 8]", (int)W);
+  if (dtype < GDN_F32 || dtype > GDN_BF16) return fail(GDN_EDTYPE, "bad dtype %d", (int)dtype);
+  if (apply_silu != 0 && apply_silu != 1) return fail(GDN_EINVAL, "apply_silu must be 0 or 1");
+  const int64_t es = elem_size(dtype), K = W - 1;
+  int64_t nx = 0, nst = 0, nw = 0;
+  if (!mul_ok(B, T, &nx) || !mul_ok(nx, C, &nx) || !mul_ok(nx, es, &nx) || nx >= ((int64_t)1 << 46))
+    return fail(GDN_ESHAPE, "x too large");
+  if (!mul_ok(B, C, &nst) || !mul_ok(nst, K, &nst) || !mul_ok(nst, es, &nst) ||
+      !mul_ok(C, (int64_t)W * es, &nw))
+    return fail(GDN_ESHAPE, "sizes overflow");
+  int64_t nblk = 0;  // workgroups along (batch, 16-token tiles)
+  if (!mul_ok(B, T > 0 ? (T + 15) / 16 : 1, &nblk) || nblk >= ((int64_t)1 << 31) ||
+      C >= ((int64_t)1 << 38))
+    return fail(GDN_ESHAPE, "grid too large");
+  if (B == 0 || C == 0) return GDN_OK;
+  if (!w) return fail(GDN_EINVAL, "null weight");
+  if (T > 0 && (!x || !y)) return fail(GDN_EINVAL, "null x or y");
+  auto al = [es](const void* p) { return (uintptr_t)p % (uintptr_t)es == 0; };
+  for (const void* p : {x, w, bias, state_in, y, state_out})
+    if (p && !al(p)) return fail(GDN_EALIGN, "pointers must be aligned to their element size");
+  auto rng = [](const char* nm, const void* p, int64_t bytes) {
+    return Range{nm, (uintptr_t)p, (uintptr_t)p + (uintptr_t)(p ? bytes : 0)};
+  };
+  const Range rx = rng("x", x, nx), rw = rng("weight", w, nw), rb = rng("bias", bias, C * es);
+  const Range rsi = rng("state_in", state_in, nst), ry = rng("y", y, nx);
+  const Range rso = rng("state_out", state_out, nst);
+  for (const Range* in : {&rx, &rw, &rb, &rsi, &rso})
+    if (overlap(ry, *in)) return fail(GDN_EALIAS, "y overlaps %s", in->name);
+  for (const Range* in : {&rx, &rw, &rb})
+    if (overlap(rso, *in)) return fail(GDN_EALIAS, "state_out overlaps %s", in->name);
+  if (state_out != state_in && overlap(rso, rsi))
+    return fail(GDN_EALIAS, "state_out partially overlaps state_in");
+  return GDN_OK;
+}
+
 }  // namespace gdn
 
 extern "C" {

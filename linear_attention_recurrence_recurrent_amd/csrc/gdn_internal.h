@@ -14,6 +14,11 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
 int check_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,
                 const void* log_decay, const void* beta, int32_t out_dtype);
 
+// Validation behind gdn_conv_silu.
+int check_conv(int64_t B, int64_t T, int64_t C, int32_t W, int32_t dtype, int32_t apply_silu,
+               const void* x, const void* w, const void* bias, const void* state_in,
+               const void* y, const void* state_out);
+
 // Replace the thread's last-error text.
 void set_error(const char* msg);
 
@@ -31,5 +36,9 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
 
 int launch_gates(int64_t n, const void* a, const void* b, int in_dtype, float decay_scale,
                  void* log_decay, void* beta, int out_dtype, void* stream);
+
+int launch_conv(int64_t B, int64_t T, int64_t C, int W, int dtype, int apply_silu,
+                const void* x, const void* w, const void* bias, const void* state_in, void* y,
+                void* state_out, void* stream);
 
 }  // namespace gdn

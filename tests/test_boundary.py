@@ -218,3 +218,29 @@ def test_gates_validation():
     assert chk(16, a, b, 2, 1.0, a + 8, be, 0, None) == 7 and "overlaps" in nat.last_error()
     assert chk(16, a, b, 2, 1.0, ld, ld + 32, 0, None) == 7
     assert chk(0, None, None, 2, 1.0, None, None, 0, None) == 0
+
+
+def test_conv_validation():
+    """gdn_conv_silu rejects bad arguments before any HIP call (status + reason)."""
+    L = nat.lib()
+    x, w, bias, si, y, so = _addrs(6)
+    f = L.gdn_conv_silu
+    # (B, T, C, W, dtype, apply_silu, x, w, bias, state_in, y, state_out, stream)
+    assert f(-1, 4, 8, 4, 2, 1, x, w, bias, si, y, so, None) == 2
+    assert f(2, 4, 8, 0, 2, 1, x, w, bias, si, y, so, None) == 5 and "width" in nat.last_error()
+    assert f(2, 4, 8, 9, 2, 1, x, w, bias, si, y, so, None) == 5
+    assert f(2, 4, 8, 4, 3, 1, x, w, bias, si, y, so, None) == 3
+    assert f(2, 4, 8, 4, 2, 2, x, w, bias, si, y, so, None) == 1
+    assert f(2, 4, 8, 4, 2, 1, x, None, bias, si, y, so, None) == 1
+    assert f(2, 4, 8, 4, 2, 1, None, w, bias, si, y, so, None) == 1
+    assert f(2, 4, 8, 4, 2, 1, x + 1, w, bias, si, y, so, None) == 6
+    assert f(2, 4, 8, 4, 2, 1, x, w, bias, si, x + 16, so, None) == 7 and "y overlaps x" in \
+        nat.last_error()
+    assert f(2, 4, 8, 4, 2, 1, x, w, bias, si, y, w, None) == 7
+    assert f(2, 4, 8, 4, 2, 1, x, w, bias, si, y, si + 2, None) == 7 and "partially" in \
+        nat.last_error()
+    assert f(1 << 40, 1 << 20, 8, 4, 2, 1, x, w, bias, si, y, so, None) == 2
+    # nothing to do: returns before any device work
+    assert f(0, 4, 8, 4, 2, 1, None, None, None, None, None, None, None) == 0
+    assert f(2, 0, 8, 4, 2, 1, None, w, None, None, None, None, None) == 0
+    assert f(2, 0, 8, 1, 2, 1, None, w, None, None, None, so, None) == 0
