@@ -132,14 +132,27 @@ def bench_decode(args, torch):
     value = state_bytes * wl.steps / (ms_per_chain * 1e-3) / 1e9
     achieved = (state_bytes + io_bytes) / launch_s / 1e9
     traffic = read_counters()
+    # a plain device copy moving the same state bytes (one read and one write)
+    src = torch.empty(wl.B * wl.Hv * wl.Dv * wl.Dk, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(20):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = state_bytes / (e0.elapsed_time(e1) * 1e-3 / 20) / 1e9
+    del src, dst
     res = dict(ms_per_step=ms_per_chain, value=value, launch_us=launch_s * 1e6,
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "kernel": "decode_kernel<bf16,bf16,128,8,2,8>",
                          "algorithmic_bytes_per_launch": state_bytes + io_bytes,
-                         "avg_launch_us": round(launch_s * 1e6, 3)})
-    log("decode: %.3f ms per 100-step chain, %.1f us per launch, state %.1f GB/s" %
-        (ms_per_chain, launch_s * 1e6, value))
+                         "avg_launch_us": round(launch_s * 1e6, 3),
+                         "copy_same_bytes_gbs": round(copy_gbs, 1)})
+    log("decode: %.3f ms per 100-step chain, %.1f us per launch, state %.1f GB/s (a device copy "
+        "of the same bytes: %.1f GB/s)" % (ms_per_chain, launch_s * 1e6, value, copy_gbs))
 
     # ablation: the literal three-pass step on the same chain (3 reads + 1 write of S)
     calls3 = [Launcher("gdn_recurrent_step_three_pass", desc,
@@ -166,6 +179,38 @@ def bench_decode(args, torch):
     log("decode three-pass: %.1f us per step (fusion speedup %.2fx)" %
         (step3_us, step3_us / (launch_s * 1e6)))
     return res, ops
+
+
+def bench_decode_single(args, torch):
+    """The single decode step at B=1 (Hk16 Hv32 D128, bf16): its 4 MiB state fits
+    in the caches, so this measures launch latency more than HBM."""
+    import linear_attention_recurrence_recurrent_amd as gdn
+    from linear_attention_recurrence_recurrent_amd import synth
+    wl = synth.WORKLOADS[1]
+    ops = synth.make(wl)
+    dev = torch.device("cuda:0")
+    d = {n: t.to(dev) for n, t in ops.items()}
+    y = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    desc = gdn._desc(wl.B, 1, wl.Hk, wl.Hv, wl.Dk, wl.Dv, False, 2, 2, True, True, 1e-6, 1e-6)
+    call = Launcher("gdn_recurrent_step", desc, [d["q"], d["k"], d["v"], d["log_decay"],
+                                                 d["beta"], d["s0"], d["z"], d["w"], y, d["s0"]],
+                    stream.cuda_stream)
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    reps = 200
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    state_bytes = 2 * 4 * wl.B * wl.Hv * wl.Dv * wl.Dk
+    log("decode B=1: %.2f us per step, state %.1f GB/s" % (us, state_bytes / (us * 1e-6) / 1e9))
+    return {"workload": wl.name, "us_per_step": round(us, 2), "state_bytes": state_bytes,
+            "state_gbs": round(state_bytes / (us * 1e-6) / 1e9, 1)}
 
 
 def bench_scan(idx, args, torch):
@@ -300,9 +345,24 @@ def cpu_baseline(ops, args):
     gbs = 2 * 4 * B * Hv * D * D * T * reps / dt / 1e9
     log("cpu oracle: %d x %d tokens x B=%d in %.2f s on %d threads: %.3f GB/s" %
         (reps, T, B, dt, threads, gbs))
+    # the same chain once on a single thread
+    t1 = time.perf_counter()
+    orc.scan(**f64, threads=1)
+    dt1 = time.perf_counter() - t1
+    gbs1 = 2 * 4 * B * Hv * D * D * T / dt1 / 1e9
+    log("cpu oracle, one thread: %.2f s per chain: %.3f GB/s" % (dt1, gbs1))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "float64 three-pass oracle on the whole decode chain (B=64 Hk16 Hv32 "
-                      "D128, 100 chained steps), run %d times in %.1f s" % (reps, dt)}
+                      "D128, 100 chained steps), run %d times in %.1f s" % (reps, dt),
+            "single_thread_value": round(gbs1, 4), "cpu_model": model}
 
 
 def copy_reference(args, torch):
@@ -325,6 +385,8 @@ def main():
     ap.add_argument("--no-scan", action="store_true", help="skip the scan sub-measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--scan-only", action="store_true",
+                    help="only the two scan workloads (for counter collection); partial JSON")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this size (counter reference)")
     args = ap.parse_args()
@@ -341,6 +403,10 @@ def main():
         copy_reference(args, torch)
         return
     import linear_attention_recurrence_recurrent_amd  # noqa: F401  (fails loudly if unbuilt)
+    if args.scan_only:
+        print(json.dumps({"scan": {"prefill_b1_t4096_bf16": bench_scan(3, args, torch),
+                                   "head_major_b16_t1024_f16": bench_scan(4, args, torch)}}))
+        return
     dec, ops = bench_decode(args, torch)
     scan = {}
     if not args.no_scan:
@@ -366,6 +432,7 @@ def main():
         "roofline": dec["roofline"],
         "ablation_three_pass_decode": dec["ablation"],
     }
+    out["decode_b1"] = bench_decode_single(args, torch)
     if scan:
         out["scan"] = scan
     if not args.no_scan:

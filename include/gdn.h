@@ -43,7 +43,7 @@
  *     between an output and any operand is rejected.
  *   - q, k, v, z, y, s0, s_out must be 16-byte aligned; log_decay, beta and w
  *     aligned to their element size.
- *   - Supported by the kernels: Dk == Dv in {16, 32, 64, 128}; dtype and
+ *   - Supported by the kernels: Dk == Dv in {16, 32, 64, 128, 256}; dtype and
  *     gate_dtype in {GDN_F32, GDN_F16, GDN_BF16}; Hv a multiple of Hk.
  *   - Error behaviour: every call returns GDN_OK or a gdn_status; the short
  *     reason of the last failure on the calling thread is gdn_last_error().

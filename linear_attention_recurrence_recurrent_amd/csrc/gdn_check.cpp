@@ -79,8 +79,9 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
   if (d->Dk != d->Dv)
     return fail(GDN_EUNSUPPORTED, "kernels need Dk == Dv (got %lld, %lld)", (long long)d->Dk,
                 (long long)d->Dv);
-  if (d->Dk != 16 && d->Dk != 32 && d->Dk != 64 && d->Dk != 128)
-    return fail(GDN_EUNSUPPORTED, "head dim %lld not in {16, 32, 64, 128}", (long long)d->Dk);
+  if (d->Dk != 16 && d->Dk != 32 && d->Dk != 64 && d->Dk != 128 && d->Dk != 256)
+    return fail(GDN_EUNSUPPORTED, "head dim %lld not in {16, 32, 64, 128, 256}",
+                (long long)d->Dk);
 
   // sizes in bytes (with overflow checks)
   int64_t bt, nqk, nv, ng, ns, tmp;

@@ -34,9 +34,6 @@ struct StepArgs {
   float qk_eps, norm_eps, qscale;
 };
 
-// N consecutive operand elements kept as their raw bits (16-bit dtypes stay
-// packed two per VGPR) and widened to f32 on use.  N = 1, 2 or 4; the access
-
 template <int DT, int D, int CL, int RPL>
 struct HeadRegs {
   static constexpr int NV4 = D / CL / 4;
@@ -306,6 +303,7 @@ template <int DT, int GT>
 int launch_step_dt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(d.B * d.Hv));
   switch (d.Dk) {
+    case 256: decode_kernel<DT, GT, 256, 16, 4, 16><<<grid, 16 * kWave, 0, st>>>(a); break;
     case 128: decode_kernel<DT, GT, 128, 8, 2, 8><<<grid, 8 * kWave, 0, st>>>(a); break;
     case 64: decode_kernel<DT, GT, 64, 4, 2, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
     case 32: decode_kernel<DT, GT, 32, 4, 1, 2><<<grid, 2 * kWave, 0, st>>>(a); break;

@@ -79,15 +79,24 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over each aligned group of CL consecutive lanes (CL = 1, 2, 4, 8, 16).
-// Butterfly order: every lane of a group ends with bit-identical sums.
+// Sum over each aligned group of CL consecutive lanes (CL = 1, 2, 4, ..., 32).
+// Butterfly order: every lane of a group ends with bit-identical sums.  The
+// step across the two DPP rows of a 32-lane group is gfx950's row swap: with
+// both operands x, v_permlane16_swap returns the even row's values in one
+// result and the odd row's in the other, in every lane of the pair.
 template <int CL>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(CL == 1 || CL == 2 || CL == 4 || CL == 8 || CL == 16, "row group size");
+  static_assert(CL == 1 || CL == 2 || CL == 4 || CL == 8 || CL == 16 || CL == 32,
+                "row group size");
   if constexpr (CL >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
   if constexpr (CL >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
   if constexpr (CL >= 8) x += dpp<0x141>(x);  // row_half_mirror: the other quad of 8
   if constexpr (CL >= 16) x += dpp<0x140>(x); // row_mirror: the other half of 16
+  if constexpr (CL >= 32) {
+    const int b = __float_as_int(x);
+    const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    x = __int_as_float(p[0]) + __int_as_float(p[1]);
+  }
   return x;
 }
 

@@ -115,7 +115,7 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
   static_assert(D % ROWS == 0 && ROWS % 4 == 0, "row blocks tile the head");
   static_assert(!FUSE_NORM || ROWS == D, "the fused norm needs the whole head");
   static_assert(TC <= kWave && TC % NW == 0, "chunk shape");
-  static_assert(D8 <= 16, "a token's q/k groups span at most one DPP row");
+  static_assert(D8 <= 32, "a token's q/k groups span at most two DPP rows");
   typedef ChunkRegs<DT, GT, D, ROWS, TC, NT, FUSE_NORM> Chunk;
   __shared__ float4 sk[TC][D4];  // raw k and q of the chunk
   __shared__ float4 sq[TC][D4];
@@ -178,7 +178,7 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
     }
   };
   // Registers -> LDS, with the per-token norm scalars: the D8 lanes holding one
-  // token's q and k are adjacent and aligned inside one DPP row, so the three
+  // token's q and k are adjacent and aligned (inside one half wave), so the three
   // dot products reduce across them.  Tokens tc..TC-1 of a short last chunk
   // become identity steps (alpha = 1, beta = 0, k = q = v = 0, rk = rq = 0).
   // FULL (tc == TC, every chunk but a short last one) drops the per-token
@@ -558,6 +558,10 @@ int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
 template <int DT, int GT>
 int launch_scan_dt(const ScanArgs& a, int D, int64_t heads, hipStream_t st) {
   switch (D) {
+    case 256:
+      // 16 workgroups per head (a whole-head workgroup would need 128 state
+      // floats per lane and spill), then the standalone gated norm
+      return launch_scan_cfg<DT, GT, 256, 16, 1, 4, 16>(a, heads, st);
     case 128:
       // enough heads to fill the chip with whole-head workgroups: keep the
       // norm fused; otherwise split each head's rows over more workgroups

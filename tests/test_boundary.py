@@ -90,7 +90,7 @@ def test_accepts_valid_arguments():
     ops["s_out"] = ops["s0"]  # exact in-place alias is allowed
     assert check(_good(), **ops)[0] == 0
     assert check(_good(head_major=1, dtype=0, gate_dtype=0, flags=0), **ops)[0] == 0
-    for D in (16, 32, 64, 128):
+    for D in (16, 32, 64, 128, 256):
         assert check(_good(Dk=D, Dv=D), **_ops())[0] == 0
     # empty batch or empty time axis
     assert check(_good(T=0), **_ops())[0] == 0
@@ -121,7 +121,7 @@ def test_rejects_bad_descriptor(field, value, status, needle):
 
 
 def test_rejects_unsupported_head_dim():
-    rc, why = check(_good(Dk=256, Dv=256), **_ops())
+    rc, why = check(_good(Dk=512, Dv=512), **_ops())
     assert rc == 5 and "head dim" in why
     rc, why = check(_good(Dk=8, Dv=8), **_ops())
     assert rc == 5

@@ -156,6 +156,8 @@ SMALL = [
     (8, 33, 16, 32, 64, "f32", False),   # D=64 whole-head
     (3, 65, 2, 6, 32, "f16", False),     # D=32, G=3
     (2, 70, 1, 3, 16, "f32", True),      # D=16, G=3
+    (1, 21, 2, 4, 256, "bf16", False),   # D=256 row split
+    (2, 9, 1, 2, 256, "f32", True),      # D=256, G=2, head-major
 ]
 
 
@@ -185,7 +187,7 @@ def test_fold_flags(flags):
 
 
 def test_step_on_small_shapes_and_dims():
-    for D in (16, 32, 64, 128):
+    for D in (16, 32, 64, 128, 256):
         for hm in (False, True):
             ops = synth.random_operands(3, 1, 2, 4, D, D, dtype="f16", head_major=hm, seed=D)
             d = dev(ops)
