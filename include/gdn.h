@@ -78,6 +78,15 @@ typedef enum gdn_status {
 /* flags */
 #define GDN_FOLD_QK_L2NORM 1u /* L2-normalise q and k inside the op */
 #define GDN_FOLD_Q_SCALE 2u   /* multiply q^ by 1/sqrt(Dk) inside the op */
+/* Form of gdn_scan's time loop.  The token-by-token form runs on the vector
+ * units for every head dim; at Dk == Dv == 128 the block form runs 16 tokens
+ * at a time as dense products on the matrix cores (the step is affine in S,
+ * "Module gdn" page, "The fusion").  Both give the same results up to
+ * rounding.  Without either flag the library picks the form it runs faster
+ * for the shape; with both, or GDN_SCAN_BLOCK at another head dim, the call
+ * is rejected (GDN_EINVAL / GDN_EUNSUPPORTED). */
+#define GDN_SCAN_PER_TOKEN 4u
+#define GDN_SCAN_BLOCK 8u
 
 typedef struct gdn_desc {
   int64_t B, T, Hk, Hv, Dk, Dv; /* batch, tokens, key heads, value heads, head dims */

@@ -17,7 +17,8 @@ from typing import Optional, Tuple
 import torch
 
 from . import _native
-from ._native import GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GdnDesc
+from ._native import (GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GDN_SCAN_BLOCK, GDN_SCAN_PER_TOKEN,
+                      GdnDesc)
 
 __all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "gates", "conv_silu", "check",
            "abi_version", "GdnError"]
@@ -43,8 +44,14 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _desc(B, T, Hk, Hv, Dk, Dv, head_major, dtype, gate_dtype, fold_qk_l2norm, fold_q_scale,
-          qk_eps, norm_eps) -> GdnDesc:
+          qk_eps, norm_eps, form=None) -> GdnDesc:
     flags = (GDN_FOLD_QK_L2NORM if fold_qk_l2norm else 0) | (GDN_FOLD_Q_SCALE if fold_q_scale else 0)
+    if form == "per_token":
+        flags |= GDN_SCAN_PER_TOKEN
+    elif form == "block":
+        flags |= GDN_SCAN_BLOCK
+    elif form is not None:
+        raise GdnError(1, "form must be None, 'per_token' or 'block'")
     return GdnDesc(B, T, Hk, Hv, Dk, Dv, int(bool(head_major)), dtype, gate_dtype, flags,
                    float(qk_eps), float(norm_eps))
 
@@ -120,21 +127,24 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
          w: Optional[torch.Tensor] = None, *, head_major: bool = False,
          fold_qk_l2norm: bool = True, fold_q_scale: bool = True, qk_eps: float = 1e-6,
          norm_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-         state_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+         state_out: Optional[torch.Tensor] = None,
+         form: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Gated DeltaNet recurrence over the time axis; returns (y, final_state).
 
     q, k: [B, T, Hk, D] (head-major: [B, Hk, T, D]); v, z: [B, T, Hv, D]
     ([B, Hv, T, D]); log_decay, beta: [B, T, Hv] ([B, Hv, T]); s0:
     float32 [B, Hv, D, D] (None: zeros); w: [D].  y is float32 in v's layout;
     final_state is float32 [B, Hv, D, D] (``state_out`` may be ``s0`` for an
-    in-place update)."""
+    in-place update).  ``form`` picks the time loop: "per_token" (vector units,
+    any D), "block" (16 tokens at a time on the matrix cores, D == 128), or
+    None for the library's choice for the shape."""
     B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
     if s0 is None:
         s0 = torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=q.device)
     y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
     s_out = state_out if state_out is not None else torch.empty_like(s0)
     desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
-                 qk_eps, norm_eps)
+                 qk_eps, norm_eps, form)
     _call("gdn_scan", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
     return y, s_out
 

@@ -72,8 +72,10 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
     return fail(GDN_EDTYPE, "bad gate_dtype %d", d->gate_dtype);
   if (d->head_major != 0 && d->head_major != 1)
     return fail(GDN_EINVAL, "head_major must be 0 or 1 (got %d)", d->head_major);
-  if (d->flags & ~(GDN_FOLD_QK_L2NORM | GDN_FOLD_Q_SCALE))
+  if (d->flags & ~(GDN_FOLD_QK_L2NORM | GDN_FOLD_Q_SCALE | GDN_SCAN_PER_TOKEN | GDN_SCAN_BLOCK))
     return fail(GDN_EINVAL, "unknown flag bits 0x%x", d->flags);
+  if ((d->flags & GDN_SCAN_PER_TOKEN) && (d->flags & GDN_SCAN_BLOCK))
+    return fail(GDN_EINVAL, "GDN_SCAN_PER_TOKEN and GDN_SCAN_BLOCK exclude each other");
   if (!(d->qk_eps >= 0.0f && d->qk_eps < 1e30f) || !(d->norm_eps >= 0.0f && d->norm_eps < 1e30f))
     return fail(GDN_EINVAL, "eps must be finite and >= 0");
   if (d->Dk != d->Dv)
@@ -82,6 +84,8 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
   if (d->Dk != 16 && d->Dk != 32 && d->Dk != 64 && d->Dk != 128 && d->Dk != 256)
     return fail(GDN_EUNSUPPORTED, "head dim %lld not in {16, 32, 64, 128, 256}",
                 (long long)d->Dk);
+  if ((d->flags & GDN_SCAN_BLOCK) && d->Dk != 128)
+    return fail(GDN_EUNSUPPORTED, "the block form needs Dk == Dv == 128");
 
   // sizes in bytes (with overflow checks)
   int64_t bt, nqk, nv, ng, ns, tmp;

@@ -1,0 +1,480 @@
+// Time-axis scan of the Gated DeltaNet recurrence in block form on the matrix
+// cores (gfx950 MFMA, FP32 in and out), for D = 128.
+//
+// The recurrence is the one of the "Module gdn" page (module description).
+// Its section "The fusion" observes that the step is affine in the memory S;
+// carrying that affine map over a block of L = 16 tokens turns the block into
+// dense products.  With S the state at the block start (true scale), k^ and
+// q^ the normalised keys and queries, and for tokens i, j of the block
+//   Dc[i][j] = alpha_{j+1} ... alpha_i  (j <= i; 1 on the diagonal),
+//   gam_i    = alpha_0 ... alpha_i,
+// the step S_i = alpha_i S_{i-1} + c_i k^_i^T with c_i = beta_i (v_i - alpha_i
+// S_{i-1} k^_i) unrolls to
+//   (I + Ls) C = diag(beta) V - diag(beta gam) K^ S^T,
+//   Ls[i][j] = beta_i (k^_i . k^_j) Dc[i][j]  (j < i),
+//   O  = diag(gam) Q^ S^T + (tril(Q^ K^^T) (.) Dc) C,
+//   S' = gam_15 S + ((diag(Dc[15][.]) K^)^T C)^T.
+// With T = (I + Ls)^-1 (unit lower triangular, 16 x 16) the state enters only
+// through products:  C = T diag(beta) V - W S^T with W = T diag(beta gam) K^.
+// Per block and head the kernel forms the state-independent pieces
+// (K K^T, Q K^T, the decay products, T by forward substitution, W) and then,
+// per 16 value rows (an "a-tile"), runs W S^T and Q S^T (16 x 128 x 16), the
+// small T V and the masked products, and the rank-16 update of S^T, all as
+// v_mfma_f32_16x16x4f32.  S^T stays in the accumulator layout for the whole
+// time axis: lane l, register r of a 16 x 16 tile holds S^T[4(l/16) + r][l%16]
+// (key row within the tile, value column), which is also a valid B operand of
+// the next product when the contraction index is taken in the matching order.
+// Decays are products (never quotients), so alpha = 0 needs no special case.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kD = 128;  // head dim handled here
+constexpr int kL = 16;   // tokens per block (the MFMA tile)
+
+struct ChunkArgs {
+  const void *q, *k, *v, *ld, *beta, *z, *w;
+  const float* s0;
+  float* y;
+  float* s_out;
+  int64_t T;
+  int Hk, Hv, G, nrb, head_major;
+  uint32_t flags;
+  float qk_eps, norm_eps, qscale;
+};
+
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Workgroup = (value head, NA a-tiles of 16 value rows); NC waves share an
+// a-tile by splitting its 8 key tiles (their partial products are summed
+// through LDS).  NW = NA * NC waves.
+template <int DT, int GT, int NA, int NC, bool FUSE>
+__global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
+  constexpr int NW = NA * NC, NT = NW * kWave, ROWS = 16 * NA, NCT = 8 / NC;
+  static_assert(NT >= 256 && NW <= 8 && NC >= 1 && 8 % NC == 0, "shape");
+  static_assert(!FUSE || ROWS == kD, "the fused norm needs the whole head");
+  static_assert(kL % NW == 0 || NW > kL, "token split of the gated output");
+  // staged chunk (raw q, k in f32; v for this workgroup's rows; z when fused)
+  __shared__ __align__(16) float sk[kL][kD];
+  __shared__ __align__(16) float sq[kL][kD];
+  __shared__ float sv[kL][ROWS];
+  __shared__ float sz[FUSE ? 2 : 1][FUSE ? kL : 1][FUSE ? kD : 1];
+  __shared__ __align__(16) float so[kL][ROWS];
+  __shared__ __align__(16) float sal[kL];
+  __shared__ float sbe[kL], srk[kL], srq[kL];
+  // block pieces
+  __shared__ float sGp[NW][kL][kL + 1], sHp[NW][kL][kL + 1];  // per-wave partial K K^T, Q K^T
+  __shared__ float sDc[kL][kL + 1];
+  __shared__ __align__(16) float sLs[kL][kL];
+  __shared__ float sT[kL][kL + 1];
+  __shared__ __align__(16) float sHd[kL][kL];
+  __shared__ __align__(16) float sW[kL][kD];
+  __shared__ __align__(16) float sKdT[kD][kL];
+  __shared__ __align__(16) float ssig[kL];
+  __shared__ float swsc[kL], sgl;
+  __shared__ v4f spart[NC > 1 ? NW : 1][2][kWave];
+
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int rb = (int)(tile % a.nrb);
+  const int64_t bh = tile / a.nrb;
+  const int hv = (int)(bh % a.Hv), hk = hv / a.G;
+  const int64_t b = bh / a.Hv;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int lg = lane / 16, lc = lane % 16;
+  const int ai = wave / NC, cp = wave % NC;  // this wave's a-tile and key-tile part
+  const int64_t T = a.T;
+  const bool has_z = FUSE && a.z != nullptr;
+
+  int64_t qk_base, qk_ts, v_base, v_ts, g_base, g_ts;
+  if (a.head_major) {
+    qk_base = (b * a.Hk + hk) * T * kD; qk_ts = kD;
+    v_base = (b * a.Hv + hv) * T * kD; v_ts = kD;
+    g_base = (b * a.Hv + hv) * T; g_ts = 1;
+  } else {
+    qk_base = (b * T * a.Hk + hk) * kD; qk_ts = (int64_t)a.Hk * kD;
+    v_base = (b * T * a.Hv + hv) * kD; v_ts = (int64_t)a.Hv * kD;
+    g_base = b * T * a.Hv + hv; g_ts = a.Hv;
+  }
+  const int row0 = rb * ROWS;
+  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
+
+  // ---- chunk staging: 256 items of 8 elements for k and for q, v pairs,
+  // z pairs (fused), one gate pair per token
+  constexpr int NQK = (2 * kL * 16 + NT - 1) / NT;
+  constexpr int NVP = (kL * ROWS / 2 + NT - 1) / NT;
+  constexpr int NZP = FUSE ? (kL * kD / 2 + NT - 1) / NT : 1;
+  struct Regs {
+    Raw<DT, 8> qk[NQK];
+    Raw<DT, 2> v[NVP];
+    Raw<DT, 2> z[NZP];
+    Raw<GT, 1> ld, be;
+  };
+  auto chunk_load = [&](Regs& P, int64_t t0, int tc) {
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int e = tid + i * NT, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
+      if (e < 512 && tt < tc) P.qk[i].load(which ? a.q : a.k, qk_base + (t0 + tt) * qk_ts + 8 * c8);
+      else P.qk[i].zero();
+    }
+#pragma unroll
+    for (int i = 0; i < NVP; ++i) {
+      const int e = tid + i * NT, tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
+      if (e < kL * ROWS / 2 && tt < tc) P.v[i].load(a.v, v_base + (t0 + tt) * v_ts + row0 + 2 * r2);
+    }
+    if constexpr (FUSE) {
+#pragma unroll
+      for (int i = 0; i < NZP; ++i) {
+        const int e = tid + i * NT, tt = e / (kD / 2), r2 = e % (kD / 2);
+        if (has_z && e < kL * kD / 2 && tt < tc)
+          P.z[i].load(a.z, v_base + (t0 + tt) * v_ts + 2 * r2);
+      }
+    }
+    if (tid < tc) {
+      P.ld.load(a.ld, g_base + (t0 + tid) * g_ts);
+      P.be.load(a.beta, g_base + (t0 + tid) * g_ts);
+    }
+  };
+  auto chunk_store = [&](const Regs& P, int tc, int zbuf) {
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): the chunk's loads are complete
+    const bool l2 = (a.flags & GDN_FOLD_QK_L2NORM) != 0;
+    float ss[NQK];
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const float4 x0 = P.qk[i].get4(0), x1 = P.qk[i].get4(1);
+      ss[i] = group_sum<16>(dot4(x1, x1, dot4(x0, x0, 0.f)));
+    }
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int e = tid + i * NT, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
+      if (e < 512) {
+        float* dst = which ? &sq[tt][8 * c8] : &sk[tt][8 * c8];
+        *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
+        *reinterpret_cast<float4*>(dst + 4) = P.qk[i].get4(1);
+        if (c8 == 0) {
+          float r = rsqrtf(l2 ? ss[i] + a.qk_eps : 1.f);
+          if (which) r *= a.qscale;
+          if (tt >= tc) r = 0.f;
+          if (which) srq[tt] = r;
+          else srk[tt] = r;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NVP; ++i) {
+      const int e = tid + i * NT, tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
+      if (e < kL * ROWS / 2) {
+        sv[tt][2 * r2] = tt < tc ? P.v[i].get(0) : 0.f;
+        sv[tt][2 * r2 + 1] = tt < tc ? P.v[i].get(1) : 0.f;
+      }
+    }
+    if constexpr (FUSE) {
+#pragma unroll
+      for (int i = 0; i < NZP; ++i) {
+        const int e = tid + i * NT, tt = e / (kD / 2), r2 = e % (kD / 2);
+        if (has_z && e < kL * kD / 2 && tt < tc) {
+          sz[zbuf][tt][2 * r2] = P.z[i].get(0);
+          sz[zbuf][tt][2 * r2 + 1] = P.z[i].get(1);
+        }
+      }
+    }
+    if (tid < kL) {
+      sal[tid] = tid < tc ? expf(P.ld.get(0)) : 1.f;
+      sbe[tid] = tid < tc ? P.be.get(0) : 0.f;
+    }
+  };
+
+  // state S^T, this wave's key tiles of its a-tile, in the accumulator layout
+  v4f St[NCT];
+  const int arow = row0 + 16 * ai + lc;  // value row of this lane
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
+                                                      16 * (cp * NCT + ct) + 4 * lg);
+    St[ct] = v4f{x.x, x.y, x.z, x.w};
+  }
+  float wgt[2];
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wgt[i] = has_z ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
+  }
+
+  Regs P;
+  chunk_load(P, 0, (int)(T < kL ? T : kL));
+  chunk_store(P, (int)(T < kL ? T : kL), 0);
+  __builtin_amdgcn_s_waitcnt(0xF70);
+
+  for (int64_t c = 0;; ++c) {
+    const int64_t t0 = c * kL;
+    const int tc = (int)((T - t0) < kL ? (T - t0) : kL);
+    const bool more = t0 + kL < T;
+    const int tcn = more ? (int)((T - t0 - kL) < kL ? (T - t0 - kL) : kL) : 0;
+    __syncthreads();
+    if (more) chunk_load(P, t0 + kL, tcn);
+
+    // ---- block pieces 1: decay products (each thread one entry, from the 16
+    // alphas in registers); partial K K^T and Q K^T over this wave's key tiles
+    if (tid < 256) {
+      const int i = tid / 16, j = tid % 16;
+      float al[kL];
+#pragma unroll
+      for (int m = 0; m < kL; m += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&sal[m]);
+        al[m] = x.x; al[m + 1] = x.y; al[m + 2] = x.z; al[m + 3] = x.w;
+      }
+      float p = j <= i ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 1; m < kL; ++m) p *= (m > j && m <= i) ? al[m] : 1.f;
+      sDc[i][j] = p;
+    }
+    {
+      v4f g = {0.f, 0.f, 0.f, 0.f}, h = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = wave; ct < 8; ct += NW) {
+        const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * ct + 4 * lg]);
+        const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * ct + 4 * lg]);
+        g = mfma4(kf.x, kf.x, g);
+        h = mfma4(qf.x, kf.x, h);
+        g = mfma4(kf.y, kf.y, g);
+        h = mfma4(qf.y, kf.y, h);
+        g = mfma4(kf.z, kf.z, g);
+        h = mfma4(qf.z, kf.z, h);
+        g = mfma4(kf.w, kf.w, g);
+        h = mfma4(qf.w, kf.w, h);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sGp[wave][4 * lg + r][lc] = g[r];
+        sHp[wave][4 * lg + r][lc] = h[r];
+      }
+    }
+    __syncthreads();
+
+    // ---- block pieces 2: Ls, the masked Q K^T, per-token scales
+    if (tid < 256) {
+      const int i = tid / 16, j = tid % 16;
+      const float dc = sDc[i][j];
+      float gij = 0.f, hij = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        gij += sGp[w2][i][j];
+        hij += sHp[w2][i][j];
+      }
+      sLs[i][j] = j < i ? sbe[i] * srk[i] * gij * srk[j] * dc : 0.f;
+      sHd[i][j] = j <= i ? srq[i] * hij * srk[j] * dc : 0.f;
+      if (j == 0) {
+        const float gam = sal[0] * sDc[i][0];
+        ssig[i] = gam * srq[i];
+        swsc[i] = sbe[i] * gam * srk[i];
+        if (i == kL - 1) sgl = gam;
+      }
+    }
+    __syncthreads();
+
+    // ---- block pieces 3: T = (I + Ls)^-1 by forward substitution (one lane
+    // per column); the other threads form (diag(rk * Dc[15][.]) K)^T
+    if (tid < kL) {  // four partial sums per row: a short dependent chain
+      const int j = tid;
+      float x[kL];
+#pragma unroll
+      for (int i = 0; i < kL; ++i) {
+        float acc[4] = {i == j ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc[m % 4] = fmaf(-sLs[i][m], x[m], acc[m % 4]);
+        const float xi = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        x[i] = i < j ? 0.f : xi;
+        sT[i][j] = x[i];
+      }
+    }
+    for (int e = tid; e < kD * kL; e += NT) {
+      const int cc = e / kL, t = e % kL;
+      sKdT[cc][t] = sk[t][cc] * srk[t] * sDc[kL - 1][t];
+    }
+    __syncthreads();
+
+    // ---- block pieces 4: W = T diag(beta gam rk) K, one 16 x 16 key tile per
+    // wave at a time
+    for (int ct = wave; ct < 8; ct += NW) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int tp = 4 * s + lg;
+        acc = mfma4(sT[lc][tp] * swsc[tp], sk[tp][16 * ct + lc], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sW[4 * lg + r][16 * ct + lc] = acc[r];
+    }
+    __syncthreads();
+
+    // ---- the state: W S^T and Q S^T over this wave's key tiles
+    v4f pw = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int kt = cp * NCT + ct;
+      const float4 wf = *reinterpret_cast<const float4*>(&sW[lc][16 * kt + 4 * lg]);
+      const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * kt + 4 * lg]);
+      pw = mfma4(wf.x, St[ct][0], pw);
+      pq = mfma4(qf.x, St[ct][0], pq);
+      pw = mfma4(wf.y, St[ct][1], pw);
+      pq = mfma4(qf.y, St[ct][1], pq);
+      pw = mfma4(wf.z, St[ct][2], pw);
+      pq = mfma4(qf.z, St[ct][2], pq);
+      pw = mfma4(wf.w, St[ct][3], pw);
+      pq = mfma4(qf.w, St[ct][3], pq);
+    }
+    if constexpr (NC > 1) {
+      spart[wave][0][lane] = pw;
+      spart[wave][1][lane] = pq;
+      __syncthreads();
+      pw = spart[ai * NC][0][lane];
+      pq = spart[ai * NC][1][lane];
+#pragma unroll
+      for (int p = 1; p < NC; ++p) {
+        pw += spart[ai * NC + p][0][lane];
+        pq += spart[ai * NC + p][1][lane];
+      }
+    }
+    // C = T diag(beta) V - W S^T   (rows: tokens, columns: this a-tile's rows)
+    v4f cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int tp = 4 * s + lg;
+      cc = mfma4(sT[lc][tp], sbe[tp] * sv[tp][16 * ai + lc], cc);
+    }
+    cc -= pw;
+    // O = diag(gam rq) Q S^T + (tril(Q^ K^^T) (.) Dc) C
+    v4f o = {0.f, 0.f, 0.f, 0.f};
+    {
+      const float4 hf = *reinterpret_cast<const float4*>(&sHd[lc][4 * lg]);
+      o = mfma4(hf.x, cc[0], o);
+      o = mfma4(hf.y, cc[1], o);
+      o = mfma4(hf.z, cc[2], o);
+      o = mfma4(hf.w, cc[3], o);
+    }
+    const float4 sg = *reinterpret_cast<const float4*>(&ssig[4 * lg]);
+    o[0] = fmaf(sg.x, pq[0], o[0]);
+    o[1] = fmaf(sg.y, pq[1], o[1]);
+    o[2] = fmaf(sg.z, pq[2], o[2]);
+    o[3] = fmaf(sg.w, pq[3], o[3]);
+    if (cp == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) so[4 * lg + r][16 * ai + lc] = o[r];
+    }
+    // S^T = gam_15 S^T + (diag(rk Dc[15][.]) K)^T C
+    const float gl = sgl;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int kt = cp * NCT + ct;
+      const float4 kf = *reinterpret_cast<const float4*>(&sKdT[16 * kt + lc][4 * lg]);
+      v4f acc = St[ct] * gl;
+      acc = mfma4(kf.x, cc[0], acc);
+      acc = mfma4(kf.y, cc[1], acc);
+      acc = mfma4(kf.z, cc[2], acc);
+      acc = mfma4(kf.w, cc[3], acc);
+      St[ct] = acc;
+    }
+    __syncthreads();
+
+    // next chunk into LDS (every chunk array was last read above); z is
+    // double-buffered because the output below reads this chunk's slot
+    chunk_store(P, tcn, (int)((c + 1) & 1));
+
+    // ---- outputs of this chunk
+    if constexpr (FUSE) {
+      if (has_z) {
+        constexpr int TPW = (kL + NW - 1) / NW;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int tt = wave + NW * u;
+          if (tt < kL) {  // uniform per wave
+            const int zb = (int)(c & 1);
+            float x0 = so[tt][lane] * silu(sz[zb][tt][lane]);
+            float x1 = so[tt][lane + kWave] * silu(sz[zb][tt][lane + kWave]);
+            const float inv = rsqrtf(wave_sum(fmaf(x0, x0, x1 * x1)) * (1.0f / kD) + a.norm_eps);
+            if (tt < tc) {
+              const int64_t vo = v_base + (t0 + tt) * v_ts;
+              a.y[vo + lane] = x0 * inv * wgt[0];
+              a.y[vo + lane + kWave] = x1 * inv * wgt[1];
+            }
+          }
+        }
+      } else {
+        for (int e = tid; e < tc * (kD / 4); e += NT) {
+          const int tt = e / (kD / 4), r4 = e % (kD / 4);
+          *reinterpret_cast<float4*>(a.y + v_base + (t0 + tt) * v_ts + 4 * r4) =
+              *reinterpret_cast<const float4*>(&so[tt][4 * r4]);
+        }
+      }
+    } else {
+      constexpr int R4 = ROWS / 4;
+      for (int e = tid; e < tc * R4; e += NT) {
+        const int tt = e / R4, r4 = e % R4;
+        *reinterpret_cast<float4*>(a.y + v_base + (t0 + tt) * v_ts + row0 + 4 * r4) =
+            *reinterpret_cast<const float4*>(&so[tt][4 * r4]);
+      }
+    }
+    if (!more) break;
+  }
+
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
+    *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * (cp * NCT + ct) +
+                               4 * lg) = x;
+  }
+}
+
+template <int DT, int GT, int NA, int NC>
+int launch_cfg(ChunkArgs a, int64_t heads, hipStream_t st) {
+  constexpr int ROWS = 16 * NA;
+  a.nrb = kD / ROWS;
+  const dim3 grid((unsigned)(heads * a.nrb));
+  if constexpr (ROWS == kD) {
+    chunk_kernel<DT, GT, NA, NC, true><<<grid, NA * NC * kWave, 0, st>>>(a);
+    return device_status("chunk_kernel launch");
+  } else {
+    chunk_kernel<DT, GT, NA, NC, false><<<grid, NA * NC * kWave, 0, st>>>(a);
+    return device_status("chunk_kernel launch");
+  }
+}
+
+template <int DT, int GT>
+int launch_dt(const ChunkArgs& a, int64_t heads, hipStream_t st) {
+  if (heads >= 256) return launch_cfg<DT, GT, 8, 1>(a, heads, st);
+  return launch_cfg<DT, GT, 1, 4>(a, heads, st);
+}
+
+template <int DT>
+int launch_gt(const ChunkArgs& a, int gdt, int64_t heads, hipStream_t st) {
+  switch (gdt) {
+    case GDN_F32: return launch_dt<DT, GDN_F32>(a, heads, st);
+    case GDN_F16: return launch_dt<DT, GDN_F16>(a, heads, st);
+    default: return launch_dt<DT, GDN_BF16>(a, heads, st);
+  }
+}
+
+}  // namespace
+
+// The block-form scan for D == 128; y receives the raw o (the gated norm, when
+// asked for and not fused, runs after it).  Returns whether the gated output
+// was written (fused) through *gated.
+int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const void* v,
+                        const void* ld, const void* beta, const float* s0, const void* z,
+                        const void* w, float* y, float* s_out, void* stream, bool* gated) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ChunkArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, d.T, (int)d.Hk, (int)d.Hv,
+                    (int)(d.Hv / d.Hk), 1, d.head_major, d.flags, d.qk_eps, d.norm_eps,
+                    q_scale(d)};
+  const int64_t heads = d.B * d.Hv;
+  *gated = heads >= 256;
+  switch (d.dtype) {
+    case GDN_F32: return launch_gt<GDN_F32>(a, d.gate_dtype, heads, st);
+    case GDN_F16: return launch_gt<GDN_F16>(a, d.gate_dtype, heads, st);
+    default: return launch_gt<GDN_BF16>(a, d.gate_dtype, heads, st);
+  }
+}
+
+}  // namespace gdn

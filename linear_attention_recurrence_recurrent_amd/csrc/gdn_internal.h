@@ -33,6 +33,11 @@ int launch_step_three_pass(const gdn_desc& d, const void* q, const void* k, cons
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
                 float* s_out, void* stream);
+// Block form on the matrix cores, Dk == Dv == 128; *gated reports whether the
+// gated norm was applied in the same launch (whole-head workgroups).
+int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const void* v,
+                        const void* ld, const void* beta, const float* s0, const void* z,
+                        const void* w, float* y, float* s_out, void* stream, bool* gated);
 
 int launch_gates(int64_t n, const void* a, const void* b, int in_dtype, float decay_scale,
                  void* log_decay, void* beta, int out_dtype, void* stream);

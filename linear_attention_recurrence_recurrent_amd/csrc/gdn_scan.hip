@@ -594,6 +594,21 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
                    (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags,
                    d.qk_eps, d.norm_eps, q_scale(d)};
   const int64_t heads = d.B * d.Hv;
+  // the block form where it is measured faster, or when asked for
+  const bool block = (d.flags & GDN_SCAN_BLOCK) != 0;
+  if (d.Dk == 128 && block) {
+    bool gated = false;
+    int rc = launch_scan_chunked(d, q, k, v, ld, beta, s0, z, w, y, s_out, stream, &gated);
+    if (rc != GDN_OK || gated || z == nullptr) return rc;
+    const int64_t nvec = heads * d.T;
+    const dim3 grid((unsigned)((nvec + 3) / 4));
+    switch (d.dtype) {
+      case GDN_F32: gated_norm_kernel<GDN_F32, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
+      case GDN_F16: gated_norm_kernel<GDN_F16, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
+      default: gated_norm_kernel<GDN_BF16, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
+    }
+    return device_status("gated_norm_kernel launch");
+  }
   switch (d.dtype) {
     case GDN_F32: return launch_scan_gt<GDN_F32>(a, d.gate_dtype, (int)d.Dk, heads, st);
     case GDN_F16: return launch_scan_gt<GDN_F16>(a, d.gate_dtype, (int)d.Dk, heads, st);

@@ -109,7 +109,8 @@ def test_accepts_valid_arguments():
     ("Dv", 48, 5, "Dk == Dv"),
     ("dtype", 7, 3, "dtype"),
     ("gate_dtype", -1, 3, "gate_dtype"),
-    ("flags", 8, 1, "flag"),
+    ("flags", 16, 1, "flag"),
+    ("flags", 12, 1, "exclude"),
     ("head_major", 2, 1, "head_major"),
     ("qk_eps", -1.0, 1, "eps"),
     ("norm_eps", float("inf"), 1, "eps"),
@@ -123,6 +124,9 @@ def test_rejects_bad_descriptor(field, value, status, needle):
 def test_rejects_unsupported_head_dim():
     rc, why = check(_good(Dk=512, Dv=512), **_ops())
     assert rc == 5 and "head dim" in why
+    rc, why = check(_good(flags=3 | 8), **_ops())  # the block form at D = 64
+    assert rc == 5 and "block form" in why
+    assert check(_good(Dk=128, Dv=128, flags=3 | 8), **_ops())[0] == 0
     rc, why = check(_good(Dk=8, Dv=8), **_ops())
     assert rc == 5
 

@@ -43,11 +43,11 @@ def assert_close(got, ref, tol, what):
         what, worst, tol, np.unravel_index(int(err.argmax()), err.shape))
 
 
-def run_both(ops, *, head_major, gated, dtype, **kw):
+def run_both(ops, *, head_major, gated, dtype, form=None, **kw):
     d = dev(ops)
     z, w = (d.get("z"), d.get("w")) if gated else (None, None)
     y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], z, w,
-                head_major=head_major, **kw)
+                head_major=head_major, form=form, **kw)
     torch.cuda.synchronize()
     yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
                       ops.get("z") if gated else None, ops.get("w") if gated else None,
@@ -169,6 +169,9 @@ def test_small_cases(case, gated):
     say("small %s gated=%s" % (case, gated))
     ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm, seed=B * 131 + T)
     run_both(ops, head_major=hm, gated=gated, dtype=dtype)
+    if D == 128:  # both forms of the time loop
+        run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="per_token")
+        run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="block")
 
 
 def test_gate_dtype_differs_from_operand_dtype():
@@ -236,7 +239,8 @@ MIXED = [
 
 @pytest.mark.parametrize("case", MIXED, ids=lambda c: "B%dT%dHv%dD%d-%s" % (
     c[0], c[1], c[3], c[4], c[5]))
-def test_mixed_fast_and_checked_chunks(case):
+@pytest.mark.parametrize("form", [None, "per_token", "block"])
+def test_mixed_fast_and_checked_chunks(case, form):
     """Chunks whose decays stay mild take the chunk-scalar loop; chunks with a
     large |log_decay| sum, an alpha of 0 or growth (alpha > 1) take the loop
     that keeps the scale per token.  Both kinds alternate along one sequence."""
@@ -254,7 +258,9 @@ def test_mixed_fast_and_checked_chunks(case):
         ld[at(t)] = 0.3                  # growth over ten tokens
     for t in range(3, 9):
         ld[at(t)] = -6.5                 # six strong decays: a sum near the bound
-    run_both(ops, head_major=hm, gated=True, dtype=dtype)
+    if form == "block" and D != 128:
+        pytest.skip("the block form is built for D == 128")
+    run_both(ops, head_major=hm, gated=True, dtype=dtype, form=form)
 
 
 def test_in_place_state_and_time_chaining():
@@ -367,24 +373,27 @@ def test_config2_chained_decode_sampled():
     _check_heads(yall, state.cpu(), ops, heads, False, TOL["bf16"], "config2")
 
 
-def test_config3_prefill_scan_sampled():
+@pytest.mark.parametrize("form", [None, "per_token", "block"])
+def test_config3_prefill_scan_sampled(form):
     wl = synth.WORKLOADS[3]
-    say("config3: B=1 T=4096 token-major scan")
+    say("config3: B=1 T=4096 token-major scan, form %s" % form)
     ops = synth.make(wl)
     d = dev(ops)
-    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"])
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"],
+                form=form)
     torch.cuda.synchronize()
     heads = _sample_heads(wl.B, wl.Hv, 6, 3)
     _check_heads(y.cpu(), s.cpu(), ops, heads, False, TOL["bf16"], "config3")
 
 
-def test_config4_head_major_scan_sampled():
+@pytest.mark.parametrize("form", [None, "per_token", "block"])
+def test_config4_head_major_scan_sampled(form):
     wl = synth.WORKLOADS[4]
-    say("config4: B=16 T=1024 head-major f16 scan")
+    say("config4: B=16 T=1024 head-major f16 scan, form %s" % form)
     ops = synth.make(wl)
     d = dev(ops)
     y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"],
-                head_major=True)
+                head_major=True, form=form)
     torch.cuda.synchronize()
     heads = _sample_heads(wl.B, wl.Hv, 10, 4)
     _check_heads(y.cpu(), s.cpu(), ops, heads, True, TOL["f16"], "config4")
