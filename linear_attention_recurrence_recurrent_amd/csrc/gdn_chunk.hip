@@ -15,12 +15,13 @@
 //   O  = diag(gam) Q^ S^T + (tril(Q^ K^^T) (.) Dc) C,
 //   S' = gam_15 S + ((diag(Dc[15][.]) K^)^T C)^T.
 // With T = (I + Ls)^-1 (unit lower triangular, 16 x 16) the state enters only
-// through products:  C = T diag(beta) V - W S^T with W = T diag(beta gam) K^.
-// Per block and head the kernel forms the state-independent pieces
-// (K K^T, Q K^T, the decay products, T by forward substitution, W) and then,
-// per 16 value rows (an "a-tile"), runs W S^T and Q S^T (16 x 128 x 16), the
-// small T V and the masked products, and the rank-16 update of S^T, all as
-// v_mfma_f32_16x16x4f32.  S^T stays in the accumulator layout for the whole
+// through products:  C = U - W S^T with U = T diag(beta) V and
+// W = T diag(beta gam) K^.  Per block and head the kernel forms the
+// state-independent pieces -- K K^T and Q K^T on the matrix cores, the decay
+// products, and U and W by forward substitution through (I + Ls), one lane
+// per key or value column -- and then, per 16 value rows (an "a-tile"), runs
+// W S^T and Q S^T (16 x 128 x 16), the masked product for O and the rank-16
+// update of S^T as v_mfma_f32_16x16x4f32.  S^T stays in the accumulator layout for the whole
 // time axis: lane l, register r of a 16 x 16 tile holds S^T[4(l/16) + r][l%16]
 // (key row within the tile, value column), which is also a valid B operand of
 // the next product when the contraction index is taken in the matching order.
@@ -53,7 +54,8 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 // a-tile by splitting its 8 key tiles (their partial products are summed
 // through LDS).  NW = NA * NC waves.
 template <int DT, int GT, int NA, int NC, bool FUSE>
-__global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(NA* NC* kWave)
+__attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void chunk_kernel(ChunkArgs a) {
   constexpr int NW = NA * NC, NT = NW * kWave, ROWS = 16 * NA, NCT = 8 / NC;
   static_assert(NT >= 256 && NW <= 8 && NC >= 1 && 8 % NC == 0, "shape");
   static_assert(!FUSE || ROWS == kD, "the fused norm needs the whole head");
@@ -67,15 +69,16 @@ __global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
   __shared__ __align__(16) float sal[kL];
   __shared__ float sbe[kL], srk[kL], srq[kL];
   // block pieces
-  __shared__ float sGp[NW][kL][kL + 1], sHp[NW][kL][kL + 1];  // per-wave partial K K^T, Q K^T
+  // K K^T and Q K^T: half the waves each, as partial sums over key tiles
+  constexpr int NH = NW / 2;
+  __shared__ float sGp[NH][kL][kL + 1], sHp[NH][kL][kL + 1];
   __shared__ float sDc[kL][kL + 1];
   __shared__ __align__(16) float sLs[kL][kL];
-  __shared__ float sT[kL][kL + 1];
   __shared__ __align__(16) float sHd[kL][kL];
-  __shared__ __align__(16) float sW[kL][kD];
-  __shared__ __align__(16) float sKdT[kD][kL];
+  __shared__ __align__(16) float sW[kL][kD];    // W = T diag(beta gam rk) K
+  __shared__ __align__(16) float sU[kL][ROWS];  // U = T diag(beta) V
   __shared__ __align__(16) float ssig[kL];
-  __shared__ float swsc[kL], sgl;
+  __shared__ float swsc[kL], srs[kL], sgl;
   __shared__ v4f spart[NC > 1 ? NW : 1][2][kWave];
 
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -230,25 +233,22 @@ __global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
       for (int m = 1; m < kL; ++m) p *= (m > j && m <= i) ? al[m] : 1.f;
       sDc[i][j] = p;
     }
-    {
-      v4f g = {0.f, 0.f, 0.f, 0.f}, h = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ct = wave; ct < 8; ct += NW) {
+    {  // waves [0, NH) K K^T, waves [NH, NW) Q K^T, each over 8/NH key tiles
+      const bool is_h = wave >= NH;
+      const int part = wave % NH;
+      v4f g = {0.f, 0.f, 0.f, 0.f};
+      for (int ct = part * (8 / NH); ct < (part + 1) * (8 / NH); ++ct) {
         const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * ct + 4 * lg]);
-        const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * ct + 4 * lg]);
-        g = mfma4(kf.x, kf.x, g);
-        h = mfma4(qf.x, kf.x, h);
-        g = mfma4(kf.y, kf.y, g);
-        h = mfma4(qf.y, kf.y, h);
-        g = mfma4(kf.z, kf.z, g);
-        h = mfma4(qf.z, kf.z, h);
-        g = mfma4(kf.w, kf.w, g);
-        h = mfma4(qf.w, kf.w, h);
+        const float4 af = is_h ? *reinterpret_cast<const float4*>(&sq[lc][16 * ct + 4 * lg]) : kf;
+        g = mfma4(af.x, kf.x, g);
+        g = mfma4(af.y, kf.y, g);
+        g = mfma4(af.z, kf.z, g);
+        g = mfma4(af.w, kf.w, g);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sGp[wave][4 * lg + r][lc] = g[r];
-        sHp[wave][4 * lg + r][lc] = h[r];
+        if (is_h) sHp[part][4 * lg + r][lc] = g[r];
+        else sGp[part][4 * lg + r][lc] = g[r];
       }
     }
     __syncthreads();
@@ -259,9 +259,9 @@ __global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
       const float dc = sDc[i][j];
       float gij = 0.f, hij = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
-        gij += sGp[w2][i][j];
-        hij += sHp[w2][i][j];
+      for (int p2 = 0; p2 < NH; ++p2) {
+        gij += sGp[p2][i][j];
+        hij += sHp[p2][i][j];
       }
       sLs[i][j] = j < i ? sbe[i] * srk[i] * gij * srk[j] * dc : 0.f;
       sHd[i][j] = j <= i ? srq[i] * hij * srk[j] * dc : 0.f;
@@ -269,44 +269,38 @@ __global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
         const float gam = sal[0] * sDc[i][0];
         ssig[i] = gam * srq[i];
         swsc[i] = sbe[i] * gam * srk[i];
+        srs[i] = srk[i] * sDc[kL - 1][i];  // k^ scale of the update: decay to the block end
         if (i == kL - 1) sgl = gam;
       }
     }
     __syncthreads();
 
-    // ---- block pieces 3: T = (I + Ls)^-1 by forward substitution (one lane
-    // per column); the other threads form (diag(rk * Dc[15][.]) K)^T
-    if (tid < kL) {  // four partial sums per row: a short dependent chain
-      const int j = tid;
+    // ---- block pieces 3: W and U by forward substitution through (I + Ls),
+    // one lane per key column (W) or value column (U); four partial sums per
+    // row keep the dependent chain short
+    // x = (I + Ls)^-1 b for one column b (b[i] = scale[i] * src[i * stride])
+    auto substitute = [&](const float* src, int stride, const float* scale, float* dst,
+                          int dstride) {
       float x[kL];
 #pragma unroll
       for (int i = 0; i < kL; ++i) {
-        float acc[4] = {i == j ? 1.f : 0.f, 0.f, 0.f, 0.f};
+        float ls[kL];  // row i of Ls (broadcast reads), then its dot with x[0..i)
 #pragma unroll
-        for (int m = 0; m < i; ++m) acc[m % 4] = fmaf(-sLs[i][m], x[m], acc[m % 4]);
-        const float xi = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        x[i] = i < j ? 0.f : xi;
-        sT[i][j] = x[i];
-      }
-    }
-    for (int e = tid; e < kD * kL; e += NT) {
-      const int cc = e / kL, t = e % kL;
-      sKdT[cc][t] = sk[t][cc] * srk[t] * sDc[kL - 1][t];
-    }
-    __syncthreads();
-
-    // ---- block pieces 4: W = T diag(beta gam rk) K, one 16 x 16 key tile per
-    // wave at a time
-    for (int ct = wave; ct < 8; ct += NW) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < kL; m += 4) {
+          const float4 r4 = *reinterpret_cast<const float4*>(&sLs[i][m]);
+          ls[m] = r4.x; ls[m + 1] = r4.y; ls[m + 2] = r4.z; ls[m + 3] = r4.w;
+        }
+        float acc[4] = {scale[i] * src[i * stride], 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int tp = 4 * s + lg;
-        acc = mfma4(sT[lc][tp] * swsc[tp], sk[tp][16 * ct + lc], acc);
+        for (int m = 0; m < i; ++m) acc[m % 4] = fmaf(-ls[m], x[m], acc[m % 4]);
+        x[i] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        asm volatile("" ::: "memory");  // row by row: no load moves across, few live registers
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sW[4 * lg + r][16 * ct + lc] = acc[r];
-    }
+      for (int i = 0; i < kL; ++i) dst[i * dstride] = x[i];
+    };
+    if (tid < kD) substitute(&sk[0][tid], kD, swsc, &sW[0][tid], kD);
+    else if (tid < kD + ROWS) substitute(&sv[0][tid - kD], ROWS, sbe, &sU[0][tid - kD], ROWS);
     __syncthreads();
 
     // ---- the state: W S^T and Q S^T over this wave's key tiles
@@ -316,6 +310,7 @@ __global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
       const int kt = cp * NCT + ct;
       const float4 wf = *reinterpret_cast<const float4*>(&sW[lc][16 * kt + 4 * lg]);
       const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * kt + 4 * lg]);
+      if (ct % 2 == 0) __builtin_amdgcn_sched_barrier(0);
       pw = mfma4(wf.x, St[ct][0], pw);
       pq = mfma4(qf.x, St[ct][0], pq);
       pw = mfma4(wf.y, St[ct][1], pw);
@@ -337,14 +332,10 @@ __global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
         pq += spart[ai * NC + p][1][lane];
       }
     }
-    // C = T diag(beta) V - W S^T   (rows: tokens, columns: this a-tile's rows)
-    v4f cc = {0.f, 0.f, 0.f, 0.f};
+    // C = U - W S^T   (rows: tokens, columns: this a-tile's rows)
+    v4f cc;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int tp = 4 * s + lg;
-      cc = mfma4(sT[lc][tp], sbe[tp] * sv[tp][16 * ai + lc], cc);
-    }
-    cc -= pw;
+    for (int r = 0; r < 4; ++r) cc[r] = sU[4 * lg + r][16 * ai + lc] - pw[r];
     // O = diag(gam rq) Q S^T + (tril(Q^ K^^T) (.) Dc) C
     v4f o = {0.f, 0.f, 0.f, 0.f};
     {
@@ -365,15 +356,15 @@ __global__ __launch_bounds__(NA* NC* kWave) void chunk_kernel(ChunkArgs a) {
     }
     // S^T = gam_15 S^T + (diag(rk Dc[15][.]) K)^T C
     const float gl = sgl;
+    float rsl[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) rsl[s2] = srs[4 * lg + s2];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int kt = cp * NCT + ct;
-      const float4 kf = *reinterpret_cast<const float4*>(&sKdT[16 * kt + lc][4 * lg]);
+      const int kc = 16 * (cp * NCT + ct) + lc;
       v4f acc = St[ct] * gl;
-      acc = mfma4(kf.x, cc[0], acc);
-      acc = mfma4(kf.y, cc[1], acc);
-      acc = mfma4(kf.z, cc[2], acc);
-      acc = mfma4(kf.w, cc[3], acc);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(sk[4 * lg + s2][kc] * rsl[s2], cc[s2], acc);
       St[ct] = acc;
     }
     __syncthreads();
