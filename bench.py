@@ -227,7 +227,7 @@ def bench_scan(idx, args, torch):
     stream = torch.cuda.current_stream(dev)
     dt = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
     desc = gdn._desc(wl.B, wl.T, wl.Hk, wl.Hv, wl.Dk, wl.Dv, wl.head_major, dt, dt, True, True,
-                     1e-6, 1e-6)
+                     1e-6, 1e-6, None if args.scan_form == "auto" else args.scan_form)
     call = Launcher("gdn_scan", desc, [d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
                                        d["z"], d["w"], y, s_out], stream.cuda_stream)
     reps = max(3, args.steps)
@@ -385,6 +385,8 @@ def main():
     ap.add_argument("--no-scan", action="store_true", help="skip the scan sub-measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--scan-form", choices=("auto", "per_token", "block"), default="auto",
+                    help="time loop of the scan (default: the library's choice per shape)")
     ap.add_argument("--scan-only", action="store_true",
                     help="only the two scan workloads (for counter collection); partial JSON")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
