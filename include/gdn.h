@@ -25,10 +25,13 @@
  *
  * Conventions common to every call.
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, dense and
- *     row-major in the layout given below.  The library allocates nothing,
- *     keeps no state between calls and never synchronises: all work is
- *     enqueued on `stream` (a hipStream_t; NULL is the null stream) on the
- *     current HIP device, and the call returns as soon as it is enqueued.
+ *     row-major in the layout given below.  The library keeps no state
+ *     between calls and never synchronises: all work is enqueued on `stream`
+ *     (a hipStream_t; NULL is the null stream) on the current HIP device, and
+ *     the call returns as soon as it is enqueued.  It allocates nothing,
+ *     except the block form of gdn_scan (below), which takes a stream-ordered
+ *     workspace with hipMallocAsync on `stream` and returns it with
+ *     hipFreeAsync on the same stream before the call returns.
  *   - Layouts (head_major == 0 / 1):
  *         q, k        [B, T, Hk, Dk]   /  [B, Hk, T, Dk]      dtype
  *         v, z        [B, T, Hv, Dv]   /  [B, Hv, T, Dv]      dtype
@@ -82,9 +85,12 @@ typedef enum gdn_status {
  * units for every head dim; at Dk == Dv == 128 the block form runs 16 tokens
  * at a time as dense products on the matrix cores (the step is affine in S,
  * "Module gdn" page, "The fusion").  Both give the same results up to
- * rounding.  Without either flag the library picks the form it runs faster
- * for the shape; with both, or GDN_SCAN_BLOCK at another head dim, the call
- * is rejected (GDN_EINVAL / GDN_EUNSUPPORTED). */
+ * rounding.  Without either flag the block form runs at Dk == Dv == 128 and
+ * the token-by-token form otherwise; with both flags, or GDN_SCAN_BLOCK at
+ * another head dim, the call is rejected (GDN_EINVAL / GDN_EUNSUPPORTED).
+ * The block form's workspace holds one 2560-byte record per value head and
+ * 16-token block: B * Hv * ceil(T / 16) * 2560 bytes (GDN_EDEVICE when it
+ * cannot be allocated). */
 #define GDN_SCAN_PER_TOKEN 4u
 #define GDN_SCAN_BLOCK 8u
 
@@ -126,7 +132,8 @@ int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* 
  * gated_delta_reference: the recurrence over the time axis returning
  * (output, final_state)).  Any T >= 0; T == 0 copies s0 to s_out (unless
  * they are the same buffer) and writes no y.  The state stays in registers
- * for the whole time axis; s_out receives the state after the last token. */
+ * for the whole time axis; s_out receives the state after the last token.
+ * The form of the time loop follows GDN_SCAN_PER_TOKEN / GDN_SCAN_BLOCK. */
 int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
              const void* log_decay, const void* beta, const float* s0, const void* z,
              const void* w, float* y, float* s_out, void* stream);

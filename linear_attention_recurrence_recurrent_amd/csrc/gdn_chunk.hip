@@ -16,7 +16,7 @@
 //   S' = gam_15 S + ((diag(Dc[15][.]) K^)^T C)^T.
 // Everything but the products with S depends on the block's own inputs, so
 // the work splits in two launches:
-//   prep_kernel  (one workgroup per head and block, all in parallel): the
+//   prep_kernel  (one wave per key head and block, all in parallel): the
 //                norms, decay products, K K^T and Q K^T on the matrix cores,
 //                T = (I + Ls)^-1 by forward substitution and the masked
 //                Hd = tril(Q^ K^^T) (.) Dc, written as a small block record;
@@ -88,124 +88,144 @@ __device__ __forceinline__ Bases head_bases(int64_t b, int hv, int hk, int Hk, i
 struct PrepArgs {
   const void *q, *k, *ld, *beta;
   float* rec;
-  int64_t T, nblk;
+  int64_t T, nblk, ntask;  // ntask = B * Hk * nblk
   int Hk, Hv, G, head_major;
   uint32_t flags;
   float qk_eps, qscale;
 };
 
+// One wave per (batch, key head, block): K K^T and Q K^T once, then the
+// records of the G value heads that share the key head (four at a time, one
+// per 16-lane group).  No workgroup barrier: each wave owns its LDS slice.
 template <int DT, int GT>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-  __shared__ __align__(16) float sk[kL][kPad];
-  __shared__ __align__(16) float sq[kL][kPad];
-  __shared__ float sGp[2][kL][kL + 1], sHp[2][kL][kL + 1];
-  __shared__ float sLs[kL][kL + 1];
-  __shared__ float sal[kL], sbe[kL], srk[kL], srq[kL];
-
-  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t c = tile % a.nblk, bh = tile / a.nblk;
-  const int hv = (int)(bh % a.Hv), hk = hv / a.G;
-  const int64_t b = bh / a.Hv;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int lg = lane / 16, lc = lane % 16;
-  const int64_t t0 = c * kL;
-  const int tc = (int)((a.T - t0) < kL ? (a.T - t0) : kL);
-  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, a.T, a.head_major);
-  float* rec = a.rec + record_at(bh, c, a.nblk);
+  const int64_t task = (int64_t)blockIdx.x * 4 + wave;
+  if (task >= a.ntask) return;  // uniform per wave
+  const int64_t c = task % a.nblk, bk = task / a.nblk;
+  const int hk = (int)(bk % a.Hk);
+  const int64_t b = bk / a.Hk, T = a.T, t0 = c * kL;
+  const int tc = (int)((T - t0) < kL ? (T - t0) : kL);
+  int64_t qk_base, qk_ts;
+  if (a.head_major) {
+    qk_base = (b * a.Hk + hk) * T * kD; qk_ts = kD;
+  } else {
+    qk_base = (b * T * a.Hk + hk) * kD; qk_ts = (int64_t)a.Hk * kD;
+  }
 
-  {  // raw k and q into LDS (thread: token tid / 16, elements 8 (tid % 16) ..), norms
-    const int tt = tid / 16, c8 = tid % 16;
-    Raw<DT, 8> rk8, rq8;
-    if (tt < tc) {
-      rk8.load(a.k, bs.qk + (t0 + tt) * bs.qk_ts + 8 * c8);
-      rq8.load(a.q, bs.qk + (t0 + tt) * bs.qk_ts + 8 * c8);
+  // rows of q and k: lane (lg, lc) holds row lc, elements [32 lg, 32 lg + 32)
+  Raw<DT, 8> kr[4], qr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (lc < tc) {
+      kr[u].load(a.k, qk_base + (t0 + lc) * qk_ts + 32 * lg + 8 * u);
+      qr[u].load(a.q, qk_base + (t0 + lc) * qk_ts + 32 * lg + 8 * u);
     } else {
-      rk8.zero();
-      rq8.zero();
+      kr[u].zero();
+      qr[u].zero();
     }
-    if (tid < kL) {
-      float al = 1.f, be = 0.f;
-      if (tid < tc) {
-        Raw<GT, 1> l1, b1;
-        l1.load(a.ld, bs.g + (t0 + tid) * bs.g_ts);
-        b1.load(a.beta, bs.g + (t0 + tid) * bs.g_ts);
-        al = expf(l1.get(0));
-        be = b1.get(0);
+  }
+  float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ssk = fmaf(kr[u].get(e), kr[u].get(e), ssk);
+      ssq = fmaf(qr[u].get(e), qr[u].get(e), ssq);
+    }
+  ssk += __shfl_xor(ssk, 16);
+  ssk += __shfl_xor(ssk, 32);
+  ssq += __shfl_xor(ssq, 16);
+  ssq += __shfl_xor(ssq, 32);
+  const bool l2 = (a.flags & GDN_FOLD_QK_L2NORM) != 0;
+  float rk = rsqrtf(l2 ? ssk + a.qk_eps : 1.f);          // of row lc
+  float rq = rsqrtf(l2 ? ssq + a.qk_eps : 1.f) * a.qscale;
+  if (lc >= tc) rk = rq = 0.f;
+
+  // G = K K^T and H = Q K^T (raw) on the matrix cores; product m contracts
+  // key index 32 lg + m.  Lane (lg, lc), register r: entry [4 lg + r][lc].
+  v4f G4 = {0.f, 0.f, 0.f, 0.f}, H4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float kv = kr[u].get(e);
+      G4 = mfma4(kv, kv, G4);
+      H4 = mfma4(qr[u].get(e), kv, H4);
+    }
+  float rki[4], rqi[4];  // norms of the lane's rows i = 4 lg + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    rki[r] = __shfl(rk, 4 * lg + r);
+    rqi[r] = __shfl(rq, 4 * lg + r);
+  }
+
+  for (int g0 = 0; g0 < a.G; g0 += 4) {
+    // gates: lane (lg, lc) loads token lc of value head g0 + lg
+    const int g = g0 + lg, hv = hk * a.G + g;
+    const bool gv = g < a.G;
+    float al = 1.f, be = 0.f;
+    if (gv && lc < tc) {
+      const int64_t gi = a.head_major ? (b * a.Hv + hv) * T + t0 + lc
+                                      : (b * T + t0 + lc) * a.Hv + hv;
+      Raw<GT, 1> l1, b1;
+      l1.load(a.ld, gi);
+      b1.load(a.beta, gi);
+      al = expf(l1.get(0));
+      be = b1.get(0);
+    }
+    const int ng = a.G - g0 < 4 ? a.G - g0 : 4;
+    for (int gq = 0; gq < ng; ++gq) {  // Ls and Hd of value head g0 + gq, all lanes
+      float als[kL];
+#pragma unroll
+      for (int m = 0; m < kL; ++m)
+        als[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * gq + m));
+      float* rec = a.rec + record_at(b * a.Hv + hk * a.G + g0 + gq, c, a.nblk);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * lg + r, j = lc;
+        const float bei = __shfl(be, 16 * gq + i);
+        float dc = j <= i ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 1; m < kL; ++m) dc *= (m > j && m <= i) ? als[m] : 1.f;
+        sLs[wave][gq][i][j] = j < i ? bei * rki[r] * G4[r] * rk * dc : 0.f;
+        rec[kRecH + 16 * i + j] = j <= i ? rqi[r] * H4[r] * rk * dc : 0.f;
       }
-      sal[tid] = al;
-      sbe[tid] = be;
     }
-    const float4 k0 = rk8.get4(0), k1 = rk8.get4(1), q0 = rq8.get4(0), q1 = rq8.get4(1);
-    *reinterpret_cast<float4*>(&sk[tt][8 * c8]) = k0;
-    *reinterpret_cast<float4*>(&sk[tt][8 * c8 + 4]) = k1;
-    *reinterpret_cast<float4*>(&sq[tt][8 * c8]) = q0;
-    *reinterpret_cast<float4*>(&sq[tt][8 * c8 + 4]) = q1;
-    const float ssk = group_sum<16>(dot4(k1, k1, dot4(k0, k0, 0.f)));
-    const float ssq = group_sum<16>(dot4(q1, q1, dot4(q0, q0, 0.f)));
-    if (c8 == 0) {
-      const bool l2 = (a.flags & GDN_FOLD_QK_L2NORM) != 0;
-      float rk = rsqrtf(l2 ? ssk + a.qk_eps : 1.f);
-      float rq = rsqrtf(l2 ? ssq + a.qk_eps : 1.f) * a.qscale;
-      if (tt >= tc) rk = rq = 0.f;
-      srk[tt] = rk;
-      srq[tt] = rq;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (gv) {  // lane group lg: value head g; lane lc: token lc and column lc
+      float* rec = a.rec + record_at(b * a.Hv + hv, c, a.nblk);
+      float gam = 1.f, tail = 1.f;
+#pragma unroll
+      for (int m = 0; m < kL; ++m) {
+        const float am = __shfl(al, 16 * lg + m);
+        gam *= m <= lc ? am : 1.f;
+        tail *= m > lc ? am : 1.f;
+      }
+      rec[kRecSig + lc] = gam * rq;
+      rec[kRecWsc + lc] = be * gam * rk;
+      rec[kRecBe + lc] = be;
+      rec[kRecSrs + lc] = rk * tail;
+      if (lc == kL - 1) rec[kRecGl] = gam;
+      // column lc of T = (I + Ls)^-1 by forward substitution
+      float x[kL];
+#pragma unroll
+      for (int r = 0; r < kL; ++r) {
+        float acc[4] = {r == lc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < r; ++m) acc[m % 4] = fmaf(-sLs[wave][lg][r][m], x[m], acc[m % 4]);
+        x[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      }
+#pragma unroll
+      for (int r = 0; r < kL; ++r) rec[kRecT + 16 * r + lc] = x[r];
     }
-  }
-  __syncthreads();
-
-  // decay products: thread (i, j) one entry
-  const int i = tid / 16, j = tid % 16;
-  float dc = j <= i ? 1.f : 0.f;
-#pragma unroll
-  for (int m = 1; m < kL; ++m) dc *= (m > j && m <= i) ? sal[m] : 1.f;
-  {  // waves 0, 1: K K^T; waves 2, 3: Q K^T; each over four key tiles
-    const bool is_h = wave >= 2;
-    const int part = wave & 1;
-    v4f g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ct = 4 * part; ct < 4 * part + 4; ++ct) {
-      const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * ct + 4 * lg]);
-      const float4 af = is_h ? *reinterpret_cast<const float4*>(&sq[lc][16 * ct + 4 * lg]) : kf;
-      g = mfma4(af.x, kf.x, g);
-      g = mfma4(af.y, kf.y, g);
-      g = mfma4(af.z, kf.z, g);
-      g = mfma4(af.w, kf.w, g);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (is_h) sHp[part][4 * lg + r][lc] = g[r];
-      else sGp[part][4 * lg + r][lc] = g[r];
-    }
-  }
-  __syncthreads();
-
-  {  // Ls, Hd and the per-token scales
-    const float gij = sGp[0][i][j] + sGp[1][i][j], hij = sHp[0][i][j] + sHp[1][i][j];
-    sLs[i][j] = j < i ? sbe[i] * srk[i] * gij * srk[j] * dc : 0.f;
-    rec[kRecH + 16 * i + j] = j <= i ? srq[i] * hij * srk[j] * dc : 0.f;
-    if (j == 0) {
-      const float gam = sal[0] * dc;
-      rec[kRecSig + i] = gam * srq[i];
-      rec[kRecWsc + i] = sbe[i] * gam * srk[i];
-      rec[kRecBe + i] = sbe[i];
-      if (i == kL - 1) rec[kRecGl] = gam;
-    }
-    if (i == kL - 1) rec[kRecSrs + j] = srk[j] * dc;
-  }
-  __syncthreads();
-
-  // T = (I + Ls)^-1, one lane per column
-  if (tid < kL) {
-    float x[kL];
-#pragma unroll
-    for (int r = 0; r < kL; ++r) {
-      float acc[4] = {r == tid ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < r; ++m) acc[m % 4] = fmaf(-sLs[r][m], x[m], acc[m % 4]);
-      x[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    }
-#pragma unroll
-    for (int r = 0; r < kL; ++r) rec[kRecT + 16 * r + tid] = x[r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -225,18 +245,20 @@ struct StateArgs {
 
 // Workgroup = (value head, NA a-tiles of 16 value rows); NC waves share an
 // a-tile by splitting its 8 key tiles (their partial products are summed
-// through LDS).  NW = NA * NC waves.
-template <int DT, int NA, int NC, bool FUSE>
+// through LDS).  NW = NA * NC waves.  The loads of block c + DEPTH are
+// issued while block c is computed.
+template <int DT, int NA, int NC, int DEPTH, bool FUSE>
 __global__ __launch_bounds__(NA* NC* kWave)
 __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(StateArgs a) {
   constexpr int NW = NA * NC, NT = NW * kWave, ROWS = 16 * NA, NCT = 8 / NC;
   static_assert(NT >= 256 && NW <= 8 && NC >= 1 && 8 % NC == 0, "shape");
   static_assert(!FUSE || ROWS == kD, "the fused norm needs the whole head");
+  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth");
   __shared__ __align__(16) float sk[kL][kPad];
   __shared__ __align__(16) float sq[kL][kPad];
   __shared__ float sv[kL][ROWS];
   __shared__ float sz[FUSE ? 2 : 1][FUSE ? kL : 1][FUSE ? kD : 1];
-  __shared__ __align__(16) float so[kL][ROWS];
+  __shared__ __align__(16) float so[2][kL][ROWS];
   __shared__ __align__(16) float srec[kRecUsed];
   __shared__ v4f spart[NC > 1 ? NW : 1][2][kWave];
 
@@ -268,57 +290,60 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
     Raw<DT, 2> z[NZP];
     Raw<GDN_F32, 4> r[NRC];
   };
+  // Every lane issues every load of a block (token and item indices clamped
+  // into range; the excess is zeroed or dropped when the block is written to
+  // LDS), so no branch skips a load.
+  auto clamp_t = [&](int tt, int tc) { return tt < tc ? tt : tc - 1; };
   auto chunk_load = [&](Regs& P, int64_t c, int tc) {
     const int64_t t0 = c * kL;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      const int e = tid + i * NT, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
-      if (e < 512 && tt < tc) P.qk[i].load(which ? a.q : a.k, bs.qk + (t0 + tt) * bs.qk_ts + 8 * c8);
-      else P.qk[i].zero();
+      const int e = (tid + i * NT) % 512, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
+      P.qk[i].load(which ? a.q : a.k, bs.qk + (t0 + clamp_t(tt, tc)) * bs.qk_ts + 8 * c8);
     }
 #pragma unroll
     for (int i = 0; i < NVP; ++i) {
-      const int e = tid + i * NT, tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
-      if (e < kL * ROWS / 2 && tt < tc) P.v[i].load(a.v, bs.v + (t0 + tt) * bs.v_ts + row0 + 2 * r2);
+      const int e = (tid + i * NT) % (kL * ROWS / 2), tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
+      P.v[i].load(a.v, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + row0 + 2 * r2);
     }
     if constexpr (FUSE) {
+      if (has_z) {
 #pragma unroll
-      for (int i = 0; i < NZP; ++i) {
-        const int e = tid + i * NT, tt = e / (kD / 2), r2 = e % (kD / 2);
-        if (has_z && e < kL * kD / 2 && tt < tc)
-          P.z[i].load(a.z, bs.v + (t0 + tt) * bs.v_ts + 2 * r2);
+        for (int i = 0; i < NZP; ++i) {
+          const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
+          P.z[i].load(a.z, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + 2 * r2);
+        }
       }
     }
 #pragma unroll
-    for (int i = 0; i < NRC; ++i) {  // every lane loads (clamped): no branch around the load
+    for (int i = 0; i < NRC; ++i) {
       const int e = tid + i * NT < NR4 ? tid + i * NT : NR4 - 1;
       P.r[i].load(rec, c * kRec + 4 * e);
     }
   };
-  auto chunk_store = [&](const Regs& P, int tc, int zbuf) {
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): the block's loads are complete
+  // Every lane also writes every item it loaded (lanes past the item count
+  // repeat an item with the same value), so no path leaves a load unread.
+  // Rows past the last token repeat its inputs; the block record gives them
+  // beta = rk = rq = 0, so they add nothing to C, O or the state.
+  auto chunk_store = [&](const Regs& P, int zbuf) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      const int e = tid + i * NT, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
-      if (e < 512) {
-        float* dst = which ? &sq[tt][8 * c8] : &sk[tt][8 * c8];
-        *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
-        *reinterpret_cast<float4*>(dst + 4) = P.qk[i].get4(1);
-      }
+      const int e = (tid + i * NT) % 512, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
+      float* dst = which ? &sq[tt][8 * c8] : &sk[tt][8 * c8];
+      *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
+      *reinterpret_cast<float4*>(dst + 4) = P.qk[i].get4(1);
     }
 #pragma unroll
     for (int i = 0; i < NVP; ++i) {
-      const int e = tid + i * NT, tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
-      if (e < kL * ROWS / 2) {
-        sv[tt][2 * r2] = tt < tc ? P.v[i].get(0) : 0.f;
-        sv[tt][2 * r2 + 1] = tt < tc ? P.v[i].get(1) : 0.f;
-      }
+      const int e = (tid + i * NT) % (kL * ROWS / 2), tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
+      sv[tt][2 * r2] = P.v[i].get(0);
+      sv[tt][2 * r2 + 1] = P.v[i].get(1);
     }
     if constexpr (FUSE) {
+      if (has_z) {
 #pragma unroll
-      for (int i = 0; i < NZP; ++i) {
-        const int e = tid + i * NT, tt = e / (kD / 2), r2 = e % (kD / 2);
-        if (has_z && e < kL * kD / 2 && tt < tc) {
+        for (int i = 0; i < NZP; ++i) {
+          const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
           sz[zbuf][tt][2 * r2] = P.z[i].get(0);
           sz[zbuf][tt][2 * r2 + 1] = P.z[i].get(1);
         }
@@ -326,8 +351,8 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
     }
 #pragma unroll
     for (int i = 0; i < NRC; ++i) {
-      const int e = tid + i * NT;
-      if (e < NR4) *reinterpret_cast<float4*>(&srec[4 * e]) = P.r[i].get4(0);
+      const int e = tid + i * NT < NR4 ? tid + i * NT : NR4 - 1;
+      *reinterpret_cast<float4*>(&srec[4 * e]) = P.r[i].get4(0);
     }
   };
 
@@ -345,33 +370,76 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
 #pragma unroll
     for (int i = 0; i < 2; ++i) wgt[i] = has_z ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
   }
+  const int64_t nblk = a.nblk;
+  auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
 
-  Regs P;
-  chunk_load(P, 0, (int)(T < kL ? T : kL));
-  chunk_store(P, (int)(T < kL ? T : kL), 0);
-
-  for (int64_t c = 0;; ++c) {
+  // Outputs of block c from LDS (a fixed number of stores per lane).  They
+  // run after the top barrier of the next block, before its loads, so the
+  // waits on those loads never have to cover these stores.
+  auto outputs = [&](int64_t c) {
     const int64_t t0 = c * kL;
-    const int tc = (int)((T - t0) < kL ? (T - t0) : kL);
-    const bool more = c + 1 < a.nblk;
-    const int tcn = more ? (int)((T - t0 - kL) < kL ? (T - t0 - kL) : kL) : 0;
-    __syncthreads();
-    if (more) chunk_load(P, c + 1, tcn);
+    const int tc = tc_of(c);
+    if constexpr (FUSE) {
+      if (has_z) {
+        constexpr int TPW = (kL + NW - 1) / NW;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int tt = wave + NW * u;
+          if (tt < kL) {  // uniform per wave
+            const int zb = (int)(c & 1);
+            float x0 = so[c & 1][tt][lane] * silu(sz[zb][tt][lane]);
+            float x1 = so[c & 1][tt][lane + kWave] * silu(sz[zb][tt][lane + kWave]);
+            const float inv = rsqrtf(wave_sum(fmaf(x0, x0, x1 * x1)) * (1.0f / kD) + a.norm_eps);
+            if (tt < tc) {
+              const int64_t vo = bs.v + (t0 + tt) * bs.v_ts;
+              a.y[vo + lane] = x0 * inv * wgt[0];
+              a.y[vo + lane + kWave] = x1 * inv * wgt[1];
+            }
+          }
+        }
+        return;
+      }
+    }
+    constexpr int R4 = ROWS / 4, NO = (kL * R4 + NT - 1) / NT;
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int e = tid + u * NT, tt = e / R4, r4 = e % R4;
+      if (e < kL * R4 && tt < tc)
+        *reinterpret_cast<float4*>(a.y + bs.v + (t0 + tt) * bs.v_ts + row0 + 4 * r4) =
+            *reinterpret_cast<const float4*>(&so[c & 1][tt][4 * r4]);
+    }
+  };
 
-    // K S^T and Q S^T over this wave's key tiles (raw k and q)
+  // One block: LDS holds block c, the loads of block c + DEPTH go into Pl
+  // (issued first), Ps holds block c + 1 in flight (Ps == Pl when DEPTH == 1).
+  // Loads and LDS writes run unconditionally (past the end they repeat the
+  // last block), so every path through the loop leaves the same loads in
+  // flight and the waits before the LDS writes only cover the older block.
+  auto step = [&](int64_t c, Regs& Pl, const Regs& Ps) {
+    const int64_t t0 = c * kL;
+    const int tc = tc_of(c);
+    const int64_t cl = c + DEPTH < nblk ? c + DEPTH : nblk - 1;
+    __syncthreads();
+    if (c > 0) outputs(c - 1);
+    chunk_load(Pl, cl, tc_of(cl));
+
+    // K S^T then Q S^T over this wave's key tiles (raw k and q); K S^T first:
+    // only it is on the chain to the next block
     v4f pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int kt = cp * NCT + ct;
-      const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * kt + 4 * lg]);
-      const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * kt + 4 * lg]);
+      const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * (cp * NCT + ct) + 4 * lg]);
       pk = mfma4(kf.x, St[ct][0], pk);
-      pq = mfma4(qf.x, St[ct][0], pq);
       pk = mfma4(kf.y, St[ct][1], pk);
-      pq = mfma4(qf.y, St[ct][1], pq);
       pk = mfma4(kf.z, St[ct][2], pk);
-      pq = mfma4(qf.z, St[ct][2], pq);
       pk = mfma4(kf.w, St[ct][3], pk);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * (cp * NCT + ct) + 4 * lg]);
+      pq = mfma4(qf.x, St[ct][0], pq);
+      pq = mfma4(qf.y, St[ct][1], pq);
+      pq = mfma4(qf.z, St[ct][2], pq);
       pq = mfma4(qf.w, St[ct][3], pq);
     }
     if constexpr (NC > 1) {
@@ -423,53 +491,43 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
       o = mfma4(hf.z, cc[2], o);
       o = mfma4(hf.w, cc[3], o);
       const float4 sg = *reinterpret_cast<const float4*>(&srec[kRecSig + 4 * lg]);
-      so[4 * lg + 0][16 * ai + lc] = fmaf(sg.x, pq[0], o[0]);
-      so[4 * lg + 1][16 * ai + lc] = fmaf(sg.y, pq[1], o[1]);
-      so[4 * lg + 2][16 * ai + lc] = fmaf(sg.z, pq[2], o[2]);
-      so[4 * lg + 3][16 * ai + lc] = fmaf(sg.w, pq[3], o[3]);
+      so[c & 1][4 * lg + 0][16 * ai + lc] = fmaf(sg.x, pq[0], o[0]);
+      so[c & 1][4 * lg + 1][16 * ai + lc] = fmaf(sg.y, pq[1], o[1]);
+      so[c & 1][4 * lg + 2][16 * ai + lc] = fmaf(sg.z, pq[2], o[2]);
+      so[c & 1][4 * lg + 3][16 * ai + lc] = fmaf(sg.w, pq[3], o[3]);
     }
     __syncthreads();
 
-    // next block into LDS (every block array was last read above); z is
-    // double-buffered because the output below reads this block's slot
-    chunk_store(P, tcn, (int)((c + 1) & 1));
+    // next block into LDS (every block array was last read above); z and o
+    // are double-buffered: the outputs of this block are written at the
+    // start of the next one
+    chunk_store(Ps, (int)((c + 1) & 1));
 
-    // ---- outputs of this block
-    if constexpr (FUSE) {
-      if (has_z) {
-        constexpr int TPW = (kL + NW - 1) / NW;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const int tt = wave + NW * u;
-          if (tt < kL) {  // uniform per wave
-            const int zb = (int)(c & 1);
-            float x0 = so[tt][lane] * silu(sz[zb][tt][lane]);
-            float x1 = so[tt][lane + kWave] * silu(sz[zb][tt][lane + kWave]);
-            const float inv = rsqrtf(wave_sum(fmaf(x0, x0, x1 * x1)) * (1.0f / kD) + a.norm_eps);
-            if (tt < tc) {
-              const int64_t vo = bs.v + (t0 + tt) * bs.v_ts;
-              a.y[vo + lane] = x0 * inv * wgt[0];
-              a.y[vo + lane + kWave] = x1 * inv * wgt[1];
-            }
-          }
-        }
-      } else {
-        for (int e = tid; e < tc * (kD / 4); e += NT) {
-          const int tt = e / (kD / 4), r4 = e % (kD / 4);
-          *reinterpret_cast<float4*>(a.y + bs.v + (t0 + tt) * bs.v_ts + 4 * r4) =
-              *reinterpret_cast<const float4*>(&so[tt][4 * r4]);
-        }
-      }
-    } else {
-      constexpr int R4 = ROWS / 4;
-      for (int e = tid; e < tc * R4; e += NT) {
-        const int tt = e / R4, r4 = e % R4;
-        *reinterpret_cast<float4*>(a.y + bs.v + (t0 + tt) * bs.v_ts + row0 + 4 * r4) =
-            *reinterpret_cast<const float4*>(&so[tt][4 * r4]);
-      }
+  };
+
+  if constexpr (DEPTH == 1) {
+    Regs P;
+    chunk_load(P, 0, tc_of(0));
+    chunk_store(P, 0);
+    for (int64_t c = 0; c < nblk; ++c) step(c, P, P);
+  } else {
+    Regs P0, P1;
+    const int64_t c1 = nblk > 1 ? 1 : 0;
+    chunk_load(P0, 0, tc_of(0));
+    chunk_load(P1, c1, tc_of(c1));
+    chunk_store(P0, 0);
+    // nothing in flight on entry: the loop's own loads are then the only
+    // ones its waits have to count
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    for (int64_t c = 0;; c += 2) {
+      step(c, P0, P1);
+      if (c + 1 >= nblk) break;
+      step(c + 1, P1, P0);
+      if (c + 2 >= nblk) break;
     }
-    if (!more) break;
   }
+  __syncthreads();
+  outputs(nblk - 1);
 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -479,15 +537,15 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
   }
 }
 
-template <int DT, int NA, int NC>
+template <int DT, int NA, int NC, int DEPTH>
 int launch_state(StateArgs a, int64_t heads, hipStream_t st) {
   constexpr int ROWS = 16 * NA;
   a.nrb = kD / ROWS;
   const dim3 grid((unsigned)(heads * a.nrb));
   if constexpr (ROWS == kD) {
-    state_kernel<DT, NA, NC, true><<<grid, NA * NC * kWave, 0, st>>>(a);
+    state_kernel<DT, NA, NC, DEPTH, true><<<grid, NA * NC * kWave, 0, st>>>(a);
   } else {
-    state_kernel<DT, NA, NC, false><<<grid, NA * NC * kWave, 0, st>>>(a);
+    state_kernel<DT, NA, NC, DEPTH, false><<<grid, NA * NC * kWave, 0, st>>>(a);
   }
   return device_status("state_kernel launch");
 }
@@ -505,11 +563,14 @@ int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
 template <int DT>
 int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t heads,
               hipStream_t st) {
-  const dim3 pgrid((unsigned)(heads * p.nblk));
+  const dim3 pgrid((unsigned)((p.ntask + 3) / 4));
   const int rc = launch_prep<DT>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;
-  if (heads >= 256) return launch_state<DT, 8, 1>(s, heads, st);
-  return launch_state<DT, 1, 4>(s, heads, st);
+  // many heads: whole-head workgroups, two per CU, the norm fused; few heads:
+  // a workgroup per 16 value rows, its four waves splitting the key tiles,
+  // loads two blocks ahead (the chain per block is short)
+  if (heads >= 256) return launch_state<DT, 8, 1, 1>(s, heads, st);
+  return launch_state<DT, 1, 4, 2>(s, heads, st);
 }
 
 int64_t block_record_bytes(int64_t heads, int64_t T) {
@@ -535,8 +596,8 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
     return GDN_EDEVICE;
   }
   float* rec = static_cast<float*>(ws);
-  const PrepArgs p{q, k, ld, beta, rec, d.T, nblk, (int)d.Hk, (int)d.Hv, (int)(d.Hv / d.Hk),
-                   d.head_major, d.flags, d.qk_eps, q_scale(d)};
+  const PrepArgs p{q, k, ld, beta, rec, d.T, nblk, d.B * d.Hk * nblk, (int)d.Hk, (int)d.Hv,
+                   (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d)};
   const StateArgs s{q, k, v, z, w, rec, s0, y, s_out, d.T, nblk, (int)d.Hk, (int)d.Hv,
                     (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps};
   int rc;

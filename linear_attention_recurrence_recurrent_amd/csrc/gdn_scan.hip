@@ -508,29 +508,58 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
 
 // ------------------------------------------------------------------ gated RMSNorm
 // In place over y viewed as [nvec, D] (both layouts keep the head dim last and
-// dense, and z shares y's layout); one wave per head vector.
+// dense, and z shares y's layout); a wave per kNormVPW head vectors.
+constexpr int kNormVPW = 8;
+inline dim3 norm_grid(int64_t nvec) {
+  const int64_t per_block = kNormVPW * (256 / kWave);
+  return dim3((unsigned)((nvec + per_block - 1) / per_block));
+}
 template <int DT, int D>
 __global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z, const void* w,
                                                          int64_t nvec, float eps) {
-  constexpr int EPL = (D + kWave - 1) / kWave;
+  // a wave handles kNormVPW vectors, all loads issued before any use; a lane
+  // owns EPL consecutive elements of each (vector loads)
+  constexpr int EPL = D >= kWave ? D / kWave : 1, V = kNormVPW;
   const int lane = threadIdx.x % kWave;
-  const int64_t vec = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
-  if (vec >= nvec) return;  // uniform per wave
-  const int64_t base = vec * D;
-  float x[EPL];
-  float ss = 0.f;
+  const int64_t v0 = ((int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave) * V;
+  const int r0 = lane * EPL;
+  const bool act = r0 < D;
+  Raw<GDN_F32, EPL> yv[V];
+  Raw<DT, EPL> zv[V];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int rr = lane + kWave * i;
-    x[i] = 0.f;
-    if (rr < D) x[i] = y[base + rr] * silu(ld1<DT>(z, base + rr));
-    ss = fmaf(x[i], x[i], ss);
+  for (int u = 0; u < V; ++u) {
+    if (act && v0 + u < nvec) {  // uniform per wave but for act
+      yv[u].load(y, (v0 + u) * D + r0);
+      zv[u].load(z, (v0 + u) * D + r0);
+    } else {
+      yv[u].zero();
+      zv[u].zero();
+    }
   }
-  const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + eps);
+  float wl[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int rr = lane + kWave * i;
-    if (rr < D) y[base + rr] = x[i] * inv * ld1<DT>(w, rr);
+  for (int i = 0; i < EPL; ++i) wl[i] = act ? ld1<DT>(w, r0 + i) : 0.f;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    float x[EPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      x[i] = yv[u].get(i) * silu(zv[u].get(i));
+      ss = fmaf(x[i], x[i], ss);
+    }
+    const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + eps);
+    if (act && v0 + u < nvec) {
+      float* dst = y + (v0 + u) * D + r0;
+      if constexpr (EPL == 4) {
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(x[0] * inv * wl[0], x[1] * inv * wl[1], x[2] * inv * wl[2], x[3] * inv * wl[3]);
+      } else if constexpr (EPL == 2) {
+        *reinterpret_cast<float2*>(dst) = make_float2(x[0] * inv * wl[0], x[1] * inv * wl[1]);
+      } else {
+        dst[0] = x[0] * inv * wl[0];
+      }
+    }
   }
 }
 
@@ -549,7 +578,7 @@ int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
     int rc = device_status("scan_kernel launch");
     if (rc != GDN_OK || a.z == nullptr) return rc;
     const int64_t nvec = heads * a.T;
-    gated_norm_kernel<DT, D><<<dim3((unsigned)((nvec + 3) / 4)), 256, 0, st>>>(
+    gated_norm_kernel<DT, D><<<norm_grid(nvec), 256, 0, st>>>(
         a.y, a.z, a.w, nvec, a.norm_eps);
     return device_status("gated_norm_kernel launch");
   }
@@ -594,14 +623,15 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
                    (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags,
                    d.qk_eps, d.norm_eps, q_scale(d)};
   const int64_t heads = d.B * d.Hv;
-  // the block form where it is measured faster, or when asked for
-  const bool block = (d.flags & GDN_SCAN_BLOCK) != 0;
-  if (d.Dk == 128 && block) {
+  // the block form at D = 128 (faster there on both the few-head and the
+  // many-head shapes) unless the token-by-token form is asked for
+  const bool block = d.Dk == 128 && (d.flags & GDN_SCAN_PER_TOKEN) == 0;
+  if (block) {
     bool gated = false;
     int rc = launch_scan_chunked(d, q, k, v, ld, beta, s0, z, w, y, s_out, stream, &gated);
     if (rc != GDN_OK || gated || z == nullptr) return rc;
     const int64_t nvec = heads * d.T;
-    const dim3 grid((unsigned)((nvec + 3) / 4));
+    const dim3 grid = norm_grid(nvec);
     switch (d.dtype) {
       case GDN_F32: gated_norm_kernel<GDN_F32, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
       case GDN_F16: gated_norm_kernel<GDN_F16, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
