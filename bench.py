@@ -10,7 +10,10 @@ state row) divided by its time, in GB/s.
 
 Also measured (object "scan"): the prefill scan B=1 T=4096 (bf16, token-major)
 and the head-major scan B=16 T=1024 (f16), in tokens/s and algorithmic
-TFLOP/s (7 * D * D flops per head-token) against the FP32 vector peak.
+TFLOP/s (7 * D * D flops per head-token) against the FP32 peak (157.3 TFLOP/s,
+the same for the vector units and for dense FP32 matrix products): the block
+form (the default at D = 128) runs on the matrix cores ("bound": "mfma"), the
+token-by-token form on the vector units ("alu").
 
 ``roofline`` is for the decode kernel: algorithmic bytes per launch over its
 average launch time (HIP events on the launch stream over the timed region),
@@ -36,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN decode state GB/s + scan tokens/s, % of MI355X HBM/FP32 roofline"
 HBM_PEAK_GBS = 8000.0
-FP32_VALU_PEAK_TFLOPS = 157.3
+FP32_PEAK_TFLOPS = 157.3  # FP32 vector and dense FP32 matrix peak alike
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_b64_counters.txt")
 # sources the decode kernel is built from: its counters are stale once these change
 DECODE_SRC = [os.path.join(ROOT, "linear_attention_recurrence_recurrent_amd", "csrc", f)
@@ -242,12 +245,16 @@ def bench_scan(idx, args, torch):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     flops = 7.0 * wl.B * wl.T * wl.Hv * wl.Dv * wl.Dk
+    form = args.scan_form
+    if form == "auto":
+        form = "block" if wl.Dk == 128 else "per_token"
+    bound = "mfma" if form == "block" else "alu"
     tflops = flops / (ms * 1e-3) / 1e12
     tok = wl.B * wl.T / (ms * 1e-3)
     log("scan %d: %.1f us per call, %.2f M tok/s, %.1f TFLOP/s" % (idx, ms * 1e3, tok / 1e6, tflops))
     return {"workload": wl.name, "us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(tok, 1),
-            "tflops": round(tflops, 2), "peak_tflops": FP32_VALU_PEAK_TFLOPS,
-            "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4), "bound": "alu",
+            "tflops": round(tflops, 2), "peak_tflops": FP32_PEAK_TFLOPS,
+            "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "bound": bound, "form": form,
             "algorithmic_flops_per_call": flops}
 
 

@@ -174,6 +174,32 @@ def test_small_cases(case, gated):
         run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="block")
 
 
+BLOCK_EDGES = [
+    # (B, T, Hk, Hv, dtype, head_major): shapes that stress the block form
+    (1, 45, 1, 6, "bf16", False),   # six value heads per key head: two prep groups; odd block count
+    (2, 16, 1, 5, "f32", True),     # one full block, five value heads per key head
+    (3, 3, 2, 4, "f16", False),     # three tokens: one block with thirteen padded rows
+    (1, 32, 4, 4, "f32", False),    # even block count, no grouping
+    (2, 47, 16, 128, "bf16", True),  # 256 heads: whole-head workgroups, ragged tail
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_EDGES, ids=lambda c: "B%dT%dHk%dHv%d-%s-%s" % (
+    c[0], c[1], c[2], c[3], c[4], "hm" if c[5] else "tm"))
+@pytest.mark.parametrize("gated", [True, False])
+def test_block_form_edge_shapes(case, gated):
+    """The block form (D = 128) on grouped heads beyond four per key head, a
+    single token, exact and ragged block counts, and both workgroup shapes;
+    the default form at D = 128 is the block form, bit for bit."""
+    B, T, Hk, Hv, dtype, hm = case
+    say("block edges %s gated=%s" % (case, gated))
+    ops = synth.random_operands(B, T, Hk, Hv, 128, 128, dtype=dtype, head_major=hm,
+                                seed=B * 7 + T + Hv)
+    yb, sb = run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="block")
+    yd, sd = run_both(ops, head_major=hm, gated=gated, dtype=dtype)
+    assert torch.equal(yb, yd) and torch.equal(sb, sd)
+
+
 def test_gate_dtype_differs_from_operand_dtype():
     ops = synth.random_operands(2, 21, 2, 4, 64, 64, dtype="bf16", gate_dtype="f32", seed=5)
     run_both(ops, head_major=False, gated=True, dtype="bf16")
