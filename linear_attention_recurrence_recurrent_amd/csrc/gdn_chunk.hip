@@ -20,8 +20,9 @@
 //                norms, decay products, K K^T and Q K^T on the matrix cores,
 //                T = (I + Ls)^-1 by forward substitution and the masked
 //                Hd = tril(Q^ K^^T) (.) Dc, written as a small block record;
-//   state_kernel (one workgroup per head and 16 * NA value rows, sequential
-//                over the blocks): P = K S^T and Q S^T, C = T (diag(beta) V -
+//   state_kernel / rows_kernel (sequential over the blocks; a workgroup per
+//                head when there are many heads, per 16 value rows when there
+//                are few): P = K S^T and Q S^T, C = T (diag(beta) V -
 //                diag(beta gam rk) P), O = diag(gam rq) Q S^T + Hd C and the
 //                rank-16 update of S^T, all as v_mfma_f32_16x16x4f32 on raw
 //                q and k with the norms folded into per-token scales.
@@ -243,37 +244,31 @@ struct StateArgs {
   float norm_eps;
 };
 
-// Workgroup = (value head, NA a-tiles of 16 value rows); NC waves share an
-// a-tile by splitting its 8 key tiles (their partial products are summed
-// through LDS).  NW = NA * NC waves.  The loads of block c + DEPTH are
-// issued while block c is computed.
-template <int DT, int NA, int NC, int DEPTH, bool FUSE>
-__global__ __launch_bounds__(NA* NC* kWave)
-__attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(StateArgs a) {
-  constexpr int NW = NA * NC, NT = NW * kWave, ROWS = 16 * NA, NCT = 8 / NC;
-  static_assert(NT >= 256 && NW <= 8 && NC >= 1 && 8 % NC == 0, "shape");
-  static_assert(!FUSE || ROWS == kD, "the fused norm needs the whole head");
-  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth");
+// The many-head shape: one workgroup per value head, its 8 waves one a-tile
+// (16 value rows) each over all 8 key tiles, two workgroups per CU; the gated
+// norm is fused.  The loads of block c + 1 are issued while block c is
+// computed.
+template <int DT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void state_kernel(
+    StateArgs a) {
+  constexpr int NW = 8, NT = NW * kWave, ROWS = kD, NCT = 8;
   __shared__ __align__(16) float sk[kL][kPad];
   __shared__ __align__(16) float sq[kL][kPad];
   __shared__ float sv[kL][ROWS];
-  __shared__ float sz[FUSE ? 2 : 1][FUSE ? kL : 1][FUSE ? kD : 1];
+  __shared__ float sz[2][kL][kD];
   __shared__ __align__(16) float so[2][kL][ROWS];
   __shared__ __align__(16) float srec[kRecUsed];
-  __shared__ v4f spart[NC > 1 ? NW : 1][2][kWave];
 
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int rb = (int)(tile % a.nrb);
-  const int64_t bh = tile / a.nrb;
+  const int64_t bh = tile;
   const int hv = (int)(bh % a.Hv), hk = hv / a.G;
   const int64_t b = bh / a.Hv;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int lg = lane / 16, lc = lane % 16;
-  const int ai = wave / NC, cp = wave % NC;  // this wave's a-tile and key-tile part
+  const int ai = wave;  // this wave's a-tile (value rows 16 ai ..), all key tiles
   const int64_t T = a.T;
-  const bool has_z = FUSE && a.z != nullptr;
+  const bool has_z = a.z != nullptr;
   const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major);
-  const int row0 = rb * ROWS;
   const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
   const float* rec = a.rec + record_at(bh, 0, a.nblk);
 
@@ -281,7 +276,7 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
   // (fused), the record as float4
   constexpr int NQK = (2 * kL * 16 + NT - 1) / NT;
   constexpr int NVP = (kL * ROWS / 2 + NT - 1) / NT;
-  constexpr int NZP = FUSE ? (kL * kD / 2 + NT - 1) / NT : 1;
+  constexpr int NZP = (kL * kD / 2 + NT - 1) / NT;
   constexpr int NR4 = kRecUsed / 4;
   constexpr int NRC = (NR4 + NT - 1) / NT;
   struct Regs {
@@ -304,15 +299,13 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
 #pragma unroll
     for (int i = 0; i < NVP; ++i) {
       const int e = (tid + i * NT) % (kL * ROWS / 2), tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
-      P.v[i].load(a.v, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + row0 + 2 * r2);
+      P.v[i].load(a.v, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + 2 * r2);
     }
-    if constexpr (FUSE) {
-      if (has_z) {
+    if (has_z) {
 #pragma unroll
-        for (int i = 0; i < NZP; ++i) {
-          const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
-          P.z[i].load(a.z, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + 2 * r2);
-        }
+      for (int i = 0; i < NZP; ++i) {
+        const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
+        P.z[i].load(a.z, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + 2 * r2);
       }
     }
 #pragma unroll
@@ -339,14 +332,12 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
       sv[tt][2 * r2] = P.v[i].get(0);
       sv[tt][2 * r2 + 1] = P.v[i].get(1);
     }
-    if constexpr (FUSE) {
-      if (has_z) {
+    if (has_z) {
 #pragma unroll
-        for (int i = 0; i < NZP; ++i) {
-          const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
-          sz[zbuf][tt][2 * r2] = P.z[i].get(0);
-          sz[zbuf][tt][2 * r2 + 1] = P.z[i].get(1);
-        }
+      for (int i = 0; i < NZP; ++i) {
+        const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
+        sz[zbuf][tt][2 * r2] = P.z[i].get(0);
+        sz[zbuf][tt][2 * r2 + 1] = P.z[i].get(1);
       }
     }
 #pragma unroll
@@ -358,18 +349,16 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
 
   // state S^T, this wave's key tiles of its a-tile, in the accumulator layout
   v4f St[NCT];
-  const int arow = row0 + 16 * ai + lc;  // value row of this lane
+  const int arow = 16 * ai + lc;  // value row of this lane
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
-                                                      16 * (cp * NCT + ct) + 4 * lg);
+                                                      16 * ct + 4 * lg);
     St[ct] = v4f{x.x, x.y, x.z, x.w};
   }
   float wgt[2];
-  if constexpr (FUSE) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wgt[i] = has_z ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
-  }
+  for (int i = 0; i < 2; ++i) wgt[i] = has_z ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
   const int64_t nblk = a.nblk;
   auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
 
@@ -379,56 +368,50 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
   auto outputs = [&](int64_t c) {
     const int64_t t0 = c * kL;
     const int tc = tc_of(c);
-    if constexpr (FUSE) {
-      if (has_z) {
-        constexpr int TPW = (kL + NW - 1) / NW;
+    if (has_z) {  // the gated norm: two tokens per wave, 128 values each
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const int tt = wave + NW * u;
-          if (tt < kL) {  // uniform per wave
-            const int zb = (int)(c & 1);
-            float x0 = so[c & 1][tt][lane] * silu(sz[zb][tt][lane]);
-            float x1 = so[c & 1][tt][lane + kWave] * silu(sz[zb][tt][lane + kWave]);
-            const float inv = rsqrtf(wave_sum(fmaf(x0, x0, x1 * x1)) * (1.0f / kD) + a.norm_eps);
-            if (tt < tc) {
-              const int64_t vo = bs.v + (t0 + tt) * bs.v_ts;
-              a.y[vo + lane] = x0 * inv * wgt[0];
-              a.y[vo + lane + kWave] = x1 * inv * wgt[1];
-            }
-          }
+      for (int u = 0; u < kL / NW; ++u) {
+        const int tt = wave + NW * u, zb = (int)(c & 1);
+        float x0 = so[c & 1][tt][lane] * silu(sz[zb][tt][lane]);
+        float x1 = so[c & 1][tt][lane + kWave] * silu(sz[zb][tt][lane + kWave]);
+        const float inv = rsqrtf(wave_sum(fmaf(x0, x0, x1 * x1)) * (1.0f / kD) + a.norm_eps);
+        if (tt < tc) {
+          const int64_t vo = bs.v + (t0 + tt) * bs.v_ts;
+          a.y[vo + lane] = x0 * inv * wgt[0];
+          a.y[vo + lane + kWave] = x1 * inv * wgt[1];
         }
-        return;
       }
+      return;
     }
     constexpr int R4 = ROWS / 4, NO = (kL * R4 + NT - 1) / NT;
 #pragma unroll
     for (int u = 0; u < NO; ++u) {
       const int e = tid + u * NT, tt = e / R4, r4 = e % R4;
       if (e < kL * R4 && tt < tc)
-        *reinterpret_cast<float4*>(a.y + bs.v + (t0 + tt) * bs.v_ts + row0 + 4 * r4) =
+        *reinterpret_cast<float4*>(a.y + bs.v + (t0 + tt) * bs.v_ts + 4 * r4) =
             *reinterpret_cast<const float4*>(&so[c & 1][tt][4 * r4]);
     }
   };
 
-  // One block: LDS holds block c, the loads of block c + DEPTH go into Pl
-  // (issued first), Ps holds block c + 1 in flight (Ps == Pl when DEPTH == 1).
+  // One block: LDS holds block c; the loads of block c + 1 go into P (issued
+  // first) and reach LDS after the block's last LDS read.
   // Loads and LDS writes run unconditionally (past the end they repeat the
   // last block), so every path through the loop leaves the same loads in
   // flight and the waits before the LDS writes only cover the older block.
-  auto step = [&](int64_t c, Regs& Pl, const Regs& Ps) {
+  auto step = [&](int64_t c, Regs& P) {
     const int64_t t0 = c * kL;
     const int tc = tc_of(c);
-    const int64_t cl = c + DEPTH < nblk ? c + DEPTH : nblk - 1;
+    const int64_t cl = c + 1 < nblk ? c + 1 : nblk - 1;
     __syncthreads();
     if (c > 0) outputs(c - 1);
-    chunk_load(Pl, cl, tc_of(cl));
+    chunk_load(P, cl, tc_of(cl));
 
     // K S^T then Q S^T over this wave's key tiles (raw k and q); K S^T first:
     // only it is on the chain to the next block
     v4f pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * (cp * NCT + ct) + 4 * lg]);
+      const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * ct + 4 * lg]);
       pk = mfma4(kf.x, St[ct][0], pk);
       pk = mfma4(kf.y, St[ct][1], pk);
       pk = mfma4(kf.z, St[ct][2], pk);
@@ -436,23 +419,11 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * (cp * NCT + ct) + 4 * lg]);
+      const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * ct + 4 * lg]);
       pq = mfma4(qf.x, St[ct][0], pq);
       pq = mfma4(qf.y, St[ct][1], pq);
       pq = mfma4(qf.z, St[ct][2], pq);
       pq = mfma4(qf.w, St[ct][3], pq);
-    }
-    if constexpr (NC > 1) {
-      spart[wave][0][lane] = pk;
-      spart[wave][1][lane] = pq;
-      __syncthreads();
-      pk = spart[ai * NC][0][lane];
-      pq = spart[ai * NC][1][lane];
-#pragma unroll
-      for (int p = 1; p < NC; ++p) {
-        pk += spart[ai * NC + p][0][lane];
-        pq += spart[ai * NC + p][1][lane];
-      }
     }
     // C = T (diag(beta) V - diag(beta gam rk) K S^T)  (rows: tokens, columns:
     // this a-tile's value rows)
@@ -476,21 +447,21 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
     for (int s2 = 0; s2 < 4; ++s2) rsl[s2] = srec[kRecSrs + 4 * lg + s2];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int kc = 16 * (cp * NCT + ct) + lc;
+      const int kc = 16 * ct + lc;
       v4f acc = St[ct] * gl;
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(sk[4 * lg + s2][kc] * rsl[s2], cc[s2], acc);
       St[ct] = acc;
     }
     // O = diag(gam rq) Q S^T + Hd C
-    if (cp == 0) {
-      v4f o = {0.f, 0.f, 0.f, 0.f};
+    {
       const float4 hf = *reinterpret_cast<const float4*>(&srec[kRecH + 16 * lc + 4 * lg]);
+      const float4 sg = *reinterpret_cast<const float4*>(&srec[kRecSig + 4 * lg]);
+      v4f o = {0.f, 0.f, 0.f, 0.f};
       o = mfma4(hf.x, cc[0], o);
       o = mfma4(hf.y, cc[1], o);
       o = mfma4(hf.z, cc[2], o);
       o = mfma4(hf.w, cc[3], o);
-      const float4 sg = *reinterpret_cast<const float4*>(&srec[kRecSig + 4 * lg]);
       so[c & 1][4 * lg + 0][16 * ai + lc] = fmaf(sg.x, pq[0], o[0]);
       so[c & 1][4 * lg + 1][16 * ai + lc] = fmaf(sg.y, pq[1], o[1]);
       so[c & 1][4 * lg + 2][16 * ai + lc] = fmaf(sg.z, pq[2], o[2]);
@@ -501,31 +472,234 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
     // next block into LDS (every block array was last read above); z and o
     // are double-buffered: the outputs of this block are written at the
     // start of the next one
-    chunk_store(Ps, (int)((c + 1) & 1));
+    chunk_store(P, (int)((c + 1) & 1));
 
   };
 
-  if constexpr (DEPTH == 1) {
-    Regs P;
-    chunk_load(P, 0, tc_of(0));
-    chunk_store(P, 0);
-    for (int64_t c = 0; c < nblk; ++c) step(c, P, P);
-  } else {
-    Regs P0, P1;
-    const int64_t c1 = nblk > 1 ? 1 : 0;
-    chunk_load(P0, 0, tc_of(0));
-    chunk_load(P1, c1, tc_of(c1));
-    chunk_store(P0, 0);
-    // nothing in flight on entry: the loop's own loads are then the only
-    // ones its waits have to count
-    __builtin_amdgcn_s_waitcnt(0xF70);
-    for (int64_t c = 0;; c += 2) {
-      step(c, P0, P1);
-      if (c + 1 >= nblk) break;
-      step(c + 1, P1, P0);
-      if (c + 2 >= nblk) break;
-    }
+  Regs P;
+  chunk_load(P, 0, tc_of(0));
+  chunk_store(P, 0);
+  for (int64_t c = 0; c < nblk; ++c) step(c, P);
+  __syncthreads();
+  outputs(nblk - 1);
+
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
+    *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * ct +
+                               4 * lg) = x;
   }
+}
+
+// The few-head shape (the prefill): one workgroup per head and 16 value rows,
+// its four waves (one per SIMD) splitting the 8 key tiles.  The chain from one
+// block to the next is K S^T -> sum of the four parts -> C -> update; around
+// it, per block:
+//   - the block's data sits in one of two LDS buffers, written during the
+//     previous block, so one barrier per block publishes it (plus the one for
+//     the K S^T parts): two barriers per block;
+//   - the loads run two blocks ahead (two register sets, a loop over block
+//     pairs with no exit inside), from per-lane offsets set up once;
+//   - every other LDS operand of the block is read while K S^T runs;
+//   - Q S^T follows K S^T on the matrix cores, and O of block c (which needs
+//     the Q S^T parts of all four waves) is formed by the first wave during
+//     block c + 1, its outputs stored during block c + 2.
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void rows_kernel(
+    StateArgs a) {
+  constexpr int NC = 4, NT = NC * kWave, NCT = 8 / NC, ROWS = 16;
+  __shared__ __align__(16) float sk[2][kL][kPad];
+  __shared__ __align__(16) float sq[2][kL][kPad];
+  __shared__ __align__(16) float sv[2][kL][ROWS];
+  __shared__ __align__(16) float srec[2][kRecUsed];
+  __shared__ __align__(16) float so[2][kL][ROWS];
+  __shared__ v4f spart[NC][3][kWave];  // [wave][K S^T | Q S^T of even | odd blocks][lane]
+
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int rb = (int)(tile % a.nrb);
+  const int64_t bh = tile / a.nrb;
+  const int hv = (int)(bh % a.Hv), hk = hv / a.G;
+  const int64_t b = bh / a.Hv;
+  const int tid = threadIdx.x, lane = tid % kWave, cp = tid / kWave;
+  const int lg = lane / 16, lc = lane % 16;
+  const int64_t T = a.T, nblk = a.nblk;
+  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major);
+  const int row0 = rb * ROWS;
+  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
+  const float* rec = a.rec + record_at(bh, 0, nblk);
+  auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
+
+  // one block in registers: 512 items of 8 q or k elements, 128 v pairs, the
+  // record as float4; every lane loads (indices clamped) and writes every item
+  constexpr int NR4 = kRecUsed / 4;
+  struct Regs {
+    Raw<DT, 8> qk[2];
+    Raw<DT, 2> v;
+    Raw<GDN_F32, 4> r;
+  };
+  // element offsets of this lane's loads for block 0 and for the last block
+  // (rows past the last token clamped); a full block advances them by 16 rows
+  const int qtt = tid / 16, qc8 = tid % 16;
+  const int ve = tid % (kL * ROWS / 2), vtt = ve / (ROWS / 2), vr2 = ve % (ROWS / 2);
+  const int tcl = tc_of(nblk - 1);
+  const int64_t qk_blk = kL * bs.qk_ts, v_blk = kL * bs.v_ts;
+  const int64_t qk_off = bs.qk + qtt * bs.qk_ts + 8 * qc8;
+  const int64_t v_off = bs.v + vtt * bs.v_ts + row0 + 2 * vr2;
+  const int64_t qk_last = bs.qk + (nblk - 1) * qk_blk + (qtt < tcl ? qtt : tcl - 1) * bs.qk_ts + 8 * qc8;
+  const int64_t v_last = bs.v + (nblk - 1) * v_blk + (vtt < tcl ? vtt : tcl - 1) * bs.v_ts + row0 + 2 * vr2;
+  const int rec_e = 4 * (tid < NR4 ? tid : NR4 - 1);
+  auto chunk_load = [&](Regs& P, int64_t c) {
+    const bool last = c == nblk - 1;
+    const int64_t oq = last ? qk_last : qk_off + c * qk_blk;
+    P.qk[0].load(a.k, oq);
+    P.qk[1].load(a.q, oq);
+    P.v.load(a.v, last ? v_last : v_off + c * v_blk);
+    P.r.load(rec, c * kRec + rec_e);
+  };
+  auto chunk_store = [&](const Regs& P, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tt = tid / 16, c8 = tid % 16;
+      float* dst = i ? &sq[buf][tt][8 * c8] : &sk[buf][tt][8 * c8];
+      *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
+      *reinterpret_cast<float4*>(dst + 4) = P.qk[i].get4(1);
+    }
+    const int e = tid % (kL * ROWS / 2), tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
+    sv[buf][tt][2 * r2] = P.v.get(0);
+    sv[buf][tt][2 * r2 + 1] = P.v.get(1);
+    *reinterpret_cast<float4*>(&srec[buf][4 * (tid < NR4 ? tid : NR4 - 1)]) = P.r.get4(0);
+  };
+
+  // state S^T: this wave's two key tiles of the 16 rows, accumulator layout
+  v4f St[NCT];
+  const int arow = row0 + lc;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
+                                                      16 * (cp * NCT + ct) + 4 * lg);
+    St[ct] = v4f{x.x, x.y, x.z, x.w};
+  }
+
+  // O of block cb from its C, Hd row and scales (first wave): O = diag(gam rq)
+  // Q S^T + Hd C, the Q S^T parts summed here
+  auto out_o = [&](int64_t cb, const float4& hf, const float4& sg, const v4f& ccb) {
+    const int slot = 1 + (int)(cb & 1);
+    const v4f p0 = spart[0][slot][lane], p1 = spart[1][slot][lane];
+    const v4f p2 = spart[2][slot][lane], p3 = spart[3][slot][lane];
+    const v4f pqs = (p0 + p1) + (p2 + p3);
+    v4f o = {0.f, 0.f, 0.f, 0.f};
+    o = mfma4(hf.x, ccb[0], o);
+    o = mfma4(hf.y, ccb[1], o);
+    o = mfma4(hf.z, ccb[2], o);
+    o = mfma4(hf.w, ccb[3], o);
+    so[cb & 1][4 * lg + 0][lc] = fmaf(sg.x, pqs[0], o[0]);
+    so[cb & 1][4 * lg + 1][lc] = fmaf(sg.y, pqs[1], o[1]);
+    so[cb & 1][4 * lg + 2][lc] = fmaf(sg.z, pqs[2], o[2]);
+    so[cb & 1][4 * lg + 3][lc] = fmaf(sg.w, pqs[3], o[3]);
+  };
+  auto outputs = [&](int64_t cb) {  // 64 lanes, one float4 of y each
+    const int tt = tid / 4, r4 = tid % 4;
+    if (tid < 4 * kL && tt < tc_of(cb))
+      *reinterpret_cast<float4*>(a.y + bs.v + (cb * kL + tt) * bs.v_ts + row0 + 4 * r4) =
+          *reinterpret_cast<const float4*>(&so[cb & 1][tt][4 * r4]);
+  };
+
+  v4f cc_prev = {0.f, 0.f, 0.f, 0.f};
+  float4 hf_prev = make_float4(0.f, 0.f, 0.f, 0.f), sg_prev = hf_prev;
+
+  // block c: LDS buffer c & 1 holds it; Pl receives block c + 2, Ps holds
+  // block c + 1 (stored into the other buffer at the end)
+  auto step = [&](int64_t c, Regs& Pl, const Regs& Ps) {
+    const int bf = (int)(c & 1);
+    __syncthreads();
+    v4f pk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 kf = *reinterpret_cast<const float4*>(&sk[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
+      pk = mfma4(kf.x, St[ct][0], pk);
+      pk = mfma4(kf.y, St[ct][1], pk);
+      pk = mfma4(kf.z, St[ct][2], pk);
+      pk = mfma4(kf.w, St[ct][3], pk);
+    }
+    // while K S^T runs: the stores of block c - 2, the loads of block c + 2
+    if (c >= 2) outputs(c - 2);
+    chunk_load(Pl, c + 2 < nblk ? c + 2 : nblk - 1);
+    // the block's other operands, read while K S^T runs
+    float bei[4], wsci[4], vi[4], ka[NCT][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bei[r] = srec[bf][kRecBe + 4 * lg + r];
+      wsci[r] = srec[bf][kRecWsc + 4 * lg + r];
+      vi[r] = sv[bf][4 * lg + r][lc];
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        ka[ct][s2] = sk[bf][4 * lg + s2][16 * (cp * NCT + ct) + lc] * srec[bf][kRecSrs + 4 * lg + s2];
+    const float4 tf = *reinterpret_cast<const float4*>(&srec[bf][kRecT + 16 * lc + 4 * lg]);
+    const float4 hf = *reinterpret_cast<const float4*>(&srec[bf][kRecH + 16 * lc + 4 * lg]);
+    const float4 sg = *reinterpret_cast<const float4*>(&srec[bf][kRecSig + 4 * lg]);
+    const float gl = srec[bf][kRecGl];
+    spart[cp][0][lane] = pk;
+
+    v4f pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 qf = *reinterpret_cast<const float4*>(&sq[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
+      pq = mfma4(qf.x, St[ct][0], pq);
+      pq = mfma4(qf.y, St[ct][1], pq);
+      pq = mfma4(qf.z, St[ct][2], pq);
+      pq = mfma4(qf.w, St[ct][3], pq);
+    }
+    if (cp == 0 && c > 0) out_o(c - 1, hf_prev, sg_prev, cc_prev);
+    __syncthreads();
+
+    {  // K S^T summed over the four key-tile parts
+      const v4f k0 = spart[0][0][lane], k1 = spart[1][0][lane];
+      const v4f k2 = spart[2][0][lane], k3 = spart[3][0][lane];
+      pk = (k0 + k1) + (k2 + k3);
+    }
+    // C = T (diag(beta) V - diag(beta gam rk) K S^T)
+    v4f yv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yv[r] = bei[r] * vi[r] - wsci[r] * pk[r];
+    v4f cc = {0.f, 0.f, 0.f, 0.f};
+    cc = mfma4(tf.x, yv[0], cc);
+    cc = mfma4(tf.y, yv[1], cc);
+    cc = mfma4(tf.z, yv[2], cc);
+    cc = mfma4(tf.w, yv[3], cc);
+    // S^T = gam_15 S^T + (diag(rk Dc[15][.]) K)^T C
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      v4f acc = St[ct] * gl;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(ka[ct][s2], cc[s2], acc);
+      St[ct] = acc;
+    }
+    spart[cp][1 + bf][lane] = pq;
+    cc_prev = cc;
+    hf_prev = hf;
+    sg_prev = sg;
+    chunk_store(Ps, bf ^ 1);
+  };
+
+  Regs P0, P1;
+  chunk_load(P0, 0);
+  chunk_load(P1, nblk > 1 ? 1 : 0);
+  chunk_store(P0, 0);
+  // nothing in flight on entry, and no exit inside the loop body: the loop's
+  // own loads are then the only ones its waits have to count
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  const int64_t npair = nblk / 2;
+  for (int64_t p = 0; p < npair; ++p) {
+    step(2 * p, P0, P1);
+    step(2 * p + 1, P1, P0);
+  }
+  if (nblk & 1) step(nblk - 1, P0, P1);
+  __syncthreads();
+  if (nblk >= 2) outputs(nblk - 2);
+  if (cp == 0) out_o(nblk - 1, hf_prev, sg_prev, cc_prev);
   __syncthreads();
   outputs(nblk - 1);
 
@@ -535,19 +709,6 @@ __attribute__((amdgpu_waves_per_eu(NA * NC >= 8 ? 4 : 1))) void state_kernel(Sta
     *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * (cp * NCT + ct) +
                                4 * lg) = x;
   }
-}
-
-template <int DT, int NA, int NC, int DEPTH>
-int launch_state(StateArgs a, int64_t heads, hipStream_t st) {
-  constexpr int ROWS = 16 * NA;
-  a.nrb = kD / ROWS;
-  const dim3 grid((unsigned)(heads * a.nrb));
-  if constexpr (ROWS == kD) {
-    state_kernel<DT, NA, NC, DEPTH, true><<<grid, NA * NC * kWave, 0, st>>>(a);
-  } else {
-    state_kernel<DT, NA, NC, DEPTH, false><<<grid, NA * NC * kWave, 0, st>>>(a);
-  }
-  return device_status("state_kernel launch");
 }
 
 template <int DT>
@@ -567,10 +728,16 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
   const int rc = launch_prep<DT>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;
   // many heads: whole-head workgroups, two per CU, the norm fused; few heads:
-  // a workgroup per 16 value rows, its four waves splitting the key tiles,
-  // loads two blocks ahead (the chain per block is short)
-  if (heads >= 256) return launch_state<DT, 8, 1, 1>(s, heads, st);
-  return launch_state<DT, 1, 4, 2>(s, heads, st);
+  // a workgroup per 16 value rows (rows_kernel)
+  StateArgs r = s;
+  if (heads >= 256) {
+    r.nrb = 1;
+    state_kernel<DT><<<dim3((unsigned)heads), 512, 0, st>>>(r);
+    return device_status("state_kernel launch");
+  }
+  r.nrb = kD / 16;
+  rows_kernel<DT><<<dim3((unsigned)(heads * r.nrb)), 256, 0, st>>>(r);
+  return device_status("rows_kernel launch");
 }
 
 int64_t block_record_bytes(int64_t heads, int64_t T) {
