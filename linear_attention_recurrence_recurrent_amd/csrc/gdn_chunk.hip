@@ -711,6 +711,229 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void r
   }
 }
 
+// The few-head shape with two waves per SIMD in different roles.  Waves 0-3
+// ("chain" waves, one per SIMD) hold the state, two key tiles each, and run
+// only the products with it: K S^T, its sum over the four waves, C, the
+// update, and Q S^T.  Waves 4-7 ("helper" waves, one per SIMD) move the data:
+// they load the blocks two ahead, write them to LDS, form O of the previous
+// block (from the C the first chain wave leaves in LDS, one product per
+// helper) and store y.  On every SIMD the helper's vector and memory work then
+// overlaps the chain wave's matrix-core work.  Two barriers per block, taken
+// by all waves.
+template <int DT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void rows_ws_kernel(
+    StateArgs a) {
+  constexpr int NC = 4, NCT = 8 / NC, ROWS = 16, HT = NC * kWave;
+  __shared__ __align__(16) float sk[2][kL][kPad];
+  __shared__ __align__(16) float sq[2][kL][kPad];
+  __shared__ __align__(16) float sv[2][kL][ROWS];
+  __shared__ __align__(16) float srec[2][kRecUsed];
+  __shared__ __align__(16) float scc[2][kL][ROWS];  // C of a block, for its O
+  __shared__ v4f sop[2][NC][kWave];  // O of a block: one part per helper
+  __shared__ v4f spart[NC][3][kWave];  // [chain wave][K S^T | Q S^T of even | odd blocks][lane]
+
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int rb = (int)(tile % a.nrb);
+  const int64_t bh = tile / a.nrb;
+  const int hv = (int)(bh % a.Hv), hk = hv / a.G;
+  const int64_t b = bh / a.Hv;
+  // the wave index through readfirstlane: the compiler then treats the role
+  // branches as uniform (no exec-mask merge of the two roles' registers)
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool chain = wave < NC;
+  const int cp = wave % NC;      // chain: key-tile part; helper: helper index
+  const int ht = tid - HT;       // helper thread index (helpers only)
+  const int lg = lane / 16, lc = lane % 16;
+  const int64_t T = a.T, nblk = a.nblk;
+  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major);
+  const int row0 = rb * ROWS;
+  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
+  const float* rec = a.rec + record_at(bh, 0, nblk);
+  auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
+
+  // ---- helpers: one block in registers (2 q/k items, a v pair, a record
+  // float4 per helper lane; indices clamped, every lane loads and writes)
+  constexpr int NR4 = kRecUsed / 4;
+  struct Regs {
+    Raw<DT, 8> qk[2];
+    Raw<DT, 2> v;
+    Raw<GDN_F32, 4> r;
+  };
+  const int qtt = (ht & (HT - 1)) / 16, qc8 = ht % 16;
+  const int ve = (ht & (HT - 1)) % (kL * ROWS / 2), vtt = ve / (ROWS / 2), vr2 = ve % (ROWS / 2);
+  const int tcl = tc_of(nblk - 1);
+  const int64_t qk_blk = kL * bs.qk_ts, v_blk = kL * bs.v_ts;
+  const int64_t qk_off = bs.qk + qtt * bs.qk_ts + 8 * qc8;
+  const int64_t v_off = bs.v + vtt * bs.v_ts + row0 + 2 * vr2;
+  const int64_t qk_last = bs.qk + (nblk - 1) * qk_blk + (qtt < tcl ? qtt : tcl - 1) * bs.qk_ts + 8 * qc8;
+  const int64_t v_last = bs.v + (nblk - 1) * v_blk + (vtt < tcl ? vtt : tcl - 1) * bs.v_ts + row0 + 2 * vr2;
+  const int rec_e = 4 * ((ht & (HT - 1)) < NR4 ? (ht & (HT - 1)) : NR4 - 1);
+  auto chunk_load = [&](Regs& P, int64_t c) {
+    const bool last = c == nblk - 1;
+    const int64_t oq = last ? qk_last : qk_off + c * qk_blk;
+    P.qk[0].load(a.k, oq);
+    P.qk[1].load(a.q, oq);
+    P.v.load(a.v, last ? v_last : v_off + c * v_blk);
+    P.r.load(rec, c * kRec + rec_e);
+  };
+  auto chunk_store = [&](const Regs& P, int buf) {
+    *reinterpret_cast<float4*>(&sk[buf][qtt][8 * qc8]) = P.qk[0].get4(0);
+    *reinterpret_cast<float4*>(&sk[buf][qtt][8 * qc8 + 4]) = P.qk[0].get4(1);
+    *reinterpret_cast<float4*>(&sq[buf][qtt][8 * qc8]) = P.qk[1].get4(0);
+    *reinterpret_cast<float4*>(&sq[buf][qtt][8 * qc8 + 4]) = P.qk[1].get4(1);
+    sv[buf][vtt][2 * vr2] = P.v.get(0);
+    sv[buf][vtt][2 * vr2 + 1] = P.v.get(1);
+    *reinterpret_cast<float4*>(&srec[buf][rec_e]) = P.r.get4(0);
+  };
+  // O of block cb = Hd C + diag(gam rq) Q S^T.  Before the block's second
+  // barrier each helper h forms the part of Hd C over the tokens 4 i + h (one
+  // product on its SIMD); after it, helper lane (t, j) sums the four parts and
+  // the four Q S^T parts and stores y[t][j] (16 lanes write a token's values).
+  const int ot = (ht & (HT - 1)) / 16, oj = ht % 16;
+  const int pl = 4 * ((ot / 4) * 16 + oj) + ot % 4;  // element (ot, oj) of a part
+  auto o_part = [&](int64_t cb) {  // before the barrier; returns gam_t rq_t of (ot, oj)
+    const int ob = (int)(cb & 1);
+    const float hd = srec[ob][kRecH + 16 * lc + 4 * lg + cp];
+    const v4f o = mfma4(hd, scc[ob][4 * lg + cp][lc], v4f{0.f, 0.f, 0.f, 0.f});
+    sop[ob][cp][lane] = o;
+    return srec[ob][kRecSig + ot];
+  };
+  auto out_y = [&](int64_t cb, float sig) {  // after the barrier
+    const int ob = (int)(cb & 1), sl = 1 + ob;
+    float pqs = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NC; ++w) {
+      pqs += reinterpret_cast<const float*>(&spart[w][sl][0])[pl];
+      o += reinterpret_cast<const float*>(&sop[ob][w][0])[pl];
+    }
+    if (ot < tc_of(cb)) a.y[bs.v + (cb * kL + ot) * bs.v_ts + row0 + oj] = fmaf(sig, pqs, o);
+  };
+
+  // ---- chain waves: the state, two key tiles of the 16 rows, accumulator layout
+  v4f St[NCT];
+  const int arow = row0 + lc;
+  if (chain) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
+                                                        16 * (cp * NCT + ct) + 4 * lg);
+      St[ct] = v4f{x.x, x.y, x.z, x.w};
+    }
+  }
+
+  // Each role runs its own loop; both take the same two barriers per block in
+  // the same order, so the workgroup stays in step while each role's
+  // registers (the state, the staged blocks) stay out of the other's code.
+  const int64_t npair = nblk / 2;
+  if (chain) {
+    // block c: LDS buffer c & 1 holds it
+    auto step = [&](int64_t c) {
+      const int bf = (int)(c & 1);
+      __syncthreads();
+      v4f pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float4 kf = *reinterpret_cast<const float4*>(&sk[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
+        pk = mfma4(kf.x, St[ct][0], pk);
+        pk = mfma4(kf.y, St[ct][1], pk);
+        pk = mfma4(kf.z, St[ct][2], pk);
+        pk = mfma4(kf.w, St[ct][3], pk);
+      }
+      float bei[4], wsci[4], vi[4], ka[NCT][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bei[r] = srec[bf][kRecBe + 4 * lg + r];
+        wsci[r] = srec[bf][kRecWsc + 4 * lg + r];
+        vi[r] = sv[bf][4 * lg + r][lc];
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          ka[ct][s2] = sk[bf][4 * lg + s2][16 * (cp * NCT + ct) + lc] * srec[bf][kRecSrs + 4 * lg + s2];
+      const float4 tf = *reinterpret_cast<const float4*>(&srec[bf][kRecT + 16 * lc + 4 * lg]);
+      const float gl = srec[bf][kRecGl];
+      spart[cp][0][lane] = pk;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float4 qf = *reinterpret_cast<const float4*>(&sq[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
+        pq = mfma4(qf.x, St[ct][0], pq);
+        pq = mfma4(qf.y, St[ct][1], pq);
+        pq = mfma4(qf.z, St[ct][2], pq);
+        pq = mfma4(qf.w, St[ct][3], pq);
+      }
+      __syncthreads();
+      const v4f k0 = spart[0][0][lane], k1 = spart[1][0][lane];
+      const v4f k2 = spart[2][0][lane], k3 = spart[3][0][lane];
+      pk = (k0 + k1) + (k2 + k3);
+      v4f yv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yv[r] = bei[r] * vi[r] - wsci[r] * pk[r];
+      v4f cc = {0.f, 0.f, 0.f, 0.f};
+      cc = mfma4(tf.x, yv[0], cc);
+      cc = mfma4(tf.y, yv[1], cc);
+      cc = mfma4(tf.z, yv[2], cc);
+      cc = mfma4(tf.w, yv[3], cc);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        v4f acc = St[ct] * gl;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(ka[ct][s2], cc[s2], acc);
+        St[ct] = acc;
+      }
+      spart[cp][1 + bf][lane] = pq;
+      if (cp == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scc[bf][4 * lg + r][lc] = cc[r];
+      }
+    };
+    for (int64_t p = 0; p < npair; ++p) {
+      step(2 * p);
+      step(2 * p + 1);
+    }
+    if (nblk & 1) step(nblk - 1);
+    __syncthreads();
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
+      *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * (cp * NCT + ct) +
+                                 4 * lg) = x;
+    }
+  } else {
+    // block c: the loads of block c + 2 go into Pl, O and y of block c - 1
+    // are formed, Ps (block c + 1) reaches the other LDS buffer after the
+    // block's second barrier
+    auto step = [&](int64_t c, Regs& Pl, const Regs& Ps) {
+      const int bf = (int)(c & 1);
+      __syncthreads();
+      chunk_load(Pl, c + 2 < nblk ? c + 2 : nblk - 1);
+      const float sig = c >= 1 ? o_part(c - 1) : 0.f;
+      __syncthreads();
+      if (c >= 1) out_y(c - 1, sig);
+      chunk_store(Ps, bf ^ 1);
+    };
+    Regs P0, P1;
+    chunk_load(P0, 0);
+    chunk_load(P1, nblk > 1 ? 1 : 0);
+    chunk_store(P0, 0);
+    // nothing in flight on entry, and no exit inside the loop body: the
+    // loop's own loads are then the only ones its waits have to count
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    for (int64_t p = 0; p < npair; ++p) {
+      step(2 * p, P0, P1);
+      step(2 * p + 1, P1, P0);
+    }
+    if (nblk & 1) step(nblk - 1, P0, P1);
+    __syncthreads();
+    const float sig = o_part(nblk - 1);
+    __syncthreads();
+    out_y(nblk - 1, sig);
+  }
+}
+
+
 template <int DT>
 int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
   switch (gdt) {
@@ -736,8 +959,8 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
     return device_status("state_kernel launch");
   }
   r.nrb = kD / 16;
-  rows_kernel<DT><<<dim3((unsigned)(heads * r.nrb)), 256, 0, st>>>(r);
-  return device_status("rows_kernel launch");
+  rows_ws_kernel<DT><<<dim3((unsigned)(heads * r.nrb)), 512, 0, st>>>(r);
+  return device_status("rows_ws_kernel launch");
 }
 
 int64_t block_record_bytes(int64_t heads, int64_t T) {
