@@ -20,9 +20,9 @@
 //                norms, decay products, K K^T and Q K^T on the matrix cores,
 //                T = (I + Ls)^-1 by forward substitution and the masked
 //                Hd = tril(Q^ K^^T) (.) Dc, written as a small block record;
-//   state_kernel / rows_kernel (sequential over the blocks; a workgroup per
-//                head when there are many heads, per 16 value rows when there
-//                are few): P = K S^T and Q S^T, C = T (diag(beta) V -
+//   state_kernel / rows_ws_kernel (sequential over the blocks; a workgroup
+//                per head when there are many heads, per 16 value rows when
+//                there are few): P = K S^T and Q S^T, C = T (diag(beta) V -
 //                diag(beta gam rk) P), O = diag(gam rq) Q S^T + Hd C and the
 //                rank-16 update of S^T, all as v_mfma_f32_16x16x4f32 on raw
 //                q and k with the norms folded into per-token scales.
@@ -491,226 +491,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   }
 }
 
-// The few-head shape (the prefill): one workgroup per head and 16 value rows,
-// its four waves (one per SIMD) splitting the 8 key tiles.  The chain from one
-// block to the next is K S^T -> sum of the four parts -> C -> update; around
-// it, per block:
-//   - the block's data sits in one of two LDS buffers, written during the
-//     previous block, so one barrier per block publishes it (plus the one for
-//     the K S^T parts): two barriers per block;
-//   - the loads run two blocks ahead (two register sets, a loop over block
-//     pairs with no exit inside), from per-lane offsets set up once;
-//   - every other LDS operand of the block is read while K S^T runs;
-//   - Q S^T follows K S^T on the matrix cores, and O of block c (which needs
-//     the Q S^T parts of all four waves) is formed by the first wave during
-//     block c + 1, its outputs stored during block c + 2.
-template <int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void rows_kernel(
-    StateArgs a) {
-  constexpr int NC = 4, NT = NC * kWave, NCT = 8 / NC, ROWS = 16;
-  __shared__ __align__(16) float sk[2][kL][kPad];
-  __shared__ __align__(16) float sq[2][kL][kPad];
-  __shared__ __align__(16) float sv[2][kL][ROWS];
-  __shared__ __align__(16) float srec[2][kRecUsed];
-  __shared__ __align__(16) float so[2][kL][ROWS];
-  __shared__ v4f spart[NC][3][kWave];  // [wave][K S^T | Q S^T of even | odd blocks][lane]
-
-  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int rb = (int)(tile % a.nrb);
-  const int64_t bh = tile / a.nrb;
-  const int hv = (int)(bh % a.Hv), hk = hv / a.G;
-  const int64_t b = bh / a.Hv;
-  const int tid = threadIdx.x, lane = tid % kWave, cp = tid / kWave;
-  const int lg = lane / 16, lc = lane % 16;
-  const int64_t T = a.T, nblk = a.nblk;
-  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major);
-  const int row0 = rb * ROWS;
-  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
-  const float* rec = a.rec + record_at(bh, 0, nblk);
-  auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
-
-  // one block in registers: 512 items of 8 q or k elements, 128 v pairs, the
-  // record as float4; every lane loads (indices clamped) and writes every item
-  constexpr int NR4 = kRecUsed / 4;
-  struct Regs {
-    Raw<DT, 8> qk[2];
-    Raw<DT, 2> v;
-    Raw<GDN_F32, 4> r;
-  };
-  // element offsets of this lane's loads for block 0 and for the last block
-  // (rows past the last token clamped); a full block advances them by 16 rows
-  const int qtt = tid / 16, qc8 = tid % 16;
-  const int ve = tid % (kL * ROWS / 2), vtt = ve / (ROWS / 2), vr2 = ve % (ROWS / 2);
-  const int tcl = tc_of(nblk - 1);
-  const int64_t qk_blk = kL * bs.qk_ts, v_blk = kL * bs.v_ts;
-  const int64_t qk_off = bs.qk + qtt * bs.qk_ts + 8 * qc8;
-  const int64_t v_off = bs.v + vtt * bs.v_ts + row0 + 2 * vr2;
-  const int64_t qk_last = bs.qk + (nblk - 1) * qk_blk + (qtt < tcl ? qtt : tcl - 1) * bs.qk_ts + 8 * qc8;
-  const int64_t v_last = bs.v + (nblk - 1) * v_blk + (vtt < tcl ? vtt : tcl - 1) * bs.v_ts + row0 + 2 * vr2;
-  const int rec_e = 4 * (tid < NR4 ? tid : NR4 - 1);
-  auto chunk_load = [&](Regs& P, int64_t c) {
-    const bool last = c == nblk - 1;
-    const int64_t oq = last ? qk_last : qk_off + c * qk_blk;
-    P.qk[0].load(a.k, oq);
-    P.qk[1].load(a.q, oq);
-    P.v.load(a.v, last ? v_last : v_off + c * v_blk);
-    P.r.load(rec, c * kRec + rec_e);
-  };
-  auto chunk_store = [&](const Regs& P, int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tt = tid / 16, c8 = tid % 16;
-      float* dst = i ? &sq[buf][tt][8 * c8] : &sk[buf][tt][8 * c8];
-      *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
-      *reinterpret_cast<float4*>(dst + 4) = P.qk[i].get4(1);
-    }
-    const int e = tid % (kL * ROWS / 2), tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
-    sv[buf][tt][2 * r2] = P.v.get(0);
-    sv[buf][tt][2 * r2 + 1] = P.v.get(1);
-    *reinterpret_cast<float4*>(&srec[buf][4 * (tid < NR4 ? tid : NR4 - 1)]) = P.r.get4(0);
-  };
-
-  // state S^T: this wave's two key tiles of the 16 rows, accumulator layout
-  v4f St[NCT];
-  const int arow = row0 + lc;
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
-                                                      16 * (cp * NCT + ct) + 4 * lg);
-    St[ct] = v4f{x.x, x.y, x.z, x.w};
-  }
-
-  // O of block cb from its C, Hd row and scales (first wave): O = diag(gam rq)
-  // Q S^T + Hd C, the Q S^T parts summed here
-  auto out_o = [&](int64_t cb, const float4& hf, const float4& sg, const v4f& ccb) {
-    const int slot = 1 + (int)(cb & 1);
-    const v4f p0 = spart[0][slot][lane], p1 = spart[1][slot][lane];
-    const v4f p2 = spart[2][slot][lane], p3 = spart[3][slot][lane];
-    const v4f pqs = (p0 + p1) + (p2 + p3);
-    v4f o = {0.f, 0.f, 0.f, 0.f};
-    o = mfma4(hf.x, ccb[0], o);
-    o = mfma4(hf.y, ccb[1], o);
-    o = mfma4(hf.z, ccb[2], o);
-    o = mfma4(hf.w, ccb[3], o);
-    so[cb & 1][4 * lg + 0][lc] = fmaf(sg.x, pqs[0], o[0]);
-    so[cb & 1][4 * lg + 1][lc] = fmaf(sg.y, pqs[1], o[1]);
-    so[cb & 1][4 * lg + 2][lc] = fmaf(sg.z, pqs[2], o[2]);
-    so[cb & 1][4 * lg + 3][lc] = fmaf(sg.w, pqs[3], o[3]);
-  };
-  auto outputs = [&](int64_t cb) {  // 64 lanes, one float4 of y each
-    const int tt = tid / 4, r4 = tid % 4;
-    if (tid < 4 * kL && tt < tc_of(cb))
-      *reinterpret_cast<float4*>(a.y + bs.v + (cb * kL + tt) * bs.v_ts + row0 + 4 * r4) =
-          *reinterpret_cast<const float4*>(&so[cb & 1][tt][4 * r4]);
-  };
-
-  v4f cc_prev = {0.f, 0.f, 0.f, 0.f};
-  float4 hf_prev = make_float4(0.f, 0.f, 0.f, 0.f), sg_prev = hf_prev;
-
-  // block c: LDS buffer c & 1 holds it; Pl receives block c + 2, Ps holds
-  // block c + 1 (stored into the other buffer at the end)
-  auto step = [&](int64_t c, Regs& Pl, const Regs& Ps) {
-    const int bf = (int)(c & 1);
-    __syncthreads();
-    v4f pk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float4 kf = *reinterpret_cast<const float4*>(&sk[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
-      pk = mfma4(kf.x, St[ct][0], pk);
-      pk = mfma4(kf.y, St[ct][1], pk);
-      pk = mfma4(kf.z, St[ct][2], pk);
-      pk = mfma4(kf.w, St[ct][3], pk);
-    }
-    // while K S^T runs: the stores of block c - 2, the loads of block c + 2
-    if (c >= 2) outputs(c - 2);
-    chunk_load(Pl, c + 2 < nblk ? c + 2 : nblk - 1);
-    // the block's other operands, read while K S^T runs
-    float bei[4], wsci[4], vi[4], ka[NCT][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      bei[r] = srec[bf][kRecBe + 4 * lg + r];
-      wsci[r] = srec[bf][kRecWsc + 4 * lg + r];
-      vi[r] = sv[bf][4 * lg + r][lc];
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-        ka[ct][s2] = sk[bf][4 * lg + s2][16 * (cp * NCT + ct) + lc] * srec[bf][kRecSrs + 4 * lg + s2];
-    const float4 tf = *reinterpret_cast<const float4*>(&srec[bf][kRecT + 16 * lc + 4 * lg]);
-    const float4 hf = *reinterpret_cast<const float4*>(&srec[bf][kRecH + 16 * lc + 4 * lg]);
-    const float4 sg = *reinterpret_cast<const float4*>(&srec[bf][kRecSig + 4 * lg]);
-    const float gl = srec[bf][kRecGl];
-    spart[cp][0][lane] = pk;
-
-    v4f pq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float4 qf = *reinterpret_cast<const float4*>(&sq[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
-      pq = mfma4(qf.x, St[ct][0], pq);
-      pq = mfma4(qf.y, St[ct][1], pq);
-      pq = mfma4(qf.z, St[ct][2], pq);
-      pq = mfma4(qf.w, St[ct][3], pq);
-    }
-    if (cp == 0 && c > 0) out_o(c - 1, hf_prev, sg_prev, cc_prev);
-    __syncthreads();
-
-    {  // K S^T summed over the four key-tile parts
-      const v4f k0 = spart[0][0][lane], k1 = spart[1][0][lane];
-      const v4f k2 = spart[2][0][lane], k3 = spart[3][0][lane];
-      pk = (k0 + k1) + (k2 + k3);
-    }
-    // C = T (diag(beta) V - diag(beta gam rk) K S^T)
-    v4f yv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yv[r] = bei[r] * vi[r] - wsci[r] * pk[r];
-    v4f cc = {0.f, 0.f, 0.f, 0.f};
-    cc = mfma4(tf.x, yv[0], cc);
-    cc = mfma4(tf.y, yv[1], cc);
-    cc = mfma4(tf.z, yv[2], cc);
-    cc = mfma4(tf.w, yv[3], cc);
-    // S^T = gam_15 S^T + (diag(rk Dc[15][.]) K)^T C
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      v4f acc = St[ct] * gl;
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(ka[ct][s2], cc[s2], acc);
-      St[ct] = acc;
-    }
-    spart[cp][1 + bf][lane] = pq;
-    cc_prev = cc;
-    hf_prev = hf;
-    sg_prev = sg;
-    chunk_store(Ps, bf ^ 1);
-  };
-
-  Regs P0, P1;
-  chunk_load(P0, 0);
-  chunk_load(P1, nblk > 1 ? 1 : 0);
-  chunk_store(P0, 0);
-  // nothing in flight on entry, and no exit inside the loop body: the loop's
-  // own loads are then the only ones its waits have to count
-  __builtin_amdgcn_s_waitcnt(0xF70);
-  const int64_t npair = nblk / 2;
-  for (int64_t p = 0; p < npair; ++p) {
-    step(2 * p, P0, P1);
-    step(2 * p + 1, P1, P0);
-  }
-  if (nblk & 1) step(nblk - 1, P0, P1);
-  __syncthreads();
-  if (nblk >= 2) outputs(nblk - 2);
-  if (cp == 0) out_o(nblk - 1, hf_prev, sg_prev, cc_prev);
-  __syncthreads();
-  outputs(nblk - 1);
-
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
-    *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * (cp * NCT + ct) +
-                               4 * lg) = x;
-  }
-}
-
 // The few-head shape with two waves per SIMD in different roles.  Waves 0-3
 // ("chain" waves, one per SIMD) hold the state, two key tiles each, and run
 // only the products with it: K S^T, its sum over the four waves, C, the
@@ -951,7 +731,7 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
   const int rc = launch_prep<DT>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;
   // many heads: whole-head workgroups, two per CU, the norm fused; few heads:
-  // a workgroup per 16 value rows (rows_kernel)
+  // a workgroup per 16 value rows (rows_ws_kernel)
   StateArgs r = s;
   if (heads >= 256) {
     r.nrb = 1;
