@@ -177,6 +177,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       al = expf(l1.get(0));
       be = b1.get(0);
     }
+    // decay products of token lc of each 16-lane row's value head: from the
+    // block start through lc, and after lc to the block end
+    const float gam = row_prefix_prod(al), tail = dpp_or_one<0x101, 0xF>(row_suffix_prod(al));
     const int ng = a.G - g0 < 4 ? a.G - g0 : 4;
     for (int gq = 0; gq < ng; ++gq) {  // Ls and Hd of value head g0 + gq, all lanes
       float als[kL];
@@ -184,13 +187,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       for (int m = 0; m < kL; ++m)
         als[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * gq + m));
       float* rec = a.rec + record_at(b * a.Hv + hk * a.G + g0 + gq, c, a.nblk);
+      // Dc[i][j] for j = lc and the rows i = 4 lg .. 4 lg + 3: the product up to
+      // row 4 lg, then one decay per row
+      const int j = lc;
+      float dc = j <= 4 * lg ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 1; m < kL; ++m) dc *= (m > j && m <= 4 * lg) ? als[m] : 1.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 4 * lg + r, j = lc;
+        const int i = 4 * lg + r;
+        if (r > 0) {
+          const float ai = lg == 0 ? als[r] : lg == 1 ? als[4 + r] : lg == 2 ? als[8 + r] : als[12 + r];
+          dc = j < i ? dc * ai : (j == i ? 1.f : 0.f);
+        }
         const float bei = __shfl(be, 16 * gq + i);
-        float dc = j <= i ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 1; m < kL; ++m) dc *= (m > j && m <= i) ? als[m] : 1.f;
         sLs[wave][gq][i][j] = j < i ? bei * rki[r] * G4[r] * rk * dc : 0.f;
         rec[kRecH + 16 * i + j] = j <= i ? rqi[r] * H4[r] * rk * dc : 0.f;
       }
@@ -200,13 +210,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (gv) {  // lane group lg: value head g; lane lc: token lc and column lc
       float* rec = a.rec + record_at(b * a.Hv + hv, c, a.nblk);
-      float gam = 1.f, tail = 1.f;
-#pragma unroll
-      for (int m = 0; m < kL; ++m) {
-        const float am = __shfl(al, 16 * lg + m);
-        gam *= m <= lc ? am : 1.f;
-        tail *= m > lc ? am : 1.f;
-      }
       rec[kRecSig + lc] = gam * rq;
       rec[kRecWsc + lc] = be * gam * rk;
       rec[kRecBe + lc] = be;

@@ -112,6 +112,31 @@ __device__ __forceinline__ float wave_sum(float x) {
           __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
+// One multiplicative DPP step: x from the lane selected by CTRL, or 1 where
+// that lane lies outside the row or the row is masked off by ROW_MASK.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_one(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+
+// Inclusive prefix and suffix products inside each row of 16 lanes
+// (Hillis-Steele with row_shr / row_shl 1, 2, 4, 8; exec must be full).
+__device__ __forceinline__ float row_prefix_prod(float x) {
+  x *= dpp_or_one<0x111, 0xF>(x);
+  x *= dpp_or_one<0x112, 0xF>(x);
+  x *= dpp_or_one<0x114, 0xF>(x);
+  x *= dpp_or_one<0x118, 0xF>(x);
+  return x;
+}
+__device__ __forceinline__ float row_suffix_prod(float x) {
+  x *= dpp_or_one<0x101, 0xF>(x);
+  x *= dpp_or_one<0x102, 0xF>(x);
+  x *= dpp_or_one<0x104, 0xF>(x);
+  x *= dpp_or_one<0x108, 0xF>(x);
+  return x;
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
 // XCD receives a contiguous range of tiles (the row blocks of one head, and
 // the value heads of one key group, then share an L2).

@@ -59,23 +59,12 @@ constexpr float kFoldMin = 9.3132257e-10f, kFoldMax = 1.0737418e9f;
 // NaN or infinite gates fail the test and take the per-token loop.
 constexpr float kFastLogSum = 41.0f;
 
-// One multiplicative DPP step: x from the lane selected by CTRL, or 1 where
-// that lane lies outside the row or the row is masked off by ROW_MASK.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_or_one(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), CTRL,
-                                                    ROW_MASK, 0xF, false));
-}
-
 // Inclusive prefix product over the 64 lanes of a wave (exec must be full):
 // Hillis-Steele inside each row of 16 (row_shr 1, 2, 4, 8), then the row
 // products carried forward (row_bcast 15 into rows 1 and 3, row_bcast 31 into
 // rows 2 and 3).
 __device__ __forceinline__ float wave_prefix_prod(float x) {
-  x *= dpp_or_one<0x111, 0xF>(x);
-  x *= dpp_or_one<0x112, 0xF>(x);
-  x *= dpp_or_one<0x114, 0xF>(x);
-  x *= dpp_or_one<0x118, 0xF>(x);
+  x = row_prefix_prod(x);
   x *= dpp_or_one<0x142, 0xA>(x);
   x *= dpp_or_one<0x143, 0xC>(x);
   return x;
