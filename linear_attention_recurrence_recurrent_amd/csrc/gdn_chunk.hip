@@ -694,8 +694,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       chunk_load(Pl, c + 2 < nblk ? c + 2 : nblk - 1);
       const float sig = c >= 1 ? o_part(c - 1) : 0.f;
       __syncthreads();
-      if (c >= 1) out_y(c - 1, sig);
       chunk_store(Ps, bf ^ 1);
+      // y after the staging: the wait before the staging then never covers a
+      // store issued in the same block
+      if (c >= 1) out_y(c - 1, sig);
     };
     Regs P0, P1;
     chunk_load(P0, 0);
