@@ -402,8 +402,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   // last block), so every path through the loop leaves the same loads in
   // flight and the waits before the LDS writes only cover the older block.
   auto step = [&](int64_t c, Regs& P) {
-    const int64_t t0 = c * kL;
-    const int tc = tc_of(c);
     const int64_t cl = c + 1 < nblk ? c + 1 : nblk - 1;
     __syncthreads();
     if (c > 0) outputs(c - 1);
