@@ -441,17 +441,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
       cc = mfma4(tf.z, yv[2], cc);
       cc = mfma4(tf.w, yv[3], cc);
     }
-    // S^T = gam_15 S^T + (diag(rk Dc[15][.]) K)^T C
+    // S^T = gam_15 S^T + K^T diag(rk Dc[15][.]) C: the key scales on C's rows
+    // (4 products per lane) rather than on K (4 per key tile)
     const float gl = srec[kRecGl];
-    float rsl[4];
+    v4f cs;
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) rsl[s2] = srec[kRecSrs + 4 * lg + s2];
+    for (int s2 = 0; s2 < 4; ++s2) cs[s2] = cc[s2] * srec[kRecSrs + 4 * lg + s2];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int kc = 16 * ct + lc;
       v4f acc = St[ct] * gl;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(sk[4 * lg + s2][kc] * rsl[s2], cc[s2], acc);
+      for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(sk[4 * lg + s2][kc], cs[s2], acc);
       St[ct] = acc;
     }
     // O = diag(gam rq) Q S^T + Hd C
@@ -621,18 +622,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         pk = mfma4(kf.z, St[ct][2], pk);
         pk = mfma4(kf.w, St[ct][3], pk);
       }
-      float bei[4], wsci[4], vi[4], ka[NCT][4];
+      float bei[4], wsci[4], vi[4], srsi[4], ka[NCT][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         bei[r] = srec[bf][kRecBe + 4 * lg + r];
         wsci[r] = srec[bf][kRecWsc + 4 * lg + r];
+        srsi[r] = srec[bf][kRecSrs + 4 * lg + r];
         vi[r] = sv[bf][4 * lg + r][lc];
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2)
-          ka[ct][s2] = sk[bf][4 * lg + s2][16 * (cp * NCT + ct) + lc] * srec[bf][kRecSrs + 4 * lg + s2];
+          ka[ct][s2] = sk[bf][4 * lg + s2][16 * (cp * NCT + ct) + lc];
       const float4 tf = *reinterpret_cast<const float4*>(&srec[bf][kRecT + 16 * lc + 4 * lg]);
       const float gl = srec[bf][kRecGl];
       spart[cp][0][lane] = pk;
@@ -656,11 +658,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       cc = mfma4(tf.y, yv[1], cc);
       cc = mfma4(tf.z, yv[2], cc);
       cc = mfma4(tf.w, yv[3], cc);
+      v4f cs;  // C with the key scales of the update on its rows
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs[r] = cc[r] * srsi[r];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         v4f acc = St[ct] * gl;
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(ka[ct][s2], cc[s2], acc);
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(ka[ct][s2], cs[s2], acc);
         St[ct] = acc;
       }
       spart[cp][1 + bf][lane] = pq;
