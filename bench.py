@@ -50,6 +50,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def settle(fn, torch, min_ms):
+    """Untimed: call fn until min_ms of wall time has passed.  The GPU's clocks
+    ramp up over the first ~100 ms of sustained load (the first kernel timed
+    in a fresh process runs up to ~20% slow), so every measurement below
+    starts from the sustained clock state a long-running job sees."""
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in DECODE_SRC:
@@ -117,7 +133,7 @@ def bench_decode(args, torch):
 
     for _ in range(args.warmup):
         chain()
-    torch.cuda.synchronize()
+    settle(chain, torch, args.settle_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
@@ -161,9 +177,11 @@ def bench_decode(args, torch):
     calls3 = [Launcher("gdn_recurrent_step_three_pass", desc,
                        [st["q"], st["k"], st["v"], st["log_decay"], st["beta"], state, st["z"], w,
                         y, state], stream.cuda_stream) for st, y in zip(d_steps, ys)]
-    for c in calls3:
-        c()
-    torch.cuda.synchronize()
+    def chain3():
+        for c in calls3:
+            c()
+
+    settle(chain3, torch, args.settle_ms / 4)
     reps3 = max(1, args.steps // 4)
     e0.record(stream)
     for _ in range(reps3):
@@ -199,9 +217,7 @@ def bench_decode_single(args, torch):
     call = Launcher("gdn_recurrent_step", desc, [d["q"], d["k"], d["v"], d["log_decay"],
                                                  d["beta"], d["s0"], d["z"], d["w"], y, d["s0"]],
                     stream.cuda_stream)
-    for _ in range(10):
-        call()
-    torch.cuda.synchronize()
+    settle(call, torch, args.settle_ms / 4)
     reps = 200
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -236,7 +252,7 @@ def bench_scan(idx, args, torch):
     reps = max(3, args.steps)
     for _ in range(max(1, args.warmup)):
         call()
-    torch.cuda.synchronize()
+    settle(call, torch, args.settle_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -274,7 +290,7 @@ def bench_gates(args, torch):
               ctypes.c_void_p(stream.cuda_stream))
     for _ in range(3):
         assert L.gdn_gates(*args_c) == 0
-    torch.cuda.synchronize()
+    settle(lambda: L.gdn_gates(*args_c), torch, args.settle_ms / 4)
     reps = 50
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -312,7 +328,7 @@ def bench_conv(args, torch):
                   ctypes.c_void_p(stream.cuda_stream))
         for _ in range(3):
             assert L.gdn_conv_silu(*args_c) == 0
-        torch.cuda.synchronize()
+        settle(lambda: L.gdn_conv_silu(*args_c), torch, args.settle_ms / 4)
         reps = 50
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -389,6 +405,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed calls for this long before each measurement (clock ramp)")
     ap.add_argument("--no-scan", action="store_true", help="skip the scan sub-measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
