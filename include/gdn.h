@@ -89,8 +89,10 @@ typedef enum gdn_status {
  * the token-by-token form otherwise; with both flags, or GDN_SCAN_BLOCK at
  * another head dim, the call is rejected (GDN_EINVAL / GDN_EUNSUPPORTED).
  * The block form's workspace holds one 2560-byte record per value head and
- * 16-token block: B * Hv * ceil(T / 16) * 2560 bytes (GDN_EDEVICE when it
- * cannot be allocated). */
+ * 16-token block, and with fewer than 256 value heads (B * Hv) also 3072
+ * bytes per key head and block: B * Hv * ceil(T / 16) * 2560
+ * (+ B * Hk * ceil(T / 16) * 3072) bytes (GDN_EDEVICE when it cannot be
+ * allocated). */
 #define GDN_SCAN_PER_TOKEN 4u
 #define GDN_SCAN_BLOCK 8u
 

@@ -19,13 +19,15 @@
 //   prep_kernel  (one wave per key head and block, all in parallel): the
 //                norms, decay products, K K^T and Q K^T on the matrix cores,
 //                T = (I + Ls)^-1 by forward substitution and the masked
-//                Hd = tril(Q^ K^^T) (.) Dc, written as a small block record;
-//   state_kernel / rows_ws_kernel (sequential over the blocks; a workgroup
-//                per head when there are many heads, per 16 value rows when
-//                there are few): P = K S^T and Q S^T, C = T (diag(beta) V -
-//                diag(beta gam rk) P), O = diag(gam rq) Q S^T + Hd C and the
-//                rank-16 update of S^T, all as v_mfma_f32_16x16x4f32 on raw
-//                q and k with the norms folded into per-token scales.
+//                Hd = tril(Q^ K^^T) (.) Dc, written as a small block record
+//                (for few heads also K and Q products across blocks);
+//   state_kernel (many heads, a workgroup per head) / rows_la_kernel (few
+//                heads, a workgroup per 16 value rows; the products with S
+//                taken one block ahead, off the sequential chain): P = K S^T
+//                and Q S^T, C = T (diag(beta) V - diag(beta gam rk) P),
+//                O = diag(gam rq) Q S^T + Hd C and the rank-16 update of S^T,
+//                all as v_mfma_f32_16x16x4f32 on raw q and k with the norms
+//                folded into per-token scales.
 // The sequential chain then holds only the products with S.  S^T stays in the
 // accumulator layout for the whole time axis: lane l, register r of a 16 x 16
 // tile holds S^T[4(l/16) + r][l%16] (key row within the tile, value column),
@@ -41,6 +43,8 @@ namespace {
 constexpr int kD = 128;       // head dim handled here
 constexpr int kL = 16;        // tokens per block (the MFMA tile)
 constexpr int kPad = kD + 4;  // LDS row of q or k: rows 16 banks apart for the operand reads
+// from this many value heads on, a workgroup per head fills the chip
+constexpr int64_t kManyHeads = 256;
 
 // Block record, per (value head, block), f32; the records of a head are
 // contiguous, kRec floats apart (256-byte aligned).
@@ -93,6 +97,7 @@ struct PrepArgs {
   int Hk, Hv, G, head_major;
   uint32_t flags;
   float qk_eps, qscale;
+  float* mx;  // null, or [B][Hk][nblk][3][16][16]: K_c K_(c-1)^T, K_c K_(c-2)^T, Q_c K_(c-1)^T (raw)
 };
 
 // One wave per (batch, key head, block): K K^T and Q K^T once, then the
@@ -156,6 +161,41 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       G4 = mfma4(kv, kv, G4);
       H4 = mfma4(qr[u].get(e), kv, H4);
     }
+  if (a.mx != nullptr) {
+    // Products of raw rows across blocks (zero where the earlier block does
+    // not exist), row-major: M1 = K_c K_(c-1)^T, M2 = K_c K_(c-2)^T and
+    // N = Q_c K_(c-1)^T.  The few-head kernel forms K S^T and Q S^T of a
+    // newer state from an older one with them.
+    v4f M1 = {0.f, 0.f, 0.f, 0.f}, M2 = M1, N1 = M1;
+    if (c > 0) {
+      Raw<DT, 8> kp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kp[u].load(a.k, qk_base + (t0 - kL + lc) * qk_ts + 32 * lg + 8 * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          M1 = mfma4(kr[u].get(e), kp[u].get(e), M1);
+          N1 = mfma4(qr[u].get(e), kp[u].get(e), N1);
+        }
+    }
+    if (c > 1) {
+      Raw<DT, 8> kp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kp[u].load(a.k, qk_base + (t0 - 2 * kL + lc) * qk_ts + 32 * lg + 8 * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) M2 = mfma4(kr[u].get(e), kp[u].get(e), M2);
+    }
+    float* mx = a.mx + task * (3 * kL * kL);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mx[16 * (4 * lg + r) + lc] = M1[r];
+      mx[kL * kL + 16 * (4 * lg + r) + lc] = M2[r];
+      mx[2 * kL * kL + 16 * (4 * lg + r) + lc] = N1[r];
+    }
+  }
   float rki[4], rqi[4];  // norms of the lane's rows i = 4 lg + r
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -245,6 +285,7 @@ struct StateArgs {
   int64_t T, nblk;
   int Hk, Hv, G, nrb, head_major;
   float norm_eps;
+  const float* mx;  // the prep's K_c K_(c-1)^T blocks (lookahead kernel only)
 };
 
 // The many-head shape: one workgroup per value head, its 8 waves one a-tile
@@ -493,234 +534,453 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   }
 }
 
-// The few-head shape with two waves per SIMD in different roles.  Waves 0-3
-// ("chain" waves, one per SIMD) hold the state, two key tiles each, and run
-// only the products with it: K S^T, its sum over the four waves, C, the
-// update, and Q S^T.  Waves 4-7 ("helper" waves, one per SIMD) move the data:
-// they load the blocks two ahead, write them to LDS, form O of the previous
-// block (from the C the first chain wave leaves in LDS, one product per
-// helper) and store y.  On every SIMD the helper's vector and memory work then
-// overlaps the chain wave's matrix-core work.  Two barriers per block, taken
-// by all waves.
+// K and Q of a block sit in LDS in the input's format (16-bit inputs as
+// their raw halves: LDS writes, not reads, limit the few-head kernel) and
+// are widened to f32 as they are read.
 template <int DT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void rows_ws_kernel(
+using LdsElem = typename std::conditional<DT == GDN_F32, float, uint16_t>::type;
+template <int DT>
+constexpr int lds_row() {  // padded row, elements: rows 4 banks apart
+  return DT == GDN_F32 ? kPad : kD + 8;
+}
+template <int DT>
+__device__ __forceinline__ float half_lo(uint32_t x) {
+  if constexpr (DT == GDN_BF16) return __uint_as_float(x << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+}
+template <int DT>
+__device__ __forceinline__ float half_hi(uint32_t x) {
+  if constexpr (DT == GDN_BF16) return __uint_as_float(x & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+}
+template <int DT>
+__device__ __forceinline__ float4 lds_get4(const LdsElem<DT>* row, int e) {  // e % 4 == 0
+  if constexpr (DT == GDN_F32) {
+    return *reinterpret_cast<const float4*>(row + e);
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(row + e);
+    return make_float4(half_lo<DT>(u.x), half_hi<DT>(u.x), half_lo<DT>(u.y), half_hi<DT>(u.y));
+  }
+}
+template <int DT>
+__device__ __forceinline__ float lds_get(const LdsElem<DT>* row, int e) {
+  if constexpr (DT == GDN_F32) return row[e];
+  else return half_lo<DT>(row[e]);
+}
+
+// The few-head shape: a workgroup per 16 value rows of a head, the block
+// recurrence taken apart so that each round (one 16-token block) has no
+// chain of products through the state.  With B_(r+1) = K_(r+1) S_(r-1)^T and
+// P_r = Q_r S_(r-1)^T formed from the state before round r's update, and
+// C-scaled_c = diag(rk Dc[15][.]) C_c:
+//   K_(r+1) S_(r+1)^T = gam(r) (gam(r-1) B_(r+1) + M2_(r+1) Cs_(r-1))
+//                       + M1_(r+1) Cs_r,
+//   Q_r S_r^T = gam(r-1) P_r + N_r Cs_(r-1),
+// gam(c) = gam_15 of block c, M1, M2, N the prep's 16 x 16 products of raw
+// rows.  Round r, after one workgroup barrier:
+//   waves 0-3 (state, two key tiles each): their parts of P_r and B_(r+1),
+//     then S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1);
+//   wave 4 (chain): C_r from the B_r parts, Y_r and its own Cs_(r-1), then
+//     M1_(r+1) Cs_r for the next round;
+//   wave 5: O and y of block r - 1;
+//   wave 6: Y_(r+1) = M2_(r+1) Cs_(r-1);  wave 7: Z_r = N_r Cs_(r-1);
+//   waves 6-7: block r + 2 into a four-slot LDS ring, the loads of block
+//     r + 5 (three register sets).
+// Every operand a wave needs from LDS is read at the start of the round
+// before it or right after its own barrier, so each role issues its matrix
+// products back to back; a round is bounded by the 24-32 products per SIMD.
+// A prologue round forms A_0 = K_0 S_0^T; the last round finishes the state
+// and O.  Each role runs its own loop with the same barriers.
+template <int DT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void rows_la_kernel(
     StateArgs a) {
-  constexpr int NC = 4, NCT = 8 / NC, ROWS = 16, HT = NC * kWave;
-  __shared__ __align__(16) float sk[2][kL][kPad];
-  __shared__ __align__(16) float sq[2][kL][kPad];
-  __shared__ __align__(16) float sv[2][kL][ROWS];
-  __shared__ __align__(16) float srec[2][kRecUsed];
-  __shared__ __align__(16) float scc[2][kL][ROWS];  // C of a block, for its O
-  __shared__ v4f sop[2][NC][kWave];  // O of a block: one part per helper
-  __shared__ v4f spart[NC][3][kWave];  // [chain wave][K S^T | Q S^T of even | odd blocks][lane]
+  constexpr int NC = 4, NCT = 8 / NC, ROWS = 16, KP = lds_row<DT>(), NM = 3 * kL * kL;
+  typedef LdsElem<DT> KT;
+  __shared__ __align__(16) KT sk[4][kL][KP];
+  __shared__ __align__(16) KT sq[4][kL][KP];
+  __shared__ __align__(16) float sv[4][kL][ROWS];
+  __shared__ __align__(16) float srec[4][kRecUsed];
+  __shared__ __align__(16) float smx[4][NM];  // M1, M2, N of a block
+  __shared__ v4f sb[2][NC][kWave];  // parts of B (of A_0 in the prologue)
+  __shared__ v4f sp[2][NC][kWave];  // parts of P
+  __shared__ v4f scs[2][kWave];     // C-scaled
+  __shared__ v4f scc[2][kWave];     // C
+  __shared__ v4f sy[2][kWave];      // Y
+  __shared__ v4f sz[2][kWave];      // Z
 
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int rb = (int)(tile % a.nrb);
   const int64_t bh = tile / a.nrb;
   const int hv = (int)(bh % a.Hv), hk = hv / a.G;
   const int64_t b = bh / a.Hv;
-  // the wave index through readfirstlane: the compiler then treats the role
-  // branches as uniform (no exec-mask merge of the two roles' registers)
   const int tid = threadIdx.x, lane = tid % kWave;
+  // the wave index through readfirstlane: the compiler then treats the role
+  // branches as uniform (no exec-mask merge of the roles' registers)
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const bool chain = wave < NC;
-  const int cp = wave % NC;      // chain: key-tile part; helper: helper index
-  const int ht = tid - HT;       // helper thread index (helpers only)
+  const int cp = wave % NC;
   const int lg = lane / 16, lc = lane % 16;
   const int64_t T = a.T, nblk = a.nblk;
   const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major);
   const int row0 = rb * ROWS;
   const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
   const float* rec = a.rec + record_at(bh, 0, nblk);
+  const float* mxh = a.mx + (b * a.Hk + hk) * nblk * NM;
   auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
-
-  // ---- helpers: one block in registers (2 q/k items, a v pair, a record
-  // float4 per helper lane; indices clamped, every lane loads and writes)
-  constexpr int NR4 = kRecUsed / 4;
-  struct Regs {
-    Raw<DT, 8> qk[2];
-    Raw<DT, 2> v;
-    Raw<GDN_F32, 4> r;
-  };
-  const int qtt = (ht & (HT - 1)) / 16, qc8 = ht % 16;
-  const int ve = (ht & (HT - 1)) % (kL * ROWS / 2), vtt = ve / (ROWS / 2), vr2 = ve % (ROWS / 2);
+  auto clampb = [&](int64_t c) { return c < nblk ? c : nblk - 1; };
   const int tcl = tc_of(nblk - 1);
-  const int64_t qk_blk = kL * bs.qk_ts, v_blk = kL * bs.v_ts;
-  const int64_t qk_off = bs.qk + qtt * bs.qk_ts + 8 * qc8;
-  const int64_t v_off = bs.v + vtt * bs.v_ts + row0 + 2 * vr2;
-  const int64_t qk_last = bs.qk + (nblk - 1) * qk_blk + (qtt < tcl ? qtt : tcl - 1) * bs.qk_ts + 8 * qc8;
-  const int64_t v_last = bs.v + (nblk - 1) * v_blk + (vtt < tcl ? vtt : tcl - 1) * bs.v_ts + row0 + 2 * vr2;
-  const int rec_e = 4 * ((ht & (HT - 1)) < NR4 ? (ht & (HT - 1)) : NR4 - 1);
-  auto chunk_load = [&](Regs& P, int64_t c) {
-    const bool last = c == nblk - 1;
-    const int64_t oq = last ? qk_last : qk_off + c * qk_blk;
-    P.qk[0].load(a.k, oq);
-    P.qk[1].load(a.q, oq);
-    P.v.load(a.v, last ? v_last : v_off + c * v_blk);
-    P.r.load(rec, c * kRec + rec_e);
-  };
-  auto chunk_store = [&](const Regs& P, int buf) {
-    *reinterpret_cast<float4*>(&sk[buf][qtt][8 * qc8]) = P.qk[0].get4(0);
-    *reinterpret_cast<float4*>(&sk[buf][qtt][8 * qc8 + 4]) = P.qk[0].get4(1);
-    *reinterpret_cast<float4*>(&sq[buf][qtt][8 * qc8]) = P.qk[1].get4(0);
-    *reinterpret_cast<float4*>(&sq[buf][qtt][8 * qc8 + 4]) = P.qk[1].get4(1);
-    sv[buf][vtt][2 * vr2] = P.v.get(0);
-    sv[buf][vtt][2 * vr2 + 1] = P.v.get(1);
-    *reinterpret_cast<float4*>(&srec[buf][rec_e]) = P.r.get4(0);
-  };
-  // O of block cb = Hd C + diag(gam rq) Q S^T.  Before the block's second
-  // barrier each helper h forms the part of Hd C over the tokens 4 i + h (one
-  // product on its SIMD); after it, helper lane (t, j) sums the four parts and
-  // the four Q S^T parts and stores y[t][j] (16 lanes write a token's values).
-  const int ot = (ht & (HT - 1)) / 16, oj = ht % 16;
-  const int pl = 4 * ((ot / 4) * 16 + oj) + ot % 4;  // element (ot, oj) of a part
-  auto o_part = [&](int64_t cb) {  // before the barrier; returns gam_t rq_t of (ot, oj)
-    const int ob = (int)(cb & 1);
-    const float hd = srec[ob][kRecH + 16 * lc + 4 * lg + cp];
-    const v4f o = mfma4(hd, scc[ob][4 * lg + cp][lc], v4f{0.f, 0.f, 0.f, 0.f});
-    sop[ob][cp][lane] = o;
-    return srec[ob][kRecSig + ot];
-  };
-  auto out_y = [&](int64_t cb, float sig) {  // after the barrier
-    const int ob = (int)(cb & 1), sl = 1 + ob;
-    float pqs = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < NC; ++w) {
-      pqs += reinterpret_cast<const float*>(&spart[w][sl][0])[pl];
-      o += reinterpret_cast<const float*>(&sop[ob][w][0])[pl];
-    }
-    if (ot < tc_of(cb)) a.y[bs.v + (cb * kL + ot) * bs.v_ts + row0 + oj] = fmaf(sig, pqs, o);
+  // M x (16 x 16, row-major in LDS) times a 16 x 16 in the accumulator layout
+  auto mat16 = [&](const float* m, const v4f& x) {
+    const float4 f = *reinterpret_cast<const float4*>(&m[16 * lc + 4 * lg]);
+    v4f d = {0.f, 0.f, 0.f, 0.f};
+    d = mfma4(f.x, x[0], d);
+    d = mfma4(f.y, x[1], d);
+    d = mfma4(f.z, x[2], d);
+    d = mfma4(f.w, x[3], d);
+    return d;
   };
 
-  // ---- chain waves: the state, two key tiles of the 16 rows, accumulator layout
-  v4f St[NCT];
-  const int arow = row0 + lc;
-  if (chain) {
+  if (wave < NC) {
+    // ---- state waves: two key tiles of the 16 rows, accumulator layout
+    v4f St[NCT];
+    const int arow = row0 + lc;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
                                                         16 * (cp * NCT + ct) + 4 * lg);
       St[ct] = v4f{x.x, x.y, x.z, x.w};
     }
-  }
-
-  // Each role runs its own loop; both take the same two barriers per block in
-  // the same order, so the workgroup stays in step while each role's
-  // registers (the state, the staged blocks) stay out of the other's code.
-  const int64_t npair = nblk / 2;
-  if (chain) {
-    // block c: LDS buffer c & 1 holds it
-    auto step = [&](int64_t c) {
-      const int bf = (int)(c & 1);
-      __syncthreads();
-      v4f pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+    // operand fragments of the 16 rows X of a slot (raw q or k) for X S^T
+    auto frag = [&](const KT (*x)[KP], float4* f) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const float4 kf = *reinterpret_cast<const float4*>(&sk[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
-        pk = mfma4(kf.x, St[ct][0], pk);
-        pk = mfma4(kf.y, St[ct][1], pk);
-        pk = mfma4(kf.z, St[ct][2], pk);
-        pk = mfma4(kf.w, St[ct][3], pk);
-      }
-      float bei[4], wsci[4], vi[4], srsi[4], ka[NCT][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bei[r] = srec[bf][kRecBe + 4 * lg + r];
-        wsci[r] = srec[bf][kRecWsc + 4 * lg + r];
-        srsi[r] = srec[bf][kRecSrs + 4 * lg + r];
-        vi[r] = sv[bf][4 * lg + r][lc];
-      }
+      for (int ct = 0; ct < NCT; ++ct) f[ct] = lds_get4<DT>(x[lc], 16 * (cp * NCT + ct) + 4 * lg);
+    };
+    // X S^T over this wave's key tiles
+    auto xst = [&](const float4* f) {
+      v4f p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+      const float4 f0 = f[0], f1 = f[1];
+      p0 = mfma4(f0.x, St[0][0], p0);
+      p1 = mfma4(f1.x, St[1][0], p1);
+      p0 = mfma4(f0.y, St[0][1], p0);
+      p1 = mfma4(f1.y, St[1][1], p1);
+      p0 = mfma4(f0.z, St[0][2], p0);
+      p1 = mfma4(f1.z, St[1][2], p1);
+      p0 = mfma4(f0.w, St[0][3], p0);
+      p1 = mfma4(f1.w, St[1][3], p1);
+      return p0 + p1;
+    };
+    // operands of round r, read in round r - 1 (staged at least a round
+    // before that): Q_r, K_(r-1) in the update's layout, gam(r-1)
+    struct Ops {
+      float4 qf[NCT];
+      float kt[NCT][4];
+      float gl;
+    };
+    auto fetch = [&](int64_t r, Ops& o) {
+      const int sp_ = (int)((r - 1) & 3);
+      frag(sq[r & 3], o.qf);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2)
-          ka[ct][s2] = sk[bf][4 * lg + s2][16 * (cp * NCT + ct) + lc];
-      const float4 tf = *reinterpret_cast<const float4*>(&srec[bf][kRecT + 16 * lc + 4 * lg]);
-      const float gl = srec[bf][kRecGl];
-      spart[cp][0][lane] = pk;
+        for (int s2 = 0; s2 < 4; ++s2) o.kt[ct][s2] = lds_get<DT>(sk[sp_][4 * lg + s2], 16 * (cp * NCT + ct) + lc);
+      o.gl = srec[sp_][kRecGl];
+    };
+    // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1)
+    auto update = [&](const v4f& cs, const Ops& o) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const float4 qf = *reinterpret_cast<const float4*>(&sq[bf][lc][16 * (cp * NCT + ct) + 4 * lg]);
-        pq = mfma4(qf.x, St[ct][0], pq);
-        pq = mfma4(qf.y, St[ct][1], pq);
-        pq = mfma4(qf.z, St[ct][2], pq);
-        pq = mfma4(qf.w, St[ct][3], pq);
-      }
-      __syncthreads();
-      const v4f k0 = spart[0][0][lane], k1 = spart[1][0][lane];
-      const v4f k2 = spart[2][0][lane], k3 = spart[3][0][lane];
-      pk = (k0 + k1) + (k2 + k3);
-      v4f yv;
+        v4f acc = St[ct] * o.gl;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yv[r] = bei[r] * vi[r] - wsci[r] * pk[r];
-      v4f cc = {0.f, 0.f, 0.f, 0.f};
-      cc = mfma4(tf.x, yv[0], cc);
-      cc = mfma4(tf.y, yv[1], cc);
-      cc = mfma4(tf.z, yv[2], cc);
-      cc = mfma4(tf.w, yv[3], cc);
-      v4f cs;  // C with the key scales of the update on its rows
-#pragma unroll
-      for (int r = 0; r < 4; ++r) cs[r] = cc[r] * srsi[r];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        v4f acc = St[ct] * gl;
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(ka[ct][s2], cs[s2], acc);
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(o.kt[ct][s2], cs[s2], acc);
         St[ct] = acc;
       }
-      spart[cp][1 + bf][lane] = pq;
-      if (cp == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) scc[bf][4 * lg + r][lc] = cc[r];
-      }
     };
+    // round r >= 1: cur holds round r's operands, nxt takes round r + 1's
+    auto round = [&](int64_t r, const Ops& cur, Ops& nxt) {
+      __syncthreads();
+      const v4f cs = scs[(r - 1) & 1][lane];
+      float4 kf[NCT];
+      frag(sk[(r + 1) & 3], kf);
+      fetch(r + 1, nxt);
+      sp[r & 1][cp][lane] = xst(cur.qf);
+      sb[(r + 1) & 1][cp][lane] = xst(kf);
+      update(cs, cur);
+    };
+    Ops o0, o1;
+    float4 kf[NCT];
+    __syncthreads();  // blocks 0 and 1 staged
+    frag(sk[0], kf);
+    sb[0][cp][lane] = xst(kf);  // A_0
+    fetch(0, o0);               // Q_0 (its K and gam parts are not used)
+    __syncthreads();
+    // round 0: P_0 and B_1 from S_0, no update
+    frag(sk[1], kf);
+    fetch(1, o1);
+    sp[0][cp][lane] = xst(o0.qf);
+    sb[1][cp][lane] = xst(kf);
+    const int64_t npair = (nblk - 1) / 2;
     for (int64_t p = 0; p < npair; ++p) {
-      step(2 * p);
-      step(2 * p + 1);
+      round(1 + 2 * p, o1, o0);
+      round(2 + 2 * p, o0, o1);
     }
-    if (nblk & 1) step(nblk - 1);
+    if ((nblk - 1) & 1) round(nblk - 1, o1, o0);
     __syncthreads();
-    __syncthreads();
+    update(scs[(nblk - 1) & 1][lane], ((nblk - 1) & 1) ? o0 : o1);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
       *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * (cp * NCT + ct) +
                                  4 * lg) = x;
     }
-  } else {
-    // block c: the loads of block c + 2 go into Pl, O and y of block c - 1
-    // are formed, Ps (block c + 1) reaches the other LDS buffer after the
-    // block's second barrier
-    auto step = [&](int64_t c, Regs& Pl, const Regs& Ps) {
-      const int bf = (int)(c & 1);
-      __syncthreads();
-      chunk_load(Pl, c + 2 < nblk ? c + 2 : nblk - 1);
-      const float sig = c >= 1 ? o_part(c - 1) : 0.f;
-      __syncthreads();
-      chunk_store(Ps, bf ^ 1);
-      // y after the staging: the wait before the staging then never covers a
-      // store issued in the same block
-      if (c >= 1) out_y(c - 1, sig);
-    };
-    Regs P0, P1;
-    chunk_load(P0, 0);
-    chunk_load(P1, nblk > 1 ? 1 : 0);
-    chunk_store(P0, 0);
-    // nothing in flight on entry, and no exit inside the loop body: the
-    // loop's own loads are then the only ones its waits have to count
-    __builtin_amdgcn_s_waitcnt(0xF70);
-    for (int64_t p = 0; p < npair; ++p) {
-      step(2 * p, P0, P1);
-      step(2 * p + 1, P1, P0);
-    }
-    if (nblk & 1) step(nblk - 1, P0, P1);
-    __syncthreads();
-    const float sig = o_part(nblk - 1);
-    __syncthreads();
-    out_y(nblk - 1, sig);
+    return;
   }
-}
 
+  if (wave == NC) {
+    // ---- chain wave: C of block r.  K_r S_r^T = gam(r-1) (gam(r-2) sum B_r
+    // + Y_r) + M1_r Cs_(r-1); the last term was formed at the end of round
+    // r - 1, the record of block r read at its start.
+    __builtin_amdgcn_s_setprio(3);  // ahead of the state wave on its SIMD
+    struct Cops {
+      float4 tf, m1;
+      float be[4], wsc[4], srs[4], v[4];
+      float g1, g2;
+      v4f mc;
+    };
+    v4f csp = {0.f, 0.f, 0.f, 0.f};
+    auto fetch = [&](int64_t r, Cops& o, float g1, float g2) {
+      const int s = (int)(r & 3);
+      o.tf = *reinterpret_cast<const float4*>(&srec[s][kRecT + 16 * lc + 4 * lg]);
+      o.m1 = *reinterpret_cast<const float4*>(&smx[s][16 * lc + 4 * lg]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o.be[i] = srec[s][kRecBe + 4 * lg + i];
+        o.wsc[i] = srec[s][kRecWsc + 4 * lg + i];
+        o.srs[i] = srec[s][kRecSrs + 4 * lg + i];
+        o.v[i] = sv[s][4 * lg + i][lc];
+      }
+      o.g1 = g1;
+      o.g2 = g2;
+    };
+    auto step = [&](int64_t r, const Cops& o, const v4f& bsum, const v4f& y) {
+      v4f yv;  // beta V - (beta gam rk) K S^T
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        yv[i] = o.be[i] * o.v[i] - o.wsc[i] * fmaf(o.g1, fmaf(o.g2, bsum[i], y[i]), o.mc[i]);
+      const float4 tf = o.tf;
+      v4f cc = {0.f, 0.f, 0.f, 0.f};
+      cc = mfma4(tf.x, yv[0], cc);
+      cc = mfma4(tf.y, yv[1], cc);
+      cc = mfma4(tf.z, yv[2], cc);
+      cc = mfma4(tf.w, yv[3], cc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) csp[i] = cc[i] * o.srs[i];
+      scs[r & 1][lane] = csp;
+      scc[r & 1][lane] = cc;
+    };
+    auto m1cs = [&](Cops& o) {  // M1 of the next block times the newest Cs
+      v4f d = {0.f, 0.f, 0.f, 0.f};
+      d = mfma4(o.m1.x, csp[0], d);
+      d = mfma4(o.m1.y, csp[1], d);
+      d = mfma4(o.m1.z, csp[2], d);
+      d = mfma4(o.m1.w, csp[3], d);
+      o.mc = d;
+    };
+    auto bparts = [&](int64_t r) {
+      const int ab = (int)(r & 1);
+      return (sb[ab][0][lane] + sb[ab][1][lane]) + (sb[ab][2][lane] + sb[ab][3][lane]);
+    };
+    auto round = [&](int64_t r, const Cops& cur, Cops& nxt) {
+      __syncthreads();
+      const v4f bsum = bparts(r);
+      const v4f y = sy[r & 1][lane];
+      fetch(r + 1, nxt, srec[r & 3][kRecGl], srec[(r - 1) & 3][kRecGl]);
+      step(r, cur, bsum, y);
+      m1cs(nxt);
+    };
+    Cops c0, c1;
+    __syncthreads();  // blocks 0 and 1 staged
+    fetch(0, c0, 1.f, 1.f);
+    c0.mc = v4f{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // A_0 formed
+    {
+      const v4f bsum = bparts(0);
+      fetch(1, c1, srec[0][kRecGl], 1.f);
+      step(0, c0, bsum, v4f{0.f, 0.f, 0.f, 0.f});
+      m1cs(c1);
+    }
+    const int64_t npair = (nblk - 1) / 2;
+    for (int64_t p = 0; p < npair; ++p) {
+      round(1 + 2 * p, c1, c0);
+      round(2 + 2 * p, c0, c1);
+    }
+    if ((nblk - 1) & 1) round(nblk - 1, c1, c0);
+    __syncthreads();
+    return;
+  }
+
+  if (wave == NC + 1) {
+    // ---- O and y of the previous block.  This wave loads nothing: with
+    // only stores in its memory queue it never waits on it.
+    // O_c = diag(gam rq) (gam(c-1) sum P_c + Z_c) + Hd C_c: lane (lg, lc)
+    // register i is token 4 lg + i, row lc
+    auto o_block = [&](int64_t cb, float g) {
+      const int s = (int)(cb & 3), ob = (int)(cb & 1);
+      const v4f pq = (sp[ob][0][lane] + sp[ob][1][lane]) + (sp[ob][2][lane] + sp[ob][3][lane]);
+      const v4f z = sz[ob][lane];
+      const v4f cc = scc[ob][lane];
+      const float4 hf = *reinterpret_cast<const float4*>(&srec[s][kRecH + 16 * lc + 4 * lg]);
+      v4f o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = srec[s][kRecSig + 4 * lg + i] * fmaf(g, pq[i], z[i]);
+      o = mfma4(hf.x, cc[0], o);
+      o = mfma4(hf.y, cc[1], o);
+      o = mfma4(hf.z, cc[2], o);
+      o = mfma4(hf.w, cc[3], o);
+      return o;
+    };
+    auto o_store = [&](int64_t cb, const v4f& o, int tc) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * lg + i < tc) a.y[bs.v + (cb * kL + 4 * lg + i) * bs.v_ts + row0 + lc] = o[i];
+    };
+    __syncthreads();  // blocks 0 and 1 staged
+    __syncthreads();  // A_0 formed
+    float g = 1.f;    // gam(r-2) in round r
+    for (int64_t r = 1; r < nblk; ++r) {
+      __syncthreads();
+      const float gn = srec[(r - 1) & 3][kRecGl];
+      o_store(r - 1, o_block(r - 1, g), kL);
+      g = gn;
+    }
+    __syncthreads();
+    o_store(nblk - 1, o_block(nblk - 1, g), tc_of(nblk - 1));
+    return;
+  }
+
+  // ---- waves 6 and 7: the staging, and Y (wave 6) or Z (wave 7).  Lane st:
+  // q and k of token st / 8, elements 16 (st % 8) .. + 15; two v values; two
+  // float4 of the record and of M1 M2 N.
+  constexpr int NR4 = kRecUsed / 4, NM4 = NM / 4;
+  struct Regs {
+    Raw<DT, 8> k[2], q[2];
+    Raw<DT, 2> v;
+    Raw<GDN_F32, 4> r[2], m[2];
+  };
+  const int st = tid - (NC + 2) * kWave;
+  const int qtt = st / 8, qc = 16 * (st % 8), vr = 2 * (st % 8);
+  int rec_e[2], mx_e[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    rec_e[u] = 4 * (st + 2 * kWave * u < NR4 ? st + 2 * kWave * u : NR4 - 1);
+    mx_e[u] = 4 * (st + 2 * kWave * u < NM4 ? st + 2 * kWave * u : NM4 - 1);
+  }
+  // branch-free addresses (a branch here splits the loop body, and the
+  // registers of a load then no longer carry over the loop edge)
+  auto load = [&](Regs& P, int64_t c) {
+    const int tcc = c == nblk - 1 ? tcl : kL;  // tokens in block c
+    const int64_t t = c * kL + (qtt < tcc ? qtt : tcc - 1);
+    const int64_t o = bs.qk + t * bs.qk_ts + qc;
+    P.k[0].load(a.k, o);
+    P.k[1].load(a.k, o + 8);
+    P.q[0].load(a.q, o);
+    P.q[1].load(a.q, o + 8);
+    P.v.load(a.v, bs.v + t * bs.v_ts + row0 + vr);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      P.r[u].load(rec, c * kRec + rec_e[u]);
+      P.m[u].load(mxh, c * NM + mx_e[u]);
+    }
+  };
+  // the loaded words pass through an empty asm first: the conversions for
+  // the LDS writes then stay below the barrier before them (hoisted above
+  // it, they would wait on the loads a round early)
+  auto pin = [](auto& raw) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(raw.w) / sizeof(raw.w[0])); ++i) asm volatile("" : "+v"(raw.w[i]));
+  };
+  // each LDS element is written once (the clamped lanes load but do not write)
+  auto store = [&](Regs& P, int sl) {
+    pin(P.k[0]);
+    pin(P.k[1]);
+    pin(P.q[0]);
+    pin(P.q[1]);
+    pin(P.v);
+    pin(P.r[0]);
+    pin(P.r[1]);
+    pin(P.m[0]);
+    pin(P.m[1]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (DT == GDN_F32) {
+        *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h]) = P.k[h].get4(0);
+        *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h + 4]) = P.k[h].get4(1);
+        *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h]) = P.q[h].get4(0);
+        *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h + 4]) = P.q[h].get4(1);
+      } else {
+        *reinterpret_cast<uint4*>(&sk[sl][qtt][qc + 8 * h]) =
+            make_uint4(P.k[h].w[0], P.k[h].w[1], P.k[h].w[2], P.k[h].w[3]);
+        *reinterpret_cast<uint4*>(&sq[sl][qtt][qc + 8 * h]) =
+            make_uint4(P.q[h].w[0], P.q[h].w[1], P.q[h].w[2], P.q[h].w[3]);
+      }
+    }
+    *reinterpret_cast<float2*>(&sv[sl][qtt][vr]) = make_float2(P.v.get(0), P.v.get(1));
+    *reinterpret_cast<float4*>(&srec[sl][rec_e[0]]) = P.r[0].get4(0);
+    if (st + 2 * kWave < NR4) *reinterpret_cast<float4*>(&srec[sl][rec_e[1]]) = P.r[1].get4(0);
+    *reinterpret_cast<float4*>(&smx[sl][mx_e[0]]) = P.m[0].get4(0);
+    if (st + 2 * kWave < NM4) *reinterpret_cast<float4*>(&smx[sl][mx_e[1]]) = P.m[1].get4(0);
+  };
+  // P's loads are kept below its LDS writes: its registers then carry over
+  // the loop edge, and no copy there waits for the loads of the last round.
+  // (The inputs are read-only, so the compiler would otherwise hoist the
+  // loads across the writes and the barrier; the block index passes through
+  // an empty asm after the writes.)
+  auto restage = [&](Regs& P, int sl, int64_t c) {
+    store(P, sl);
+    __builtin_amdgcn_sched_barrier(0);
+    int64_t cn = clampb(c);
+    asm volatile("" : "+s"(cn) : : "memory");
+    load(P, cn);
+  };
+  const bool ywave = wave == NC + 2;
+  // round r >= 1: Y_(r+1) = M2_(r+1) Cs_(r-1) (wave 6) or Z_r = N_r Cs_(r-1)
+  // (wave 7); P holds block r + 2, loaded three rounds before (right after
+  // its previous contents went to LDS, so two whole rounds hide the load
+  // latency); it goes to its slot, then takes the loads of block r + 5.
+  // Three register sets in turn, the loop unrolled by three.
+  auto round = [&](int64_t r, Regs& P) {
+    __syncthreads();
+    const v4f cs = scs[(r - 1) & 1][lane];
+    const float* m = ywave ? &smx[(r + 1) & 3][kL * kL] : &smx[r & 3][2 * kL * kL];
+    const v4f d = mat16(m, cs);
+    restage(P, (int)((r + 2) & 3), r + 5);
+    if (ywave) sy[(r + 1) & 1][lane] = d;
+    else sz[r & 1][lane] = d;
+  };
+  Regs P0, P1, P2;
+  load(P0, 0);
+  load(P1, clampb(1));
+  store(P0, 0);
+  store(P1, 1);
+  load(P0, clampb(2));
+  load(P1, clampb(3));
+  load(P2, clampb(4));
+  __syncthreads();  // blocks 0 and 1 staged
+  __syncthreads();  // A_0 formed
+  // round 0: Y_1 = Z_0 = 0 (no C-scaled before block 0)
+  restage(P0, 2, 5);
+  if (ywave) sy[1][lane] = v4f{0.f, 0.f, 0.f, 0.f};
+  else sz[0][lane] = v4f{0.f, 0.f, 0.f, 0.f};
+  // nothing but the loads of blocks 3 to 5 in flight on entry, and no exit
+  // inside the loop body
+  const int64_t ntri = (nblk - 1) / 3, rem = (nblk - 1) % 3;
+  for (int64_t p = 0; p < ntri; ++p) {
+    round(1 + 3 * p, P1);
+    round(2 + 3 * p, P2);
+    round(3 + 3 * p, P0);
+  }
+  if (rem >= 1) round(1 + 3 * ntri, P1);
+  if (rem >= 2) round(2 + 3 * ntri, P2);
+  __syncthreads();
+}
 
 template <int DT>
 int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
@@ -739,20 +999,25 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
   const int rc = launch_prep<DT>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;
   // many heads: whole-head workgroups, two per CU, the norm fused; few heads:
-  // a workgroup per 16 value rows (rows_ws_kernel)
+  // a workgroup per 16 value rows with the one-block lookahead
   StateArgs r = s;
-  if (heads >= 256) {
+  if (heads >= kManyHeads) {
     r.nrb = 1;
     state_kernel<DT><<<dim3((unsigned)heads), 512, 0, st>>>(r);
     return device_status("state_kernel launch");
   }
   r.nrb = kD / 16;
-  rows_ws_kernel<DT><<<dim3((unsigned)(heads * r.nrb)), 512, 0, st>>>(r);
-  return device_status("rows_ws_kernel launch");
+  rows_la_kernel<DT><<<dim3((unsigned)(heads * r.nrb)), 512, 0, st>>>(r);
+  return device_status("rows_la_kernel launch");
 }
 
 int64_t block_record_bytes(int64_t heads, int64_t T) {
   return heads * ((T + kL - 1) / kL) * (int64_t)kRec * (int64_t)sizeof(float);
+}
+
+// the prep's cross-block products (few heads only): 3 KiB per key head and block
+int64_t key_cross_bytes(int64_t bk, int64_t T) {
+  return bk * ((T + kL - 1) / kL) * (int64_t)(3 * kL * kL) * (int64_t)sizeof(float);
 }
 
 }  // namespace
@@ -766,18 +1031,21 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
                         const void* w, float* y, float* s_out, void* stream, bool* gated) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t heads = d.B * d.Hv, nblk = (d.T + kL - 1) / kL;
-  *gated = heads >= 256;
+  *gated = heads >= kManyHeads;
+  const int64_t rec_bytes = block_record_bytes(heads, d.T);
+  const int64_t mx_bytes = *gated ? 0 : key_cross_bytes(d.B * d.Hk, d.T);
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)block_record_bytes(heads, d.T), st) != hipSuccess) {
+  if (hipMallocAsync(&ws, (size_t)(rec_bytes + mx_bytes), st) != hipSuccess) {
     (void)hipGetLastError();
     set_error("gdn_scan: no device memory for the block records");
     return GDN_EDEVICE;
   }
   float* rec = static_cast<float*>(ws);
+  float* mx = *gated ? nullptr : rec + rec_bytes / (int64_t)sizeof(float);
   const PrepArgs p{q, k, ld, beta, rec, d.T, nblk, d.B * d.Hk * nblk, (int)d.Hk, (int)d.Hv,
-                   (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d)};
+                   (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d), mx};
   const StateArgs s{q, k, v, z, w, rec, s0, y, s_out, d.T, nblk, (int)d.Hk, (int)d.Hv,
-                    (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps};
+                    (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps, mx};
   int rc;
   switch (d.dtype) {
     case GDN_F32: rc = launch_dt<GDN_F32>(d, p, s, heads, st); break;
