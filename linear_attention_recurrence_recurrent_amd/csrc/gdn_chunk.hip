@@ -103,7 +103,9 @@ struct PrepArgs {
 // One wave per (batch, key head, block): K K^T and Q K^T once, then the
 // records of the G value heads that share the key head (four at a time, one
 // per 16-lane group).  No workgroup barrier: each wave owns its LDS slice.
-template <int DT, int GT>
+// XB: also the products across blocks into a.mx (the few-head kernel's; a
+// separate instance, so the many-head prep keeps its register count)
+template <int DT, int GT, bool XB>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       G4 = mfma4(kv, kv, G4);
       H4 = mfma4(qr[u].get(e), kv, H4);
     }
-  if (a.mx != nullptr) {
+  if constexpr (XB) {
     // Products of raw rows across blocks (zero where the earlier block does
     // not exist), row-major: M1 = K_c K_(c-1)^T, M2 = K_c K_(c-2)^T and
     // N = Q_c K_(c-1)^T.  The few-head kernel forms K S^T and Q S^T of a
@@ -237,7 +239,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * lg + r;
         if (r > 0) {
-          const float ai = lg == 0 ? als[r] : lg == 1 ? als[4 + r] : lg == 2 ? als[8 + r] : als[12 + r];
+          // alpha of row i from the lane that holds it (selecting it from
+          // als by lg becomes an indexed array in scratch memory)
+          const float ai = __shfl(al, 16 * gq + i);
           dc = j < i ? dc * ai : (j == i ? 1.f : 0.f);
         }
         const float bei = __shfl(be, 16 * gq + i);
@@ -984,10 +988,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
 
 template <int DT>
 int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
+  const bool xb = p.mx != nullptr;
   switch (gdt) {
-    case GDN_F32: prep_kernel<DT, GDN_F32><<<grid, 256, 0, st>>>(p); break;
-    case GDN_F16: prep_kernel<DT, GDN_F16><<<grid, 256, 0, st>>>(p); break;
-    default: prep_kernel<DT, GDN_BF16><<<grid, 256, 0, st>>>(p); break;
+    case GDN_F32:
+      if (xb) prep_kernel<DT, GDN_F32, true><<<grid, 256, 0, st>>>(p);
+      else prep_kernel<DT, GDN_F32, false><<<grid, 256, 0, st>>>(p);
+      break;
+    case GDN_F16:
+      if (xb) prep_kernel<DT, GDN_F16, true><<<grid, 256, 0, st>>>(p);
+      else prep_kernel<DT, GDN_F16, false><<<grid, 256, 0, st>>>(p);
+      break;
+    default:
+      if (xb) prep_kernel<DT, GDN_BF16, true><<<grid, 256, 0, st>>>(p);
+      else prep_kernel<DT, GDN_BF16, false><<<grid, 256, 0, st>>>(p);
+      break;
   }
   return device_status("prep_kernel launch");
 }
