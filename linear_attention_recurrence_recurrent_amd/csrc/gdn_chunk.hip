@@ -557,6 +557,34 @@ __device__ __forceinline__ float half_hi(uint32_t x) {
   if constexpr (DT == GDN_BF16) return __uint_as_float(x & 0xffff0000u);
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
 }
+// 16-bit fragments widened on the matrix cores.  With lane (lg, lc) holding
+// X[lc][4 lg .. 4 lg + 3] of a 16 x 16 tile packed (its raw A-operand fragment)
+// and E the identity in the same packing, the 16x16x16 product E X^T leaves
+// X[lc][4 lg + s] in register s (the f32 A-operand fragment) and X E leaves
+// X[4 lg + s][lc] (the transposed one), exactly.  A product right behind
+// vector work of the same wave issues only once the matrix pipe has
+// drained, so widening with vector instructions between the products cost
+// more than these products do.
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h16 __attribute__((ext_vector_type(4)));
+template <int DT>
+__device__ __forceinline__ v4f mm16(uint2 a, uint2 b) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (DT == GDN_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s16, a),
+                                                      __builtin_bit_cast(v4s16, b), z, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h16, a),
+                                                  __builtin_bit_cast(v4h16, b), z, 0, 0, 0);
+}
+template <int DT>
+__device__ __forceinline__ uint2 eye16(int lg, int lc) {  // the identity, packed as above
+  const uint32_t one = DT == GDN_BF16 ? 0x3F80u : 0x3C00u;
+  uint32_t e[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) e[s] = 4 * lg + s == lc ? one : 0u;
+  return make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+}
 template <int DT>
 __device__ __forceinline__ float4 lds_get4(const LdsElem<DT>* row, int e) {  // e % 4 == 0
   if constexpr (DT == GDN_F32) {
@@ -565,6 +593,10 @@ __device__ __forceinline__ float4 lds_get4(const LdsElem<DT>* row, int e) {  // 
     const uint2 u = *reinterpret_cast<const uint2*>(row + e);
     return make_float4(half_lo<DT>(u.x), half_hi<DT>(u.x), half_lo<DT>(u.y), half_hi<DT>(u.y));
   }
+}
+// the raw 16-bit fragment: 4 elements of a row, packed
+__device__ __forceinline__ uint2 lds_raw16(const uint16_t* row, int e) {  // e % 4 == 0
+  return *reinterpret_cast<const uint2*>(row + e);
 }
 template <int DT>
 __device__ __forceinline__ float lds_get(const LdsElem<DT>* row, int e) {
@@ -653,48 +685,72 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
                                                         16 * (cp * NCT + ct) + 4 * lg);
       St[ct] = v4f{x.x, x.y, x.z, x.w};
     }
-    // operand fragments of the 16 rows X of a slot (raw q or k) for X S^T
-    auto frag = [&](const KT (*x)[KP], float4* f) {
+    // Operand fragments of the 16 rows X of a slot (raw q or k) for X S^T:
+    // 16-bit inputs read raw (one 8-byte LDS read per key tile) and widened
+    // on the matrix cores (mm16), f32 read as is
+    constexpr bool MMW = DT != GDN_F32;
+    typedef typename std::conditional<MMW, uint2, float4>::type Frag;
+    [[maybe_unused]] const uint2 eye = eye16<DT>(lg, lc);
+    auto frag = [&](const KT (*x)[KP], Frag* f) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) f[ct] = lds_get4<DT>(x[lc], 16 * (cp * NCT + ct) + 4 * lg);
+      for (int ct = 0; ct < NCT; ++ct) {
+        if constexpr (MMW) f[ct] = lds_raw16(x[lc], 16 * (cp * NCT + ct) + 4 * lg);
+        else f[ct] = *reinterpret_cast<const float4*>(&x[lc][16 * (cp * NCT + ct) + 4 * lg]);
+      }
+    };
+    // the f32 A-operand fragments of frag()
+    auto widen = [&](const Frag* f, v4f* w) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if constexpr (MMW) w[ct] = mm16<DT>(eye, f[ct]);
+        else w[ct] = v4f{f[ct].x, f[ct].y, f[ct].z, f[ct].w};
+      }
     };
     // X S^T over this wave's key tiles
-    auto xst = [&](const float4* f) {
+    auto xst = [&](const v4f* f) {
       v4f p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
-      const float4 f0 = f[0], f1 = f[1];
-      p0 = mfma4(f0.x, St[0][0], p0);
-      p1 = mfma4(f1.x, St[1][0], p1);
-      p0 = mfma4(f0.y, St[0][1], p0);
-      p1 = mfma4(f1.y, St[1][1], p1);
-      p0 = mfma4(f0.z, St[0][2], p0);
-      p1 = mfma4(f1.z, St[1][2], p1);
-      p0 = mfma4(f0.w, St[0][3], p0);
-      p1 = mfma4(f1.w, St[1][3], p1);
+      p0 = mfma4(f[0][0], St[0][0], p0);
+      p1 = mfma4(f[1][0], St[1][0], p1);
+      p0 = mfma4(f[0][1], St[0][1], p0);
+      p1 = mfma4(f[1][1], St[1][1], p1);
+      p0 = mfma4(f[0][2], St[0][2], p0);
+      p1 = mfma4(f[1][2], St[1][2], p1);
+      p0 = mfma4(f[0][3], St[0][3], p0);
+      p1 = mfma4(f[1][3], St[1][3], p1);
       return p0 + p1;
     };
     // operands of round r, read in round r - 1 (staged at least a round
-    // before that): Q_r, K_(r-1) in the update's layout, gam(r-1)
+    // before that): Q_r, K_(r-1) (16-bit: its raw fragment, turned into the
+    // update's layout by X E; f32: that layout read directly), gam(r-1)
     struct Ops {
-      float4 qf[NCT];
+      Frag qf[NCT];
+      Frag kr[NCT];
       float kt[NCT][4];
       float gl;
     };
     auto fetch = [&](int64_t r, Ops& o) {
       const int sp_ = (int)((r - 1) & 3);
       frag(sq[r & 3], o.qf);
+      if constexpr (MMW) {
+        frag(sk[sp_], o.kr);
+      } else {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) o.kt[ct][s2] = lds_get<DT>(sk[sp_][4 * lg + s2], 16 * (cp * NCT + ct) + lc);
+          for (int s2 = 0; s2 < 4; ++s2) o.kt[ct][s2] = sk[sp_][4 * lg + s2][16 * (cp * NCT + ct) + lc];
+      }
       o.gl = srec[sp_][kRecGl];
     };
     // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1)
     auto update = [&](const v4f& cs, const Ops& o) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
+        v4f kt;
+        if constexpr (MMW) kt = mm16<DT>(o.kr[ct], eye);
+        else kt = v4f{o.kt[ct][0], o.kt[ct][1], o.kt[ct][2], o.kt[ct][3]};
         v4f acc = St[ct] * o.gl;
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(o.kt[ct][s2], cs[s2], acc);
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(kt[s2], cs[s2], acc);
         St[ct] = acc;
       }
     };
@@ -702,25 +758,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
     auto round = [&](int64_t r, const Ops& cur, Ops& nxt) {
       __syncthreads();
       const v4f cs = scs[(r - 1) & 1][lane];
-      float4 kf[NCT];
+      Frag kf[NCT];
       frag(sk[(r + 1) & 3], kf);
       fetch(r + 1, nxt);
-      sp[r & 1][cp][lane] = xst(cur.qf);
-      sb[(r + 1) & 1][cp][lane] = xst(kf);
+      v4f qw[NCT], kw[NCT];
+      widen(cur.qf, qw);
+      sp[r & 1][cp][lane] = xst(qw);
+      widen(kf, kw);
+      sb[(r + 1) & 1][cp][lane] = xst(kw);
       update(cs, cur);
     };
     Ops o0, o1;
-    float4 kf[NCT];
+    Frag kf[NCT];
+    v4f kw[NCT], qw[NCT];
     __syncthreads();  // blocks 0 and 1 staged
     frag(sk[0], kf);
-    sb[0][cp][lane] = xst(kf);  // A_0
+    widen(kf, kw);
+    sb[0][cp][lane] = xst(kw);  // A_0
     fetch(0, o0);               // Q_0 (its K and gam parts are not used)
     __syncthreads();
     // round 0: P_0 and B_1 from S_0, no update
     frag(sk[1], kf);
     fetch(1, o1);
-    sp[0][cp][lane] = xst(o0.qf);
-    sb[1][cp][lane] = xst(kf);
+    widen(o0.qf, qw);
+    sp[0][cp][lane] = xst(qw);
+    widen(kf, kw);
+    sb[1][cp][lane] = xst(kw);
     const int64_t npair = (nblk - 1) / 2;
     for (int64_t p = 0; p < npair; ++p) {
       round(1 + 2 * p, o1, o0);
