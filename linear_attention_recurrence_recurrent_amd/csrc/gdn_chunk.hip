@@ -68,6 +68,22 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 16x16x16 product of 16-bit operands (bf16 or f16), f32 accumulation: a lane
+// holds 4 elements of the contraction index packed in a uint2.  The products
+// of 16-bit values are exact in f32, so this equals the f32 product of the
+// widened operands up to the order of the sums.
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h16 __attribute__((ext_vector_type(4)));
+template <int DT>
+__device__ __forceinline__ v4f mm16(uint2 a, uint2 b, v4f c = v4f{0.f, 0.f, 0.f, 0.f}) {
+  if constexpr (DT == GDN_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s16, a),
+                                                      __builtin_bit_cast(v4s16, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h16, a),
+                                                  __builtin_bit_cast(v4h16, b), c, 0, 0, 0);
+}
+
 struct Bases {
   int64_t qk, qk_ts, v, v_ts, g, g_ts;
 };
@@ -152,17 +168,27 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   float rq = rsqrtf(l2 ? ssq + a.qk_eps : 1.f) * a.qscale;
   if (lc >= tc) rk = rq = 0.f;
 
-  // G = K K^T and H = Q K^T (raw) on the matrix cores; product m contracts
-  // key index 32 lg + m.  Lane (lg, lc), register r: entry [4 lg + r][lc].
-  v4f G4 = {0.f, 0.f, 0.f, 0.f}, H4 = {0.f, 0.f, 0.f, 0.f};
+  // X Y^T of 16 raw rows each on the matrix cores; lane (lg, lc), register
+  // r: entry [4 lg + r][lc].  The contraction runs over the lane's own 32
+  // elements: f32, one element per 16x16x4 product; 16-bit, four per 16x16x16
+  // product straight from the loaded words (no widening).
+  auto gram = [&](const Raw<DT, 8>* x, const Raw<DT, 8>* y) {
+    v4f d = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == GDN_F32) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float kv = kr[u].get(e);
-      G4 = mfma4(kv, kv, G4);
-      H4 = mfma4(qr[u].get(e), kv, H4);
+        for (int e = 0; e < 8; ++e) d = mfma4(x[u].get(e), y[u].get(e), d);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        d = mm16<DT>(make_uint2(x[m / 2].w[2 * (m % 2)], x[m / 2].w[2 * (m % 2) + 1]),
+                     make_uint2(y[m / 2].w[2 * (m % 2)], y[m / 2].w[2 * (m % 2) + 1]), d);
     }
+    return d;
+  };
+  // G = K K^T and H = Q K^T (raw)
+  const v4f G4 = gram(kr, kr), H4 = gram(qr, kr);
   if constexpr (XB) {
     // Products of raw rows across blocks (zero where the earlier block does
     // not exist), row-major: M1 = K_c K_(c-1)^T, M2 = K_c K_(c-2)^T and
@@ -173,22 +199,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       Raw<DT, 8> kp[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) kp[u].load(a.k, qk_base + (t0 - kL + lc) * qk_ts + 32 * lg + 8 * u);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          M1 = mfma4(kr[u].get(e), kp[u].get(e), M1);
-          N1 = mfma4(qr[u].get(e), kp[u].get(e), N1);
-        }
+      M1 = gram(kr, kp);
+      N1 = gram(qr, kp);
     }
     if (c > 1) {
       Raw<DT, 8> kp[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) kp[u].load(a.k, qk_base + (t0 - 2 * kL + lc) * qk_ts + 32 * lg + 8 * u);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) M2 = mfma4(kr[u].get(e), kp[u].get(e), M2);
+      M2 = gram(kr, kp);
     }
     float* mx = a.mx + task * (3 * kL * kL);
 #pragma unroll
@@ -559,24 +577,11 @@ __device__ __forceinline__ float half_hi(uint32_t x) {
 }
 // 16-bit fragments widened on the matrix cores.  With lane (lg, lc) holding
 // X[lc][4 lg .. 4 lg + 3] of a 16 x 16 tile packed (its raw A-operand fragment)
-// and E the identity in the same packing, the 16x16x16 product E X^T leaves
-// X[lc][4 lg + s] in register s (the f32 A-operand fragment) and X E leaves
-// X[4 lg + s][lc] (the transposed one), exactly.  A product right behind
-// vector work of the same wave issues only once the matrix pipe has
-// drained, so widening with vector instructions between the products cost
-// more than these products do.
-typedef short v4s16 __attribute__((ext_vector_type(4)));
-typedef _Float16 v4h16 __attribute__((ext_vector_type(4)));
-template <int DT>
-__device__ __forceinline__ v4f mm16(uint2 a, uint2 b) {
-  const v4f z = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (DT == GDN_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s16, a),
-                                                      __builtin_bit_cast(v4s16, b), z, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h16, a),
-                                                  __builtin_bit_cast(v4h16, b), z, 0, 0, 0);
-}
+// and E the identity in the same packing, mm16(E, X) leaves X[lc][4 lg + s] in
+// register s (the f32 A-operand fragment) and mm16(X, E) leaves X[4 lg + s][lc]
+// (the transposed one), exactly.  A product right behind vector work of the
+// same wave issues only once the matrix pipe has drained, so widening with
+// vector instructions between the products cost more than these products do.
 template <int DT>
 __device__ __forceinline__ uint2 eye16(int lg, int lc) {  // the identity, packed as above
   const uint32_t one = DT == GDN_BF16 ? 0x3F80u : 0x3C00u;
