@@ -181,6 +181,11 @@ BLOCK_EDGES = [
     (3, 3, 2, 4, "f16", False),     # three tokens: one block with thirteen padded rows
     (1, 32, 4, 4, "f32", False),    # even block count, no grouping
     (2, 47, 16, 128, "bf16", True),  # 256 heads: whole-head workgroups, ragged tail
+    # few heads: the staging loop runs blocks in threes and the state loop in pairs; block
+    # counts 5, 6 and 7 reach every remainder of both with at least one full pass
+    (1, 70, 2, 4, "bf16", False),   # 5 blocks, ragged
+    (1, 96, 1, 2, "f16", True),     # 6 blocks, exact
+    (2, 99, 2, 2, "f32", False),    # 7 blocks, ragged
 ]
 
 
