@@ -84,6 +84,37 @@ __device__ __forceinline__ v4f mm16(uint2 a, uint2 b, v4f c = v4f{0.f, 0.f, 0.f,
                                                   __builtin_bit_cast(v4h16, b), c, 0, 0, 0);
 }
 
+// 16x16x32 product of bf16 operands, f32 accumulation: a lane holds 8
+// elements of the contraction index packed in a uint4, the same 8 for A's
+// row and B's column.
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mm32bf(uint4 a, uint4 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, a),
+                                                 __builtin_bit_cast(v8bf16, b), c, 0, 0, 0);
+}
+
+// An f32 value as the exact sum of three bf16 values.  hi keeps the top 8
+// significant bits (truncation), the rest x - hi has at most 16 significant
+// bits, its own truncation mid takes 8 of them and lo = x - hi - mid the last
+// 8 or fewer, so lo is a bf16 value as it stands.  Both subtractions are
+// exact.  With bf16 q and k the products against the three parts are exact
+// in f32, so a state product through them is an f32 product up to the order
+// of the sums.  Two values are packed per word, the first in the low half.
+struct Bf3 {
+  uint32_t h, m, l;
+};
+__device__ __forceinline__ Bf3 split_bf3(float x0, float x1) {
+  const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+  const float r0 = x0 - __uint_as_float(u0 & 0xffff0000u);
+  const float r1 = x1 - __uint_as_float(u1 & 0xffff0000u);
+  const uint32_t w0 = __float_as_uint(r0), w1 = __float_as_uint(r1);
+  const uint32_t t0 = __float_as_uint(r0 - __uint_as_float(w0 & 0xffff0000u));
+  const uint32_t t1 = __float_as_uint(r1 - __uint_as_float(w1 & 0xffff0000u));
+  // the high halves of two words, the first word's in the low half
+  return Bf3{__builtin_amdgcn_perm(u1, u0, 0x07060302u), __builtin_amdgcn_perm(w1, w0, 0x07060302u),
+             __builtin_amdgcn_perm(t1, t0, 0x07060302u)};
+}
+
 struct Bases {
   int64_t qk, qk_ts, v, v_ts, g, g_ts;
 };
@@ -680,7 +711,106 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
     return d;
   };
 
-  if (wave < NC) {
+  if constexpr (DT == GDN_BF16) {
+    if (wave < NC) {
+      // ---- state waves, bf16 inputs.  The wave's 32 key columns go in the
+      // order that makes lane (lg, lc) hold columns 32 cp + 8 lg .. + 7 of
+      // its row: tile ct keeps S^T row 32 cp + 8 (i / 4) + 4 ct + i % 4 at
+      // tile row i.  Its registers are then the B operand of a 16x16x32
+      // product whose A operand is 8 consecutive raw elements of a q or k
+      // row, one LDS read.  X S^T runs on the three bf16 parts of S, and the
+      // update on those of Cs, against the transposed raw k.
+      v4f St[NCT];
+      const int64_t soff = sbase + (int64_t)(row0 + lc) * kD + 32 * cp + 8 * lg;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float4 x = *reinterpret_cast<const float4*>(a.s0 + soff + 4 * ct);
+        St[ct] = v4f{x.x, x.y, x.z, x.w};
+      }
+      uint4 Sh, Sm, Sl;
+      auto split_state = [&]() {
+        const Bf3 p0 = split_bf3(St[0][0], St[0][1]), p1 = split_bf3(St[0][2], St[0][3]);
+        const Bf3 p2 = split_bf3(St[1][0], St[1][1]), p3 = split_bf3(St[1][2], St[1][3]);
+        Sh = make_uint4(p0.h, p1.h, p2.h, p3.h);
+        Sm = make_uint4(p0.m, p1.m, p2.m, p3.m);
+        Sl = make_uint4(p0.l, p1.l, p2.l, p3.l);
+      };
+      auto raw8 = [&](const KT (*x)[KP]) {
+        return *reinterpret_cast<const uint4*>(&x[lc][32 * cp + 8 * lg]);
+      };
+      // X S^T over this wave's key columns, the small parts first
+      auto xst = [&](const uint4& f) {
+        v4f p = mm32bf(f, Sl, v4f{0.f, 0.f, 0.f, 0.f});
+        p = mm32bf(f, Sm, p);
+        return mm32bf(f, Sh, p);
+      };
+      // operands of round r, read in round r - 1: Q_r raw, K_(r-1) transposed
+      // (lane (lg, lc): tokens 4 lg .. + 3 of the tile's column lc), gam(r-1)
+      struct Ops {
+        uint4 qf;
+        uint2 kt[NCT];
+        float gl;
+      };
+      auto fetch = [&](int64_t r, Ops& o) {
+        const int sp_ = (int)((r - 1) & 3);
+        o.qf = raw8(sq[r & 3]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const KT* c0 = &sk[sp_][4 * lg][32 * cp + 8 * (lc / 4) + 4 * ct + lc % 4];
+          o.kt[ct] = make_uint2((uint32_t)c0[0] | ((uint32_t)c0[KP] << 16),
+                                (uint32_t)c0[2 * KP] | ((uint32_t)c0[3 * KP] << 16));
+        }
+        o.gl = srec[sp_][kRecGl];
+      };
+      // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1), then its parts
+      auto update = [&](const v4f& cs, const Ops& o) {
+        const Bf3 c0 = split_bf3(cs[0], cs[1]), c1 = split_bf3(cs[2], cs[3]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          v4f acc = St[ct] * o.gl;
+          acc = mm16<GDN_BF16>(o.kt[ct], make_uint2(c0.l, c1.l), acc);
+          acc = mm16<GDN_BF16>(o.kt[ct], make_uint2(c0.m, c1.m), acc);
+          St[ct] = mm16<GDN_BF16>(o.kt[ct], make_uint2(c0.h, c1.h), acc);
+        }
+        split_state();
+      };
+      auto round = [&](int64_t r, const Ops& cur, Ops& nxt) {
+        __syncthreads();
+        const v4f cs = scs[(r - 1) & 1][lane];
+        const uint4 kf = raw8(sk[(r + 1) & 3]);
+        fetch(r + 1, nxt);
+        sp[r & 1][cp][lane] = xst(cur.qf);
+        sb[(r + 1) & 1][cp][lane] = xst(kf);
+        update(cs, cur);
+      };
+      Ops o0, o1;
+      split_state();
+      __syncthreads();  // blocks 0 and 1 staged
+      sb[0][cp][lane] = xst(raw8(sk[0]));  // A_0
+      fetch(0, o0);                        // Q_0 (its K and gam parts are not used)
+      __syncthreads();
+      {  // round 0: P_0 and B_1 from S_0, no update
+        const uint4 kf = raw8(sk[1]);
+        fetch(1, o1);
+        sp[0][cp][lane] = xst(o0.qf);
+        sb[1][cp][lane] = xst(kf);
+      }
+      const int64_t npair = (nblk - 1) / 2;
+      for (int64_t p = 0; p < npair; ++p) {
+        round(1 + 2 * p, o1, o0);
+        round(2 + 2 * p, o0, o1);
+      }
+      if ((nblk - 1) & 1) round(nblk - 1, o1, o0);
+      __syncthreads();
+      update(scs[(nblk - 1) & 1][lane], ((nblk - 1) & 1) ? o0 : o1);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        *reinterpret_cast<float4*>(a.s_out + soff + 4 * ct) =
+            make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
+      return;
+    }
+  }
+  if (DT != GDN_BF16 && wave < NC) {
     // ---- state waves: two key tiles of the 16 rows, accumulator layout
     v4f St[NCT];
     const int arow = row0 + lc;
