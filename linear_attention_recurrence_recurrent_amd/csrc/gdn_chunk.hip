@@ -744,23 +744,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         p = mm32bf(f, Sm, p);
         return mm32bf(f, Sh, p);
       };
-      // operands of round r, read in round r - 1: Q_r raw, K_(r-1) transposed
-      // (lane (lg, lc): tokens 4 lg .. + 3 of the tile's column lc), gam(r-1)
+      // operands of round r: Q_r raw and gam(r-1), read in round r - 1;
+      // K_(r-1) transposed (lane (lg, lc): tokens 4 lg .. + 3 of the tile's
+      // column lc), formed in round r - 2 from the raw rows read there
       struct Ops {
         uint4 qf;
         uint2 kt[NCT];
         float gl;
       };
       auto fetch = [&](int64_t r, Ops& o) {
-        const int sp_ = (int)((r - 1) & 3);
         o.qf = raw8(sq[r & 3]);
+        o.gl = srec[(r - 1) & 3][kRecGl];
+      };
+      // the raw rows f (this wave's 8 columns per lane) transposed, as bf16:
+      // each half of f is the 16x16x16 A fragment of one tile, E turns it over
+      // exactly, and the high halves of the f32 results are the bf16 values
+      [[maybe_unused]] const uint2 eye = eye16<GDN_BF16>(lg, lc);
+      auto transpose = [&](const uint4& f, uint2* kt) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const KT* c0 = &sk[sp_][4 * lg][32 * cp + 8 * (lc / 4) + 4 * ct + lc % 4];
-          o.kt[ct] = make_uint2((uint32_t)c0[0] | ((uint32_t)c0[KP] << 16),
-                                (uint32_t)c0[2 * KP] | ((uint32_t)c0[3 * KP] << 16));
+          const v4f x = mm16<GDN_BF16>(ct ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y), eye);
+          kt[ct] = make_uint2(
+              __builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u),
+              __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u));
         }
-        o.gl = srec[sp_][kRecGl];
       };
       // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1), then its parts
       auto update = [&](const v4f& cs, const Ops& o) {
@@ -774,7 +781,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         }
         split_state();
       };
-      auto round = [&](int64_t r, const Ops& cur, Ops& nxt) {
+      // round r >= 1: cur holds round r's operands and then takes
+      // K_(r+1)^T for round r + 2, nxt takes round r + 1's Q and gam
+      auto round = [&](int64_t r, Ops& cur, Ops& nxt) {
         __syncthreads();
         const v4f cs = scs[(r - 1) & 1][lane];
         const uint4 kf = raw8(sk[(r + 1) & 3]);
@@ -782,18 +791,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         sp[r & 1][cp][lane] = xst(cur.qf);
         sb[(r + 1) & 1][cp][lane] = xst(kf);
         update(cs, cur);
+        transpose(kf, cur.kt);
       };
       Ops o0, o1;
       split_state();
       __syncthreads();  // blocks 0 and 1 staged
-      sb[0][cp][lane] = xst(raw8(sk[0]));  // A_0
-      fetch(0, o0);                        // Q_0 (its K and gam parts are not used)
+      {
+        const uint4 kf = raw8(sk[0]);
+        sb[0][cp][lane] = xst(kf);  // A_0
+        transpose(kf, o1.kt);       // K_0^T for round 1
+      }
+      fetch(0, o0);  // Q_0 (its gam part is not used)
       __syncthreads();
       {  // round 0: P_0 and B_1 from S_0, no update
         const uint4 kf = raw8(sk[1]);
         fetch(1, o1);
         sp[0][cp][lane] = xst(o0.qf);
         sb[1][cp][lane] = xst(kf);
+        transpose(kf, o0.kt);  // K_1^T for round 2
       }
       const int64_t npair = (nblk - 1) / 2;
       for (int64_t p = 0; p < npair; ++p) {
@@ -1148,12 +1163,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   // its previous contents went to LDS, so two whole rounds hide the load
   // latency); it goes to its slot, then takes the loads of block r + 5.
   // Three register sets in turn, the loop unrolled by three.
+  // The two LDS reads go first, the block's LDS writes right behind them,
+  // and the products last: the writes, the longer part, then start at the
+  // barrier instead of after the products.
   auto round = [&](int64_t r, Regs& P) {
     __syncthreads();
     const v4f cs = scs[(r - 1) & 1][lane];
     const float* m = ywave ? &smx[(r + 1) & 3][kL * kL] : &smx[r & 3][2 * kL * kL];
-    const v4f d = mat16(m, cs);
+    const float4 mf = *reinterpret_cast<const float4*>(&m[16 * lc + 4 * lg]);
     restage(P, (int)((r + 2) & 3), r + 5);
+    v4f d = {0.f, 0.f, 0.f, 0.f};
+    d = mfma4(mf.x, cs[0], d);
+    d = mfma4(mf.y, cs[1], d);
+    d = mfma4(mf.z, cs[2], d);
+    d = mfma4(mf.w, cs[3], d);
     if (ywave) sy[(r + 1) & 1][lane] = d;
     else sz[r & 1][lane] = d;
   };
