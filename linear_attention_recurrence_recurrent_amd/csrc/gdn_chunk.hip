@@ -718,8 +718,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       // its row: tile ct keeps S^T row 32 cp + 8 (i / 4) + 4 ct + i % 4 at
       // tile row i.  Its registers are then the B operand of a 16x16x32
       // product whose A operand is 8 consecutive raw elements of a q or k
-      // row, one LDS read.  X S^T runs on the three bf16 parts of S, and the
-      // update on those of Cs, against the transposed raw k.
+      // row, one 16-byte load.  X S^T runs on the three bf16 parts of S, and
+      // the update on those of Cs, against the transposed raw k.  The wave
+      // loads its own q and k slices from global memory (LDS writes, not
+      // reads, bound the staging), four blocks ahead.
       v4f St[NCT];
       const int64_t soff = sbase + (int64_t)(row0 + lc) * kD + 32 * cp + 8 * lg;
 #pragma unroll
@@ -735,26 +737,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         Sm = make_uint4(p0.m, p1.m, p2.m, p3.m);
         Sl = make_uint4(p0.l, p1.l, p2.l, p3.l);
       };
-      auto raw8 = [&](const KT (*x)[KP]) {
-        return *reinterpret_cast<const uint4*>(&x[lc][32 * cp + 8 * lg]);
-      };
       // X S^T over this wave's key columns, the small parts first
       auto xst = [&](const uint4& f) {
         v4f p = mm32bf(f, Sl, v4f{0.f, 0.f, 0.f, 0.f});
         p = mm32bf(f, Sm, p);
         return mm32bf(f, Sh, p);
       };
-      // operands of round r: Q_r raw and gam(r-1), read in round r - 1;
-      // K_(r-1) transposed (lane (lg, lc): tokens 4 lg .. + 3 of the tile's
-      // column lc), formed in round r - 2 from the raw rows read there
-      struct Ops {
-        uint4 qf;
-        uint2 kt[NCT];
-        float gl;
+      // q and k of a block, row lc (rows past the last token repeat it)
+      struct Blk {
+        uint4 q, k;
       };
-      auto fetch = [&](int64_t r, Ops& o) {
-        o.qf = raw8(sq[r & 3]);
-        o.gl = srec[(r - 1) & 3][kRecGl];
+      auto ld = [&](Blk& x, int64_t c) {
+        const int tcc = c == nblk - 1 ? tcl : kL;
+        const int64_t o = bs.qk + (c * kL + (lc < tcc ? lc : tcc - 1)) * bs.qk_ts + 32 * cp + 8 * lg;
+        x.q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + o);
+        x.k = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + o);
+      };
+      // the next loads of a set stay below its last use (the inputs are
+      // read-only: hoisted, they would need new registers and a copy at the
+      // loop edge that waits for them)
+      auto reload = [&](Blk& x, int64_t c) {
+        __builtin_amdgcn_sched_barrier(0);
+        int64_t cn = clampb(c);
+        asm volatile("" : "+s"(cn) : : "memory");
+        ld(x, cn);
       };
       // the raw rows f (this wave's 8 columns per lane) transposed, as bf16:
       // each half of f is the 16x16x16 A fragment of one tile, E turns it over
@@ -769,6 +775,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
               __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u));
         }
       };
+      // operands of round r's update: K_(r-1) transposed (lane (lg, lc):
+      // tokens 4 lg .. + 3 of the tile's column lc), formed in round r - 2,
+      // and gam(r-1), read in round r - 1
+      struct Ops {
+        uint2 kt[NCT];
+        float gl;
+      };
       // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1), then its parts
       auto update = [&](const v4f& cs, const Ops& o) {
         const Bf3 c0 = split_bf3(cs[0], cs[1]), c1 = split_bf3(cs[2], cs[3]);
@@ -781,41 +794,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         }
         split_state();
       };
-      // round r >= 1: cur holds round r's operands and then takes
-      // K_(r+1)^T for round r + 2, nxt takes round r + 1's Q and gam
-      auto round = [&](int64_t r, Ops& cur, Ops& nxt) {
+      // round r >= 1: bq holds block r, bk block r + 1; cur holds round r's
+      // update operands and then takes K_(r+1)^T for round r + 2, nxt takes
+      // gam(r); bq then takes the loads of block r + 4
+      auto round = [&](int64_t r, Ops& cur, Ops& nxt, Blk& bq, const Blk& bk) {
         __syncthreads();
         const v4f cs = scs[(r - 1) & 1][lane];
-        const uint4 kf = raw8(sk[(r + 1) & 3]);
-        fetch(r + 1, nxt);
-        sp[r & 1][cp][lane] = xst(cur.qf);
-        sb[(r + 1) & 1][cp][lane] = xst(kf);
+        nxt.gl = srec[r & 3][kRecGl];
+        sp[r & 1][cp][lane] = xst(bq.q);
+        sb[(r + 1) & 1][cp][lane] = xst(bk.k);
         update(cs, cur);
-        transpose(kf, cur.kt);
+        transpose(bk.k, cur.kt);
+        reload(bq, r + 4);
       };
       Ops o0, o1;
+      Blk b0, b1, b2, b3;
+      ld(b0, 0);
+      ld(b1, clampb(1));
+      ld(b2, clampb(2));
+      ld(b3, clampb(3));
       split_state();
       __syncthreads();  // blocks 0 and 1 staged
-      {
-        const uint4 kf = raw8(sk[0]);
-        sb[0][cp][lane] = xst(kf);  // A_0
-        transpose(kf, o1.kt);       // K_0^T for round 1
-      }
-      fetch(0, o0);  // Q_0 (its gam part is not used)
+      sb[0][cp][lane] = xst(b0.k);  // A_0
+      transpose(b0.k, o1.kt);       // K_0^T for round 1
       __syncthreads();
-      {  // round 0: P_0 and B_1 from S_0, no update
-        const uint4 kf = raw8(sk[1]);
-        fetch(1, o1);
-        sp[0][cp][lane] = xst(o0.qf);
-        sb[1][cp][lane] = xst(kf);
-        transpose(kf, o0.kt);  // K_1^T for round 2
+      // round 0: P_0 and B_1 from S_0, no update
+      o1.gl = srec[0][kRecGl];
+      sp[0][cp][lane] = xst(b0.q);
+      sb[1][cp][lane] = xst(b1.k);
+      transpose(b1.k, o0.kt);  // K_1^T for round 2
+      reload(b0, 4);
+      // rounds in fours (the ring of four sets), then up to three more
+      const int64_t nq = (nblk - 1) / 4, rm = (nblk - 1) % 4;
+      for (int64_t p = 0; p < nq; ++p) {
+        round(4 * p + 1, o1, o0, b1, b2);
+        round(4 * p + 2, o0, o1, b2, b3);
+        round(4 * p + 3, o1, o0, b3, b0);
+        round(4 * p + 4, o0, o1, b0, b1);
       }
-      const int64_t npair = (nblk - 1) / 2;
-      for (int64_t p = 0; p < npair; ++p) {
-        round(1 + 2 * p, o1, o0);
-        round(2 + 2 * p, o0, o1);
-      }
-      if ((nblk - 1) & 1) round(nblk - 1, o1, o0);
+      if (rm >= 1) round(4 * nq + 1, o1, o0, b1, b2);
+      if (rm >= 2) round(4 * nq + 2, o0, o1, b2, b3);
+      if (rm >= 3) round(4 * nq + 3, o1, o0, b3, b0);
       __syncthreads();
       update(scs[(nblk - 1) & 1][lane], ((nblk - 1) & 1) ? o0 : o1);
 #pragma unroll
@@ -1074,9 +1093,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   }
 
   // ---- waves 6 and 7: the staging, and Y (wave 6) or Z (wave 7).  Lane st:
-  // q and k of token st / 8, elements 16 (st % 8) .. + 15; two v values; two
-  // float4 of the record and of M1 M2 N.
+  // q and k of token st / 8, elements 16 (st % 8) .. + 15 (not with bf16
+  // inputs: the state waves load their own); two v values; two float4 of the
+  // record and of M1 M2 N.
   constexpr int NR4 = kRecUsed / 4, NM4 = NM / 4;
+  constexpr bool QK = DT != GDN_BF16;
   struct Regs {
     Raw<DT, 8> k[2], q[2];
     Raw<DT, 2> v;
@@ -1096,10 +1117,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
     const int tcc = c == nblk - 1 ? tcl : kL;  // tokens in block c
     const int64_t t = c * kL + (qtt < tcc ? qtt : tcc - 1);
     const int64_t o = bs.qk + t * bs.qk_ts + qc;
-    P.k[0].load(a.k, o);
-    P.k[1].load(a.k, o + 8);
-    P.q[0].load(a.q, o);
-    P.q[1].load(a.q, o + 8);
+    if constexpr (QK) {
+      P.k[0].load(a.k, o);
+      P.k[1].load(a.k, o + 8);
+      P.q[0].load(a.q, o);
+      P.q[1].load(a.q, o + 8);
+    }
     P.v.load(a.v, bs.v + t * bs.v_ts + row0 + vr);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -1116,10 +1139,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   };
   // each LDS element is written once (the clamped lanes load but do not write)
   auto store = [&](Regs& P, int sl) {
-    pin(P.k[0]);
-    pin(P.k[1]);
-    pin(P.q[0]);
-    pin(P.q[1]);
+    if constexpr (QK) {
+      pin(P.k[0]);
+      pin(P.k[1]);
+      pin(P.q[0]);
+      pin(P.q[1]);
+    }
     pin(P.v);
     pin(P.r[0]);
     pin(P.r[1]);
@@ -1132,7 +1157,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h + 4]) = P.k[h].get4(1);
         *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h]) = P.q[h].get4(0);
         *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h + 4]) = P.q[h].get4(1);
-      } else {
+      } else if constexpr (QK) {
         *reinterpret_cast<uint4*>(&sk[sl][qtt][qc + 8 * h]) =
             make_uint4(P.k[h].w[0], P.k[h].w[1], P.k[h].w[2], P.k[h].w[3]);
         *reinterpret_cast<uint4*>(&sq[sl][qtt][qc + 8 * h]) =
