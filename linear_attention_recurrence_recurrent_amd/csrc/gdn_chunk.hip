@@ -170,7 +170,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     qk_base = (b * T * a.Hk + hk) * kD; qk_ts = (int64_t)a.Hk * kD;
   }
 
-  // rows of q and k: lane (lg, lc) holds row lc, elements [32 lg, 32 lg + 32)
+  // Every load of the wave is issued here, before any of them is used, so
+  // that their latencies overlap (one round trip instead of one per use).
+  // Rows of q and k: lane (lg, lc) holds row lc, elements [32 lg, 32 lg + 32)
   Raw<DT, 8> kr[4], qr[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -182,6 +184,31 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       qr[u].zero();
     }
   }
+  // XB: the key rows of the two blocks before (block 0's where there is
+  // none; those products are replaced by zero below)
+  [[maybe_unused]] Raw<DT, 8> kp1[4], kp2[4];
+  if constexpr (XB) {
+    const int64_t c1 = c > 0 ? c - 1 : 0, c2 = c > 1 ? c - 2 : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kp1[u].load(a.k, qk_base + (c1 * kL + lc) * qk_ts + 32 * lg + 8 * u);
+      kp2[u].load(a.k, qk_base + (c2 * kL + lc) * qk_ts + 32 * lg + 8 * u);
+    }
+  }
+  // gates: lane (lg, lc) loads token lc of value head g0 + lg
+  Raw<GT, 1> l1, b1;
+  bool gld = false;
+  auto gates_load = [&](int g0) {
+    const int g = g0 + lg, hv = hk * a.G + g;
+    gld = g < a.G && lc < tc;
+    if (gld) {
+      const int64_t gi = a.head_major ? (b * a.Hv + hv) * T + t0 + lc
+                                      : (b * T + t0 + lc) * a.Hv + hv;
+      l1.load(a.ld, gi);
+      b1.load(a.beta, gi);
+    }
+  };
+  gates_load(0);
   float ssk = 0.f, ssq = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
@@ -225,20 +252,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     // not exist), row-major: M1 = K_c K_(c-1)^T, M2 = K_c K_(c-2)^T and
     // N = Q_c K_(c-1)^T.  The few-head kernel forms K S^T and Q S^T of a
     // newer state from an older one with them.
-    v4f M1 = {0.f, 0.f, 0.f, 0.f}, M2 = M1, N1 = M1;
-    if (c > 0) {
-      Raw<DT, 8> kp[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kp[u].load(a.k, qk_base + (t0 - kL + lc) * qk_ts + 32 * lg + 8 * u);
-      M1 = gram(kr, kp);
-      N1 = gram(qr, kp);
-    }
-    if (c > 1) {
-      Raw<DT, 8> kp[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kp[u].load(a.k, qk_base + (t0 - 2 * kL + lc) * qk_ts + 32 * lg + 8 * u);
-      M2 = gram(kr, kp);
-    }
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const v4f M1 = c > 0 ? gram(kr, kp1) : zero, N1 = c > 0 ? gram(qr, kp1) : zero;
+    const v4f M2 = c > 1 ? gram(kr, kp2) : zero;
     float* mx = a.mx + task * (3 * kL * kL);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -255,19 +271,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   }
 
   for (int g0 = 0; g0 < a.G; g0 += 4) {
-    // gates: lane (lg, lc) loads token lc of value head g0 + lg
+    if (g0 > 0) gates_load(g0);
     const int g = g0 + lg, hv = hk * a.G + g;
     const bool gv = g < a.G;
-    float al = 1.f, be = 0.f;
-    if (gv && lc < tc) {
-      const int64_t gi = a.head_major ? (b * a.Hv + hv) * T + t0 + lc
-                                      : (b * T + t0 + lc) * a.Hv + hv;
-      Raw<GT, 1> l1, b1;
-      l1.load(a.ld, gi);
-      b1.load(a.beta, gi);
-      al = expf(l1.get(0));
-      be = b1.get(0);
-    }
+    const float al = gld ? expf(l1.get(0)) : 1.f, be = gld ? b1.get(0) : 0.f;
     // decay products of token lc of each 16-lane row's value head: from the
     // block start through lc, and after lc to the block end
     const float gam = row_prefix_prod(al), tail = dpp_or_one<0x101, 0xF>(row_suffix_prod(al));
