@@ -115,6 +115,28 @@ __device__ __forceinline__ Bf3 split_bf3(float x0, float x1) {
              __builtin_amdgcn_perm(t1, t0, 0x07060302u)};
 }
 
+// 16-bit fragments widened on the matrix cores.  With lane (lg, lc) holding
+// X[lc][4 lg .. 4 lg + 3] of a 16 x 16 tile packed (its raw A-operand fragment)
+// and E the identity in the same packing, mm16(E, X) leaves X[lc][4 lg + s] in
+// register s (the f32 A-operand fragment) and mm16(X, E) leaves X[4 lg + s][lc]
+// (the transposed one), exactly.  A product right behind vector work of the
+// same wave issues only once the matrix pipe has drained, so widening with
+// vector instructions between the products cost more than these products do.
+template <int DT>
+__device__ __forceinline__ uint2 eye16(int lg, int lc) {  // the identity, packed as above
+  const uint32_t one = DT == GDN_BF16 ? 0x3F80u : 0x3C00u;
+  uint32_t e[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) e[s] = 4 * lg + s == lc ? one : 0u;
+  return make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+}
+// The bf16 values of four f32 results of mm16(X, E) (bf16 values already),
+// packed two per word
+__device__ __forceinline__ uint2 pack_bf16(const v4f& x) {
+  return make_uint2(__builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u),
+                    __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u));
+}
+
 struct Bases {
   int64_t qk, qk_ts, v, v_ts, g, g_ts;
 };
@@ -356,8 +378,15 @@ template <int DT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void state_kernel(
     StateArgs a) {
   constexpr int NW = 8, NT = NW * kWave, ROWS = kD, NCT = 8;
+  // 16-bit inputs: q and k in LDS as bf16 parts (bf16: the value; f16: its
+  // exact split into two bf16 values), the products on the bf16 matrix cores
+  // against the three exact bf16 parts of the state; f32 inputs: f32 products
+  constexpr bool W16 = DT != GDN_F32;
+  constexpr int NPART = DT == GDN_F16 ? 2 : 1, KP16 = kD + 8;
   __shared__ __align__(16) float sk[kL][kPad];
   __shared__ __align__(16) float sq[kL][kPad];
+  __shared__ __align__(16) uint16_t sk16[NPART][kL][KP16];
+  __shared__ __align__(16) uint16_t sq16[NPART][kL][KP16];
   __shared__ float sv[kL][ROWS];
   __shared__ float sz[2][kL][kD];
   __shared__ __align__(16) float so[2][kL][ROWS];
@@ -426,9 +455,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int e = (tid + i * NT) % 512, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
-      float* dst = which ? &sq[tt][8 * c8] : &sk[tt][8 * c8];
-      *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
-      *reinterpret_cast<float4*>(dst + 4) = P.qk[i].get4(1);
+      if constexpr (DT == GDN_F32) {
+        float* dst = which ? &sq[tt][8 * c8] : &sk[tt][8 * c8];
+        *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
+        *reinterpret_cast<float4*>(dst + 4) = P.qk[i].get4(1);
+      } else if constexpr (DT == GDN_BF16) {
+        uint16_t* dst = which ? &sq16[0][tt][8 * c8] : &sk16[0][tt][8 * c8];
+        *reinterpret_cast<uint4*>(dst) = make_uint4(P.qk[i].w[0], P.qk[i].w[1], P.qk[i].w[2], P.qk[i].w[3]);
+      } else {
+        // an f16 value x is hi + lo exactly: hi its top 8 significant bits
+        // (truncation), lo the other 3 or fewer
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(P.qk[i].w[w] & 0xffffu));
+          const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(P.qk[i].w[w] >> 16));
+          const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+          const uint32_t r0 = __float_as_uint(x0 - __uint_as_float(u0 & 0xffff0000u));
+          const uint32_t r1 = __float_as_uint(x1 - __uint_as_float(u1 & 0xffff0000u));
+          h[w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+          l[w] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
+        }
+        *reinterpret_cast<uint4*>(which ? &sq16[0][tt][8 * c8] : &sk16[0][tt][8 * c8]) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(which ? &sq16[1][tt][8 * c8] : &sk16[1][tt][8 * c8]) = make_uint4(l[0], l[1], l[2], l[3]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NVP; ++i) {
@@ -451,15 +501,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
   };
 
-  // state S^T, this wave's key tiles of its a-tile, in the accumulator layout
+  // state S^T, this wave's key tiles of its a-tile, in the accumulator layout.
+  // 16-bit inputs: the keys in the order that makes lane (lg, lc) hold keys
+  // 32 g + 8 lg .. + 7 of its row in tiles 2 g and 2 g + 1 (tile ct keeps
+  // key 32 (ct / 2) + 8 (i / 4) + 4 (ct % 2) + i % 4 at tile row i): the two
+  // tiles' registers are then the B operand of a 16x16x32 product whose A
+  // operand is 8 consecutive elements of a q or k row.
   v4f St[NCT];
   const int arow = 16 * ai + lc;  // value row of this lane
+  auto key0 = [&](int ct) { return W16 ? 32 * (ct / 2) + 8 * lg + 4 * (ct % 2) : 16 * ct + 4 * lg; };
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
-                                                      16 * ct + 4 * lg);
+    const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD + key0(ct));
     St[ct] = v4f{x.x, x.y, x.z, x.w};
   }
+  [[maybe_unused]] const uint2 eye = eye16<GDN_BF16>(lg, lc);
   float wgt[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) wgt[i] = has_z ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
@@ -511,21 +567,48 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     // K S^T then Q S^T over this wave's key tiles (raw k and q); K S^T first:
     // only it is on the chain to the next block
     v4f pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (W16) {
+      // per group of 32 keys: the three parts of S (small first) against
+      // each part of k and q
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * ct + 4 * lg]);
-      pk = mfma4(kf.x, St[ct][0], pk);
-      pk = mfma4(kf.y, St[ct][1], pk);
-      pk = mfma4(kf.z, St[ct][2], pk);
-      pk = mfma4(kf.w, St[ct][3], pk);
-    }
+      for (int g4 = 0; g4 < NCT / 2; ++g4) {
+        const Bf3 a0 = split_bf3(St[2 * g4][0], St[2 * g4][1]), a1 = split_bf3(St[2 * g4][2], St[2 * g4][3]);
+        const Bf3 b0 = split_bf3(St[2 * g4 + 1][0], St[2 * g4 + 1][1]);
+        const Bf3 b1 = split_bf3(St[2 * g4 + 1][2], St[2 * g4 + 1][3]);
+        const uint4 sh = make_uint4(a0.h, a1.h, b0.h, b1.h), sm = make_uint4(a0.m, a1.m, b0.m, b1.m);
+        const uint4 sl = make_uint4(a0.l, a1.l, b0.l, b1.l);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * ct + 4 * lg]);
-      pq = mfma4(qf.x, St[ct][0], pq);
-      pq = mfma4(qf.y, St[ct][1], pq);
-      pq = mfma4(qf.z, St[ct][2], pq);
-      pq = mfma4(qf.w, St[ct][3], pq);
+        for (int p = 0; p < NPART; ++p) {
+          const uint4 kA = *reinterpret_cast<const uint4*>(&sk16[p][lc][32 * g4 + 8 * lg]);
+          const uint4 qA = *reinterpret_cast<const uint4*>(&sq16[p][lc][32 * g4 + 8 * lg]);
+          pk = mm32bf(kA, sl, pk);
+          pq = mm32bf(qA, sl, pq);
+          pk = mm32bf(kA, sm, pk);
+          pq = mm32bf(qA, sm, pq);
+          pk = mm32bf(kA, sh, pk);
+          pq = mm32bf(qA, sh, pq);
+        }
+        // one group at a time (interleaved, the groups' parts overflow the
+        // 128 registers of four waves per SIMD)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float4 kf = *reinterpret_cast<const float4*>(&sk[lc][16 * ct + 4 * lg]);
+        pk = mfma4(kf.x, St[ct][0], pk);
+        pk = mfma4(kf.y, St[ct][1], pk);
+        pk = mfma4(kf.z, St[ct][2], pk);
+        pk = mfma4(kf.w, St[ct][3], pk);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float4 qf = *reinterpret_cast<const float4*>(&sq[lc][16 * ct + 4 * lg]);
+        pq = mfma4(qf.x, St[ct][0], pq);
+        pq = mfma4(qf.y, St[ct][1], pq);
+        pq = mfma4(qf.z, St[ct][2], pq);
+        pq = mfma4(qf.w, St[ct][3], pq);
+      }
     }
     // C = T (diag(beta) V - diag(beta gam rk) K S^T)  (rows: tokens, columns:
     // this a-tile's value rows)
@@ -548,13 +631,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     v4f cs;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) cs[s2] = cc[s2] * srec[kRecSrs + 4 * lg + s2];
+    if constexpr (W16) {
+      // the parts of Cs against the parts of k, transposed on the matrix
+      // cores (mm16(X, E)); with two parts of k both go into one 16x16x32
+      // product (contraction: 16 tokens x 2 parts, Cs's part given twice)
+      const Bf3 c0 = split_bf3(cs[0], cs[1]), c1 = split_bf3(cs[2], cs[3]);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int kc = 16 * ct + lc;
-      v4f acc = St[ct] * gl;
+      for (int ct = 0; ct < NCT; ++ct) {
+        uint2 kt[NPART];
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(sk[4 * lg + s2][kc], cs[s2], acc);
-      St[ct] = acc;
+        for (int p = 0; p < NPART; ++p)
+          kt[p] = pack_bf16(mm16<GDN_BF16>(*reinterpret_cast<const uint2*>(&sk16[p][lc][key0(ct)]), eye));
+        v4f acc = St[ct] * gl;
+        if constexpr (NPART == 1) {
+          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.l, c1.l), acc);
+          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.m, c1.m), acc);
+          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.h, c1.h), acc);
+        } else {
+          const uint4 ka = make_uint4(kt[0].x, kt[0].y, kt[1].x, kt[1].y);
+          acc = mm32bf(ka, make_uint4(c0.l, c1.l, c0.l, c1.l), acc);
+          acc = mm32bf(ka, make_uint4(c0.m, c1.m, c0.m, c1.m), acc);
+          acc = mm32bf(ka, make_uint4(c0.h, c1.h, c0.h, c1.h), acc);
+        }
+        St[ct] = acc;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int kc = 16 * ct + lc;
+        v4f acc = St[ct] * gl;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(sk[4 * lg + s2][kc], cs[s2], acc);
+        St[ct] = acc;
+      }
     }
     // O = diag(gam rq) Q S^T + Hd C
     {
@@ -589,8 +699,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
-    *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * ct +
-                               4 * lg) = x;
+    *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + key0(ct)) = x;
   }
 }
 
@@ -612,21 +721,6 @@ template <int DT>
 __device__ __forceinline__ float half_hi(uint32_t x) {
   if constexpr (DT == GDN_BF16) return __uint_as_float(x & 0xffff0000u);
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
-}
-// 16-bit fragments widened on the matrix cores.  With lane (lg, lc) holding
-// X[lc][4 lg .. 4 lg + 3] of a 16 x 16 tile packed (its raw A-operand fragment)
-// and E the identity in the same packing, mm16(E, X) leaves X[lc][4 lg + s] in
-// register s (the f32 A-operand fragment) and mm16(X, E) leaves X[4 lg + s][lc]
-// (the transposed one), exactly.  A product right behind vector work of the
-// same wave issues only once the matrix pipe has drained, so widening with
-// vector instructions between the products cost more than these products do.
-template <int DT>
-__device__ __forceinline__ uint2 eye16(int lg, int lc) {  // the identity, packed as above
-  const uint32_t one = DT == GDN_BF16 ? 0x3F80u : 0x3C00u;
-  uint32_t e[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) e[s] = 4 * lg + s == lc ? one : 0u;
-  return make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
 }
 template <int DT>
 __device__ __forceinline__ float4 lds_get4(const LdsElem<DT>* row, int e) {  // e % 4 == 0
