@@ -422,29 +422,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   // into range; the excess is zeroed or dropped when the block is written to
   // LDS), so no branch skips a load.
   auto clamp_t = [&](int tt, int tc) { return tt < tc ? tt : tc - 1; };
+  // addresses: the block's base (uniform) plus a 32-bit offset per lane, so
+  // no 64-bit per-lane address stays live across the loop
   auto chunk_load = [&](Regs& P, int64_t c, int tc) {
     const int64_t t0 = c * kL;
+    const int64_t qkb = bs.qk + t0 * bs.qk_ts, vb = bs.v + t0 * bs.v_ts;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      const int e = (tid + i * NT) % 512, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
-      P.qk[i].load(which ? a.q : a.k, bs.qk + (t0 + clamp_t(tt, tc)) * bs.qk_ts + 8 * c8);
+      const int e = (tid + i * NT) % 512, it = e % 256, tt = it / 16, c8 = it % 16;
+      const int which = __builtin_amdgcn_readfirstlane(e / 256);  // uniform per wave
+      const uint32_t off = (uint32_t)clamp_t(tt, tc) * (uint32_t)bs.qk_ts + 8u * (uint32_t)c8;
+      P.qk[i].load(which ? a.q : a.k, qkb + (int64_t)off);
     }
 #pragma unroll
     for (int i = 0; i < NVP; ++i) {
       const int e = (tid + i * NT) % (kL * ROWS / 2), tt = e / (ROWS / 2), r2 = e % (ROWS / 2);
-      P.v[i].load(a.v, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + 2 * r2);
+      const uint32_t off = (uint32_t)clamp_t(tt, tc) * (uint32_t)bs.v_ts + 2u * (uint32_t)r2;
+      P.v[i].load(a.v, vb + (int64_t)off);
     }
     if (has_z) {
 #pragma unroll
       for (int i = 0; i < NZP; ++i) {
         const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
-        P.z[i].load(a.z, bs.v + (t0 + clamp_t(tt, tc)) * bs.v_ts + 2 * r2);
+        const uint32_t off = (uint32_t)clamp_t(tt, tc) * (uint32_t)bs.v_ts + 2u * (uint32_t)r2;
+        P.z[i].load(a.z, vb + (int64_t)off);
       }
     }
 #pragma unroll
     for (int i = 0; i < NRC; ++i) {
       const int e = tid + i * NT < NR4 ? tid + i * NT : NR4 - 1;
-      P.r[i].load(rec, c * kRec + 4 * e);
+      P.r[i].load(rec, c * kRec + (int64_t)(uint32_t)(4 * e));
     }
   };
   // Every lane also writes every item it loaded (lanes past the item count
@@ -588,9 +595,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
           pk = mm32bf(kA, sh, pk);
           pq = mm32bf(qA, sh, pq);
         }
-        // one group at a time (interleaved, the groups' parts overflow the
-        // 128 registers of four waves per SIMD)
-        __builtin_amdgcn_sched_barrier(0);
+        // one group at a time: the accumulators pass through an empty asm, so
+        // no product of a later group moves above it (interleaved, the
+        // groups' parts overflow the 128 registers of four waves per SIMD)
+        asm volatile("" : "+v"(pk), "+v"(pq));
       }
     } else {
 #pragma unroll
