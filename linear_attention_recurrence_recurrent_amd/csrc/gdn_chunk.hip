@@ -97,9 +97,11 @@ __device__ __forceinline__ v4f mm32bf(uint4 a, uint4 b, v4f c) {
 // significant bits (truncation), the rest x - hi has at most 16 significant
 // bits, its own truncation mid takes 8 of them and lo = x - hi - mid the last
 // 8 or fewer, so lo is a bf16 value as it stands.  Both subtractions are
-// exact.  With bf16 q and k the products against the three parts are exact
-// in f32, so a state product through them is an f32 product up to the order
-// of the sums.  Two values are packed per word, the first in the low half.
+// exact.  (That holds for |x| >= 2^-110; below, lo reaches f32's subnormal
+// range and its high half drops bits under 2^-133.)  With bf16 q and k the
+// products against the three parts are exact in f32, so a state product
+// through them is an f32 product up to the order of the sums.  Two values are
+// packed per word, the first in the low half.
 struct Bf3 {
   uint32_t h, m, l;
 };
