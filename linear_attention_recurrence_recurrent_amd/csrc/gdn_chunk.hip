@@ -787,6 +787,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   __shared__ v4f sb[2][NC][kWave];  // parts of B (of A_0 in the prologue)
   __shared__ v4f sp[2][NC][kWave];  // parts of P
   __shared__ v4f scs[2][kWave];     // C-scaled
+  __shared__ uint2 scp[2][3][kWave];  // its bf16 parts (bf16 inputs): lo, mid, hi
   __shared__ v4f scc[2][kWave];     // C
   __shared__ v4f sy[2][kWave];      // Y
   __shared__ v4f sz[2][kWave];      // Z
@@ -893,15 +894,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         uint2 kt[NCT];
         float gl;
       };
-      // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1), then its parts
-      auto update = [&](const v4f& cs, const Ops& o) {
-        const Bf3 c0 = split_bf3(cs[0], cs[1]), c1 = split_bf3(cs[2], cs[3]);
+      // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1), then its parts; Cs comes
+      // as its three bf16 parts (the chain wave splits it once for all four
+      // state waves)
+      struct CsParts {
+        uint2 l, m, h;
+      };
+      auto cs_parts = [&](int sl) { return CsParts{scp[sl][0][lane], scp[sl][1][lane], scp[sl][2][lane]}; };
+      auto update = [&](const CsParts& c, const Ops& o) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           v4f acc = St[ct] * o.gl;
-          acc = mm16<GDN_BF16>(o.kt[ct], make_uint2(c0.l, c1.l), acc);
-          acc = mm16<GDN_BF16>(o.kt[ct], make_uint2(c0.m, c1.m), acc);
-          St[ct] = mm16<GDN_BF16>(o.kt[ct], make_uint2(c0.h, c1.h), acc);
+          acc = mm16<GDN_BF16>(o.kt[ct], c.l, acc);
+          acc = mm16<GDN_BF16>(o.kt[ct], c.m, acc);
+          St[ct] = mm16<GDN_BF16>(o.kt[ct], c.h, acc);
         }
         split_state();
       };
@@ -910,7 +916,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       // gam(r); bq then takes the loads of block r + 4
       auto round = [&](int64_t r, Ops& cur, Ops& nxt, Blk& bq, const Blk& bk) {
         __syncthreads();
-        const v4f cs = scs[(r - 1) & 1][lane];
+        const CsParts cs = cs_parts((int)((r - 1) & 1));
         nxt.gl = srec[r & 3][kRecGl];
         sp[r & 1][cp][lane] = xst(bq.q);
         sb[(r + 1) & 1][cp][lane] = xst(bk.k);
@@ -947,7 +953,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       if (rm >= 2) round(4 * nq + 2, o0, o1, b2, b3);
       if (rm >= 3) round(4 * nq + 3, o1, o0, b3, b0);
       __syncthreads();
-      update(scs[(nblk - 1) & 1][lane], ((nblk - 1) & 1) ? o0 : o1);
+      update(cs_parts((int)((nblk - 1) & 1)), ((nblk - 1) & 1) ? o0 : o1);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
         *reinterpret_cast<float4*>(a.s_out + soff + 4 * ct) =
@@ -1122,6 +1128,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       for (int i = 0; i < 4; ++i) csp[i] = cc[i] * o.srs[i];
       scs[r & 1][lane] = csp;
       scc[r & 1][lane] = cc;
+      if constexpr (DT == GDN_BF16) {
+        const Bf3 p0 = split_bf3(csp[0], csp[1]), p1 = split_bf3(csp[2], csp[3]);
+        scp[r & 1][0][lane] = make_uint2(p0.l, p1.l);
+        scp[r & 1][1][lane] = make_uint2(p0.m, p1.m);
+        scp[r & 1][2][lane] = make_uint2(p0.h, p1.h);
+      }
     };
     auto m1cs = [&](Cops& o) {  // M1 of the next block times the newest Cs
       v4f d = {0.f, 0.f, 0.f, 0.f};
