@@ -186,6 +186,10 @@ BLOCK_EDGES = [
     (1, 70, 2, 4, "bf16", False),   # 5 blocks, ragged
     (1, 96, 1, 2, "f16", True),     # 6 blocks, exact
     (2, 99, 2, 2, "f32", False),    # 7 blocks, ragged
+    # few heads, long scans: many passes of both loops, ragged ends, both layouts
+    (1, 1030, 2, 4, "bf16", False),  # 65 blocks, the last ragged
+    (1, 1600, 1, 2, "f16", True),    # 100 blocks, head-major
+    (2, 2100, 1, 2, "f32", False),   # 132 blocks, ragged, two batches
 ]
 
 
