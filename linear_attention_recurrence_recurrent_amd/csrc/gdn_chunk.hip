@@ -26,14 +26,21 @@
 //                taken one block ahead, off the sequential chain): P = K S^T
 //                and Q S^T, C = T (diag(beta) V - diag(beta gam rk) P),
 //                O = diag(gam rq) Q S^T + Hd C and the rank-16 update of S^T,
-//                all as v_mfma_f32_16x16x4f32 on raw q and k with the norms
-//                folded into per-token scales.
+//                on raw q and k with the norms folded into per-token scales.
+//                With f32 inputs these are v_mfma_f32_16x16x4f32 products.
+//                With 16-bit inputs the products with the f32 state run on
+//                the bf16 matrix cores over exact bf16 parts: the state and
+//                Cs as three parts each, f16 q and k as two (split_bf3
+//                below), so every term is an exact product in f32 and the
+//                sums differ from f32 products only in their order (the
+//                few-head kernel does this for bf16 inputs).
 // The sequential chain then holds only the products with S.  S^T stays in the
 // accumulator layout for the whole time axis: lane l, register r of a 16 x 16
 // tile holds S^T[4(l/16) + r][l%16] (key row within the tile, value column),
 // which is also a valid B operand of the next product when the contraction
-// index is taken in the matching order.  Decays are products (never
-// quotients), so alpha = 0 needs no special case.
+// index is taken in the matching order (the kernels with bf16 parts take a
+// tile's keys in a permuted order, stated where they do).  Decays are
+// products (never quotients), so alpha = 0 needs no special case.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -761,19 +768,21 @@ __device__ __forceinline__ float lds_get(const LdsElem<DT>* row, int e) {
 //   Q_r S_r^T = gam(r-1) P_r + N_r Cs_(r-1),
 // gam(c) = gam_15 of block c, M1, M2, N the prep's 16 x 16 products of raw
 // rows.  Round r, after one workgroup barrier:
-//   waves 0-3 (state, two key tiles each): their parts of P_r and B_(r+1),
-//     then S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1);
+//   waves 0-3 (state, 32 keys each): their parts of P_r and B_(r+1), then
+//     S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1) (bf16 inputs: on the bf16
+//     parts of S and Cs, with their own q and k loaded four blocks ahead);
 //   wave 4 (chain): C_r from the B_r parts, Y_r and its own Cs_(r-1), then
-//     M1_(r+1) Cs_r for the next round;
+//     M1_(r+1) Cs_r for the next round (and Cs_r's bf16 parts);
 //   wave 5: O and y of block r - 1;
 //   wave 6: Y_(r+1) = M2_(r+1) Cs_(r-1);  wave 7: Z_r = N_r Cs_(r-1);
-//   waves 6-7: block r + 2 into a four-slot LDS ring, the loads of block
+//   waves 6-7: block r + 2 into a four-slot LDS ring (v, the record, M1 M2
+//     N, and q and k unless the state waves load them), the loads of block
 //     r + 5 (three register sets).
 // Every operand a wave needs from LDS is read at the start of the round
 // before it or right after its own barrier, so each role issues its matrix
-// products back to back; a round is bounded by the 24-32 products per SIMD.
-// A prologue round forms A_0 = K_0 S_0^T; the last round finishes the state
-// and O.  Each role runs its own loop with the same barriers.
+// products back to back.  A prologue round forms A_0 = K_0 S_0^T; the last
+// round finishes the state and O.  Each role runs its own loop with the same
+// barriers.
 template <int DT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void rows_la_kernel(
     StateArgs a) {
