@@ -173,6 +173,33 @@ def bench_decode(args, torch):
     log("decode: %.3f ms per 100-step chain, %.1f us per launch, state %.1f GB/s (a device copy "
         "of the same bytes: %.1f GB/s)" % (ms_per_chain, launch_s * 1e6, value, copy_gbs))
 
+    # the same chain with the state double-buffered (each step reads one buffer
+    # and writes the other, s_out of a step is s0 of the next): the same bytes,
+    # no read and write of the same lines within a launch
+    state_b = torch.empty_like(state)
+    calls_db = [Launcher("gdn_recurrent_step", desc,
+                         [st["q"], st["k"], st["v"], st["log_decay"], st["beta"],
+                          state if i % 2 == 0 else state_b, st["z"], w, y,
+                          state_b if i % 2 == 0 else state], stream.cuda_stream)
+                for i, (st, y) in enumerate(zip(d_steps, ys))]
+
+    def chain_db():
+        for c in calls_db:
+            c()
+
+    settle(chain_db, torch, args.settle_ms / 4)
+    e0.record(stream)
+    for _ in range(args.steps):
+        chain_db()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    db_us = e0.elapsed_time(e1) * 1e3 / launches
+    del state_b
+    res["double_buffered"] = {"us_per_step": round(db_us, 2),
+                              "state_gbs": round(state_bytes / (db_us * 1e-6) / 1e9, 1)}
+    log("decode double-buffered: %.1f us per launch, state %.1f GB/s" %
+        (db_us, state_bytes / (db_us * 1e-6) / 1e9))
+
     # ablation: the literal three-pass step on the same chain (3 reads + 1 write of S)
     calls3 = [Launcher("gdn_recurrent_step_three_pass", desc,
                        [st["q"], st["k"], st["v"], st["log_decay"], st["beta"], state, st["z"], w,
@@ -458,6 +485,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": dec["roofline"],
         "ablation_three_pass_decode": dec["ablation"],
+        "decode_double_buffered": dec["double_buffered"],
     }
     out["decode_b1"] = bench_decode_single(args, torch)
     if scan:
