@@ -1098,8 +1098,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
 
   if (wave == NC) {
     // ---- chain wave: C of block r.  K_r S_r^T = gam(r-1) (gam(r-2) sum B_r
-    // + Y_r) + M1_r Cs_(r-1); the last term was formed at the end of round
-    // r - 1, the record of block r read at its start.
+    // + Y_r) + M1_r Cs_(r-1); the last term is formed at the start of round
+    // r, the record of block r read at the start of round r - 1.
     __builtin_amdgcn_s_setprio(3);  // ahead of the state wave on its SIMD
     struct Cops {
       float4 tf, m1;
@@ -1144,7 +1144,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         scp[r & 1][2][lane] = make_uint2(p0.h, p1.h);
       }
     };
-    auto m1cs = [&](Cops& o) {  // M1 of the next block times the newest Cs
+    auto m1cs = [&](Cops& o) {  // M1 of o's block times the newest Cs (the one before)
       v4f d = {0.f, 0.f, 0.f, 0.f};
       d = mfma4(o.m1.x, csp[0], d);
       d = mfma4(o.m1.y, csp[1], d);
@@ -1156,13 +1156,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       const int ab = (int)(r & 1);
       return (sb[ab][0][lane] + sb[ab][1][lane]) + (sb[ab][2][lane] + sb[ab][3][lane]);
     };
-    auto round = [&](int64_t r, const Cops& cur, Cops& nxt) {
+    // M1_r Cs_(r-1) goes right after the barrier, in the shadow of the
+    // round's LDS reads, rather than in front of the barrier
+    auto round = [&](int64_t r, Cops& cur, Cops& nxt) {
       __syncthreads();
       const v4f bsum = bparts(r);
       const v4f y = sy[r & 1][lane];
       fetch(r + 1, nxt, srec[r & 3][kRecGl], srec[(r - 1) & 3][kRecGl]);
+      m1cs(cur);
       step(r, cur, bsum, y);
-      m1cs(nxt);
     };
     Cops c0, c1;
     __syncthreads();  // blocks 0 and 1 staged
@@ -1173,7 +1175,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       const v4f bsum = bparts(0);
       fetch(1, c1, srec[0][kRecGl], 1.f);
       step(0, c0, bsum, v4f{0.f, 0.f, 0.f, 0.f});
-      m1cs(c1);
     }
     const int64_t npair = (nblk - 1) / 2;
     for (int64_t p = 0; p < npair; ++p) {
