@@ -446,7 +446,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (each (batch, "
-              "value head) pair is independent; see the sharding note in DESIGN.md)",
+              "value head) pair is independent, so several GPUs would each run their share of the heads)",
               file=sys.stderr)
         sys.exit(2)
     import torch
