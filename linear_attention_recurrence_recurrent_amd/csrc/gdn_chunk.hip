@@ -532,6 +532,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     St[ct] = v4f{x.x, x.y, x.z, x.w};
   }
   [[maybe_unused]] const uint2 eye = eye16<GDN_BF16>(lg, lc);
+  // 16-bit inputs: the decay is applied lazily, the state being gsc * St
+  // (gsc uniform; St rescaled and gsc reset to 1 only when gsc would drop
+  // under 2^-80, a zero decay included), so each block scales the four
+  // values of K S^T and Q S^T and Cs instead of the 32 of St
+  float gsc = 1.f;
   float wgt[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) wgt[i] = has_z ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
@@ -627,6 +632,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
         pq = mfma4(qf.w, St[ct][3], pq);
       }
     }
+    if constexpr (W16) {
+      pk *= gsc;
+      pq *= gsc;
+    }
     // C = T (diag(beta) V - diag(beta gam rk) K S^T)  (rows: tokens, columns:
     // this a-tile's value rows)
     v4f yv;
@@ -646,8 +655,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     // (4 products per lane) rather than on K (4 per key tile)
     const float gl = srec[kRecGl];
     v4f cs;
+    if constexpr (W16) {
+      // S' = gl S + K^T Cs with S = gsc St: St' = St + K^T (Cs / g) and
+      // gsc' = g for g = gl gsc, or (g under 2^-80) St' = g St + K^T Cs and
+      // gsc' = 1
+      const float g = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gl))) * gsc;
+      float cscale;
+      if (g < 0x1p-80f) {
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) cs[s2] = cc[s2] * srec[kRecSrs + 4 * lg + s2];
+        for (int ct = 0; ct < NCT; ++ct) St[ct] *= g;
+        gsc = 1.f;
+        cscale = 1.f;
+      } else {
+        gsc = g;
+        cscale = __builtin_amdgcn_rcpf(g);  // 1 ulp
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) cs[s2] = cc[s2] * (srec[kRecSrs + 4 * lg + s2] * cscale);
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) cs[s2] = cc[s2] * srec[kRecSrs + 4 * lg + s2];
+    }
     if constexpr (W16) {
       // the parts of Cs against the parts of k, transposed on the matrix
       // cores (mm16(X, E)); with two parts of k both go into one 16x16x32
@@ -659,7 +687,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
 #pragma unroll
         for (int p = 0; p < NPART; ++p)
           kt[p] = pack_bf16(mm16<GDN_BF16>(*reinterpret_cast<const uint2*>(&sk16[p][lc][key0(ct)]), eye));
-        v4f acc = St[ct] * gl;
+        v4f acc = St[ct];
         if constexpr (NPART == 1) {
           acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.l, c1.l), acc);
           acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.m, c1.m), acc);
@@ -715,6 +743,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
+    if constexpr (W16) St[ct] *= gsc;
     float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
     *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + key0(ct)) = x;
   }

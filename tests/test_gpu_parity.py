@@ -302,6 +302,10 @@ MIXED = [
     (16, 40, 8, 32, 128, "f32", False),  # whole-head workgroups, fused norm
     (2, 90, 2, 4, 64, "f16", False),     # D=64 row split
     (8, 70, 16, 32, 64, "f32", True),    # D=64 whole-head
+    # 256 heads with 16-bit inputs: the block form's many-head kernel applies the decay lazily
+    # and rescales its state when the product of decays falls under 2^-80 or to zero
+    (8, 100, 16, 32, 128, "bf16", True),
+    (8, 100, 16, 32, 128, "f16", False),
 ]
 
 
