@@ -240,22 +240,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
   };
   gates_load(0);
+  // squared norms of row lc (16-bit inputs: below, from the products)
   float ssk = 0.f, ssq = 0.f;
+  if constexpr (DT == GDN_F32) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ssk = fmaf(kr[u].get(e), kr[u].get(e), ssk);
-      ssq = fmaf(qr[u].get(e), qr[u].get(e), ssq);
-    }
-  ssk += __shfl_xor(ssk, 16);
-  ssk += __shfl_xor(ssk, 32);
-  ssq += __shfl_xor(ssq, 16);
-  ssq += __shfl_xor(ssq, 32);
-  const bool l2 = (a.flags & GDN_FOLD_QK_L2NORM) != 0;
-  float rk = rsqrtf(l2 ? ssk + a.qk_eps : 1.f);          // of row lc
-  float rq = rsqrtf(l2 ? ssq + a.qk_eps : 1.f) * a.qscale;
-  if (lc >= tc) rk = rq = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        ssk = fmaf(kr[u].get(e), kr[u].get(e), ssk);
+        ssq = fmaf(qr[u].get(e), qr[u].get(e), ssq);
+      }
+    ssk += __shfl_xor(ssk, 16);
+    ssk += __shfl_xor(ssk, 32);
+    ssq += __shfl_xor(ssq, 16);
+    ssq += __shfl_xor(ssq, 32);
+  }
 
   // X Y^T of 16 raw rows each on the matrix cores; lane (lg, lc), register
   // r: entry [4 lg + r][lc].  The contraction runs over the lane's own 32
@@ -278,6 +277,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   };
   // G = K K^T and H = Q K^T (raw)
   const v4f G4 = gram(kr, kr), H4 = gram(qr, kr);
+  if constexpr (DT != GDN_F32) {
+    // 16-bit inputs: the squared norms are the diagonals of K K^T (above) and
+    // Q Q^T (one more product on the otherwise idle matrix cores instead of
+    // 64 widening multiply-adds per lane): entry [lc][lc] sits in register
+    // lc % 4 of lane (lc / 4) * 16 + lc
+    const v4f Q4 = gram(qr, qr);
+    auto diag = [&](const v4f& m) {
+      const int r = lc % 4;
+      const float v = r == 0 ? m[0] : (r == 1 ? m[1] : (r == 2 ? m[2] : m[3]));
+      return __shfl(v, (lc / 4) * 16 + lc);
+    };
+    ssk = diag(G4);
+    ssq = diag(Q4);
+  }
+  const bool l2 = (a.flags & GDN_FOLD_QK_L2NORM) != 0;
+  float rk = rsqrtf(l2 ? ssk + a.qk_eps : 1.f);          // of row lc
+  float rq = rsqrtf(l2 ? ssq + a.qk_eps : 1.f) * a.qscale;
+  if (lc >= tc) rk = rq = 0.f;
   if constexpr (XB) {
     // Products of raw rows across blocks (zero where the earlier block does
     // not exist), row-major: M1 = K_c K_(c-1)^T, M2 = K_c K_(c-2)^T and
