@@ -1,0 +1,127 @@
+"""The block form's algebra, on the host in float64, against the per-token oracle.
+
+Both GPU scan kernels at D = 128 carry the recurrence over blocks of L = 16
+tokens ("Module gdn", section "The fusion": the step is affine in S).  With
+k^, q^ the normalised rows, Dc[i][j] = alpha_(j+1) ... alpha_i (1 on the
+diagonal, 0 above), gam_i = alpha_0 ... alpha_i and S^T the state transposed:
+  (I + Ls) C = diag(beta) V - diag(beta gam) K^ S^T,
+      Ls[i][j] = beta_i (k^_i . k^_j) Dc[i][j] for j < i,
+  O = diag(gam) Q^ S^T + (tril(Q^ K^^T) (.) Dc) C,
+  S^T <- gam_last S^T + (diag(Dc[last][.]) K^)^T C.
+The few-head kernel takes the products with S one block ahead: with S_r the
+state at the start of block r, raw rows K, Q, Cs_c = diag(rk Dc[last][.]) C_c
+and gam(c) the block's gam_last,
+  K_(r+1) S_(r+1)^T = gam(r) (gam(r-1) K_(r+1) S_(r-1)^T + M2 Cs_(r-1)) + M1 Cs_r,
+  Q_r S_r^T         = gam(r-1) Q_r S_(r-1)^T + N Cs_(r-1),
+M1 = K_(r+1) K_r^T, M2 = K_(r+1) K_(r-1)^T, N = Q_r K_(r-1)^T.
+This module runs the block form as written (a different algorithm from the
+oracle's token loop) and checks it against the oracle, and checks the
+lookahead identities on the states it passes through.
+"""
+import numpy as np
+import pytest
+
+from linear_attention_recurrence_recurrent_amd import synth
+from oracle import gdn_oracle as orc
+
+L = 16
+EPS = 1e-6
+
+
+def f64(t):
+    return t.double().numpy() if hasattr(t, "double") else np.asarray(t, dtype=np.float64)
+
+
+def block_scan(q, k, v, log_decay, beta, s0, gam_short=False):
+    """Token-major operands; returns the raw outputs, the final state and, per
+    head, the per-block quantities the lookahead identities use."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    G = Hv // Hk
+    y = np.zeros((B, T, Hv, Dv))
+    s_out = np.zeros((B, Hv, Dv, Dk))
+    blocks = {}
+    for b in range(B):
+        for hv in range(Hv):
+            hk = hv // G
+            St = s0[b, hv].T.copy()  # S^T: keys x values
+            per = []
+            for c0 in range(0, T, L):
+                t = slice(c0, min(c0 + L, T))
+                n = t.stop - t.start
+                K, Q, V = k[b, t, hk], q[b, t, hk], v[b, t, hv]
+                rk = 1.0 / np.sqrt((K * K).sum(1) + EPS)
+                rq = 1.0 / np.sqrt((Q * Q).sum(1) + EPS) / np.sqrt(Dk)
+                Kh, Qh = K * rk[:, None], Q * rq[:, None]
+                a = np.exp(log_decay[b, t, hv])
+                be = beta[b, t, hv]
+                gam = np.cumprod(a)
+                if gam_short:  # a planted mistake: gam_i = alpha_1 .. alpha_i
+                    gam = np.cumprod(np.concatenate([[1.0], a[1:]]))
+                Dc = np.zeros((n, n))
+                for i in range(n):
+                    for j in range(i + 1):
+                        Dc[i, j] = np.prod(a[j + 1:i + 1])
+                Ls = np.tril(be[:, None] * (Kh @ Kh.T) * Dc, -1)
+                Tm = np.linalg.inv(np.eye(n) + Ls)
+                C = Tm @ (be[:, None] * V - (be * gam)[:, None] * (Kh @ St))
+                O = gam[:, None] * (Qh @ St) + (np.tril(Qh @ Kh.T) * Dc) @ C
+                per.append(dict(K=K, Q=Q, St=St.copy(), gl=gam[-1], Cs=(rk * Dc[-1])[:, None] * C))
+                St = gam[-1] * St + (Dc[-1][:, None] * Kh).T @ C
+                y[b, t, hv] = O
+            s_out[b, hv] = St.T
+            blocks[(b, hv)] = per
+    return y, s_out, blocks
+
+
+@pytest.mark.parametrize("T", [16, 70, 96])
+def test_block_form_equals_the_token_recurrence(T):
+    ops = synth.random_operands(2, T, 2, 4, 32, 24, dtype="f32", seed=T)
+    q, k, v, ld, be, s0 = (f64(ops[n]) for n in ("q", "k", "v", "log_decay", "beta", "s0"))
+    y, s, _ = block_scan(q, k, v, ld, be, s0)
+    yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"])
+    np.testing.assert_allclose(y, yr, rtol=0, atol=1e-10 * (1 + np.abs(yr).max()))
+    np.testing.assert_allclose(s, sr, rtol=0, atol=1e-10 * (1 + np.abs(sr).max()))
+
+
+def test_block_form_with_zero_and_unit_decays():
+    ops = synth.random_operands(1, 48, 1, 2, 16, 16, dtype="f32", seed=5)
+    ops["log_decay"][:, 7] = -np.inf   # alpha = 0 inside a block: Dc and gam vanish past it
+    ops["log_decay"][:, 20:36] = 0.0   # a whole block of alpha = 1
+    q, k, v, ld, be, s0 = (f64(ops[n]) for n in ("q", "k", "v", "log_decay", "beta", "s0"))
+    y, s, _ = block_scan(q, k, v, ld, be, s0)
+    yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"])
+    np.testing.assert_allclose(y, yr, rtol=0, atol=1e-10 * (1 + np.abs(yr).max()))
+    np.testing.assert_allclose(s, sr, rtol=0, atol=1e-10 * (1 + np.abs(sr).max()))
+
+
+def test_one_block_lookahead_identities():
+    ops = synth.random_operands(1, 112, 2, 4, 32, 32, dtype="f32", seed=7)
+    q, k, v, ld, be, s0 = (f64(ops[n]) for n in ("q", "k", "v", "log_decay", "beta", "s0"))
+    _, _, blocks = block_scan(q, k, v, ld, be, s0)
+    for per in blocks.values():
+        for r in range(1, len(per) - 1):
+            P, Cur, Nx = per[r - 1], per[r], per[r + 1]
+            # K_(r+1) S_(r+1)^T from S_(r-1): the state after block r is the start of r + 1
+            s_next = Cur["gl"] * Cur["St"] + Cur["K"].T @ Cur["Cs"]
+            lhs = Nx["K"] @ s_next
+            M1, M2 = Nx["K"] @ Cur["K"].T, Nx["K"] @ P["K"].T
+            rhs = Cur["gl"] * (P["gl"] * (Nx["K"] @ P["St"]) + M2 @ P["Cs"]) + M1 @ Cur["Cs"]
+            np.testing.assert_allclose(lhs, rhs, rtol=1e-10, atol=1e-10)
+            # Q_r S_r^T from S_(r-1)
+            N = Cur["Q"] @ P["K"].T
+            np.testing.assert_allclose(Cur["Q"] @ Cur["St"],
+                                       P["gl"] * (Cur["Q"] @ P["St"]) + N @ P["Cs"],
+                                       rtol=1e-10, atol=1e-10)
+            # and the state update in raw rows: S_(r+1)^T = gam(r) S_r^T + K_r^T Cs_r
+            np.testing.assert_allclose(Nx["St"], s_next, rtol=1e-12, atol=1e-12)
+
+
+def test_a_wrong_decay_index_fails():
+    """The check has teeth: a block form that takes gam_i = alpha_1 .. alpha_i
+    (one decay short) no longer matches the oracle."""
+    ops = synth.random_operands(1, 32, 1, 1, 16, 16, dtype="f32", seed=9)
+    q, k, v, ld, be, s0 = (f64(ops[n]) for n in ("q", "k", "v", "log_decay", "beta", "s0"))
+    y, s, _ = block_scan(q, k, v, ld, be, s0, gam_short=True)
+    yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"])
+    assert np.abs(y - yr).max() > 1e-3 * (1 + np.abs(yr).max())
