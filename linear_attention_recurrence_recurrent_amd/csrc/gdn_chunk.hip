@@ -867,16 +867,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
   auto clampb = [&](int64_t c) { return c < nblk ? c : nblk - 1; };
   const int tcl = tc_of(nblk - 1);
-  // M x (16 x 16, row-major in LDS) times a 16 x 16 in the accumulator layout
-  auto mat16 = [&](const float* m, const v4f& x) {
-    const float4 f = *reinterpret_cast<const float4*>(&m[16 * lc + 4 * lg]);
-    v4f d = {0.f, 0.f, 0.f, 0.f};
-    d = mfma4(f.x, x[0], d);
-    d = mfma4(f.y, x[1], d);
-    d = mfma4(f.z, x[2], d);
-    d = mfma4(f.w, x[3], d);
-    return d;
-  };
 
   if constexpr (DT == GDN_BF16) {
     if (wave < NC) {
