@@ -85,7 +85,9 @@ typedef enum gdn_status {
  * units for every head dim; at Dk == Dv == 128 the block form runs 16 tokens
  * at a time as dense products on the matrix cores (the step is affine in S,
  * "Module gdn" page, "The fusion").  Both give the same results up to
- * rounding.  Without either flag the block form runs at Dk == Dv == 128 and
+ * rounding: with f16/bf16 q and k the block form multiplies the f32 state
+ * on the bf16 matrix cores through exact bf16 parts of its operands, each
+ * term an exact f32 product, so its accuracy is that of f32 arithmetic.  Without either flag the block form runs at Dk == Dv == 128 and
  * the token-by-token form otherwise; with both flags, or GDN_SCAN_BLOCK at
  * another head dim, the call is rejected (GDN_EINVAL / GDN_EUNSUPPORTED).
  * The block form's workspace holds one 2560-byte record per value head and
