@@ -13,7 +13,9 @@ and the head-major scan B=16 T=1024 (f16), in tokens/s and algorithmic
 TFLOP/s (7 * D * D flops per head-token) against the FP32 peak (157.3 TFLOP/s,
 the same for the vector units and for dense FP32 matrix products): the block
 form (the default at D = 128) runs on the matrix cores ("bound": "mfma"), the
-token-by-token form on the vector units ("alu").
+token-by-token form on the vector units ("alu").  With bf16/f16 operands the
+block form multiplies the f32 state on the bf16 matrix cores through exact
+bf16 parts (field "products"): f32 accuracy, counted in the method's f32 flops.
 
 ``roofline`` is for the decode kernel: algorithmic bytes per launch over its
 average launch time (HIP events on the launch stream over the timed region),
@@ -295,10 +297,14 @@ def bench_scan(idx, args, torch):
     tflops = flops / (ms * 1e-3) / 1e12
     tok = wl.B * wl.T / (ms * 1e-3)
     log("scan %d: %.1f us per call, %.2f M tok/s, %.1f TFLOP/s" % (idx, ms * 1e3, tok / 1e6, tflops))
+    products = ("f32 arithmetic; the products with the f32 state on the bf16 matrix cores over "
+                "exact bf16 parts (state 3, f16 q/k 2), each term an exact f32 product"
+                if form == "block" and (wl.dtype == "bf16" or (wl.dtype == "f16" and wl.B * wl.Hv >= 256))
+                else "f32")
     return {"workload": wl.name, "us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(tok, 1),
             "tflops": round(tflops, 2), "peak_tflops": FP32_PEAK_TFLOPS,
             "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "bound": bound, "form": form,
-            "algorithmic_flops_per_call": flops}
+            "algorithmic_flops_per_call": flops, "products": products}
 
 
 def bench_gates(args, torch):
