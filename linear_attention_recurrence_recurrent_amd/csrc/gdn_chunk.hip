@@ -176,6 +176,9 @@ struct PrepArgs {
   uint32_t flags;
   float qk_eps, qscale;
   float* mx;  // null, or [B][Hk][nblk][3][16][16]: K_c K_(c-1)^T, K_c K_(c-2)^T, Q_c K_(c-1)^T (raw)
+  // null, or (f16 inputs, few heads) [B][Hk][nblk][4][16][128] bf16: the
+  // exact parts of the raw rows, q hi, q lo, k hi, k lo
+  uint16_t* qkp;
 };
 
 // One wave per (batch, key head, block): K K^T and Q K^T once, then the
@@ -310,6 +313,31 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       mx[kL * kL + 16 * (4 * lg + r) + lc] = M2[r];
       mx[2 * kL * kL + 16 * (4 * lg + r) + lc] = N1[r];
     }
+    if constexpr (DT == GDN_F16) {
+      // the exact bf16 parts of the raw rows for the few-head kernel: an f16
+      // value x is hi + lo, hi its top 8 significant bits (truncation), lo
+      // the other 3 or fewer; rows past the last token are zero
+      uint16_t* pp = a.qkp + task * (4 * kL * kD) + lc * kD + 32 * lg;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const Raw<DT, 8>& rw = x ? kr[u] : qr[u];
+          uint32_t h[4], l[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(rw.w[w] & 0xffffu));
+            const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(rw.w[w] >> 16));
+            const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+            const uint32_t r0 = __float_as_uint(x0 - __uint_as_float(u0 & 0xffff0000u));
+            const uint32_t r1 = __float_as_uint(x1 - __uint_as_float(u1 & 0xffff0000u));
+            h[w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+            l[w] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
+          }
+          *reinterpret_cast<uint4*>(pp + (2 * x) * kL * kD + 8 * u) = make_uint4(h[0], h[1], h[2], h[3]);
+          *reinterpret_cast<uint4*>(pp + (2 * x + 1) * kL * kD + 8 * u) = make_uint4(l[0], l[1], l[2], l[3]);
+        }
+    }
   }
   float rki[4], rqi[4];  // norms of the lane's rows i = 4 lg + r
 #pragma unroll
@@ -394,6 +422,7 @@ struct StateArgs {
   int Hk, Hv, G, nrb, head_major;
   float norm_eps;
   const float* mx;  // the prep's K_c K_(c-1)^T blocks (lookahead kernel only)
+  const uint16_t* qkp;  // the prep's bf16 parts of q and k (f16 inputs, lookahead kernel)
 };
 
 // The many-head shape: one workgroup per value head, its 8 waves one a-tile
@@ -794,10 +823,6 @@ __device__ __forceinline__ float4 lds_get4(const LdsElem<DT>* row, int e) {  // 
     return make_float4(half_lo<DT>(u.x), half_hi<DT>(u.x), half_lo<DT>(u.y), half_hi<DT>(u.y));
   }
 }
-// the raw 16-bit fragment: 4 elements of a row, packed
-__device__ __forceinline__ uint2 lds_raw16(const uint16_t* row, int e) {  // e % 4 == 0
-  return *reinterpret_cast<const uint2*>(row + e);
-}
 template <int DT>
 __device__ __forceinline__ float lds_get(const LdsElem<DT>* row, int e) {
   if constexpr (DT == GDN_F32) return row[e];
@@ -842,7 +867,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   __shared__ v4f sb[2][NC][kWave];  // parts of B (of A_0 in the prologue)
   __shared__ v4f sp[2][NC][kWave];  // parts of P
   __shared__ v4f scs[2][kWave];     // C-scaled
-  __shared__ uint2 scp[2][3][kWave];  // its bf16 parts (bf16 inputs): lo, mid, hi
+  __shared__ uint2 scp[2][3][kWave];  // its bf16 parts (16-bit inputs): lo, mid, hi
   __shared__ v4f scc[2][kWave];     // C
   __shared__ v4f sy[2][kWave];      // Y
   __shared__ v4f sz[2][kWave];      // Z
@@ -868,16 +893,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   auto clampb = [&](int64_t c) { return c < nblk ? c : nblk - 1; };
   const int tcl = tc_of(nblk - 1);
 
-  if constexpr (DT == GDN_BF16) {
+  if constexpr (DT != GDN_F32) {
     if (wave < NC) {
-      // ---- state waves, bf16 inputs.  The wave's 32 key columns go in the
+      // ---- state waves, 16-bit inputs.  The wave's 32 key columns go in the
       // order that makes lane (lg, lc) hold columns 32 cp + 8 lg .. + 7 of
       // its row: tile ct keeps S^T row 32 cp + 8 (i / 4) + 4 ct + i % 4 at
       // tile row i.  Its registers are then the B operand of a 16x16x32
-      // product whose A operand is 8 consecutive raw elements of a q or k
-      // row, one 16-byte load.  X S^T runs on the three bf16 parts of S, and
-      // the update on those of Cs, against the transposed raw k.  The wave
-      // loads its own q and k slices from global memory (LDS writes, not
+      // product whose A operand is 8 consecutive elements of a q or k row
+      // (bf16: raw; f16: its exact hi or lo bf16 part, which the prep
+      // wrote), one 16-byte load.  X S^T runs on the three bf16 parts of S,
+      // and the update on those of Cs, against the transposed k (parts).  The
+      // wave loads its own q and k slices from global memory (LDS writes, not
       // reads, bound the staging), four blocks ahead.
       v4f St[NCT];
       const int64_t soff = sbase + (int64_t)(row0 + lc) * kD + 32 * cp + 8 * lg;
@@ -894,21 +920,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         Sm = make_uint4(p0.m, p1.m, p2.m, p3.m);
         Sl = make_uint4(p0.l, p1.l, p2.l, p3.l);
       };
-      // X S^T over this wave's key columns, the small parts first
-      auto xst = [&](const uint4& f) {
-        v4f p = mm32bf(f, Sl, v4f{0.f, 0.f, 0.f, 0.f});
-        p = mm32bf(f, Sm, p);
-        return mm32bf(f, Sh, p);
-      };
-      // q and k of a block, row lc (rows past the last token repeat it)
+      // q and k of a block, row lc, as NPART bf16 parts: bf16 inputs as they
+      // are (rows past the last token repeat it), f16 inputs as the prep's
+      // hi and lo parts (rows past the last token zero)
+      constexpr int NPART = DT == GDN_F16 ? 2 : 1;
       struct Blk {
-        uint4 q, k;
+        uint4 q[NPART], k[NPART];
       };
+      [[maybe_unused]] const uint16_t* qkp =
+          a.qkp + (b * a.Hk + hk) * nblk * (4 * kL * kD) + lc * kD + 32 * cp + 8 * lg;
       auto ld = [&](Blk& x, int64_t c) {
-        const int tcc = c == nblk - 1 ? tcl : kL;
-        const int64_t o = bs.qk + (c * kL + (lc < tcc ? lc : tcc - 1)) * bs.qk_ts + 32 * cp + 8 * lg;
-        x.q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + o);
-        x.k = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + o);
+        if constexpr (NPART == 1) {
+          const int tcc = c == nblk - 1 ? tcl : kL;
+          const int64_t o = bs.qk + (c * kL + (lc < tcc ? lc : tcc - 1)) * bs.qk_ts + 32 * cp + 8 * lg;
+          x.q[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + o);
+          x.k[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + o);
+        } else {
+          const uint16_t* pc = qkp + c * (4 * kL * kD);
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) {
+            x.q[pt] = *reinterpret_cast<const uint4*>(pc + pt * kL * kD);
+            x.k[pt] = *reinterpret_cast<const uint4*>(pc + (2 + pt) * kL * kD);
+          }
+        }
+      };
+      // X S^T over this wave's key columns (the parts of X), the small parts
+      // of S first
+      auto xst = [&](const uint4* f) {
+        v4f p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pt = NPART - 1; pt >= 0; --pt) {
+          p = mm32bf(f[pt], Sl, p);
+          p = mm32bf(f[pt], Sm, p);
+          p = mm32bf(f[pt], Sh, p);
+        }
+        return p;
       };
       // the next loads of a set stay below its last use (the inputs are
       // read-only: hoisted, they would need new registers and a copy at the
@@ -923,20 +969,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       // each half of f is the 16x16x16 A fragment of one tile, E turns it over
       // exactly, and the high halves of the f32 results are the bf16 values
       [[maybe_unused]] const uint2 eye = eye16<GDN_BF16>(lg, lc);
-      auto transpose = [&](const uint4& f, uint2* kt) {
+      typedef typename std::conditional<NPART == 1, uint2, uint4>::type KtT;
+      auto transpose = [&](const uint4* f, KtT* kt) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const v4f x = mm16<GDN_BF16>(ct ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y), eye);
-          kt[ct] = make_uint2(
-              __builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u),
-              __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u));
-        }
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int pt = 0; pt < NPART; ++pt) {
+            const v4f x = mm16<GDN_BF16>(ct ? make_uint2(f[pt].z, f[pt].w) : make_uint2(f[pt].x, f[pt].y), eye);
+            const uint32_t w0 = __builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u);
+            const uint32_t w1 = __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u);
+            if constexpr (NPART == 1) kt[ct] = make_uint2(w0, w1);
+            else if (pt == 0) { kt[ct].x = w0; kt[ct].y = w1; }
+            else { kt[ct].z = w0; kt[ct].w = w1; }
+          }
       };
       // operands of round r's update: K_(r-1) transposed (lane (lg, lc):
-      // tokens 4 lg .. + 3 of the tile's column lc), formed in round r - 2,
-      // and gam(r-1), read in round r - 1
+      // tokens 4 lg .. + 3 of the tile's column lc; f16: the hi part's four,
+      // then the lo part's), formed in round r - 2, and gam(r-1), read in
+      // round r - 1
       struct Ops {
-        uint2 kt[NCT];
+        KtT kt[NCT];
         float gl;
       };
       // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1), then its parts; Cs comes
@@ -950,9 +1002,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           v4f acc = St[ct] * o.gl;
-          acc = mm16<GDN_BF16>(o.kt[ct], c.l, acc);
-          acc = mm16<GDN_BF16>(o.kt[ct], c.m, acc);
-          St[ct] = mm16<GDN_BF16>(o.kt[ct], c.h, acc);
+          if constexpr (NPART == 1) {
+            acc = mm16<GDN_BF16>(o.kt[ct], c.l, acc);
+            acc = mm16<GDN_BF16>(o.kt[ct], c.m, acc);
+            St[ct] = mm16<GDN_BF16>(o.kt[ct], c.h, acc);
+          } else {
+            // one 16x16x32 product per part of Cs: k's hi and lo parts
+            // against the same four tokens of Cs
+            acc = mm32bf(o.kt[ct], make_uint4(c.l.x, c.l.y, c.l.x, c.l.y), acc);
+            acc = mm32bf(o.kt[ct], make_uint4(c.m.x, c.m.y, c.m.x, c.m.y), acc);
+            St[ct] = mm32bf(o.kt[ct], make_uint4(c.h.x, c.h.y, c.h.x, c.h.y), acc);
+          }
         }
         split_state();
       };
@@ -1006,8 +1066,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       return;
     }
   }
-  if (DT != GDN_BF16 && wave < NC) {
-    // ---- state waves: two key tiles of the 16 rows, accumulator layout
+  if constexpr (DT == GDN_F32) if (wave < NC) {
+    // ---- state waves, f32 inputs: two key tiles of the 16 rows,
+    // accumulator layout
     v4f St[NCT];
     const int arow = row0 + lc;
 #pragma unroll
@@ -1016,26 +1077,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
                                                         16 * (cp * NCT + ct) + 4 * lg);
       St[ct] = v4f{x.x, x.y, x.z, x.w};
     }
-    // Operand fragments of the 16 rows X of a slot (raw q or k) for X S^T:
-    // 16-bit inputs read raw (one 8-byte LDS read per key tile) and widened
-    // on the matrix cores (mm16), f32 read as is
-    constexpr bool MMW = DT != GDN_F32;
-    typedef typename std::conditional<MMW, uint2, float4>::type Frag;
-    [[maybe_unused]] const uint2 eye = eye16<DT>(lg, lc);
+    // Operand fragments of the 16 rows X of a slot (raw q or k) for X S^T
+    typedef float4 Frag;
     auto frag = [&](const KT (*x)[KP], Frag* f) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        if constexpr (MMW) f[ct] = lds_raw16(x[lc], 16 * (cp * NCT + ct) + 4 * lg);
-        else f[ct] = *reinterpret_cast<const float4*>(&x[lc][16 * (cp * NCT + ct) + 4 * lg]);
-      }
+      for (int ct = 0; ct < NCT; ++ct)
+        f[ct] = *reinterpret_cast<const float4*>(&x[lc][16 * (cp * NCT + ct) + 4 * lg]);
     };
-    // the f32 A-operand fragments of frag()
+    // as A-operand fragments
     auto widen = [&](const Frag* f, v4f* w) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        if constexpr (MMW) w[ct] = mm16<DT>(eye, f[ct]);
-        else w[ct] = v4f{f[ct].x, f[ct].y, f[ct].z, f[ct].w};
-      }
+      for (int ct = 0; ct < NCT; ++ct) w[ct] = v4f{f[ct].x, f[ct].y, f[ct].z, f[ct].w};
     };
     // X S^T over this wave's key tiles
     auto xst = [&](const v4f* f) {
@@ -1051,34 +1103,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       return p0 + p1;
     };
     // operands of round r, read in round r - 1 (staged at least a round
-    // before that): Q_r, K_(r-1) (16-bit: its raw fragment, turned into the
-    // update's layout by X E; f32: that layout read directly), gam(r-1)
+    // before that): Q_r, K_(r-1) in the update's layout, gam(r-1)
     struct Ops {
       Frag qf[NCT];
-      Frag kr[NCT];
       float kt[NCT][4];
       float gl;
     };
     auto fetch = [&](int64_t r, Ops& o) {
       const int sp_ = (int)((r - 1) & 3);
       frag(sq[r & 3], o.qf);
-      if constexpr (MMW) {
-        frag(sk[sp_], o.kr);
-      } else {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) o.kt[ct][s2] = sk[sp_][4 * lg + s2][16 * (cp * NCT + ct) + lc];
-      }
+        for (int s2 = 0; s2 < 4; ++s2) o.kt[ct][s2] = sk[sp_][4 * lg + s2][16 * (cp * NCT + ct) + lc];
       o.gl = srec[sp_][kRecGl];
     };
     // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1)
     auto update = [&](const v4f& cs, const Ops& o) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        v4f kt;
-        if constexpr (MMW) kt = mm16<DT>(o.kr[ct], eye);
-        else kt = v4f{o.kt[ct][0], o.kt[ct][1], o.kt[ct][2], o.kt[ct][3]};
+        const v4f kt = v4f{o.kt[ct][0], o.kt[ct][1], o.kt[ct][2], o.kt[ct][3]};
         v4f acc = St[ct] * o.gl;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(kt[s2], cs[s2], acc);
@@ -1173,7 +1217,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       for (int i = 0; i < 4; ++i) csp[i] = cc[i] * o.srs[i];
       scs[r & 1][lane] = csp;
       scc[r & 1][lane] = cc;
-      if constexpr (DT == GDN_BF16) {
+      if constexpr (DT != GDN_F32) {
         const Bf3 p0 = split_bf3(csp[0], csp[1]), p1 = split_bf3(csp[2], csp[3]);
         scp[r & 1][0][lane] = make_uint2(p0.l, p1.l);
         scp[r & 1][1][lane] = make_uint2(p0.m, p1.m);
@@ -1266,7 +1310,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   // inputs: the state waves load their own); two v values; two float4 of the
   // record and of M1 M2 N.
   constexpr int NR4 = kRecUsed / 4, NM4 = NM / 4;
-  constexpr bool QK = DT != GDN_BF16;
+  constexpr bool QK = DT == GDN_F32;
   struct Regs {
     Raw<DT, 8> k[2], q[2];
     Raw<DT, 2> v;
@@ -1463,18 +1507,21 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
   *gated = heads >= kManyHeads;
   const int64_t rec_bytes = block_record_bytes(heads, d.T);
   const int64_t mx_bytes = *gated ? 0 : key_cross_bytes(d.B * d.Hk, d.T);
+  // f16 inputs, few heads: the bf16 parts of q and k (16 KiB per key head and block)
+  const int64_t qkp_bytes = (*gated || d.dtype != GDN_F16) ? 0 : d.B * d.Hk * nblk * 4 * kL * kD * 2;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)(rec_bytes + mx_bytes), st) != hipSuccess) {
+  if (hipMallocAsync(&ws, (size_t)(rec_bytes + mx_bytes + qkp_bytes), st) != hipSuccess) {
     (void)hipGetLastError();
     set_error("gdn_scan: no device memory for the block records");
     return GDN_EDEVICE;
   }
   float* rec = static_cast<float*>(ws);
   float* mx = *gated ? nullptr : rec + rec_bytes / (int64_t)sizeof(float);
+  uint16_t* qkp = qkp_bytes ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rec_bytes + mx_bytes) : nullptr;
   const PrepArgs p{q, k, ld, beta, rec, d.T, nblk, d.B * d.Hk * nblk, (int)d.Hk, (int)d.Hv,
-                   (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d), mx};
+                   (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d), mx, qkp};
   const StateArgs s{q, k, v, z, w, rec, s0, y, s_out, d.T, nblk, (int)d.Hk, (int)d.Hv,
-                    (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps, mx};
+                    (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps, mx, qkp};
   int rc;
   switch (d.dtype) {
     case GDN_F32: rc = launch_dt<GDN_F32>(d, p, s, heads, st); break;
