@@ -299,8 +299,7 @@ def bench_scan(idx, args, torch):
     log("scan %d: %.1f us per call, %.2f M tok/s, %.1f TFLOP/s" % (idx, ms * 1e3, tok / 1e6, tflops))
     products = ("f32 arithmetic; the products with the f32 state on the bf16 matrix cores over "
                 "exact bf16 parts (state 3, f16 q/k 2), each term an exact f32 product"
-                if form == "block" and (wl.dtype == "bf16" or (wl.dtype == "f16" and wl.B * wl.Hv >= 256))
-                else "f32")
+                if form == "block" and wl.dtype in ("bf16", "f16") else "f32")
     return {"workload": wl.name, "us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(tok, 1),
             "tflops": round(tflops, 2), "peak_tflops": FP32_PEAK_TFLOPS,
             "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "bound": bound, "form": form,
