@@ -186,6 +186,7 @@ BLOCK_EDGES = [
     (1, 70, 2, 4, "bf16", False),   # 5 blocks, ragged
     (1, 96, 1, 2, "f16", True),     # 6 blocks, exact
     (2, 99, 2, 2, "f32", False),    # 7 blocks, ragged
+    (2, 83, 2, 6, "f16", False),    # 6 blocks, ragged; three value heads share a key head's bf16 parts
     # few heads, long scans: many passes of both loops, ragged ends, both layouts
     (1, 1030, 2, 4, "bf16", False),  # 65 blocks, the last ragged
     (1, 1600, 1, 2, "f16", True),    # 100 blocks, head-major
