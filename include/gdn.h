@@ -92,9 +92,9 @@ typedef enum gdn_status {
  * another head dim, the call is rejected (GDN_EINVAL / GDN_EUNSUPPORTED).
  * The block form's workspace holds one 2560-byte record per value head and
  * 16-token block, and with fewer than 256 value heads (B * Hv) also 3072
- * bytes per key head and block (f16 q and k: 19456, which adds their bf16
- * parts): B * Hv * ceil(T / 16) * 2560 (+ B * Hk * ceil(T / 16) * 3072,
- * or * 19456 for f16) bytes (GDN_EDEVICE when it cannot be allocated). */
+ * bytes per key head and block: B * Hv * ceil(T / 16) * 2560
+ * (+ B * Hk * ceil(T / 16) * 3072) bytes (GDN_EDEVICE when it cannot be
+ * allocated). */
 #define GDN_SCAN_PER_TOKEN 4u
 #define GDN_SCAN_BLOCK 8u
 

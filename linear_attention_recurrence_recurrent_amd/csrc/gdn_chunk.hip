@@ -176,9 +176,6 @@ struct PrepArgs {
   uint32_t flags;
   float qk_eps, qscale;
   float* mx;  // null, or [B][Hk][nblk][3][16][16]: K_c K_(c-1)^T, K_c K_(c-2)^T, Q_c K_(c-1)^T (raw)
-  // null, or (f16 inputs, few heads) [B][Hk][nblk][4][16][128] bf16: the
-  // exact parts of the raw rows, q hi, q lo, k hi, k lo
-  uint16_t* qkp;
 };
 
 // One wave per (batch, key head, block): K K^T and Q K^T once, then the
@@ -313,31 +310,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       mx[kL * kL + 16 * (4 * lg + r) + lc] = M2[r];
       mx[2 * kL * kL + 16 * (4 * lg + r) + lc] = N1[r];
     }
-    if constexpr (DT == GDN_F16) {
-      // the exact bf16 parts of the raw rows for the few-head kernel: an f16
-      // value x is hi + lo, hi its top 8 significant bits (truncation), lo
-      // the other 3 or fewer; rows past the last token are zero
-      uint16_t* pp = a.qkp + task * (4 * kL * kD) + lc * kD + 32 * lg;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const Raw<DT, 8>& rw = x ? kr[u] : qr[u];
-          uint32_t h[4], l[4];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(rw.w[w] & 0xffffu));
-            const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(rw.w[w] >> 16));
-            const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
-            const uint32_t r0 = __float_as_uint(x0 - __uint_as_float(u0 & 0xffff0000u));
-            const uint32_t r1 = __float_as_uint(x1 - __uint_as_float(u1 & 0xffff0000u));
-            h[w] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-            l[w] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
-          }
-          *reinterpret_cast<uint4*>(pp + (2 * x) * kL * kD + 8 * u) = make_uint4(h[0], h[1], h[2], h[3]);
-          *reinterpret_cast<uint4*>(pp + (2 * x + 1) * kL * kD + 8 * u) = make_uint4(l[0], l[1], l[2], l[3]);
-        }
-    }
   }
   float rki[4], rqi[4];  // norms of the lane's rows i = 4 lg + r
 #pragma unroll
@@ -422,7 +394,6 @@ struct StateArgs {
   int Hk, Hv, G, nrb, head_major;
   float norm_eps;
   const float* mx;  // the prep's K_c K_(c-1)^T blocks (lookahead kernel only)
-  const uint16_t* qkp;  // the prep's bf16 parts of q and k (f16 inputs, lookahead kernel)
 };
 
 // The many-head shape: one workgroup per value head, its 8 waves one a-tile
@@ -920,28 +891,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         Sm = make_uint4(p0.m, p1.m, p2.m, p3.m);
         Sl = make_uint4(p0.l, p1.l, p2.l, p3.l);
       };
-      // q and k of a block, row lc, as NPART bf16 parts: bf16 inputs as they
-      // are (rows past the last token repeat it), f16 inputs as the prep's
-      // hi and lo parts (rows past the last token zero)
-      constexpr int NPART = DT == GDN_F16 ? 2 : 1;
+      // q and k of a block, row lc, raw (rows past the last token repeat it)
       struct Blk {
-        uint4 q[NPART], k[NPART];
+        uint4 q, k;
       };
-      [[maybe_unused]] const uint16_t* qkp =
-          a.qkp + (b * a.Hk + hk) * nblk * (4 * kL * kD) + lc * kD + 32 * cp + 8 * lg;
       auto ld = [&](Blk& x, int64_t c) {
+        const int tcc = c == nblk - 1 ? tcl : kL;
+        const int64_t o = bs.qk + (c * kL + (lc < tcc ? lc : tcc - 1)) * bs.qk_ts + 32 * cp + 8 * lg;
+        x.q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + o);
+        x.k = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + o);
+      };
+      // their NPART bf16 parts: bf16 as it is; an f16 value x as hi + lo, hi
+      // its top 8 significant bits (truncation), lo the other 3 or fewer
+      constexpr int NPART = DT == GDN_F16 ? 2 : 1;
+      auto parts = [&](const uint4& r, uint4* f) {
         if constexpr (NPART == 1) {
-          const int tcc = c == nblk - 1 ? tcl : kL;
-          const int64_t o = bs.qk + (c * kL + (lc < tcc ? lc : tcc - 1)) * bs.qk_ts + 32 * cp + 8 * lg;
-          x.q[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + o);
-          x.k[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + o);
+          f[0] = r;
         } else {
-          const uint16_t* pc = qkp + c * (4 * kL * kD);
+          uint32_t h[4], l[4];
+          const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-          for (int pt = 0; pt < 2; ++pt) {
-            x.q[pt] = *reinterpret_cast<const uint4*>(pc + pt * kL * kD);
-            x.k[pt] = *reinterpret_cast<const uint4*>(pc + (2 + pt) * kL * kD);
+          for (int i = 0; i < 4; ++i) {
+            const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+            const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+            const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+            const uint32_t r0 = __float_as_uint(x0 - __uint_as_float(u0 & 0xffff0000u));
+            const uint32_t r1 = __float_as_uint(x1 - __uint_as_float(u1 & 0xffff0000u));
+            h[i] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+            l[i] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
           }
+          f[0] = make_uint4(h[0], h[1], h[2], h[3]);
+          f[1] = make_uint4(l[0], l[1], l[2], l[3]);
         }
       };
       // X S^T over this wave's key columns (the parts of X), the small parts
@@ -1023,10 +1003,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         __syncthreads();
         const CsParts cs = cs_parts((int)((r - 1) & 1));
         nxt.gl = srec[r & 3][kRecGl];
-        sp[r & 1][cp][lane] = xst(bq.q);
-        sb[(r + 1) & 1][cp][lane] = xst(bk.k);
+        uint4 qp[NPART], kp[NPART];
+        parts(bq.q, qp);
+        parts(bk.k, kp);
+        sp[r & 1][cp][lane] = xst(qp);
+        sb[(r + 1) & 1][cp][lane] = xst(kp);
         update(cs, cur);
-        transpose(bk.k, cur.kt);
+        transpose(kp, cur.kt);
         reload(bq, r + 4);
       };
       Ops o0, o1;
@@ -1037,14 +1020,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       ld(b3, clampb(3));
       split_state();
       __syncthreads();  // blocks 0 and 1 staged
-      sb[0][cp][lane] = xst(b0.k);  // A_0
-      transpose(b0.k, o1.kt);       // K_0^T for round 1
+      uint4 qp[NPART], kp[NPART];
+      parts(b0.k, kp);
+      sb[0][cp][lane] = xst(kp);  // A_0
+      transpose(kp, o1.kt);       // K_0^T for round 1
       __syncthreads();
       // round 0: P_0 and B_1 from S_0, no update
       o1.gl = srec[0][kRecGl];
-      sp[0][cp][lane] = xst(b0.q);
-      sb[1][cp][lane] = xst(b1.k);
-      transpose(b1.k, o0.kt);  // K_1^T for round 2
+      parts(b0.q, qp);
+      sp[0][cp][lane] = xst(qp);
+      parts(b1.k, kp);
+      sb[1][cp][lane] = xst(kp);
+      transpose(kp, o0.kt);  // K_1^T for round 2
       reload(b0, 4);
       // rounds in fours (the ring of four sets), then up to three more
       const int64_t nq = (nblk - 1) / 4, rm = (nblk - 1) % 4;
@@ -1507,21 +1494,18 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
   *gated = heads >= kManyHeads;
   const int64_t rec_bytes = block_record_bytes(heads, d.T);
   const int64_t mx_bytes = *gated ? 0 : key_cross_bytes(d.B * d.Hk, d.T);
-  // f16 inputs, few heads: the bf16 parts of q and k (16 KiB per key head and block)
-  const int64_t qkp_bytes = (*gated || d.dtype != GDN_F16) ? 0 : d.B * d.Hk * nblk * 4 * kL * kD * 2;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)(rec_bytes + mx_bytes + qkp_bytes), st) != hipSuccess) {
+  if (hipMallocAsync(&ws, (size_t)(rec_bytes + mx_bytes), st) != hipSuccess) {
     (void)hipGetLastError();
     set_error("gdn_scan: no device memory for the block records");
     return GDN_EDEVICE;
   }
   float* rec = static_cast<float*>(ws);
   float* mx = *gated ? nullptr : rec + rec_bytes / (int64_t)sizeof(float);
-  uint16_t* qkp = qkp_bytes ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + rec_bytes + mx_bytes) : nullptr;
   const PrepArgs p{q, k, ld, beta, rec, d.T, nblk, d.B * d.Hk * nblk, (int)d.Hk, (int)d.Hv,
-                   (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d), mx, qkp};
+                   (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d), mx};
   const StateArgs s{q, k, v, z, w, rec, s0, y, s_out, d.T, nblk, (int)d.Hk, (int)d.Hv,
-                    (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps, mx, qkp};
+                    (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps, mx};
   int rc;
   switch (d.dtype) {
     case GDN_F32: rc = launch_dt<GDN_F32>(d, p, s, heads, st); break;
