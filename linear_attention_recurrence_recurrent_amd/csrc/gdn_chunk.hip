@@ -871,8 +871,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       // its row: tile ct keeps S^T row 32 cp + 8 (i / 4) + 4 ct + i % 4 at
       // tile row i.  Its registers are then the B operand of a 16x16x32
       // product whose A operand is 8 consecutive elements of a q or k row
-      // (bf16: raw; f16: its exact hi or lo bf16 part, which the prep
-      // wrote), one 16-byte load.  X S^T runs on the three bf16 parts of S,
+      // (bf16: raw; f16: its exact hi or lo bf16 part, split from the raw
+      // row after one 16-byte load).  X S^T runs on the three bf16 parts of S,
       // and the update on those of Cs, against the transposed k (parts).  The
       // wave loads its own q and k slices from global memory (LDS writes, not
       // reads, bound the staging), four blocks ahead.
