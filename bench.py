@@ -96,13 +96,13 @@ def read_counters():
 class Launcher:
     """Pre-marshalled C-ABI call (no per-call Python validation in the timed loop)."""
 
-    def __init__(self, fn_name, desc, tensors, stream):
+    def __init__(self, fn_name, desc, tensors, stream, extra=()):
         from linear_attention_recurrence_recurrent_amd import _native
         self.fn = getattr(_native.lib(), fn_name)
         self.desc = desc
         self.args = [ctypes.byref(desc)] + [
             None if t is None else ctypes.c_void_p(t.data_ptr()) for t in tensors
-        ] + [ctypes.c_void_p(stream)]
+        ] + list(extra) + [ctypes.c_void_p(stream)]
 
     def __call__(self):
         rc = self.fn(*self.args)
@@ -276,8 +276,11 @@ def bench_scan(idx, args, torch):
     dt = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
     desc = gdn._desc(wl.B, wl.T, wl.Hk, wl.Hv, wl.Dk, wl.Dv, wl.head_major, dt, dt, True, True,
                      1e-6, 1e-6, None if args.scan_form == "auto" else args.scan_form)
+    ws_bytes = gdn.scan_workspace_bytes(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # caller-owned workspace
     call = Launcher("gdn_scan", desc, [d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
-                                       d["z"], d["w"], y, s_out], stream.cuda_stream)
+                                       d["z"], d["w"], y, s_out], stream.cuda_stream,
+                    extra=(ctypes.c_void_p(ws.data_ptr()), ctypes.c_uint64(ws_bytes)))
     reps = max(3, args.steps)
     for _ in range(max(1, args.warmup)):
         call()

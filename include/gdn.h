@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
 
@@ -75,7 +75,8 @@ typedef enum gdn_status {
   GDN_EUNSUPPORTED = 5, /* valid, but not covered by the kernels (head dims, T != 1 for a step) */
   GDN_EALIGN = 6,       /* pointer alignment */
   GDN_EALIAS = 7,       /* an output overlaps an operand (other than s_out == s0) */
-  GDN_EDEVICE = 8       /* the HIP runtime reported an error */
+  GDN_EDEVICE = 8,      /* the HIP runtime reported an error */
+  GDN_EWORKSPACE = 9    /* gdn_scan's workspace is missing or smaller than it needs */
 } gdn_status;
 
 /* flags */
@@ -90,11 +91,8 @@ typedef enum gdn_status {
  * term an exact f32 product, so its accuracy is that of f32 arithmetic.  Without either flag the block form runs at Dk == Dv == 128 and
  * the token-by-token form otherwise; with both flags, or GDN_SCAN_BLOCK at
  * another head dim, the call is rejected (GDN_EINVAL / GDN_EUNSUPPORTED).
- * The block form's workspace holds one 2560-byte record per value head and
- * 16-token block, and with fewer than 256 value heads (B * Hv) also 3072
- * bytes per key head and block: B * Hv * ceil(T / 16) * 2560
- * (+ B * Hk * ceil(T / 16) * 3072) bytes (GDN_EDEVICE when it cannot be
- * allocated). */
+ * The block form keeps per-block records in a caller-supplied workspace
+ * (gdn_scan_workspace_size). */
 #define GDN_SCAN_PER_TOKEN 4u
 #define GDN_SCAN_BLOCK 8u
 
@@ -117,9 +115,9 @@ int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const vo
                        const void* log_decay, const void* beta, const float* s0,
                        const void* z, const void* w, float* y, float* s_out, void* stream);
 
-/* The same step in its literal three-pass form ("Module gdn" page, "The
- * fusion": written literally the step is three passes over S -- one for S.k,
- * one for the rank-1 update, one for S.q), as three launches: u = S.k into
+/* The same step without the fusion ("Module gdn" page, "The fusion": the
+ * unfused step visits the state three times, for the product with k, for the
+ * rank-1 update and for the product with q), as three launches: u = S.k into
  * the y buffer (reads S), the update (reads S, writes s_out), o = S.q on the
  * updated state plus the output (reads s_out).  Same arguments and results
  * as gdn_recurrent_step; it exists to measure the fusion's saving (three
@@ -132,15 +130,33 @@ int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* 
                                   const float* s0, const void* z, const void* w, float* y,
                                   float* s_out, void* stream);
 
+/* Bytes of device workspace gdn_scan needs for the descriptor `d`, written to
+ * *bytes.  Zero when the chosen time loop keeps nothing between its kernels
+ * (T <= 1, B == 0, the token-by-token form).  The block form (Dk == Dv ==
+ * 128 unless GDN_SCAN_PER_TOKEN) needs one 2560-byte record per value head
+ * and 16-token block, plus 3072 bytes per key head and block when B * Hv is
+ * below 256 (the few-head kernel's cross-block key products):
+ *     B*Hv*ceil(T/16)*2560  [+ B*Hk*ceil(T/16)*3072].
+ * Validates the descriptor as gdn_check does (pointers aside) and returns
+ * GDN_OK or that status.  Host-only, no device work. */
+int gdn_scan_workspace_size(const gdn_desc* d, uint64_t* bytes);
+
 /* The recurrence over the whole time axis ("gated_delta" page,
  * gated_delta_reference: the recurrence over the time axis returning
  * (output, final_state)).  Any T >= 0; T == 0 copies s0 to s_out (unless
- * they are the same buffer) and writes no y.  The state stays in registers
- * for the whole time axis; s_out receives the state after the last token.
- * The form of the time loop follows GDN_SCAN_PER_TOKEN / GDN_SCAN_BLOCK. */
+ * they are the same buffer) and writes no y.  The state stays on chip for
+ * the whole time axis; s_out receives the state after the last token.
+ * The form of the time loop follows GDN_SCAN_PER_TOKEN / GDN_SCAN_BLOCK.
+ * workspace: caller-owned device memory of at least
+ * gdn_scan_workspace_size() bytes, 256-byte aligned, overlapping no operand
+ * or output, used only by the work this call enqueues (it may be reused or
+ * freed once that work has finished on `stream`).  May be NULL when the size
+ * is 0.  Too small or NULL when needed: GDN_EWORKSPACE; misaligned:
+ * GDN_EALIGN; overlapping: GDN_EALIAS; in each case nothing is enqueued. */
 int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
              const void* log_decay, const void* beta, const float* s0, const void* z,
-             const void* w, float* y, float* s_out, void* stream);
+             const void* w, float* y, float* s_out, void* workspace, uint64_t workspace_bytes,
+             void* stream);
 
 /* Gate producer: both gates from their pre-activations in one launch ("Module
  * gdn" page, QWEN38_KERNELS: the gate kernel computes both gates from one
@@ -179,18 +195,23 @@ int gdn_conv_silu(int64_t B, int64_t T, int64_t C, int32_t W, int32_t dtype, int
                   void* state_out, void* stream);
 
 /* Validation only, no device work: GDN_OK when gdn_scan would accept these
- * arguments, else the status with its short reason in gdn_last_error()
- * ("gated_delta" page, native_gdn_reject_reason: why operands cannot become
- * the fused operator, as a short reason for logging).  Host-only; safe to
- * call on a machine with no GPU. */
+ * arguments (workspace included), else the status with its short reason in
+ * gdn_last_error() ("gated_delta" page, native_gdn_reject_reason: a rejected
+ * operand comes with a short, loggable reason, so the caller can fall back).
+ * Host-only; safe to call on a machine with no GPU. */
 int gdn_check(const gdn_desc* d, const void* q, const void* k, const void* v,
               const void* log_decay, const void* beta, const float* s0, const void* z,
-              const void* w, const float* y, const float* s_out);
+              const void* w, const float* y, const float* s_out, const void* workspace,
+              uint64_t workspace_bytes);
 
-/* Short reason for the last non-OK status returned on this thread ("" if none). */
+/* Short reason for the last non-OK status returned on this thread ("" if
+ * none): the loggable reject reason of the "gated_delta" page,
+ * native_gdn_reject_reason.  The text stays valid until the thread's next
+ * call into the library. */
 const char* gdn_last_error(void);
 
-/* Static name of a gdn_status value. */
+/* Static name of a gdn_status value ("GDN_UNKNOWN" for other values), for
+ * the same logging. */
 const char* gdn_status_str(int status);
 
 /* GDN_ABI_VERSION of the loaded library ("gated_delta" page,

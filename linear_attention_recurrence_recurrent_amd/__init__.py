@@ -20,8 +20,8 @@ from . import _native
 from ._native import (GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GDN_SCAN_BLOCK, GDN_SCAN_PER_TOKEN,
                       GdnDesc)
 
-__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "gates", "conv_silu", "check",
-           "abi_version", "GdnError"]
+__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "scan_workspace_bytes", "gates",
+           "conv_silu", "check", "abi_version", "GdnError"]
 
 _DT = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
        torch.bfloat16: _native.GDN_BF16}
@@ -108,6 +108,45 @@ def _prepare(q, k, v, log_decay, beta, s0, z, w, head_major, T_expected=None):
     return B, T, Hk, Hv, Dk, Dv, dt, gdt
 
 
+def _check_out(t: torch.Tensor, name: str, shape, dev) -> None:
+    """A caller-supplied output must be float32, contiguous, on q's device and
+    of the exact shape the kernels write (the library sizes its writes from
+    the descriptor, not from the tensor)."""
+    if t.dtype != torch.float32:
+        raise GdnError(3, "%s must be float32 (got %s)" % (name, t.dtype))
+    if t.device != dev:
+        raise GdnError(1, "%s is on %s, q on %s" % (name, t.device, dev))
+    if tuple(t.shape) != tuple(shape):
+        raise GdnError(2, "%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise GdnError(1, "%s must be contiguous" % name)
+
+
+def _outputs(q, v, s0, out, state_out, B, Hv, Dv, Dk):
+    if out is not None:
+        _check_out(out, "out", v.shape, q.device)
+    if state_out is not None:
+        _check_out(state_out, "state_out", (B, Hv, Dv, Dk), q.device)
+    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    return y
+
+
+def _raise(rc: int) -> None:
+    reason = _native.last_error()
+    if rc == 8:
+        raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
+    raise GdnError(rc, reason)
+
+
+def scan_workspace_bytes(desc: GdnDesc) -> int:
+    """Device workspace gdn_scan needs for ``desc`` (gdn_scan_workspace_size)."""
+    n = ctypes.c_uint64(0)
+    rc = _native.lib().gdn_scan_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if rc != 0:
+        _raise(rc)
+    return int(n.value)
+
+
 def _call(fn_name, desc, q, k, v, log_decay, beta, s0, z, w, y, s_out):
     L = _native.lib()
     stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -116,10 +155,7 @@ def _call(fn_name, desc, q, k, v, log_decay, beta, s0, z, w, y, s_out):
                                  _ptr(beta), _ptr(s0), _ptr(z), _ptr(w), _ptr(y), _ptr(s_out),
                                  ctypes.c_void_p(stream))
     if rc != 0:
-        reason = _native.last_error()
-        if rc == 8:
-            raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
-        raise GdnError(rc, reason)
+        _raise(rc)
 
 
 def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
@@ -127,8 +163,8 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
          w: Optional[torch.Tensor] = None, *, head_major: bool = False,
          fold_qk_l2norm: bool = True, fold_q_scale: bool = True, qk_eps: float = 1e-6,
          norm_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-         state_out: Optional[torch.Tensor] = None,
-         form: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+         state_out: Optional[torch.Tensor] = None, form: Optional[str] = None,
+         workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Gated DeltaNet recurrence over the time axis; returns (y, final_state).
 
     q, k: [B, T, Hk, D] (head-major: [B, Hk, T, D]); v, z: [B, T, Hv, D]
@@ -137,15 +173,35 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
     final_state is float32 [B, Hv, D, D] (``state_out`` may be ``s0`` for an
     in-place update).  ``form`` picks the time loop: "per_token" (vector units,
     any D), "block" (16 tokens at a time on the matrix cores, D == 128), or
-    None for the library's choice for the shape."""
+    None for the library's choice for the shape.  The block form's workspace
+    (``scan_workspace_bytes``) is allocated here with torch on the current
+    stream unless ``workspace`` (a contiguous uint8 device tensor at least
+    that large) is passed."""
     B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
     if s0 is None:
         s0 = torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=q.device)
-    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    y = _outputs(q, v, s0, out, state_out, B, Hv, Dv, Dk)
     s_out = state_out if state_out is not None else torch.empty_like(s0)
     desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
                  qk_eps, norm_eps, form)
-    _call("gdn_scan", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
+    need = scan_workspace_bytes(desc)
+    ws = None
+    if need:
+        if workspace is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        else:
+            if workspace.dtype != torch.uint8 or workspace.device != q.device or \
+                    not workspace.is_contiguous():
+                raise GdnError(1, "workspace must be a contiguous uint8 tensor on q's device")
+            ws = workspace
+    L = _native.lib()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = L.gdn_scan(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay),
+                        _ptr(beta), _ptr(s0), _ptr(z), _ptr(w), _ptr(y), _ptr(s_out), _ptr(ws),
+                        ws.numel() if ws is not None else 0, ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
     return y, s_out
 
 
@@ -160,7 +216,7 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay:
     B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
     if s0 is None:
         raise GdnError(1, "recurrent_step needs s0")
-    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    y = _outputs(q, v, s0, out, None, B, Hv, Dv, Dk)
     s_out = s0 if inplace else torch.empty_like(s0)
     desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
                  qk_eps, norm_eps)
@@ -178,7 +234,7 @@ def recurrent_step_three_pass(q, k, v, log_decay, beta, s0, z=None, w=None, *,
     B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
     if s0 is None:
         raise GdnError(1, "recurrent_step_three_pass needs s0")
-    y = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    y = _outputs(q, v, s0, out, None, B, Hv, Dv, Dk)
     s_out = s0 if inplace else torch.empty_like(s0)
     desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
                  qk_eps, norm_eps)
@@ -205,10 +261,7 @@ def gates(a: torch.Tensor, b: torch.Tensor, *, decay_scale: float = 1.0,
         rc = L.gdn_gates(a.numel(), _ptr(a), _ptr(b), _dtype_code(a, "a"), float(decay_scale),
                          _ptr(ld), _ptr(be), _DT[odt], ctypes.c_void_p(stream))
     if rc != 0:
-        reason = _native.last_error()
-        if rc == 8:
-            raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
-        raise GdnError(rc, reason)
+        _raise(rc)
     return ld, be
 
 
@@ -248,18 +301,15 @@ def conv_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor
                              _ptr(weight), _ptr(bias), _ptr(state), _ptr(y), _ptr(new_state),
                              ctypes.c_void_p(stream))
     if rc != 0:
-        reason = _native.last_error()
-        if rc == 8:
-            raise RuntimeError("%s: %s" % (_native.STATUS[rc], reason))
-        raise GdnError(rc, reason)
+        _raise(rc)
     return y, new_state
 
 
 def check(desc: GdnDesc, q=None, k=None, v=None, log_decay=None, beta=None, s0=None, z=None,
-          w=None, y=None, s_out=None) -> Tuple[int, str]:
+          w=None, y=None, s_out=None, workspace=None, workspace_bytes=0) -> Tuple[int, str]:
     """Host-only validation (gdn_check) on raw integer addresses; returns (status, reason)."""
     L = _native.lib()
     vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
     rc = L.gdn_check(ctypes.byref(desc), vp(q), vp(k), vp(v), vp(log_decay), vp(beta), vp(s0),
-                     vp(z), vp(w), vp(y), vp(s_out))
+                     vp(z), vp(w), vp(y), vp(s_out), vp(workspace), int(workspace_bytes))
     return rc, (_native.last_error() if rc else "")

@@ -18,11 +18,13 @@ GDN_FOLD_Q_SCALE = 2
 GDN_SCAN_PER_TOKEN = 4
 GDN_SCAN_BLOCK = 8
 STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_ESHAPE", 3: "GDN_EDTYPE", 4: "GDN_EGROUP",
-          5: "GDN_EUNSUPPORTED", 6: "GDN_EALIGN", 7: "GDN_EALIAS", 8: "GDN_EDEVICE"}
+          5: "GDN_EUNSUPPORTED", 6: "GDN_EALIGN", 7: "GDN_EALIAS", 8: "GDN_EDEVICE",
+          9: "GDN_EWORKSPACE"}
+ABI_VERSION = 2
 
 # Every symbol include/gdn.h declares.
-EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan", "gdn_gates",
-           "gdn_conv_silu", "gdn_check",
+EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan",
+           "gdn_scan_workspace_size", "gdn_gates", "gdn_conv_silu", "gdn_check",
            "gdn_last_error", "gdn_status_str", "gdn_abi_version")
 
 
@@ -50,17 +52,22 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp = ctypes.c_void_p
         dp = ctypes.POINTER(GdnDesc)
-        for name in ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan"):
+        for name in ("gdn_recurrent_step", "gdn_recurrent_step_three_pass"):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [dp] + [vp] * 11
+        # (desc, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace, workspace_bytes, stream)
+        L.gdn_scan.restype = ctypes.c_int
+        L.gdn_scan.argtypes = [dp] + [vp] * 11 + [ctypes.c_uint64, vp]
+        L.gdn_scan_workspace_size.restype = ctypes.c_int
+        L.gdn_scan_workspace_size.argtypes = [dp, ctypes.POINTER(ctypes.c_uint64)]
         L.gdn_gates.restype = ctypes.c_int
         L.gdn_gates.argtypes = [ctypes.c_int64, vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
                                 ctypes.c_int32, vp]
         L.gdn_conv_silu.restype = ctypes.c_int
         L.gdn_conv_silu.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int32] * 3 + [vp] * 7
         L.gdn_check.restype = ctypes.c_int
-        L.gdn_check.argtypes = [dp] + [vp] * 10
+        L.gdn_check.argtypes = [dp] + [vp] * 11 + [ctypes.c_uint64]
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
         L.gdn_status_str.restype = ctypes.c_char_p

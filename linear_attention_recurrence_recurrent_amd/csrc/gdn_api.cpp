@@ -10,7 +10,7 @@ extern "C" {
 int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const void* v,
                        const void* log_decay, const void* beta, const float* s0, const void* z,
                        const void* w, float* y, float* s_out, void* stream) {
-  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out, nullptr, 0);
   if (rc != GDN_OK) return rc;
   if (d->T != 1) {
     gdn::set_error("gdn_recurrent_step needs T == 1 (use gdn_scan for a time axis)");
@@ -24,7 +24,7 @@ int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* 
                                   const void* v, const void* log_decay, const void* beta,
                                   const float* s0, const void* z, const void* w, float* y,
                                   float* s_out, void* stream) {
-  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out, nullptr, 0);
   if (rc != GDN_OK) return rc;
   if (d->T != 1) {
     gdn::set_error("gdn_recurrent_step_three_pass needs T == 1");
@@ -36,8 +36,10 @@ int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* 
 
 int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
              const void* log_decay, const void* beta, const float* s0, const void* z,
-             const void* w, float* y, float* s_out, void* stream) {
-  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+             const void* w, float* y, float* s_out, void* workspace, uint64_t workspace_bytes,
+             void* stream) {
+  int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace,
+                      workspace_bytes);
   if (rc != GDN_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d->B == 0) return GDN_OK;
@@ -50,7 +52,7 @@ int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
   }
   if (d->T == 1)  // one token: the decode kernel is the same computation, streamed once
     return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
-  return gdn::launch_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
+  return gdn::launch_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace, stream);
 }
 
 int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -54,9 +55,7 @@ void set_error(const char* msg) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
 }
 
-int check(const gdn_desc* d, const void* q, const void* k, const void* v, const void* log_decay,
-          const void* beta, const float* s0, const void* z, const void* w, const float* y,
-          const float* s_out) {
+int check_desc(const gdn_desc* d) {
   g_last_error[0] = '\0';
   if (!d) return fail(GDN_EINVAL, "null descriptor");
   if (d->B < 0 || d->T < 0) return fail(GDN_ESHAPE, "negative B (%lld) or T (%lld)",
@@ -87,7 +86,7 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
   if ((d->flags & GDN_SCAN_BLOCK) && d->Dk != 128)
     return fail(GDN_EUNSUPPORTED, "the block form needs Dk == Dv == 128");
 
-  // sizes in bytes (with overflow checks)
+  // sizes (with overflow checks)
   int64_t bt, nqk, nv, ng, ns, tmp;
   if (!mul_ok(d->B, d->T, &bt) || !mul_ok(bt, d->Hk, &tmp) || !mul_ok(tmp, d->Dk, &nqk) ||
       !mul_ok(bt, d->Hv, &ng) || !mul_ok(ng, d->Dv, &nv) || !mul_ok(d->B, d->Hv, &tmp) ||
@@ -96,7 +95,37 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
     return fail(GDN_ESHAPE, "operand sizes overflow");
   if (ng >= (int64_t)1 << 31 || nv >= (int64_t)1 << 40)
     return fail(GDN_ESHAPE, "B*T*Hv (%lld) too large for the launch grid", (long long)ng);
+  return GDN_OK;
+}
 
+bool scan_uses_block_form(const gdn_desc& d) {
+  return d.Dk == 128 && d.Dv == 128 && (d.flags & GDN_SCAN_PER_TOKEN) == 0 && d.T >= 2 &&
+         d.B > 0;
+}
+
+int64_t scan_record_bytes(const gdn_desc& d) {
+  if (!scan_uses_block_form(d)) return 0;
+  const int64_t nblk = (d.T + kBlockTokens - 1) / kBlockTokens;
+  return d.B * d.Hv * nblk * kBlockRecordBytes;
+}
+
+int64_t scan_workspace_bytes(const gdn_desc& d) {
+  if (!scan_uses_block_form(d)) return 0;
+  const int64_t nblk = (d.T + kBlockTokens - 1) / kBlockTokens;
+  int64_t bytes = scan_record_bytes(d);
+  if (d.B * d.Hv < kManyHeads) bytes += d.B * d.Hk * nblk * kKeyCrossBytes;
+  return bytes;
+}
+
+int check(const gdn_desc* d, const void* q, const void* k, const void* v, const void* log_decay,
+          const void* beta, const float* s0, const void* z, const void* w, const float* y,
+          const float* s_out, const void* workspace, uint64_t workspace_bytes) {
+  const int rc = check_desc(d);
+  if (rc != GDN_OK) return rc;
+
+  // sizes in bytes (check_desc has ruled out overflow)
+  const int64_t bt = d->B * d->T, nqk = bt * d->Hk * d->Dk, ng = bt * d->Hv, nv = ng * d->Dv;
+  const int64_t ns = d->B * d->Hv * d->Dv * d->Dk;
   const int64_t es = elem_size(d->dtype), ges = elem_size(d->gate_dtype);
   const bool has_tokens = bt > 0;
   const bool has_state = d->B > 0;
@@ -131,6 +160,23 @@ int check(const gdn_desc* d, const void* q, const void* k, const void* v, const 
   if (overlap(ry, rso)) return fail(GDN_EALIAS, "y overlaps s_out");
   if (overlap(rso, rs0) && rso.lo != rs0.lo)
     return fail(GDN_EALIAS, "s_out partially overlaps s0 (only s_out == s0 is allowed)");
+
+  // the block form's workspace
+  const int64_t need = scan_workspace_bytes(*d);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < (uint64_t)need)
+      return fail(GDN_EWORKSPACE,
+                  "gdn_scan needs %lld bytes of workspace for this shape (got %llu%s)",
+                  (long long)need, (unsigned long long)workspace_bytes,
+                  workspace ? "" : ", NULL");
+    if ((uintptr_t)workspace % kWorkspaceAlign)
+      return fail(GDN_EALIGN, "workspace must be %d-byte aligned", (int)kWorkspaceAlign);
+    const Range rws = rng("workspace", workspace, need);
+    for (const Range& r : ins)
+      if (overlap(rws, r)) return fail(GDN_EALIAS, "workspace overlaps %s", r.name);
+    for (const Range* r : {&ry, &rs0, &rso})
+      if (overlap(rws, *r)) return fail(GDN_EALIAS, "workspace overlaps %s", r->name);
+  }
   return GDN_OK;
 }
 
@@ -208,8 +254,18 @@ extern "C" {
 
 int gdn_check(const gdn_desc* d, const void* q, const void* k, const void* v,
               const void* log_decay, const void* beta, const float* s0, const void* z,
-              const void* w, const float* y, const float* s_out) {
-  return gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out);
+              const void* w, const float* y, const float* s_out, const void* workspace,
+              uint64_t workspace_bytes) {
+  return gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace,
+                    workspace_bytes);
+}
+
+int gdn_scan_workspace_size(const gdn_desc* d, uint64_t* bytes) {
+  const int rc = gdn::check_desc(d);
+  if (rc != GDN_OK) return rc;
+  if (!bytes) return fail(GDN_EINVAL, "null size pointer");
+  *bytes = (uint64_t)gdn::scan_workspace_bytes(*d);
+  return GDN_OK;
 }
 
 const char* gdn_last_error(void) { return g_last_error; }
@@ -225,6 +281,7 @@ const char* gdn_status_str(int status) {
     case GDN_EALIGN: return "GDN_EALIGN";
     case GDN_EALIAS: return "GDN_EALIAS";
     case GDN_EDEVICE: return "GDN_EDEVICE";
+    case GDN_EWORKSPACE: return "GDN_EWORKSPACE";
     default: return "GDN_UNKNOWN";
   }
 }

@@ -50,8 +50,7 @@ namespace {
 constexpr int kD = 128;       // head dim handled here
 constexpr int kL = 16;        // tokens per block (the MFMA tile)
 constexpr int kPad = kD + 4;  // LDS row of q or k: rows 16 banks apart for the operand reads
-// from this many value heads on, a workgroup per head fills the chip
-constexpr int64_t kManyHeads = 256;
+// (from kManyHeads value heads on, a workgroup per head fills the chip)
 
 // Block record, per (value head, block), f32; the records of a head are
 // contiguous, kRec floats apart (256-byte aligned).
@@ -1471,50 +1470,33 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
   return device_status("rows_la_kernel launch");
 }
 
-int64_t block_record_bytes(int64_t heads, int64_t T) {
-  return heads * ((T + kL - 1) / kL) * (int64_t)kRec * (int64_t)sizeof(float);
-}
-
-// the prep's cross-block products (few heads only): 3 KiB per key head and block
-int64_t key_cross_bytes(int64_t bk, int64_t T) {
-  return bk * ((T + kL - 1) / kL) * (int64_t)(3 * kL * kL) * (int64_t)sizeof(float);
-}
-
 }  // namespace
 
 // The block-form scan for D == 128; y receives the raw o (the gated norm, when
 // asked for and not fused, runs after it).  Returns whether the gated output
-// was written (fused) through *gated.  The block records live in a
-// stream-ordered allocation released on the same stream after the scan.
+// was written (fused) through *gated.  The block records (and, for few heads,
+// the cross-block key products) live in the caller's workspace, laid out as
+// scan_workspace_bytes() sizes it: records first, then the key products.
 int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const void* v,
                         const void* ld, const void* beta, const float* s0, const void* z,
-                        const void* w, float* y, float* s_out, void* stream, bool* gated) {
+                        const void* w, float* y, float* s_out, void* workspace, void* stream,
+                        bool* gated) {
+  static_assert(kRec * sizeof(float) == kBlockRecordBytes, "record size");
+  static_assert(kL == kBlockTokens, "block length");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t heads = d.B * d.Hv, nblk = (d.T + kL - 1) / kL;
   *gated = heads >= kManyHeads;
-  const int64_t rec_bytes = block_record_bytes(heads, d.T);
-  const int64_t mx_bytes = *gated ? 0 : key_cross_bytes(d.B * d.Hk, d.T);
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)(rec_bytes + mx_bytes), st) != hipSuccess) {
-    (void)hipGetLastError();
-    set_error("gdn_scan: no device memory for the block records");
-    return GDN_EDEVICE;
-  }
-  float* rec = static_cast<float*>(ws);
-  float* mx = *gated ? nullptr : rec + rec_bytes / (int64_t)sizeof(float);
+  float* rec = static_cast<float*>(workspace);
+  float* mx = *gated ? nullptr : rec + scan_record_bytes(d) / (int64_t)sizeof(float);
   const PrepArgs p{q, k, ld, beta, rec, d.T, nblk, d.B * d.Hk * nblk, (int)d.Hk, (int)d.Hv,
                    (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d), mx};
   const StateArgs s{q, k, v, z, w, rec, s0, y, s_out, d.T, nblk, (int)d.Hk, (int)d.Hv,
                     (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps, mx};
-  int rc;
   switch (d.dtype) {
-    case GDN_F32: rc = launch_dt<GDN_F32>(d, p, s, heads, st); break;
-    case GDN_F16: rc = launch_dt<GDN_F16>(d, p, s, heads, st); break;
-    default: rc = launch_dt<GDN_BF16>(d, p, s, heads, st); break;
+    case GDN_F32: return launch_dt<GDN_F32>(d, p, s, heads, st);
+    case GDN_F16: return launch_dt<GDN_F16>(d, p, s, heads, st);
+    default: return launch_dt<GDN_BF16>(d, p, s, heads, st);
   }
-  const hipError_t fe = hipFreeAsync(ws, st);
-  if (rc == GDN_OK && fe != hipSuccess) return device_status("gdn_scan: releasing the block records");
-  return rc;
 }
 
 }  // namespace gdn

@@ -200,8 +200,8 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
 }
 
 // ---------------------------------------------------------------- three-pass form
-// The literal form of the step ("Module gdn" page, "The fusion": written
-// literally it is three passes over S), kept to measure what the fusion saves:
+// The step without the fusion ("Module gdn" page, "The fusion": unfused, the
+// state is visited three times), kept to measure what the fusion saves:
 //   pass 1: u = S.k^            (reads S; u goes to the y buffer)
 //   pass 2: S = alpha*S + beta*(v - alpha*u) k^T   (reads S, writes S)
 //   pass 3: o = S.q^ on the updated S, then the gated norm (reads S)

@@ -5,10 +5,30 @@
 
 namespace gdn {
 
-// Validation behind gdn_check (sets the thread's last error on failure).
+// Layout of the block form's workspace (shared by the validator, which sizes
+// it, and the launcher, which lays it out): a record of kBlockRecordBytes per
+// (value head, 16-token block), then, when fewer than kManyHeads value heads
+// run, kKeyCrossBytes per (key head, block).
+constexpr int64_t kBlockTokens = 16;
+constexpr int64_t kBlockRecordBytes = 2560;
+constexpr int64_t kKeyCrossBytes = 3 * 16 * 16 * 4;
+constexpr int64_t kManyHeads = 256;
+constexpr uintptr_t kWorkspaceAlign = 256;
+
+// Whether gdn_scan runs the block form for this (valid) descriptor.
+bool scan_uses_block_form(const gdn_desc& d);
+// Bytes of the records (first part of the workspace) and in total.
+int64_t scan_record_bytes(const gdn_desc& d);
+int64_t scan_workspace_bytes(const gdn_desc& d);
+
+// Descriptor validation (no pointers); sets the thread's last error on failure.
+int check_desc(const gdn_desc* d);
+
+// Validation behind gdn_check (sets the thread's last error on failure).  The
+// workspace is checked against scan_workspace_bytes(*d).
 int check(const gdn_desc* d, const void* q, const void* k, const void* v, const void* log_decay,
           const void* beta, const float* s0, const void* z, const void* w, const float* y,
-          const float* s_out);
+          const float* s_out, const void* workspace, uint64_t workspace_bytes);
 
 // Validation behind gdn_gates.
 int check_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,
@@ -32,12 +52,14 @@ int launch_step_three_pass(const gdn_desc& d, const void* q, const void* k, cons
                            const void* w, float* y, float* s_out, void* stream);
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
-                float* s_out, void* stream);
-// Block form on the matrix cores, Dk == Dv == 128; *gated reports whether the
+                float* s_out, void* workspace, void* stream);
+// Block form on the matrix cores, Dk == Dv == 128, with its records in
+// `workspace` (scan_workspace_bytes(d) bytes); *gated reports whether the
 // gated norm was applied in the same launch (whole-head workgroups).
 int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const void* v,
                         const void* ld, const void* beta, const float* s0, const void* z,
-                        const void* w, float* y, float* s_out, void* stream, bool* gated);
+                        const void* w, float* y, float* s_out, void* workspace, void* stream,
+                        bool* gated);
 
 int launch_gates(int64_t n, const void* a, const void* b, int in_dtype, float decay_scale,
                  void* log_decay, void* beta, int out_dtype, void* stream);

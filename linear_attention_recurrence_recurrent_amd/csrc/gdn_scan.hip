@@ -606,7 +606,7 @@ int launch_scan_gt(const ScanArgs& a, int gdt, int D, int64_t heads, hipStream_t
 
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
-                float* s_out, void* stream) {
+                float* s_out, void* workspace, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const ScanArgs a{q, k, v, ld, beta, z, w, s0, y, s_out, d.T, (int)d.Hk, (int)d.Hv,
                    (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags,
@@ -614,10 +614,10 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
   const int64_t heads = d.B * d.Hv;
   // the block form at D = 128 (faster there on both the few-head and the
   // many-head shapes) unless the token-by-token form is asked for
-  const bool block = d.Dk == 128 && (d.flags & GDN_SCAN_PER_TOKEN) == 0;
-  if (block) {
+  if (scan_uses_block_form(d)) {
     bool gated = false;
-    int rc = launch_scan_chunked(d, q, k, v, ld, beta, s0, z, w, y, s_out, stream, &gated);
+    int rc = launch_scan_chunked(d, q, k, v, ld, beta, s0, z, w, y, s_out, workspace, stream,
+                                 &gated);
     if (rc != GDN_OK || gated || z == nullptr) return rc;
     const int64_t nvec = heads * d.T;
     const dim3 grid = norm_grid(nvec);

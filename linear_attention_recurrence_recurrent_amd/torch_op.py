@@ -2,9 +2,9 @@
 
 ``gdn::scan`` and ``gdn::recurrent_step`` let torch.export / torch.compile /
 opcheck trace the recurrence.  Their fake kernels state the output contract of
-the "gated_delta" page (gated_delta_fake): y takes the PROMOTED dtype, float32,
-whatever the input dtype, because the recurrence accumulates against a float32
-state; final_state is float32 [B, Hv, D, D].  The real kernels are the HIP
+the "gated_delta" page (gated_delta_fake): y is float32 for every operand dtype
+(the recurrence runs against a float32 state, so the output is widened to it);
+final_state is float32 [B, Hv, D, D].  The real kernels are the HIP
 library's, called through ``linear_attention_recurrence_recurrent_amd.scan`` /
 ``recurrent_step`` (argument marshalling only).
 """

@@ -10,13 +10,14 @@
  * What it computes (the pages, cited by page title and section):
  *   - "Module gdn" (logicaffeine codegen_cuda/gdn), module description: each
  *     value head keeps a D x D memory S; per token u = S.k, then
- *     S = alpha*S + beta*(v - alpha*u) k^T, then o = S.q read from the UPDATED
- *     memory, then o = rmsnorm(o * silu(z)) * GN with the gate applied before
- *     the normalisation.
- *   - Same page, "The fusion": the literal form is three passes over S (one for
- *     S.k, one for the rank-1 update, one for S.q).  This oracle runs exactly
- *     those three passes, on purpose, so that the fused kernels are checked
- *     against the unfused definition.
+ *     S = alpha*S + beta*(v - alpha*u) k^T, then o = S.q taken after that
+ *     update (the memory of this token, not the previous one), then
+ *     o = rmsnorm(o * silu(z)) * GN with the gate multiplied in before the
+ *     normalisation.
+ *   - Same page, "The fusion": unfused, a token visits S three times (the
+ *     product with k, the rank-1 update, the product with q).  This oracle
+ *     makes exactly those three visits, on purpose, so that the fused kernels
+ *     are checked against the unfused definition.
  *   - "gated_delta" (torch-to-nnef op reference), native_gdn_reject_reason: the
  *     fused decode operator folds the q/k L2 norm and the 1/sqrt(head_dim)
  *     scale; l2norm: the L2 normalisation of the last axis uses HF's eps.
@@ -181,7 +182,7 @@ static void run_head(const oracle_job* J, int64_t b, int64_t hv) {
       const double corr = beta * (vt[a] - alpha * u[a]);
       for (int64_t c = 0; c < Dk; ++c) S[a * Dk + c] = alpha * S[a * Dk + c] + corr * kv[c];
     }
-    /* pass 3: o = S.q -- read the updated memory */
+    /* pass 3: o = S.q on the state this token just produced */
     for (int64_t a = 0; a < Dv; ++a) {
       double acc = 0.0;
       for (int64_t c = 0; c < Dk; ++c) acc += S[a * Dk + c] * qv[c];

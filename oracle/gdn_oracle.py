@@ -188,34 +188,3 @@ def conv_silu(x, weight, bias=None, state=None, *, apply_silu: bool = True):
     _load().gdn_oracle_conv(B, T, C, W, int(bool(apply_silu)), _ptr(x), _ptr(weight), _ptr(bias),
                             _ptr(state), _ptr(y), _ptr(st))
     return y, st
-
-
-def select_heads(ops: dict, heads, *, head_major: bool) -> dict:
-    """Restrict operands to a list of (b, hv) value heads for sampled checks.
-
-    Each selected head becomes its own batch entry with Hk = Hv = 1, carrying
-    the key head hv // G it reads (contiguous groups).  Heads are independent
-    through the whole recurrence, so the oracle may compute them one by one."""
-    q = _f64(ops["q"])
-    v = _f64(ops["v"])
-    Hk = q.shape[1] if head_major else q.shape[2]
-    Hv = v.shape[1] if head_major else v.shape[2]
-    G = Hv // Hk
-    out = {}
-    for name in ("q", "k", "v", "z", "log_decay", "beta"):
-        if ops.get(name) is None:
-            continue
-        a = _f64(ops[name])
-        parts = []
-        for (b, hv) in heads:
-            h = hv // G if name in ("q", "k") else hv
-            if head_major:
-                parts.append(a[b:b + 1, h:h + 1])
-            else:
-                parts.append(a[b:b + 1, :, h:h + 1])
-        out[name] = np.concatenate(parts, axis=0)
-    s0 = _f64(ops["s0"])
-    out["s0"] = np.concatenate([s0[b:b + 1, hv:hv + 1] for (b, hv) in heads], axis=0)
-    if ops.get("w") is not None:
-        out["w"] = _f64(ops["w"])
-    return out

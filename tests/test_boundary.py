@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_names():
-    assert abi_version() == 1
+    assert abi_version() == nat.ABI_VERSION == 2
     L = nat.lib()
     for code, name in nat.STATUS.items():
         assert L.gdn_status_str(code).decode() == name
@@ -90,8 +90,11 @@ def test_accepts_valid_arguments():
     ops["s_out"] = ops["s0"]  # exact in-place alias is allowed
     assert check(_good(), **ops)[0] == 0
     assert check(_good(head_major=1, dtype=0, gate_dtype=0, flags=0), **ops)[0] == 0
-    for D in (16, 32, 64, 128, 256):
+    for D in (16, 32, 64, 256):
         assert check(_good(Dk=D, Dv=D), **_ops())[0] == 0
+    # D = 128 runs the block form, which needs its workspace
+    assert check(_good(Dk=128, Dv=128), **_ops(), workspace=BASE + 20 * (1 << 28),
+                 workspace_bytes=1 << 20)[0] == 0
     # empty batch or empty time axis
     assert check(_good(T=0), **_ops())[0] == 0
     ops = _ops()
@@ -126,14 +129,15 @@ def test_rejects_unsupported_head_dim():
     assert rc == 5 and "head dim" in why
     rc, why = check(_good(flags=3 | 8), **_ops())  # the block form at D = 64
     assert rc == 5 and "block form" in why
-    assert check(_good(Dk=128, Dv=128, flags=3 | 8), **_ops())[0] == 0
+    assert check(_good(Dk=128, Dv=128, flags=3 | 8), **_ops(), workspace=BASE + 20 * (1 << 28),
+                 workspace_bytes=1 << 20)[0] == 0
     rc, why = check(_good(Dk=8, Dv=8), **_ops())
     assert rc == 5
 
 
 def test_rejects_null_and_half_gate_pair():
     L = nat.lib()
-    assert L.gdn_check(None, *([None] * 10)) == 1
+    assert L.gdn_check(None, *([None] * 11), 0) == 1
     assert "null descriptor" in nat.last_error()
     ops = _ops()
     ops["q"] = None
@@ -190,7 +194,62 @@ def test_step_needs_one_token_and_no_device_work_on_reject():
     assert rc == 5 and "T == 1" in nat.last_error()
     # a descriptor rejected by validation returns before any HIP call
     d = _good(Hv=3)
-    assert L.gdn_scan(ctypes.byref(d), *args, None) == 4
+    assert L.gdn_scan(ctypes.byref(d), *args, None, 0, None) == 4
+
+
+def _ws_size(**kw):
+    n = ctypes.c_uint64(12345)
+    rc = nat.lib().gdn_scan_workspace_size(ctypes.byref(_good(**kw)), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_query():
+    """Records of 2560 bytes per (value head, 16-token block), plus 3072 bytes
+    per (key head, block) below 256 value heads; nothing for the token-by-token
+    form, a single token or an empty batch."""
+    D = dict(Dk=128, Dv=128)
+    assert _ws_size(B=1, T=4096, Hk=16, Hv=32, **D) == (0, 32 * 256 * 2560 + 16 * 256 * 3072)
+    assert _ws_size(B=16, T=1024, Hk=16, Hv=32, **D) == (0, 512 * 64 * 2560)
+    assert _ws_size(B=2, T=17, Hk=2, Hv=4, **D) == (0, 8 * 2 * 2560 + 4 * 2 * 3072)
+    assert _ws_size(B=8, T=16, Hk=8, Hv=32, **D) == (0, 256 * 1 * 2560)  # 256 heads: no keys
+    assert _ws_size(B=2, T=4096, Hk=2, Hv=4, Dk=64, Dv=64) == (0, 0)     # per-token form
+    assert _ws_size(B=2, T=4096, Hk=2, Hv=4, flags=3 | 4, **D) == (0, 0)  # asked per-token
+    assert _ws_size(B=2, T=1, Hk=2, Hv=4, **D) == (0, 0)                   # decode kernel
+    assert _ws_size(B=2, T=0, Hk=2, Hv=4, **D) == (0, 0)
+    assert _ws_size(B=0, T=99, Hk=2, Hv=4, **D) == (0, 0)
+    rc, _ = _ws_size(Hv=3)
+    assert rc == 4 and "multiple" in nat.last_error()
+    assert nat.lib().gdn_scan_workspace_size(ctypes.byref(_good()), None) == 1
+
+
+def test_workspace_rejects():
+    """gdn_check / gdn_scan reject a missing, short, misaligned or overlapping
+    workspace before any device work, with a reason."""
+    d = _good(Dk=128, Dv=128, T=40)
+    need = 2 * 4 * 3 * 2560 + 2 * 2 * 3 * 3072
+    ws = BASE + 20 * (1 << 28)
+    assert check(d, **_ops(), workspace=ws, workspace_bytes=need)[0] == 0
+    assert check(d, **_ops(), workspace=ws, workspace_bytes=need + 999)[0] == 0
+    rc, why = check(d, **_ops())
+    assert rc == 9 and "workspace" in why and str(need) in why
+    rc, why = check(d, **_ops(), workspace=ws, workspace_bytes=need - 1)
+    assert rc == 9 and str(need) in why
+    rc, why = check(d, **_ops(), workspace=ws + 16, workspace_bytes=need)
+    assert rc == 6 and "256-byte" in why
+    ops = _ops()
+    rc, why = check(d, **ops, workspace=ops["v"] - 256, workspace_bytes=need)
+    assert rc == 7 and "workspace overlaps" in why
+    rc, why = check(d, **ops, workspace=ops["s_out"], workspace_bytes=need)
+    assert rc == 7 and "s_out" in why
+    # the token-by-token form needs none, so a missing workspace is fine there
+    assert check(_good(Dk=128, Dv=128, T=40, flags=3 | 4), **_ops())[0] == 0
+    # through the entry point: rejected before any HIP call
+    L = nat.lib()
+    args = [ctypes.c_void_p(ops[n]) for n in
+            ("q", "k", "v", "log_decay", "beta", "s0", "z", "w", "y", "s_out")]
+    assert L.gdn_scan(ctypes.byref(d), *args, None, 0, None) == 9
+    assert L.gdn_scan(ctypes.byref(d), *args, ctypes.c_void_p(ws), need - 256, None) == 9
+    assert L.gdn_scan(ctypes.byref(d), *args, ctypes.c_void_p(ws + 8), need, None) == 6
 
 
 def test_last_error_is_per_thread():

@@ -14,7 +14,9 @@ import pytest
 import torch
 
 from linear_attention_recurrence_recurrent_amd import (GdnError, gates, recurrent_step,
-                                                       recurrent_step_three_pass, scan, synth)
+                                                       recurrent_step_three_pass, scan,
+                                                       scan_workspace_bytes, synth)
+from linear_attention_recurrence_recurrent_amd import _desc
 from oracle import gdn_oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -218,7 +220,7 @@ def test_block_form_edge_shapes(case, gated):
 F32_LEVEL = 2e-5
 SIXTEEN_BIT_CASES = [
     (1, 200, 2, 4, "bf16", False),   # few heads (rows_la_kernel), token-major
-    (1, 200, 2, 4, "f16", True),     # few heads, f16 (f32 products), head-major
+    (1, 200, 2, 4, "f16", True),     # few heads, f16 q/k split in two bf16 parts, head-major
     (2, 47, 16, 128, "bf16", True),  # 256 heads (state_kernel), bf16 parts
     (1, 64, 16, 256, "f16", True),   # 256 heads, f16 split in two bf16 parts
 ]
@@ -405,68 +407,119 @@ def test_rejections_raise():
         scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], s0, state_out=s_out)
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled heads
-def _sample_heads(B, Hv, n, seed):
-    r = np.random.default_rng(seed)
-    pairs = [(0, 0), (B - 1, Hv - 1)]
-    while len(pairs) < n:
-        p = (int(r.integers(B)), int(r.integers(Hv)))
-        if p not in pairs:
-            pairs.append(p)
-    return pairs
+def test_bad_outputs_rejected_before_launch():
+    """A caller's out / state_out must be float32, contiguous, on q's device
+    and exactly shaped: the kernels size their writes from the operands."""
+    ops = dev(synth.random_operands(1, 6, 2, 4, 64, 64, dtype="bf16", seed=1))
+    a = (ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"])
+    good_y = torch.empty(ops["v"].shape, dtype=torch.float32, device=DEV)
+    bad = [
+        dict(out=torch.empty(ops["v"].shape, dtype=torch.bfloat16, device=DEV)),
+        dict(out=torch.empty((1, 5, 4, 64), dtype=torch.float32, device=DEV)),
+        dict(out=torch.empty((1, 4, 6, 64), dtype=torch.float32,
+                             device=DEV).transpose(1, 2)),
+        dict(out=torch.empty(ops["v"].shape, dtype=torch.float32)),
+        dict(out=good_y, state_out=torch.empty((1, 4, 64, 63), dtype=torch.float32, device=DEV)),
+        dict(out=good_y, state_out=torch.empty((1, 4, 64, 64), dtype=torch.float64, device=DEV)),
+        dict(out=good_y, state_out=torch.empty((1, 4, 64, 64), dtype=torch.float32,
+                                               device=DEV).transpose(2, 3)),
+    ]
+    for kw in bad:
+        with pytest.raises(GdnError):
+            scan(*a, **kw)
+    with pytest.raises(GdnError):
+        recurrent_step(*(x[:, :1].contiguous() for x in a[:5]), ops["s0"],
+                       out=torch.empty((1, 1, 4, 32), dtype=torch.float32, device=DEV))
 
 
-def _check_heads(y, s, ops, heads, head_major, tol, what):
-    sel = orc.select_heads(ops, heads, head_major=head_major)
-    yr, sr = orc.scan(sel["q"], sel["k"], sel["v"], sel["log_decay"], sel["beta"], sel["s0"],
-                      sel.get("z"), sel.get("w"), head_major=head_major)
-    for i, (b, hv) in enumerate(heads):
-        yg = y[b, hv] if head_major else y[b, :, hv]
-        yo = yr[i, 0] if head_major else yr[i, :, 0]
-        assert_close(yg, yo, tol, "%s y head (%d,%d)" % (what, b, hv))
-        assert_close(s[b, hv], sr[i, 0], tol, "%s state head (%d,%d)" % (what, b, hv))
+def test_caller_workspace():
+    """The block form runs on a caller-supplied workspace (bit-identical to the
+    binding's own allocation), and a short one is rejected before any launch."""
+    for (B, T, Hk, Hv) in ((1, 50, 2, 4), (8, 40, 16, 32)):
+        ops = dev(synth.random_operands(B, T, Hk, Hv, 128, 128, dtype="bf16", seed=B + T))
+        a = (ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"], ops["z"],
+             ops["w"])
+        need = scan_workspace_bytes(_desc(B, T, Hk, Hv, 128, 128, False, 2, 2, True, True, 1e-6,
+                                          1e-6))
+        nblk = (T + 15) // 16
+        assert need == B * Hv * nblk * 2560 + (B * Hk * nblk * 3072 if B * Hv < 256 else 0)
+        y0, s0 = scan(*a)
+        ws = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device=DEV)
+        y1, s1 = scan(*a, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(s0, s1)
+        with pytest.raises(GdnError, match="EWORKSPACE"):
+            scan(*a, workspace=ws[:need - 256])
+        with pytest.raises(GdnError):
+            scan(*a, workspace=torch.empty(need, dtype=torch.float32, device=DEV))
 
 
-def test_config2_chained_decode_sampled():
+# ------------------------------------------------------------------ full-size workloads, every head
+# The float64 oracle computes the whole workload (every batch entry and value
+# head, the whole time axis) in seconds on the host's cores, so every output
+# element is compared.  Each workload runs gated and with z = None: the raw o
+# is the operator contract of the "gated_delta" page (native_gdn_reject_reason,
+# no gate), and the RMSNorm of the gated output would hide a wrong scale.
+_ORACLE = {}
+
+
+def _oracle_full(idx, gated):
+    key = (idx, gated)
+    if key not in _ORACLE:
+        wl = synth.WORKLOADS[idx]
+        ops = synth.make(wl)
+        say("oracle: workload %d (%s), gated=%s" % (idx, wl.name, gated))
+        _ORACLE[key] = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"],
+                                ops["s0"], ops["z"] if gated else None,
+                                ops["w"] if gated else None, head_major=wl.head_major)
+    return _ORACLE[key]
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_config2_chained_decode_every_head(gated):
     wl = synth.WORKLOADS[2]
-    say("config2: 100 chained in-place decode steps, B=64")
+    say("config2: 100 chained in-place decode steps, B=64, gated=%s" % gated)
     ops = synth.make(wl)
     steps = synth.step_slices(ops, head_major=False)
     d_steps = [dev(st) for st in steps]
-    wd = ops["w"].to(DEV)
+    wd = ops["w"].to(DEV) if gated else None
     state = ops["s0"].to(DEV).clone()
     ys = []
     for st in d_steps:
         y, _ = recurrent_step(st["q"], st["k"], st["v"], st["log_decay"], st["beta"], state,
-                              st["z"], wd, inplace=True)
+                              st["z"] if gated else None, wd, inplace=True)
         ys.append(y)
     torch.cuda.synchronize()
-    yall = torch.cat(ys, dim=1).cpu()  # [B, 100, Hv, D]
-    heads = _sample_heads(wl.B, wl.Hv, 12, 2)
-    _check_heads(yall, state.cpu(), ops, heads, False, TOL["bf16"], "config2")
+    yall = torch.cat(ys, dim=1)  # [B, 100, Hv, D]: the chain is the scan over 100 tokens
+    yr, sr = _oracle_full(2, gated)
+    assert_close(yall, yr, TOL["bf16"], "config2 y (all %d heads)" % (wl.B * wl.Hv))
+    assert_close(state, sr, TOL["bf16"], "config2 final state")
 
 
+@pytest.mark.parametrize("gated", [True, False])
 @pytest.mark.parametrize("form", [None, "per_token", "block"])
-def test_config3_prefill_scan_sampled(form):
+def test_config3_prefill_scan_every_head(form, gated):
     wl = synth.WORKLOADS[3]
-    say("config3: B=1 T=4096 token-major scan, form %s" % form)
-    ops = synth.make(wl)
-    d = dev(ops)
-    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"],
+    say("config3: B=1 T=4096 token-major scan, form %s, gated=%s" % (form, gated))
+    d = dev(synth.make(wl))
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
+                d["z"] if gated else None, d["w"] if gated else None, form=form)
+    torch.cuda.synchronize()
+    yr, sr = _oracle_full(3, gated)
+    assert_close(y, yr, TOL["bf16"], "config3 y")
+    assert_close(s, sr, TOL["bf16"], "config3 final state")
+
+
+@pytest.mark.parametrize("gated", [True, False])
+@pytest.mark.parametrize("form", [None, "per_token", "block"])
+def test_config4_head_major_scan_every_head(form, gated):
+    wl = synth.WORKLOADS[4]
+    say("config4: B=16 T=1024 head-major f16 scan, form %s, gated=%s" % (form, gated))
+    d = dev(synth.make(wl))
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
+                d["z"] if gated else None, d["w"] if gated else None, head_major=True,
                 form=form)
     torch.cuda.synchronize()
-    heads = _sample_heads(wl.B, wl.Hv, 6, 3)
-    _check_heads(y.cpu(), s.cpu(), ops, heads, False, TOL["bf16"], "config3")
-
-
-@pytest.mark.parametrize("form", [None, "per_token", "block"])
-def test_config4_head_major_scan_sampled(form):
-    wl = synth.WORKLOADS[4]
-    say("config4: B=16 T=1024 head-major f16 scan, form %s" % form)
-    ops = synth.make(wl)
-    d = dev(ops)
-    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"],
-                head_major=True, form=form)
-    torch.cuda.synchronize()
-    heads = _sample_heads(wl.B, wl.Hv, 10, 4)
-    _check_heads(y.cpu(), s.cpu(), ops, heads, True, TOL["f16"], "config4")
+    yr, sr = _oracle_full(4, gated)
+    assert_close(y, yr, TOL["f16"], "config4 y")
+    assert_close(s, sr, TOL["f16"], "config4 final state")

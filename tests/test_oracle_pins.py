@@ -330,7 +330,7 @@ def test_gated_norm_closed_forms():
 
 
 def test_gate_first_is_distinguished_from_norm_first():
-    """The page says gate FIRST, then normalise.  With o = [1, 1] and z = [0, 10]:
+    """The page multiplies the gate in before normalising.  With o = [1, 1] and z = [0, 10]:
     gate-first gives y = [0, sqrt(2)*x/sqrt(x^2 + 2eps)]*w with x = silu(10), while
     normalising first would give [0, x/sqrt(1 + eps)]*w."""
     w = np.array([1.0, 2.0])

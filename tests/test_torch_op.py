@@ -1,14 +1,30 @@
-"""torch custom ops: the fake kernels give the promoted float32 output (CPU, meta
-tensors), and on the GPU the ops equal the direct C-ABI calls and pass opcheck."""
+"""torch custom ops gdn::scan and gdn::recurrent_step.
+
+The fake kernels must state the real op's output contract ("gated_delta" page,
+gated_delta_fake: a fake kernel that disagreed with the real op would break
+torch.export, opcheck and torch.compile): y is float32 whatever the operand
+dtype, in v's layout, and the final state is float32 like s0.  On the CPU the
+fake kernels are checked on meta tensors and through torch.export; on the GPU
+the ops are compared with the float64 oracle and pass opcheck with its
+default tests.
+"""
+import numpy as np
 import pytest
 import torch
 
-from linear_attention_recurrence_recurrent_amd import scan, synth
+from linear_attention_recurrence_recurrent_amd import synth
 from linear_attention_recurrence_recurrent_amd.torch_op import recurrent_step_op, scan_op
+
+TOL = {"f32": 1e-4, "f16": 3e-3, "bf16": 3e-3}
 
 
 def _meta(ops):
     return {n: t.to("meta") for n, t in ops.items()}
+
+
+def _args(ops, head_major=False):
+    return (ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"], ops["z"],
+            ops["w"], head_major)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -17,8 +33,7 @@ def test_fake_kernel_promotes_to_f32(dtype, head_major):
     ops = _meta(synth.random_operands(2, 5, 2, 4, 64, 64, dtype=dtype, head_major=head_major))
     from torch._subclasses.fake_tensor import FakeTensorMode
     with FakeTensorMode(allow_non_fake_inputs=True):
-        y, s = scan_op(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
-                       ops["z"], ops["w"], head_major)
+        y, s = scan_op(*_args(ops, head_major))
     assert y.dtype == torch.float32 and tuple(y.shape) == tuple(ops["v"].shape)
     assert s.dtype == torch.float32 and tuple(s.shape) == tuple(ops["s0"].shape)
 
@@ -32,16 +47,91 @@ def test_fake_kernel_step():
     assert y.dtype == torch.float32 and tuple(y.shape) == (3, 1, 4, 32)
 
 
+class _Layer(torch.nn.Module):
+    """A module that calls both ops, as a model layer would."""
+
+    def forward(self, q, k, v, log_decay, beta, s0, z, w):
+        y, s = torch.ops.gdn.scan(q, k, v, log_decay, beta, s0, z, w, False)
+        last = [x[:, -1:].contiguous() for x in (q, k, v, log_decay, beta, z)]
+        y1, s1 = torch.ops.gdn.recurrent_step(*last[:5], s, last[5], w, False)
+        return y * 2.0, y1, s1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_export_sees_promoted_outputs(dtype):
+    """torch.export traces the layer through the fake kernels only (no device
+    work, CPU tensors): the graph holds both ops and its outputs are float32
+    of the real op's shapes, also with a dynamic time axis."""
+    ops = synth.random_operands(2, 7, 2, 4, 32, 32, dtype=dtype, seed=1)
+    args = tuple(ops[n] for n in ("q", "k", "v", "log_decay", "beta", "s0", "z", "w"))
+    T = torch.export.Dim("T", min=2, max=4096)
+    dyn = {"q": {1: T}, "k": {1: T}, "v": {1: T}, "log_decay": {1: T}, "beta": {1: T},
+           "s0": None, "z": {1: T}, "w": None}
+    ep = torch.export.export(_Layer(), args, dynamic_shapes=dyn)
+    targets = {str(n.target) for n in ep.graph.nodes if n.op == "call_function"}
+    assert "gdn.scan.default" in targets and "gdn.recurrent_step.default" in targets
+    out = [n for n in ep.graph.nodes if n.op == "output"][0]
+    y, y1, s1 = (a.meta["val"] for a in out.args[0])
+    assert y.dtype == y1.dtype == s1.dtype == torch.float32
+    assert y.shape[0] == 2 and y.shape[2:] == (4, 32)
+    assert tuple(y1.shape) == (2, 1, 4, 32) and tuple(s1.shape) == (2, 4, 32, 32)
+
+
+def _close(got, ref, tol, what):
+    got = got.detach().double().cpu().numpy()
+    err = np.abs(got - ref) / (1.0 + np.abs(ref))
+    assert float(err.max()) <= tol, "%s: %.3e > %.1e" % (what, float(err.max()), tol)
+
+
 @pytest.mark.gpu
-def test_op_equals_direct_call_and_opcheck():
-    ops = {n: t.cuda() for n, t in synth.random_operands(2, 9, 2, 4, 64, 64, dtype="bf16",
-                                                         seed=3).items()}
-    y, s = scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"], ops["z"],
-                ops["w"])
-    yo, so = scan_op(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
-                     ops["z"], ops["w"], False)
+@pytest.mark.parametrize("dtype,head_major,D", [("bf16", False, 128), ("f16", True, 128),
+                                                ("f32", False, 64)])
+def test_ops_match_oracle(dtype, head_major, D):
+    from oracle import gdn_oracle as orc
+    ops = synth.random_operands(2, 37, 2, 4, D, D, dtype=dtype, head_major=head_major, seed=3)
+    d = {n: t.cuda() for n, t in ops.items()}
+    y, s = scan_op(*_args(d, head_major))
     torch.cuda.synchronize()
-    assert torch.equal(y, yo) and torch.equal(s, so)
-    torch.library.opcheck(scan_op, (ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"],
-                                    ops["s0"], ops["z"], ops["w"], False),
-                          test_utils=("test_schema", "test_faketensor"))
+    yr, sr = orc.scan(*_args(ops)[:8], head_major=head_major)
+    _close(y, yr, TOL[dtype], "scan_op y")
+    _close(s, sr, TOL[dtype], "scan_op state")
+    st = {n: (t[:, :1] if not head_major else t[:, :, :1]).contiguous()
+          for n, t in ops.items() if n in ("q", "k", "v", "z", "log_decay", "beta")}
+    ds = {n: t.cuda() for n, t in st.items()}
+    y1, s1 = recurrent_step_op(ds["q"], ds["k"], ds["v"], ds["log_decay"], ds["beta"], d["s0"],
+                               ds["z"], d["w"], head_major)
+    torch.cuda.synchronize()
+    yr1, sr1 = orc.step(st["q"], st["k"], st["v"], st["log_decay"], st["beta"], ops["s0"],
+                        st["z"], ops["w"], head_major=head_major)
+    _close(y1, yr1, TOL[dtype], "recurrent_step_op y")
+    _close(s1, sr1, TOL[dtype], "recurrent_step_op state")
+
+
+@pytest.mark.gpu
+def test_opcheck_default_tests():
+    """opcheck with its default test set (schema, autograd registration, fake
+    tensor, AOT dispatch with dynamic shapes) on both ops."""
+    ops = {n: t.cuda() for n, t in synth.random_operands(2, 9, 2, 4, 128, 128, dtype="bf16",
+                                                         seed=3).items()}
+    torch.library.opcheck(scan_op, _args(ops))
+    st = {n: ops[n][:, :1].contiguous() for n in ("q", "k", "v", "z", "log_decay", "beta")}
+    torch.library.opcheck(recurrent_step_op, (st["q"], st["k"], st["v"], st["log_decay"],
+                                              st["beta"], ops["s0"], st["z"], ops["w"], False))
+
+
+@pytest.mark.gpu
+def test_exported_layer_runs_on_gpu():
+    """The exported program runs the real kernels and matches the oracle."""
+    from oracle import gdn_oracle as orc
+    ops = synth.random_operands(2, 20, 2, 4, 128, 128, dtype="bf16", seed=4)
+    names = ("q", "k", "v", "log_decay", "beta", "s0", "z", "w")
+    ep = torch.export.export(_Layer(), tuple(ops[n] for n in names))
+    y, y1, s1 = ep.module()(*(ops[n].cuda() for n in names))
+    torch.cuda.synchronize()
+    yr, sr = orc.scan(*(ops[n] for n in names))
+    _close(y, 2.0 * yr, TOL["bf16"], "exported y")
+    last = {n: ops[n][:, -1:].contiguous() for n in ("q", "k", "v", "z", "log_decay", "beta")}
+    yr1, sr1 = orc.step(last["q"], last["k"], last["v"], last["log_decay"], last["beta"], sr,
+                        last["z"], ops["w"])
+    _close(y1, yr1, TOL["bf16"], "exported step y")
+    _close(s1, sr1, TOL["bf16"], "exported step state")
