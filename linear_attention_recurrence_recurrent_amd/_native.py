@@ -22,10 +22,12 @@ STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_ESHAPE", 3: "GDN_EDTYPE", 4: "GD
           9: "GDN_EWORKSPACE"}
 ABI_VERSION = 2
 
-# Every symbol include/gdn.h declares.
+# Every symbol include/gdn.h and include/gdn_calib.h declare.
 EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan",
            "gdn_scan_workspace_size", "gdn_gates", "gdn_conv_silu", "gdn_check",
-           "gdn_last_error", "gdn_status_str", "gdn_abi_version")
+           "gdn_last_error", "gdn_status_str", "gdn_abi_version", "gdn_calib_stream",
+           "gdn_calib_variant_name")
+GDN_CALIB_RMW, GDN_CALIB_COPY, GDN_CALIB_VARIANTS = 0, 1, 12
 
 
 class GdnDesc(ctypes.Structure):
@@ -74,6 +76,11 @@ def lib():
         L.gdn_status_str.argtypes = [ctypes.c_int]
         L.gdn_abi_version.restype = ctypes.c_int
         L.gdn_abi_version.argtypes = []
+        L.gdn_calib_stream.restype = ctypes.c_int
+        L.gdn_calib_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, ctypes.c_uint64,
+                                       vp]
+        L.gdn_calib_variant_name.restype = ctypes.c_char_p
+        L.gdn_calib_variant_name.argtypes = [ctypes.c_int32]
         _lib = L
     return _lib
 

@@ -1,0 +1,121 @@
+// Streaming reference kernels (include/gdn_calib.h): in-place read-modify-write
+// and copy of a large buffer with the decode step's access shape, to measure
+// the HBM rate an in-place state update can reach on this GPU.
+#include <cstdio>
+
+#include "gdn_calib.h"
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+// A workgroup owns TPB * U consecutive 16-byte vectors; lane t takes vectors
+// t, t + TPB, ... (coalesced), issues all U loads, then all U stores.
+template <int TPB, int U, bool NT, bool RMW>
+__global__ __launch_bounds__(TPB) void stream_kernel(const float* src, float* dst, int64_t n4) {
+  const int64_t base = (int64_t)blockIdx.x * (TPB * U) + threadIdx.x;
+  float4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + (int64_t)u * TPB;
+    if (i < n4) {
+      if constexpr (NT) v[u] = nt_load4(src + 4 * i);
+      else v[u] = *reinterpret_cast<const float4*>(src + 4 * i);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + (int64_t)u * TPB;
+    if (i < n4) {
+      float4 s = v[u];
+      if constexpr (RMW) {
+        s.x = fmaf(s.x, 1.0000001f, 1e-7f);
+        s.y = fmaf(s.y, 1.0000001f, 1e-7f);
+        s.z = fmaf(s.z, 1.0000001f, 1e-7f);
+        s.w = fmaf(s.w, 1.0000001f, 1e-7f);
+      }
+      if constexpr (NT) nt_store4(s, dst + 4 * i);
+      else *reinterpret_cast<float4*>(dst + 4 * i) = s;
+    }
+  }
+}
+
+// names in the order of the launch switch below
+constexpr const char* kVariantNames[GDN_CALIB_VARIANTS] = {
+    "512 threads x 8 vectors, nontemporal",  "256 threads x 8 vectors, nontemporal",
+    "512 threads x 16 vectors, nontemporal", "256 threads x 16 vectors, nontemporal",
+    "1024 threads x 4 vectors, nontemporal", "256 threads x 4 vectors, nontemporal",
+    "512 threads x 8 vectors, ordinary",     "256 threads x 8 vectors, ordinary",
+    "512 threads x 16 vectors, ordinary",    "256 threads x 16 vectors, ordinary",
+    "1024 threads x 4 vectors, ordinary",    "256 threads x 4 vectors, ordinary",
+};
+
+template <int TPB, int U, bool NT>
+void launch_v(bool rmw, const float* src, float* dst, int64_t n4, hipStream_t st) {
+  const dim3 grid((unsigned)((n4 + TPB * U - 1) / (TPB * U)));
+  if (rmw) stream_kernel<TPB, U, NT, true><<<grid, TPB, 0, st>>>(src, dst, n4);
+  else stream_kernel<TPB, U, NT, false><<<grid, TPB, 0, st>>>(src, dst, n4);
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" {
+
+int gdn_calib_stream(int32_t op, int32_t variant, const void* src, void* dst, uint64_t bytes,
+                     void* stream) {
+  using namespace gdn;
+  if (op != GDN_CALIB_RMW && op != GDN_CALIB_COPY) {
+    set_error("op must be GDN_CALIB_RMW or GDN_CALIB_COPY");
+    return GDN_EINVAL;
+  }
+  if (variant < 0 || variant >= GDN_CALIB_VARIANTS) {
+    set_error("variant out of range");
+    return GDN_EINVAL;
+  }
+  if (bytes % 16 || bytes / 16 >= ((uint64_t)1 << 40)) {
+    set_error("bytes must be a multiple of 16 (and below 2^44)");
+    return GDN_ESHAPE;
+  }
+  if (bytes == 0) return GDN_OK;
+  if (!src || !dst || (uintptr_t)src % 16 || (uintptr_t)dst % 16) {
+    set_error("src and dst must be non-null and 16-byte aligned");
+    return src && dst ? GDN_EALIGN : GDN_EINVAL;
+  }
+  const bool rmw = op == GDN_CALIB_RMW;
+  if (rmw && src != dst) {
+    set_error("the read-modify-write works in place: src must equal dst");
+    return GDN_EINVAL;
+  }
+  if (!rmw && (uintptr_t)src < (uintptr_t)dst + bytes && (uintptr_t)dst < (uintptr_t)src + bytes) {
+    set_error("copy source and destination overlap");
+    return GDN_EALIAS;
+  }
+  const float* s = static_cast<const float*>(src);
+  float* d = static_cast<float*>(dst);
+  const int64_t n4 = (int64_t)(bytes / 16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (variant) {
+    case 0: launch_v<512, 8, true>(rmw, s, d, n4, st); break;
+    case 1: launch_v<256, 8, true>(rmw, s, d, n4, st); break;
+    case 2: launch_v<512, 16, true>(rmw, s, d, n4, st); break;
+    case 3: launch_v<256, 16, true>(rmw, s, d, n4, st); break;
+    case 4: launch_v<1024, 4, true>(rmw, s, d, n4, st); break;
+    case 5: launch_v<256, 4, true>(rmw, s, d, n4, st); break;
+    case 6: launch_v<512, 8, false>(rmw, s, d, n4, st); break;
+    case 7: launch_v<256, 8, false>(rmw, s, d, n4, st); break;
+    case 8: launch_v<512, 16, false>(rmw, s, d, n4, st); break;
+    case 9: launch_v<256, 16, false>(rmw, s, d, n4, st); break;
+    case 10: launch_v<1024, 4, false>(rmw, s, d, n4, st); break;
+    default: launch_v<256, 4, false>(rmw, s, d, n4, st); break;
+  }
+  return device_status("stream_kernel launch");
+}
+
+const char* gdn_calib_variant_name(int32_t variant) {
+  if (variant < 0 || variant >= GDN_CALIB_VARIANTS) return "";
+  return gdn::kVariantNames[variant];
+}
+
+}  // extern "C"

@@ -2,6 +2,7 @@
 declares, agrees with the header on the descriptor layout, and rejects bad
 arguments with a status and a short reason (no device work, no GPU needed)."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -12,13 +13,15 @@ from linear_attention_recurrence_recurrent_amd import _native as nat
 from linear_attention_recurrence_recurrent_amd import GdnDesc, abi_version, check
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gdn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -201,6 +204,24 @@ def _ws_size(**kw):
     n = ctypes.c_uint64(12345)
     rc = nat.lib().gdn_scan_workspace_size(ctypes.byref(_good(**kw)), ctypes.byref(n))
     return rc, n.value
+
+
+def test_calib_validation():
+    """The streaming reference kernels reject bad arguments before any launch."""
+    L = nat.lib()
+    a, b = _addrs(2)
+    f = L.gdn_calib_stream
+    assert f(2, 0, a, a, 1 << 20, None) == 1
+    assert f(0, nat.GDN_CALIB_VARIANTS, a, a, 1 << 20, None) == 1
+    assert f(0, 0, a, a, 17, None) == 2
+    assert f(0, 0, a, b, 1 << 20, None) == 1 and "in place" in nat.last_error()
+    assert f(1, 0, a, a + 256, 1 << 20, None) == 7
+    assert f(1, 0, a + 4, b, 1 << 20, None) == 6
+    assert f(1, 0, None, b, 1 << 20, None) == 1
+    assert f(0, 0, None, None, 0, None) == 0
+    names = [L.gdn_calib_variant_name(i).decode() for i in range(nat.GDN_CALIB_VARIANTS)]
+    assert len(set(names)) == nat.GDN_CALIB_VARIANTS and all(names)
+    assert L.gdn_calib_variant_name(-1).decode() == ""
 
 
 def test_workspace_size_query():
