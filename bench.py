@@ -111,6 +111,60 @@ class Launcher:
             raise RuntimeError("launch rejected: %s" % _native.last_error())
 
 
+def streaming_ceiling(torch, nbytes, args):
+    """The HBM rate an in-place state update can reach here: the library's
+    streaming reference kernels (include/gdn_calib.h) rewrite a buffer of the
+    decode state's size in place (read + write, one multiply-add per element)
+    or copy it, each call on the next of four such buffers, so the working set
+    (4x the state) exceeds the 256 MB Infinity Cache.  Every access variant is
+    timed; the fastest read-modify-write is the ceiling."""
+    from linear_attention_recurrence_recurrent_amd import _native
+    L = _native.lib()
+    dev = torch.device("cuda:0")
+    nbuf = 4
+    bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(0.5)
+            for _ in range(nbuf)]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ptr = [ctypes.c_void_p(b.data_ptr()) for b in bufs]
+
+    def timed(fn, reps=24):
+        settle(lambda: [fn(i) for i in range(nbuf)], torch, args.settle_ms / 8)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    def call(op, v, a, b):
+        rc = L.gdn_calib_stream(op, v, ptr[a], ptr[b], nbytes, sp)
+        if rc:
+            raise RuntimeError(_native.last_error())
+
+    rmw, copy = {}, {}
+    for v in range(_native.GDN_CALIB_VARIANTS):
+        name = L.gdn_calib_variant_name(v).decode()
+        rmw[name] = 2 * nbytes / timed(lambda i: call(_native.GDN_CALIB_RMW, v, i % nbuf,
+                                                      i % nbuf)) / 1e9
+        copy[name] = 2 * nbytes / timed(lambda i: call(_native.GDN_CALIB_COPY, v, i % nbuf,
+                                                       (i + 1) % nbuf)) / 1e9
+    torch_copy = 2 * nbytes / timed(lambda i: bufs[(i + 1) % nbuf].copy_(bufs[i % nbuf])) / 1e9
+    del bufs
+    best_rmw = max(rmw, key=rmw.get)
+    best_copy = max(copy, key=copy.get)
+    log("streaming ceiling at %d MB per buffer, %d buffers in turn: in-place %.1f GB/s (%s), "
+        "copy %.1f GB/s (%s), torch copy %.1f GB/s" % (nbytes >> 20, nbuf, rmw[best_rmw],
+                                                        best_rmw, copy[best_copy], best_copy,
+                                                        torch_copy))
+    return {"rmw_gbs": round(rmw[best_rmw], 1), "rmw_variant": best_rmw,
+            "copy_gbs": round(copy[best_copy], 1), "copy_variant": best_copy,
+            "torch_copy_gbs": round(torch_copy, 1), "buffer_bytes": nbytes, "buffers": nbuf,
+            "working_set_bytes": nbuf * nbytes,
+            "rmw_all_gbs": {k: round(x, 1) for k, x in rmw.items()}}
+
+
 def bench_decode(args, torch):
     import linear_attention_recurrence_recurrent_amd as gdn
     from linear_attention_recurrence_recurrent_amd import synth
@@ -151,29 +205,23 @@ def bench_decode(args, torch):
     launch_s = ms * 1e-3 / launches
     ms_per_chain = ms / args.steps
     value = state_bytes * wl.steps / (ms_per_chain * 1e-3) / 1e9
-    achieved = (state_bytes + io_bytes) / launch_s / 1e9
+    achieved = state_bytes / launch_s / 1e9
     traffic = read_counters()
-    # a plain device copy moving the same state bytes (one read and one write)
-    src = torch.empty(wl.B * wl.Hv * wl.Dv * wl.Dk, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(20):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = state_bytes / (e0.elapsed_time(e1) * 1e-3 / 20) / 1e9
-    del src, dst
+    ceiling = streaming_ceiling(torch, state_bytes // 2, args)
+    kernel = "decode_kernel<bf16,bf16,128,16,2,16>"
     res = dict(ms_per_step=ms_per_chain, value=value, launch_us=launch_s * 1e6,
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": traffic, "kernel": "decode_kernel<bf16,bf16,128,8,2,8>",
-                         "algorithmic_bytes_per_launch": state_bytes + io_bytes,
+                         "traffic": traffic, "kernel": kernel,
+                         "algorithmic_bytes_per_launch": state_bytes,
+                         "operand_io_bytes_per_launch": io_bytes,
                          "avg_launch_us": round(launch_s * 1e6, 3),
-                         "copy_same_bytes_gbs": round(copy_gbs, 1)})
-    log("decode: %.3f ms per 100-step chain, %.1f us per launch, state %.1f GB/s (a device copy "
-        "of the same bytes: %.1f GB/s)" % (ms_per_chain, launch_s * 1e6, value, copy_gbs))
+                         "ceiling": ceiling,
+                         "frac_of_rmw_ceiling": round(achieved / ceiling["rmw_gbs"], 4)})
+    log("decode: %.3f ms per 100-step chain, %.2f us per launch, state %.1f GB/s = %.1f%% of "
+        "8 TB/s, %.1f%% of the in-place streaming ceiling (%.1f GB/s)" %
+        (ms_per_chain, launch_s * 1e6, achieved, 100 * achieved / HBM_PEAK_GBS,
+         100 * achieved / ceiling["rmw_gbs"], ceiling["rmw_gbs"]))
 
     # the same chain with the state double-buffered (each step reads one buffer
     # and writes the other, s_out of a step is s0 of the next): the same bytes,
@@ -435,6 +483,83 @@ def copy_reference(args, torch):
     print(json.dumps({"copy_reference_bytes_each_way": n * 4, "launches": max(1, args.steps)}))
 
 
+# ------------------------------------------------------------------ profile summaries
+# rocprofv3 writes CSV files (a kernel trace with one row per dispatch, or a
+# counter collection with one row per dispatch and counter); these turn them
+# into the short summaries kept under profiles/.
+
+def _short_kernel(name):
+    """'gdn::(anonymous namespace)::decode_kernel<2, 2, 128>(gdn::...)' -> 'decode_kernel<2, 2, 128>'."""
+    name = name.replace("(anonymous namespace)", "anon")
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # the parameter list starts at the first '(' outside <>
+        depth += (ch == "<") - (ch == ">")
+        if ch == "(" and depth == 0:
+            cut = i
+            break
+    base = name[:cut].strip()
+    depth, start = 0, 0
+    for i, ch in enumerate(base):  # keep what follows the last '::' outside <>
+        depth += (ch == "<") - (ch == ">")
+        if depth == 0 and base.startswith("::", i):
+            start = i + 2
+    base = base[start:]
+    return base.split(" ")[-1] if " " in base and "<" not in base else base
+
+
+def _grid(row):
+    if "Grid_Size" in row and row["Grid_Size"]:
+        return int(float(row["Grid_Size"]))
+    g = 1
+    for ax in ("X", "Y", "Z"):
+        v = row.get("Grid_Size_" + ax)
+        if v:
+            g *= int(float(v))
+    return g
+
+
+def trace_summary(path):
+    """Per (kernel, grid size): calls, average / median / min / max duration."""
+    import csv
+    import statistics
+    groups = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            key = (_short_kernel(row["Kernel_Name"]), _grid(row))
+            us = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3
+            groups.setdefault(key, []).append(us)
+    total = sum(sum(v) for v in groups.values())
+    print("| kernel | grid (threads) | calls | avg us | median us | min us | max us | share |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print("| %s | %d | %d | %.2f | %.2f | %.2f | %.2f | %.1f%% |" % (
+            k, g, len(v), sum(v) / len(v), statistics.median(v), min(v), max(v),
+            100 * sum(v) / total))
+
+
+def counter_summary(paths):
+    """Per (kernel, grid size): every counter averaged over the dispatches
+    (counter values are summed over the GPU's XCDs and dimensions first)."""
+    import csv
+    acc = {}
+    for path in paths:
+        per_dispatch = {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                key = (_short_kernel(row["Kernel_Name"]), _grid(row))
+                d = per_dispatch.setdefault((row["Dispatch_Id"], key), {})
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(
+                    row["Counter_Value"])
+        for (_, key), d in per_dispatch.items():
+            a = acc.setdefault(key, {})
+            for c, v in d.items():
+                a.setdefault(c, []).append(v)
+    for (k, g), cs in sorted(acc.items()):
+        print("%s grid %d:" % (k, g))
+        for c, v in sorted(cs.items()):
+            print("  %s %.6g per dispatch (%d dispatches)" % (c, sum(v) / len(v), len(v)))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -451,7 +576,17 @@ def main():
                     help="only the two scan workloads (for counter collection); partial JSON")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this size (counter reference)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print the per-kernel, per-grid summary of a rocprofv3 kernel trace")
+    ap.add_argument("--counter-summary", metavar="CSV", nargs="+",
+                    help="print per-kernel averages of rocprofv3 --pmc counter CSV files")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (each (batch, "
               "value head) pair is independent, so several GPUs would each run their share of the heads)",
