@@ -158,6 +158,23 @@ int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
              const void* w, float* y, float* s_out, void* workspace, uint64_t workspace_bytes,
              void* stream);
 
+/* gdn_scan for callers that cannot allocate device memory at all: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as gdn_scan without the workspace: the block
+ * form's records go to a static device array of GDN_NOALLOC_SCRATCH_BYTES
+ * that every GPU the library runs on holds until the process ends (its device
+ * address is looked up on the first call on each device).  A shape whose
+ * workspace (gdn_scan_workspace_size) exceeds it is rejected with
+ * GDN_EWORKSPACE before anything is enqueued; the prefill shape B=1 T=4096
+ * Hk=16 Hv=32 needs exactly 32 MiB.  All calls on one GPU share its array:
+ * calls ordered on one stream are safe, calls that overlap on one GPU (other
+ * streams or threads) race on it and give undefined results.  Allocates
+ * nothing (no hipMalloc, no allocating library routine). */
+#define GDN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int gdn_scan_noalloc(const gdn_desc* d, const void* q, const void* k, const void* v,
+                     const void* log_decay, const void* beta, const float* s0, const void* z,
+                     const void* w, float* y, float* s_out, void* stream);
+
 /* Gate producer: both gates from their pre-activations in one launch ("Module
  * gdn" page, QWEN38_KERNELS: the gate kernel computes both gates from one
  * launch; the pages do not give the formulas, these are the workloads' own):

@@ -20,7 +20,8 @@ from . import _native
 from ._native import (GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GDN_SCAN_BLOCK, GDN_SCAN_PER_TOKEN,
                       GdnDesc)
 
-__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "scan_workspace_bytes", "gates",
+__all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "scan_noalloc",
+           "scan_workspace_bytes", "gates",
            "conv_silu", "check", "abi_version", "GdnError"]
 
 _DT = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
@@ -202,6 +203,29 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
                         ws.numel() if ws is not None else 0, ctypes.c_void_p(stream))
     if rc != 0:
         _raise(rc)
+    return y, s_out
+
+
+def scan_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+                 beta: torch.Tensor, s0: torch.Tensor, z: Optional[torch.Tensor] = None,
+                 w: Optional[torch.Tensor] = None, *, head_major: bool = False,
+                 fold_qk_l2norm: bool = True, fold_q_scale: bool = True, qk_eps: float = 1e-6,
+                 norm_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+                 state_out: Optional[torch.Tensor] = None,
+                 form: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``scan`` through gdn_scan_noalloc: the library takes no workspace and
+    allocates nothing (the block form's records go to its static per-GPU
+    scratch, at most 64 MiB of them; larger shapes raise GdnError).  Calls
+    that overlap on one GPU race on that scratch.  Pass ``out`` and
+    ``state_out`` to keep this call free of allocations on the torch side too."""
+    B, T, Hk, Hv, Dk, Dv, dt, gdt = _prepare(q, k, v, log_decay, beta, s0, z, w, head_major)
+    if s0 is None:
+        raise GdnError(1, "scan_noalloc needs s0")
+    y = _outputs(q, v, s0, out, state_out, B, Hv, Dv, Dk)
+    s_out = state_out if state_out is not None else torch.empty_like(s0)
+    desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
+                 qk_eps, norm_eps, form)
+    _call("gdn_scan_noalloc", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
     return y, s_out
 
 

@@ -24,10 +24,11 @@ ABI_VERSION = 2
 
 # Every symbol include/gdn.h and include/gdn_calib.h declare.
 EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan",
-           "gdn_scan_workspace_size", "gdn_gates", "gdn_conv_silu", "gdn_check",
+           "gdn_scan_workspace_size", "gdn_scan_noalloc", "gdn_gates", "gdn_conv_silu", "gdn_check",
            "gdn_last_error", "gdn_status_str", "gdn_abi_version", "gdn_calib_stream",
            "gdn_calib_variant_name")
 GDN_CALIB_RMW, GDN_CALIB_COPY, GDN_CALIB_VARIANTS = 0, 1, 12
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class GdnDesc(ctypes.Structure):
@@ -54,7 +55,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp = ctypes.c_void_p
         dp = ctypes.POINTER(GdnDesc)
-        for name in ("gdn_recurrent_step", "gdn_recurrent_step_three_pass"):
+        for name in ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan_noalloc"):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [dp] + [vp] * 11

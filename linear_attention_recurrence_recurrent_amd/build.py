@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn_hip.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("gdn_decode.hip", "gdn_scan.hip", "gdn_chunk.hip", "gdn_gates.hip", "gdn_conv.hip",
-            "gdn_calib.hip", "gdn_api.cpp", "gdn_check.cpp")]
+            "gdn_calib.hip", "gdn_noalloc.hip", "gdn_api.cpp", "gdn_check.cpp")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gdn_device.h", "gdn_launch.h", "gdn_internal.h")] + [
     os.path.join(INCLUDE, "gdn.h"), os.path.join(INCLUDE, "gdn_calib.h")]
 

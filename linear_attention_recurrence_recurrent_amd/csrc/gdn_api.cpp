@@ -5,6 +5,27 @@
 #include "gdn_internal.h"
 #include "gdn_launch.h"
 
+namespace gdn {
+
+int run_scan(const gdn_desc& d, const void* q, const void* k, const void* v,
+             const void* log_decay, const void* beta, const float* s0, const void* z,
+             const void* w, float* y, float* s_out, void* workspace, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d.B == 0) return GDN_OK;
+  if (d.T == 0) {
+    if (s_out == s0) return GDN_OK;
+    const size_t bytes = (size_t)(d.B * d.Hv * d.Dv * d.Dk) * sizeof(float);
+    if (hipMemcpyAsync(s_out, s0, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return device_status("state copy for T == 0");
+    return GDN_OK;
+  }
+  if (d.T == 1)  // one token: the decode kernel is the same computation, streamed once
+    return launch_step(d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
+  return launch_scan(d, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace, stream);
+}
+
+}  // namespace gdn
+
 extern "C" {
 
 int gdn_recurrent_step(const gdn_desc* d, const void* q, const void* k, const void* v,
@@ -41,18 +62,7 @@ int gdn_scan(const gdn_desc* d, const void* q, const void* k, const void* v,
   int rc = gdn::check(d, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace,
                       workspace_bytes);
   if (rc != GDN_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (d->B == 0) return GDN_OK;
-  if (d->T == 0) {
-    if (s_out == s0) return GDN_OK;
-    const size_t bytes = (size_t)(d->B * d->Hv * d->Dv * d->Dk) * sizeof(float);
-    if (hipMemcpyAsync(s_out, s0, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
-      return gdn::device_status("state copy for T == 0");
-    return GDN_OK;
-  }
-  if (d->T == 1)  // one token: the decode kernel is the same computation, streamed once
-    return gdn::launch_step(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, stream);
-  return gdn::launch_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace, stream);
+  return gdn::run_scan(*d, q, k, v, log_decay, beta, s0, z, w, y, s_out, workspace, stream);
 }
 
 int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,

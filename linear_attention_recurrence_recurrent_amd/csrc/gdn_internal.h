@@ -61,6 +61,12 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
                         const void* w, float* y, float* s_out, void* workspace, void* stream,
                         bool* gated);
 
+// gdn_scan after validation: the empty cases, T == 1 on the decode kernel,
+// else the scan (the workspace, validated, holds scan_workspace_bytes(d)).
+int run_scan(const gdn_desc& d, const void* q, const void* k, const void* v,
+             const void* log_decay, const void* beta, const float* s0, const void* z,
+             const void* w, float* y, float* s_out, void* workspace, void* stream);
+
 int launch_gates(int64_t n, const void* a, const void* b, int in_dtype, float decay_scale,
                  void* log_decay, void* beta, int out_dtype, void* stream);
 
