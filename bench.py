@@ -43,9 +43,15 @@ METRIC = "GDN decode state GB/s + scan tokens/s, % of MI355X HBM/FP32 roofline"
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3  # FP32 vector and dense FP32 matrix peak alike
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_b64_counters.txt")
-# sources the decode kernel is built from: its counters are stale once these change
-DECODE_SRC = [os.path.join(ROOT, "linear_attention_recurrence_recurrent_amd", "csrc", f)
-              for f in ("gdn_decode.hip", "gdn_device.h")]
+SCAN_COUNTERS = os.path.join(ROOT, "profiles", "scan_kernels_instruction_counters.txt")
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak
+# the kernels one default gdn_scan call launches, per scan workload
+SCAN_KERNELS = {3: ("rows_la_kernel<2, 2>", "prep_kernel<2, 2, true>", "gated_norm_kernel<2, 128>"),
+                4: ("state_kernel<1, 2>", "prep_kernel<1, 1, false>")}
+# sources the kernels are built from: their counters are stale once these change
+_CSRC = os.path.join(ROOT, "linear_attention_recurrence_recurrent_amd", "csrc")
+DECODE_SRC = [os.path.join(_CSRC, f) for f in ("gdn_decode.hip", "gdn_device.h")]
+SCAN_SRC = [os.path.join(_CSRC, f) for f in ("gdn_chunk.hip", "gdn_scan.hip", "gdn_device.h")]
 
 
 def log(msg):
@@ -68,11 +74,74 @@ def settle(fn, torch, min_ms):
     return n
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=None) -> str:
     h = hashlib.sha256()
-    for f in DECODE_SRC:
+    for f in files or DECODE_SRC:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
+
+
+def scan_matrix_figures(idx, ms):
+    """Matrix-core work of one default scan call, from the committed rocprofv3
+    counter summary (flops of the kernels' MFMA instructions per dispatch, the
+    main kernel's matrix-core busy fraction) over this run's live call time.
+    None when the summary is missing or was taken on another kernel source."""
+    if not os.path.exists(SCAN_COUNTERS):
+        return None
+    kv = {}
+    for line in open(SCAN_COUNTERS):
+        m = re.match(r"^(scan_source_sha256|matrix\.\S.*?):\s*(.*)$", line.strip())
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("scan_source_sha256") != kernel_source_hash(SCAN_SRC):
+        return None
+    tot = {"bf16": 0.0, "f16": 0.0, "f32": 0.0}
+    busy = None
+    for i, kern in enumerate(SCAN_KERNELS[idx]):
+        fields = dict(f.split("=", 1) for f in kv.get("matrix." + kern, "").split())
+        if not fields:
+            return None
+        for t in tot:
+            tot[t] += float(fields[t + "_flop"])
+        if i == 0:
+            busy = float(fields["busy"])
+    sec = ms * 1e-3
+    half = (tot["bf16"] + tot["f16"]) / sec / 1e12
+    return {"main_kernel": SCAN_KERNELS[idx][0],
+            "bf16_f16_tflops_issued": round(half, 1), "bf16_peak_tflops": BF16_PEAK_TFLOPS,
+            "frac_of_bf16_peak": round(half / BF16_PEAK_TFLOPS, 4),
+            "f32_mfma_tflops_issued": round(tot["f32"] / sec / 1e12, 2),
+            "main_kernel_matrix_busy": busy,
+            "source": "profiles/scan_kernels_instruction_counters.txt"}
+
+
+def matrix_lines(paths):
+    """Machine-readable per-kernel lines of the matrix-core counters (MOPS of
+    512 flops each; busy = SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of
+    the dispatch, GRBM_GUI_ACTIVE summing the 8 XCDs, 1024 SIMDs)."""
+    import csv
+    acc = {}
+    for path in paths:
+        per = {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                key = (row["Dispatch_Id"], _short_kernel(row["Kernel_Name"]))
+                d = per.setdefault(key, {})
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        for (_, k), d in per.items():
+            for c, v in d.items():
+                acc.setdefault(k, {}).setdefault(c, []).append(v)
+    print("scan_source_sha256: %s" % kernel_source_hash(SCAN_SRC))
+    for k, cs in sorted(acc.items()):
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        need = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+        if not all(n in avg for n in need):
+            continue
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * avg["GRBM_GUI_ACTIVE"] / 8)
+        print("matrix.%s: bf16_flop=%.6g f16_flop=%.6g f32_flop=%.6g busy=%.4f" % (
+            k, 512 * avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"], 512 * avg["SQ_INSTS_VALU_MFMA_MOPS_F16"],
+            512 * avg["SQ_INSTS_VALU_MFMA_MOPS_F32"], busy))
 
 
 def read_counters():
@@ -322,24 +391,29 @@ def bench_scan(idx, args, torch):
     s_out = torch.empty_like(d["s0"])
     stream = torch.cuda.current_stream(dev)
     dt = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
-    desc = gdn._desc(wl.B, wl.T, wl.Hk, wl.Hv, wl.Dk, wl.Dv, wl.head_major, dt, dt, True, True,
-                     1e-6, 1e-6, None if args.scan_form == "auto" else args.scan_form)
-    ws_bytes = gdn.scan_workspace_bytes(desc)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # caller-owned workspace
-    call = Launcher("gdn_scan", desc, [d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
-                                       d["z"], d["w"], y, s_out], stream.cuda_stream,
-                    extra=(ctypes.c_void_p(ws.data_ptr()), ctypes.c_uint64(ws_bytes)))
-    reps = max(3, args.steps)
-    for _ in range(max(1, args.warmup)):
-        call()
-    settle(call, torch, args.settle_ms)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    form_arg = None if args.scan_form == "auto" else args.scan_form
+
+    def timed_call(exact):
+        desc = gdn._desc(wl.B, wl.T, wl.Hk, wl.Hv, wl.Dk, wl.Dv, wl.head_major, dt, dt, True,
+                         True, 1e-6, 1e-6, form_arg, exact)
+        ws_bytes = gdn.scan_workspace_bytes(desc)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # caller-owned
+        call = Launcher("gdn_scan", desc, [d["q"], d["k"], d["v"], d["log_decay"], d["beta"],
+                                           d["s0"], d["z"], d["w"], y, s_out], stream.cuda_stream,
+                        extra=(ctypes.c_void_p(ws.data_ptr()), ctypes.c_uint64(ws_bytes)))
+        reps = max(3, args.steps)
+        for _ in range(max(1, args.warmup)):
+            call()
+        settle(call, torch, args.settle_ms)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed_call(False)
     flops = 7.0 * wl.B * wl.T * wl.Hv * wl.Dv * wl.Dk
     form = args.scan_form
     if form == "auto":
@@ -348,13 +422,24 @@ def bench_scan(idx, args, torch):
     tflops = flops / (ms * 1e-3) / 1e12
     tok = wl.B * wl.T / (ms * 1e-3)
     log("scan %d: %.1f us per call, %.2f M tok/s, %.1f TFLOP/s" % (idx, ms * 1e3, tok / 1e6, tflops))
-    products = ("f32 arithmetic; the products with the f32 state on the bf16 matrix cores over "
-                "exact bf16 parts (state 3, f16 q/k 2), each term an exact f32 product"
-                if form == "block" and wl.dtype in ("bf16", "f16") else "f32")
-    return {"workload": wl.name, "us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(tok, 1),
-            "tflops": round(tflops, 2), "peak_tflops": FP32_PEAK_TFLOPS,
-            "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "bound": bound, "form": form,
-            "algorithmic_flops_per_call": flops, "products": products}
+    res = {"workload": wl.name, "us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(tok, 1),
+           "tflops": round(tflops, 2), "peak_tflops": FP32_PEAK_TFLOPS,
+           "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "bound": bound, "form": form,
+           "algorithmic_flops_per_call": flops}
+    if form == "block" and wl.dtype in ("bf16", "f16"):
+        res["products"] = ("f32 state; its products on the bf16 matrix cores over two bf16 parts "
+                           "rounded to nearest (each term within 2^-16 of the f32 product; f16 q "
+                           "and k split exactly in two)")
+        ms_x = timed_call(True)
+        log("scan %d exact products: %.1f us per call" % (idx, ms_x * 1e3))
+        res["exact_products"] = {"us_per_call": round(ms_x * 1e3, 2),
+                                 "tflops": round(flops / (ms_x * 1e-3) / 1e12, 2),
+                                 "products": "three exact bf16 parts of the state: exact f32 "
+                                             "products"}
+    else:
+        res["products"] = "f32"
+    res["matrix_cores"] = scan_matrix_figures(idx, ms)
+    return res
 
 
 def bench_gates(args, torch):
@@ -580,12 +665,18 @@ def main():
                     help="print the per-kernel, per-grid summary of a rocprofv3 kernel trace")
     ap.add_argument("--counter-summary", metavar="CSV", nargs="+",
                     help="print per-kernel averages of rocprofv3 --pmc counter CSV files")
+    ap.add_argument("--matrix-lines", metavar="CSV", nargs="+",
+                    help="print the per-kernel matrix-core lines bench.py reads back from "
+                         "profiles/ (from the MOPS / MFMA-busy counter CSV)")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary)
         return
     if args.counter_summary:
         counter_summary(args.counter_summary)
+        return
+    if args.matrix_lines:
+        matrix_lines(args.matrix_lines)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (each (batch, "

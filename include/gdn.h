@@ -86,15 +86,19 @@ typedef enum gdn_status {
  * units for every head dim; at Dk == Dv == 128 the block form runs 16 tokens
  * at a time as dense products on the matrix cores (the step is affine in S,
  * "Module gdn" page, "The fusion").  Both give the same results up to
- * rounding: with f16/bf16 q and k the block form multiplies the f32 state
- * on the bf16 matrix cores through exact bf16 parts of its operands, each
- * term an exact f32 product, so its accuracy is that of f32 arithmetic.  Without either flag the block form runs at Dk == Dv == 128 and
- * the token-by-token form otherwise; with both flags, or GDN_SCAN_BLOCK at
- * another head dim, the call is rejected (GDN_EINVAL / GDN_EUNSUPPORTED).
- * The block form keeps per-block records in a caller-supplied workspace
- * (gdn_scan_workspace_size). */
+ * rounding.  With f16/bf16 q and k the block form multiplies the f32 state
+ * (and its per-block correction) on the bf16 matrix cores through bf16 parts:
+ * by default two parts rounded to nearest, each term then within 2^-16
+ * relative of the f32 product; with GDN_SCAN_EXACT three exact parts, each
+ * term an exact f32 product (f32 accuracy; up to 1.2x the time).
+ * f32 q and k take f32 products either way.  Without a form flag the block
+ * form runs at Dk == Dv == 128 and the token-by-token form otherwise; with
+ * both form flags, or GDN_SCAN_BLOCK at another head dim, the call is
+ * rejected (GDN_EINVAL / GDN_EUNSUPPORTED).  The block form keeps per-block
+ * records in a caller-supplied workspace (gdn_scan_workspace_size). */
 #define GDN_SCAN_PER_TOKEN 4u
 #define GDN_SCAN_BLOCK 8u
+#define GDN_SCAN_EXACT 16u
 
 typedef struct gdn_desc {
   int64_t B, T, Hk, Hv, Dk, Dv; /* batch, tokens, key heads, value heads, head dims */

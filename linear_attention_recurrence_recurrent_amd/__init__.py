@@ -17,8 +17,8 @@ from typing import Optional, Tuple
 import torch
 
 from . import _native
-from ._native import (GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GDN_SCAN_BLOCK, GDN_SCAN_PER_TOKEN,
-                      GdnDesc)
+from ._native import (GDN_FOLD_Q_SCALE, GDN_FOLD_QK_L2NORM, GDN_SCAN_BLOCK, GDN_SCAN_EXACT,
+                      GDN_SCAN_PER_TOKEN, GdnDesc)
 
 __all__ = ["recurrent_step", "recurrent_step_three_pass", "scan", "scan_noalloc",
            "scan_workspace_bytes", "gates",
@@ -45,8 +45,10 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _desc(B, T, Hk, Hv, Dk, Dv, head_major, dtype, gate_dtype, fold_qk_l2norm, fold_q_scale,
-          qk_eps, norm_eps, form=None) -> GdnDesc:
+          qk_eps, norm_eps, form=None, exact=False) -> GdnDesc:
     flags = (GDN_FOLD_QK_L2NORM if fold_qk_l2norm else 0) | (GDN_FOLD_Q_SCALE if fold_q_scale else 0)
+    if exact:
+        flags |= GDN_SCAN_EXACT
     if form == "per_token":
         flags |= GDN_SCAN_PER_TOKEN
     elif form == "block":
@@ -165,6 +167,7 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
          fold_qk_l2norm: bool = True, fold_q_scale: bool = True, qk_eps: float = 1e-6,
          norm_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
          state_out: Optional[torch.Tensor] = None, form: Optional[str] = None,
+         exact: bool = False,
          workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Gated DeltaNet recurrence over the time axis; returns (y, final_state).
 
@@ -174,7 +177,10 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
     final_state is float32 [B, Hv, D, D] (``state_out`` may be ``s0`` for an
     in-place update).  ``form`` picks the time loop: "per_token" (vector units,
     any D), "block" (16 tokens at a time on the matrix cores, D == 128), or
-    None for the library's choice for the shape.  The block form's workspace
+    None for the library's choice for the shape.  ``exact`` makes the block
+    form's products with the f32 state exact f32 products for 16-bit q and k
+    (three bf16 parts of the state instead of two rounded ones, whose terms
+    are within 2^-16 relative).  The block form's workspace
     (``scan_workspace_bytes``) is allocated here with torch on the current
     stream unless ``workspace`` (a contiguous uint8 device tensor at least
     that large) is passed."""
@@ -184,7 +190,7 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
     y = _outputs(q, v, s0, out, state_out, B, Hv, Dv, Dk)
     s_out = state_out if state_out is not None else torch.empty_like(s0)
     desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
-                 qk_eps, norm_eps, form)
+                 qk_eps, norm_eps, form, exact)
     need = scan_workspace_bytes(desc)
     ws = None
     if need:
@@ -211,8 +217,8 @@ def scan_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: t
                  w: Optional[torch.Tensor] = None, *, head_major: bool = False,
                  fold_qk_l2norm: bool = True, fold_q_scale: bool = True, qk_eps: float = 1e-6,
                  norm_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-                 state_out: Optional[torch.Tensor] = None,
-                 form: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 state_out: Optional[torch.Tensor] = None, form: Optional[str] = None,
+                 exact: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """``scan`` through gdn_scan_noalloc: the library takes no workspace and
     allocates nothing (the block form's records go to its static per-GPU
     scratch, at most 64 MiB of them; larger shapes raise GdnError).  Calls
@@ -224,7 +230,7 @@ def scan_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: t
     y = _outputs(q, v, s0, out, state_out, B, Hv, Dv, Dk)
     s_out = state_out if state_out is not None else torch.empty_like(s0)
     desc = _desc(B, T, Hk, Hv, Dk, Dv, head_major, dt, gdt, fold_qk_l2norm, fold_q_scale,
-                 qk_eps, norm_eps, form)
+                 qk_eps, norm_eps, form, exact)
     _call("gdn_scan_noalloc", desc, q, k, v, log_decay, beta, s0, z, w, y, s_out)
     return y, s_out
 

@@ -17,6 +17,7 @@ GDN_FOLD_QK_L2NORM = 1
 GDN_FOLD_Q_SCALE = 2
 GDN_SCAN_PER_TOKEN = 4
 GDN_SCAN_BLOCK = 8
+GDN_SCAN_EXACT = 16
 STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_ESHAPE", 3: "GDN_EDTYPE", 4: "GDN_EGROUP",
           5: "GDN_EUNSUPPORTED", 6: "GDN_EALIGN", 7: "GDN_EALIAS", 8: "GDN_EDEVICE",
           9: "GDN_EWORKSPACE"}

@@ -71,7 +71,8 @@ int check_desc(const gdn_desc* d) {
     return fail(GDN_EDTYPE, "bad gate_dtype %d", d->gate_dtype);
   if (d->head_major != 0 && d->head_major != 1)
     return fail(GDN_EINVAL, "head_major must be 0 or 1 (got %d)", d->head_major);
-  if (d->flags & ~(GDN_FOLD_QK_L2NORM | GDN_FOLD_Q_SCALE | GDN_SCAN_PER_TOKEN | GDN_SCAN_BLOCK))
+  if (d->flags & ~(GDN_FOLD_QK_L2NORM | GDN_FOLD_Q_SCALE | GDN_SCAN_PER_TOKEN | GDN_SCAN_BLOCK |
+                   GDN_SCAN_EXACT))
     return fail(GDN_EINVAL, "unknown flag bits 0x%x", d->flags);
   if ((d->flags & GDN_SCAN_PER_TOKEN) && (d->flags & GDN_SCAN_BLOCK))
     return fail(GDN_EINVAL, "GDN_SCAN_PER_TOKEN and GDN_SCAN_BLOCK exclude each other");

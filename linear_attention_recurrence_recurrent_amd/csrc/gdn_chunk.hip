@@ -123,6 +123,24 @@ __device__ __forceinline__ Bf3 split_bf3(float x0, float x1) {
              __builtin_amdgcn_perm(t1, t0, 0x07060302u)};
 }
 
+// An f32 value as the sum hi + lo of two bf16 values, each rounded to nearest
+// even (gfx950's v_cvt_pk_bf16_f32): hi = RN(x), lo = RN(x - hi).  x - hi is
+// exact, and each rounding keeps 8 significant bits, so
+// |x - hi - lo| <= 2^-16 |x|: a product through the two parts is the f32
+// product up to that relative error per term (the default for the state and
+// Cs with 16-bit q and k; split_bf3 keeps them exact).  Two values are packed
+// per word, the first in the low half.
+struct Bf2 {
+  uint32_t h, l;
+};
+__device__ __forceinline__ Bf2 split_bf2(float x0, float x1) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, b2));
+  const f2 r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
+  return Bf2{h, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, b2))};
+}
+
 // 16-bit fragments widened on the matrix cores.  With lane (lg, lc) holding
 // X[lc][4 lg .. 4 lg + 3] of a 16 x 16 tile packed (its raw A-operand fragment)
 // and E the identity in the same packing, mm16(E, X) leaves X[lc][4 lg + s] in
@@ -398,10 +416,12 @@ struct StateArgs {
 // The many-head shape: one workgroup per value head, its 8 waves one a-tile
 // (16 value rows) each over all 8 key tiles, two workgroups per CU; the gated
 // norm is fused.  The loads of block c + 1 are issued while block c is
-// computed.
-template <int DT>
+// computed.  NSP: parts of the state and of Cs in the products of 16-bit
+// inputs (3: exact, split_bf3; 2: rounded, split_bf2).
+template <int DT, int NSP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void state_kernel(
     StateArgs a) {
+  static_assert(NSP == 2 || NSP == 3, "two or three parts");
   constexpr int NW = 8, NT = NW * kWave, ROWS = kD, NCT = 8;
   // 16-bit inputs: q and k in LDS as bf16 parts (bf16: the value; f16: its
   // exact split into two bf16 values), the products on the bf16 matrix cores
@@ -605,23 +625,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     // only it is on the chain to the next block
     v4f pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
     if constexpr (W16) {
-      // per group of 32 keys: the three parts of S (small first) against
-      // each part of k and q
+      // per group of 32 keys: the parts of S (small first) against each part
+      // of k and q
 #pragma unroll
       for (int g4 = 0; g4 < NCT / 2; ++g4) {
-        const Bf3 a0 = split_bf3(St[2 * g4][0], St[2 * g4][1]), a1 = split_bf3(St[2 * g4][2], St[2 * g4][3]);
-        const Bf3 b0 = split_bf3(St[2 * g4 + 1][0], St[2 * g4 + 1][1]);
-        const Bf3 b1 = split_bf3(St[2 * g4 + 1][2], St[2 * g4 + 1][3]);
-        const uint4 sh = make_uint4(a0.h, a1.h, b0.h, b1.h), sm = make_uint4(a0.m, a1.m, b0.m, b1.m);
-        const uint4 sl = make_uint4(a0.l, a1.l, b0.l, b1.l);
+        uint4 sh, sm, sl;
+        if constexpr (NSP == 3) {
+          const Bf3 a0 = split_bf3(St[2 * g4][0], St[2 * g4][1]), a1 = split_bf3(St[2 * g4][2], St[2 * g4][3]);
+          const Bf3 b0 = split_bf3(St[2 * g4 + 1][0], St[2 * g4 + 1][1]);
+          const Bf3 b1 = split_bf3(St[2 * g4 + 1][2], St[2 * g4 + 1][3]);
+          sh = make_uint4(a0.h, a1.h, b0.h, b1.h);
+          sm = make_uint4(a0.m, a1.m, b0.m, b1.m);
+          sl = make_uint4(a0.l, a1.l, b0.l, b1.l);
+        } else {
+          const Bf2 a0 = split_bf2(St[2 * g4][0], St[2 * g4][1]), a1 = split_bf2(St[2 * g4][2], St[2 * g4][3]);
+          const Bf2 b0 = split_bf2(St[2 * g4 + 1][0], St[2 * g4 + 1][1]);
+          const Bf2 b1 = split_bf2(St[2 * g4 + 1][2], St[2 * g4 + 1][3]);
+          sh = make_uint4(a0.h, a1.h, b0.h, b1.h);
+          sl = make_uint4(a0.l, a1.l, b0.l, b1.l);
+        }
 #pragma unroll
         for (int p = 0; p < NPART; ++p) {
           const uint4 kA = *reinterpret_cast<const uint4*>(&sk16[p][lc][32 * g4 + 8 * lg]);
           const uint4 qA = *reinterpret_cast<const uint4*>(&sq16[p][lc][32 * g4 + 8 * lg]);
           pk = mm32bf(kA, sl, pk);
           pq = mm32bf(qA, sl, pq);
-          pk = mm32bf(kA, sm, pk);
-          pq = mm32bf(qA, sm, pq);
+          if constexpr (NSP == 3) {
+            pk = mm32bf(kA, sm, pk);
+            pq = mm32bf(qA, sm, pq);
+          }
           pk = mm32bf(kA, sh, pk);
           pq = mm32bf(qA, sh, pq);
         }
@@ -696,7 +728,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
       // the parts of Cs against the parts of k, transposed on the matrix
       // cores (mm16(X, E)); with two parts of k both go into one 16x16x32
       // product (contraction: 16 tokens x 2 parts, Cs's part given twice)
-      const Bf3 c0 = split_bf3(cs[0], cs[1]), c1 = split_bf3(cs[2], cs[3]);
+      uint32_t c0h, c0m = 0, c0l, c1h, c1m = 0, c1l;
+      if constexpr (NSP == 3) {
+        const Bf3 c0 = split_bf3(cs[0], cs[1]), c1 = split_bf3(cs[2], cs[3]);
+        c0h = c0.h, c0m = c0.m, c0l = c0.l, c1h = c1.h, c1m = c1.m, c1l = c1.l;
+      } else {
+        const Bf2 c0 = split_bf2(cs[0], cs[1]), c1 = split_bf2(cs[2], cs[3]);
+        c0h = c0.h, c0l = c0.l, c1h = c1.h, c1l = c1.l;
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         uint2 kt[NPART];
@@ -705,14 +744,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
           kt[p] = pack_bf16(mm16<GDN_BF16>(*reinterpret_cast<const uint2*>(&sk16[p][lc][key0(ct)]), eye));
         v4f acc = St[ct];
         if constexpr (NPART == 1) {
-          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.l, c1.l), acc);
-          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.m, c1.m), acc);
-          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0.h, c1.h), acc);
+          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0l, c1l), acc);
+          if constexpr (NSP == 3) acc = mm16<GDN_BF16>(kt[0], make_uint2(c0m, c1m), acc);
+          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0h, c1h), acc);
         } else {
           const uint4 ka = make_uint4(kt[0].x, kt[0].y, kt[1].x, kt[1].y);
-          acc = mm32bf(ka, make_uint4(c0.l, c1.l, c0.l, c1.l), acc);
-          acc = mm32bf(ka, make_uint4(c0.m, c1.m, c0.m, c1.m), acc);
-          acc = mm32bf(ka, make_uint4(c0.h, c1.h, c0.h, c1.h), acc);
+          acc = mm32bf(ka, make_uint4(c0l, c1l, c0l, c1l), acc);
+          if constexpr (NSP == 3) acc = mm32bf(ka, make_uint4(c0m, c1m, c0m, c1m), acc);
+          acc = mm32bf(ka, make_uint4(c0h, c1h, c0h, c1h), acc);
         }
         St[ct] = acc;
         __builtin_amdgcn_sched_barrier(0);
@@ -824,9 +863,10 @@ __device__ __forceinline__ float lds_get(const LdsElem<DT>* row, int e) {
 // products back to back.  A prologue round forms A_0 = K_0 S_0^T; the last
 // round finishes the state and O.  Each role runs its own loop with the same
 // barriers.
-template <int DT>
+template <int DT, int NSP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void rows_la_kernel(
     StateArgs a) {
+  static_assert(NSP == 2 || NSP == 3, "two or three parts of the state and Cs");
   constexpr int NC = 4, NCT = 8 / NC, ROWS = 16, KP = lds_row<DT>(), NM = 3 * kL * kL;
   typedef LdsElem<DT> KT;
   __shared__ __align__(16) KT sk[4][kL][KP];
@@ -837,7 +877,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   __shared__ v4f sb[2][NC][kWave];  // parts of B (of A_0 in the prologue)
   __shared__ v4f sp[2][NC][kWave];  // parts of P
   __shared__ v4f scs[2][kWave];     // C-scaled
-  __shared__ uint2 scp[2][3][kWave];  // its bf16 parts (16-bit inputs): lo, mid, hi
+  __shared__ uint2 scp[2][NSP][kWave];  // its bf16 parts (16-bit inputs): lo, (mid,) hi
   __shared__ v4f scc[2][kWave];     // C
   __shared__ v4f sy[2][kWave];      // Y
   __shared__ v4f sz[2][kWave];      // Z
@@ -884,11 +924,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       }
       uint4 Sh, Sm, Sl;
       auto split_state = [&]() {
-        const Bf3 p0 = split_bf3(St[0][0], St[0][1]), p1 = split_bf3(St[0][2], St[0][3]);
-        const Bf3 p2 = split_bf3(St[1][0], St[1][1]), p3 = split_bf3(St[1][2], St[1][3]);
-        Sh = make_uint4(p0.h, p1.h, p2.h, p3.h);
-        Sm = make_uint4(p0.m, p1.m, p2.m, p3.m);
-        Sl = make_uint4(p0.l, p1.l, p2.l, p3.l);
+        if constexpr (NSP == 3) {
+          const Bf3 p0 = split_bf3(St[0][0], St[0][1]), p1 = split_bf3(St[0][2], St[0][3]);
+          const Bf3 p2 = split_bf3(St[1][0], St[1][1]), p3 = split_bf3(St[1][2], St[1][3]);
+          Sh = make_uint4(p0.h, p1.h, p2.h, p3.h);
+          Sm = make_uint4(p0.m, p1.m, p2.m, p3.m);
+          Sl = make_uint4(p0.l, p1.l, p2.l, p3.l);
+        } else {
+          const Bf2 p0 = split_bf2(St[0][0], St[0][1]), p1 = split_bf2(St[0][2], St[0][3]);
+          const Bf2 p2 = split_bf2(St[1][0], St[1][1]), p3 = split_bf2(St[1][2], St[1][3]);
+          Sh = make_uint4(p0.h, p1.h, p2.h, p3.h);
+          Sl = make_uint4(p0.l, p1.l, p2.l, p3.l);
+        }
       };
       // q and k of a block, row lc, raw (rows past the last token repeat it)
       struct Blk {
@@ -930,7 +977,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
 #pragma unroll
         for (int pt = NPART - 1; pt >= 0; --pt) {
           p = mm32bf(f[pt], Sl, p);
-          p = mm32bf(f[pt], Sm, p);
+          if constexpr (NSP == 3) p = mm32bf(f[pt], Sm, p);
           p = mm32bf(f[pt], Sh, p);
         }
         return p;
@@ -976,20 +1023,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       struct CsParts {
         uint2 l, m, h;
       };
-      auto cs_parts = [&](int sl) { return CsParts{scp[sl][0][lane], scp[sl][1][lane], scp[sl][2][lane]}; };
+      auto cs_parts = [&](int sl) {
+        if constexpr (NSP == 3) return CsParts{scp[sl][0][lane], scp[sl][1][lane], scp[sl][2][lane]};
+        else return CsParts{scp[sl][0][lane], make_uint2(0u, 0u), scp[sl][1][lane]};
+      };
       auto update = [&](const CsParts& c, const Ops& o) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           v4f acc = St[ct] * o.gl;
           if constexpr (NPART == 1) {
             acc = mm16<GDN_BF16>(o.kt[ct], c.l, acc);
-            acc = mm16<GDN_BF16>(o.kt[ct], c.m, acc);
+            if constexpr (NSP == 3) acc = mm16<GDN_BF16>(o.kt[ct], c.m, acc);
             St[ct] = mm16<GDN_BF16>(o.kt[ct], c.h, acc);
           } else {
             // one 16x16x32 product per part of Cs: k's hi and lo parts
             // against the same four tokens of Cs
             acc = mm32bf(o.kt[ct], make_uint4(c.l.x, c.l.y, c.l.x, c.l.y), acc);
-            acc = mm32bf(o.kt[ct], make_uint4(c.m.x, c.m.y, c.m.x, c.m.y), acc);
+            if constexpr (NSP == 3)
+              acc = mm32bf(o.kt[ct], make_uint4(c.m.x, c.m.y, c.m.x, c.m.y), acc);
             St[ct] = mm32bf(o.kt[ct], make_uint4(c.h.x, c.h.y, c.h.x, c.h.y), acc);
           }
         }
@@ -1203,11 +1254,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       for (int i = 0; i < 4; ++i) csp[i] = cc[i] * o.srs[i];
       scs[r & 1][lane] = csp;
       scc[r & 1][lane] = cc;
-      if constexpr (DT != GDN_F32) {
+      if constexpr (DT != GDN_F32 && NSP == 3) {
         const Bf3 p0 = split_bf3(csp[0], csp[1]), p1 = split_bf3(csp[2], csp[3]);
         scp[r & 1][0][lane] = make_uint2(p0.l, p1.l);
         scp[r & 1][1][lane] = make_uint2(p0.m, p1.m);
         scp[r & 1][2][lane] = make_uint2(p0.h, p1.h);
+      } else if constexpr (DT != GDN_F32) {
+        const Bf2 p0 = split_bf2(csp[0], csp[1]), p1 = split_bf2(csp[2], csp[3]);
+        scp[r & 1][0][lane] = make_uint2(p0.l, p1.l);
+        scp[r & 1][1][lane] = make_uint2(p0.h, p1.h);
       }
     };
     auto m1cs = [&](Cops& o) {  // M1 of o's block times the newest Cs (the one before)
@@ -1451,7 +1506,7 @@ int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
   return device_status("prep_kernel launch");
 }
 
-template <int DT>
+template <int DT, int NSP>
 int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t heads,
               hipStream_t st) {
   const dim3 pgrid((unsigned)((p.ntask + 3) / 4));
@@ -1462,11 +1517,11 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
   StateArgs r = s;
   if (heads >= kManyHeads) {
     r.nrb = 1;
-    state_kernel<DT><<<dim3((unsigned)heads), 512, 0, st>>>(r);
+    state_kernel<DT, NSP><<<dim3((unsigned)heads), 512, 0, st>>>(r);
     return device_status("state_kernel launch");
   }
   r.nrb = kD / 16;
-  rows_la_kernel<DT><<<dim3((unsigned)(heads * r.nrb)), 512, 0, st>>>(r);
+  rows_la_kernel<DT, NSP><<<dim3((unsigned)(heads * r.nrb)), 512, 0, st>>>(r);
   return device_status("rows_la_kernel launch");
 }
 
@@ -1492,10 +1547,17 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
                    (int)(d.Hv / d.Hk), d.head_major, d.flags, d.qk_eps, q_scale(d), mx};
   const StateArgs s{q, k, v, z, w, rec, s0, y, s_out, d.T, nblk, (int)d.Hk, (int)d.Hv,
                     (int)(d.Hv / d.Hk), 1, d.head_major, d.norm_eps, mx};
+  // 16-bit inputs: the state and Cs in two rounded bf16 parts, or three
+  // exact ones with GDN_SCAN_EXACT; f32 inputs use f32 products either way
+  const bool exact = (d.flags & GDN_SCAN_EXACT) != 0;
   switch (d.dtype) {
-    case GDN_F32: return launch_dt<GDN_F32>(d, p, s, heads, st);
-    case GDN_F16: return launch_dt<GDN_F16>(d, p, s, heads, st);
-    default: return launch_dt<GDN_BF16>(d, p, s, heads, st);
+    case GDN_F32: return launch_dt<GDN_F32, 3>(d, p, s, heads, st);
+    case GDN_F16:
+      return exact ? launch_dt<GDN_F16, 3>(d, p, s, heads, st)
+                   : launch_dt<GDN_F16, 2>(d, p, s, heads, st);
+    default:
+      return exact ? launch_dt<GDN_BF16, 3>(d, p, s, heads, st)
+                   : launch_dt<GDN_BF16, 2>(d, p, s, heads, st);
   }
 }
 

@@ -115,7 +115,7 @@ def test_accepts_valid_arguments():
     ("Dv", 48, 5, "Dk == Dv"),
     ("dtype", 7, 3, "dtype"),
     ("gate_dtype", -1, 3, "gate_dtype"),
-    ("flags", 16, 1, "flag"),
+    ("flags", 32, 1, "flag"),
     ("flags", 12, 1, "exclude"),
     ("head_major", 2, 1, "head_major"),
     ("qk_eps", -1.0, 1, "eps"),

@@ -64,7 +64,7 @@ def _ops(B, T, Hk, Hv, dt, seed):
     return ops
 
 
-def _run(ops, dt, head_major, gated):
+def _run(ops, dt, head_major, gated, exact=False):
     """GPU scan (default form = block form at D = 128) and the oracle on the same values."""
     tdt = synth.DTYPES[dt]
 
@@ -79,7 +79,8 @@ def _run(ops, dt, head_major, gated):
 
     d = {n: dev(n) for n in ops}
     y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
-                d["z"] if gated else None, d["w"] if gated else None, head_major=head_major)
+                d["z"] if gated else None, d["w"] if gated else None, head_major=head_major,
+                exact=exact)
     torch.cuda.synchronize()
     y = y.double().cpu().numpy()
     if head_major:
@@ -101,6 +102,7 @@ def _close(got, ref, tol, what):
 
 
 CASES = [(kind, dt, hm) for kind in SHAPES for dt in ("f32", "bf16", "f16") for hm in (False, True)]
+# the 16-bit block form's default (two rounded bf16 parts of the state) and exact (three) modes
 IDS = ["%s-%s-%s" % (c[0], c[1], "hm" if c[2] else "tm") for c in CASES]
 
 
@@ -157,9 +159,17 @@ def _hadamard_keys(B, T, Hk, seed):
     return k
 
 
-@pytest.mark.parametrize("case", CASES, ids=IDS)
+# f32 operands take f32 products in both modes, so only 16-bit cases run exact
+RECALL = [(c, False) for c in CASES] + [(c, True) for c in CASES if c[1] != "f32"]
+
+
+RECALL_IDS = ["%s-%s-%s-%s" % (c[0], c[1], "hm" if c[2] else "tm", "exact" if e else "default")
+              for c, e in RECALL]
+
+
+@pytest.mark.parametrize("case,exact", RECALL, ids=RECALL_IDS)
 @pytest.mark.parametrize("T", [128, 100])
-def test_associative_recall_orthonormal_keys(case, T):
+def test_associative_recall_orthonormal_keys(case, exact, T):
     kind, dt, hm = case
     B, Hk, Hv = SHAPES[kind]
     say("identity associative recall T=%d %s" % (T, case))
@@ -173,7 +183,7 @@ def test_associative_recall_orthonormal_keys(case, T):
     # each query repeats the key of an earlier (or the same) token
     src = np.array([r.integers(0, t + 1) for t in range(T)])
     ops["q"] = ops["k"][:, src].copy()
-    y, s = _run(ops, dt, hm, gated=False)
+    y, s = _run(ops, dt, hm, gated=False, exact=exact)
     kh = _unit(np.repeat(ops["k"], G, axis=2))                     # [B, T, Hv, D]
     recall = np.einsum("bhac,bthc->btha", s, kh)
     _close(recall, ops["v"], CLOSED, "S_T k^_j = v_j")

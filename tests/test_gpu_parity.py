@@ -213,11 +213,16 @@ def test_block_form_edge_shapes(case, gated):
 
 
 # The block form with 16-bit q and k forms its products with the f32 state on
-# the bf16 matrix cores over exact bf16 parts (three of the state and of Cs,
-# two of an f16 value), so it must be as accurate as the f32 path: within
-# f32 rounding of the float64 oracle, far inside the 3e-3 bar for 16-bit
-# operands.  (Measured: <= 2.3e-6 on the gated y, <= 1e-7 on the state.)
+# the bf16 matrix cores over bf16 parts.  With exact=True the state and Cs go
+# in three exact parts (two for an f16 value of q or k), so every term is an
+# exact f32 product and the result is within f32 rounding of the float64
+# oracle (measured: <= 7.4e-6 on the gated y, <= 8.8e-7 on the state, over
+# these cases and the full-size workloads).  By default they go in two parts
+# rounded to nearest, each term within 2^-16 relative of the f32 product
+# (measured: <= 8.5e-5 on the gated y, <= 8.5e-6 on the state), still 35x
+# inside the 3e-3 bar for 16-bit operands.
 F32_LEVEL = 2e-5
+TWO_PART_LEVEL = 2e-4
 SIXTEEN_BIT_CASES = [
     (1, 200, 2, 4, "bf16", False),   # few heads (rows_la_kernel), token-major
     (1, 200, 2, 4, "f16", True),     # few heads, f16 q/k split in two bf16 parts, head-major
@@ -229,20 +234,23 @@ SIXTEEN_BIT_CASES = [
 @pytest.mark.parametrize("case", SIXTEEN_BIT_CASES, ids=lambda c: "B%dT%dHk%dHv%d-%s-%s" % (
     c[0], c[1], c[2], c[3], c[4], "hm" if c[5] else "tm"))
 @pytest.mark.parametrize("gated", [True, False])
-def test_block_form_16bit_at_f32_accuracy(case, gated):
+@pytest.mark.parametrize("exact", [True, False])
+def test_block_form_16bit_accuracy(case, gated, exact):
     B, T, Hk, Hv, dtype, hm = case
-    say("16-bit block form at f32 accuracy %s gated=%s" % (case, gated))
+    say("16-bit block form accuracy %s gated=%s exact=%s" % (case, gated, exact))
     ops = synth.random_operands(B, T, Hk, Hv, 128, 128, dtype=dtype, head_major=hm,
                                 seed=B * 7 + T + Hv)
     d = dev(ops)
     z, w = (d.get("z"), d.get("w")) if gated else (None, None)
-    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], z, w, head_major=hm)
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], z, w, head_major=hm,
+                exact=exact)
     torch.cuda.synchronize()
     yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
                       ops.get("z") if gated else None, ops.get("w") if gated else None,
                       head_major=hm)
-    assert_close(y, yr, F32_LEVEL, "y")
-    assert_close(s, sr, F32_LEVEL, "final_state")
+    level = F32_LEVEL if exact else TWO_PART_LEVEL
+    assert_close(y, yr, level, "y")
+    assert_close(s, sr, level, "final_state")
 
 
 def test_gate_dtype_differs_from_operand_dtype():
@@ -338,22 +346,28 @@ def test_mixed_fast_and_checked_chunks(case, form):
     run_both(ops, head_major=hm, gated=True, dtype=dtype, form=form)
 
 
-def test_in_place_state_and_time_chaining():
+@pytest.mark.parametrize("exact", [True, False])
+def test_in_place_state_and_time_chaining(exact):
+    """Chaining pieces (in place) equals one scan: within f32 rounding for exact
+    products, within the two-part level by default (the pieces block the tokens
+    differently, so the rounded parts differ)."""
     ops = synth.random_operands(2, 40, 2, 4, 128, 128, dtype="bf16", seed=9)
     d = dev(ops)
-    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"])
+    tol = 1e-5 if exact else TWO_PART_LEVEL
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"],
+                exact=exact)
     st = d["s0"].clone()
     parts = []
     for a, b in ((0, 13), (13, 14), (14, 40)):  # includes a single-token piece
         sl = {n: d[n][:, a:b].contiguous() for n in ("q", "k", "v", "z", "log_decay", "beta")}
         yp, st2 = scan(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["beta"], st, sl["z"],
-                       d["w"], state_out=st)
+                       d["w"], state_out=st, exact=exact)
         assert st2.data_ptr() == st.data_ptr()
         parts.append(yp)
     torch.cuda.synchronize()
     ych = torch.cat(parts, dim=1)
-    assert_close(ych, y.double().cpu().numpy(), 1e-5, "chained y")
-    assert_close(st, s.double().cpu().numpy(), 1e-5, "chained state")
+    assert_close(ych, y.double().cpu().numpy(), tol, "chained y")
+    assert_close(st, s.double().cpu().numpy(), tol, "chained state")
 
 
 def test_steps_equal_scan():
@@ -496,14 +510,17 @@ def test_config2_chained_decode_every_head(gated):
     assert_close(state, sr, TOL["bf16"], "config2 final state")
 
 
+FORMS = [(None, False), ("per_token", False), ("block", False), ("block", True)]
+
+
 @pytest.mark.parametrize("gated", [True, False])
-@pytest.mark.parametrize("form", [None, "per_token", "block"])
-def test_config3_prefill_scan_every_head(form, gated):
+@pytest.mark.parametrize("form,exact", FORMS)
+def test_config3_prefill_scan_every_head(form, exact, gated):
     wl = synth.WORKLOADS[3]
-    say("config3: B=1 T=4096 token-major scan, form %s, gated=%s" % (form, gated))
+    say("config3: B=1 T=4096 token-major scan, form %s exact %s, gated=%s" % (form, exact, gated))
     d = dev(synth.make(wl))
     y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
-                d["z"] if gated else None, d["w"] if gated else None, form=form)
+                d["z"] if gated else None, d["w"] if gated else None, form=form, exact=exact)
     torch.cuda.synchronize()
     yr, sr = _oracle_full(3, gated)
     assert_close(y, yr, TOL["bf16"], "config3 y")
@@ -511,14 +528,15 @@ def test_config3_prefill_scan_every_head(form, gated):
 
 
 @pytest.mark.parametrize("gated", [True, False])
-@pytest.mark.parametrize("form", [None, "per_token", "block"])
-def test_config4_head_major_scan_every_head(form, gated):
+@pytest.mark.parametrize("form,exact", FORMS)
+def test_config4_head_major_scan_every_head(form, exact, gated):
     wl = synth.WORKLOADS[4]
-    say("config4: B=16 T=1024 head-major f16 scan, form %s, gated=%s" % (form, gated))
+    say("config4: B=16 T=1024 head-major f16 scan, form %s exact %s, gated=%s" % (
+        form, exact, gated))
     d = dev(synth.make(wl))
     y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
                 d["z"] if gated else None, d["w"] if gated else None, head_major=True,
-                form=form)
+                form=form, exact=exact)
     torch.cuda.synchronize()
     yr, sr = _oracle_full(4, gated)
     assert_close(y, yr, TOL["f16"], "config4 y")
