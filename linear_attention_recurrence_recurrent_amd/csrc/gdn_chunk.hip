@@ -185,6 +185,19 @@ __device__ __forceinline__ Bases head_bases(int64_t b, int hv, int hk, int Hk, i
 // ---------------------------------------------------------------------------
 // Block pieces that do not depend on the state.
 
+// Entry (row, col) of a 16 x 16 block written as two bf16 parts rounded to
+// nearest (hi = RN(x), lo = RN(x - hi)), in 16-byte chunks of four columns:
+// chunk 4 row + col / 4 holds the four hi values, then the four lo values.
+// A lane reading chunk 4 lc + lg then has the hi and lo A fragments of a
+// 16x16x16 bf16 product over row lc (the few-head chain wave's T and M1).
+__device__ __forceinline__ void store_parts16(float* base, int row, int col, float x) {
+  const uint16_t h = __builtin_bit_cast(uint16_t, (__bf16)x);
+  const uint16_t l = __builtin_bit_cast(uint16_t, (__bf16)(x - __uint_as_float((uint32_t)h << 16)));
+  uint16_t* p = reinterpret_cast<uint16_t*>(base) + 8 * (4 * row + col / 4) + col % 4;
+  p[0] = h;
+  p[4] = l;
+}
+
 struct PrepArgs {
   const void *q, *k, *ld, *beta;
   float* rec;
@@ -199,9 +212,12 @@ struct PrepArgs {
 // records of the G value heads that share the key head (four at a time, one
 // per 16-lane group).  No workgroup barrier: each wave owns its LDS slice.
 // XB: also the products across blocks into a.mx (the few-head kernel's; a
-// separate instance, so the many-head prep keeps its register count)
-template <int DT, int GT, bool XB>
+// separate instance, so the many-head prep keeps its register count).
+// TP: T, M1, M2 and N written as two rounded bf16 parts (store_parts16) for
+// the few-head kernel's default products.
+template <int DT, int GT, bool XB, bool TP>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  static_assert(XB || !TP, "the parts layout is the few-head kernel's");
   __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int lg = lane / 16, lc = lane % 16;
@@ -323,9 +339,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     float* mx = a.mx + task * (3 * kL * kL);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      mx[16 * (4 * lg + r) + lc] = M1[r];
-      mx[kL * kL + 16 * (4 * lg + r) + lc] = M2[r];
-      mx[2 * kL * kL + 16 * (4 * lg + r) + lc] = N1[r];
+      if constexpr (TP) {
+        store_parts16(mx, 4 * lg + r, lc, M1[r]);
+        store_parts16(mx + kL * kL, 4 * lg + r, lc, M2[r]);
+        store_parts16(mx + 2 * kL * kL, 4 * lg + r, lc, N1[r]);
+      } else {
+        mx[16 * (4 * lg + r) + lc] = M1[r];
+        mx[kL * kL + 16 * (4 * lg + r) + lc] = M2[r];
+        mx[2 * kL * kL + 16 * (4 * lg + r) + lc] = N1[r];
+      }
     }
   }
   float rki[4], rqi[4];  // norms of the lane's rows i = 4 lg + r
@@ -390,7 +412,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         x[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
 #pragma unroll
-      for (int r = 0; r < kL; ++r) rec[kRecT + 16 * r + lc] = x[r];
+      for (int r = 0; r < kL; ++r) {
+        if constexpr (TP) store_parts16(rec + kRecT, r, lc, x[r]);
+        else rec[kRecT + 16 * r + lc] = x[r];
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -879,6 +904,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   __shared__ v4f scs[2][kWave];     // C-scaled
   __shared__ uint2 scp[2][NSP][kWave];  // its bf16 parts (16-bit inputs): lo, (mid,) hi
   __shared__ v4f scc[2][kWave];     // C
+  // chain, Y and Z products on bf16 parts (16-bit inputs, two parts): the
+  // prep then writes T, M1, M2 and N as parts (store_parts16), staged like
+  // the f32 values
+  constexpr bool BFCHAIN = DT != GDN_F32 && NSP == 2;
   __shared__ v4f sy[2][kWave];      // Y
   __shared__ v4f sz[2][kWave];      // Z
 
@@ -1216,19 +1245,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   if (wave == NC) {
     // ---- chain wave: C of block r.  K_r S_r^T = gam(r-1) (gam(r-2) sum B_r
     // + Y_r) + M1_r Cs_(r-1); the last term is formed at the start of round
-    // r, the record of block r read at the start of round r - 1.
+    // r, the record of block r read at the start of round r - 1.  With two
+    // bf16 parts (BFCHAIN) both products run as three 16x16x16 bf16 products
+    // over the rounded parts (hi.hi + hi.lo + lo.hi; the prep writes T and M1
+    // as parts, this wave splits Y and Cs), instead of four f32 16x16x4 ones
+    // each: the SIMD's issue is shared with a state wave.
     __builtin_amdgcn_s_setprio(3);  // ahead of the state wave on its SIMD
     struct Cops {
       float4 tf, m1;
+      uint2 th, tl, mh, ml;
       float be[4], wsc[4], srs[4], v[4];
       float g1, g2;
       v4f mc;
     };
     v4f csp = {0.f, 0.f, 0.f, 0.f};
+    uint2 cph = make_uint2(0u, 0u), cpl = make_uint2(0u, 0u);  // csp's parts (BFCHAIN)
     auto fetch = [&](int64_t r, Cops& o, float g1, float g2) {
       const int s = (int)(r & 3);
-      o.tf = *reinterpret_cast<const float4*>(&srec[s][kRecT + 16 * lc + 4 * lg]);
-      o.m1 = *reinterpret_cast<const float4*>(&smx[s][16 * lc + 4 * lg]);
+      if constexpr (BFCHAIN) {  // T[lc][4 lg ..] and M1[lc][4 lg ..]: four hi, four lo
+        const uint4 t = *reinterpret_cast<const uint4*>(&srec[s][kRecT + 16 * lc + 4 * lg]);
+        const uint4 m = *reinterpret_cast<const uint4*>(&smx[s][16 * lc + 4 * lg]);
+        o.th = make_uint2(t.x, t.y);
+        o.tl = make_uint2(t.z, t.w);
+        o.mh = make_uint2(m.x, m.y);
+        o.ml = make_uint2(m.z, m.w);
+      } else {
+        o.tf = *reinterpret_cast<const float4*>(&srec[s][kRecT + 16 * lc + 4 * lg]);
+        o.m1 = *reinterpret_cast<const float4*>(&smx[s][16 * lc + 4 * lg]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         o.be[i] = srec[s][kRecBe + 4 * lg + i];
@@ -1244,15 +1288,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         yv[i] = o.be[i] * o.v[i] - o.wsc[i] * fmaf(o.g1, fmaf(o.g2, bsum[i], y[i]), o.mc[i]);
-      const float4 tf = o.tf;
       v4f cc = {0.f, 0.f, 0.f, 0.f};
-      cc = mfma4(tf.x, yv[0], cc);
-      cc = mfma4(tf.y, yv[1], cc);
-      cc = mfma4(tf.z, yv[2], cc);
-      cc = mfma4(tf.w, yv[3], cc);
+      if constexpr (BFCHAIN) {
+        const Bf2 y0 = split_bf2(yv[0], yv[1]), y1 = split_bf2(yv[2], yv[3]);
+        const uint2 yh = make_uint2(y0.h, y1.h), yl = make_uint2(y0.l, y1.l);
+        cc = mm16<GDN_BF16>(o.tl, yh, cc);
+        cc = mm16<GDN_BF16>(o.th, yl, cc);
+        cc = mm16<GDN_BF16>(o.th, yh, cc);
+      } else {
+        const float4 tf = o.tf;
+        cc = mfma4(tf.x, yv[0], cc);
+        cc = mfma4(tf.y, yv[1], cc);
+        cc = mfma4(tf.z, yv[2], cc);
+        cc = mfma4(tf.w, yv[3], cc);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) csp[i] = cc[i] * o.srs[i];
-      scs[r & 1][lane] = csp;
+      if constexpr (!BFCHAIN) scs[r & 1][lane] = csp;  // (BFCHAIN: Y and Z take its parts)
       scc[r & 1][lane] = cc;
       if constexpr (DT != GDN_F32 && NSP == 3) {
         const Bf3 p0 = split_bf3(csp[0], csp[1]), p1 = split_bf3(csp[2], csp[3]);
@@ -1261,16 +1313,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
         scp[r & 1][2][lane] = make_uint2(p0.h, p1.h);
       } else if constexpr (DT != GDN_F32) {
         const Bf2 p0 = split_bf2(csp[0], csp[1]), p1 = split_bf2(csp[2], csp[3]);
-        scp[r & 1][0][lane] = make_uint2(p0.l, p1.l);
-        scp[r & 1][1][lane] = make_uint2(p0.h, p1.h);
+        cpl = make_uint2(p0.l, p1.l);
+        cph = make_uint2(p0.h, p1.h);
+        scp[r & 1][0][lane] = cpl;
+        scp[r & 1][1][lane] = cph;
       }
     };
     auto m1cs = [&](Cops& o) {  // M1 of o's block times the newest Cs (the one before)
       v4f d = {0.f, 0.f, 0.f, 0.f};
-      d = mfma4(o.m1.x, csp[0], d);
-      d = mfma4(o.m1.y, csp[1], d);
-      d = mfma4(o.m1.z, csp[2], d);
-      d = mfma4(o.m1.w, csp[3], d);
+      if constexpr (BFCHAIN) {
+        d = mm16<GDN_BF16>(o.ml, cph, d);
+        d = mm16<GDN_BF16>(o.mh, cpl, d);
+        d = mm16<GDN_BF16>(o.mh, cph, d);
+      } else {
+        d = mfma4(o.m1.x, csp[0], d);
+        d = mfma4(o.m1.y, csp[1], d);
+        d = mfma4(o.m1.z, csp[2], d);
+        d = mfma4(o.m1.w, csp[3], d);
+      }
       o.mc = d;
     };
     auto bparts = [&](int64_t r) {
@@ -1447,15 +1507,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   // barrier instead of after the products.
   auto round = [&](int64_t r, Regs& P) {
     __syncthreads();
-    const v4f cs = scs[(r - 1) & 1][lane];
     const float* m = ywave ? &smx[(r + 1) & 3][kL * kL] : &smx[r & 3][2 * kL * kL];
-    const float4 mf = *reinterpret_cast<const float4*>(&m[16 * lc + 4 * lg]);
-    restage(P, (int)((r + 2) & 3), r + 5);
     v4f d = {0.f, 0.f, 0.f, 0.f};
-    d = mfma4(mf.x, cs[0], d);
-    d = mfma4(mf.y, cs[1], d);
-    d = mfma4(mf.z, cs[2], d);
-    d = mfma4(mf.w, cs[3], d);
+    if constexpr (BFCHAIN) {
+      // M2 or N as two bf16 parts (prep), Cs as its parts (chain wave):
+      // three 16x16x16 bf16 products
+      const uint2 cl = scp[(r - 1) & 1][0][lane], ch = scp[(r - 1) & 1][1][lane];
+      const uint4 mp = *reinterpret_cast<const uint4*>(&m[16 * lc + 4 * lg]);
+      restage(P, (int)((r + 2) & 3), r + 5);
+      d = mm16<GDN_BF16>(make_uint2(mp.z, mp.w), ch, d);
+      d = mm16<GDN_BF16>(make_uint2(mp.x, mp.y), cl, d);
+      d = mm16<GDN_BF16>(make_uint2(mp.x, mp.y), ch, d);
+    } else {
+      const v4f cs = scs[(r - 1) & 1][lane];
+      const float4 mf = *reinterpret_cast<const float4*>(&m[16 * lc + 4 * lg]);
+      restage(P, (int)((r + 2) & 3), r + 5);
+      d = mfma4(mf.x, cs[0], d);
+      d = mfma4(mf.y, cs[1], d);
+      d = mfma4(mf.z, cs[2], d);
+      d = mfma4(mf.w, cs[3], d);
+    }
     if (ywave) sy[(r + 1) & 1][lane] = d;
     else sz[r & 1][lane] = d;
   };
@@ -1486,22 +1557,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   __syncthreads();
 }
 
-template <int DT>
+template <int DT, int GT, bool TP>
+void launch_prep_gt(const PrepArgs& p, dim3 grid, hipStream_t st) {
+  if (p.mx != nullptr) prep_kernel<DT, GT, true, TP><<<grid, 256, 0, st>>>(p);
+  else prep_kernel<DT, GT, false, false><<<grid, 256, 0, st>>>(p);
+}
+
+template <int DT, bool TP>
 int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
-  const bool xb = p.mx != nullptr;
   switch (gdt) {
-    case GDN_F32:
-      if (xb) prep_kernel<DT, GDN_F32, true><<<grid, 256, 0, st>>>(p);
-      else prep_kernel<DT, GDN_F32, false><<<grid, 256, 0, st>>>(p);
-      break;
-    case GDN_F16:
-      if (xb) prep_kernel<DT, GDN_F16, true><<<grid, 256, 0, st>>>(p);
-      else prep_kernel<DT, GDN_F16, false><<<grid, 256, 0, st>>>(p);
-      break;
-    default:
-      if (xb) prep_kernel<DT, GDN_BF16, true><<<grid, 256, 0, st>>>(p);
-      else prep_kernel<DT, GDN_BF16, false><<<grid, 256, 0, st>>>(p);
-      break;
+    case GDN_F32: launch_prep_gt<DT, GDN_F32, TP>(p, grid, st); break;
+    case GDN_F16: launch_prep_gt<DT, GDN_F16, TP>(p, grid, st); break;
+    default: launch_prep_gt<DT, GDN_BF16, TP>(p, grid, st); break;
   }
   return device_status("prep_kernel launch");
 }
@@ -1510,7 +1577,8 @@ template <int DT, int NSP>
 int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t heads,
               hipStream_t st) {
   const dim3 pgrid((unsigned)((p.ntask + 3) / 4));
-  const int rc = launch_prep<DT>(p, d.gate_dtype, pgrid, st);
+  // the few-head kernel's default products take T and M1 as bf16 parts
+  const int rc = launch_prep<DT, DT != GDN_F32 && NSP == 2>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;
   // many heads: whole-head workgroups, two per CU, the norm fused; few heads:
   // a workgroup per 16 value rows with the one-block lookahead
