@@ -219,6 +219,7 @@ template <int DT, int GT, bool XB, bool TP>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   static_assert(XB || !TP, "the parts layout is the few-head kernel's");
   __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
+  __shared__ __align__(16) float sAB[4][2][4][kL];  // [wave][alpha, beta][value head][token]
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int lg = lane / 16, lc = lane % 16;
   const int64_t task = (int64_t)blockIdx.x * 4 + wave;
@@ -366,11 +367,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     // block start through lc, and after lc to the block end
     const float gam = row_prefix_prod(al), tail = dpp_or_one<0x101, 0xF>(row_suffix_prod(al));
     const int ng = a.G - g0 < 4 ? a.G - g0 : 4;
+    // every lane's alpha and beta into the wave's LDS slice ([value head of
+    // the group][token]); each lane then reads what it needs in a few vector
+    // reads (cross-lane shuffles one row at a time formed a chain of LDS
+    // round trips)
+    sAB[wave][0][lg][lc] = al;
+    sAB[wave][1][lg][lc] = be;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int gq = 0; gq < ng; ++gq) {  // Ls and Hd of value head g0 + gq, all lanes
-      float als[kL];
+      float als[kL];  // the 16 alphas of value head g0 + gq (the same in every lane)
 #pragma unroll
-      for (int m = 0; m < kL; ++m)
-        als[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * gq + m));
+      for (int m4 = 0; m4 < kL / 4; ++m4) {
+        const float4 x = *reinterpret_cast<const float4*>(&sAB[wave][0][gq][4 * m4]);
+        als[4 * m4] = x.x, als[4 * m4 + 1] = x.y, als[4 * m4 + 2] = x.z, als[4 * m4 + 3] = x.w;
+      }
+      // alpha and beta of the lane's rows i = 4 lg .. 4 lg + 3
+      const float4 ar = *reinterpret_cast<const float4*>(&sAB[wave][0][gq][4 * lg]);
+      const float4 br = *reinterpret_cast<const float4*>(&sAB[wave][1][gq][4 * lg]);
+      const float ari[4] = {ar.x, ar.y, ar.z, ar.w}, bri[4] = {br.x, br.y, br.z, br.w};
       float* rec = a.rec + record_at(b * a.Hv + hk * a.G + g0 + gq, c, a.nblk);
       // Dc[i][j] for j = lc and the rows i = 4 lg .. 4 lg + 3: the product up to
       // row 4 lg, then one decay per row
@@ -381,14 +397,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * lg + r;
-        if (r > 0) {
-          // alpha of row i from the lane that holds it (selecting it from
-          // als by lg becomes an indexed array in scratch memory)
-          const float ai = __shfl(al, 16 * gq + i);
-          dc = j < i ? dc * ai : (j == i ? 1.f : 0.f);
-        }
-        const float bei = __shfl(be, 16 * gq + i);
-        sLs[wave][gq][i][j] = j < i ? bei * rki[r] * G4[r] * rk * dc : 0.f;
+        if (r > 0) dc = j < i ? dc * ari[r] : (j == i ? 1.f : 0.f);
+        sLs[wave][gq][i][j] = j < i ? bri[r] * rki[r] * G4[r] * rk * dc : 0.f;
         rec[kRecH + 16 * i + j] = j <= i ? rqi[r] * H4[r] * rk * dc : 0.f;
       }
     }
