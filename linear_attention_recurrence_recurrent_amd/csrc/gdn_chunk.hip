@@ -220,13 +220,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   static_assert(XB || !TP, "the parts layout is the few-head kernel's");
   __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
   __shared__ __align__(16) float sAB[4][2][4][kL];  // [wave][alpha, beta][value head][token]
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  // the wave index through readfirstlane: everything derived from the task
+  // is then uniform (scalar), not computed per lane; the task count is below
+  // 2^31 (B * T * Hv is), so 32-bit divisions suffice
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
   const int64_t task = (int64_t)blockIdx.x * 4 + wave;
   if (task >= a.ntask) return;  // uniform per wave
-  const int64_t c = task % a.nblk, bk = task / a.nblk;
-  const int hk = (int)(bk % a.Hk);
-  const int64_t b = bk / a.Hk, T = a.T, t0 = c * kL;
+  const uint32_t tk = (uint32_t)task, nb = (uint32_t)a.nblk;
+  const int64_t c = tk % nb, bk = tk / nb;
+  const int hk = (int)((uint32_t)bk % (uint32_t)a.Hk);
+  const int64_t b = (uint32_t)bk / (uint32_t)a.Hk, T = a.T, t0 = c * kL;
   const int tc = (int)((T - t0) < kL ? (T - t0) : kL);
   int64_t qk_base, qk_ts;
   if (a.head_major) {
@@ -238,12 +243,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   // Every load of the wave is issued here, before any of them is used, so
   // that their latencies overlap (one round trip instead of one per use).
   // Rows of q and k: lane (lg, lc) holds row lc, elements [32 lg, 32 lg + 32)
+  // Addresses: a block base (uniform) plus a 32-bit offset per lane, so no
+  // lane computes a 64-bit product.
+  const uint32_t loff = (uint32_t)lc * (uint32_t)qk_ts + 32u * (uint32_t)lg;
   Raw<DT, 8> kr[4], qr[4];
+  const int64_t rowb = qk_base + t0 * qk_ts;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (lc < tc) {
-      kr[u].load(a.k, qk_base + (t0 + lc) * qk_ts + 32 * lg + 8 * u);
-      qr[u].load(a.q, qk_base + (t0 + lc) * qk_ts + 32 * lg + 8 * u);
+      kr[u].load(a.k, rowb + (int64_t)(loff + 8u * u));
+      qr[u].load(a.q, rowb + (int64_t)(loff + 8u * u));
     } else {
       kr[u].zero();
       qr[u].zero();
@@ -254,23 +263,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   [[maybe_unused]] Raw<DT, 8> kp1[4], kp2[4];
   if constexpr (XB) {
     const int64_t c1 = c > 0 ? c - 1 : 0, c2 = c > 1 ? c - 2 : 0;
+    const int64_t b1r = qk_base + c1 * kL * qk_ts, b2r = qk_base + c2 * kL * qk_ts;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      kp1[u].load(a.k, qk_base + (c1 * kL + lc) * qk_ts + 32 * lg + 8 * u);
-      kp2[u].load(a.k, qk_base + (c2 * kL + lc) * qk_ts + 32 * lg + 8 * u);
+      kp1[u].load(a.k, b1r + (int64_t)(loff + 8u * u));
+      kp2[u].load(a.k, b2r + (int64_t)(loff + 8u * u));
     }
   }
   // gates: lane (lg, lc) loads token lc of value head g0 + lg
   Raw<GT, 1> l1, b1;
   bool gld = false;
   auto gates_load = [&](int g0) {
-    const int g = g0 + lg, hv = hk * a.G + g;
+    const int g = g0 + lg;
     gld = g < a.G && lc < tc;
+    const int64_t hv0 = (int64_t)hk * a.G + g0;  // first value head of the group
+    const int64_t gb = a.head_major ? (b * a.Hv + hv0) * T + t0 : (b * T + t0) * a.Hv + hv0;
+    const uint32_t go = a.head_major ? (uint32_t)lg * (uint32_t)T + (uint32_t)lc
+                                     : (uint32_t)lc * (uint32_t)a.Hv + (uint32_t)lg;
     if (gld) {
-      const int64_t gi = a.head_major ? (b * a.Hv + hv) * T + t0 + lc
-                                      : (b * T + t0 + lc) * a.Hv + hv;
-      l1.load(a.ld, gi);
-      b1.load(a.beta, gi);
+      l1.load(a.ld, gb + (int64_t)go);
+      b1.load(a.beta, gb + (int64_t)go);
     }
   };
   gates_load(0);
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
   for (int g0 = 0; g0 < a.G; g0 += 4) {
     if (g0 > 0) gates_load(g0);
-    const int g = g0 + lg, hv = hk * a.G + g;
+    const int g = g0 + lg;
     const bool gv = g < a.G;
     const float al = gld ? expf(l1.get(0)) : 1.f, be = gld ? b1.get(0) : 0.f;
     // decay products of token lc of each 16-lane row's value head: from the
@@ -406,7 +418,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (gv) {  // lane group lg: value head g; lane lc: token lc and column lc
-      float* rec = a.rec + record_at(b * a.Hv + hv, c, a.nblk);
+      float* rec = a.rec + record_at(b * a.Hv + hk * a.G + g0, c, a.nblk) +
+                   (int64_t)lg * (a.nblk * kRec);
       rec[kRecSig + lc] = gam * rq;
       rec[kRecWsc + lc] = be * gam * rk;
       rec[kRecBe + lc] = be;
@@ -476,7 +489,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int64_t bh = tile;
   const int hv = (int)(bh % a.Hv), hk = hv / a.G;
   const int64_t b = bh / a.Hv;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar index math
   const int lg = lane / 16, lc = lane % 16;
   const int ai = wave;  // this wave's a-tile (value rows 16 ai ..), all key tiles
   const int64_t T = a.T;
