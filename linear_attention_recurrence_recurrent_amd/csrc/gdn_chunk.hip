@@ -213,8 +213,8 @@ struct PrepArgs {
 // per 16-lane group).  No workgroup barrier: each wave owns its LDS slice.
 // XB: also the products across blocks into a.mx (the few-head kernel's; a
 // separate instance, so the many-head prep keeps its register count).
-// TP: T, M1, M2 and N written as two rounded bf16 parts (store_parts16) for
-// the few-head kernel's default products.
+// TP: T, Hd, M1, M2 and N written as two rounded bf16 parts (store_parts16)
+// for the few-head kernel's default products.
 template <int DT, int GT, bool XB, bool TP>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   static_assert(XB || !TP, "the parts layout is the few-head kernel's");
@@ -411,7 +411,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const int i = 4 * lg + r;
         if (r > 0) dc = j < i ? dc * ari[r] : (j == i ? 1.f : 0.f);
         sLs[wave][gq][i][j] = j < i ? bri[r] * rki[r] * G4[r] * rk * dc : 0.f;
-        rec[kRecH + 16 * i + j] = j <= i ? rqi[r] * H4[r] * rk * dc : 0.f;
+        const float hd = j <= i ? rqi[r] * H4[r] * rk * dc : 0.f;
+        if constexpr (TP) store_parts16(rec + kRecH, i, j, hd);
+        else rec[kRecH + 16 * i + j] = hd;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1401,14 +1403,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       const v4f pq = (sp[ob][0][lane] + sp[ob][1][lane]) + (sp[ob][2][lane] + sp[ob][3][lane]);
       const v4f z = sz[ob][lane];
       const v4f cc = scc[ob][lane];
-      const float4 hf = *reinterpret_cast<const float4*>(&srec[s][kRecH + 16 * lc + 4 * lg]);
       v4f o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = srec[s][kRecSig + 4 * lg + i] * fmaf(g, pq[i], z[i]);
-      o = mfma4(hf.x, cc[0], o);
-      o = mfma4(hf.y, cc[1], o);
-      o = mfma4(hf.z, cc[2], o);
-      o = mfma4(hf.w, cc[3], o);
+      if constexpr (BFCHAIN) {  // Hd as parts (prep), C split here: three bf16 products
+        const uint4 hp = *reinterpret_cast<const uint4*>(&srec[s][kRecH + 16 * lc + 4 * lg]);
+        const Bf2 c0 = split_bf2(cc[0], cc[1]), c1 = split_bf2(cc[2], cc[3]);
+        const uint2 ch = make_uint2(c0.h, c1.h), cl = make_uint2(c0.l, c1.l);
+        o = mm16<GDN_BF16>(make_uint2(hp.z, hp.w), ch, o);
+        o = mm16<GDN_BF16>(make_uint2(hp.x, hp.y), cl, o);
+        o = mm16<GDN_BF16>(make_uint2(hp.x, hp.y), ch, o);
+      } else {
+        const float4 hf = *reinterpret_cast<const float4*>(&srec[s][kRecH + 16 * lc + 4 * lg]);
+        o = mfma4(hf.x, cc[0], o);
+        o = mfma4(hf.y, cc[1], o);
+        o = mfma4(hf.z, cc[2], o);
+        o = mfma4(hf.w, cc[3], o);
+      }
       return o;
     };
     auto o_store = [&](int64_t cb, const v4f& o, int tc) {
