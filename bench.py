@@ -10,12 +10,13 @@ state row) divided by its time, in GB/s.
 
 Also measured (object "scan"): the prefill scan B=1 T=4096 (bf16, token-major)
 and the head-major scan B=16 T=1024 (f16), in tokens/s and algorithmic
-TFLOP/s (7 * D * D flops per head-token) against the FP32 peak (157.3 TFLOP/s,
-the same for the vector units and for dense FP32 matrix products): the block
-form (the default at D = 128) runs on the matrix cores ("bound": "mfma"), the
-token-by-token form on the vector units ("alu").  With bf16/f16 operands the
-block form multiplies the f32 state on the bf16 matrix cores through exact
-bf16 parts (field "products"): f32 accuracy, counted in the method's f32 flops.
+TFLOP/s (7 * D * D flops per head-token) against the FP32 vector peak
+(157.3 TFLOP/s): the block form (the default at D = 128) runs its products on
+the matrix cores ("bound": "mfma"; with bf16/f16 operands over bf16 parts of
+the f32 state, field "products"), so that fraction can pass 1; the matrix work
+it actually issues is reported against the 2.5 PFLOP/s bf16 peak in
+"matrix_cores" (from the committed counter summary).  The exact-products mode
+is timed beside the default.
 
 ``roofline`` is for the decode kernel: algorithmic bytes per launch over its
 average launch time (HIP events on the launch stream over the timed region),
@@ -423,10 +424,15 @@ def bench_scan(idx, args, torch):
     tflops = flops / (ms * 1e-3) / 1e12
     tok = wl.B * wl.T / (ms * 1e-3)
     log("scan %d: %.1f us per call, %.2f M tok/s, %.1f TFLOP/s" % (idx, ms * 1e3, tok / 1e6, tflops))
+    # the method's flops (7 D^2 per head-token) against the FP32 vector peak: the
+    # unit the scan's target is set in; the block form runs its products on the
+    # matrix cores, so this fraction can pass 1 (the matrix work actually issued
+    # is in "matrix_cores", against the bf16 peak)
     res = {"workload": wl.name, "us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(tok, 1),
-           "tflops": round(tflops, 2), "peak_tflops": FP32_PEAK_TFLOPS,
-           "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "bound": bound, "form": form,
-           "algorithmic_flops_per_call": flops}
+           "algorithmic_tflops": round(tflops, 2),
+           "fp32_vector_peak_tflops": FP32_PEAK_TFLOPS,
+           "frac_of_fp32_vector_peak": round(tflops / FP32_PEAK_TFLOPS, 4), "bound": bound,
+           "form": form, "algorithmic_flops_per_call": flops}
     if form == "block" and wl.dtype in ("bf16", "f16"):
         res["products"] = ("f32 state; its products on the bf16 matrix cores over two bf16 parts "
                            "rounded to nearest (each term within 2^-16 of the f32 product; f16 q "
@@ -434,7 +440,7 @@ def bench_scan(idx, args, torch):
         ms_x = timed_call(True)
         log("scan %d exact products: %.1f us per call" % (idx, ms_x * 1e3))
         res["exact_products"] = {"us_per_call": round(ms_x * 1e3, 2),
-                                 "tflops": round(flops / (ms_x * 1e-3) / 1e12, 2),
+                                 "algorithmic_tflops": round(flops / (ms_x * 1e-3) / 1e12, 2),
                                  "products": "three exact bf16 parts of the state: exact f32 "
                                              "products"}
     else:
