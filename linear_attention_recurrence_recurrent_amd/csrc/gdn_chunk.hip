@@ -794,9 +794,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
         for (int p = 0; p < NPART; ++p)
           kt[p] = pack_bf16(mm16<GDN_BF16>(*reinterpret_cast<const uint2*>(&sk16[p][lc][key0(ct)]), eye));
         v4f acc = St[ct];
-        if constexpr (NPART == 1) {
+        if constexpr (NPART == 1 && NSP == 2) {
+          // k's four tokens twice against the two parts of Cs side by side
+          acc = mm32bf(make_uint4(kt[0].x, kt[0].y, kt[0].x, kt[0].y), make_uint4(c0l, c1l, c0h, c1h), acc);
+        } else if constexpr (NPART == 1) {
           acc = mm16<GDN_BF16>(kt[0], make_uint2(c0l, c1l), acc);
-          if constexpr (NSP == 3) acc = mm16<GDN_BF16>(kt[0], make_uint2(c0m, c1m), acc);
+          acc = mm16<GDN_BF16>(kt[0], make_uint2(c0m, c1m), acc);
           acc = mm16<GDN_BF16>(kt[0], make_uint2(c0h, c1h), acc);
         } else {
           const uint4 ka = make_uint4(kt[0].x, kt[0].y, kt[1].x, kt[1].y);
@@ -1086,9 +1089,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           v4f acc = St[ct] * o.gl;
-          if constexpr (NPART == 1) {
+          if constexpr (NPART == 1 && NSP == 2) {
+            // k's four tokens twice against the two parts of Cs side by side:
+            // one 16x16x32 product for two 16x16x16 ones
+            const uint4 kk = make_uint4(o.kt[ct].x, o.kt[ct].y, o.kt[ct].x, o.kt[ct].y);
+            St[ct] = mm32bf(kk, make_uint4(c.l.x, c.l.y, c.h.x, c.h.y), acc);
+          } else if constexpr (NPART == 1) {
+            // three parts: three 16x16x16 products (a 16x16x16 product must not
+            // take a 16x16x32 one's result as its accumulator straight away)
             acc = mm16<GDN_BF16>(o.kt[ct], c.l, acc);
-            if constexpr (NSP == 3) acc = mm16<GDN_BF16>(o.kt[ct], c.m, acc);
+            acc = mm16<GDN_BF16>(o.kt[ct], c.m, acc);
             St[ct] = mm16<GDN_BF16>(o.kt[ct], c.h, acc);
           } else {
             // one 16x16x32 product per part of Cs: k's hi and lo parts
