@@ -83,8 +83,8 @@ typedef enum gdn_status {
 #define GDN_FOLD_QK_L2NORM 1u /* L2-normalise q and k inside the op */
 #define GDN_FOLD_Q_SCALE 2u   /* multiply q^ by 1/sqrt(Dk) inside the op */
 /* Form of gdn_scan's time loop.  The token-by-token form runs on the vector
- * units for every head dim; at Dk == Dv == 128 the block form runs 16 tokens
- * at a time as dense products on the matrix cores (the step is affine in S,
+ * units for every head dim; at Dk == Dv in {32, 64, 128} the block form runs
+ * 16 tokens at a time as dense products on the matrix cores (the step is affine in S,
  * "Module gdn" page, "The fusion").  Both give the same results up to
  * rounding.  With f16/bf16 q and k the block form multiplies the f32 state
  * (and its per-block correction) on the bf16 matrix cores through bf16 parts:
@@ -92,7 +92,7 @@ typedef enum gdn_status {
  * relative of the f32 product; with GDN_SCAN_EXACT three exact parts, each
  * term an exact f32 product (f32 accuracy; up to 1.2x the time).
  * f32 q and k take f32 products either way.  Without a form flag the block
- * form runs at Dk == Dv == 128 and the token-by-token form otherwise; with
+ * form runs at those head dims and the token-by-token form otherwise; with
  * both form flags, or GDN_SCAN_BLOCK at another head dim, the call is
  * rejected (GDN_EINVAL / GDN_EUNSUPPORTED).  The block form keeps per-block
  * records in a caller-supplied workspace (gdn_scan_workspace_size). */
@@ -136,8 +136,8 @@ int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* 
 
 /* Bytes of device workspace gdn_scan needs for the descriptor `d`, written to
  * *bytes.  Zero when the chosen time loop keeps nothing between its kernels
- * (T <= 1, B == 0, the token-by-token form).  The block form (Dk == Dv ==
- * 128 unless GDN_SCAN_PER_TOKEN) needs one 2560-byte record per value head
+ * (T <= 1, B == 0, the token-by-token form).  The block form (Dk == Dv in
+ * {32, 64, 128} unless GDN_SCAN_PER_TOKEN) needs one 2560-byte record per value head
  * and 16-token block, plus 3072 bytes per key head and block when B * Hv is
  * below 256 (the few-head kernel's cross-block key products):
  *     B*Hv*ceil(T/16)*2560  [+ B*Hk*ceil(T/16)*3072].

@@ -84,8 +84,8 @@ int check_desc(const gdn_desc* d) {
   if (d->Dk != 16 && d->Dk != 32 && d->Dk != 64 && d->Dk != 128 && d->Dk != 256)
     return fail(GDN_EUNSUPPORTED, "head dim %lld not in {16, 32, 64, 128, 256}",
                 (long long)d->Dk);
-  if ((d->flags & GDN_SCAN_BLOCK) && d->Dk != 128)
-    return fail(GDN_EUNSUPPORTED, "the block form needs Dk == Dv == 128");
+  if ((d->flags & GDN_SCAN_BLOCK) && !block_form_head_dim(d->Dk))
+    return fail(GDN_EUNSUPPORTED, "the block form needs Dk == Dv in {32, 64, 128}");
 
   // sizes (with overflow checks)
   int64_t bt, nqk, nv, ng, ns, tmp;
@@ -99,9 +99,11 @@ int check_desc(const gdn_desc* d) {
   return GDN_OK;
 }
 
+bool block_form_head_dim(int64_t D) { return D == 32 || D == 64 || D == 128; }
+
 bool scan_uses_block_form(const gdn_desc& d) {
-  return d.Dk == 128 && d.Dv == 128 && (d.flags & GDN_SCAN_PER_TOKEN) == 0 && d.T >= 2 &&
-         d.B > 0;
+  return block_form_head_dim(d.Dk) && d.Dv == d.Dk && (d.flags & GDN_SCAN_PER_TOKEN) == 0 &&
+         d.T >= 2 && d.B > 0;
 }
 
 int64_t scan_record_bytes(const gdn_desc& d) {

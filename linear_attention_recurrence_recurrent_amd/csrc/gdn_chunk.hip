@@ -1,5 +1,5 @@
 // Time-axis scan of the Gated DeltaNet recurrence in block form on the matrix
-// cores (gfx950 MFMA, FP32 in and out), for D = 128.
+// cores (gfx950 MFMA, FP32 in and out), for D = 32, 64 and 128.
 //
 // The recurrence is the one of the "Module gdn" page (module description).
 // Its section "The fusion" observes that the step is affine in the memory S;
@@ -47,9 +47,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kD = 128;       // head dim handled here
 constexpr int kL = 16;        // tokens per block (the MFMA tile)
-constexpr int kPad = kD + 4;  // LDS row of q or k: rows 16 banks apart for the operand reads
 // (from kManyHeads value heads on, a workgroup per head fills the chip)
 
 // Block record, per (value head, block), f32; the records of a head are
@@ -168,15 +166,15 @@ struct Bases {
 };
 
 __device__ __forceinline__ Bases head_bases(int64_t b, int hv, int hk, int Hk, int Hv, int64_t T,
-                                            int head_major) {
+                                            int head_major, int D) {
   Bases r;
   if (head_major) {
-    r.qk = (b * Hk + hk) * T * kD; r.qk_ts = kD;
-    r.v = (b * Hv + hv) * T * kD; r.v_ts = kD;
+    r.qk = (b * Hk + hk) * T * D; r.qk_ts = D;
+    r.v = (b * Hv + hv) * T * D; r.v_ts = D;
     r.g = (b * Hv + hv) * T; r.g_ts = 1;
   } else {
-    r.qk = (b * T * Hk + hk) * kD; r.qk_ts = (int64_t)Hk * kD;
-    r.v = (b * T * Hv + hv) * kD; r.v_ts = (int64_t)Hv * kD;
+    r.qk = (b * T * Hk + hk) * D; r.qk_ts = (int64_t)Hk * D;
+    r.v = (b * T * Hv + hv) * D; r.v_ts = (int64_t)Hv * D;
     r.g = b * T * Hv + hv; r.g_ts = Hv;
   }
   return r;
@@ -215,9 +213,12 @@ struct PrepArgs {
 // separate instance, so the many-head prep keeps its register count).
 // TP: T, Hd, M1, M2 and N written as two rounded bf16 parts (store_parts16)
 // for the few-head kernel's default products.
-template <int DT, int GT, bool XB, bool TP>
+template <int DT, int GT, int D, bool XB, bool TP>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   static_assert(XB || !TP, "the parts layout is the few-head kernel's");
+  // a lane holds D / 4 elements of a row: NU loads of 8
+  constexpr int NU = D / 32;
+  static_assert(NU >= 1 && D % 32 == 0, "head dim a multiple of 32");
   __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
   __shared__ __align__(16) float sAB[4][2][4][kL];  // [wave][alpha, beta][value head][token]
   // the wave index through readfirstlane: everything derived from the task
@@ -235,21 +236,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   const int tc = (int)((T - t0) < kL ? (T - t0) : kL);
   int64_t qk_base, qk_ts;
   if (a.head_major) {
-    qk_base = (b * a.Hk + hk) * T * kD; qk_ts = kD;
+    qk_base = (b * a.Hk + hk) * T * D; qk_ts = D;
   } else {
-    qk_base = (b * T * a.Hk + hk) * kD; qk_ts = (int64_t)a.Hk * kD;
+    qk_base = (b * T * a.Hk + hk) * D; qk_ts = (int64_t)a.Hk * D;
   }
 
   // Every load of the wave is issued here, before any of them is used, so
   // that their latencies overlap (one round trip instead of one per use).
-  // Rows of q and k: lane (lg, lc) holds row lc, elements [32 lg, 32 lg + 32)
+  // Rows of q and k: lane (lg, lc) holds row lc, elements [D/4 lg, D/4 (lg + 1))
   // Addresses: a block base (uniform) plus a 32-bit offset per lane, so no
   // lane computes a 64-bit product.
-  const uint32_t loff = (uint32_t)lc * (uint32_t)qk_ts + 32u * (uint32_t)lg;
-  Raw<DT, 8> kr[4], qr[4];
+  const uint32_t loff = (uint32_t)lc * (uint32_t)qk_ts + (uint32_t)(D / 4) * (uint32_t)lg;
+  Raw<DT, 8> kr[NU], qr[NU];
   const int64_t rowb = qk_base + t0 * qk_ts;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < NU; ++u) {
     if (lc < tc) {
       kr[u].load(a.k, rowb + (int64_t)(loff + 8u * u));
       qr[u].load(a.q, rowb + (int64_t)(loff + 8u * u));
@@ -260,12 +261,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   }
   // XB: the key rows of the two blocks before (block 0's where there is
   // none; those products are replaced by zero below)
-  [[maybe_unused]] Raw<DT, 8> kp1[4], kp2[4];
+  [[maybe_unused]] Raw<DT, 8> kp1[NU], kp2[NU];
   if constexpr (XB) {
     const int64_t c1 = c > 0 ? c - 1 : 0, c2 = c > 1 ? c - 2 : 0;
     const int64_t b1r = qk_base + c1 * kL * qk_ts, b2r = qk_base + c2 * kL * qk_ts;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NU; ++u) {
       kp1[u].load(a.k, b1r + (int64_t)(loff + 8u * u));
       kp2[u].load(a.k, b2r + (int64_t)(loff + 8u * u));
     }
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   float ssk = 0.f, ssq = 0.f;
   if constexpr (DT == GDN_F32) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ssk = fmaf(kr[u].get(e), kr[u].get(e), ssk);
@@ -303,19 +304,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   }
 
   // X Y^T of 16 raw rows each on the matrix cores; lane (lg, lc), register
-  // r: entry [4 lg + r][lc].  The contraction runs over the lane's own 32
+  // r: entry [4 lg + r][lc].  The contraction runs over the lane's own D / 4
   // elements: f32, one element per 16x16x4 product; 16-bit, four per 16x16x16
   // product straight from the loaded words (no widening).
   auto gram = [&](const Raw<DT, 8>* x, const Raw<DT, 8>* y) {
     v4f d = {0.f, 0.f, 0.f, 0.f};
     if constexpr (DT == GDN_F32) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = mfma4(x[u].get(e), y[u].get(e), d);
     } else {
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 2 * NU; ++m)
         d = mm16<DT>(make_uint2(x[m / 2].w[2 * (m % 2)], x[m / 2].w[2 * (m % 2) + 1]),
                      make_uint2(y[m / 2].w[2 * (m % 2)], y[m / 2].w[2 * (m % 2) + 1]), d);
     }
@@ -468,22 +469,24 @@ struct StateArgs {
 // norm is fused.  The loads of block c + 1 are issued while block c is
 // computed.  NSP: parts of the state and of Cs in the products of 16-bit
 // inputs (3: exact, split_bf3; 2: rounded, split_bf2).
-template <int DT, int NSP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void state_kernel(
+template <int DT, int NSP, int D>
+__global__ __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) void state_kernel(
     StateArgs a) {
   static_assert(NSP == 2 || NSP == 3, "two or three parts");
-  constexpr int NW = 8, NT = NW * kWave, ROWS = kD, NCT = 8;
+  static_assert(D % 32 == 0 && D <= 128, "head dim 32, 64 or 128");
+  // a wave per 16 value rows (a-tile), each over all D / 16 key tiles
+  constexpr int NW = D / 16, NT = NW * kWave, ROWS = D, NCT = D / 16;
   // 16-bit inputs: q and k in LDS as bf16 parts (bf16: the value; f16: its
   // exact split into two bf16 values), the products on the bf16 matrix cores
   // against the three exact bf16 parts of the state; f32 inputs: f32 products
   constexpr bool W16 = DT != GDN_F32;
-  constexpr int NPART = DT == GDN_F16 ? 2 : 1, KP16 = kD + 8;
-  __shared__ __align__(16) float sk[kL][kPad];
-  __shared__ __align__(16) float sq[kL][kPad];
+  constexpr int NPART = DT == GDN_F16 ? 2 : 1, KP16 = D + 8, KPF = D + 4;
+  __shared__ __align__(16) float sk[kL][KPF];
+  __shared__ __align__(16) float sq[kL][KPF];
   __shared__ __align__(16) uint16_t sk16[NPART][kL][KP16];
   __shared__ __align__(16) uint16_t sq16[NPART][kL][KP16];
   __shared__ float sv[kL][ROWS];
-  __shared__ float sz[2][kL][kD];
+  __shared__ float sz[2][kL][D];
   __shared__ __align__(16) float so[2][kL][ROWS];
   __shared__ __align__(16) float srec[kRecUsed];
 
@@ -497,15 +500,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int ai = wave;  // this wave's a-tile (value rows 16 ai ..), all key tiles
   const int64_t T = a.T;
   const bool has_z = a.z != nullptr;
-  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major);
-  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
+  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major, D);
+  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(D * D);
   const float* rec = a.rec + record_at(bh, 0, a.nblk);
 
-  // staging of one block: 512 items of 8 q or k elements, v pairs, z pairs
-  // (fused), the record as float4
-  constexpr int NQK = (2 * kL * 16 + NT - 1) / NT;
+  // staging of one block: items of 8 q or k elements (IPR per row, NI in
+  // all, k first), v pairs, z pairs (fused), the record as float4
+  constexpr int IPR = D / 8, NI = 2 * kL * IPR;
+  constexpr int NQK = (NI + NT - 1) / NT;
   constexpr int NVP = (kL * ROWS / 2 + NT - 1) / NT;
-  constexpr int NZP = (kL * kD / 2 + NT - 1) / NT;
+  constexpr int NZP = (kL * D / 2 + NT - 1) / NT;
   constexpr int NR4 = kRecUsed / 4;
   constexpr int NRC = (NR4 + NT - 1) / NT;
   struct Regs {
@@ -525,8 +529,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int64_t qkb = bs.qk + t0 * bs.qk_ts, vb = bs.v + t0 * bs.v_ts;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      const int e = (tid + i * NT) % 512, it = e % 256, tt = it / 16, c8 = it % 16;
-      const int which = __builtin_amdgcn_readfirstlane(e / 256);  // uniform per wave
+      const int e = (tid + i * NT) % NI, it = e % (NI / 2), tt = it / IPR, c8 = it % IPR;
+      const int which = __builtin_amdgcn_readfirstlane(e / (NI / 2));  // uniform per wave
       const uint32_t off = (uint32_t)clamp_t(tt, tc) * (uint32_t)bs.qk_ts + 8u * (uint32_t)c8;
       P.qk[i].load(which ? a.q : a.k, qkb + (int64_t)off);
     }
@@ -539,7 +543,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     if (has_z) {
 #pragma unroll
       for (int i = 0; i < NZP; ++i) {
-        const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
+        const int e = (tid + i * NT) % (kL * D / 2), tt = e / (D / 2), r2 = e % (D / 2);
         const uint32_t off = (uint32_t)clamp_t(tt, tc) * (uint32_t)bs.v_ts + 2u * (uint32_t)r2;
         P.z[i].load(a.z, vb + (int64_t)off);
       }
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   auto chunk_store = [&](const Regs& P, int zbuf) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      const int e = (tid + i * NT) % 512, which = e / 256, it = e % 256, tt = it / 16, c8 = it % 16;
+      const int e = (tid + i * NT) % NI, which = e / (NI / 2), it = e % (NI / 2), tt = it / IPR, c8 = it % IPR;
       if constexpr (DT == GDN_F32) {
         float* dst = which ? &sq[tt][8 * c8] : &sk[tt][8 * c8];
         *reinterpret_cast<float4*>(dst) = P.qk[i].get4(0);
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     if (has_z) {
 #pragma unroll
       for (int i = 0; i < NZP; ++i) {
-        const int e = (tid + i * NT) % (kL * kD / 2), tt = e / (kD / 2), r2 = e % (kD / 2);
+        const int e = (tid + i * NT) % (kL * D / 2), tt = e / (D / 2), r2 = e % (D / 2);
         sz[zbuf][tt][2 * r2] = P.z[i].get(0);
         sz[zbuf][tt][2 * r2 + 1] = P.z[i].get(1);
       }
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   auto key0 = [&](int ct) { return W16 ? 32 * (ct / 2) + 8 * lg + 4 * (ct % 2) : 16 * ct + 4 * lg; };
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD + key0(ct));
+    const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * D + key0(ct));
     St[ct] = v4f{x.x, x.y, x.z, x.w};
   }
   [[maybe_unused]] const uint2 eye = eye16<GDN_BF16>(lg, lc);
@@ -624,9 +628,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   // under 2^-80, a zero decay included), so each block scales the four
   // values of K S^T and Q S^T and Cs instead of the 32 of St
   float gsc = 1.f;
-  float wgt[2];
+  // the gated norm: a lane holds EPL of a token's D values (lanes past D,
+  // below 64, hold none)
+  constexpr int EPL = D >= kWave ? D / kWave : 1;
+  const bool nact = D >= kWave || lane < D;
+  float wgt[EPL];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) wgt[i] = has_z ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
+  for (int i = 0; i < EPL; ++i) wgt[i] = has_z && nact ? ld1<DT>(a.w, lane + kWave * i) : 0.f;
   const int64_t nblk = a.nblk;
   auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
 
@@ -636,17 +644,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   auto outputs = [&](int64_t c) {
     const int64_t t0 = c * kL;
     const int tc = tc_of(c);
-    if (has_z) {  // the gated norm: two tokens per wave, 128 values each
+    if (has_z) {  // the gated norm: kL / NW tokens per wave, D values each
 #pragma unroll
       for (int u = 0; u < kL / NW; ++u) {
         const int tt = wave + NW * u, zb = (int)(c & 1);
-        float x0 = so[c & 1][tt][lane] * silu(sz[zb][tt][lane]);
-        float x1 = so[c & 1][tt][lane + kWave] * silu(sz[zb][tt][lane + kWave]);
-        const float inv = rsqrtf(wave_sum(fmaf(x0, x0, x1 * x1)) * (1.0f / kD) + a.norm_eps);
-        if (tt < tc) {
+        float x[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          x[i] = nact ? so[c & 1][tt][lane + kWave * i] * silu(sz[zb][tt][lane + kWave * i]) : 0.f;
+        float ss = x[EPL - 1] * x[EPL - 1];
+#pragma unroll
+        for (int i = EPL - 2; i >= 0; --i) ss = fmaf(x[i], x[i], ss);
+        const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + a.norm_eps);
+        if (tt < tc && nact) {
           const int64_t vo = bs.v + (t0 + tt) * bs.v_ts;
-          a.y[vo + lane] = x0 * inv * wgt[0];
-          a.y[vo + lane + kWave] = x1 * inv * wgt[1];
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) a.y[vo + lane + kWave * i] = x[i] * inv * wgt[i];
         }
       }
       return;
@@ -854,7 +867,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   for (int ct = 0; ct < NCT; ++ct) {
     if constexpr (W16) St[ct] *= gsc;
     float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
-    *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + key0(ct)) = x;
+    *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * D + key0(ct)) = x;
   }
 }
 
@@ -863,9 +876,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
 // are widened to f32 as they are read.
 template <int DT>
 using LdsElem = typename std::conditional<DT == GDN_F32, float, uint16_t>::type;
-template <int DT>
+template <int DT, int D>
 constexpr int lds_row() {  // padded row, elements: rows 4 banks apart
-  return DT == GDN_F32 ? kPad : kD + 8;
+  return DT == GDN_F32 ? D + 4 : D + 8;
+}
+
+// Threads of the few-head kernel: D / 32 state waves of 32 keys, then the
+// chain, O and two staging waves.
+constexpr int rows_la_threads(int D) { return (D / 32 + 4) * kWave; }
+
+// The sum of the state waves' partial products, pairwise
+template <int N>
+__device__ __forceinline__ v4f sum_parts(const v4f (*p)[kWave], int lane) {
+  if constexpr (N == 1) return p[0][lane];
+  else return sum_parts<N / 2>(p, lane) + sum_parts<N / 2>(p + N / 2, lane);
 }
 template <int DT>
 __device__ __forceinline__ float half_lo(uint32_t x) {
@@ -917,11 +941,13 @@ __device__ __forceinline__ float lds_get(const LdsElem<DT>* row, int e) {
 // products back to back.  A prologue round forms A_0 = K_0 S_0^T; the last
 // round finishes the state and O.  Each role runs its own loop with the same
 // barriers.
-template <int DT, int NSP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void rows_la_kernel(
-    StateArgs a) {
+template <int DT, int NSP, int D>
+__global__ __launch_bounds__(rows_la_threads(D)) __attribute__((amdgpu_waves_per_eu(2))) void
+rows_la_kernel(StateArgs a) {
   static_assert(NSP == 2 || NSP == 3, "two or three parts of the state and Cs");
-  constexpr int NC = 4, NCT = 8 / NC, ROWS = 16, KP = lds_row<DT>(), NM = 3 * kL * kL;
+  static_assert(D % 32 == 0 && D <= 128, "head dim 32, 64 or 128");
+  // NC state waves of two 16-key tiles each
+  constexpr int NC = D / 32, NCT = 2, ROWS = 16, KP = lds_row<DT, D>(), NM = 3 * kL * kL;
   typedef LdsElem<DT> KT;
   __shared__ __align__(16) KT sk[4][kL][KP];
   __shared__ __align__(16) KT sq[4][kL][KP];
@@ -952,9 +978,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   const int cp = wave % NC;
   const int lg = lane / 16, lc = lane % 16;
   const int64_t T = a.T, nblk = a.nblk;
-  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major);
+  const Bases bs = head_bases(b, hv, hk, a.Hk, a.Hv, T, a.head_major, D);
   const int row0 = rb * ROWS;
-  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(kD * kD);
+  const int64_t sbase = (b * a.Hv + hv) * (int64_t)(D * D);
   const float* rec = a.rec + record_at(bh, 0, nblk);
   const float* mxh = a.mx + (b * a.Hk + hk) * nblk * NM;
   auto tc_of = [&](int64_t c) { return (int)((T - c * kL) < kL ? (T - c * kL) : kL); };
@@ -974,7 +1000,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       // wave loads its own q and k slices from global memory (LDS writes, not
       // reads, bound the staging), four blocks ahead.
       v4f St[NCT];
-      const int64_t soff = sbase + (int64_t)(row0 + lc) * kD + 32 * cp + 8 * lg;
+      const int64_t soff = sbase + (int64_t)(row0 + lc) * D + 32 * cp + 8 * lg;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const float4 x = *reinterpret_cast<const float4*>(a.s0 + soff + 4 * ct);
@@ -1175,7 +1201,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
     const int arow = row0 + lc;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * kD +
+      const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * D +
                                                         16 * (cp * NCT + ct) + 4 * lg);
       St[ct] = v4f{x.x, x.y, x.z, x.w};
     }
@@ -1272,7 +1298,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
-      *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * kD + 16 * (cp * NCT + ct) +
+      *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * D + 16 * (cp * NCT + ct) +
                                  4 * lg) = x;
     }
     return;
@@ -1369,10 +1395,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       }
       o.mc = d;
     };
-    auto bparts = [&](int64_t r) {
-      const int ab = (int)(r & 1);
-      return (sb[ab][0][lane] + sb[ab][1][lane]) + (sb[ab][2][lane] + sb[ab][3][lane]);
-    };
+    auto bparts = [&](int64_t r) { return sum_parts<NC>(sb[r & 1], lane); };
     // M1_r Cs_(r-1) goes right after the barrier, in the shadow of the
     // round's LDS reads, rather than in front of the barrier
     auto round = [&](int64_t r, Cops& cur, Cops& nxt) {
@@ -1410,7 +1433,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
     // register i is token 4 lg + i, row lc
     auto o_block = [&](int64_t cb, float g) {
       const int s = (int)(cb & 3), ob = (int)(cb & 1);
-      const v4f pq = (sp[ob][0][lane] + sp[ob][1][lane]) + (sp[ob][2][lane] + sp[ob][3][lane]);
+      const v4f pq = sum_parts<NC>(sp[ob], lane);
       const v4f z = sz[ob][lane];
       const v4f cc = scc[ob][lane];
       v4f o;
@@ -1463,7 +1486,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
     Raw<GDN_F32, 4> r[2], m[2];
   };
   const int st = tid - (NC + 2) * kWave;
-  const int qtt = st / 8, qc = 16 * (st % 8), vr = 2 * (st % 8);
+  // f32 q and k: CPR chunks of 16 elements per row, a chunk per lane (lanes
+  // past the kL * CPR chunks load the last one and do not write it); v: two
+  // values of one token per lane
+  constexpr int CPR = D / 16;
+  constexpr bool QKALL = kL * CPR >= 2 * kWave;  // every staging lane writes a chunk
+  const int sqi = st < kL * CPR ? st : kL * CPR - 1;
+  const int qtt = sqi / CPR, qc = 16 * (sqi % CPR), vtt = st / 8, vr = 2 * (st % 8);
   int rec_e[2], mx_e[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -1475,6 +1504,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   auto load = [&](Regs& P, int64_t c) {
     const int tcc = c == nblk - 1 ? tcl : kL;  // tokens in block c
     const int64_t t = c * kL + (qtt < tcc ? qtt : tcc - 1);
+    const int64_t tv = c * kL + (vtt < tcc ? vtt : tcc - 1);
     const int64_t o = bs.qk + t * bs.qk_ts + qc;
     if constexpr (QK) {
       P.k[0].load(a.k, o);
@@ -1482,7 +1512,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
       P.q[0].load(a.q, o);
       P.q[1].load(a.q, o + 8);
     }
-    P.v.load(a.v, bs.v + t * bs.v_ts + row0 + vr);
+    P.v.load(a.v, bs.v + tv * bs.v_ts + row0 + vr);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       P.r[u].load(rec, c * kRec + rec_e[u]);
@@ -1509,21 +1539,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
     pin(P.r[1]);
     pin(P.m[0]);
     pin(P.m[1]);
+    if (QKALL || st < kL * CPR) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if constexpr (DT == GDN_F32) {
-        *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h]) = P.k[h].get4(0);
-        *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h + 4]) = P.k[h].get4(1);
-        *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h]) = P.q[h].get4(0);
-        *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h + 4]) = P.q[h].get4(1);
-      } else if constexpr (QK) {
-        *reinterpret_cast<uint4*>(&sk[sl][qtt][qc + 8 * h]) =
-            make_uint4(P.k[h].w[0], P.k[h].w[1], P.k[h].w[2], P.k[h].w[3]);
-        *reinterpret_cast<uint4*>(&sq[sl][qtt][qc + 8 * h]) =
-            make_uint4(P.q[h].w[0], P.q[h].w[1], P.q[h].w[2], P.q[h].w[3]);
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (DT == GDN_F32) {
+          *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h]) = P.k[h].get4(0);
+          *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h + 4]) = P.k[h].get4(1);
+          *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h]) = P.q[h].get4(0);
+          *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h + 4]) = P.q[h].get4(1);
+        } else if constexpr (QK) {
+          *reinterpret_cast<uint4*>(&sk[sl][qtt][qc + 8 * h]) =
+              make_uint4(P.k[h].w[0], P.k[h].w[1], P.k[h].w[2], P.k[h].w[3]);
+          *reinterpret_cast<uint4*>(&sq[sl][qtt][qc + 8 * h]) =
+              make_uint4(P.q[h].w[0], P.q[h].w[1], P.q[h].w[2], P.q[h].w[3]);
+        }
       }
     }
-    *reinterpret_cast<float2*>(&sv[sl][qtt][vr]) = make_float2(P.v.get(0), P.v.get(1));
+    *reinterpret_cast<float2*>(&sv[sl][vtt][vr]) = make_float2(P.v.get(0), P.v.get(1));
     *reinterpret_cast<float4*>(&srec[sl][rec_e[0]]) = P.r[0].get4(0);
     if (st + 2 * kWave < NR4) *reinterpret_cast<float4*>(&srec[sl][rec_e[1]]) = P.r[1].get4(0);
     *reinterpret_cast<float4*>(&smx[sl][mx_e[0]]) = P.m[0].get4(0);
@@ -1602,40 +1634,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void r
   __syncthreads();
 }
 
-template <int DT, int GT, bool TP>
+template <int DT, int GT, int D, bool TP>
 void launch_prep_gt(const PrepArgs& p, dim3 grid, hipStream_t st) {
-  if (p.mx != nullptr) prep_kernel<DT, GT, true, TP><<<grid, 256, 0, st>>>(p);
-  else prep_kernel<DT, GT, false, false><<<grid, 256, 0, st>>>(p);
+  if (p.mx != nullptr) prep_kernel<DT, GT, D, true, TP><<<grid, 256, 0, st>>>(p);
+  else prep_kernel<DT, GT, D, false, false><<<grid, 256, 0, st>>>(p);
 }
 
-template <int DT, bool TP>
+template <int DT, int D, bool TP>
 int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
   switch (gdt) {
-    case GDN_F32: launch_prep_gt<DT, GDN_F32, TP>(p, grid, st); break;
-    case GDN_F16: launch_prep_gt<DT, GDN_F16, TP>(p, grid, st); break;
-    default: launch_prep_gt<DT, GDN_BF16, TP>(p, grid, st); break;
+    case GDN_F32: launch_prep_gt<DT, GDN_F32, D, TP>(p, grid, st); break;
+    case GDN_F16: launch_prep_gt<DT, GDN_F16, D, TP>(p, grid, st); break;
+    default: launch_prep_gt<DT, GDN_BF16, D, TP>(p, grid, st); break;
   }
   return device_status("prep_kernel launch");
 }
 
-template <int DT, int NSP>
+template <int DT, int NSP, int D>
 int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t heads,
               hipStream_t st) {
   const dim3 pgrid((unsigned)((p.ntask + 3) / 4));
   // the few-head kernel's default products take T and M1 as bf16 parts
-  const int rc = launch_prep<DT, DT != GDN_F32 && NSP == 2>(p, d.gate_dtype, pgrid, st);
+  const int rc = launch_prep<DT, D, DT != GDN_F32 && NSP == 2>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;
-  // many heads: whole-head workgroups, two per CU, the norm fused; few heads:
-  // a workgroup per 16 value rows with the one-block lookahead
+  // many heads: whole-head workgroups, the norm fused; few heads: a
+  // workgroup per 16 value rows with the one-block lookahead
   StateArgs r = s;
   if (heads >= kManyHeads) {
     r.nrb = 1;
-    state_kernel<DT, NSP><<<dim3((unsigned)heads), 512, 0, st>>>(r);
+    state_kernel<DT, NSP, D><<<dim3((unsigned)heads), 4 * D, 0, st>>>(r);
     return device_status("state_kernel launch");
   }
-  r.nrb = kD / 16;
-  rows_la_kernel<DT, NSP><<<dim3((unsigned)(heads * r.nrb)), 512, 0, st>>>(r);
+  r.nrb = D / 16;
+  rows_la_kernel<DT, NSP, D><<<dim3((unsigned)(heads * r.nrb)), rows_la_threads(D), 0, st>>>(r);
   return device_status("rows_la_kernel launch");
+}
+
+template <int DT, int NSP>
+int launch_d(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t heads,
+             hipStream_t st) {
+  switch (d.Dk) {
+    case 32: return launch_dt<DT, NSP, 32>(d, p, s, heads, st);
+    case 64: return launch_dt<DT, NSP, 64>(d, p, s, heads, st);
+    default: return launch_dt<DT, NSP, 128>(d, p, s, heads, st);
+  }
 }
 
 }  // namespace
@@ -1664,13 +1706,13 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
   // exact ones with GDN_SCAN_EXACT; f32 inputs use f32 products either way
   const bool exact = (d.flags & GDN_SCAN_EXACT) != 0;
   switch (d.dtype) {
-    case GDN_F32: return launch_dt<GDN_F32, 3>(d, p, s, heads, st);
+    case GDN_F32: return launch_d<GDN_F32, 3>(d, p, s, heads, st);
     case GDN_F16:
-      return exact ? launch_dt<GDN_F16, 3>(d, p, s, heads, st)
-                   : launch_dt<GDN_F16, 2>(d, p, s, heads, st);
+      return exact ? launch_d<GDN_F16, 3>(d, p, s, heads, st)
+                   : launch_d<GDN_F16, 2>(d, p, s, heads, st);
     default:
-      return exact ? launch_dt<GDN_BF16, 3>(d, p, s, heads, st)
-                   : launch_dt<GDN_BF16, 2>(d, p, s, heads, st);
+      return exact ? launch_d<GDN_BF16, 3>(d, p, s, heads, st)
+                   : launch_d<GDN_BF16, 2>(d, p, s, heads, st);
   }
 }
 

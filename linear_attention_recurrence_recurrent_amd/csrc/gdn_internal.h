@@ -15,6 +15,8 @@ constexpr int64_t kKeyCrossBytes = 3 * 16 * 16 * 4;
 constexpr int64_t kManyHeads = 256;
 constexpr uintptr_t kWorkspaceAlign = 256;
 
+// Head dims the block form covers (Dk == Dv).
+bool block_form_head_dim(int64_t D);
 // Whether gdn_scan runs the block form for this (valid) descriptor.
 bool scan_uses_block_form(const gdn_desc& d);
 // Bytes of the records (first part of the workspace) and in total.
@@ -53,7 +55,7 @@ int launch_step_three_pass(const gdn_desc& d, const void* q, const void* k, cons
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
                 float* s_out, void* workspace, void* stream);
-// Block form on the matrix cores, Dk == Dv == 128, with its records in
+// Block form on the matrix cores, Dk == Dv in {32, 64, 128}, with its records in
 // `workspace` (scan_workspace_bytes(d) bytes); *gated reports whether the
 // gated norm was applied in the same launch (whole-head workgroups).
 int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const void* v,

@@ -604,6 +604,18 @@ int launch_scan_gt(const ScanArgs& a, int gdt, int D, int64_t heads, hipStream_t
   }
 }
 
+// the standalone gated norm over y in place (the few-head block form)
+template <int DT>
+void launch_norm(int D, float* y, const void* z, const void* w, int64_t nvec, float eps,
+                 hipStream_t st) {
+  const dim3 grid = norm_grid(nvec);
+  switch (D) {
+    case 32: gated_norm_kernel<DT, 32><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
+    case 64: gated_norm_kernel<DT, 64><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
+    default: gated_norm_kernel<DT, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
+  }
+}
+
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
                 float* s_out, void* workspace, void* stream) {
@@ -612,19 +624,18 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
                    (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags,
                    d.qk_eps, d.norm_eps, q_scale(d)};
   const int64_t heads = d.B * d.Hv;
-  // the block form at D = 128 (faster there on both the few-head and the
-  // many-head shapes) unless the token-by-token form is asked for
+  // the block form at D = 32, 64 and 128 (faster there on both the few-head
+  // and the many-head shapes) unless the token-by-token form is asked for
   if (scan_uses_block_form(d)) {
     bool gated = false;
     int rc = launch_scan_chunked(d, q, k, v, ld, beta, s0, z, w, y, s_out, workspace, stream,
                                  &gated);
     if (rc != GDN_OK || gated || z == nullptr) return rc;
     const int64_t nvec = heads * d.T;
-    const dim3 grid = norm_grid(nvec);
     switch (d.dtype) {
-      case GDN_F32: gated_norm_kernel<GDN_F32, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
-      case GDN_F16: gated_norm_kernel<GDN_F16, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
-      default: gated_norm_kernel<GDN_BF16, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, d.norm_eps); break;
+      case GDN_F32: launch_norm<GDN_F32>((int)d.Dv, y, z, w, nvec, d.norm_eps, st); break;
+      case GDN_F16: launch_norm<GDN_F16>((int)d.Dv, y, z, w, nvec, d.norm_eps, st); break;
+      default: launch_norm<GDN_BF16>((int)d.Dv, y, z, w, nvec, d.norm_eps, st); break;
     }
     return device_status("gated_norm_kernel launch");
   }

@@ -171,7 +171,7 @@ def test_small_cases(case, gated):
     say("small %s gated=%s" % (case, gated))
     ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm, seed=B * 131 + T)
     run_both(ops, head_major=hm, gated=gated, dtype=dtype)
-    if D == 128:  # both forms of the time loop
+    if D in (32, 64, 128):  # both forms of the time loop
         run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="per_token")
         run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="block")
 
@@ -212,6 +212,31 @@ def test_block_form_edge_shapes(case, gated):
     assert torch.equal(yb, yd) and torch.equal(sb, sd)
 
 
+HEAD_DIMS = [
+    # (B, T, Hk, Hv, D): a workgroup per 16 value rows (few heads) or per head (256 heads)
+    (1, 45, 2, 4, 64),
+    (8, 45, 16, 32, 64),
+    (2, 45, 1, 3, 32),
+    (8, 45, 16, 32, 32),
+]
+
+
+@pytest.mark.parametrize("shape", HEAD_DIMS, ids=lambda c: "B%dT%dHk%dHv%dD%d" % c)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("hm", [False, True], ids=["tm", "hm"])
+@pytest.mark.parametrize("gated", [True, False])
+def test_block_form_head_dims(shape, dtype, hm, gated):
+    """The block form at D = 32 and 64 on both kernels, three ragged blocks,
+    against the oracle; the default form there is the block form, bit for bit."""
+    B, T, Hk, Hv, D = shape
+    say("block form D=%d %s %s hm=%s gated=%s" % (D, shape, dtype, hm, gated))
+    ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm,
+                                seed=B * 11 + D + Hv)
+    yb, sb = run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="block")
+    yd, sd = run_both(ops, head_major=hm, gated=gated, dtype=dtype)
+    assert torch.equal(yb, yd) and torch.equal(sb, sd)
+
+
 # The block form with 16-bit q and k forms its products with the f32 state on
 # the bf16 matrix cores over bf16 parts.  With exact=True the state and Cs go
 # in three exact parts (two for an f16 value of q or k), so every term is an
@@ -224,21 +249,26 @@ def test_block_form_edge_shapes(case, gated):
 F32_LEVEL = 2e-5
 TWO_PART_LEVEL = 2e-4
 SIXTEEN_BIT_CASES = [
-    (1, 200, 2, 4, "bf16", False),   # few heads (rows_la_kernel), token-major
-    (1, 200, 2, 4, "f16", True),     # few heads, f16 q/k split in two bf16 parts, head-major
-    (2, 47, 16, 128, "bf16", True),  # 256 heads (state_kernel), bf16 parts
-    (1, 64, 16, 256, "f16", True),   # 256 heads, f16 split in two bf16 parts
+    # (B, T, Hk, Hv, D, dtype, head_major)
+    (1, 200, 2, 4, 128, "bf16", False),   # few heads (rows_la_kernel), token-major
+    (1, 200, 2, 4, 128, "f16", True),     # few heads, f16 q/k split in two bf16 parts, head-major
+    (2, 47, 16, 128, 128, "bf16", True),  # 256 heads (state_kernel), bf16 parts
+    (1, 64, 16, 256, 128, "f16", True),   # 256 heads, f16 split in two bf16 parts
+    (1, 150, 2, 4, 64, "f16", False),     # D = 64, few heads
+    (2, 40, 16, 128, 64, "bf16", True),   # D = 64, 256 heads
+    (1, 150, 1, 3, 32, "bf16", True),     # D = 32, few heads
+    (8, 40, 16, 32, 32, "f16", False),    # D = 32, 256 heads
 ]
 
 
-@pytest.mark.parametrize("case", SIXTEEN_BIT_CASES, ids=lambda c: "B%dT%dHk%dHv%d-%s-%s" % (
-    c[0], c[1], c[2], c[3], c[4], "hm" if c[5] else "tm"))
+@pytest.mark.parametrize("case", SIXTEEN_BIT_CASES, ids=lambda c: "B%dT%dHk%dHv%dD%d-%s-%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "hm" if c[6] else "tm"))
 @pytest.mark.parametrize("gated", [True, False])
 @pytest.mark.parametrize("exact", [True, False])
 def test_block_form_16bit_accuracy(case, gated, exact):
-    B, T, Hk, Hv, dtype, hm = case
+    B, T, Hk, Hv, D, dtype, hm = case
     say("16-bit block form accuracy %s gated=%s exact=%s" % (case, gated, exact))
-    ops = synth.random_operands(B, T, Hk, Hv, 128, 128, dtype=dtype, head_major=hm,
+    ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm,
                                 seed=B * 7 + T + Hv)
     d = dev(ops)
     z, w = (d.get("z"), d.get("w")) if gated else (None, None)
@@ -341,8 +371,8 @@ def test_mixed_fast_and_checked_chunks(case, form):
         ld[at(t)] = 0.3                  # growth over ten tokens
     for t in range(3, 9):
         ld[at(t)] = -6.5                 # six strong decays: a sum near the bound
-    if form == "block" and D != 128:
-        pytest.skip("the block form is built for D == 128")
+    if form == "block" and D not in (32, 64, 128):
+        pytest.skip("the block form is built for D = 32, 64 and 128")
     run_both(ops, head_major=hm, gated=True, dtype=dtype, form=form)
 
 
@@ -370,10 +400,16 @@ def test_in_place_state_and_time_chaining(exact):
     assert_close(st, s.double().cpu().numpy(), tol, "chained state")
 
 
-def test_steps_equal_scan():
+@pytest.mark.parametrize("form,exact,tol", [("per_token", False, 1e-5), ("block", True, 1e-5),
+                                            (None, False, TWO_PART_LEVEL)])
+def test_steps_equal_scan(form, exact, tol):
+    """Ten decode steps equal one scan: within f32 rounding for the token-by-token
+    form and for exact block products, within the two-part level for the
+    default form at D = 64 (the block form with rounded bf16 parts)."""
     ops = synth.random_operands(3, 10, 2, 6, 64, 64, dtype="f16", seed=11)
     d = dev(ops)
-    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"])
+    y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], d["w"],
+                form=form, exact=exact)
     st = d["s0"].clone()
     ys = []
     for t in range(10):
@@ -382,8 +418,8 @@ def test_steps_equal_scan():
                                 sl["z"], d["w"], inplace=True)
         ys.append(yt)
     torch.cuda.synchronize()
-    assert_close(torch.cat(ys, dim=1), y.double().cpu().numpy(), 1e-5, "steps y")
-    assert_close(st, s.double().cpu().numpy(), 1e-5, "steps state")
+    assert_close(torch.cat(ys, dim=1), y.double().cpu().numpy(), tol, "steps y")
+    assert_close(st, s.double().cpu().numpy(), tol, "steps state")
 
 
 def test_head_major_equals_token_major_bitwise():
