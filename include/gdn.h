@@ -83,8 +83,9 @@ typedef enum gdn_status {
 #define GDN_FOLD_QK_L2NORM 1u /* L2-normalise q and k inside the op */
 #define GDN_FOLD_Q_SCALE 2u   /* multiply q^ by 1/sqrt(Dk) inside the op */
 /* Form of gdn_scan's time loop.  The token-by-token form runs on the vector
- * units for every head dim; at Dk == Dv in {32, 64, 128} the block form runs
- * 16 tokens at a time as dense products on the matrix cores (the step is affine in S,
+ * units for every head dim; at Dk == Dv in {32, 64, 128}, and 256 with f16 or
+ * bf16 q and k, the block form runs 16 tokens at a time as dense products on
+ * the matrix cores (the step is affine in S,
  * "Module gdn" page, "The fusion").  Both give the same results up to
  * rounding.  With f16/bf16 q and k the block form multiplies the f32 state
  * (and its per-block correction) on the bf16 matrix cores through bf16 parts:
@@ -136,10 +137,11 @@ int gdn_recurrent_step_three_pass(const gdn_desc* d, const void* q, const void* 
 
 /* Bytes of device workspace gdn_scan needs for the descriptor `d`, written to
  * *bytes.  Zero when the chosen time loop keeps nothing between its kernels
- * (T <= 1, B == 0, the token-by-token form).  The block form (Dk == Dv in
- * {32, 64, 128} unless GDN_SCAN_PER_TOKEN) needs one 2560-byte record per value head
- * and 16-token block, plus 3072 bytes per key head and block when B * Hv is
- * below 256 (the few-head kernel's cross-block key products):
+ * (T <= 1, B == 0, the token-by-token form).  The block form (where it runs,
+ * see GDN_SCAN_BLOCK, unless GDN_SCAN_PER_TOKEN) needs one 2560-byte record
+ * per value head and 16-token block, plus 3072 bytes per key head and block
+ * when B * Hv is below 256 or the head dim is 256 (the few-head kernel's
+ * cross-block key products):
  *     B*Hv*ceil(T/16)*2560  [+ B*Hk*ceil(T/16)*3072].
  * Validates the descriptor as gdn_check does (pointers aside) and returns
  * GDN_OK or that status.  Host-only, no device work. */

@@ -84,8 +84,9 @@ int check_desc(const gdn_desc* d) {
   if (d->Dk != 16 && d->Dk != 32 && d->Dk != 64 && d->Dk != 128 && d->Dk != 256)
     return fail(GDN_EUNSUPPORTED, "head dim %lld not in {16, 32, 64, 128, 256}",
                 (long long)d->Dk);
-  if ((d->flags & GDN_SCAN_BLOCK) && !block_form_head_dim(d->Dk))
-    return fail(GDN_EUNSUPPORTED, "the block form needs Dk == Dv in {32, 64, 128}");
+  if ((d->flags & GDN_SCAN_BLOCK) && !block_form_fits(*d))
+    return fail(GDN_EUNSUPPORTED,
+                "the block form needs Dk == Dv in {32, 64, 128}, or 256 with 16-bit q and k");
 
   // sizes (with overflow checks)
   int64_t bt, nqk, nv, ng, ns, tmp;
@@ -99,12 +100,16 @@ int check_desc(const gdn_desc* d) {
   return GDN_OK;
 }
 
-bool block_form_head_dim(int64_t D) { return D == 32 || D == 64 || D == 128; }
+bool block_form_fits(const gdn_desc& d) {
+  return d.Dv == d.Dk && (d.Dk == 32 || d.Dk == 64 || d.Dk == 128 ||
+                          (d.Dk == 256 && d.dtype != GDN_F32));
+}
 
 bool scan_uses_block_form(const gdn_desc& d) {
-  return block_form_head_dim(d.Dk) && d.Dv == d.Dk && (d.flags & GDN_SCAN_PER_TOKEN) == 0 &&
-         d.T >= 2 && d.B > 0;
+  return block_form_fits(d) && (d.flags & GDN_SCAN_PER_TOKEN) == 0 && d.T >= 2 && d.B > 0;
 }
+
+bool scan_uses_key_products(const gdn_desc& d) { return d.B * d.Hv < kManyHeads || d.Dk > 128; }
 
 int64_t scan_record_bytes(const gdn_desc& d) {
   if (!scan_uses_block_form(d)) return 0;
@@ -116,7 +121,7 @@ int64_t scan_workspace_bytes(const gdn_desc& d) {
   if (!scan_uses_block_form(d)) return 0;
   const int64_t nblk = (d.T + kBlockTokens - 1) / kBlockTokens;
   int64_t bytes = scan_record_bytes(d);
-  if (d.B * d.Hv < kManyHeads) bytes += d.B * d.Hk * nblk * kKeyCrossBytes;
+  if (scan_uses_key_products(d)) bytes += d.B * d.Hk * nblk * kKeyCrossBytes;
   return bytes;
 }
 

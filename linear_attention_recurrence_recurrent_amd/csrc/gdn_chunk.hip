@@ -216,9 +216,13 @@ struct PrepArgs {
 template <int DT, int GT, int D, bool XB, bool TP>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   static_assert(XB || !TP, "the parts layout is the few-head kernel's");
-  // a lane holds D / 4 elements of a row: NU loads of 8
-  constexpr int NU = D / 32;
+  // a lane holds D / 4 elements of a row: NU loads of 8, taken in NCH chunks
+  // of NUC (more than 32 elements per lane would not fit beside the
+  // cross-block products: those rows are loaded and their products
+  // accumulated a chunk at a time)
+  constexpr int NU = D / 32, NUC = NU < 4 ? NU : 4, NCH = NU / NUC;
   static_assert(NU >= 1 && D % 32 == 0, "head dim a multiple of 32");
+  static_assert(NCH == 1 || (DT != GDN_F32 && XB), "chunked rows: 16-bit inputs, few heads");
   __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
   __shared__ __align__(16) float sAB[4][2][4][kL];  // [wave][alpha, beta][value head][token]
   // the wave index through readfirstlane: everything derived from the task
@@ -247,30 +251,34 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   // Addresses: a block base (uniform) plus a 32-bit offset per lane, so no
   // lane computes a 64-bit product.
   const uint32_t loff = (uint32_t)lc * (uint32_t)qk_ts + (uint32_t)(D / 4) * (uint32_t)lg;
-  Raw<DT, 8> kr[NU], qr[NU];
+  Raw<DT, 8> kr[NUC], qr[NUC];
   const int64_t rowb = qk_base + t0 * qk_ts;
+  auto load_rows = [&](int ch) {
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    if (lc < tc) {
-      kr[u].load(a.k, rowb + (int64_t)(loff + 8u * u));
-      qr[u].load(a.q, rowb + (int64_t)(loff + 8u * u));
-    } else {
-      kr[u].zero();
-      qr[u].zero();
+    for (int u = 0; u < NUC; ++u) {
+      if (lc < tc) {
+        kr[u].load(a.k, rowb + (int64_t)(loff + 8u * (ch * NUC + u)));
+        qr[u].load(a.q, rowb + (int64_t)(loff + 8u * (ch * NUC + u)));
+      } else {
+        kr[u].zero();
+        qr[u].zero();
+      }
     }
-  }
+  };
+  load_rows(0);
   // XB: the key rows of the two blocks before (block 0's where there is
   // none; those products are replaced by zero below)
-  [[maybe_unused]] Raw<DT, 8> kp1[NU], kp2[NU];
-  if constexpr (XB) {
-    const int64_t c1 = c > 0 ? c - 1 : 0, c2 = c > 1 ? c - 2 : 0;
-    const int64_t b1r = qk_base + c1 * kL * qk_ts, b2r = qk_base + c2 * kL * qk_ts;
+  [[maybe_unused]] Raw<DT, 8> kp1[NUC], kp2[NUC];
+  const int64_t c1 = c > 0 ? c - 1 : 0, c2 = c > 1 ? c - 2 : 0;
+  const int64_t b1r = qk_base + c1 * kL * qk_ts, b2r = qk_base + c2 * kL * qk_ts;
+  auto load_prev = [&](int ch) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      kp1[u].load(a.k, b1r + (int64_t)(loff + 8u * u));
-      kp2[u].load(a.k, b2r + (int64_t)(loff + 8u * u));
+    for (int u = 0; u < NUC; ++u) {
+      kp1[u].load(a.k, b1r + (int64_t)(loff + 8u * (ch * NUC + u)));
+      kp2[u].load(a.k, b2r + (int64_t)(loff + 8u * (ch * NUC + u)));
     }
-  }
+  };
+  if constexpr (XB) load_prev(0);
   // gates: lane (lg, lc) loads token lc of value head g0 + lg
   Raw<GT, 1> l1, b1;
   bool gld = false;
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   float ssk = 0.f, ssq = 0.f;
   if constexpr (DT == GDN_F32) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < NUC; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ssk = fmaf(kr[u].get(e), kr[u].get(e), ssk);
@@ -307,29 +315,48 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   // r: entry [4 lg + r][lc].  The contraction runs over the lane's own D / 4
   // elements: f32, one element per 16x16x4 product; 16-bit, four per 16x16x16
   // product straight from the loaded words (no widening).
-  auto gram = [&](const Raw<DT, 8>* x, const Raw<DT, 8>* y) {
-    v4f d = {0.f, 0.f, 0.f, 0.f};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  auto gram = [&](const Raw<DT, 8>* x, const Raw<DT, 8>* y, v4f d) {
     if constexpr (DT == GDN_F32) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
+      for (int u = 0; u < NUC; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = mfma4(x[u].get(e), y[u].get(e), d);
     } else {
 #pragma unroll
-      for (int m = 0; m < 2 * NU; ++m)
+      for (int m = 0; m < 2 * NUC; ++m)
         d = mm16<DT>(make_uint2(x[m / 2].w[2 * (m % 2)], x[m / 2].w[2 * (m % 2) + 1]),
                      make_uint2(y[m / 2].w[2 * (m % 2)], y[m / 2].w[2 * (m % 2) + 1]), d);
     }
     return d;
   };
-  // G = K K^T and H = Q K^T (raw)
-  const v4f G4 = gram(kr, kr), H4 = gram(qr, kr);
+  // chunked rows: every product accumulated chunk by chunk (Q Q^T and the
+  // cross-block ones too, since the chunk's rows are gone afterwards)
+  [[maybe_unused]] v4f Q4c = zero, M1c = zero, M2c = zero, N1c = zero;
+  v4f G4 = gram(kr, kr, zero), H4 = gram(qr, kr, zero);
+  if constexpr (NCH > 1) {
+    Q4c = gram(qr, qr, zero);
+    M1c = gram(kr, kp1, zero);
+    N1c = gram(qr, kp1, zero);
+    M2c = gram(kr, kp2, zero);
+#pragma unroll
+    for (int ch = 1; ch < NCH; ++ch) {
+      load_rows(ch);
+      load_prev(ch);
+      G4 = gram(kr, kr, G4);
+      H4 = gram(qr, kr, H4);
+      Q4c = gram(qr, qr, Q4c);
+      M1c = gram(kr, kp1, M1c);
+      N1c = gram(qr, kp1, N1c);
+      M2c = gram(kr, kp2, M2c);
+    }
+  }
   if constexpr (DT != GDN_F32) {
     // 16-bit inputs: the squared norms are the diagonals of K K^T (above) and
     // Q Q^T (one more product on the otherwise idle matrix cores instead of
     // 64 widening multiply-adds per lane): entry [lc][lc] sits in register
     // lc % 4 of lane (lc / 4) * 16 + lc
-    const v4f Q4 = gram(qr, qr);
+    const v4f Q4 = NCH > 1 ? Q4c : gram(qr, qr, zero);
     auto diag = [&](const v4f& m) {
       const int r = lc % 4;
       const float v = r == 0 ? m[0] : (r == 1 ? m[1] : (r == 2 ? m[2] : m[3]));
@@ -347,9 +374,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     // not exist), row-major: M1 = K_c K_(c-1)^T, M2 = K_c K_(c-2)^T and
     // N = Q_c K_(c-1)^T.  The few-head kernel forms K S^T and Q S^T of a
     // newer state from an older one with them.
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    const v4f M1 = c > 0 ? gram(kr, kp1) : zero, N1 = c > 0 ? gram(qr, kp1) : zero;
-    const v4f M2 = c > 1 ? gram(kr, kp2) : zero;
+    v4f M1, N1, M2;
+    if constexpr (NCH > 1) {
+      M1 = c > 0 ? M1c : zero;
+      N1 = c > 0 ? N1c : zero;
+      M2 = c > 1 ? M2c : zero;
+    } else {
+      M1 = c > 0 ? gram(kr, kp1, zero) : zero;
+      N1 = c > 0 ? gram(qr, kp1, zero) : zero;
+      M2 = c > 1 ? gram(kr, kp2, zero) : zero;
+    }
     float* mx = a.mx + task * (3 * kL * kL);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -945,12 +979,15 @@ template <int DT, int NSP, int D>
 __global__ __launch_bounds__(rows_la_threads(D)) __attribute__((amdgpu_waves_per_eu(2))) void
 rows_la_kernel(StateArgs a) {
   static_assert(NSP == 2 || NSP == 3, "two or three parts of the state and Cs");
-  static_assert(D % 32 == 0 && D <= 128, "head dim 32, 64 or 128");
+  static_assert(D % 32 == 0 && D <= (DT == GDN_F32 ? 128 : 256), "head dim 32 to 128 (256: 16-bit)");
   // NC state waves of two 16-key tiles each
   constexpr int NC = D / 32, NCT = 2, ROWS = 16, KP = lds_row<DT, D>(), NM = 3 * kL * kL;
   typedef LdsElem<DT> KT;
-  __shared__ __align__(16) KT sk[4][kL][KP];
-  __shared__ __align__(16) KT sq[4][kL][KP];
+  // f32 q and k rows staged in LDS (16-bit inputs: the state waves load their own;
+  // at D = 256 their unused slots shrink to a token)
+  constexpr int SKS = DT == GDN_F32 || D <= 128 ? 4 : 1, SKP = DT == GDN_F32 || D <= 128 ? KP : 8;
+  __shared__ __align__(16) KT sk[SKS][kL][SKP];
+  __shared__ __align__(16) KT sq[SKS][kL][SKP];
   __shared__ __align__(16) float sv[4][kL][ROWS];
   __shared__ __align__(16) float srec[4][kRecUsed];
   __shared__ __align__(16) float smx[4][NM];  // M1, M2, N of a block
@@ -1637,7 +1674,7 @@ rows_la_kernel(StateArgs a) {
 template <int DT, int GT, int D, bool TP>
 void launch_prep_gt(const PrepArgs& p, dim3 grid, hipStream_t st) {
   if (p.mx != nullptr) prep_kernel<DT, GT, D, true, TP><<<grid, 256, 0, st>>>(p);
-  else prep_kernel<DT, GT, D, false, false><<<grid, 256, 0, st>>>(p);
+  else if constexpr (D <= 128) prep_kernel<DT, GT, D, false, false><<<grid, 256, 0, st>>>(p);
 }
 
 template <int DT, int D, bool TP>
@@ -1657,13 +1694,16 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
   // the few-head kernel's default products take T and M1 as bf16 parts
   const int rc = launch_prep<DT, D, DT != GDN_F32 && NSP == 2>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;
-  // many heads: whole-head workgroups, the norm fused; few heads: a
-  // workgroup per 16 value rows with the one-block lookahead
+  // many heads: whole-head workgroups, the norm fused; few heads (and D =
+  // 256, whose whole-head state would overflow the registers): a workgroup
+  // per 16 value rows with the one-block lookahead
   StateArgs r = s;
-  if (heads >= kManyHeads) {
-    r.nrb = 1;
-    state_kernel<DT, NSP, D><<<dim3((unsigned)heads), 4 * D, 0, st>>>(r);
-    return device_status("state_kernel launch");
+  if constexpr (D <= 128) {
+    if (!scan_uses_key_products(d)) {
+      r.nrb = 1;
+      state_kernel<DT, NSP, D><<<dim3((unsigned)heads), 4 * D, 0, st>>>(r);
+      return device_status("state_kernel launch");
+    }
   }
   r.nrb = D / 16;
   rows_la_kernel<DT, NSP, D><<<dim3((unsigned)(heads * r.nrb)), rows_la_threads(D), 0, st>>>(r);
@@ -1676,6 +1716,10 @@ int launch_d(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t h
   switch (d.Dk) {
     case 32: return launch_dt<DT, NSP, 32>(d, p, s, heads, st);
     case 64: return launch_dt<DT, NSP, 64>(d, p, s, heads, st);
+    case 256:
+      if constexpr (DT != GDN_F32) return launch_dt<DT, NSP, 256>(d, p, s, heads, st);
+      set_error("the block form at D = 256 needs 16-bit q and k");
+      return GDN_EUNSUPPORTED;
     default: return launch_dt<DT, NSP, 128>(d, p, s, heads, st);
   }
 }
@@ -1695,7 +1739,7 @@ int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const v
   static_assert(kL == kBlockTokens, "block length");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t heads = d.B * d.Hv, nblk = (d.T + kL - 1) / kL;
-  *gated = heads >= kManyHeads;
+  *gated = !scan_uses_key_products(d);
   float* rec = static_cast<float*>(workspace);
   float* mx = *gated ? nullptr : rec + scan_record_bytes(d) / (int64_t)sizeof(float);
   const PrepArgs p{q, k, ld, beta, rec, d.T, nblk, d.B * d.Hk * nblk, (int)d.Hk, (int)d.Hv,

@@ -7,18 +7,22 @@ namespace gdn {
 
 // Layout of the block form's workspace (shared by the validator, which sizes
 // it, and the launcher, which lays it out): a record of kBlockRecordBytes per
-// (value head, 16-token block), then, when fewer than kManyHeads value heads
-// run, kKeyCrossBytes per (key head, block).
+// (value head, 16-token block), then, when the few-head kernel runs
+// (scan_uses_key_products), kKeyCrossBytes per (key head, block).
 constexpr int64_t kBlockTokens = 16;
 constexpr int64_t kBlockRecordBytes = 2560;
 constexpr int64_t kKeyCrossBytes = 3 * 16 * 16 * 4;
 constexpr int64_t kManyHeads = 256;
 constexpr uintptr_t kWorkspaceAlign = 256;
 
-// Head dims the block form covers (Dk == Dv).
-bool block_form_head_dim(int64_t D);
+// Whether the block form covers the head dim (Dk == Dv in {32, 64, 128}, or
+// 256 with 16-bit q and k).
+bool block_form_fits(const gdn_desc& d);
 // Whether gdn_scan runs the block form for this (valid) descriptor.
 bool scan_uses_block_form(const gdn_desc& d);
+// Whether the block form runs its few-head kernel (fewer than kManyHeads value
+// heads, or D = 256), which also keeps the cross-block key products.
+bool scan_uses_key_products(const gdn_desc& d);
 // Bytes of the records (first part of the workspace) and in total.
 int64_t scan_record_bytes(const gdn_desc& d);
 int64_t scan_workspace_bytes(const gdn_desc& d);
@@ -55,7 +59,7 @@ int launch_step_three_pass(const gdn_desc& d, const void* q, const void* k, cons
 int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, const void* ld,
                 const void* beta, const float* s0, const void* z, const void* w, float* y,
                 float* s_out, void* workspace, void* stream);
-// Block form on the matrix cores, Dk == Dv in {32, 64, 128}, with its records in
+// Block form on the matrix cores (block_form_fits), with its records in
 // `workspace` (scan_workspace_bytes(d) bytes); *gated reports whether the
 // gated norm was applied in the same launch (whole-head workgroups).
 int launch_scan_chunked(const gdn_desc& d, const void* q, const void* k, const void* v,

@@ -612,6 +612,7 @@ void launch_norm(int D, float* y, const void* z, const void* w, int64_t nvec, fl
   switch (D) {
     case 32: gated_norm_kernel<DT, 32><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
     case 64: gated_norm_kernel<DT, 64><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
+    case 256: gated_norm_kernel<DT, 256><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
     default: gated_norm_kernel<DT, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
   }
 }
@@ -624,8 +625,8 @@ int launch_scan(const gdn_desc& d, const void* q, const void* k, const void* v, 
                    (int)(d.Hv / d.Hk), 1, d.dtype, d.gate_dtype, d.head_major, d.flags,
                    d.qk_eps, d.norm_eps, q_scale(d)};
   const int64_t heads = d.B * d.Hv;
-  // the block form at D = 32, 64 and 128 (faster there on both the few-head
-  // and the many-head shapes) unless the token-by-token form is asked for
+  // the block form where it fits (faster there on both the few-head and the
+  // many-head shapes) unless the token-by-token form is asked for
   if (scan_uses_block_form(d)) {
     bool gated = false;
     int rc = launch_scan_chunked(d, q, k, v, ld, beta, s0, z, w, y, s_out, workspace, stream,

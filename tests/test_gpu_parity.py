@@ -171,7 +171,7 @@ def test_small_cases(case, gated):
     say("small %s gated=%s" % (case, gated))
     ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm, seed=B * 131 + T)
     run_both(ops, head_major=hm, gated=gated, dtype=dtype)
-    if D in (32, 64, 128):  # both forms of the time loop
+    if block_fits(D, dtype):  # both forms of the time loop
         run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="per_token")
         run_both(ops, head_major=hm, gated=gated, dtype=dtype, form="block")
 
@@ -213,12 +213,19 @@ def test_block_form_edge_shapes(case, gated):
 
 
 HEAD_DIMS = [
-    # (B, T, Hk, Hv, D): a workgroup per 16 value rows (few heads) or per head (256 heads)
+    # (B, T, Hk, Hv, D): a workgroup per 16 value rows (few heads) or per head (256 heads;
+    # at D = 256 a workgroup per 16 rows at any head count)
     (1, 45, 2, 4, 64),
     (8, 45, 16, 32, 64),
     (2, 45, 1, 3, 32),
     (8, 45, 16, 32, 32),
+    (1, 45, 2, 4, 256),
+    (8, 21, 16, 32, 256),
 ]
+
+
+def block_fits(D, dtype):
+    return D in (32, 64, 128) or (D == 256 and dtype != "f32")
 
 
 @pytest.mark.parametrize("shape", HEAD_DIMS, ids=lambda c: "B%dT%dHk%dHv%dD%d" % c)
@@ -226,9 +233,18 @@ HEAD_DIMS = [
 @pytest.mark.parametrize("hm", [False, True], ids=["tm", "hm"])
 @pytest.mark.parametrize("gated", [True, False])
 def test_block_form_head_dims(shape, dtype, hm, gated):
-    """The block form at D = 32 and 64 on both kernels, three ragged blocks,
-    against the oracle; the default form there is the block form, bit for bit."""
+    """The block form at D = 32, 64 and (16-bit) 256 on its kernels, ragged
+    blocks, against the oracle; the default form there is the block form, bit
+    for bit.  f32 at D = 256 takes the token-by-token form, and asking for the
+    block form there is rejected."""
     B, T, Hk, Hv, D = shape
+    if not block_fits(D, dtype):
+        ops = dev(synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm, seed=1))
+        with pytest.raises(GdnError) as e:
+            scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                 head_major=hm, form="block")
+        assert e.value.status == "GDN_EUNSUPPORTED"
+        return
     say("block form D=%d %s %s hm=%s gated=%s" % (D, shape, dtype, hm, gated))
     ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm,
                                 seed=B * 11 + D + Hv)
@@ -258,6 +274,8 @@ SIXTEEN_BIT_CASES = [
     (2, 40, 16, 128, 64, "bf16", True),   # D = 64, 256 heads
     (1, 150, 1, 3, 32, "bf16", True),     # D = 32, few heads
     (8, 40, 16, 32, 32, "f16", False),    # D = 32, 256 heads
+    (1, 60, 2, 4, 256, "bf16", False),    # D = 256, few heads
+    (8, 20, 16, 32, 256, "f16", True),    # D = 256, 256 heads (few-head kernel)
 ]
 
 
@@ -371,8 +389,8 @@ def test_mixed_fast_and_checked_chunks(case, form):
         ld[at(t)] = 0.3                  # growth over ten tokens
     for t in range(3, 9):
         ld[at(t)] = -6.5                 # six strong decays: a sum near the bound
-    if form == "block" and D not in (32, 64, 128):
-        pytest.skip("the block form is built for D = 32, 64 and 128")
+    if form == "block" and not block_fits(D, dtype):
+        pytest.skip("the block form covers D = 32, 64, 128 (and 256 with 16-bit q and k)")
     run_both(ops, head_major=hm, gated=True, dtype=dtype, form=form)
 
 
