@@ -47,9 +47,9 @@ DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_b64_counters.txt
 SCAN_COUNTERS = os.path.join(ROOT, "profiles", "scan_kernels_instruction_counters.txt")
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak
 # the kernels one default gdn_scan call launches, per scan workload
-SCAN_KERNELS = {3: ("rows_la_kernel<2, 2>", "prep_kernel<2, 2, true, true>",
+SCAN_KERNELS = {3: ("rows_la_kernel<2, 2, 128>", "prep_kernel<2, 2, 128, true, true>",
                     "gated_norm_kernel<2, 128>"),
-                4: ("state_kernel<1, 2>", "prep_kernel<1, 1, false, false>")}
+                4: ("state_kernel<1, 2, 128>", "prep_kernel<1, 1, 128, false, false>")}
 # sources the kernels are built from: their counters are stale once these change
 _CSRC = os.path.join(ROOT, "linear_attention_recurrence_recurrent_amd", "csrc")
 DECODE_SRC = [os.path.join(_CSRC, f) for f in ("gdn_decode.hip", "gdn_device.h")]
