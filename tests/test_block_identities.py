@@ -1,7 +1,8 @@
 """The block form's algebra, on the host in float64, against the per-token oracle.
 
-Both GPU scan kernels at D = 128 carry the recurrence over blocks of L = 16
-tokens ("Module gdn", section "The fusion": the step is affine in S).  With
+Both GPU block-form scan kernels carry the recurrence over blocks of L = 16
+tokens ("Module gdn", section "The fusion": the step is affine in S), at every
+head dim they take; the algebra below does not depend on it.  With
 k^, q^ the normalised rows, Dc[i][j] = alpha_(j+1) ... alpha_i (1 on the
 diagonal, 0 above), gam_i = alpha_0 ... alpha_i and S^T the state transposed:
   (I + Ls) C = diag(beta) V - diag(beta gam) K^ S^T,

@@ -1,4 +1,4 @@
-"""The recurrence's own identities on the GPU block form (D = 128), through the C ABI.
+"""The recurrence's own identities on the GPU block form, through the C ABI.
 
 The update S = alpha*S + beta*(v - alpha*S.k^) k^T of the "Module gdn" page
 (module description) fixes, for special gates and keys, results that need no
@@ -11,11 +11,13 @@ oracle:
     reads its value back;
   - beta = 1 and a unit key overwrite: S_new . k^ = v for any alpha, so a key
     repeated on consecutive tokens of one block keeps only the latest value.
-Each case runs on both block-form kernels (fewer than 256 value heads: the
-kernel with a workgroup per 16 state rows; 256 and more: a workgroup per
-head) in both layouts and all three operand dtypes, and is also compared with
-the float64 oracle at the usual bar.  The closed forms are evaluated in
-float64 from the exact operand values.
+Each case runs at head dim 128 on both block-form kernels (fewer than 256
+value heads: the kernel with a workgroup per 16 state rows; 256 and more: a
+workgroup per head) in both layouts and all three operand dtypes, at head dims
+32 and 64 with float32 and bfloat16 operands, and at 256 with float16 and
+bfloat16 (where both head counts take the kernel with a workgroup per 16 rows);
+each is also compared with the float64 oracle at the usual bar.  The closed
+forms are evaluated in float64 from the exact operand values.
 """
 import sys
 
@@ -30,7 +32,6 @@ from oracle import gdn_oracle as orc
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-D = 128
 TOL = {"f32": 1e-4, "f16": 3e-3, "bf16": 3e-3}
 CLOSED = 1e-4  # closed forms: f32 arithmetic on exact inputs
 SHAPES = {"few_heads": (1, 2, 4), "many_heads": (8, 16, 32)}  # (B, Hk, Hv)
@@ -50,7 +51,7 @@ def _cast(a, dt):
     return synth._cast(np.asarray(a, dtype=np.float64), dt).double().numpy()
 
 
-def _ops(B, T, Hk, Hv, dt, seed):
+def _ops(B, T, Hk, Hv, dt, seed, D):
     """Random operands, token-major, float64 arrays holding values exact in dt."""
     r = np.random.default_rng(seed)
     ops = dict(q=_cast(r.standard_normal((B, T, Hk, D)), dt),
@@ -65,7 +66,8 @@ def _ops(B, T, Hk, Hv, dt, seed):
 
 
 def _run(ops, dt, head_major, gated, exact=False):
-    """GPU scan (default form = block form at D = 128) and the oracle on the same values."""
+    """GPU scan (the default form, which is the block form at these head dims) and the
+    oracle on the same values."""
     tdt = synth.DTYPES[dt]
 
     def dev(name):
@@ -101,18 +103,20 @@ def _close(got, ref, tol, what):
         what, worst, tol, np.unravel_index(int(err.argmax()), err.shape))
 
 
-CASES = [(kind, dt, hm) for kind in SHAPES for dt in ("f32", "bf16", "f16") for hm in (False, True)]
-# the 16-bit block form's default (two rounded bf16 parts of the state) and exact (three) modes
-IDS = ["%s-%s-%s" % (c[0], c[1], "hm" if c[2] else "tm") for c in CASES]
+CASES = ([(kind, dt, hm, 128) for kind in SHAPES for dt in ("f32", "bf16", "f16")
+          for hm in (False, True)]
+         + [(kind, dt, False, d) for d in (32, 64) for kind in SHAPES for dt in ("f32", "bf16")]
+         + [(kind, dt, False, 256) for kind in SHAPES for dt in ("bf16", "f16")])
+IDS = ["%s-%s-%s-d%d" % (c[0], c[1], "hm" if c[2] else "tm", c[3]) for c in CASES]
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_decay_one_beta_zero_leaves_state(case):
-    kind, dt, hm = case
+    kind, dt, hm, D = case
     B, Hk, Hv = SHAPES[kind]
     T = 45  # two full blocks and a ragged one
     say("identity alpha=1 beta=0 %s" % (case,))
-    ops = _ops(B, T, Hk, Hv, dt, seed=1)
+    ops = _ops(B, T, Hk, Hv, dt, seed=1, D=D)
     ops["log_decay"][:] = 0.0
     ops["beta"][:] = 0.0
     y, s = _run(ops, dt, hm, gated=False)
@@ -125,12 +129,12 @@ def test_decay_one_beta_zero_leaves_state(case):
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_zero_decay_mid_block_restarts_memory(case):
-    kind, dt, hm = case
+    kind, dt, hm, D = case
     B, Hk, Hv = SHAPES[kind]
     say("identity alpha=0 mid-block %s" % (case,))
     G = Hv // Hk
     for j in (5, 23):  # row 5 of block 0, row 7 of block 1
-        ops = _ops(B, j + 1, Hk, Hv, dt, seed=2 + j)
+        ops = _ops(B, j + 1, Hk, Hv, dt, seed=2 + j, D=D)
         ops["log_decay"][:, j] = -np.inf
         y, s = _run(ops, dt, hm, gated=False)
         kh = _unit(np.repeat(ops["k"][:, j], G, axis=1))          # [B, Hv, D]
@@ -141,14 +145,14 @@ def test_zero_decay_mid_block_restarts_memory(case):
         o = be * ops["v"][:, j] * (kh * qh).sum(-1, keepdims=True)
         _close(y[:, j], o, CLOSED, "o = beta v (k^.q^) at the restart")
     # the restart in the middle of a longer scan, gated, against the oracle only
-    ops = _ops(B, 70, Hk, Hv, dt, seed=9)
+    ops = _ops(B, 70, Hk, Hv, dt, seed=9, D=D)
     ops["log_decay"][:, 37] = -np.inf
     _run(ops, dt, hm, gated=True)
 
 
-def _hadamard_keys(B, T, Hk, seed):
-    """Rows of a 128 x 128 +-1 Hadamard matrix with random signs, a random
-    subset per (batch, key head): exactly orthogonal, exact in every dtype."""
+def _hadamard_keys(B, T, Hk, seed, D):
+    """Rows of a D x D +-1 Hadamard matrix with random signs, a random subset
+    per (batch, key head): exactly orthogonal, exact in every dtype."""
     r = np.random.default_rng(seed)
     H = scipy.linalg.hadamard(D).astype(np.float64)
     k = np.empty((B, T, Hk, D))
@@ -163,20 +167,23 @@ def _hadamard_keys(B, T, Hk, seed):
 RECALL = [(c, False) for c in CASES] + [(c, True) for c in CASES if c[1] != "f32"]
 
 
-RECALL_IDS = ["%s-%s-%s-%s" % (c[0], c[1], "hm" if c[2] else "tm", "exact" if e else "default")
-              for c, e in RECALL]
+RECALL_IDS = ["%s-%s-%s-d%d-%s" % (c[0], c[1], "hm" if c[2] else "tm", c[3],
+                                   "exact" if e else "default") for c, e in RECALL]
+# at most D orthonormal keys: a whole number of blocks and a ragged count per head dim
+RECALL_T = {32: (32, 27), 64: (64, 50), 128: (128, 100), 256: (128, 100)}
 
 
 @pytest.mark.parametrize("case,exact", RECALL, ids=RECALL_IDS)
-@pytest.mark.parametrize("T", [128, 100])
-def test_associative_recall_orthonormal_keys(case, exact, T):
-    kind, dt, hm = case
+@pytest.mark.parametrize("which", [0, 1], ids=["whole-blocks", "ragged"])
+def test_associative_recall_orthonormal_keys(case, exact, which):
+    kind, dt, hm, D = case
+    T = RECALL_T[D][which]
     B, Hk, Hv = SHAPES[kind]
     say("identity associative recall T=%d %s" % (T, case))
     G = Hv // Hk
     r = np.random.default_rng(T)
-    ops = _ops(B, T, Hk, Hv, dt, seed=3)
-    ops["k"] = _hadamard_keys(B, T, Hk, seed=4)
+    ops = _ops(B, T, Hk, Hv, dt, seed=3, D=D)
+    ops["k"] = _hadamard_keys(B, T, Hk, seed=4, D=D)
     ops["s0"][:] = 0.0
     ops["log_decay"][:] = 0.0
     ops["beta"][:] = 1.0
@@ -193,12 +200,12 @@ def test_associative_recall_orthonormal_keys(case, exact, T):
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_repeated_key_in_block_keeps_latest_value(case):
-    kind, dt, hm = case
+    kind, dt, hm, D = case
     B, Hk, Hv = SHAPES[kind]
     say("identity repeated key %s" % (case,))
     G = Hv // Hk
     T = 26  # the run covers rows 3..9 of block 1 (tokens 19..25)
-    ops = _ops(B, T, Hk, Hv, dt, seed=5)
+    ops = _ops(B, T, Hk, Hv, dt, seed=5, D=D)
     run = slice(19, 26)
     ops["k"][:, run] = ops["k"][:, 19:20]
     ops["q"][:, run] = ops["k"][:, 19:20]

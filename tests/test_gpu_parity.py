@@ -2,9 +2,10 @@
 
 Bar: |gpu - ref| <= tol * (1 + |ref|) element by element, with tol = 1e-4 for
 float32 operands and 3e-3 for float16/bfloat16 operands (float32 state in both
-cases), applied to y AND the final state.  Small cases are compared in full;
-the full-size workloads compare every output of a sample of heads, which the
-oracle computes one by one (heads are independent through the recurrence).
+cases), applied to y AND the final state.  Small cases are compared in full,
+and so are the full-size workloads: the oracle computes every batch entry and
+value head of them in seconds.  The block form is also compared at head dims 32,
+64 and 256 (the last with 16-bit q and k only).
 """
 import math
 import sys
@@ -61,18 +62,18 @@ def run_both(ops, *, head_major, gated, dtype, form=None, **kw):
     return y, s
 
 
-# ------------------------------------------------------------------ configs 0 and 1 in full
+# ------------------------------------------------------------------ tiny scan and single decode step, in full
 @pytest.mark.parametrize("gated", [True, False])
-def test_config0_tiny_scan_f32(gated):
+def test_tiny_scan_f32_b1_t8_d16(gated):
     w = synth.WORKLOADS[0]
-    say("config0 gated=%s" % gated)
+    say("tiny scan f32 B=1 T=8 D=16, gated=%s" % gated)
     run_both(synth.make(w), head_major=False, gated=gated, dtype="f32")
 
 
 @pytest.mark.parametrize("gated", [True, False])
-def test_config1_decode_step_bf16(gated):
+def test_decode_step_bf16_b1(gated):
     wl = synth.WORKLOADS[1]
-    say("config1 gated=%s" % gated)
+    say("decode step bf16 B=1, gated=%s" % gated)
     ops = synth.make(wl)
     d = dev(ops)
     z, w = (d["z"], d["w"]) if gated else (None, None)
@@ -544,9 +545,9 @@ def _oracle_full(idx, gated):
 
 
 @pytest.mark.parametrize("gated", [True, False])
-def test_config2_chained_decode_every_head(gated):
+def test_decode_b64_chained_steps_every_head(gated):
     wl = synth.WORKLOADS[2]
-    say("config2: 100 chained in-place decode steps, B=64, gated=%s" % gated)
+    say("decode: 100 chained in-place decode steps, B=64, gated=%s" % gated)
     ops = synth.make(wl)
     steps = synth.step_slices(ops, head_major=False)
     d_steps = [dev(st) for st in steps]
@@ -560,8 +561,8 @@ def test_config2_chained_decode_every_head(gated):
     torch.cuda.synchronize()
     yall = torch.cat(ys, dim=1)  # [B, 100, Hv, D]: the chain is the scan over 100 tokens
     yr, sr = _oracle_full(2, gated)
-    assert_close(yall, yr, TOL["bf16"], "config2 y (all %d heads)" % (wl.B * wl.Hv))
-    assert_close(state, sr, TOL["bf16"], "config2 final state")
+    assert_close(yall, yr, TOL["bf16"], "chained decode y (all %d heads)" % (wl.B * wl.Hv))
+    assert_close(state, sr, TOL["bf16"], "chained decode final state")
 
 
 FORMS = [(None, False), ("per_token", False), ("block", False), ("block", True)]
@@ -569,23 +570,23 @@ FORMS = [(None, False), ("per_token", False), ("block", False), ("block", True)]
 
 @pytest.mark.parametrize("gated", [True, False])
 @pytest.mark.parametrize("form,exact", FORMS)
-def test_config3_prefill_scan_every_head(form, exact, gated):
+def test_prefill_b1_t4096_every_head(form, exact, gated):
     wl = synth.WORKLOADS[3]
-    say("config3: B=1 T=4096 token-major scan, form %s exact %s, gated=%s" % (form, exact, gated))
+    say("prefill: B=1 T=4096 token-major scan, form %s exact %s, gated=%s" % (form, exact, gated))
     d = dev(synth.make(wl))
     y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
                 d["z"] if gated else None, d["w"] if gated else None, form=form, exact=exact)
     torch.cuda.synchronize()
     yr, sr = _oracle_full(3, gated)
-    assert_close(y, yr, TOL["bf16"], "config3 y")
-    assert_close(s, sr, TOL["bf16"], "config3 final state")
+    assert_close(y, yr, TOL["bf16"], "prefill y")
+    assert_close(s, sr, TOL["bf16"], "prefill final state")
 
 
 @pytest.mark.parametrize("gated", [True, False])
 @pytest.mark.parametrize("form,exact", FORMS)
-def test_config4_head_major_scan_every_head(form, exact, gated):
+def test_head_major_b16_t1024_every_head(form, exact, gated):
     wl = synth.WORKLOADS[4]
-    say("config4: B=16 T=1024 head-major f16 scan, form %s exact %s, gated=%s" % (
+    say("head-major: B=16 T=1024 head-major f16 scan, form %s exact %s, gated=%s" % (
         form, exact, gated))
     d = dev(synth.make(wl))
     y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"],
@@ -593,5 +594,5 @@ def test_config4_head_major_scan_every_head(form, exact, gated):
                 form=form, exact=exact)
     torch.cuda.synchronize()
     yr, sr = _oracle_full(4, gated)
-    assert_close(y, yr, TOL["f16"], "config4 y")
-    assert_close(s, sr, TOL["f16"], "config4 final state")
+    assert_close(y, yr, TOL["f16"], "head-major y")
+    assert_close(s, sr, TOL["f16"], "head-major final state")
