@@ -92,10 +92,12 @@ typedef enum gdn_status {
  * by default two parts rounded to nearest, each term then within 2^-16
  * relative of the f32 product; with GDN_SCAN_EXACT three exact parts, each
  * term an exact f32 product (f32 accuracy; up to 1.2x the time).
- * f32 q and k take f32 products either way.  Without a form flag the block
- * form runs at those head dims and the token-by-token form otherwise; with
- * both form flags, or GDN_SCAN_BLOCK at another head dim, the call is
- * rejected (GDN_EINVAL / GDN_EUNSUPPORTED).  The block form keeps per-block
+ * f32 q and k take f32 products either way.  The block form also needs
+ * Hk*Dk and Hv*Dv below 2^27 and T below 2^29 (its offsets inside a block are
+ * 32-bit).  Without a form flag the block form runs where it fits and the
+ * token-by-token form otherwise; with both form flags, or GDN_SCAN_BLOCK
+ * where the block form does not fit, the call is rejected (GDN_EINVAL /
+ * GDN_EUNSUPPORTED).  The block form keeps per-block
  * records in a caller-supplied workspace (gdn_scan_workspace_size). */
 #define GDN_SCAN_PER_TOKEN 4u
 #define GDN_SCAN_BLOCK 8u

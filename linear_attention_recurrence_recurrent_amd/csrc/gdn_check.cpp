@@ -86,7 +86,9 @@ int check_desc(const gdn_desc* d) {
                 (long long)d->Dk);
   if ((d->flags & GDN_SCAN_BLOCK) && !block_form_fits(*d))
     return fail(GDN_EUNSUPPORTED,
-                "the block form needs Dk == Dv in {32, 64, 128}, or 256 with 16-bit q and k");
+                block_head_dims_fit(*d)
+                    ? "the block form needs Hk*Dk and Hv*Dv below 2^27 and T below 2^29"
+                    : "the block form needs Dk == Dv in {32, 64, 128}, or 256 with 16-bit q and k");
 
   // sizes (with overflow checks)
   int64_t bt, nqk, nv, ng, ns, tmp;
@@ -100,9 +102,19 @@ int check_desc(const gdn_desc* d) {
   return GDN_OK;
 }
 
-bool block_form_fits(const gdn_desc& d) {
+bool block_head_dims_fit(const gdn_desc& d) {
   return d.Dv == d.Dk && (d.Dk == 32 || d.Dk == 64 || d.Dk == 128 ||
                           (d.Dk == 256 && d.dtype != GDN_F32));
+}
+
+// The block-form kernels address the rows of a 16-token block from the
+// block's 64-bit base with 32-bit per-lane offsets: up to 15 token strides of
+// Hk*Dk or Hv*Dv elements, or (head-major gates) 3 time strides of T.  Shapes
+// past these bounds take the per-token form, whose offsets are all 64-bit.
+bool block_form_fits(const gdn_desc& d) {
+  const int64_t lim = (int64_t)1 << 27;  // 16 * H * D < 2^31
+  return block_head_dims_fit(d) && d.Hk < lim / d.Dk && d.Hv < lim / d.Dv &&
+         d.T < ((int64_t)1 << 29);
 }
 
 bool scan_uses_block_form(const gdn_desc& d) {

@@ -17,6 +17,9 @@ constexpr uintptr_t kWorkspaceAlign = 256;
 
 // Whether the block form covers the head dim (Dk == Dv in {32, 64, 128}, or
 // 256 with 16-bit q and k).
+bool block_head_dims_fit(const gdn_desc& d);
+// ... and the shape: Hk*Dk and Hv*Dv below 2^27 and T below 2^29, which keep
+// the kernels' 32-bit offsets inside a 16-token block in range.
 bool block_form_fits(const gdn_desc& d);
 // Whether gdn_scan runs the block form for this (valid) descriptor.
 bool scan_uses_block_form(const gdn_desc& d);

@@ -144,6 +144,23 @@ def test_rejects_unsupported_head_dim():
     assert rc == 5
 
 
+def test_block_form_bounds_its_in_block_offsets():
+    """The block-form kernels address a 16-token block's rows with 32-bit lane
+    offsets: past Hk*Dk or Hv*Dv = 2^27 or T = 2^29 an explicit block form is
+    rejected with a reason and the automatic choice is the per-token form,
+    whose offsets are 64-bit (so it needs no workspace)."""
+    D = dict(Dk=128, Dv=128)
+    for kw in (dict(B=1, T=16, Hk=1 << 20, Hv=1 << 20), dict(B=1, T=16, Hk=16, Hv=1 << 20),
+               dict(B=1, T=1 << 29, Hk=1, Hv=2)):
+        rc, why = check(_good(flags=3 | 8, **kw, **D), **_ops())
+        assert rc == 5 and "2^27" in why, (kw, rc, why)
+        assert _ws_size(**kw, **D) == (0, 0), kw
+    # just inside the bounds the block form runs: key heads x D = 2^27 - 128
+    inside = dict(B=1, T=16, Hk=(1 << 20) - 1, Hv=(1 << 20) - 1, **D)
+    assert _ws_size(**inside) == (0, ((1 << 20) - 1) * 2560)
+    assert _ws_size(B=1, T=(1 << 29) - 1, Hk=1, Hv=2, **D)[1] > 0
+
+
 def test_rejects_null_and_half_gate_pair():
     L = nat.lib()
     assert L.gdn_check(None, *([None] * 11), 0) == 1
