@@ -1,5 +1,6 @@
 // Time-axis scan of the Gated DeltaNet recurrence in block form on the matrix
-// cores (gfx950 MFMA, FP32 in and out), for D = 32, 64 and 128.
+// cores (gfx950 MFMA, FP32 in and out), for D = 32, 64 and 128, and 256 with
+// 16-bit q and k.
 //
 // The recurrence is the one of the "Module gdn" page (module description).
 // Its section "The fusion" observes that the step is affine in the memory S;
@@ -29,11 +30,13 @@
 //                on raw q and k with the norms folded into per-token scales.
 //                With f32 inputs these are v_mfma_f32_16x16x4f32 products.
 //                With 16-bit inputs the products with the f32 state run on
-//                the bf16 matrix cores over exact bf16 parts: the state and
-//                Cs as three parts each, f16 q and k as two (split_bf3
-//                below), so every term is an exact product in f32 and the
-//                sums differ from f32 products only in their order (the
-//                few-head kernel does this for bf16 inputs).
+//                the bf16 matrix cores over bf16 parts of the state and of
+//                Cs: by default two parts rounded to nearest (split_bf2
+//                below; each term within 2^-16 relative of the f32
+//                product), with GDN_SCAN_EXACT three exact ones (split_bf3:
+//                every term an exact f32 product, the sums differing from
+//                f32 products only in their order); f16 q and k enter as two
+//                exact bf16 parts, bf16 ones as they are.
 // The sequential chain then holds only the products with S.  S^T stays in the
 // accumulator layout for the whole time axis: lane l, register r of a 16 x 16
 // tile holds S^T[4(l/16) + r][l%16] (key row within the tile, value column),
@@ -1726,8 +1729,8 @@ int launch_d(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t h
 
 }  // namespace
 
-// The block-form scan for D == 128; y receives the raw o (the gated norm, when
-// asked for and not fused, runs after it).  Returns whether the gated output
+// The block-form scan at the head dims block_form_fits admits; y receives the
+// raw o (the gated norm, when asked for and not fused, runs after it).  Returns whether the gated output
 // was written (fused) through *gated.  The block records (and, for few heads,
 // the cross-block key products) live in the caller's workspace, laid out as
 // scan_workspace_bytes() sizes it: records first, then the key products.
