@@ -279,7 +279,10 @@ def bench_decode(args, torch):
     achieved = state_bytes / launch_s / 1e9
     traffic = read_counters()
     ceiling = streaming_ceiling(torch, state_bytes // 2, args)
-    kernel = "decode_kernel<bf16,bf16,128,16,2,16>"
+    # template arguments: operand and gate dtype, D, lanes per row, rows per
+    # lane, waves, the state stores' cache policy (18 = nt | sc1: from 128 MiB
+    # of state the stores are written through at device scope)
+    kernel = "decode_kernel<bf16,bf16,128,16,2,16,18>"
     res = dict(ms_per_step=ms_per_chain, value=value, launch_us=launch_s * 1e6,
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

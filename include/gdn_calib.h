@@ -15,8 +15,10 @@
  * `variant` picks the access shape (GDN_CALIB_VARIANTS of them): a workgroup
  * of 256, 512 or 1024 threads owns a contiguous chunk of 16-byte vectors,
  * each lane issues all of its 4, 8 or 16 loads before any store, with
- * nontemporal or ordinary loads and stores; gdn_calib_variant_name() names
- * it.  bytes must be a multiple of 16 and src/dst 16-byte aligned device
+ * nontemporal or ordinary loads and stores, or (the last three) buffer loads
+ * and stores with the decode's cache policies: nontemporal loads, stores
+ * nontemporal and written through to device scope; gdn_calib_variant_name()
+ * names it.  bytes must be a multiple of 16 and src/dst 16-byte aligned device
  * pointers owned by the caller; for GDN_CALIB_COPY they must not overlap.
  * Asynchronous on `stream`; allocates nothing; returns a gdn_status
  * (include/gdn.h) with the reason in gdn_last_error().
@@ -32,7 +34,7 @@ extern "C" {
 
 #define GDN_CALIB_RMW 0
 #define GDN_CALIB_COPY 1
-#define GDN_CALIB_VARIANTS 12
+#define GDN_CALIB_VARIANTS 15
 
 int gdn_calib_stream(int32_t op, int32_t variant, const void* src, void* dst, uint64_t bytes,
                      void* stream);

@@ -28,7 +28,7 @@ EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan",
            "gdn_scan_workspace_size", "gdn_scan_noalloc", "gdn_gates", "gdn_conv_silu", "gdn_check",
            "gdn_last_error", "gdn_status_str", "gdn_abi_version", "gdn_calib_stream",
            "gdn_calib_variant_name")
-GDN_CALIB_RMW, GDN_CALIB_COPY, GDN_CALIB_VARIANTS = 0, 1, 12
+GDN_CALIB_RMW, GDN_CALIB_COPY, GDN_CALIB_VARIANTS = 0, 1, 15
 GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 

@@ -41,6 +41,32 @@ __global__ __launch_bounds__(TPB) void stream_kernel(const float* src, float* ds
   }
 }
 
+// The same through buffer loads and stores with the decode's cache policies
+// (nt loads, nt | sc1 stores, gdn_device.h); a workgroup's resources span its
+// chunk, so the tail of the last chunk reads zeros and writes nothing.
+template <int TPB, int U, bool RMW>
+__global__ __launch_bounds__(TPB) void stream_buf_kernel(const float* src, float* dst, int64_t n4) {
+  const int64_t c0 = (int64_t)blockIdx.x * (TPB * U);
+  const int64_t left = n4 - c0;
+  const uint32_t bytes = (uint32_t)((left < TPB * U ? left : TPB * U) * 16);
+  const __amdgpu_buffer_rsrc_t rs = stream_rsrc(src + 4 * c0, bytes);
+  const __amdgpu_buffer_rsrc_t rd = stream_rsrc(dst + 4 * c0, bytes);
+  float4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = buf_load4<kStreamLoad>(rs, 16u * (threadIdx.x + u * TPB));
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float4 s = v[u];
+    if constexpr (RMW) {
+      s.x = fmaf(s.x, 1.0000001f, 1e-7f);
+      s.y = fmaf(s.y, 1.0000001f, 1e-7f);
+      s.z = fmaf(s.z, 1.0000001f, 1e-7f);
+      s.w = fmaf(s.w, 1.0000001f, 1e-7f);
+    }
+    buf_store4<kStoreThrough>(s, rd, 16u * (threadIdx.x + u * TPB));
+  }
+}
+
 // names in the order of the launch switch below
 constexpr const char* kVariantNames[GDN_CALIB_VARIANTS] = {
     "512 threads x 8 vectors, nontemporal",  "256 threads x 8 vectors, nontemporal",
@@ -49,6 +75,9 @@ constexpr const char* kVariantNames[GDN_CALIB_VARIANTS] = {
     "512 threads x 8 vectors, ordinary",     "256 threads x 8 vectors, ordinary",
     "512 threads x 16 vectors, ordinary",    "256 threads x 16 vectors, ordinary",
     "1024 threads x 4 vectors, ordinary",    "256 threads x 4 vectors, ordinary",
+    "256 threads x 4 vectors, buffer, stores through to device scope",
+    "1024 threads x 4 vectors, buffer, stores through to device scope",
+    "512 threads x 8 vectors, buffer, stores through to device scope",
 };
 
 template <int TPB, int U, bool NT>
@@ -56,6 +85,13 @@ void launch_v(bool rmw, const float* src, float* dst, int64_t n4, hipStream_t st
   const dim3 grid((unsigned)((n4 + TPB * U - 1) / (TPB * U)));
   if (rmw) stream_kernel<TPB, U, NT, true><<<grid, TPB, 0, st>>>(src, dst, n4);
   else stream_kernel<TPB, U, NT, false><<<grid, TPB, 0, st>>>(src, dst, n4);
+}
+
+template <int TPB, int U>
+void launch_b(bool rmw, const float* src, float* dst, int64_t n4, hipStream_t st) {
+  const dim3 grid((unsigned)((n4 + TPB * U - 1) / (TPB * U)));
+  if (rmw) stream_buf_kernel<TPB, U, true><<<grid, TPB, 0, st>>>(src, dst, n4);
+  else stream_buf_kernel<TPB, U, false><<<grid, TPB, 0, st>>>(src, dst, n4);
 }
 
 }  // namespace
@@ -108,7 +144,10 @@ int gdn_calib_stream(int32_t op, int32_t variant, const void* src, void* dst, ui
     case 8: launch_v<512, 16, false>(rmw, s, d, n4, st); break;
     case 9: launch_v<256, 16, false>(rmw, s, d, n4, st); break;
     case 10: launch_v<1024, 4, false>(rmw, s, d, n4, st); break;
-    default: launch_v<256, 4, false>(rmw, s, d, n4, st); break;
+    case 11: launch_v<256, 4, false>(rmw, s, d, n4, st); break;
+    case 12: launch_b<256, 4>(rmw, s, d, n4, st); break;
+    case 13: launch_b<1024, 4>(rmw, s, d, n4, st); break;
+    default: launch_b<512, 8>(rmw, s, d, n4, st); break;
   }
   return device_status("stream_kernel launch");
 }

@@ -17,7 +17,9 @@
 // columns with the same coefficient.  A workgroup owns a whole head: it
 // streams the head's rows from HBM with nontemporal 16-byte loads and stores,
 // issuing every load of a lane before any arithmetic, and applies the gated
-// RMSNorm in the same launch.
+// RMSNorm in the same launch.  The state goes through buffer loads and
+// stores with streaming cache policies (stores written through at device
+// scope from kWriteThroughBytes of state on: stream_rsrc in gdn_device.h).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -70,22 +72,24 @@ __device__ __forceinline__ void decode_fetch(const StepArgs& a, int64_t head,
     R.k[m].load(a.k, qk + 4 * (m * CL + j));
     R.q[m].load(a.q, qk + 4 * (m * CL + j));
   }
-  const float* s0 = a.s0 + head * (int64_t)(D * D);
+  const __amdgpu_buffer_rsrc_t rs = stream_rsrc(a.s0 + head * (int64_t)(D * D), D * D * 4);
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
 #pragma unroll
-    for (int m = 0; m < NV4; ++m) R.S[r][m] = nt_load4(s0 + (row0 + r) * D + 4 * (m * CL + j));
+    for (int m = 0; m < NV4; ++m)
+      R.S[r][m] = buf_load4<kStreamLoad>(rs, 4 * ((row0 + r) * D + 4 * (m * CL + j)));
   }
   R.v.load(a.v, head * D + row0);
   if (a.z) R.z.load(a.z, head * D + row0);
 }
 
 // Fold the norms, run the fused row pass, write the state back and the
-// (gated) output.  The L2 norms and the q scale are applied to the reduced
-// dots as scalars (u = rk*(S.k), w = rq*(S.q), S += (coef*rk) k), so the
-// normalised vectors are never materialised.  red[NW] is this head's slot for
+// (gated) output, the state stored with cache policy SP.  The L2 norms and
+// the q scale are applied to the reduced dots as scalars (u = rk*(S.k),
+// w = rq*(S.q), S += (coef*rk) k), so the normalised vectors are never
+// materialised.  red[NW] is this head's slot for
 // the cross-wave sum of the gated norm.
-template <int DT, int GT, int D, int CL, int RPL, int NW>
+template <int DT, int GT, int D, int CL, int RPL, int NW, int SP>
 __device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
                                               HeadRegs<DT, D, CL, RPL>& R, float* red) {
   constexpr int NV4 = D / CL / 4;
@@ -136,7 +140,7 @@ __device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
     ck[r] = coef * rk;  // coefficient of the raw k in the update
   }
   // S = alpha*S + coef*k^, written back from the registers
-  float* so = a.s_out + head * (int64_t)(D * D);
+  const __amdgpu_buffer_rsrc_t ro = stream_rsrc(a.s_out + head * (int64_t)(D * D), D * D * 4);
 #pragma unroll
   for (int m = 0; m < NV4; ++m) {
     const float4 kf = R.k[m].get4(0);
@@ -147,7 +151,7 @@ __device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
       s.y = fmaf(ck[r], kf.y, al * s.y);
       s.z = fmaf(ck[r], kf.z, al * s.z);
       s.w = fmaf(ck[r], kf.w, al * s.w);
-      nt_store4(s, so + (row0 + r) * D + 4 * (m * CL + j));
+      buf_store4<SP>(s, ro, 4 * ((row0 + r) * D + 4 * (m * CL + j)));
     }
   }
 
@@ -188,7 +192,7 @@ __device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
 // and written once.  Heads are taken in launch order: for this pure stream
 // the plain order spreads the concurrent workgroups' addresses over the HBM
 // channels better than grouping contiguous head ranges per XCD (measured).
-template <int DT, int GT, int D, int CL, int RPL, int NW>
+template <int DT, int GT, int D, int CL, int RPL, int NW, int SP>
 __global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
   static_assert((D / CL) % 4 == 0, "a lane owns whole float4 chunks");
   static_assert(NW * (kWave / CL) * RPL == D, "a workgroup owns the whole head");
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(StepArgs a) {
   const int64_t head = blockIdx.x;
   HeadRegs<DT, D, CL, RPL> R;
   decode_fetch<DT, GT, D, CL, RPL, NW>(a, head, R);
-  decode_finish<DT, GT, D, CL, RPL, NW>(a, head, R, red);
+  decode_finish<DT, GT, D, CL, RPL, NW, SP>(a, head, R, red);
 }
 
 // ---------------------------------------------------------------- three-pass form
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(NW* kWave) void threepass_kernel(StepArgs a) {
     rq *= rsqrtf(sqq + a.qk_eps);
   }
   float* y = a.y + head * D + row0;
-  float* so = a.s_out + head * (int64_t)(D * D);
+  const __amdgpu_buffer_rsrc_t ro = stream_rsrc(a.s_out + head * (int64_t)(D * D), D * D * 4);
   if constexpr (PASS == 1) {  // u = S.k^
     float u[RPL];
 #pragma unroll
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(NW* kWave) void threepass_kernel(StepArgs a) {
         s.y = fmaf(ck, kf.y, al * s.y);
         s.z = fmaf(ck, kf.z, al * s.z);
         s.w = fmaf(ck, kf.w, al * s.w);
-        nt_store4(s, so + (row0 + r) * D + 4 * (m * CL + j));
+        buf_store4<kStoreThrough>(s, ro, 4 * ((row0 + r) * D + 4 * (m * CL + j)));
       }
     }
   } else {  // o = S.q^ on the updated S, then the output
@@ -299,22 +303,34 @@ __global__ __launch_bounds__(NW* kWave) void threepass_kernel(StepArgs a) {
 
 }  // namespace
 
-template <int DT, int GT>
-int launch_step_dt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
+// State stores are written through at device scope from this much state on:
+// a step then reads and writes at least the 256 MB Infinity Cache's worth, so
+// nothing it leaves in the caches survives to the next step.
+constexpr int64_t kWriteThroughBytes = (int64_t)128 << 20;
+
+template <int DT, int GT, int SP>
+int launch_step_sp(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(d.B * d.Hv));
   switch (d.Dk) {
-    case 256: decode_kernel<DT, GT, 256, 16, 4, 16><<<grid, 16 * kWave, 0, st>>>(a); break;
+    case 256: decode_kernel<DT, GT, 256, 16, 4, 16, SP><<<grid, 16 * kWave, 0, st>>>(a); break;
     // 16 lanes per row (256-byte segments per load), 1024 threads: 49 VGPRs, so
     // 8 waves per SIMD hold two heads per CU and 2048 heads run in four even
     // rounds (8 lanes x 512 threads needed 80 VGPRs: three heads per CU and a
     // ragged last round; 46.6 against 45.3 us per step at B = 64)
-    case 128: decode_kernel<DT, GT, 128, 16, 2, 16><<<grid, 16 * kWave, 0, st>>>(a); break;
-    case 64: decode_kernel<DT, GT, 64, 4, 2, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
-    case 32: decode_kernel<DT, GT, 32, 4, 1, 2><<<grid, 2 * kWave, 0, st>>>(a); break;
-    case 16: decode_kernel<DT, GT, 16, 4, 1, 1><<<grid, 1 * kWave, 0, st>>>(a); break;
+    case 128: decode_kernel<DT, GT, 128, 16, 2, 16, SP><<<grid, 16 * kWave, 0, st>>>(a); break;
+    case 64: decode_kernel<DT, GT, 64, 4, 2, 2, SP><<<grid, 2 * kWave, 0, st>>>(a); break;
+    case 32: decode_kernel<DT, GT, 32, 4, 1, 2, SP><<<grid, 2 * kWave, 0, st>>>(a); break;
+    case 16: decode_kernel<DT, GT, 16, 4, 1, 1, SP><<<grid, 1 * kWave, 0, st>>>(a); break;
     default: set_error("unsupported head dim"); return GDN_EUNSUPPORTED;
   }
   return device_status("decode_kernel launch");
+}
+
+template <int DT, int GT>
+int launch_step_dt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
+  const int64_t state_bytes = d.B * d.Hv * d.Dv * d.Dk * (int64_t)sizeof(float);
+  return state_bytes >= kWriteThroughBytes ? launch_step_sp<DT, GT, kStoreThrough>(d, a, st)
+                                           : launch_step_sp<DT, GT, kStoreStream>(d, a, st);
 }
 
 template <int DT>
