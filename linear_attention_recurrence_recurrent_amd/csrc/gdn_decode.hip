@@ -19,7 +19,8 @@
 // issuing every load of a lane before any arithmetic, and applies the gated
 // RMSNorm in the same launch.  The state goes through buffer loads and
 // stores with streaming cache policies (stores written through at device
-// scope from kWriteThroughBytes of state on: stream_rsrc in gdn_device.h).
+// scope from kWriteThroughBytes of state on, with no hint up to
+// kCachedStoreBytes: stream_rsrc in gdn_device.h).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -305,8 +306,10 @@ __global__ __launch_bounds__(NW* kWave) void threepass_kernel(StepArgs a) {
 
 // State stores are written through at device scope from this much state on:
 // a step then reads and writes at least the 256 MB Infinity Cache's worth, so
-// nothing it leaves in the caches survives to the next step.
-constexpr int64_t kWriteThroughBytes = (int64_t)128 << 20;
+// nothing it leaves in the caches survives to the next step.  Up to
+// kCachedStoreBytes (half of the eight XCDs' 4 MB L2s) they carry no hint, so
+// the state stays in L2 for the next step; nontemporal in between.
+constexpr int64_t kWriteThroughBytes = (int64_t)128 << 20, kCachedStoreBytes = (int64_t)16 << 20;
 
 template <int DT, int GT, int SP>
 int launch_step_sp(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
@@ -329,8 +332,9 @@ int launch_step_sp(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
 template <int DT, int GT>
 int launch_step_dt(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
   const int64_t state_bytes = d.B * d.Hv * d.Dv * d.Dk * (int64_t)sizeof(float);
-  return state_bytes >= kWriteThroughBytes ? launch_step_sp<DT, GT, kStoreThrough>(d, a, st)
-                                           : launch_step_sp<DT, GT, kStoreStream>(d, a, st);
+  if (state_bytes >= kWriteThroughBytes) return launch_step_sp<DT, GT, kStoreThrough>(d, a, st);
+  if (state_bytes <= kCachedStoreBytes) return launch_step_sp<DT, GT, kStoreCached>(d, a, st);
+  return launch_step_sp<DT, GT, kStoreStream>(d, a, st);
 }
 
 template <int DT>

@@ -78,12 +78,13 @@ __device__ __forceinline__ void nt_store4(const float4 s, float* p) {
 // scope, so a store is written through to where every XCD sees it rather
 // than left dirty in this XCD's L2).  Loads take nt.  Stores take nt | sc1
 // (kStoreThrough) when a step's state traffic exceeds the caches anyway
-// (about 2% faster than nt alone at 128 MiB of state), and nt alone
+// (about 2% faster than nt alone at 128 MiB of state), nt alone
 // (kStoreStream) for smaller states, which the next step then finds in the
-// caches (up to 20% faster there).  A resource spans `bytes` from `base` (at
-// most 4 GiB); offsets are in bytes, and accesses outside the span read zeros
-// and write nothing.
-constexpr int kStreamLoad = 2, kStoreStream = 2, kStoreThrough = 2 | 16;
+// caches (up to 20% faster there), and no hint (kStoreCached) for states that
+// fit in half of the L2s, which then keep them.  A resource spans `bytes`
+// from `base` (at most 4 GiB); offsets are in bytes, and accesses outside the
+// span read zeros and write nothing.
+constexpr int kStreamLoad = 2, kStoreCached = 0, kStoreStream = 2, kStoreThrough = 2 | 16;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const float* base, uint32_t bytes) {
   // dword 3 = 0x00020000: 32-bit data format, the value raw buffers use on gfx9
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
