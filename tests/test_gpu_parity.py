@@ -464,6 +464,56 @@ def test_bitwise_deterministic():
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+DETERMINISM = [
+    # (name, B, T, Hk, Hv, D, dtype, head_major, exact)
+    ("prefill few-head bf16", 1, 4096, 16, 32, 128, "bf16", False, False),
+    ("prefill few-head bf16 exact", 1, 4096, 16, 32, 128, "bf16", False, True),
+    ("head-major many-head f16", 16, 1024, 16, 32, 128, "f16", True, False),
+    ("head-major many-head f16 exact", 16, 1024, 16, 32, 128, "f16", True, True),
+    ("few-head f16", 1, 1000, 16, 32, 128, "f16", False, False),
+    ("few-head f32", 1, 1000, 16, 32, 128, "f32", False, False),
+    ("D=32 few-head", 2, 999, 4, 8, 32, "bf16", False, False),
+    ("D=64 many-head", 8, 333, 16, 32, 64, "bf16", True, False),
+    ("D=256 few-head", 1, 500, 2, 4, 256, "bf16", False, False),
+]
+
+
+@pytest.mark.parametrize("case", DETERMINISM, ids=[c[0] for c in DETERMINISM])
+def test_bitwise_deterministic_at_size(case):
+    """Races (a missing barrier, an LDS slot read after its next write) show as
+    results that change from run to run: three runs of each kernel shape, over
+    hundreds of blocks, must agree bit for bit."""
+    name, B, T, Hk, Hv, D, dt, hm, exact = case
+    say("determinism: %s" % name)
+    ops = dev(synth.random_operands(B, T, Hk, Hv, D, D, dtype=dt, head_major=hm, seed=17))
+    runs = [scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"], ops["z"],
+                 ops["w"], head_major=hm, exact=exact) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y, st in runs[1:]:
+        assert torch.equal(y, runs[0][0]) and torch.equal(st, runs[0][1])
+
+
+def test_decode_bitwise_deterministic_across_store_regimes():
+    """The decode step at batches whose state takes each store policy (no hint
+    up to 16 MiB, nontemporal, written through from 128 MiB), three in-place
+    steps twice over, bit for bit."""
+    for B in (1, 16, 64):
+        say("decode determinism B=%d" % B)
+        ops = dev(synth.random_operands(B, 3, 16, 32, 128, 128, dtype="bf16", seed=B))
+        outs = []
+        for _ in range(2):
+            st = ops["s0"].clone()
+            ys = []
+            for t in range(3):
+                sl = {n: ops[n][:, t:t + 1].contiguous() for n in ("q", "k", "v", "z", "log_decay", "beta")}
+                y, _ = recurrent_step(sl["q"], sl["k"], sl["v"], sl["log_decay"], sl["beta"], st,
+                                      sl["z"], ops["w"], inplace=True)
+                ys.append(y)
+            torch.cuda.synchronize()
+            outs.append((torch.cat(ys, 1), st))
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_rejections_raise():
     ops = dev(synth.random_operands(1, 4, 2, 4, 64, 64, dtype="bf16", seed=1))
     with pytest.raises(GdnError, match="together"):
