@@ -83,16 +83,15 @@ typedef enum gdn_status {
 #define GDN_FOLD_QK_L2NORM 1u /* L2-normalise q and k inside the op */
 #define GDN_FOLD_Q_SCALE 2u   /* multiply q^ by 1/sqrt(Dk) inside the op */
 /* Form of gdn_scan's time loop.  The token-by-token form runs on the vector
- * units for every head dim; at Dk == Dv in {32, 64, 128}, and 256 with f16 or
- * bf16 q and k, the block form runs 16 tokens at a time as dense products on
- * the matrix cores (the step is affine in S,
+ * units for every head dim; at Dk == Dv in {32, 64, 128, 256} the block form
+ * runs 16 tokens at a time as dense products on the matrix cores (the step is affine in S,
  * "Module gdn" page, "The fusion").  Both give the same results up to
  * rounding.  With f16/bf16 q and k the block form multiplies the f32 state
  * (and its per-block correction) on the bf16 matrix cores through bf16 parts:
  * by default two parts rounded to nearest, each term then within 2^-16
  * relative of the f32 product; with GDN_SCAN_EXACT three exact parts, each
  * term an exact f32 product (f32 accuracy; up to 1.2x the time).
- * f32 q and k take f32 products either way.  The block form also needs
+ * f32 q and k take f32 products either way (at D == 256 too).  The block form also needs
  * Hk*Dk and Hv*Dv below 2^27 and T below 2^29 (its offsets inside a block are
  * 32-bit).  Without a form flag the block form runs where it fits and the
  * token-by-token form otherwise; with both form flags, or GDN_SCAN_BLOCK

@@ -176,9 +176,9 @@ def scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Ten
     float32 [B, Hv, D, D] (None: zeros); w: [D].  y is float32 in v's layout;
     final_state is float32 [B, Hv, D, D] (``state_out`` may be ``s0`` for an
     in-place update).  ``form`` picks the time loop: "per_token" (vector units,
-    any D), "block" (16 tokens at a time on the matrix cores; D of 32, 64 or
-    128, or 256 with 16-bit q and k), or None for the library's choice for the
-    shape (the block form wherever it runs, for T of 2 or more).  ``exact`` makes the block
+    any D), "block" (16 tokens at a time on the matrix cores; D of 32, 64, 128
+    or 256), or None for the library's choice for the shape (the block form
+    wherever it runs, for T of 2 or more).  ``exact`` makes the block
     form's products with the f32 state exact f32 products for 16-bit q and k
     (three bf16 parts of the state instead of two rounded ones, whose terms
     are within 2^-16 relative).  The block form's workspace

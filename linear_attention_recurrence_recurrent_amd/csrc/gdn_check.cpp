@@ -88,7 +88,7 @@ int check_desc(const gdn_desc* d) {
     return fail(GDN_EUNSUPPORTED,
                 block_head_dims_fit(*d)
                     ? "the block form needs Hk*Dk and Hv*Dv below 2^27 and T below 2^29"
-                    : "the block form needs Dk == Dv in {32, 64, 128}, or 256 with 16-bit q and k");
+                    : "the block form needs Dk == Dv in {32, 64, 128, 256}");
 
   // sizes (with overflow checks)
   int64_t bt, nqk, nv, ng, ns, tmp;
@@ -103,8 +103,7 @@ int check_desc(const gdn_desc* d) {
 }
 
 bool block_head_dims_fit(const gdn_desc& d) {
-  return d.Dv == d.Dk && (d.Dk == 32 || d.Dk == 64 || d.Dk == 128 ||
-                          (d.Dk == 256 && d.dtype != GDN_F32));
+  return d.Dv == d.Dk && (d.Dk == 32 || d.Dk == 64 || d.Dk == 128 || d.Dk == 256);
 }
 
 // The block-form kernels address the rows of a 16-token block from the

@@ -1,6 +1,5 @@
 // Time-axis scan of the Gated DeltaNet recurrence in block form on the matrix
-// cores (gfx950 MFMA, FP32 in and out), for D = 32, 64 and 128, and 256 with
-// 16-bit q and k.
+// cores (gfx950 MFMA, FP32 in and out), for D = 32, 64, 128 and 256.
 //
 // The recurrence is the one of the "Module gdn" page (module description).
 // Its section "The fusion" observes that the step is affine in the memory S;
@@ -220,12 +219,12 @@ template <int DT, int GT, int D, bool XB, bool TP>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   static_assert(XB || !TP, "the parts layout is the few-head kernel's");
   // a lane holds D / 4 elements of a row: NU loads of 8, taken in NCH chunks
-  // of NUC (more than 32 elements per lane would not fit beside the
-  // cross-block products: those rows are loaded and their products
-  // accumulated a chunk at a time)
-  constexpr int NU = D / 32, NUC = NU < 4 ? NU : 4, NCH = NU / NUC;
+  // of NUC (more than 32 elements per lane, 16 for f32 rows at D = 256, would
+  // not fit beside the cross-block products: those rows are loaded and their
+  // products accumulated a chunk at a time)
+  constexpr int NU = D / 32, NUC = DT == GDN_F32 && D > 128 ? 2 : (NU < 4 ? NU : 4), NCH = NU / NUC;
   static_assert(NU >= 1 && D % 32 == 0, "head dim a multiple of 32");
-  static_assert(NCH == 1 || (DT != GDN_F32 && XB), "chunked rows: 16-bit inputs, few heads");
+  static_assert(NCH == 1 || XB, "chunked rows: few heads (D = 256)");
   __shared__ float sLs[4][4][kL][kL + 1];  // [wave][value head of the group][i][j]
   __shared__ __align__(16) float sAB[4][2][4][kL];  // [wave][alpha, beta][value head][token]
   // the wave index through readfirstlane: everything derived from the task
@@ -298,9 +297,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
   };
   gates_load(0);
-  // squared norms of row lc (16-bit inputs: below, from the products)
+  // squared norms of row lc (16-bit inputs: below, from the products; f32
+  // ones chunk by chunk, summed over the lane groups at the end)
   float ssk = 0.f, ssq = 0.f;
-  if constexpr (DT == GDN_F32) {
+  [[maybe_unused]] auto norms = [&]() {
 #pragma unroll
     for (int u = 0; u < NUC; ++u)
 #pragma unroll
@@ -308,11 +308,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         ssk = fmaf(kr[u].get(e), kr[u].get(e), ssk);
         ssq = fmaf(qr[u].get(e), qr[u].get(e), ssq);
       }
-    ssk += __shfl_xor(ssk, 16);
-    ssk += __shfl_xor(ssk, 32);
-    ssq += __shfl_xor(ssq, 16);
-    ssq += __shfl_xor(ssq, 32);
-  }
+  };
+  if constexpr (DT == GDN_F32) norms();
 
   // X Y^T of 16 raw rows each on the matrix cores; lane (lg, lc), register
   // r: entry [4 lg + r][lc].  The contraction runs over the lane's own D / 4
@@ -338,7 +335,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   [[maybe_unused]] v4f Q4c = zero, M1c = zero, M2c = zero, N1c = zero;
   v4f G4 = gram(kr, kr, zero), H4 = gram(qr, kr, zero);
   if constexpr (NCH > 1) {
-    Q4c = gram(qr, qr, zero);
+    if constexpr (DT != GDN_F32) Q4c = gram(qr, qr, zero);  // (f32: the norms come from the rows)
     M1c = gram(kr, kp1, zero);
     N1c = gram(qr, kp1, zero);
     M2c = gram(kr, kp2, zero);
@@ -346,15 +343,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     for (int ch = 1; ch < NCH; ++ch) {
       load_rows(ch);
       load_prev(ch);
+      if constexpr (DT == GDN_F32) norms();
       G4 = gram(kr, kr, G4);
       H4 = gram(qr, kr, H4);
-      Q4c = gram(qr, qr, Q4c);
+      if constexpr (DT != GDN_F32) Q4c = gram(qr, qr, Q4c);
       M1c = gram(kr, kp1, M1c);
       N1c = gram(qr, kp1, N1c);
       M2c = gram(kr, kp2, M2c);
     }
   }
-  if constexpr (DT != GDN_F32) {
+  if constexpr (DT == GDN_F32) {
+    ssk += __shfl_xor(ssk, 16);
+    ssk += __shfl_xor(ssk, 32);
+    ssq += __shfl_xor(ssq, 16);
+    ssq += __shfl_xor(ssq, 32);
+  } else {
     // 16-bit inputs: the squared norms are the diagonals of K K^T (above) and
     // Q Q^T (one more product on the otherwise idle matrix cores instead of
     // 64 widening multiply-adds per lane): entry [lc][lc] sits in register
@@ -918,9 +921,12 @@ constexpr int lds_row() {  // padded row, elements: rows 4 banks apart
   return DT == GDN_F32 ? D + 4 : D + 8;
 }
 
-// Threads of the few-head kernel: D / 32 state waves of 32 keys, then the
-// chain, O and two staging waves.
-constexpr int rows_la_threads(int D) { return (D / 32 + 4) * kWave; }
+// State waves of the few-head kernel: D / 32 of 32 keys each.  Threads: the
+// state waves, then the chain, O and two staging waves.
+template <int DT, int D>
+constexpr int rows_nc() { return D / 32; }
+template <int DT, int D>
+constexpr int rows_la_threads() { return (rows_nc<DT, D>() + 4) * kWave; }
 
 // The sum of the state waves' partial products, pairwise
 template <int N>
@@ -979,16 +985,17 @@ __device__ __forceinline__ float lds_get(const LdsElem<DT>* row, int e) {
 // round finishes the state and O.  Each role runs its own loop with the same
 // barriers.
 template <int DT, int NSP, int D>
-__global__ __launch_bounds__(rows_la_threads(D)) __attribute__((amdgpu_waves_per_eu(2))) void
+__global__ __launch_bounds__((rows_la_threads<DT, D>())) __attribute__((amdgpu_waves_per_eu(2))) void
 rows_la_kernel(StateArgs a) {
   static_assert(NSP == 2 || NSP == 3, "two or three parts of the state and Cs");
-  static_assert(D % 32 == 0 && D <= (DT == GDN_F32 ? 128 : 256), "head dim 32 to 128 (256: 16-bit)");
+  static_assert(D % 32 == 0 && D <= 256, "head dim 32 to 256");
   // NC state waves of two 16-key tiles each
-  constexpr int NC = D / 32, NCT = 2, ROWS = 16, KP = lds_row<DT, D>(), NM = 3 * kL * kL;
+  constexpr int NC = rows_nc<DT, D>(), NCT = 2, ROWS = 16, KP = lds_row<DT, D>(), NM = 3 * kL * kL;
   typedef LdsElem<DT> KT;
-  // f32 q and k rows staged in LDS (16-bit inputs: the state waves load their own;
-  // at D = 256 their unused slots shrink to a token)
-  constexpr int SKS = DT == GDN_F32 || D <= 128 ? 4 : 1, SKP = DT == GDN_F32 || D <= 128 ? KP : 8;
+  // f32 q and k rows staged in LDS up to D = 128 (16-bit inputs, and f32 ones
+  // at D = 256, whose rows would take 133 KB: the state waves load their own;
+  // at D = 256 the unused slots shrink to a token)
+  constexpr int SKS = D <= 128 ? 4 : 1, SKP = D <= 128 ? KP : 8;
   __shared__ __align__(16) KT sk[SKS][kL][SKP];
   __shared__ __align__(16) KT sq[SKS][kL][SKP];
   __shared__ __align__(16) float sv[4][kL][ROWS];
@@ -1234,7 +1241,132 @@ rows_la_kernel(StateArgs a) {
       return;
     }
   }
-  if constexpr (DT == GDN_F32) if (wave < NC) {
+  if constexpr (DT == GDN_F32 && D > 128) if (wave < NC) {
+    // ---- state waves, f32 inputs at D = 256: the products of the branch
+    // below (f32 16x16x4), two key tiles of the 16 rows per wave, with q and
+    // k loaded by the wave itself from global memory, two blocks ahead in a
+    // ring of two register sets (LDS would need 133 KB for the f32 rows, and
+    // three waves per SIMD leave no registers for a deeper ring);
+    // K^T for the update is formed from the loaded rows on the matrix cores:
+    // four products per tile against slices of the identity (X E exactly;
+    // lane (lg, lc) then holds X[4 lg + r][lc]).
+    constexpr int NT4 = D / (16 * NC);
+    v4f St[NT4];
+    const int arow = row0 + lc;
+    auto key0 = [&](int ct) { return 16 * (cp * NT4 + ct) + 4 * lg; };
+#pragma unroll
+    for (int ct = 0; ct < NT4; ++ct) {
+      const float4 x = *reinterpret_cast<const float4*>(a.s0 + sbase + (int64_t)arow * D + key0(ct));
+      St[ct] = v4f{x.x, x.y, x.z, x.w};
+    }
+    // q and k of a block: row lc, keys key0(ct) .. + 3 (rows past the last
+    // token repeat it)
+    struct Blk {
+      float4 q[NT4], k[NT4];
+    };
+    auto ld = [&](Blk& x, int64_t c) {
+      const int tcc = c == nblk - 1 ? tcl : kL;
+      const int64_t o = bs.qk + (c * kL + (lc < tcc ? lc : tcc - 1)) * bs.qk_ts;
+#pragma unroll
+      for (int ct = 0; ct < NT4; ++ct) {
+        x.q[ct] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + o + key0(ct));
+        x.k[ct] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + o + key0(ct));
+      }
+    };
+    // the next loads of a set stay below its last use (see the 16-bit branch)
+    auto reload = [&](Blk& x, int64_t c) {
+      __builtin_amdgcn_sched_barrier(0);
+      int64_t cn = clampb(c);
+      asm volatile("" : "+s"(cn) : : "memory");
+      ld(x, cn);
+    };
+    // X S^T over the wave's key tiles: two chains of dependent products
+    auto xst = [&](const float4* f) {
+      v4f p[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ct = 0; ct < NT4; ++ct) {
+        v4f& acc = p[ct & 1];
+        acc = mfma4(f[ct].x, St[ct][0], acc);
+        acc = mfma4(f[ct].y, St[ct][1], acc);
+        acc = mfma4(f[ct].z, St[ct][2], acc);
+        acc = mfma4(f[ct].w, St[ct][3], acc);
+      }
+      return p[0] + p[1];
+    };
+    // E_e[kk][j] = (4 kk + e == j): lane (lg, lc) holds E_e[lg][lc]
+    float eye[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) eye[e] = 4 * lg + e == lc ? 1.f : 0.f;
+    struct Ops {
+      float kt[NT4][4];
+      float gl;
+    };
+    auto transpose = [&](const float4* f, Ops& o) {
+#pragma unroll
+      for (int ct = 0; ct < NT4; ++ct) {
+        v4f d = {0.f, 0.f, 0.f, 0.f};
+        d = mfma4(f[ct].x, eye[0], d);
+        d = mfma4(f[ct].y, eye[1], d);
+        d = mfma4(f[ct].z, eye[2], d);
+        d = mfma4(f[ct].w, eye[3], d);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o.kt[ct][r] = d[r];
+      }
+    };
+    // S_r = gam(r-1) S_(r-1) + K_(r-1)^T Cs_(r-1)
+    auto update = [&](const v4f& cs, const Ops& o) {
+#pragma unroll
+      for (int ct = 0; ct < NT4; ++ct) {
+        v4f acc = St[ct] * o.gl;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(o.kt[ct][s2], cs[s2], acc);
+        St[ct] = acc;
+      }
+    };
+    // round r >= 1: bq holds block r, bk block r + 1; cur holds round r's
+    // update operands and then takes K_(r+1)^T for round r + 2, nxt takes
+    // gam(r); bq then takes the loads of block r + 2
+    auto round = [&](int64_t r, Ops& cur, Ops& nxt, Blk& bq, const Blk& bk) {
+      __syncthreads();
+      const v4f cs = scs[(r - 1) & 1][lane];
+      nxt.gl = srec[r & 3][kRecGl];
+      sp[r & 1][cp][lane] = xst(bq.q);
+      sb[(r + 1) & 1][cp][lane] = xst(bk.k);
+      update(cs, cur);
+      transpose(bk.k, cur);
+      reload(bq, r + 2);
+    };
+    Ops o0, o1;
+    Blk b0, b1;
+    ld(b0, 0);
+    ld(b1, clampb(1));
+    __syncthreads();  // blocks 0 and 1 staged
+    sb[0][cp][lane] = xst(b0.k);  // A_0
+    transpose(b0.k, o1);           // K_0^T for round 1
+    __syncthreads();
+    // round 0: P_0 and B_1 from S_0, no update
+    o1.gl = srec[0][kRecGl];
+    sp[0][cp][lane] = xst(b0.q);
+    sb[1][cp][lane] = xst(b1.k);
+    transpose(b1.k, o0);  // K_1^T for round 2
+    reload(b0, 2);
+    // rounds in pairs (two register sets, two operand sets), then one more
+    const int64_t npair = (nblk - 1) / 2;
+    for (int64_t p = 0; p < npair; ++p) {
+      round(2 * p + 1, o1, o0, b1, b0);
+      round(2 * p + 2, o0, o1, b0, b1);
+    }
+    if ((nblk - 1) & 1) round(nblk - 1, o1, o0, b1, b0);
+    __syncthreads();
+    update(scs[(nblk - 1) & 1][lane], ((nblk - 1) & 1) ? o0 : o1);
+#pragma unroll
+    for (int ct = 0; ct < NT4; ++ct) {
+      float4 x = make_float4(St[ct][0], St[ct][1], St[ct][2], St[ct][3]);
+      *reinterpret_cast<float4*>(a.s_out + sbase + (int64_t)arow * D + key0(ct)) = x;
+    }
+    return;
+  }
+  if constexpr (DT == GDN_F32 && D <= 128) if (wave < NC) {
     // ---- state waves, f32 inputs: two key tiles of the 16 rows,
     // accumulator layout
     v4f St[NCT];
@@ -1519,7 +1651,7 @@ rows_la_kernel(StateArgs a) {
   // inputs: the state waves load their own); two v values; two float4 of the
   // record and of M1 M2 N.
   constexpr int NR4 = kRecUsed / 4, NM4 = NM / 4;
-  constexpr bool QK = DT == GDN_F32;
+  constexpr bool QK = DT == GDN_F32 && D <= 128;
   struct Regs {
     Raw<DT, 8> k[2], q[2];
     Raw<DT, 2> v;
@@ -1582,7 +1714,7 @@ rows_la_kernel(StateArgs a) {
     if (QKALL || st < kL * CPR) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        if constexpr (DT == GDN_F32) {
+        if constexpr (DT == GDN_F32 && QK) {
           *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h]) = P.k[h].get4(0);
           *reinterpret_cast<float4*>(&sk[sl][qtt][qc + 8 * h + 4]) = P.k[h].get4(1);
           *reinterpret_cast<float4*>(&sq[sl][qtt][qc + 8 * h]) = P.q[h].get4(0);
@@ -1709,7 +1841,7 @@ int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t 
     }
   }
   r.nrb = D / 16;
-  rows_la_kernel<DT, NSP, D><<<dim3((unsigned)(heads * r.nrb)), rows_la_threads(D), 0, st>>>(r);
+  rows_la_kernel<DT, NSP, D><<<dim3((unsigned)(heads * r.nrb)), rows_la_threads<DT, D>(), 0, st>>>(r);
   return device_status("rows_la_kernel launch");
 }
 
@@ -1719,10 +1851,7 @@ int launch_d(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t h
   switch (d.Dk) {
     case 32: return launch_dt<DT, NSP, 32>(d, p, s, heads, st);
     case 64: return launch_dt<DT, NSP, 64>(d, p, s, heads, st);
-    case 256:
-      if constexpr (DT != GDN_F32) return launch_dt<DT, NSP, 256>(d, p, s, heads, st);
-      set_error("the block form at D = 256 needs 16-bit q and k");
-      return GDN_EUNSUPPORTED;
+    case 256: return launch_dt<DT, NSP, 256>(d, p, s, heads, st);
     default: return launch_dt<DT, NSP, 128>(d, p, s, heads, st);
   }
 }

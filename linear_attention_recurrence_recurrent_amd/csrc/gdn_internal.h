@@ -15,8 +15,7 @@ constexpr int64_t kKeyCrossBytes = 3 * 16 * 16 * 4;
 constexpr int64_t kManyHeads = 256;
 constexpr uintptr_t kWorkspaceAlign = 256;
 
-// Whether the block form covers the head dim (Dk == Dv in {32, 64, 128}, or
-// 256 with 16-bit q and k).
+// Whether the block form covers the head dim (Dk == Dv in {32, 64, 128, 256}).
 bool block_head_dims_fit(const gdn_desc& d);
 // ... and the shape: Hk*Dk and Hv*Dv below 2^27 and T below 2^29, which keep
 // the kernels' 32-bit offsets inside a 16-token block in range.

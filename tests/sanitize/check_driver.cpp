@@ -101,11 +101,11 @@ int main() {
     e.qk_eps = -1.0f;
     expect(run(&e, p, kWs), GDN_EINVAL, "eps");
     e = good();
-    e.Dk = e.Dv = 256;
+    e.Dk = e.Dv = 16;
     e.dtype = e.gate_dtype = GDN_F32;
     expect(run(&e, p, 0), GDN_OK, "per-token form needs no workspace");
     e.flags = 3 | GDN_SCAN_BLOCK;
-    expect(run(&e, p, kWs), GDN_EUNSUPPORTED, "block form at D = 256 with f32 q and k");
+    expect(run(&e, p, kWs), GDN_EUNSUPPORTED, "block form at D = 16");
     e = good();
     e.T = 0;
     expect(run(&e, p, 0), GDN_OK, "empty time axis");

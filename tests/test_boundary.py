@@ -94,7 +94,7 @@ def test_accepts_valid_arguments():
     ops["s_out"] = ops["s0"]  # exact in-place alias is allowed
     assert check(_good(), **ops)[0] == 0
     assert check(_good(head_major=1, dtype=0, gate_dtype=0, flags=0), **ops)[0] == 0
-    assert check(_good(Dk=256, Dv=256, dtype=0, gate_dtype=0), **_ops())[0] == 0  # f32: per token
+    assert check(_good(Dk=16, Dv=16, dtype=0, gate_dtype=0), **_ops())[0] == 0  # D=16: per token
     # D = 32, 64, 128 and (16-bit q and k) 256 run the block form, which needs its workspace
     for D in (32, 64, 128, 256):
         rc, why = check(_good(Dk=D, Dv=D), **_ops())
@@ -133,13 +133,14 @@ def test_rejects_bad_descriptor(field, value, status, needle):
 def test_rejects_unsupported_head_dim():
     rc, why = check(_good(Dk=512, Dv=512), **_ops())
     assert rc == 5 and "head dim" in why
-    # the block form covers 32, 64, 128, and 256 with 16-bit q and k
-    for D, dt in ((16, 2), (16, 0), (256, 0)):
+    # the block form covers 32, 64, 128 and 256, every dtype
+    for D, dt in ((16, 2), (16, 0)):
         rc, why = check(_good(Dk=D, Dv=D, dtype=dt, gate_dtype=dt, flags=3 | 8), **_ops())
         assert rc == 5 and "block form" in why
     for D in (32, 64, 128, 256):
-        assert check(_good(Dk=D, Dv=D, flags=3 | 8), **_ops(), workspace=BASE + 20 * (1 << 28),
-                     workspace_bytes=1 << 20)[0] == 0
+        for dt in (0, 1, 2):
+            assert check(_good(Dk=D, Dv=D, dtype=dt, gate_dtype=dt, flags=3 | 8), **_ops(),
+                         workspace=BASE + 20 * (1 << 28), workspace_bytes=1 << 20)[0] == 0
     rc, why = check(_good(Dk=8, Dv=8), **_ops())
     assert rc == 5
 
@@ -257,7 +258,8 @@ def test_workspace_size_query():
     assert _ws_size(B=2, T=17, Hk=2, Hv=4, **D) == (0, 8 * 2 * 2560 + 4 * 2 * 3072)
     assert _ws_size(B=8, T=16, Hk=8, Hv=32, **D) == (0, 256 * 1 * 2560)  # 256 heads: no keys
     assert _ws_size(B=2, T=4096, Hk=2, Hv=4, Dk=16, Dv=16) == (0, 0)     # per-token form
-    assert _ws_size(B=2, T=64, Hk=2, Hv=4, Dk=256, Dv=256, dtype=0) == (0, 0)  # f32 at 256
+    assert _ws_size(B=2, T=64, Hk=2, Hv=4, Dk=256, Dv=256, dtype=0) == (
+        0, 8 * 4 * 2560 + 4 * 4 * 3072)  # f32 at 256 too
     # D = 256 runs the few-head kernel at any head count: key products for 512 heads too
     assert _ws_size(B=16, T=32, Hk=16, Hv=32, Dk=256, Dv=256) == (0, 512 * 2 * 2560 + 256 * 2 * 3072)
     for Dh in (32, 64):  # the records do not depend on the head dim

@@ -14,8 +14,8 @@ oracle:
 Each case runs at head dim 128 on both block-form kernels (fewer than 256
 value heads: the kernel with a workgroup per 16 state rows; 256 and more: a
 workgroup per head) in both layouts and all three operand dtypes, at head dims
-32 and 64 with float32 and bfloat16 operands, and at 256 with float16 and
-bfloat16 (where both head counts take the kernel with a workgroup per 16 rows);
+32 and 64 with float32 and bfloat16 operands, and at 256 with all three (where
+both head counts take the kernel with a workgroup per 16 rows);
 each is also compared with the float64 oracle at the usual bar.  The closed
 forms are evaluated in float64 from the exact operand values.
 """
@@ -106,7 +106,7 @@ def _close(got, ref, tol, what):
 CASES = ([(kind, dt, hm, 128) for kind in SHAPES for dt in ("f32", "bf16", "f16")
           for hm in (False, True)]
          + [(kind, dt, False, d) for d in (32, 64) for kind in SHAPES for dt in ("f32", "bf16")]
-         + [(kind, dt, False, 256) for kind in SHAPES for dt in ("bf16", "f16")])
+         + [(kind, dt, False, 256) for kind in SHAPES for dt in ("f32", "bf16", "f16")])
 IDS = ["%s-%s-%s-d%d" % (c[0], c[1], "hm" if c[2] else "tm", c[3]) for c in CASES]
 
 

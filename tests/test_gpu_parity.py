@@ -215,18 +215,19 @@ def test_block_form_edge_shapes(case, gated):
 
 HEAD_DIMS = [
     # (B, T, Hk, Hv, D): a workgroup per 16 value rows (few heads) or per head (256 heads;
-    # at D = 256 a workgroup per 16 rows at any head count)
+    # at D = 256 a workgroup per 16 rows at any head count; D = 16: the per-token form)
     (1, 45, 2, 4, 64),
     (8, 45, 16, 32, 64),
     (2, 45, 1, 3, 32),
     (8, 45, 16, 32, 32),
     (1, 45, 2, 4, 256),
     (8, 21, 16, 32, 256),
+    (1, 20, 1, 2, 16),
 ]
 
 
 def block_fits(D, dtype):
-    return D in (32, 64, 128) or (D == 256 and dtype != "f32")
+    return D in (32, 64, 128, 256)
 
 
 @pytest.mark.parametrize("shape", HEAD_DIMS, ids=lambda c: "B%dT%dHk%dHv%dD%d" % c)
@@ -234,10 +235,10 @@ def block_fits(D, dtype):
 @pytest.mark.parametrize("hm", [False, True], ids=["tm", "hm"])
 @pytest.mark.parametrize("gated", [True, False])
 def test_block_form_head_dims(shape, dtype, hm, gated):
-    """The block form at D = 32, 64 and (16-bit) 256 on its kernels, ragged
-    blocks, against the oracle; the default form there is the block form, bit
-    for bit.  f32 at D = 256 takes the token-by-token form, and asking for the
-    block form there is rejected."""
+    """The block form at D = 32, 64 and 256 on its kernels, ragged blocks,
+    against the oracle; the default form there is the block form, bit for bit
+    (D = 16 takes the token-by-token form, and asking for the block form there
+    is rejected)."""
     B, T, Hk, Hv, D = shape
     if not block_fits(D, dtype):
         ops = dev(synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, head_major=hm, seed=1))
