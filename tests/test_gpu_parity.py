@@ -476,6 +476,7 @@ DETERMINISM = [
     ("D=32 few-head", 2, 999, 4, 8, 32, "bf16", False, False),
     ("D=64 many-head", 8, 333, 16, 32, 64, "bf16", True, False),
     ("D=256 few-head", 1, 500, 2, 4, 256, "bf16", False, False),
+    ("D=256 few-head f32", 1, 500, 2, 4, 256, "f32", True, False),
 ]
 
 
