@@ -457,50 +457,58 @@ HEAD_DIM_SHAPES = [
     ("prefill_b1_t4096_bf16", 1, 4096, 16, 32, "bf16", False),
     ("head_major_b16_t1024_f16", 16, 1024, 16, 32, "f16", True),
 ]
+# and with f32 operands at head dim 256 (the block form's f32 path with q and k from global memory)
+F32_256_SHAPES = [
+    ("prefill_b1_t4096_f32", 1, 4096, 16, 32, "f32", False),
+    ("head_major_b16_t1024_f32", 16, 1024, 16, 32, "f32", True),
+]
+DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 
 
 def bench_head_dims(args, torch):
     """Both time loops of the scan at head dims 32, 64 and 256 on the shapes of
-    the two scan workloads (synthetic operands, the workloads' recipe)."""
+    the two scan workloads (synthetic operands, the workloads' recipe), and at
+    256 with f32 operands too."""
     import linear_attention_recurrence_recurrent_amd as gdn
     from linear_attention_recurrence_recurrent_amd import synth
     dev = torch.device("cuda:0")
     out = []
-    for D in (32, 64, 256):
-        for name, B, T, Hk, Hv, dt, hm in HEAD_DIM_SHAPES:
-            ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dt, head_major=hm, seed=D)
-            d = {n: t.to(dev) for n, t in ops.items()}
-            y = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
-            s_out = torch.empty_like(d["s0"])
-            row = {"shape": name, "D": D, "dtype": dt}
-            flops = 7.0 * B * T * Hv * D * D
-            for form in ("per_token", "block"):
-                desc = gdn._desc(B, T, Hk, Hv, D, D, hm, 1 if dt == "f16" else 2,
-                                 1 if dt == "f16" else 2, True, True, 1e-6, 1e-6, form, False)
-                ws = torch.empty(max(gdn.scan_workspace_bytes(desc), 1), dtype=torch.uint8,
-                                 device=dev)
+    cases = [(D, sh) for D in (32, 64, 256) for sh in HEAD_DIM_SHAPES]
+    cases += [(256, sh) for sh in F32_256_SHAPES]
+    for D, (name, B, T, Hk, Hv, dt, hm) in cases:
+        ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dt, head_major=hm, seed=D)
+        d = {n: t.to(dev) for n, t in ops.items()}
+        y = torch.empty(d["v"].shape, dtype=torch.float32, device=dev)
+        s_out = torch.empty_like(d["s0"])
+        row = {"shape": name, "D": D, "dtype": dt}
+        flops = 7.0 * B * T * Hv * D * D
+        for form in ("per_token", "block"):
+            desc = gdn._desc(B, T, Hk, Hv, D, D, hm, DT_CODE[dt], DT_CODE[dt], True, True,
+                             1e-6, 1e-6, form, False)
+            ws = torch.empty(max(gdn.scan_workspace_bytes(desc), 1), dtype=torch.uint8,
+                             device=dev)
 
-                def call():
-                    gdn.scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"],
-                             d["w"], head_major=hm, form=form, out=y, state_out=s_out,
-                             workspace=ws)
-                for _ in range(max(1, args.warmup)):
-                    call()
-                settle(call, torch, args.settle_ms)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = max(3, args.steps)
-                e0.record()
-                for _ in range(reps):
-                    call()
-                e1.record()
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / reps * 1e3
-                row[form] = {"us_per_call": round(us, 1),
-                             "frac_of_fp32_vector_peak": round(flops / us / 1e6 / FP32_PEAK_TFLOPS, 4)}
-                log("D=%d %s %s: %.1f us" % (D, name, form, us))
-            row["speedup"] = round(row["per_token"]["us_per_call"] / row["block"]["us_per_call"], 2)
-            out.append(row)
-            del d, y, s_out
+            def call():
+                gdn.scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"],
+                         d["w"], head_major=hm, form=form, out=y, state_out=s_out,
+                         workspace=ws)
+            for _ in range(max(1, args.warmup)):
+                call()
+            settle(call, torch, args.settle_ms)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(3, args.steps)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            row[form] = {"us_per_call": round(us, 1),
+                         "frac_of_fp32_vector_peak": round(flops / us / 1e6 / FP32_PEAK_TFLOPS, 4)}
+            log("D=%d %s %s: %.1f us" % (D, name, form, us))
+        row["speedup"] = round(row["per_token"]["us_per_call"] / row["block"]["us_per_call"], 2)
+        out.append(row)
+        del d, y, s_out
     return out
 
 
@@ -722,7 +730,8 @@ def main():
     ap.add_argument("--scan-only", action="store_true",
                     help="only the two scan workloads (for counter collection); partial JSON")
     ap.add_argument("--head-dims", action="store_true",
-                    help="only both scan forms at head dims 32, 64 and 256 on the scan shapes")
+                    help="only both scan forms at head dims 32, 64 and 256 on the scan shapes "
+                         "(and f32 operands at 256)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this size (counter reference)")
     ap.add_argument("--trace-summary", metavar="CSV",
