@@ -5,7 +5,7 @@ float32 operands and 3e-3 for float16/bfloat16 operands (float32 state in both
 cases), applied to y AND the final state.  Small cases are compared in full,
 and so are the full-size workloads: the oracle computes every batch entry and
 value head of them in seconds.  The block form is also compared at head dims 32,
-64 and 256 (the last with 16-bit q and k only).
+64 and 256, with every operand dtype.
 """
 import math
 import sys
