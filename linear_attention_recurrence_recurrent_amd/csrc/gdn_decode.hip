@@ -42,7 +42,7 @@ struct HeadRegs {
   static constexpr int NV4 = D / CL / 4;
   Raw<DT, 4> k[NV4], q[NV4];
   float4 S[RPL][NV4];
-  Raw<DT, RPL> v, z;
+  Raw<DT, RPL> v, z, w;  // z and the norm weight w only for the gated output
   float ld, be;
 };
 
@@ -81,7 +81,10 @@ __device__ __forceinline__ void decode_fetch(const StepArgs& a, int64_t head,
       R.S[r][m] = buf_load4<kStreamLoad>(rs, 4 * ((row0 + r) * D + 4 * (m * CL + j)));
   }
   R.v.load(a.v, head * D + row0);
-  if (a.z) R.z.load(a.z, head * D + row0);
+  if (a.z) {
+    R.z.load(a.z, head * D + row0);
+    R.w.load(a.w, row0);  // in flight with the state, not after the norm's barrier
+  }
 }
 
 // Fold the norms, run the fused row pass, write the state back and the
@@ -172,10 +175,8 @@ __device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
 #pragma unroll
     for (int i = 0; i < NW; ++i) tot += red[i];
     const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
-    Raw<DT, RPL> wr;
-    wr.load(a.w, row0);
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) o[r] *= inv * wr.get(r);
+    for (int r = 0; r < RPL; ++r) o[r] *= inv * R.w.get(r);
   }
   if (j == 0) {
     if constexpr (RPL == 4) {
