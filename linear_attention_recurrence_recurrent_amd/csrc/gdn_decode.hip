@@ -42,7 +42,8 @@ struct HeadRegs {
   static constexpr int NV4 = D / CL / 4;
   Raw<DT, 4> k[NV4], q[NV4];
   float4 S[RPL][NV4];
-  Raw<DT, RPL> v, z, w;  // z and the norm weight w only for the gated output
+  Raw<DT, RPL> v, z;  // z and the norm weight w only for the gated output
+  float w[RPL];
   float ld, be;
 };
 
@@ -83,7 +84,10 @@ __device__ __forceinline__ void decode_fetch(const StepArgs& a, int64_t head,
   R.v.load(a.v, head * D + row0);
   if (a.z) {
     R.z.load(a.z, head * D + row0);
-    R.w.load(a.w, row0);  // in flight with the state, not after the norm's barrier
+    // w in flight with the state, not after the norm's barrier; it is aligned
+    // to its element size only, so one element per load
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) R.w[r] = ld1<DT>(a.w, row0 + r);
   }
 }
 
@@ -176,7 +180,7 @@ __device__ __forceinline__ void decode_finish(const StepArgs& a, int64_t head,
     for (int i = 0; i < NW; ++i) tot += red[i];
     const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) o[r] *= inv * R.w.get(r);
+    for (int r = 0; r < RPL; ++r) o[r] *= inv * R.w[r];
   }
   if (j == 0) {
     if constexpr (RPL == 4) {
@@ -291,10 +295,8 @@ __global__ __launch_bounds__(NW* kWave) void threepass_kernel(StepArgs a) {
 #pragma unroll
       for (int i = 0; i < NW; ++i) tot += red[i];
       const float inv = rsqrtf(tot * (1.0f / D) + a.norm_eps);
-      Raw<DT, RPL> wr;
-      wr.load(a.w, row0);
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) o[r] *= inv * wr.get(r);
+      for (int r = 0; r < RPL; ++r) o[r] *= inv * R.w[r];  // fetched with the operands
     }
     if (j == 0) {
 #pragma unroll

@@ -497,58 +497,63 @@ __attribute__((amdgpu_waves_per_eu(FUSE_NORM ? 2 : 1))) void scan_kernel(ScanArg
 
 // ------------------------------------------------------------------ gated RMSNorm
 // In place over y viewed as [nvec, D] (both layouts keep the head dim last and
-// dense, and z shares y's layout); a wave per kNormVPW head vectors.
-constexpr int kNormVPW = 8;
+// dense, and z shares y's layout).  A lane owns four consecutive elements of a
+// vector (16-byte loads and stores of y), D/4 lanes one vector, so a wave
+// instruction covers 256/D vectors; a wave takes kNormVectors vectors (at
+// least one instruction's worth) with all its loads issued before any use.
+constexpr int kNormVectors = 8;
+template <int D>
+constexpr int norm_vectors_per_wave() {
+  return kWave / (D / 4) > kNormVectors ? kWave / (D / 4) : kNormVectors;
+}
+template <int D>
 inline dim3 norm_grid(int64_t nvec) {
-  const int64_t per_block = kNormVPW * (256 / kWave);
+  const int64_t per_block = norm_vectors_per_wave<D>() * (256 / kWave);
   return dim3((unsigned)((nvec + per_block - 1) / per_block));
 }
 template <int DT, int D>
 __global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z, const void* w,
                                                          int64_t nvec, float eps) {
-  // a wave handles kNormVPW vectors, all loads issued before any use; a lane
-  // owns EPL consecutive elements of each (vector loads)
-  constexpr int EPL = D >= kWave ? D / kWave : 1, V = kNormVPW;
+  static_assert(D % 4 == 0 && D / 4 <= kWave, "four elements per lane, a vector within a wave");
+  constexpr int LPV = D / 4, VPI = kWave / LPV, V = norm_vectors_per_wave<D>() / VPI;
   const int lane = threadIdx.x % kWave;
-  const int64_t v0 = ((int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave) * V;
-  const int r0 = lane * EPL;
-  const bool act = r0 < D;
-  Raw<GDN_F32, EPL> yv[V];
-  Raw<DT, EPL> zv[V];
+  const int64_t v0 =
+      ((int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave) * (V * VPI) + lane / LPV;
+  const int r0 = (lane % LPV) * 4;
+  Raw<GDN_F32, 4> yv[V];
+  Raw<DT, 4> zv[V];
 #pragma unroll
   for (int u = 0; u < V; ++u) {
-    if (act && v0 + u < nvec) {  // uniform per wave but for act
-      yv[u].load(y, (v0 + u) * D + r0);
-      zv[u].load(z, (v0 + u) * D + r0);
+    const int64_t vec = v0 + (int64_t)u * VPI;
+    if (vec < nvec) {  // uniform within a vector's lanes
+      yv[u].load(y, vec * D + r0);
+      zv[u].load(z, vec * D + r0);
     } else {
       yv[u].zero();
       zv[u].zero();
     }
   }
-  float wl[EPL];
+  float wl[4];  // w is aligned to its element size only: one element per load
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) wl[i] = act ? ld1<DT>(w, r0 + i) : 0.f;
+  for (int i = 0; i < 4; ++i) wl[i] = ld1<DT>(w, r0 + i);
 #pragma unroll
   for (int u = 0; u < V; ++u) {
-    float x[EPL];
+    float x[4];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
+    for (int i = 0; i < 4; ++i) {
       x[i] = yv[u].get(i) * silu(zv[u].get(i));
       ss = fmaf(x[i], x[i], ss);
     }
-    const float inv = rsqrtf(wave_sum(ss) * (1.0f / D) + eps);
-    if (act && v0 + u < nvec) {
-      float* dst = y + (v0 + u) * D + r0;
-      if constexpr (EPL == 4) {
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(x[0] * inv * wl[0], x[1] * inv * wl[1], x[2] * inv * wl[2], x[3] * inv * wl[3]);
-      } else if constexpr (EPL == 2) {
-        *reinterpret_cast<float2*>(dst) = make_float2(x[0] * inv * wl[0], x[1] * inv * wl[1]);
-      } else {
-        dst[0] = x[0] * inv * wl[0];
-      }
-    }
+    // the sum over the vector's lanes (the exec mask is full here)
+    if constexpr (LPV == kWave) ss = wave_sum(ss);
+    else ss = group_sum<LPV>(ss);
+    const float inv = rsqrtf(ss * (1.0f / D) + eps);
+    const int64_t vec = v0 + (int64_t)u * VPI;
+    if (vec < nvec)
+      *reinterpret_cast<float4*>(y + vec * D + r0) =
+          make_float4(x[0] * inv * wl[0], x[1] * inv * wl[1], x[2] * inv * wl[2],
+                      x[3] * inv * wl[3]);
   }
 }
 
@@ -567,7 +572,7 @@ int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
     int rc = device_status("scan_kernel launch");
     if (rc != GDN_OK || a.z == nullptr) return rc;
     const int64_t nvec = heads * a.T;
-    gated_norm_kernel<DT, D><<<norm_grid(nvec), 256, 0, st>>>(
+    gated_norm_kernel<DT, D><<<norm_grid<D>(nvec), 256, 0, st>>>(
         a.y, a.z, a.w, nvec, a.norm_eps);
     return device_status("gated_norm_kernel launch");
   }
@@ -608,12 +613,15 @@ int launch_scan_gt(const ScanArgs& a, int gdt, int D, int64_t heads, hipStream_t
 template <int DT>
 void launch_norm(int D, float* y, const void* z, const void* w, int64_t nvec, float eps,
                  hipStream_t st) {
-  const dim3 grid = norm_grid(nvec);
   switch (D) {
-    case 32: gated_norm_kernel<DT, 32><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
-    case 64: gated_norm_kernel<DT, 64><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
-    case 256: gated_norm_kernel<DT, 256><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
-    default: gated_norm_kernel<DT, 128><<<grid, 256, 0, st>>>(y, z, w, nvec, eps); break;
+    case 32: gated_norm_kernel<DT, 32><<<norm_grid<32>(nvec), 256, 0, st>>>(y, z, w, nvec, eps); break;
+    case 64: gated_norm_kernel<DT, 64><<<norm_grid<64>(nvec), 256, 0, st>>>(y, z, w, nvec, eps); break;
+    case 256:
+      gated_norm_kernel<DT, 256><<<norm_grid<256>(nvec), 256, 0, st>>>(y, z, w, nvec, eps);
+      break;
+    default:
+      gated_norm_kernel<DT, 128><<<norm_grid<128>(nvec), 256, 0, st>>>(y, z, w, nvec, eps);
+      break;
   }
 }
 

@@ -303,6 +303,39 @@ def test_block_form_16bit_accuracy(case, gated, exact):
     assert_close(s, sr, level, "final_state")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [32, 128])
+def test_norm_weight_aligned_to_its_element_only(dtype, D):
+    """w need only be aligned to its element size: a weight one element into a
+    larger buffer gives the oracle's output through the block form's separate
+    norm, the per-token form and the decode step."""
+    B, T, Hk, Hv = 1, 37, 2, 4
+    ops = synth.random_operands(B, T, Hk, Hv, D, D, dtype=dtype, seed=77 + D)
+    d = dev(ops)
+    buf = torch.zeros(D + 1, dtype=d["w"].dtype, device=DEV)
+    buf[1:] = d["w"]
+    w_odd = buf[1:]
+    assert w_odd.data_ptr() % (2 * w_odd.element_size()) != 0
+    yr, sr = orc.scan(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                      ops["z"], ops["w"])
+    for form in ("block", "per_token"):
+        say("odd w offset D=%d %s %s" % (D, dtype, form))
+        y, s = scan(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], d["z"], w_odd,
+                    form=form)
+        torch.cuda.synchronize()
+        assert_close(y, yr, TOL[dtype], "y, %s" % form)
+        assert_close(s, sr, TOL[dtype], "state, %s" % form)
+    one = {n: (t[:, :1].contiguous() if t.dim() >= 3 and n != "s0" else t) for n, t in d.items()}
+    y1r, s1r = orc.scan(*(one[n].cpu().numpy() if one[n].dtype == torch.float32 else
+                          one[n].float().cpu().numpy()
+                          for n in ("q", "k", "v", "log_decay", "beta", "s0", "z", "w")))
+    y1, s1 = recurrent_step(one["q"], one["k"], one["v"], one["log_decay"], one["beta"],
+                            one["s0"], one["z"], w_odd)
+    torch.cuda.synchronize()
+    assert_close(y1, y1r, TOL[dtype], "step y")
+    assert_close(s1, s1r, TOL[dtype], "step state")
+
+
 def test_gate_dtype_differs_from_operand_dtype():
     ops = synth.random_operands(2, 21, 2, 4, 64, 64, dtype="bf16", gate_dtype="f32", seed=5)
     run_both(ops, head_major=False, gated=True, dtype="bf16")
