@@ -48,6 +48,11 @@
  *     aligned to their element size.
  *   - Supported by the kernels: Dk == Dv in {16, 32, 64, 128, 256}; dtype and
  *     gate_dtype in {GDN_F32, GDN_F16, GDN_BF16}; Hv a multiple of Hk.
+ *   - Size limits (GDN_ESHAPE): B*T*Hv below 2^31, and every kernel launch of
+ *     the call at most 2^32 - 1 threads (the 32-bit grid size of a dispatch):
+ *     about B*Hv*1024 for the decode at D >= 128, B*Hv*12288 for the scan at
+ *     D = 256, 4*B*T*Hk for the block form's per-block prep.  Larger calls
+ *     are rejected, not split.
  *   - Error behaviour: every call returns GDN_OK or a gdn_status; the short
  *     reason of the last failure on the calling thread is gdn_last_error().
  *     A rejected call enqueues nothing.  A HIP launch failure returns
@@ -190,7 +195,8 @@ int gdn_scan_noalloc(const gdn_desc* d, const void* q, const void* k, const void
  * out_dtype (16-bit outputs rounded to nearest even), ready to be passed to
  * gdn_recurrent_step / gdn_scan as their gates.  Pointers aligned to their
  * element size; outputs must not overlap inputs or each other (GDN_EALIAS).
- * n == 0 does nothing.  Asynchronous on `stream`, allocates nothing. */
+ * n == 0 does nothing; n must be below 2^33 (one launch of n/4 threads).
+ * Asynchronous on `stream`, allocates nothing. */
 int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float decay_scale,
               void* log_decay, void* beta, int32_t out_dtype, void* stream);
 
@@ -207,7 +213,8 @@ int gdn_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float d
  * x, y: [B, T, C]; w: [C, W]; bias: [C] or NULL; state_in, state_out:
  * [B, C, W-1] or NULL (state_out NULL: not written).  Every tensor is dtype
  * (y rounded to nearest even for 16-bit types; the state holds exact copies of
- * inputs).  1 <= W <= 8.  Device pointers aligned to the element size
+ * inputs).  1 <= W <= 8; C and B*ceil(T/16) below 2^31 (one launch, a thread
+ * per one or four channels across).  Device pointers aligned to the element size
  * (16-byte alignment of x and y and C % 4 == 0 take the vector path).
  * state_out may be exactly state_in (updated in place); any other overlap of
  * an output with an operand is GDN_EALIAS.  T == 0 only writes state_out

@@ -18,7 +18,8 @@
  * nontemporal or ordinary loads and stores, or (the last three) buffer loads
  * and stores with the decode's cache policies: nontemporal loads, stores
  * nontemporal and written through to device scope; gdn_calib_variant_name()
- * names it.  bytes must be a multiple of 16 and src/dst 16-byte aligned device
+ * names it.  bytes must be a multiple of 16 and below 2^37 (one launch of at
+ * most 2^31 threads), and src/dst 16-byte aligned device
  * pointers owned by the caller; for GDN_CALIB_COPY they must not overlap.
  * Asynchronous on `stream`; allocates nothing; returns a gdn_status
  * (include/gdn.h) with the reason in gdn_last_error().

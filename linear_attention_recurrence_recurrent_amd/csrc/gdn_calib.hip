@@ -110,8 +110,10 @@ int gdn_calib_stream(int32_t op, int32_t variant, const void* src, void* dst, ui
     set_error("variant out of range");
     return GDN_EINVAL;
   }
-  if (bytes % 16 || bytes / 16 >= ((uint64_t)1 << 40)) {
-    set_error("bytes must be a multiple of 16 (and below 2^44)");
+  // at least four 16-byte vectors per thread: below 2^33 vectors keeps a
+  // launch's work-items under the 32-bit grid size of the dispatch packet
+  if (bytes % 16 || bytes / 16 >= ((uint64_t)1 << 33)) {
+    set_error("bytes must be a multiple of 16 (and below 2^37)");
     return GDN_ESHAPE;
   }
   if (bytes == 0) return GDN_OK;

@@ -55,6 +55,38 @@ void set_error(const char* msg) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
 }
 
+// Work-items per value head of the decode kernel (launch_step_sp) and of the
+// per-token scan kernel (launch_scan_dt / launch_scan_cfg: workgroups of 16,
+// 32, 64 or 128 rows at D = 128, by head count).
+static int64_t step_threads_per_head(int64_t D) { return D >= 128 ? 1024 : D >= 32 ? 128 : 64; }
+static int64_t scan_threads_per_head(int64_t D, int64_t heads) {
+  switch (D) {
+    case 256: return 16 * 256;
+    case 128: return heads >= 512 ? 256 : heads >= 128 ? 4 * 256 : 8 * 256;
+    case 64: return heads >= 256 ? 256 : 4 * 128;
+    case 32: return 128;
+    default: return 64;
+  }
+}
+
+int64_t max_launch_items(const gdn_desc& d) {
+  if (d.B == 0 || d.T == 0) return 0;
+  const int64_t heads = d.B * d.Hv, D = d.Dk;
+  if (d.T == 1) return heads * step_threads_per_head(D);  // the decode kernel (also three-pass)
+  // (the separate gated norm splits itself into launches of bounded size)
+  int64_t main = 0;
+  if (scan_uses_block_form(d)) {
+    const int64_t nblk = (d.T + kBlockTokens - 1) / kBlockTokens;
+    const int64_t prep = (d.B * d.Hk * nblk + 3) / 4 * 256;  // a wave per (batch, key head, block)
+    main = scan_uses_key_products(d) ? heads * (D / 16) * (D / 32 + 4) * 64  // rows_la_kernel
+                                     : heads * 4 * D;                        // state_kernel
+    if (prep > main) main = prep;
+  } else {
+    main = heads * scan_threads_per_head(D, heads);
+  }
+  return main;
+}
+
 int check_desc(const gdn_desc* d) {
   g_last_error[0] = '\0';
   if (!d) return fail(GDN_EINVAL, "null descriptor");
@@ -99,6 +131,10 @@ int check_desc(const gdn_desc* d) {
     return fail(GDN_ESHAPE, "operand sizes overflow");
   if (ng >= (int64_t)1 << 31 || nv >= (int64_t)1 << 40)
     return fail(GDN_ESHAPE, "B*T*Hv (%lld) too large for the launch grid", (long long)ng);
+  const int64_t items = max_launch_items(*d);
+  if (items > kMaxLaunchItems)
+    return fail(GDN_ESHAPE, "the shape needs a launch of %lld work-items (at most 2^32 - 1)",
+                (long long)items);
   return GDN_OK;
 }
 
@@ -203,7 +239,8 @@ int check_gates(int64_t n, const void* a, const void* b, int32_t in_dtype, float
                 const void* log_decay, const void* beta, int32_t out_dtype) {
   g_last_error[0] = '\0';
   if (n < 0) return fail(GDN_ESHAPE, "negative element count %lld", (long long)n);
-  if (n >= (int64_t)1 << 40) return fail(GDN_ESHAPE, "element count too large");
+  // four elements per thread: n / 4 work-items in one launch
+  if (n >= (int64_t)1 << 33) return fail(GDN_ESHAPE, "element count too large (at most 2^33 - 1)");
   if (in_dtype < GDN_F32 || in_dtype > GDN_BF16 || out_dtype < GDN_F32 || out_dtype > GDN_BF16)
     return fail(GDN_EDTYPE, "bad dtype (in %d, out %d)", in_dtype, out_dtype);
   if (!(decay_scale >= 0.0f && decay_scale < 1e30f))
@@ -243,9 +280,10 @@ int check_conv(int64_t B, int64_t T, int64_t C, int32_t W, int32_t dtype, int32_
       !mul_ok(C, (int64_t)W * es, &nw))
     return fail(GDN_ESHAPE, "sizes overflow");
   int64_t nblk = 0;  // workgroups along (batch, 16-token tiles)
+  // one launch: a thread per channel (or four) across, (batch, tile) pairs down
   if (!mul_ok(B, T > 0 ? (T + 15) / 16 : 1, &nblk) || nblk >= ((int64_t)1 << 31) ||
-      C >= ((int64_t)1 << 38))
-    return fail(GDN_ESHAPE, "grid too large");
+      C >= ((int64_t)1 << 31))
+    return fail(GDN_ESHAPE, "grid too large (B * ceil(T / 16) and C below 2^31)");
   if (B == 0 || C == 0) return GDN_OK;
   if (!w) return fail(GDN_EINVAL, "null weight");
   if (T > 0 && (!x || !y)) return fail(GDN_EINVAL, "null x or y");

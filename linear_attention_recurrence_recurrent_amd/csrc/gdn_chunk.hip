@@ -1825,7 +1825,13 @@ int launch_prep(const PrepArgs& p, int gdt, dim3 grid, hipStream_t st) {
 template <int DT, int NSP, int D>
 int launch_dt(const gdn_desc& d, const PrepArgs& p, const StateArgs& s, int64_t heads,
               hipStream_t st) {
-  const dim3 pgrid((unsigned)((p.ntask + 3) / 4));
+  const int64_t pblocks = (p.ntask + 3) / 4;
+  const bool rows = D > 128 || scan_uses_key_products(d);
+  if (!launch_fits(pblocks, 256, "prep_kernel") ||
+      !(rows ? launch_fits(heads * (D / 16), rows_la_threads<DT, D>(), "rows_la_kernel")
+             : launch_fits(heads, 4 * D, "state_kernel")))
+    return GDN_ESHAPE;
+  const dim3 pgrid((unsigned)pblocks);
   // the few-head kernel's default products take T and M1 as bf16 parts
   const int rc = launch_prep<DT, D, DT != GDN_F32 && NSP == 2>(p, d.gate_dtype, pgrid, st);
   if (rc != GDN_OK) return rc;

@@ -188,6 +188,9 @@ int launch_conv(int64_t B, int64_t T, int64_t C, int W, int dtype, int apply_sil
   const int64_t vec = vec4 ? 4 : 1;
   const int64_t ntiles = T > 0 ? (T + kTT - 1) / kTT : 1;
   const ConvArgs a{x, w, bias, state_in, y, state_out, T, C, ntiles};
+  if (!launch_fits((C / vec + 255) / 256, 256, "conv_kernel") ||
+      !launch_fits(B * ntiles, 1, "conv_kernel"))
+    return GDN_ESHAPE;
   const dim3 grid((unsigned)((C / vec + 255) / 256), (unsigned)(B * ntiles));
   switch (dtype) {
     case GDN_F32: launch_dt<GDN_F32>(a, grid, vec4, W, apply_silu != 0, st); break;

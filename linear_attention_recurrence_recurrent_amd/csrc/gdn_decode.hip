@@ -316,6 +316,8 @@ constexpr int64_t kWriteThroughBytes = (int64_t)128 << 20, kCachedStoreBytes = (
 
 template <int DT, int GT, int SP>
 int launch_step_sp(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
+  const int64_t threads = d.Dk >= 128 ? 16 * kWave : d.Dk >= 32 ? 2 * kWave : kWave;
+  if (!launch_fits(d.B * d.Hv, threads, "decode_kernel")) return GDN_ESHAPE;
   const dim3 grid((unsigned)(d.B * d.Hv));
   switch (d.Dk) {
     case 256: decode_kernel<DT, GT, 256, 16, 4, 16, SP><<<grid, 16 * kWave, 0, st>>>(a); break;
@@ -370,6 +372,7 @@ int launch_three_pass_dt(const gdn_desc& d, StepArgs a, hipStream_t st) {
     set_error("the three-pass step is built for D == 128 only");
     return GDN_EUNSUPPORTED;
   }
+  if (!launch_fits(d.B * d.Hv, 16 * kWave, "threepass_kernel")) return GDN_ESHAPE;
   // pass 1 reads s0 and pass 2 rewrites it into s_out (the launches are
   // ordered on the stream, so s_out == s0 is fine); pass 3 reads s_out
   threepass_kernel<DT, GT, 128, 16, 2, 16, 1><<<grid, 16 * kWave, 0, st>>>(a);

@@ -62,6 +62,7 @@ void launch_gates_it(int64_t n, const void* a, const void* b, float s, void* ld,
 int launch_gates(int64_t n, const void* a, const void* b, int in_dtype, float decay_scale,
                  void* log_decay, void* beta, int out_dtype, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!launch_fits((n + 1023) / 1024, 256, "gates_kernel")) return GDN_ESHAPE;
   switch (in_dtype) {
     case GDN_F32: launch_gates_it<GDN_F32>(n, a, b, decay_scale, log_decay, beta, out_dtype, st); break;
     case GDN_F16: launch_gates_it<GDN_F16>(n, a, b, decay_scale, log_decay, beta, out_dtype, st); break;

@@ -29,6 +29,15 @@ bool scan_uses_key_products(const gdn_desc& d);
 int64_t scan_record_bytes(const gdn_desc& d);
 int64_t scan_workspace_bytes(const gdn_desc& d);
 
+// A launch's work-items (grid x workgroup) travel as a 32-bit count in the
+// dispatch packet, and a larger grid is not reliably refused by the runtime
+// (it can wrap to a few workgroups), so every launch stays at or below this.
+constexpr int64_t kMaxLaunchItems = ((int64_t)1 << 32) - 1;
+// The most work-items any one launch of the call that `d` describes takes
+// (gdn_recurrent_step, its three-pass form, or gdn_scan), from the shapes the
+// launchers pick; 0 when nothing is launched.
+int64_t max_launch_items(const gdn_desc& d);
+
 // Descriptor validation (no pointers); sets the thread's last error on failure.
 int check_desc(const gdn_desc* d);
 

@@ -557,12 +557,28 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(float* y, const void* z
   }
 }
 
+// The gated norm over nvec vectors in launches of at most kNormChunk vectors
+// each (2^31 work-items at most: a dispatch counts them in 32 bits), so its
+// size is bounded only by the operands.
+constexpr int64_t kNormChunk = (int64_t)1 << 28;
+template <int DT, int D>
+void launch_norm_d(float* y, const void* z, const void* w, int64_t nvec, float eps,
+                   hipStream_t st) {
+  constexpr int64_t es = DT == GDN_F32 ? 4 : 2;
+  for (int64_t v0 = 0; v0 < nvec; v0 += kNormChunk) {
+    const int64_t n = nvec - v0 < kNormChunk ? nvec - v0 : kNormChunk;
+    gated_norm_kernel<DT, D><<<norm_grid<D>(n), 256, 0, st>>>(
+        y + v0 * D, static_cast<const char*>(z) + v0 * D * es, w, n, eps);
+  }
+}
+
 }  // namespace
 
 template <int DT, int GT, int D, int CL, int RPL, int NW, int TC>
 int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
   constexpr int ROWS = NW * (kWave / CL) * RPL;
   a.nrb = D / ROWS;
+  if (!launch_fits(heads * a.nrb, NW * kWave, "scan_kernel")) return GDN_ESHAPE;
   const dim3 grid((unsigned)(heads * a.nrb));
   if constexpr (ROWS == D) {
     scan_kernel<DT, GT, D, CL, RPL, NW, TC, true><<<grid, NW * kWave, 0, st>>>(a);
@@ -571,9 +587,7 @@ int launch_scan_cfg(ScanArgs a, int64_t heads, hipStream_t st) {
     scan_kernel<DT, GT, D, CL, RPL, NW, TC, false><<<grid, NW * kWave, 0, st>>>(a);
     int rc = device_status("scan_kernel launch");
     if (rc != GDN_OK || a.z == nullptr) return rc;
-    const int64_t nvec = heads * a.T;
-    gated_norm_kernel<DT, D><<<norm_grid<D>(nvec), 256, 0, st>>>(
-        a.y, a.z, a.w, nvec, a.norm_eps);
+    launch_norm_d<DT, D>(a.y, a.z, a.w, heads * a.T, a.norm_eps, st);
     return device_status("gated_norm_kernel launch");
   }
 }
@@ -614,14 +628,10 @@ template <int DT>
 void launch_norm(int D, float* y, const void* z, const void* w, int64_t nvec, float eps,
                  hipStream_t st) {
   switch (D) {
-    case 32: gated_norm_kernel<DT, 32><<<norm_grid<32>(nvec), 256, 0, st>>>(y, z, w, nvec, eps); break;
-    case 64: gated_norm_kernel<DT, 64><<<norm_grid<64>(nvec), 256, 0, st>>>(y, z, w, nvec, eps); break;
-    case 256:
-      gated_norm_kernel<DT, 256><<<norm_grid<256>(nvec), 256, 0, st>>>(y, z, w, nvec, eps);
-      break;
-    default:
-      gated_norm_kernel<DT, 128><<<norm_grid<128>(nvec), 256, 0, st>>>(y, z, w, nvec, eps);
-      break;
+    case 32: launch_norm_d<DT, 32>(y, z, w, nvec, eps, st); break;
+    case 64: launch_norm_d<DT, 64>(y, z, w, nvec, eps, st); break;
+    case 256: launch_norm_d<DT, 256>(y, z, w, nvec, eps, st); break;
+    default: launch_norm_d<DT, 128>(y, z, w, nvec, eps, st); break;
   }
 }
 

@@ -211,6 +211,50 @@ def test_rejects_size_overflow():
     assert rc == 2
 
 
+LAUNCH_EDGES = [
+    # (descriptor fields, status): the last shape each kernel's launch fits, and the next
+    # the decode at D = 128: a workgroup of 1024 threads per head
+    (dict(B=(1 << 22) - 1, T=1, Hk=1, Hv=1, Dk=128, Dv=128), 0),
+    (dict(B=1 << 22, T=1, Hk=1, Hv=1, Dk=128, Dv=128), 2),
+    # the decode at D = 16: one wave per head
+    (dict(B=(1 << 26) - 1, T=1, Hk=1, Hv=1, Dk=16, Dv=16), 0),
+    (dict(B=1 << 26, T=1, Hk=1, Hv=1, Dk=16, Dv=16), 2),
+    # the block form at D = 256 (the few-head kernel at any head count): 16 x 768 threads
+    (dict(B=349525, T=2, Hk=1, Hv=1, Dk=256, Dv=256), 0),
+    (dict(B=349526, T=2, Hk=1, Hv=1, Dk=256, Dv=256), 2),
+    # the per-token form at D = 256: 16 workgroups of 256 threads per head
+    (dict(B=(1 << 20) - 1, T=2, Hk=1, Hv=1, Dk=256, Dv=256, flags=7), 0),
+    (dict(B=1 << 20, T=2, Hk=1, Hv=1, Dk=256, Dv=256, flags=7), 2),
+    # the block form's prep: a wave per (batch, key head, 16-token block), four per workgroup
+    (dict(B=1, T=(1 << 27) - 16, Hk=8, Hv=8, Dk=32, Dv=32), 0),
+    (dict(B=1, T=(1 << 27) - 15, Hk=8, Hv=8, Dk=32, Dv=32), 2),
+    # the separate gated norm is split into launches of bounded size: 2^30 head-tokens pass
+    (dict(B=1, T=1 << 29, Hk=1, Hv=2, Dk=128, Dv=128), 0),
+]
+
+
+@pytest.mark.parametrize("fields,status", LAUNCH_EDGES)
+def test_every_launch_fits_one_dispatch(fields, status):
+    """A launch's work-items (grid x workgroup) travel as a 32-bit count, and
+    the runtime does not reliably refuse more (a grid just past 2^32
+    work-items can wrap to a few workgroups), so validation bounds every
+    launch a call makes, at the exact edge of each kernel's shape."""
+    rc, _ = _ws_size(**fields)
+    assert rc == status, (fields, nat.last_error())
+    if status:
+        assert "work-items" in nat.last_error()
+
+
+def test_producers_fit_one_dispatch():
+    """The producers and the streaming reference kernels bound their single
+    launch the same way (rejected before any HIP call)."""
+    L = nat.lib()
+    a, b, ld, be, x, w, y = _addrs(7)
+    assert L.gdn_gates(1 << 33, a, b, 2, 1.0, ld, be, 0, None) == 2
+    assert L.gdn_conv_silu(1, 4, 1 << 31, 4, 2, 1, x, w, None, None, y, None, None) == 2
+    assert L.gdn_calib_stream(0, 0, a, a, 1 << 37, None) == 2 and "2^37" in nat.last_error()
+
+
 def test_step_needs_one_token_and_no_device_work_on_reject():
     L = nat.lib()
     ops = _ops()
