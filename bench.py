@@ -182,6 +182,47 @@ class Launcher:
             raise RuntimeError("launch rejected: %s" % _native.last_error())
 
 
+def shader_clock(torch, args):
+    """The shader clock the chip sustains under a vector-ALU load (the FP32
+    peak is quoted at 2.4 GHz): the library's clock reference kernel
+    (include/gdn_calib.h) with one wave per SIMD and with eight, each after the
+    settle period.  The clock is the waves' shader cycles over their ticks of
+    the constant 100 MHz counter; that counter's rate is checked against the
+    HIP events around the same launch.  The FMAs issued per second are the
+    unpacked FP32 rate the vector units reach there."""
+    from linear_attention_recurrence_recurrent_amd import _native
+    L = _native.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, waves, iters in (("one_wave_per_simd", 1024, 40000),
+                               ("eight_waves_per_simd", 8192, 8000)):
+        out = torch.zeros(4 * waves, dtype=torch.int64, device=dev)
+
+        def call():
+            rc = L.gdn_calib_clock(waves, iters, ctypes.c_void_p(out.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream))
+            if rc:
+                raise RuntimeError("clock kernel rejected: %s" % _native.last_error())
+        settle(call, torch, args.settle_ms)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        o = out.view(waves, 4).cpu().double()
+        ghz = float(o[:, 0].sum() / o[:, 1].sum()) * 0.1
+        res[name + "_ghz"] = round(ghz, 3)
+        res[name + "_us"] = round(us, 1)
+        # eight FMAs per round on each of 64 lanes: the unpacked FP32 rate achieved
+        res[name + "_fma_tflops"] = round(waves * iters * 8 * 64 * 2 / (us * 1e-6) / 1e12, 1)
+        if name == "one_wave_per_simd":
+            res["realtime_counter_mhz"] = round(float(o[:, 1].max()) / us, 1)
+        log("shader clock, %s: %.3f GHz over %.0f us" % (name.replace("_", " "), ghz, us))
+    return res
+
+
 def streaming_ceiling(torch, nbytes, args):
     """The HBM rate an in-place state update can reach here: the library's
     streaming reference kernels (include/gdn_calib.h) rewrite a buffer of the
@@ -798,6 +839,7 @@ def main():
         "decode_double_buffered": dec["double_buffered"],
     }
     out["decode_b1"] = bench_decode_single(args, torch)
+    out["shader_clock"] = shader_clock(torch, args)
     if scan:
         out["scan"] = scan
     if not args.no_scan:

@@ -43,6 +43,19 @@ int gdn_calib_stream(int32_t op, int32_t variant, const void* src, void* dst, ui
 /* Static description of a variant ("" when out of range). */
 const char* gdn_calib_variant_name(int32_t variant);
 
+/* The shader clock under a vector-ALU load, to set the FP32 peak (quoted at
+ * 2.4 GHz) beside the clock the chip sustains.  `waves` waves of 64 lanes
+ * (workgroups of four; a multiple of 4 from 4 to 8192, i.e. up to 8 per SIMD
+ * over 256 CUs) each run `iters` (1 to 2^24) rounds of eight independent
+ * chains of dependent FMAs, reading the shader-cycle counter and the constant
+ * 100 MHz real-time counter before and after.  out: caller-owned device
+ * buffer of 4 * waves uint64, 8-byte aligned; wave i writes out[4i] = shader
+ * cycles, out[4i+1] = real-time ticks, out[4i+2] = the bits of the chains'
+ * float sum, out[4i+3] = 0.  The clock is sum(cycles) / sum(ticks) * 100 MHz.
+ * Asynchronous on `stream`; allocates nothing; returns a gdn_status with the
+ * reason in gdn_last_error(). */
+int gdn_calib_clock(int32_t waves, int32_t iters, uint64_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ ABI_VERSION = 2
 EXPORTS = ("gdn_recurrent_step", "gdn_recurrent_step_three_pass", "gdn_scan",
            "gdn_scan_workspace_size", "gdn_scan_noalloc", "gdn_gates", "gdn_conv_silu", "gdn_check",
            "gdn_last_error", "gdn_status_str", "gdn_abi_version", "gdn_calib_stream",
-           "gdn_calib_variant_name")
+           "gdn_calib_variant_name", "gdn_calib_clock")
 GDN_CALIB_RMW, GDN_CALIB_COPY, GDN_CALIB_VARIANTS = 0, 1, 15
 GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -83,6 +83,8 @@ def lib():
                                        vp]
         L.gdn_calib_variant_name.restype = ctypes.c_char_p
         L.gdn_calib_variant_name.argtypes = [ctypes.c_int32]
+        L.gdn_calib_clock.restype = ctypes.c_int
+        L.gdn_calib_clock.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
         _lib = L
     return _lib
 

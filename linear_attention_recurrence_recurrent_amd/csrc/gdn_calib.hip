@@ -67,6 +67,36 @@ __global__ __launch_bounds__(TPB) void stream_buf_kernel(const float* src, float
   }
 }
 
+// Shader-clock reference: every lane runs eight independent chains of
+// dependent FMAs (enough to keep a SIMD's vector unit issuing with one wave
+// on it) between two reads of the shader-cycle counter and of the constant
+// 100 MHz real-time counter.  The chains start from the first readings and an
+// empty asm consumes them before the second, so the loop stays between the
+// two (and each pair of readings stays together).  Lanes 0 to 3 of each wave store its cycles, its ticks and the chains'
+// sum (vector stores; the sum keeps the arithmetic alive).
+__global__ __launch_bounds__(256) void clock_kernel(uint64_t* out, int iters) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  float x[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) x[c] = (float)(((c0 ^ r0) & 7) + threadIdx.x + c) * 1e-3f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = fmaf(x[c], 0.9999999f, 1e-7f);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) asm volatile("" : : "v"(x[c]));
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc += x[c];
+  const int lane = threadIdx.x % kWave;
+  const int64_t wave = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  const uint64_t word[4] = {c1 - c0, r1 - r0, (uint64_t)__float_as_uint(acc), 0};
+  if (lane < 4) out[4 * wave + lane] = word[lane];
+}
+
 // names in the order of the launch switch below
 constexpr const char* kVariantNames[GDN_CALIB_VARIANTS] = {
     "512 threads x 8 vectors, nontemporal",  "256 threads x 8 vectors, nontemporal",
@@ -152,6 +182,25 @@ int gdn_calib_stream(int32_t op, int32_t variant, const void* src, void* dst, ui
     default: launch_b<512, 8>(rmw, s, d, n4, st); break;
   }
   return device_status("stream_kernel launch");
+}
+
+int gdn_calib_clock(int32_t waves, int32_t iters, uint64_t* out, void* stream) {
+  using namespace gdn;
+  if (waves < 4 || waves > 8192 || waves % 4) {
+    set_error("waves must be a multiple of 4 from 4 to 8192");
+    return GDN_ESHAPE;
+  }
+  if (iters < 1 || iters > (1 << 24)) {
+    set_error("iters must be from 1 to 2^24");
+    return GDN_ESHAPE;
+  }
+  if (!out || (uintptr_t)out % 8) {
+    set_error("out must be a non-null 8-byte aligned device pointer");
+    return out ? GDN_EALIGN : GDN_EINVAL;
+  }
+  clock_kernel<<<dim3((unsigned)(waves / 4)), 256, 0, static_cast<hipStream_t>(stream)>>>(out,
+                                                                                          iters);
+  return device_status("clock_kernel launch");
 }
 
 const char* gdn_calib_variant_name(int32_t variant) {

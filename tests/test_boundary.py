@@ -287,6 +287,10 @@ def test_calib_validation():
     assert f(1, 0, a + 4, b, 1 << 20, None) == 6
     assert f(1, 0, None, b, 1 << 20, None) == 1
     assert f(0, 0, None, None, 0, None) == 0
+    clk = L.gdn_calib_clock
+    assert clk(3, 10, a, None) == 2 and clk(8196, 10, a, None) == 2 and clk(4, 0, a, None) == 2
+    assert clk(4, 1 << 25, a, None) == 2
+    assert clk(4, 10, None, None) == 1 and clk(4, 10, a + 4, None) == 6
     names = [L.gdn_calib_variant_name(i).decode() for i in range(nat.GDN_CALIB_VARIANTS)]
     assert len(set(names)) == nat.GDN_CALIB_VARIANTS and all(names)
     assert L.gdn_calib_variant_name(-1).decode() == ""

@@ -1,4 +1,4 @@
-"""The streaming reference kernels (include/gdn_calib.h) on the GPU: every
+"""The streaming and clock reference kernels (include/gdn_calib.h) on the GPU: every
 variant's copy is exact and its in-place update is buf * 1.0000001 + 1e-7 to
 within one float32 rounding (the kernels fuse the multiply-add), on a size
 that leaves a ragged last workgroup, and nothing outside the buffer is
@@ -51,3 +51,37 @@ def test_stream_variant_results(variant):
             + np.float64(np.float32(1e-7)))
     ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
     assert np.all(np.abs(got_a[PAD:PAD + n] - want) <= ulp), "in-place update"
+
+
+@pytest.mark.parametrize("waves,iters", [(4, 1000), (1024, 20000), (8192, 2000)])
+def test_clock_reference(waves, iters):
+    """The clock reference writes four words per wave and nothing past them:
+    positive shader cycles and real-time ticks whose ratio is a plausible
+    shader clock (0.3 to 3 GHz against the constant 100 MHz counter), the
+    chains' float sum (finite), and a zero; the ticks match the HIP events'
+    duration of the launch at 100 MHz."""
+    print("clock reference: %d waves x %d rounds" % (waves, iters), flush=True)
+    L = _native.lib()
+    stream = torch.cuda.current_stream()
+    out = torch.full((4 * waves + 8,), -7, dtype=torch.int64, device="cuda:0")
+    for _ in range(3):  # clocks up first
+        assert L.gdn_calib_clock(waves, iters, ctypes.c_void_p(out.data_ptr()),
+                                 ctypes.c_void_p(stream.cuda_stream)) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    assert L.gdn_calib_clock(waves, iters, ctypes.c_void_p(out.data_ptr()),
+                             ctypes.c_void_p(stream.cuda_stream)) == 0
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    o = out.cpu().numpy()
+    assert np.all(o[4 * waves:] == -7)
+    w = o[:4 * waves].reshape(waves, 4)
+    assert np.all(w[:, 0] > 0) and np.all(w[:, 1] > 0) and np.all(w[:, 3] == 0)
+    sums = w[:, 2].astype(np.uint32).view(np.float32)
+    assert np.all(np.isfinite(sums))
+    ghz = w[:, 0].sum() / w[:, 1].sum() * 0.1
+    assert 0.3 < ghz < 3.0, ghz
+    if iters * waves >= 1 << 24:  # long enough for the launch overhead not to matter
+        mhz = w[:, 1].max() / us
+        assert 70 < mhz < 130, (mhz, us)
