@@ -25,6 +25,10 @@ FETCH_SIZE/WRITE_SIZE summary when it was taken on the current kernel source.
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
 workload on this host.  ``gate_producer`` and ``conv_producer`` time the two
 producers next to the recurrence (HBM-bound, algorithmic GB/s).
+``shader_clock`` is the clock the chip sustains under a vector-ALU load and the
+unpacked FP32 rate reached there (one and eight waves per SIMD), beside the
+2.4 GHz at which the FP32 peak is quoted; ``decode_b1`` is the single decode
+step, bound by launch latency.
 """
 from __future__ import annotations
 
