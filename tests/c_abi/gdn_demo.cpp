@@ -63,14 +63,29 @@ bool ok(hipError_t e, const char* what) {
   return false;
 }
 
-template <typename X>
-X* to_device(const std::vector<X>& h) {
-  X* p = nullptr;
-  if (!ok(hipMalloc(&p, h.size() * sizeof(X)), "hipMalloc")) return nullptr;
-  if (!ok(hipMemcpy(p, h.data(), h.size() * sizeof(X), hipMemcpyHostToDevice), "hipMemcpy"))
-    return nullptr;
-  return p;
-}
+// Device buffers and the stream, released on every way out of the run.
+struct Owned {
+  std::vector<void*> bufs;
+  hipStream_t stream = nullptr;
+  ~Owned() {
+    for (void* p : bufs) (void)hipFree(p);
+    if (stream) (void)hipStreamDestroy(stream);
+  }
+  template <typename X>
+  X* alloc(size_t n) {
+    X* p = nullptr;
+    if (!ok(hipMalloc(&p, n * sizeof(X)), "hipMalloc")) return nullptr;
+    bufs.push_back(p);
+    return p;
+  }
+  template <typename X>
+  X* to_device(const std::vector<X>& h) {
+    X* p = alloc<X>(h.size());
+    if (p && !ok(hipMemcpy(p, h.data(), h.size() * sizeof(X), hipMemcpyHostToDevice), "hipMemcpy"))
+      return nullptr;
+    return p;
+  }
+};
 
 template <typename X>
 bool to_host(std::vector<X>& h, const X* p) {
@@ -108,15 +123,16 @@ extern "C" int gdn_demo_run(const char* out_file) {
   std::vector<float> s0(ns);
   for (auto& x : s0) x = 0.02f * uniform();
 
-  const uint16_t *dq = to_device(q), *dk = to_device(k), *dv = to_device(v), *dz = to_device(z),
-                 *dg = to_device(g), *db = to_device(be), *dq1 = to_device(q1),
-                 *dk1 = to_device(k1), *dv1 = to_device(v1), *dz1 = to_device(z1),
-                 *dg1 = to_device(g1), *db1 = to_device(be1), *dw = to_device(w);
-  const float* ds0 = to_device(s0);
-  float *dy = nullptr, *dy1 = nullptr, *ds = nullptr;
+  Owned own;
+  const uint16_t *dq = own.to_device(q), *dk = own.to_device(k), *dv = own.to_device(v),
+                 *dz = own.to_device(z), *dg = own.to_device(g), *db = own.to_device(be),
+                 *dq1 = own.to_device(q1), *dk1 = own.to_device(k1), *dv1 = own.to_device(v1),
+                 *dz1 = own.to_device(z1), *dg1 = own.to_device(g1), *db1 = own.to_device(be1),
+                 *dw = own.to_device(w);
+  const float* ds0 = own.to_device(s0);
+  float *dy = own.alloc<float>(nv), *dy1 = own.alloc<float>(nv1), *ds = own.alloc<float>(ns);
   if (!dq || !dk || !dv || !dz || !dg || !db || !dq1 || !dk1 || !dv1 || !dz1 || !dg1 || !db1 ||
-      !dw || !ds0 || !ok(hipMalloc(&dy, nv * 4), "hipMalloc") ||
-      !ok(hipMalloc(&dy1, nv1 * 4), "hipMalloc") || !ok(hipMalloc(&ds, ns * 4), "hipMalloc"))
+      !dw || !ds0 || !dy || !dy1 || !ds)
     return 1;
   uint64_t ws_bytes = 0;
   int rc = gdn_scan_workspace_size(&d, &ws_bytes);
@@ -125,10 +141,9 @@ extern "C" int gdn_demo_run(const char* out_file) {
                  (unsigned long long)ws_bytes);
     return 1;
   }
-  void* ws = nullptr;
-  hipStream_t st = nullptr;
-  if (!ok(hipMalloc(&ws, ws_bytes), "hipMalloc") || !ok(hipStreamCreate(&st), "hipStreamCreate"))
-    return 1;
+  void* ws = own.alloc<unsigned char>(ws_bytes);
+  if (!ws || !ok(hipStreamCreate(&own.stream), "hipStreamCreate")) return 1;
+  hipStream_t st = own.stream;
 
   // a refused call: a value-head count that is not a multiple of the key heads
   gdn_desc bad = d;
@@ -169,13 +184,6 @@ extern "C" int gdn_demo_run(const char* out_file) {
   put(f, y), put(f, s_scan), put(f, y1), put(f, s_step);
   std::fclose(f);
 
-  for (const void* p : {(const void*)dq, (const void*)dk, (const void*)dv, (const void*)dz,
-                        (const void*)dg, (const void*)db, (const void*)dq1, (const void*)dk1,
-                        (const void*)dv1, (const void*)dz1, (const void*)dg1, (const void*)db1,
-                        (const void*)dw, (const void*)ds0, (const void*)dy, (const void*)dy1,
-                        (const void*)ds, (const void*)ws})
-    (void)hipFree(const_cast<void*>(p));
-  (void)hipStreamDestroy(st);
   std::printf("gdn_demo: scan (B=%lld T=%lld Hk=%lld Hv=%lld D=%lld, %llu workspace bytes) and "
               "one decode step done\n",
               (long long)B, (long long)T, (long long)Hk, (long long)Hv, (long long)D,
