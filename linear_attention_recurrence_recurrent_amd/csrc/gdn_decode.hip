@@ -313,6 +313,9 @@ __global__ __launch_bounds__(NW* kWave) void threepass_kernel(StepArgs a) {
 // kCachedStoreBytes (half of the eight XCDs' 4 MB L2s) they carry no hint, so
 // the state stays in L2 for the next step; nontemporal in between.
 constexpr int64_t kWriteThroughBytes = (int64_t)128 << 20, kCachedStoreBytes = (int64_t)16 << 20;
+// Up to this many heads (one workgroup per CU at most) the D = 128 step takes
+// the latency shape below.
+constexpr int64_t kLatencyBoundHeads = 256;
 
 template <int DT, int GT, int SP>
 int launch_step_sp(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
@@ -321,11 +324,20 @@ int launch_step_sp(const gdn_desc& d, const StepArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(d.B * d.Hv));
   switch (d.Dk) {
     case 256: decode_kernel<DT, GT, 256, 16, 4, 16, SP><<<grid, 16 * kWave, 0, st>>>(a); break;
-    // 16 lanes per row (256-byte segments per load), 1024 threads: 49 VGPRs, so
-    // 8 waves per SIMD hold two heads per CU and 2048 heads run in four even
-    // rounds (8 lanes x 512 threads needed 80 VGPRs: three heads per CU and a
-    // ragged last round; 46.6 against 45.3 us per step at B = 64)
-    case 128: decode_kernel<DT, GT, 128, 16, 2, 16, SP><<<grid, 16 * kWave, 0, st>>>(a); break;
+    // 16 lanes per row (256-byte segments per load).  From 512 heads on, 1024
+    // threads at 53 VGPRs: 8 waves per SIMD hold two heads per CU and 2048
+    // heads run in four even rounds (8 lanes x 512 threads needed 80 VGPRs:
+    // three heads per CU and a ragged last round; 46.6 against 45.3 us per
+    // step at B = 64).  Up to 256 heads, at most one workgroup per CU, the step
+    // is bound by latency: 512 threads of four rows per lane finish sooner
+    // (one barrier across 8 waves instead of 16: 3.83 against 4.09 us at B = 1,
+    // 5.6 against 5.8 at B = 8; from 512 heads 1024 threads are faster).
+    case 128:
+      if (d.B * d.Hv <= kLatencyBoundHeads)
+        decode_kernel<DT, GT, 128, 16, 4, 8, SP><<<grid, 8 * kWave, 0, st>>>(a);
+      else
+        decode_kernel<DT, GT, 128, 16, 2, 16, SP><<<grid, 16 * kWave, 0, st>>>(a);
+      break;
     case 64: decode_kernel<DT, GT, 64, 4, 2, 2, SP><<<grid, 2 * kWave, 0, st>>>(a); break;
     case 32: decode_kernel<DT, GT, 32, 4, 1, 2, SP><<<grid, 2 * kWave, 0, st>>>(a); break;
     case 16: decode_kernel<DT, GT, 16, 4, 1, 1, SP><<<grid, 1 * kWave, 0, st>>>(a); break;
