@@ -85,6 +85,25 @@ def test_decode_step_bf16_b1(gated):
     assert_close(s, sr, TOL["bf16"], "state")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B", [8, 9], ids=["256_heads", "288_heads"])
+@pytest.mark.parametrize("gated", [True, False])
+def test_decode_on_both_sides_of_the_shape_switch(B, gated, dtype):
+    """At D = 128 the decode takes 512-thread workgroups up to 256 heads and
+    1024-thread ones above: both shapes against the oracle at the switch
+    (Hk 16, Hv 32: B = 8 is 256 heads, B = 9 is 288)."""
+    say("decode at the shape switch: B=%d %s gated=%s" % (B, dtype, gated))
+    ops = synth.random_operands(B, 1, 16, 32, 128, 128, dtype=dtype, seed=90 + B, s0_std=0.02)
+    d = dev(ops)
+    z, w = (d["z"], d["w"]) if gated else (None, None)
+    y, s = recurrent_step(d["q"], d["k"], d["v"], d["log_decay"], d["beta"], d["s0"], z, w)
+    torch.cuda.synchronize()
+    yr, sr = orc.step(ops["q"], ops["k"], ops["v"], ops["log_decay"], ops["beta"], ops["s0"],
+                      ops["z"] if gated else None, ops["w"] if gated else None)
+    assert_close(y, yr, TOL[dtype], "y")
+    assert_close(s, sr, TOL[dtype], "state")
+
+
 @pytest.mark.parametrize("gated", [True, False])
 def test_three_pass_step_matches_oracle_and_fused_step(gated):
     """The literal three-pass form gives the oracle's result (and the fused step's, to
