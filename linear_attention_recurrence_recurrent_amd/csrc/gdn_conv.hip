@@ -94,7 +94,13 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v)
         st[j][v] = a.state_in ? ld1<DT>(a.state_in, (b * C + c0 + v) * K + j) : 0.f;
-    if (a.state_out) {  // the next call's context; read before written (in place is safe)
+    // The next call's context.  With one tile per sequence (T <= 16: decode)
+    // it is the window after the loop, stored at the end, so no store precedes
+    // the loads of x (one vmcnt counts both: a wait for those loads would
+    // also wait for the stores).  With more tiles this tile writes it here,
+    // before any other tile could need state_in; read before written either
+    // way, so the in-place update is safe.
+    if (a.state_out && a.ntiles > 1) {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         const int64_t tt = T - K + j;
@@ -149,6 +155,12 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
         storev<DT, VEC>(a.y, xb + (t + u) * C, out);
       }
     }
+  }
+  if (a.state_out && a.ntiles == 1) {  // the last K inputs (or the carried context)
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) store1<DT>(a.state_out, (b * C + c0 + v) * K + j, win[j][v]);
   }
 }
 
